@@ -1,0 +1,298 @@
+"""Seeded synthetic inputs for the decode-step workloads.
+
+This module is shared by the CPU oracle's tests and by the GPU path's tests
+and benchmark. It holds no arithmetic of the decode step: it only produces
+weights, KV-cache contents, token ids, sequence lengths and block tables
+from fixed seeds, with the shapes and value distributions of the workloads
+(8B-class decoder shapes with random N(0, 0.02) weights, N(0, 1) KV).
+
+Random numbers come from the counter-based generator in ``synth.c``
+(SplitMix64 words, Box-Muller normals), so results do not depend on the
+thread count. Norm gains are 1.0 (the N(0, 0.02) draw applies to matrices).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+from dataclasses import dataclass, field, replace
+from typing import Dict, List, Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libsynth.so")
+_lib = None
+
+# fixed seeds per input family
+SEED_WEIGHTS = 0
+SEED_KV = 1
+SEED_TOKENS = 2
+SEED_LENGTHS = 3
+SEED_BLOCKS = 4
+SEED_HIDDEN = 5
+
+BF16_ONE = 0x3F80
+
+
+def build(force: bool = False) -> str:
+    """Compile libsynth.so with gcc (OpenMP)."""
+    src = os.path.join(_HERE, "synth.c")
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(src):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", tmp, src, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        u64, i64, dbl, vp = ctypes.c_uint64, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+        lib.synth_normal_f32.argtypes = [u64, u64, dbl, dbl, i64, vp]
+        lib.synth_normal_bf16.argtypes = [u64, u64, dbl, dbl, i64, vp]
+        lib.synth_uniform_int.argtypes = [u64, u64, i64, i64, i64, vp]
+        lib.synth_uniform_f64.argtypes = [u64, u64, i64, vp]
+        _lib = lib
+    return _lib
+
+
+# ----------------------------------------------------------------------------
+# raw generators
+
+
+def normal(seed: int, stream: int, shape, std: float = 1.0, dtype: str = "bf16", mean: float = 0.0) -> np.ndarray:
+    """N(mean, std) array; dtype 'bf16' returns uint16 bit patterns, 'f32' float32."""
+    n = int(np.prod(shape)) if len(shape) else 1
+    lib = _load()
+    if dtype == "bf16":
+        out = np.empty(shape, dtype=np.uint16)
+        lib.synth_normal_bf16(seed, stream, mean, std, n, out.ctypes.data)
+    elif dtype == "f32":
+        out = np.empty(shape, dtype=np.float32)
+        lib.synth_normal_f32(seed, stream, mean, std, n, out.ctypes.data)
+    else:
+        raise ValueError(dtype)
+    return out
+
+
+def uniform_int(seed: int, stream: int, lo: int, hi: int, n: int) -> np.ndarray:
+    out = np.empty(n, dtype=np.int64)
+    _load().synth_uniform_int(seed, stream, lo, hi, n, out.ctypes.data)
+    return out
+
+
+def uniform01(seed: int, stream: int, n: int) -> np.ndarray:
+    out = np.empty(n, dtype=np.float64)
+    _load().synth_uniform_f64(seed, stream, n, out.ctypes.data)
+    return out
+
+
+def bf16_to_f32(a: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns (uint16) to float32."""
+    return (a.astype(np.uint32) << 16).view(np.float32)
+
+
+def f32_to_bf16(a: np.ndarray) -> np.ndarray:
+    """Round-to-nearest-even narrowing of float32 to bf16 bit patterns."""
+    b = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    nan = (b & 0x7F800000) == 0x7F800000
+    nan &= (b & 0x007FFFFF) != 0
+    r = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+    r[nan] = ((b[nan] >> 16) | 0x40).astype(np.uint16)
+    return r
+
+
+# ----------------------------------------------------------------------------
+# model shapes and workloads
+
+
+@dataclass(frozen=True)
+class ModelShape:
+    n_layers: int
+    hidden: int
+    n_heads: int
+    n_kv_heads: int
+    head_dim: int
+    ffn: int
+    vocab: int
+    eps: float = 1e-6
+    rope_base: float = 10000.0
+    qk_norm: bool = True
+    wdtype: str = "bf16"  # 'bf16' or 'f32'
+    kv_dtype: str = "bf16"
+    embed_head: bool = True  # False: hidden-state in/out (one layer, no embedding / LM head)
+
+    @property
+    def qdim(self) -> int:
+        return self.n_heads * self.head_dim
+
+    @property
+    def kvdim(self) -> int:
+        return self.n_kv_heads * self.head_dim
+
+    @property
+    def kv_bytes_per_token_layer(self) -> int:
+        es = 2 if self.kv_dtype == "bf16" else 4
+        return 2 * self.kvdim * es
+
+    def layer_weight_bytes(self) -> int:
+        es = 2 if self.wdtype == "bf16" else 4
+        H, F = self.hidden, self.ffn
+        mats = (self.qdim + 2 * self.kvdim) * H + H * self.qdim + 3 * F * H
+        norms = 2 * H + (2 * self.head_dim if self.qk_norm else 0)
+        return (mats + norms) * es
+
+    def step_weight_bytes(self) -> int:
+        """Weight bytes one decode step streams (embedding rows not included)."""
+        es = 2 if self.wdtype == "bf16" else 4
+        b = self.n_layers * self.layer_weight_bytes()
+        if self.embed_head:
+            b += self.vocab * self.hidden * es + self.hidden * es
+        return b
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    shape: ModelShape
+    batch: int
+    steps: int
+    kv_len: str  # 'fixed:N', 'loguniform:lo:hi', 'uniform:lo:hi'
+    prompt: int = 0  # >0: prefill this many teacher-forced tokens instead of random KV
+    paged: bool = False
+    kv_block: int = 16
+
+    def capacity(self) -> int:
+        """KV capacity per sequence needed for the whole run."""
+        kind, *a = self.kv_len.split(":")
+        hi = int(a[-1])
+        return max(hi, self.prompt) + self.steps + 1
+
+
+TINY = ModelShape(n_layers=2, hidden=256, n_heads=4, n_kv_heads=4, head_dim=64, ffn=1024, vocab=1024,
+                  qk_norm=False, wdtype="f32", kv_dtype="f32")
+Q8B = ModelShape(n_layers=36, hidden=4096, n_heads=32, n_kv_heads=8, head_dim=128, ffn=12288, vocab=151936)
+Q8B_LAYER = replace(Q8B, n_layers=1, embed_head=False)
+
+WORKLOADS: Dict[str, Workload] = {
+    "tiny": Workload("tiny", TINY, batch=1, steps=16, kv_len="fixed:32"),
+    "layer8b": Workload("layer8b", Q8B_LAYER, batch=1, steps=64, kv_len="fixed:512"),
+    "q8b_b1": Workload("q8b_b1", Q8B, batch=1, steps=128, kv_len="fixed:1024", prompt=1024),
+    "q8b_b16": Workload("q8b_b16", Q8B, batch=16, steps=64, kv_len="loguniform:32:4096"),
+    "q8b_b8_paged": Workload("q8b_b8_paged", Q8B, batch=8, steps=32, kv_len="uniform:4096:16384", paged=True),
+}
+
+
+# ----------------------------------------------------------------------------
+# generators for the workloads
+
+# matrix ids inside one layer (stream = layer * 32 + id)
+_MATS = ["wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down"]
+_STREAM_EMBED = 1_000_001
+_STREAM_LM = 1_000_002
+
+
+def _gain(n: int, wdtype: str) -> np.ndarray:
+    if wdtype == "bf16":
+        return np.full(n, BF16_ONE, dtype=np.uint16)
+    return np.ones(n, dtype=np.float32)
+
+
+def layer_weights(shape: ModelShape, layer: int, seed: int = SEED_WEIGHTS, std: float = 0.02) -> Dict[str, np.ndarray]:
+    H, F, D = shape.hidden, shape.ffn, shape.head_dim
+    dims = {"wq": (shape.qdim, H), "wk": (shape.kvdim, H), "wv": (shape.kvdim, H), "wo": (H, shape.qdim),
+            "w_gate": (F, H), "w_up": (F, H), "w_down": (H, F)}
+    out = {}
+    for i, name in enumerate(_MATS):
+        out[name] = normal(seed, layer * 32 + i, dims[name], std, shape.wdtype)
+    out["attn_norm"] = _gain(H, shape.wdtype)
+    out["mlp_norm"] = _gain(H, shape.wdtype)
+    if shape.qk_norm:
+        out["q_norm"] = _gain(D, shape.wdtype)
+        out["k_norm"] = _gain(D, shape.wdtype)
+    return out
+
+
+def model_weights(shape: ModelShape, seed: int = SEED_WEIGHTS, std: float = 0.02) -> Dict[str, object]:
+    w: Dict[str, object] = {"layers": [layer_weights(shape, l, seed, std) for l in range(shape.n_layers)]}
+    if shape.embed_head:
+        w["embed"] = normal(seed, _STREAM_EMBED, (shape.vocab, shape.hidden), std, shape.wdtype)
+        w["lm_head"] = normal(seed, _STREAM_LM, (shape.vocab, shape.hidden), std, shape.wdtype)
+        w["final_norm"] = _gain(shape.hidden, shape.wdtype)
+    return w
+
+
+def seq_lengths(wl: Workload, seed: int = SEED_LENGTHS) -> np.ndarray:
+    """Initial KV length per sequence."""
+    kind, *a = wl.kv_len.split(":")
+    B = wl.batch
+    if kind == "fixed":
+        return np.full(B, int(a[0]), dtype=np.int64)
+    lo, hi = int(a[0]), int(a[1])
+    if kind == "uniform":
+        return uniform_int(seed, 0, lo, hi, B)
+    if kind == "loguniform":
+        u = uniform01(seed, 1, B)
+        v = np.exp(math.log(lo) + u * (math.log(hi) - math.log(lo)))
+        return np.clip(np.rint(v).astype(np.int64), lo, hi)
+    raise ValueError(kind)
+
+
+def kv_contents(shape: ModelShape, lengths: np.ndarray, capacity: int, seed: int = SEED_KV) -> List[Dict[str, np.ndarray]]:
+    """Per sequence: k, v arrays [n_layers, n_kv_heads, capacity, head_dim] (cache dtype).
+
+    Positions < length hold N(0, 1) values; the rest are zero.
+    """
+    out = []
+    L, Hkv, D = shape.n_layers, shape.n_kv_heads, shape.head_dim
+    dt = np.uint16 if shape.kv_dtype == "bf16" else np.float32
+    for b, n in enumerate(lengths):
+        n = int(n)
+        seq = {}
+        for kind, kid in (("k", 0), ("v", 1)):
+            arr = np.zeros((L, Hkv, capacity, D), dtype=dt)
+            for l in range(L):
+                for h in range(Hkv):
+                    stream = ((b * 4096 + l) * 256 + h) * 2 + kid
+                    arr[l, h, :n] = normal(seed, stream, (n, D), 1.0, shape.kv_dtype)
+            seq[kind] = arr
+        out.append(seq)
+    return out
+
+
+def tokens(wl: Workload, n: Optional[int] = None, seed: int = SEED_TOKENS, stream: int = 0) -> np.ndarray:
+    n = wl.batch if n is None else n
+    return uniform_int(seed, stream, 0, wl.shape.vocab - 1, n).astype(np.int32)
+
+
+def hidden_inputs(shape: ModelShape, batch: int, step: int, seed: int = SEED_HIDDEN) -> np.ndarray:
+    """N(0, 1) hidden-state input for hidden-I/O workloads, per step."""
+    return normal(seed, step, (batch, shape.hidden), 1.0, "f32")
+
+
+def block_table(lengths_cap: List[int], block: int, seed: int = SEED_BLOCKS) -> np.ndarray:
+    """Random permutation of a pool of ceil(cap_b / block) blocks per sequence.
+
+    Returns [B, max_blocks] int32 (unused entries = -1).
+    """
+    nblk = [(int(c) + block - 1) // block for c in lengths_cap]
+    pool = sum(nblk)
+    # Fisher-Yates with the counter generator
+    perm = np.arange(pool, dtype=np.int64)
+    if pool > 1:
+        r = uniform_int(seed, 0, 0, (1 << 62), pool)
+        for i in range(pool - 1, 0, -1):
+            j = int(r[i] % (i + 1))
+            perm[i], perm[j] = perm[j], perm[i]
+    mb = max(nblk)
+    tab = np.full((len(nblk), mb), -1, dtype=np.int32)
+    o = 0
+    for b, n in enumerate(nblk):
+        tab[b, :n] = perm[o:o + n]
+        o += n
+    return tab

@@ -1,0 +1,329 @@
+"""Pins of the CPU oracle against closed forms, invariants, independent
+library routines and brute force on tiny inputs (no GPU).
+
+Each test is chosen so that a plausible slip in the oracle (dropped term,
+wrong sign or index, transposed operand, wrong head mapping, append after
+instead of before attention, missing residual) fails at least one of them.
+"""
+import math
+from dataclasses import replace
+
+import numpy as np
+import pytest
+from scipy.special import expit, softmax
+
+import oracle
+import synth
+
+RNG = np.random.default_rng(1234)
+
+
+def f32(a):
+    return np.asarray(a, dtype=np.float32)
+
+
+# ----------------------------------------------------------------- RMSNorm
+
+def test_rmsnorm_constant_vector_closed_form():
+    # x = c * 1, unit gain: y_i = c / sqrt(c^2 + eps)
+    for c in (0.5, -3.0, 1e-3):
+        for eps in (1e-6, 0.25):
+            y = oracle.rmsnorm(np.full(64, c, np.float32), np.ones(64, np.float32), eps)
+            want = c / math.sqrt(c * c + eps)
+            np.testing.assert_allclose(y, want, rtol=1e-6)
+
+
+def test_rmsnorm_scale_invariance_and_unit_rms():
+    x = f32(RNG.normal(size=512) * 7.0)
+    g = np.ones(512, np.float32)
+    y1 = oracle.rmsnorm(x, g, 0.0)
+    y2 = oracle.rmsnorm(x * 3.5, g, 0.0)
+    np.testing.assert_allclose(y1, y2, rtol=2e-7, atol=1e-7)
+    # with eps = 0 the output has unit root-mean-square
+    assert abs(math.sqrt(np.mean(y1.astype(np.float64) ** 2)) - 1.0) < 1e-6
+
+
+def test_rmsnorm_gain_is_elementwise_and_bf16_gain():
+    x = f32(RNG.normal(size=128))
+    g = np.zeros(128, np.float32)
+    g[17] = 2.0
+    y = oracle.rmsnorm(x, g, 1e-6)
+    assert np.count_nonzero(y) == 1 and y[17] != 0
+    # bf16 gain of value 2.0 (0x4000) equals fp32 gain of 2.0
+    yb = oracle.rmsnorm(x, np.full(128, 0x4000, np.uint16), 1e-6)
+    yf = oracle.rmsnorm(x, np.full(128, 2.0, np.float32), 1e-6)
+    np.testing.assert_array_equal(yb, yf)
+
+
+# ----------------------------------------------------------------- matvec
+
+def test_matvec_hand_example_and_orientation():
+    W = f32([[1, 2], [3, 4], [5, 6]])  # [rows=3, cols=2]: y_r = sum_c W[r,c] x[c]
+    y = oracle.matvec(W, f32([1, -1]))
+    np.testing.assert_array_equal(y, f32([-1, -1, -1]))
+    y = oracle.matvec(W, f32([2, 0.5]))
+    np.testing.assert_array_equal(y, f32([3, 8, 13]))
+
+
+def test_matvec_identity_and_numpy_float64():
+    n = 96
+    x = f32(RNG.normal(size=n))
+    np.testing.assert_array_equal(oracle.matvec(np.eye(n, dtype=np.float32), x), x)
+    W = f32(RNG.normal(size=(37, 300)))
+    x = f32(RNG.normal(size=300))
+    ref = W.astype(np.float64) @ x.astype(np.float64)
+    np.testing.assert_allclose(oracle.matvec(W, x), ref.astype(np.float32), rtol=1e-6, atol=1e-6)
+
+
+def test_matvec_bf16_weights_widen_exactly():
+    Wf = f32(RNG.normal(size=(20, 64)))
+    Wb = synth.f32_to_bf16(Wf)
+    x = f32(RNG.normal(size=64))
+    ref = synth.bf16_to_f32(Wb).astype(np.float64) @ x.astype(np.float64)
+    np.testing.assert_allclose(oracle.matvec(Wb, x), ref.astype(np.float32), rtol=1e-6, atol=1e-6)
+
+
+# ----------------------------------------------------------------- RoPE
+
+def test_rope_position_zero_is_identity():
+    v = f32(RNG.normal(size=128))
+    np.testing.assert_array_equal(oracle.rope(v, 0), v)
+
+
+def test_rope_pairs_and_first_frequency():
+    D = 64
+    for i in (0, 5, D // 2 - 1):
+        e = np.zeros(D, np.float32)
+        e[i] = 1.0
+        r = oracle.rope(e, 3)
+        nz = set(np.flatnonzero(np.abs(r) > 0))
+        assert nz <= {i, i + D // 2}
+    # pair 0 turns by exactly pos radians (frequency base^0 = 1)
+    e = np.zeros(D, np.float32)
+    e[0] = 1.0
+    r = oracle.rope(e, 3)
+    assert abs(r[0] - math.cos(3.0)) < 1e-7 and abs(r[D // 2] - math.sin(3.0)) < 1e-7
+
+
+def test_rope_frequencies_geometric_in_base():
+    # angle of pair i at pos 1, recovered with atan2, is base^(-2i/D)
+    D, base = 16, 10000.0
+    ang = []
+    for i in range(D // 2):
+        e = np.zeros(D, np.float32)
+        e[i] = 1.0
+        r = oracle.rope(e, 1, base)
+        ang.append(math.atan2(float(r[i + D // 2]), float(r[i])))
+    ratios = np.array(ang[1:]) / np.array(ang[:-1])
+    np.testing.assert_allclose(ratios, base ** (-2.0 / D), rtol=1e-5)
+
+
+def test_rope_norm_preserved_and_relative_position():
+    D = 128
+    q = f32(RNG.normal(size=D))
+    k = f32(RNG.normal(size=D))
+    for p in (1, 17, 1000):
+        r = oracle.rope(q, p)
+        a = q[: D // 2].astype(np.float64) ** 2 + q[D // 2:].astype(np.float64) ** 2
+        b = r[: D // 2].astype(np.float64) ** 2 + r[D // 2:].astype(np.float64) ** 2
+        np.testing.assert_allclose(a, b, rtol=1e-5, atol=1e-6)
+    # <R(m) q, R(n) k> = <R(m - n) q, k>
+    for m, n in ((9, 4), (300, 100), (7, 7)):
+        lhs = float(np.dot(oracle.rope(q, m).astype(np.float64), oracle.rope(k, n).astype(np.float64)))
+        rhs = float(np.dot(oracle.rope(q, m - n).astype(np.float64), k.astype(np.float64)))
+        assert abs(lhs - rhs) < 1e-4 * (1 + abs(rhs))
+
+
+# ----------------------------------------------------------------- attention
+
+def test_attention_single_key_returns_v():
+    D = 64
+    q = f32(RNG.normal(size=D))
+    K = f32(RNG.normal(size=(1, D)))
+    V = f32(RNG.normal(size=(1, D)))
+    out, p = oracle.attention_head(q, K, V, return_probs=True)
+    np.testing.assert_array_equal(out, V[0])
+    assert p[0] == 1.0
+
+
+def test_attention_probs_sum_to_one_and_numpy():
+    D, n = 32, 57
+    q = f32(RNG.normal(size=D))
+    K = f32(RNG.normal(size=(n, D)))
+    V = f32(RNG.normal(size=(n, D)))
+    out, p = oracle.attention_head(q, K, V, return_probs=True)
+    assert abs(p.sum() - 1.0) < 1e-12
+    s = K.astype(np.float64) @ q.astype(np.float64) / math.sqrt(D)
+    ref = softmax(s) @ V.astype(np.float64)
+    np.testing.assert_allclose(out, ref, rtol=1e-6, atol=1e-7)
+    np.testing.assert_allclose(p, softmax(s), rtol=1e-12)
+
+
+def test_attention_two_key_closed_form():
+    # D = 2, q = (1, 0): scores (0, ln 3) give weights (1/4, 3/4)
+    a = math.sqrt(2.0) * math.log(3.0)
+    q = f32([1, 0])
+    K = f32([[0, 0], [a, 0]])
+    V = f32([[4, 8], [0, -4]])
+    out = oracle.attention_head(q, K, V)
+    np.testing.assert_allclose(out, [1.0, -1.0], rtol=1e-6, atol=1e-6)
+
+
+def test_attention_equal_keys_mean_dominant_and_permutation():
+    D, n = 16, 9
+    q = f32(RNG.normal(size=D))
+    V = f32(RNG.normal(size=(n, D)))
+    K = np.tile(f32(RNG.normal(size=D)), (n, 1))
+    np.testing.assert_allclose(oracle.attention_head(q, K, V), V.astype(np.float64).mean(0), rtol=1e-6, atol=1e-6)
+    K = f32(RNG.normal(size=(n, D)) * 0.01)
+    K[4] = q * 100.0
+    np.testing.assert_allclose(oracle.attention_head(q, K, V), V[4], rtol=1e-6, atol=1e-6)
+    K = f32(RNG.normal(size=(n, D)))
+    perm = RNG.permutation(n)
+    a = oracle.attention_head(q, K, V)
+    b = oracle.attention_head(q, np.ascontiguousarray(K[perm]), np.ascontiguousarray(V[perm]))
+    np.testing.assert_allclose(a, b, rtol=1e-6, atol=1e-7)
+
+
+# ----------------------------------------------------------------- SwiGLU
+
+def test_swiglu_closed_form():
+    g = f32([0.0, 1.0, -1.0, 30.0, -30.0, 0.5])
+    u = f32([5.0, 2.0, 3.0, 1.0, 1.0, -4.0])
+    out = oracle.swiglu(g, u)
+    ref = g.astype(np.float64) * expit(g.astype(np.float64)) * u
+    np.testing.assert_allclose(out, ref, rtol=1e-6, atol=1e-12)
+    assert out[0] == 0.0
+
+
+# ----------------------------------------------------------------- layer / model
+
+def _tiny_shape(**kw):
+    base = synth.ModelShape(n_layers=1, hidden=64, n_heads=4, n_kv_heads=2, head_dim=16, ffn=96, vocab=50,
+                            qk_norm=True, wdtype="f32", kv_dtype="f32")
+    return replace(base, **kw)
+
+
+def _weights(shape, seed=7):
+    return synth.model_weights(shape, seed=seed, std=0.2)
+
+
+def _cache(shape, cap, length, seed=8):
+    return synth.kv_contents(shape, np.array([length]), cap, seed=seed)[0]
+
+
+def test_layer_identity_when_output_projections_zero():
+    # W_o = W_d = 0: the layer returns x unchanged; logits = W_lm . RMSNorm(E[tok])
+    shape = _tiny_shape(n_layers=2)
+    w = _weights(shape)
+    for lw in w["layers"]:
+        lw["wo"][:] = 0
+        lw["w_down"][:] = 0
+    o = oracle.Oracle(shape, w)
+    cache = _cache(shape, 8, 3)
+    tok = 11
+    logits = o.model_forward(cache, tok, 3)
+    x = w["embed"][tok].astype(np.float64)
+    xn = x / np.sqrt(np.mean(x * x) + shape.eps)
+    ref = w["lm_head"].astype(np.float64) @ xn
+    np.testing.assert_allclose(logits, ref, rtol=1e-5, atol=1e-6)
+
+
+def test_layer_append_before_attention_at_position_zero():
+    # At pos 0 attention sees only the new key, so every q head of group g
+    # returns v_g rounded to the cache type; with W_d = 0 the layer output is
+    # x + W_o [v_{g(h)}]_h. bf16 cache: the rounded value is what counts.
+    shape = _tiny_shape(kv_dtype="bf16", qk_norm=False)
+    w = _weights(shape)
+    lw = w["layers"][0]
+    lw["w_down"][:] = 0
+    o = oracle.Oracle(shape, w)
+    cache = _cache(shape, 4, 0)
+    x = f32(RNG.normal(size=shape.hidden))
+    y = o.layer_forward(0, cache, 0, x)
+    xd = x.astype(np.float64)
+    xn = xd / np.sqrt(np.mean(xd * xd) + shape.eps)
+    v = (lw["wv"].astype(np.float64) @ xn).astype(np.float32)
+    vb = synth.bf16_to_f32(synth.f32_to_bf16(v)).reshape(shape.n_kv_heads, shape.head_dim)
+    # appended row equals the rounded projection (1 bf16 ulp slack for fp64-vs-fp32 ties)
+    got_v = synth.bf16_to_f32(cache["v"][0, :, 0, :])
+    np.testing.assert_allclose(got_v, vb, rtol=2 ** -7, atol=1e-6)
+    G = shape.n_heads // shape.n_kv_heads
+    att = np.concatenate([got_v[h // G] for h in range(shape.n_heads)]).astype(np.float64)
+    ref = xd + lw["wo"].astype(np.float64) @ att
+    np.testing.assert_allclose(y, ref, rtol=1e-5, atol=1e-6)
+    # positions other than 0 untouched
+    assert not np.any(cache["v"][0, :, 1:, :])
+
+
+def test_gqa_equals_mha_with_duplicated_kv_heads():
+    # consecutive query heads share a KV head: h -> floor(h * Hkv / Hq)
+    shape_g = _tiny_shape(n_heads=4, n_kv_heads=2)
+    shape_m = replace(shape_g, n_kv_heads=4)
+    wg = _weights(shape_g)
+    wm = {"layers": [dict(wg["layers"][0])]}
+    D = shape_g.head_dim
+    dup = np.concatenate([np.arange(0, D), np.arange(0, D), np.arange(D, 2 * D), np.arange(D, 2 * D)])
+    wm["layers"][0]["wk"] = np.ascontiguousarray(wg["layers"][0]["wk"][dup])
+    wm["layers"][0]["wv"] = np.ascontiguousarray(wg["layers"][0]["wv"][dup])
+    cg = _cache(shape_g, 12, 9)
+    cm = {k: np.ascontiguousarray(cg[k][:, [0, 0, 1, 1]]) for k in ("k", "v")}
+    x = f32(RNG.normal(size=shape_g.hidden))
+    yg = oracle.Oracle(shape_g, wg).layer_forward(0, cg, 9, x)
+    ym = oracle.Oracle(shape_m, wm).layer_forward(0, cm, 9, x)
+    np.testing.assert_array_equal(yg, ym)
+    # an interleaved mapping (h mod Hkv) would differ
+    cm2 = {k: np.ascontiguousarray(cg[k][:, [0, 1, 0, 1]]) for k in ("k", "v")}
+    wm2 = {"layers": [dict(wg["layers"][0])]}
+    dup2 = np.concatenate([np.arange(0, D), np.arange(D, 2 * D), np.arange(0, D), np.arange(D, 2 * D)])
+    wm2["layers"][0]["wk"] = np.ascontiguousarray(wg["layers"][0]["wk"][dup2])
+    wm2["layers"][0]["wv"] = np.ascontiguousarray(wg["layers"][0]["wv"][dup2])
+    ym2 = oracle.Oracle(shape_m, wm2).layer_forward(0, cm2, 9, x)
+    assert not np.array_equal(yg, ym2)
+
+
+def test_layer_matches_float64_composition_of_pinned_primitives():
+    # the layer equals the composition of the individually pinned primitives
+    shape = _tiny_shape()
+    w = _weights(shape)
+    lw = w["layers"][0]
+    o = oracle.Oracle(shape, w)
+    pos = 5
+    cache = _cache(shape, 8, pos)
+    cache_ref = {k: cache[k].copy() for k in cache}
+    x = f32(RNG.normal(size=shape.hidden))
+    y = o.layer_forward(0, cache, pos, x)
+    # reference in float64 numpy + scipy, independently of the oracle's loops
+    D, Hq, Hkv = shape.head_dim, shape.n_heads, shape.n_kv_heads
+    xd = x.astype(np.float64)
+
+    def rms(v, g):
+        return v / np.sqrt(np.mean(v * v) + shape.eps) * g
+
+    def rot(v, p):
+        h = D // 2
+        th = p * shape.rope_base ** (-2.0 * np.arange(h) / D)
+        a, b = v[:h], v[h:]
+        return np.concatenate([a * np.cos(th) - b * np.sin(th), b * np.cos(th) + a * np.sin(th)])
+
+    xn = rms(xd, 1.0)
+    q = (lw["wq"].astype(np.float64) @ xn).reshape(Hq, D)
+    k = (lw["wk"].astype(np.float64) @ xn).reshape(Hkv, D)
+    v = (lw["wv"].astype(np.float64) @ xn).reshape(Hkv, D)
+    q = np.stack([rot(rms(q[h], 1.0), pos) for h in range(Hq)])
+    k = np.stack([rot(rms(k[h], 1.0), pos) for h in range(Hkv)])
+    K = cache_ref["k"][0].astype(np.float64)
+    V = cache_ref["v"][0].astype(np.float64)
+    K[:, pos] = k
+    V[:, pos] = v
+    att = []
+    for h in range(Hq):
+        g = h * Hkv // Hq
+        s = K[g, : pos + 1] @ q[h] / math.sqrt(D)
+        att.append(softmax(s) @ V[g, : pos + 1])
+    x1 = xd + lw["wo"].astype(np.float64) @ np.concatenate(att)
+    xn = rms(x1, 1.0)
+    gt = lw["w_gate"].astype(np.float64) @ xn
+    up = lw["w_up"].astype(np.float64) @ xn
+    x2 = x1 + lw["w_down"].astype(np.float64) @ (gt * expit(gt) * up)
+    np.testing.assert_allclose(y, x2, rtol=2e-5, atol=2e-5)
