@@ -1,0 +1,246 @@
+"""Decode throughput of the persistent task-graph megakernel on one MI355X.
+
+Workload (the headline): the 36-layer Qwen3-8B-shaped decoder (hidden 4096,
+32 query / 8 KV heads of 128, SwiGLU 12288, vocab 151936, bf16 weights
+~N(0, 0.02) from a fixed seed), batch 1, a prompt of 1024 random token ids
+prefilled by teacher-forced decode steps (outside the timed region), then
+greedy decode. One timed step = one mk_decode_step (the whole step in one
+persistent launch) + mk_argmax + the caller's seq_lens increment.
+A second line of numbers (reported inside the same JSON object) covers the
+same model at batch 16 with KV lengths log-uniform in [32, 4096].
+
+Printed: ONE JSON line with tok/s (value), ms/step, HBM roofline of the
+megakernel (algorithmic bytes / average launch time from HIP events on the
+launch stream) and the CPU oracle's throughput on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--prompt", type=int, default=1024, help="prefill length (teacher-forced steps)")
+    ap.add_argument("--no-b16", action="store_true", help="skip the batch-16 measurement")
+    ap.add_argument("--b16-steps", type=int, default=64)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the CPU-oracle sample")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--mode", type=int, default=0, help="0 persistent, 1 kernel-per-op")
+    ap.add_argument("--jit", type=int, default=0)
+    ap.add_argument("--kv-chunk", type=int, default=0)
+    ap.add_argument("--workers", type=int, default=0)
+    ap.add_argument("--quick", action="store_true", help="tiny prompt, few steps (profiling runs)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if args.quick:
+        args.prompt, args.steps, args.warmup, args.b16_steps = 64, 8, 2, 8
+
+    import torch
+
+    import synth
+    from persistent_task_graph_amd import harness, mk
+
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    shape = synth.Q8B
+    wl = synth.WORKLOADS["q8b_b1"]
+    t0 = time.time()
+    weights = synth.model_weights(shape)
+    log("weights generated in %.1fs" % (time.time() - t0))
+    t0 = time.time()
+    dm = harness.DeviceModel(shape, weights, dev)
+    torch.cuda.synchronize()
+    log("weights uploaded in %.1fs" % (time.time() - t0))
+    opts = dict(mode=args.mode, jit=args.jit, kv_chunk=args.kv_chunk, workers=args.workers)
+
+    # ---------------------------------------------------------------- batch 1
+    B = 1
+    cap = args.prompt + args.warmup + args.steps + 8
+    kv = harness.DeviceKV(shape, B, cap)
+    plan = harness.build_plan(shape, B, cap, **opts)
+    info = plan.info()
+    st = torch.cuda.current_stream()
+    prompt = synth.tokens(wl, n=max(args.prompt, 1)).reshape(-1)
+    d_tok = torch.zeros(B, dtype=torch.int32, device=dev)
+    d_len = torch.zeros(B, dtype=torch.int32, device=dev)
+    logits = torch.empty((B, shape.vocab), dtype=torch.float32, device=dev)
+    t0 = time.time()
+    d_prompt = torch.from_numpy(prompt.astype(np.int32)).to(dev)
+    for i in range(args.prompt):  # teacher-forced prefill through the decode path
+        d_tok.copy_(d_prompt[i:i + 1])
+        plan.step(dm.struct, kv.struct, d_tok, d_len, logits)
+        d_len += 1
+    plan.argmax(logits, d_tok)
+    torch.cuda.synchronize()
+    log("prefill of %d tokens in %.1fs" % (args.prompt, time.time() - t0))
+    err = plan.device_error()
+    if err:
+        raise SystemExit("device error %d during prefill" % err)
+
+    def run(n, plan, kv, d_tok, d_len, logits, events=None):
+        for i in range(n):
+            if events is not None:
+                events[i][0].record(st)
+            plan.step(dm.struct, kv.struct, d_tok, d_len, logits)
+            if events is not None:
+                events[i][1].record(st)
+            plan.argmax(logits, d_tok)
+            d_len += 1
+
+    run(args.warmup, plan, kv, d_tok, d_len, logits)
+    torch.cuda.synchronize()
+    len0 = int(d_len.item())
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(st)
+    run(args.steps, plan, kv, d_tok, d_len, logits, ev)
+    e1.record(st)
+    torch.cuda.synchronize()
+    err = plan.device_error()
+    if err:
+        raise SystemExit("device error %d during timed steps" % err)
+    total_ms = e0.elapsed_time(e1)
+    k_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    ms_per_step = total_ms / args.steps
+    # algorithmic bytes per launch: weights once + KV of L+1 keys read + append + embed row + logits
+    bytes_per = [harness.step_bytes(shape, [len0 + i], B) for i in range(args.steps)]
+    avg_bytes = float(np.mean(bytes_per))
+    k_avg = float(k_ms.mean())
+    achieved = avg_bytes / (k_avg * 1e-3) / 1e9
+    tok_s = B * args.steps / (total_ms * 1e-3)
+    log("B=1: %.3f ms/step (kernel avg %.3f, median %.3f, p99 %.3f), %.1f tok/s, %.0f GB/s = %.1f%% of 8 TB/s"
+        % (ms_per_step, k_avg, np.median(k_ms), np.percentile(k_ms, 99), tok_s, achieved, 100 * achieved / PEAK_HBM_GBS))
+    plan.close()
+    del kv
+
+    result = {
+        "metric": "decode tokens/s at batch 1 (36-layer Qwen3-8B-shaped, bf16 weights)",
+        "value": round(tok_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded random-init weights N(0,0.02), random prompt ids)",
+        "config": {
+            "workload": "q8b_b1: 36-layer Qwen3-8B-shaped decoder, batch 1, prompt %d (prefilled), greedy decode"
+                        % args.prompt,
+            "batch": B, "kv_len_start": len0, "mode": "persistent" if args.mode == 0 else "kernel_per_op",
+            "workers": info.workers, "sched_waves": info.sched_waves, "kv_chunk": info.kv_chunk,
+            "jit": bool(info.jit),
+        },
+        "kernel_ms": {"mean": round(k_avg, 4), "median": round(float(np.median(k_ms)), 4),
+                      "p99": round(float(np.percentile(k_ms, 99)), 4)},
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+            "kernel": "persistent decode-step megakernel (one launch per step)",
+            "bytes_per_launch": int(avg_bytes),
+        },
+    }
+
+    # ---------------------------------------------------------------- batch 16
+    if not args.no_b16:
+        wl16 = synth.WORKLOADS["q8b_b16"]
+        B16 = wl16.batch
+        lens = synth.seq_lengths(wl16)
+        cap16 = int(lens.max()) + args.warmup + args.b16_steps + 8
+        t0 = time.time()
+        kv16 = harness.DeviceKV(shape, B16, cap16)
+        caches = synth.kv_contents(shape, lens, int(lens.max()) + 1)
+        for b in range(B16):
+            kv16.load_sequence(b, caches[b]["k"], caches[b]["v"], int(lens[b]))
+        del caches
+        torch.cuda.synchronize()
+        log("B=16 KV ready in %.1fs" % (time.time() - t0))
+        plan16 = harness.build_plan(shape, B16, cap16, **opts)
+        d_tok16 = torch.from_numpy(synth.tokens(wl16)).to(dev)
+        d_len16 = torch.from_numpy(lens.astype(np.int32)).to(dev)
+        logits16 = torch.empty((B16, shape.vocab), dtype=torch.float32, device=dev)
+        run(args.warmup, plan16, kv16, d_tok16, d_len16, logits16)
+        torch.cuda.synchronize()
+        l16 = d_len16.cpu().numpy().copy()
+        ev16 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.b16_steps)]
+        e0.record(st)
+        run(args.b16_steps, plan16, kv16, d_tok16, d_len16, logits16, ev16)
+        e1.record(st)
+        torch.cuda.synchronize()
+        err = plan16.device_error()
+        if err:
+            raise SystemExit("device error %d during batch-16 steps" % err)
+        t16 = e0.elapsed_time(e1)
+        k16 = np.array([a.elapsed_time(b) for a, b in ev16])
+        b16_bytes = float(np.mean([harness.step_bytes(shape, (l16 + i).tolist(), B16) for i in range(args.b16_steps)]))
+        ach16 = b16_bytes / (k16.mean() * 1e-3) / 1e9
+        tok16 = B16 * args.b16_steps / (t16 * 1e-3)
+        log("B=16: %.3f ms/step (kernel avg %.3f), %.1f tok/s, %.0f GB/s = %.1f%%"
+            % (t16 / args.b16_steps, k16.mean(), tok16, ach16, 100 * ach16 / PEAK_HBM_GBS))
+        result["batch16"] = {
+            "workload": "q8b_b16: same model, batch 16, KV lengths log-uniform in [32, 4096] (seeded)",
+            "value": round(tok16, 2), "unit": "tokens/s", "ms_per_step": round(t16 / args.b16_steps, 4),
+            "kernel_ms_mean": round(float(k16.mean()), 4), "hbm_gbs": round(ach16, 1),
+            "hbm_frac": round(ach16 / PEAK_HBM_GBS, 4), "bytes_per_launch": int(b16_bytes),
+        }
+        plan16.close()
+        del kv16
+
+    # ---------------------------------------------------------------- CPU oracle sample
+    if not args.no_cpu:
+        import oracle
+
+        threads = len(os.sched_getaffinity(0))
+        oracle.set_threads(threads)
+        orc = oracle.Oracle(shape, weights)
+        kvlen = 1024
+        cache = synth.kv_contents(shape, np.array([kvlen]), kvlen + 64)[0]
+        tok = int(prompt[0])
+        n = 0
+        t0 = time.time()
+        while True:
+            logits_c = orc.model_forward(cache, tok, kvlen + n)
+            tok = int(np.argmax(logits_c))
+            n += 1
+            if time.time() - t0 >= args.cpu_seconds or n >= 64:
+                break
+        dt = time.time() - t0
+        result["cpu_baseline"] = {
+            "value": round(n / dt, 4), "unit": "tokens/s", "cores": oracle.get_threads(), "kind": "oracle",
+            "sample": "%d greedy decode steps of the same 36-layer model, batch 1, KV length %d..%d "
+                      "(random N(0,1) KV), plain C oracle with OpenMP over output rows" % (n, kvlen, kvlen + n - 1),
+        }
+        log("CPU oracle: %d steps in %.1fs (%.3f tok/s, %d threads)" % (n, dt, n / dt, oracle.get_threads()))
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,165 @@
+// Device-side helpers and the kernel parameter block shared by the
+// persistent megakernel and the kernel-per-operator launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mk_internal.h"
+
+namespace mk {
+
+using bf16_t = uint16_t;
+
+constexpr int kThreads = 256;  // one workgroup = 4 wave64
+constexpr int kWaves = kThreads / 64;
+
+// Per-layer weight pointers (same layout as mk_layer_weights).
+struct LayerPtrs {
+    const void *attn_norm, *wq, *wk, *wv, *q_norm, *k_norm, *wo, *mlp_norm, *w_gate, *w_up, *w_down;
+};
+static_assert(sizeof(LayerPtrs) == sizeof(mk_layer_weights), "LayerPtrs layout");
+
+// Everything a task body needs; passed by value to every kernel.
+struct KParams {
+    // task graph
+    const TaskRec* tasks;
+    const int32_t* qoff;
+    const int32_t* queue;
+    const EventRec* evrec;
+    uint32_t* ev;
+    uint32_t* arrive;  // [B * Hkv] last-arrival counters (self-resetting)
+    RingSlot* jit;
+    RingSlot* mb;
+    Ctrl* ctrl;
+    const float2* rope;  // [cap][D/2] (cos, sin)
+    float* partials;     // [B * Hkv][max_splits][G * D + 2 G]
+    // activations (fp32)
+    const float* x0;  // layer-0 input [B, H]
+    float* x0_w;      // writable view of x0 (token mode: the embedding gather writes it)
+    float* act;       // per-layer blocks
+    int64_t act_stride;
+    int64_t off_qkv, off_attn, off_xmid, off_h, off_xnext;
+    float* x_final;  // output of the last layer's down projection
+    float* logits;
+    // weights
+    const LayerPtrs* lw;
+    const void* embed;
+    const void* final_norm;
+    const void* lm_head;
+    // KV cache
+    void* kv_k;
+    void* kv_v;
+    int64_t kv_layer_stride;
+    const int32_t* block_table;
+    // step inputs
+    const int32_t* tokens;
+    const int32_t* seq_lens;
+    // shape
+    int B, H, Hq, Hkv, D, F, V, L, QD, KD, cap, chunk, max_splits, qk_norm, paged, kv_block, max_blocks;
+    float eps, scale;
+    // schedule
+    uint32_t epoch;
+    int n_workers;
+    int jit_on;
+    int persistent;  // 1: events are signalled (persistent mode)
+    int jit_mask;
+    int mb_mask;
+    uint64_t watchdog_ticks;  // 100 MHz ticks
+};
+
+// ---------------------------------------------------------------- numerics
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    uint32_t b = __float_as_uint(f);
+    if ((b & 0x7F800000u) == 0x7F800000u && (b & 0x007FFFFFu)) return (bf16_t)((b >> 16) | 0x40u);
+    b += 0x7FFFu + ((b >> 16) & 1u);
+    return (bf16_t)(b >> 16);
+}
+
+// 16 bytes of weights widened to floats: 8 bf16 or 4 f32
+template <typename WT>
+struct Vec16;
+template <>
+struct Vec16<bf16_t> {
+    static constexpr int N = 8;
+    __device__ __forceinline__ static void widen(const uint4& w, float* f) {
+        f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x);
+        f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
+        f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z);
+        f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
+    }
+};
+template <>
+struct Vec16<float> {
+    static constexpr int N = 4;
+    __device__ __forceinline__ static void widen(const uint4& w, float* f) {
+        f[0] = __uint_as_float(w.x); f[1] = __uint_as_float(w.y);
+        f[2] = __uint_as_float(w.z); f[3] = __uint_as_float(w.w);
+    }
+};
+
+template <typename WT>
+__device__ __forceinline__ float load_scalar(const WT* p, int64_t i);
+template <>
+__device__ __forceinline__ float load_scalar<bf16_t>(const bf16_t* p, int64_t i) {
+    return __uint_as_float((uint32_t)p[i] << 16);
+}
+template <>
+__device__ __forceinline__ float load_scalar<float>(const float* p, int64_t i) {
+    return p[i];
+}
+
+template <typename WT>
+__device__ __forceinline__ float to_float(WT v);
+template <>
+__device__ __forceinline__ float to_float<bf16_t>(bf16_t v) { return __uint_as_float((uint32_t)v << 16); }
+template <>
+__device__ __forceinline__ float to_float<float>(float v) { return v; }
+
+template <typename WT>
+__device__ __forceinline__ WT from_float(float f);
+template <>
+__device__ __forceinline__ bf16_t from_float<bf16_t>(float f) { return f32_to_bf16(f); }
+template <>
+__device__ __forceinline__ float from_float<float>(float f) { return f; }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// ---------------------------------------------------------------- memory model
+
+__device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int64_t ld_acquire64(const int64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int64_t ld_relaxed64(const int64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+__device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
+
+__device__ __forceinline__ void raise_error(Ctrl* c, uint32_t bits) {
+    __hip_atomic_fetch_or(&c->error, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void raise_abort(Ctrl* c) {
+    raise_error(c, MK_ERR_TIMEOUT);
+    __hip_atomic_store(&c->abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool aborted(Ctrl* c) { return ld_relaxed(&c->abort) != 0; }
+
+}  // namespace mk

@@ -1,0 +1,126 @@
+// Internal records shared by the host planner (plan.cpp) and the device
+// runtime (runtime.hip). Plain C++ types only; no HIP headers here.
+#pragma once
+
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/mk.h"
+
+namespace mk {
+
+// Operator of a task. The numbering is also the index into
+// mk_plan_info::tasks_per_op.
+enum Op : uint8_t {
+    OP_NONE = 0,
+    OP_QKV = 1,     // [q|k|v] = W_qkv . RMSNorm(x)            (AOT GEMV)
+    OP_O = 2,       // x_mid = x + W_o . attn                  (AOT GEMV)
+    OP_GATEUP = 3,  // h = silu(W_g . RMSNorm(x_mid)) * (W_u . RMSNorm(x_mid))
+    OP_DOWN = 4,    // x_next = x_mid + W_d . h                (AOT GEMV)
+    OP_LM = 5,      // logits = W_lm . RMSNorm(x_final)        (AOT GEMV)
+    OP_ATTN = 6,    // split-KV attention + last-arrival combine (JIT, or AOT fallback)
+    OP_EMBED = 7,   // x_0 = E[token] (AOT row copy)
+};
+
+constexpr int kNumOps = 8;
+
+// Task record, 32 bytes (the MPK article's TaskDesc, §2.1, as our own
+// fixed-size record: operator, tile, the one event it waits on and the one
+// it signals).
+struct TaskRec {
+    uint8_t op;
+    uint8_t flags;
+    uint16_t layer;
+    int32_t a0;       // GEMV/EMBED: first row; ATTN: b * n_kv_heads + g
+    int32_t a1;       // GEMV/EMBED: end row;   ATTN: split index
+    int32_t wait_ev;  // event to wait on, -1 = none
+    int32_t sig_ev;   // event to signal on completion, -1 = none
+    int32_t level;    // task-graph level (kernel-per-op grouping, queue order)
+    int32_t pad[2];
+};
+static_assert(sizeof(TaskRec) == 32, "TaskRec size");
+
+// Event record (the article's Event, §2.1): the counter itself lives in a
+// separate uint32 array and only grows; step e is complete for this event
+// when counter - required * (e + 1) >= 0 (wrap-safe signed difference).
+struct EventRec {
+    uint32_t required;  // producer tasks per step
+    int32_t jit_layer;  // >= 0: the completing arrival posts "expand attention of this layer"
+};
+
+// One slot of the JIT ready ring or the scheduler mailbox. `tag` is
+// position + 1 once the payload is published (monotonic positions).
+struct RingSlot {
+    int64_t tag;
+    int32_t p0;
+    int32_t p1;
+};
+
+// Device control block (one per plan, zeroed at build).
+struct Ctrl {
+    uint32_t error;      // sticky mk_device_error bits
+    uint32_t abort;      // set when any wait times out; all loops exit
+    uint32_t pad0[14];
+    int64_t jit_tail;    // next JIT position to reserve (64 B apart from the head)
+    int64_t pad1[7];
+    int64_t jit_head;    // next JIT position to pop
+    int64_t pad2[7];
+    int64_t mb_tail;     // mailbox reserve position
+    int64_t pad3[7];
+    int64_t mb_head;     // mailbox pop position
+    int64_t pad4[7];
+};
+
+// Host-side plan (task graph) produced by the planner. Device buffers are
+// added by the runtime.
+struct HostPlan {
+    mk_model_desc desc;
+    int workers = 0;
+    int sched_wgs = 0;
+    int jit = 1;  // 1 JIT, 0 AOT attention
+    int kv_chunk = 256;
+    int max_splits = 0;
+    int n_levels = 0;
+    int cap = 0;  // KV positions per sequence
+    std::vector<TaskRec> tasks;
+    std::vector<EventRec> events;
+    std::vector<int32_t> queue_off;  // workers + 1
+    std::vector<int32_t> queue;      // task ids
+    std::vector<int32_t> level_off;  // n_levels + 1 (kernel-per-op)
+    std::vector<int32_t> level_tasks;
+    std::vector<uint8_t> level_op;   // op of each level
+    std::vector<uint16_t> level_layer;
+    int jit_ring_cap = 0;  // power of two
+    int mb_cap = 0;        // power of two
+    int max_jit_tasks = 0;
+    int tasks_per_op[kNumOps] = {0};
+    int64_t weight_bytes = 0;
+    int64_t kv_bytes_per_token = 0;
+};
+
+// Build / validate on the host. Returns false with `err` set on failure.
+bool build_host_plan(const mk_model_desc& desc, int device_cus, HostPlan& out, std::string& err);
+bool verify_plan(const HostPlan& p, std::string& err);
+// Dry run (see mk_plan_dry_run).
+bool dry_run(const HostPlan& p, int n_threads, uint64_t seed, int drop_task, int timeout_ms,
+             const int32_t* seq_lens, std::string& err);
+
+#if defined(__HIPCC__)
+#define MK_HD __host__ __device__
+#else
+#define MK_HD
+#endif
+
+// event id helpers: five events per layer, plus the embedding event
+MK_HD inline int ev_qkv(int l) { return 5 * l + 0; }
+MK_HD inline int ev_attn(int l) { return 5 * l + 1; }
+MK_HD inline int ev_o(int l) { return 5 * l + 2; }
+MK_HD inline int ev_gateup(int l) { return 5 * l + 3; }
+MK_HD inline int ev_down(int l) { return 5 * l + 4; }
+MK_HD inline int ev_embed(int n_layers) { return 5 * n_layers; }
+
+MK_HD inline int n_splits_for(int keys, int chunk) { return (keys + chunk - 1) / chunk; }
+
+}  // namespace mk

@@ -1,0 +1,531 @@
+// Host task-graph builder, verifier and dry-run executor.
+//
+// The builder turns one decode step into output-tile tasks linked by
+// event counters (MPK article, devpress.csdn.net, §2.1 TaskDesc / Event),
+// classifies each operator as JIT or AOT (§2.2 classify_task: the
+// attention, whose split count depends on the sequence lengths held on
+// the device, is JIT; every GEMV consumes a full vector produced by all
+// tiles of the previous operator, i.e. AOT_AFTER_BARRIER, expressed as an
+// event whose required count is the producer count), and places AOT
+// tasks in per-worker queues sorted by level (§5.1: workers = CUs - 4).
+#include <algorithm>
+#include <atomic>
+#include <chrono>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <random>
+#include <thread>
+
+#include "mk_internal.h"
+
+namespace mk {
+
+static int next_pow2(int v) {
+    int p = 1;
+    while (p < v) p <<= 1;
+    return p;
+}
+
+static bool fail(std::string& err, const std::string& m) {
+    err = m;
+    return false;
+}
+
+static int64_t op_rows(const mk_model_desc& d, int op) {
+    const int64_t QD = (int64_t)d.n_heads * d.head_dim, KD = (int64_t)d.n_kv_heads * d.head_dim;
+    switch (op) {
+        case OP_QKV: return QD + 2 * KD;
+        case OP_O: return d.hidden;
+        case OP_GATEUP: return d.ffn;
+        case OP_DOWN: return d.hidden;
+        case OP_LM: return d.vocab;
+        case OP_EMBED: return d.hidden;
+        default: return 0;
+    }
+}
+
+bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::string& err) {
+    // ---- validation
+    if (d.n_layers < 1 || d.n_layers > 1024) return fail(err, "n_layers must be in [1, 1024]");
+    if (d.hidden < 8 || d.hidden % 8) return fail(err, "hidden must be a positive multiple of 8");
+    if (d.head_dim != 64 && d.head_dim != 128) return fail(err, "head_dim must be 64 or 128");
+    if (d.n_heads < 1 || d.n_kv_heads < 1 || d.n_heads % d.n_kv_heads)
+        return fail(err, "n_heads must be a positive multiple of n_kv_heads");
+    if (d.n_heads / d.n_kv_heads > 8) return fail(err, "at most 8 query heads per KV head");
+    if (d.n_kv_heads > 64) return fail(err, "at most 64 KV heads");
+    if (d.ffn < 8 || d.ffn % 8) return fail(err, "ffn must be a positive multiple of 8");
+    if (!d.hidden_io && (d.vocab < 1)) return fail(err, "vocab must be positive");
+    if (d.batch < 1 || d.batch > 16) return fail(err, "batch must be in [1, 16]");
+    if (d.weight_dtype != MK_BF16 && d.weight_dtype != MK_F32) return fail(err, "weight_dtype must be MK_BF16 or MK_F32");
+    if (d.kv_dtype != d.weight_dtype) return fail(err, "kv_dtype must equal weight_dtype (bf16/bf16 or f32/f32)");
+    if (d.weight_dtype == MK_F32 && d.batch > 4) return fail(err, "f32 weights support batch <= 4");
+    {
+        const int64_t seg = d.weight_dtype == MK_BF16 ? 512 : 256;
+        const int64_t kmax = 4 * 8 * seg;  // four waves x eight 16-byte segments per lane
+        if (d.hidden > kmax || d.ffn > kmax || (int64_t)d.n_heads * d.head_dim > kmax)
+            return fail(err, "hidden, ffn and n_heads*head_dim must be <= " + std::to_string(kmax));
+    }
+    if (d.max_seq_len < 1 || d.max_seq_len > (1 << 22)) return fail(err, "max_seq_len must be in [1, 4M]");
+    if (!(d.rms_eps >= 0.f) || !(d.rope_base > 1.f)) return fail(err, "rms_eps must be >= 0 and rope_base > 1");
+    if (d.kv_layout != MK_KV_CONTIGUOUS && d.kv_layout != MK_KV_PAGED) return fail(err, "bad kv_layout");
+    if (d.kv_layout == MK_KV_PAGED) {
+        if (d.kv_block < 1 || d.kv_block > 1024) return fail(err, "kv_block must be in [1, 1024]");
+        if (d.max_blocks_per_seq < 1) return fail(err, "max_blocks_per_seq must be positive");
+        if ((int64_t)d.max_blocks_per_seq * d.kv_block < d.max_seq_len)
+            return fail(err, "max_blocks_per_seq * kv_block must cover max_seq_len");
+    }
+    const mk_exec_opts& o = d.opts;
+    if (o.mode != MK_PERSISTENT && o.mode != MK_KERNEL_PER_OP) return fail(err, "opts.mode must be 0 or 1");
+    if (device_cus < 2) return fail(err, "device has too few CUs");
+    p = HostPlan();
+    p.desc = d;
+    p.sched_wgs = o.sched_wgs > 0 ? o.sched_wgs : 4;
+    p.workers = o.workers > 0 ? o.workers : device_cus - p.sched_wgs;
+    if (p.workers < 1 || p.workers + p.sched_wgs > device_cus)
+        return fail(err, "workers + sched_wgs must be in [2, CU count] (one workgroup per CU)");
+    if (o.jit < 0 || o.jit > 2) return fail(err, "opts.jit must be 0, 1 or 2");
+    p.jit = (o.jit == 2) ? 0 : 1;
+    p.kv_chunk = o.kv_chunk > 0 ? o.kv_chunk : 256;
+    if (p.kv_chunk % 16 || p.kv_chunk > 4096) return fail(err, "kv_chunk must be a multiple of 16, at most 4096");
+    if (p.kv_chunk * (d.n_heads / d.n_kv_heads) > 16384) return fail(err, "kv_chunk * (n_heads / n_kv_heads) must be <= 16384");
+    p.cap = d.max_seq_len;
+    p.max_splits = n_splits_for(p.cap, p.kv_chunk);
+    if (p.max_splits > 65535) return fail(err, "too many splits per sequence");
+
+    const int L = d.n_layers, W = p.workers, B = d.batch, Hkv = d.n_kv_heads;
+    p.events.assign(5 * L + 1, EventRec{0, -1});
+    int rot = 0;
+    std::vector<std::vector<int32_t>> q(W);
+    int level = 0;
+
+    auto add_level = [&](int op, int layer) {
+        p.level_op.push_back((uint8_t)op);
+        p.level_layer.push_back((uint16_t)layer);
+        p.level_off.push_back((int32_t)p.level_tasks.size());
+    };
+    auto add_gemv = [&](int op, int layer, int wait, int sig, int min_rows) {
+        const int64_t rows = op_rows(d, op);
+        int64_t nt = std::min<int64_t>(W, (rows + min_rows - 1) / min_rows);
+        add_level(op, layer);
+        for (int64_t i = 0; i < nt; ++i) {
+            TaskRec t{};
+            t.op = (uint8_t)op;
+            t.layer = (uint16_t)layer;
+            t.a0 = (int32_t)(i * rows / nt);
+            t.a1 = (int32_t)((i + 1) * rows / nt);
+            if (t.a1 <= t.a0) continue;
+            t.wait_ev = wait;
+            t.sig_ev = sig;
+            t.level = level;
+            int id = (int)p.tasks.size();
+            p.tasks.push_back(t);
+            p.level_tasks.push_back(id);
+            q[(i + rot) % W].push_back(id);
+            if (sig >= 0) p.events[sig].required++;
+            p.tasks_per_op[op]++;
+        }
+        rot = (int)((rot + nt) % W);
+        level++;
+    };
+
+    int prev = -1;
+    if (!d.hidden_io) {
+        add_gemv(OP_EMBED, 0, -1, ev_embed(L), 256);
+        prev = ev_embed(L);
+    }
+    for (int l = 0; l < L; ++l) {
+        add_gemv(OP_QKV, l, prev, ev_qkv(l), 1);
+        // attention: one level; tasks exist in AOT mode only (JIT tasks are
+        // created on the device by the scheduler waves)
+        add_level(OP_ATTN, l);
+        if (p.jit) {
+            p.events[ev_qkv(l)].jit_layer = l;
+        } else {
+            for (int bg = 0; bg < B * Hkv; ++bg)
+                for (int s = 0; s < p.max_splits; ++s) {
+                    TaskRec t{};
+                    t.op = OP_ATTN;
+                    t.layer = (uint16_t)l;
+                    t.a0 = bg;
+                    t.a1 = s;
+                    t.wait_ev = ev_qkv(l);
+                    t.sig_ev = ev_attn(l);
+                    t.level = level;
+                    int id = (int)p.tasks.size();
+                    p.tasks.push_back(t);
+                    p.level_tasks.push_back(id);
+                    q[rot].push_back(id);
+                    rot = (rot + 1) % W;
+                    p.tasks_per_op[OP_ATTN]++;
+                }
+        }
+        p.events[ev_attn(l)].required = (uint32_t)(B * Hkv);
+        level++;
+        add_gemv(OP_O, l, ev_attn(l), ev_o(l), 1);
+        add_gemv(OP_GATEUP, l, ev_o(l), ev_gateup(l), 1);
+        add_gemv(OP_DOWN, l, ev_gateup(l), ev_down(l), 1);
+        prev = ev_down(l);
+    }
+    if (!d.hidden_io) add_gemv(OP_LM, 0, prev, -1, 1);
+    p.n_levels = level;
+    p.level_off.push_back((int32_t)p.level_tasks.size());
+
+    p.queue_off.assign(W + 1, 0);
+    for (int w = 0; w < W; ++w) p.queue_off[w + 1] = p.queue_off[w] + (int32_t)q[w].size();
+    p.queue.reserve(p.queue_off[W]);
+    for (int w = 0; w < W; ++w) p.queue.insert(p.queue.end(), q[w].begin(), q[w].end());
+
+    if (o.debug_extra_required > 0) {
+        if (o.debug_event < 0 || o.debug_event >= (int)p.events.size()) return fail(err, "debug_event out of range");
+        p.events[o.debug_event].required += (uint32_t)o.debug_extra_required;
+    }
+
+    const int64_t per_layer_jit = (int64_t)B * Hkv * p.max_splits;
+    if (per_layer_jit > (1 << 26)) return fail(err, "too many attention tasks per layer");
+    p.max_jit_tasks = (int)per_layer_jit;
+    p.jit_ring_cap = next_pow2(std::max<int>(64, (int)per_layer_jit));
+    p.mb_cap = next_pow2(std::max(16, L));
+
+    const int64_t es = d.weight_dtype == MK_BF16 ? 2 : 4;
+    const int64_t H = d.hidden, F = d.ffn, QD = (int64_t)d.n_heads * d.head_dim, KD = (int64_t)Hkv * d.head_dim;
+    int64_t layer = ((QD + 2 * KD) * H + H * QD + 3 * F * H + 2 * H + (d.qk_norm ? 2 * d.head_dim : 0)) * es;
+    p.weight_bytes = L * layer + (d.hidden_io ? 0 : ((int64_t)d.vocab * H + H) * es);
+    p.kv_bytes_per_token = (int64_t)L * 2 * KD * (d.kv_dtype == MK_BF16 ? 2 : 4);
+    return true;
+}
+
+bool verify_plan(const HostPlan& p, std::string& err) {
+    const mk_model_desc& d = p.desc;
+    const int nt = (int)p.tasks.size();
+    // queues: every task exactly once, levels non-decreasing
+    std::vector<int> seen(nt, 0);
+    if ((int)p.queue_off.size() != p.workers + 1) return fail(err, "queue_off size");
+    for (int w = 0; w < p.workers; ++w) {
+        int last = -1;
+        for (int i = p.queue_off[w]; i < p.queue_off[w + 1]; ++i) {
+            int t = p.queue[i];
+            if (t < 0 || t >= nt) return fail(err, "queue holds a bad task id");
+            seen[t]++;
+            if (p.tasks[t].level < last) return fail(err, "queue of worker " + std::to_string(w) + " not level-sorted");
+            last = p.tasks[t].level;
+        }
+    }
+    for (int t = 0; t < nt; ++t)
+        if (seen[t] != 1) return fail(err, "task " + std::to_string(t) + " queued " + std::to_string(seen[t]) + " times");
+    // producers per event; waits only on strictly lower levels
+    std::vector<uint32_t> prod(p.events.size(), 0);
+    std::vector<int> prod_level(p.events.size(), -1);
+    for (const TaskRec& t : p.tasks) {
+        if (t.sig_ev >= (int)p.events.size() || t.wait_ev >= (int)p.events.size()) return fail(err, "event id range");
+        if (t.sig_ev >= 0 && t.op != OP_ATTN) {
+            prod[t.sig_ev]++;
+            prod_level[t.sig_ev] = std::max(prod_level[t.sig_ev], t.level);
+        }
+    }
+    for (int l = 0; l < d.n_layers; ++l) {
+        prod[ev_attn(l)] += (uint32_t)(d.batch * d.n_kv_heads);  // combines
+        prod_level[ev_attn(l)] = -2;                              // checked through levels below
+    }
+    for (size_t e = 0; e < p.events.size(); ++e) {
+        uint32_t req = p.events[e].required;
+        if ((int)e == d.opts.debug_event && d.opts.debug_extra_required > 0) req -= (uint32_t)d.opts.debug_extra_required;
+        if (req != prod[e]) return fail(err, "event " + std::to_string(e) + " required " + std::to_string(req) +
+                                                 " != producers " + std::to_string(prod[e]));
+    }
+    for (const TaskRec& t : p.tasks) {
+        if (t.wait_ev < 0) continue;
+        if (prod_level[t.wait_ev] >= t.level)
+            return fail(err, "task waits on an event produced at its own or a later level");
+    }
+    // row coverage per GEMV level
+    for (int lv = 0; lv < p.n_levels; ++lv) {
+        int op = p.level_op[lv];
+        if (op == OP_ATTN) continue;
+        std::vector<std::pair<int, int>> r;
+        for (int i = p.level_off[lv]; i < p.level_off[lv + 1]; ++i) {
+            const TaskRec& t = p.tasks[p.level_tasks[i]];
+            if (t.op != op || t.level != lv) return fail(err, "level list mixes operators");
+            r.push_back({t.a0, t.a1});
+        }
+        std::sort(r.begin(), r.end());
+        int64_t at = 0;
+        for (auto& x : r) {
+            if (x.first != at || x.second <= x.first) return fail(err, "rows not covered exactly once at level " + std::to_string(lv));
+            at = x.second;
+        }
+        if (at != op_rows(d, op)) return fail(err, "rows not fully covered at level " + std::to_string(lv));
+    }
+    if (!p.jit) {
+        for (int lv = 0; lv < p.n_levels; ++lv) {
+            if (p.level_op[lv] != OP_ATTN) continue;
+            int n = p.level_off[lv + 1] - p.level_off[lv];
+            if (n != d.batch * d.n_kv_heads * p.max_splits) return fail(err, "AOT attention level incomplete");
+        }
+    }
+    return true;
+}
+
+// ---------------------------------------------------------------------------
+// Dry run: host threads replay the persistent protocol on integer data.
+
+namespace {
+
+inline uint64_t mix64(uint64_t z) {
+    z += 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+struct DryState {
+    const HostPlan& p;
+    std::vector<int> seq;
+    // per level: output array
+    std::vector<std::vector<std::atomic<uint64_t>>> out;
+    std::vector<std::atomic<uint32_t>> ev;
+    std::vector<std::atomic<uint32_t>> arrive;
+    std::vector<std::atomic<uint64_t>> partial;  // [B*Hkv][max_splits]
+    std::vector<RingSlot> jit;
+    std::vector<std::atomic<int64_t>> jit_tag;
+    std::atomic<int64_t> jit_tail{0}, jit_head{0};
+    std::vector<std::atomic<int64_t>> mb_tag;
+    std::vector<int32_t> mb_payload;
+    std::atomic<int64_t> mb_tail{0}, mb_head{0};
+    std::atomic<int> abort{0};
+    int drop;
+    std::chrono::steady_clock::time_point deadline;
+    std::vector<int> level_of_event;  // producing level
+    explicit DryState(const HostPlan& pl) : p(pl) {}
+};
+
+uint64_t level_input_sum(DryState& s, int lv) {
+    uint64_t h = 0;
+    for (auto& v : s.out[lv]) h += v.load(std::memory_order_acquire);
+    return h;
+}
+
+// level whose outputs a task at `lv` consumes: the previous level (or none)
+int input_level(const HostPlan& p, int lv) { return lv - 1; }
+
+int64_t level_rows(const HostPlan& p, int lv) {
+    const mk_model_desc& d = p.desc;
+    if (p.level_op[lv] == OP_ATTN) return (int64_t)d.batch * d.n_kv_heads;
+    return op_rows(d, p.level_op[lv]);
+}
+
+void run_gemv(DryState& s, const TaskRec& t) {
+    int in = input_level(s.p, t.level);
+    uint64_t sum = in >= 0 ? level_input_sum(s, in) : 0x1234;
+    for (int r = t.a0; r < t.a1; ++r)
+        s.out[t.level][r].store(mix64(sum ^ ((uint64_t)t.level << 40) ^ (uint64_t)r), std::memory_order_release);
+}
+
+bool run_attn(DryState& s, int layer, int bg, int split, int lv) {
+    const HostPlan& p = s.p;
+    int b = bg / p.desc.n_kv_heads;
+    int keys = s.seq[b] + 1;
+    int ns = n_splits_for(keys, p.kv_chunk);
+    if (split >= ns) return false;  // reserved but unused (AOT mode)
+    uint64_t sum = level_input_sum(s, lv - 1);
+    s.partial[(size_t)bg * p.max_splits + split].store(mix64(sum ^ ((uint64_t)bg << 20) ^ (uint64_t)split),
+                                                       std::memory_order_release);
+    uint32_t old = s.arrive[bg].fetch_add(1, std::memory_order_acq_rel);
+    if ((int)old + 1 == ns) {
+        uint64_t c = 0;
+        for (int i = 0; i < ns; ++i) c = mix64(c ^ s.partial[(size_t)bg * p.max_splits + i].load(std::memory_order_acquire));
+        s.out[lv][bg].store(c, std::memory_order_release);
+        s.arrive[bg].store(0, std::memory_order_relaxed);
+        return true;  // completing split signals the attention event
+    }
+    return false;
+}
+
+}  // namespace
+
+bool dry_run(const HostPlan& p, int n_threads, uint64_t seed, int drop_task, int timeout_ms, const int32_t* seq_lens,
+             std::string& err) {
+    const mk_model_desc& d = p.desc;
+    DryState s(p);
+    s.seq.resize(d.batch);
+    for (int b = 0; b < d.batch; ++b) {
+        int v = seq_lens ? seq_lens[b] : 0;
+        if (v < 0 || v + 1 > p.cap) return fail(err, "seq_lens out of range for the plan");
+        s.seq[b] = v;
+    }
+    s.drop = drop_task;
+    s.out = std::vector<std::vector<std::atomic<uint64_t>>>(p.n_levels);
+    for (int lv = 0; lv < p.n_levels; ++lv) {
+        s.out[lv] = std::vector<std::atomic<uint64_t>>(level_rows(p, lv));
+        for (auto& v : s.out[lv]) v.store(0);
+    }
+    s.ev = std::vector<std::atomic<uint32_t>>(p.events.size());
+    for (auto& e : s.ev) e.store(0);
+    s.arrive = std::vector<std::atomic<uint32_t>>(d.batch * d.n_kv_heads);
+    for (auto& a : s.arrive) a.store(0);
+    s.partial = std::vector<std::atomic<uint64_t>>((size_t)d.batch * d.n_kv_heads * p.max_splits);
+    s.jit.resize(p.jit_ring_cap);
+    s.jit_tag = std::vector<std::atomic<int64_t>>(p.jit_ring_cap);
+    for (auto& t : s.jit_tag) t.store(0);
+    s.mb_tag = std::vector<std::atomic<int64_t>>(p.mb_cap);
+    for (auto& t : s.mb_tag) t.store(0);
+    s.mb_payload.assign(p.mb_cap, 0);
+    s.deadline = std::chrono::steady_clock::now() + std::chrono::milliseconds(timeout_ms > 0 ? timeout_ms : 5000);
+
+    const int W = p.workers;
+    const int nthr = std::max(1, std::min(n_threads, W));
+
+    auto timed_out = [&]() {
+        if (s.abort.load()) return true;
+        if (std::chrono::steady_clock::now() > s.deadline) {
+            s.abort.store(1);
+            return true;
+        }
+        return false;
+    };
+    auto signal = [&](int e) {
+        if (e < 0) return;
+        uint32_t old = s.ev[e].fetch_add(1, std::memory_order_acq_rel);
+        if (old + 1 == p.events[e].required && p.events[e].jit_layer >= 0) {
+            int64_t pos = s.mb_tail.fetch_add(1);
+            s.mb_payload[pos % p.mb_cap] = p.events[e].jit_layer;
+            s.mb_tag[pos % p.mb_cap].store(pos + 1, std::memory_order_release);
+        }
+    };
+    auto attn_level = [&](int layer) {
+        for (int lv = 0; lv < p.n_levels; ++lv)
+            if (p.level_op[lv] == OP_ATTN && p.level_layer[lv] == layer) return lv;
+        return -1;
+    };
+    auto try_pop_jit = [&](int& layer, int& bg, int& split) {
+        int64_t h = s.jit_head.load(std::memory_order_acquire);
+        RingSlot& sl = s.jit[h % p.jit_ring_cap];
+        if (s.jit_tag[h % p.jit_ring_cap].load(std::memory_order_acquire) != h + 1) return false;
+        int p0 = sl.p0, p1 = sl.p1;
+        if (!s.jit_head.compare_exchange_strong(h, h + 1)) return false;
+        layer = p0 >> 16;
+        bg = p0 & 0xFFFF;
+        split = p1;
+        return true;
+    };
+    auto run_jit = [&](int layer, int bg, int split, std::mt19937_64& rng) {
+        std::this_thread::sleep_for(std::chrono::microseconds(rng() % 40));
+        int lv = attn_level(layer);
+        if (run_attn(s, layer, bg, split, lv)) signal(ev_attn(layer));
+    };
+
+    // scheduler thread: pops the mailbox and expands attention tasks
+    std::thread sched;
+    if (p.jit) {
+        sched = std::thread([&]() {
+            std::mt19937_64 rng(seed ^ 0xABCDEF);
+            int64_t want = d.n_layers;
+            while (s.mb_head.load() < want) {
+                if (timed_out()) return;
+                int64_t h = s.mb_head.load();
+                if (s.mb_tag[h % p.mb_cap].load(std::memory_order_acquire) != h + 1) {
+                    std::this_thread::yield();
+                    continue;
+                }
+                int layer = s.mb_payload[h % p.mb_cap];
+                if (!s.mb_head.compare_exchange_strong(h, h + 1)) continue;
+                std::this_thread::sleep_for(std::chrono::microseconds(rng() % 30));
+                for (int b = 0; b < d.batch; ++b) {
+                    int ns = n_splits_for(s.seq[b] + 1, p.kv_chunk);
+                    for (int g = 0; g < d.n_kv_heads; ++g)
+                        for (int sp = 0; sp < ns; ++sp) {
+                            int64_t pos = s.jit_tail.fetch_add(1);
+                            RingSlot& sl = s.jit[pos % p.jit_ring_cap];
+                            sl.p0 = (layer << 16) | (b * d.n_kv_heads + g);
+                            sl.p1 = sp;
+                            s.jit_tag[pos % p.jit_ring_cap].store(pos + 1, std::memory_order_release);
+                        }
+                }
+            }
+        });
+    }
+
+    // worker threads: each host thread plays workers ti, ti + nthr, ...
+    // round-robin, advancing one whose next task is ready, and running JIT
+    // tasks while none is (as the device workers drain the JIT ring while
+    // they wait)
+    std::vector<std::thread> th;
+    for (int ti = 0; ti < nthr; ++ti) {
+        th.emplace_back([&, ti]() {
+            std::mt19937_64 rng(seed * 1000003ull + ti);
+            std::vector<int> mine, cur;
+            for (int w = ti; w < W; w += nthr) {
+                mine.push_back(w);
+                cur.push_back(p.queue_off[w]);
+            }
+            size_t left = mine.size();
+            while (left) {
+                if (timed_out()) return;
+                bool progressed = false;
+                for (size_t k = 0; k < mine.size(); ++k) {
+                    int w = mine[k];
+                    if (cur[k] >= p.queue_off[w + 1]) continue;
+                    const TaskRec& t = p.tasks[p.queue[cur[k]]];
+                    if (t.wait_ev >= 0) {
+                        uint32_t tgt = p.events[t.wait_ev].required;
+                        if ((int32_t)(s.ev[t.wait_ev].load(std::memory_order_acquire) - tgt) < 0) continue;
+                    }
+                    if (rng() % 4 == 0) std::this_thread::sleep_for(std::chrono::microseconds(rng() % 50));
+                    cur[k]++;
+                    if (cur[k] >= p.queue_off[w + 1]) left--;
+                    progressed = true;
+                    if (t.op == OP_ATTN) {
+                        if (run_attn(s, t.layer, t.a0, t.a1, t.level)) signal(t.sig_ev);
+                        continue;
+                    }
+                    run_gemv(s, t);
+                    if ((int)(&t - p.tasks.data()) == s.drop) continue;  // injected fault: never signals
+                    signal(t.sig_ev);
+                }
+                if (!progressed) {
+                    int layer, bg, sp;
+                    if (p.jit && try_pop_jit(layer, bg, sp)) run_jit(layer, bg, sp, rng);
+                    else std::this_thread::yield();
+                }
+            }
+        });
+    }
+    for (auto& t : th) t.join();
+    if (p.jit) {
+        s.abort.store(s.abort.load() | 0);  // scheduler exits on its own once every message is popped
+        sched.join();
+    }
+    if (!s.abort.load())
+        for (int l = 0; l < d.n_layers; ++l)
+            if (s.ev[ev_attn(l)].load() != p.events[ev_attn(l)].required)
+                return fail(err, "attention tasks left undone when every worker finished its queue");
+    if (s.abort.load()) return fail(err, "timeout: dry run did not complete (a wait never became ready)");
+
+    // sequential reference: evaluate levels in order
+    std::vector<std::vector<uint64_t>> ref(p.n_levels);
+    for (int lv = 0; lv < p.n_levels; ++lv) {
+        ref[lv].assign(level_rows(p, lv), 0);
+        uint64_t sum = 0x1234;
+        if (lv > 0) {
+            sum = 0;
+            for (uint64_t v : ref[lv - 1]) sum += v;
+        }
+        if (p.level_op[lv] == OP_ATTN) {
+            for (int bg = 0; bg < d.batch * d.n_kv_heads; ++bg) {
+                int ns = n_splits_for(s.seq[bg / d.n_kv_heads] + 1, p.kv_chunk);
+                uint64_t c = 0;
+                for (int i = 0; i < ns; ++i) c = mix64(c ^ mix64(sum ^ ((uint64_t)bg << 20) ^ (uint64_t)i));
+                ref[lv][bg] = c;
+            }
+        } else {
+            for (int64_t r = 0; r < (int64_t)ref[lv].size(); ++r) ref[lv][r] = mix64(sum ^ ((uint64_t)lv << 40) ^ (uint64_t)r);
+        }
+    }
+    for (int lv = 0; lv < p.n_levels; ++lv)
+        for (size_t r = 0; r < ref[lv].size(); ++r)
+            if (s.out[lv][r].load() != ref[lv][r])
+                return fail(err, "checksum mismatch at level " + std::to_string(lv) + " row " + std::to_string(r));
+    return true;
+}
+
+}  // namespace mk

@@ -1,0 +1,544 @@
+// Persistent megakernel, kernel-per-operator launches and the C ABI.
+//
+// Persistent mode (MPK article, devpress.csdn.net, §2.1 "Mega-Kernel执行模型"):
+// one cooperative launch of (workers + scheduler) workgroups, one per CU.
+//  - Worker workgroups walk their ahead-of-time queue. Before a task they
+//    wait for its event counter to reach required * (epoch + 1); while
+//    waiting they pop just-in-time attention tasks from the ready ring
+//    (§2.2: attention is JIT, GEMVs AOT).
+//  - Scheduler workgroups run four independent waves each (16 waves with
+//    the default four scheduler CUs, §5.1). A wave pops "layer l finished
+//    its QKV" messages from the mailbox, reads seq_lens on the device and
+//    publishes one attention task per (sequence, KV head, KV split).
+//  - Every spin wait is bounded by a watchdog on the 100 MHz real-time
+//    counter; on expiry the error word gets MK_ERR_TIMEOUT and every
+//    workgroup leaves its loops.
+// Kernel-per-operator mode (§1, the execution model MPK replaces) launches
+// one kernel per task-graph level running the same task bodies.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "tasks.h"
+#include "kernels.h"
+
+namespace mk {
+
+// argmax over each logits row, lowest index on ties
+__global__ __launch_bounds__(kThreads) void k_argmax(const float* logits, int V, int32_t* out) {
+    __shared__ float sv[kWaves];
+    __shared__ int si[kWaves];
+    const float* row = logits + (int64_t)blockIdx.x * V;
+    float best = -INFINITY;
+    int bi = V;
+    for (int i = threadIdx.x; i < V; i += kThreads) {
+        const float v = row[i];
+        if (v > best) {  // strict: the first (lowest) index wins ties; NaN never wins
+            best = v;
+            bi = i;
+        }
+    }
+    for (int o = 32; o >= 1; o >>= 1) {
+        const float ov = __shfl_xor(best, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        if (ov > best || (ov == best && oi < bi)) {
+            best = ov;
+            bi = oi;
+        }
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) {
+        sv[wave] = best;
+        si[wave] = bi;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < kWaves; ++w)
+            if (sv[w] > best || (sv[w] == best && si[w] < bi)) {
+                best = sv[w];
+                bi = si[w];
+            }
+        out[blockIdx.x] = bi < V ? bi : 0;
+    }
+}
+
+}  // namespace mk
+
+// ============================================================================
+// host side
+
+using namespace mk;
+
+struct mk_plan {
+    HostPlan hp;
+    int device = 0;
+    int cus = 0;
+    bool host_only = false;
+    // device memory
+    char* dmem = nullptr;
+    size_t dbytes = 0;
+    TaskRec* d_tasks = nullptr;
+    int32_t* d_qoff = nullptr;
+    int32_t* d_queue = nullptr;
+    int32_t* d_level_tasks = nullptr;
+    EventRec* d_evrec = nullptr;
+    uint32_t* d_ev = nullptr;
+    uint32_t* d_arrive = nullptr;
+    RingSlot* d_jit = nullptr;
+    RingSlot* d_mb = nullptr;
+    Ctrl* d_ctrl = nullptr;
+    float2* d_rope = nullptr;
+    float* d_partials = nullptr;
+    float* d_act = nullptr;
+    float* d_x0 = nullptr;
+    float* d_xfinal = nullptr;
+    LayerPtrs* d_lw = nullptr;
+    int64_t act_stride = 0, off_qkv = 0, off_attn = 0, off_xmid = 0, off_h = 0, off_xnext = 0;
+    size_t ctrl_off = 0, ev_off = 0, arrive_off = 0, jit_off = 0, mb_off = 0, ctrl_bytes = 0;
+    // state
+    std::vector<LayerPtrs> cached_lw;
+    LayerPtrs* h_lw_pinned = nullptr;
+    uint32_t epoch = 0;
+    int lds_bytes = 0;
+    int lds_bytes_persistent = 0;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+void set_err(const std::string& s) { g_err = s; }
+
+bool hip_ok(hipError_t e, const char* what) {
+    if (e == hipSuccess) return true;
+    set_err(std::string(what) + ": " + hipGetErrorString(e));
+    return false;
+}
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int nb_for(int B) { return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : B <= 8 ? 8 : 16; }
+
+void* kernel_for(const mk_plan* pl, int kind) {
+    const int nb = nb_for(pl->hp.desc.batch);
+    if (pl->hp.desc.weight_dtype == MK_BF16) {
+        switch (nb) {
+            case 1: return mk_kernels_bf16_1(kind);
+            case 2: return mk_kernels_bf16_2(kind);
+            case 4: return mk_kernels_bf16_4(kind);
+            case 8: return mk_kernels_bf16_8(kind);
+            default: return mk_kernels_bf16_16(kind);
+        }
+    }
+    switch (nb) {
+        case 1: return mk_kernels_f32_1(kind);
+        case 2: return mk_kernels_f32_2(kind);
+        default: return mk_kernels_f32_4(kind);
+    }
+}
+void* persistent_kernel(const mk_plan* pl) { return kernel_for(pl, KK_PERSISTENT); }
+void* level_kernel(const mk_plan* pl) { return kernel_for(pl, KK_LEVEL_GEMV); }
+void* attn_kernel(const mk_plan* pl) { return kernel_for(pl, KK_LEVEL_ATTN); }
+
+bool upload_plan(mk_plan* pl) {
+    const HostPlan& hp = pl->hp;
+    const mk_model_desc& d = hp.desc;
+    const int L = d.n_layers, B = d.batch, H = d.hidden, F = d.ffn, Hkv = d.n_kv_heads, D = d.head_dim;
+    const int G = d.n_heads / Hkv;
+    const int64_t QD = (int64_t)d.n_heads * D, KD = (int64_t)Hkv * D;
+    // activation layout per layer (floats, 64-float aligned blocks)
+    auto a64 = [](int64_t v) { return (v + 63) / 64 * 64; };
+    pl->off_qkv = 0;
+    pl->off_attn = pl->off_qkv + a64(B * (QD + 2 * KD));
+    pl->off_xmid = pl->off_attn + a64(B * QD);
+    pl->off_h = pl->off_xmid + a64((int64_t)B * H);
+    pl->off_xnext = pl->off_h + a64((int64_t)B * F);
+    pl->act_stride = pl->off_xnext + a64((int64_t)B * H);
+
+    struct Region { size_t off, bytes; };
+    size_t at = 0;
+    auto take = [&](size_t bytes) {
+        Region r{align_up(at, 256), bytes};
+        at = r.off + bytes;
+        return r;
+    };
+    Region r_tasks = take(sizeof(TaskRec) * std::max<size_t>(1, hp.tasks.size()));
+    Region r_qoff = take(sizeof(int32_t) * hp.queue_off.size());
+    Region r_queue = take(sizeof(int32_t) * std::max<size_t>(1, hp.queue.size()));
+    Region r_lvl = take(sizeof(int32_t) * std::max<size_t>(1, hp.level_tasks.size()));
+    Region r_evrec = take(sizeof(EventRec) * hp.events.size());
+    // zero-initialised control area: events, arrivals, rings, ctrl
+    Region r_ev = take(sizeof(uint32_t) * hp.events.size());
+    Region r_arr = take(sizeof(uint32_t) * (size_t)B * Hkv);
+    Region r_jit = take(sizeof(RingSlot) * (size_t)hp.jit_ring_cap);
+    Region r_mb = take(sizeof(RingSlot) * (size_t)hp.mb_cap);
+    Region r_ctrl = take(sizeof(Ctrl));
+    Region r_rope = take(sizeof(float2) * (size_t)hp.cap * (D / 2));
+    Region r_part = take(sizeof(float) * (size_t)B * Hkv * hp.max_splits * (G * D + 2 * G));
+    Region r_act = take(sizeof(float) * (size_t)L * pl->act_stride);
+    Region r_x0 = take(sizeof(float) * (size_t)B * H);
+    Region r_xf = take(sizeof(float) * (size_t)B * H);
+    Region r_lw = take(sizeof(LayerPtrs) * L);
+    pl->dbytes = align_up(at, 256);
+    if (!hip_ok(hipSetDevice(pl->device), "hipSetDevice")) return false;
+    if (!hip_ok(hipMalloc((void**)&pl->dmem, pl->dbytes), "hipMalloc(plan)")) return false;
+    if (!hip_ok(hipMemset(pl->dmem, 0, pl->dbytes), "hipMemset(plan)")) return false;
+    char* m = pl->dmem;
+    pl->d_tasks = (TaskRec*)(m + r_tasks.off);
+    pl->d_qoff = (int32_t*)(m + r_qoff.off);
+    pl->d_queue = (int32_t*)(m + r_queue.off);
+    pl->d_level_tasks = (int32_t*)(m + r_lvl.off);
+    pl->d_evrec = (EventRec*)(m + r_evrec.off);
+    pl->d_ev = (uint32_t*)(m + r_ev.off);
+    pl->d_arrive = (uint32_t*)(m + r_arr.off);
+    pl->d_jit = (RingSlot*)(m + r_jit.off);
+    pl->d_mb = (RingSlot*)(m + r_mb.off);
+    pl->d_ctrl = (Ctrl*)(m + r_ctrl.off);
+    pl->d_rope = (float2*)(m + r_rope.off);
+    pl->d_partials = (float*)(m + r_part.off);
+    pl->d_act = (float*)(m + r_act.off);
+    pl->d_x0 = (float*)(m + r_x0.off);
+    pl->d_xfinal = (float*)(m + r_xf.off);
+    pl->d_lw = (LayerPtrs*)(m + r_lw.off);
+    pl->ctrl_off = r_ev.off;
+    pl->ctrl_bytes = r_ctrl.off + r_ctrl.bytes - r_ev.off;
+    auto up = [&](void* dst, const void* src, size_t n) {
+        return n == 0 || hip_ok(hipMemcpy(dst, src, n, hipMemcpyHostToDevice), "hipMemcpy(plan tables)");
+    };
+    if (!up(pl->d_tasks, hp.tasks.data(), sizeof(TaskRec) * hp.tasks.size())) return false;
+    if (!up(pl->d_qoff, hp.queue_off.data(), sizeof(int32_t) * hp.queue_off.size())) return false;
+    if (!up(pl->d_queue, hp.queue.data(), sizeof(int32_t) * hp.queue.size())) return false;
+    if (!up(pl->d_level_tasks, hp.level_tasks.data(), sizeof(int32_t) * hp.level_tasks.size())) return false;
+    if (!up(pl->d_evrec, hp.events.data(), sizeof(EventRec) * hp.events.size())) return false;
+    // RoPE table: theta_i = pos * base^(-2i/D), cos/sin in double, stored as float
+    std::vector<float2> rope((size_t)hp.cap * (D / 2));
+    for (int pos = 0; pos < hp.cap; ++pos)
+        for (int i = 0; i < D / 2; ++i) {
+            const double th = (double)pos * std::pow((double)d.rope_base, -2.0 * (double)i / (double)D);
+            rope[(size_t)pos * (D / 2) + i] = make_float2((float)std::cos(th), (float)std::sin(th));
+        }
+    if (!up(pl->d_rope, rope.data(), sizeof(float2) * rope.size())) return false;
+    if (!hip_ok(hipHostMalloc((void**)&pl->h_lw_pinned, sizeof(LayerPtrs) * L, hipHostMallocDefault), "hipHostMalloc"))
+        return false;
+    pl->lds_bytes = lds_bytes_for(G, hp.kv_chunk);
+    pl->lds_bytes_persistent = std::max(pl->lds_bytes, 82 * 1024);  // > half the CU's LDS: one workgroup per CU
+    if (pl->lds_bytes_persistent > 160 * 1024) {
+        set_err("LDS need exceeds 160 KB (reduce kv_chunk)");
+        return false;
+    }
+    void* kp = persistent_kernel(pl);
+    void* kl = level_kernel(pl);
+    void* ka = attn_kernel(pl);
+    if (!hip_ok(hipFuncSetAttribute(kp, hipFuncAttributeMaxDynamicSharedMemorySize, pl->lds_bytes_persistent),
+                "hipFuncSetAttribute(persistent)"))
+        return false;
+    if (!hip_ok(hipFuncSetAttribute(kl, hipFuncAttributeMaxDynamicSharedMemorySize, pl->lds_bytes), "hipFuncSetAttribute"))
+        return false;
+    if (!hip_ok(hipFuncSetAttribute(ka, hipFuncAttributeMaxDynamicSharedMemorySize, pl->lds_bytes), "hipFuncSetAttribute"))
+        return false;
+    // every persistent workgroup must be co-resident
+    int per_cu = 0;
+    if (!hip_ok(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kp, kThreads, pl->lds_bytes_persistent),
+                "hipOccupancyMaxActiveBlocksPerMultiprocessor"))
+        return false;
+    if (per_cu < 1 || (int64_t)per_cu * pl->cus < hp.workers + hp.sched_wgs) {
+        set_err("persistent grid cannot be co-resident on this device");
+        return false;
+    }
+    return true;
+}
+
+KParams make_params(const mk_plan* pl, const mk_weights* w, const mk_kv_cache* kv, const int32_t* tokens,
+                    const int32_t* seq_lens, const float* x_in, float* out) {
+    const HostPlan& hp = pl->hp;
+    const mk_model_desc& d = hp.desc;
+    KParams p{};
+    p.tasks = pl->d_tasks;
+    p.qoff = pl->d_qoff;
+    p.queue = pl->d_queue;
+    p.evrec = pl->d_evrec;
+    p.ev = pl->d_ev;
+    p.arrive = pl->d_arrive;
+    p.jit = pl->d_jit;
+    p.mb = pl->d_mb;
+    p.ctrl = pl->d_ctrl;
+    p.rope = pl->d_rope;
+    p.partials = pl->d_partials;
+    p.act = pl->d_act;
+    p.act_stride = pl->act_stride;
+    p.off_qkv = pl->off_qkv;
+    p.off_attn = pl->off_attn;
+    p.off_xmid = pl->off_xmid;
+    p.off_h = pl->off_h;
+    p.off_xnext = pl->off_xnext;
+    if (d.hidden_io) {
+        p.x0 = x_in;
+        p.x0_w = nullptr;
+        p.x_final = out;
+        p.logits = nullptr;
+    } else {
+        p.x0 = pl->d_x0;
+        p.x0_w = pl->d_x0;
+        p.x_final = pl->d_xfinal;
+        p.logits = out;
+    }
+    p.lw = pl->d_lw;
+    p.embed = w->embed;
+    p.final_norm = w->final_norm;
+    p.lm_head = w->lm_head;
+    p.kv_k = kv->k;
+    p.kv_v = kv->v;
+    p.kv_layer_stride = kv->layer_stride;
+    p.block_table = kv->block_table;
+    p.tokens = tokens;
+    p.seq_lens = seq_lens;
+    p.B = d.batch;
+    p.H = d.hidden;
+    p.Hq = d.n_heads;
+    p.Hkv = d.n_kv_heads;
+    p.D = d.head_dim;
+    p.F = d.ffn;
+    p.V = d.vocab;
+    p.L = d.n_layers;
+    p.QD = d.n_heads * d.head_dim;
+    p.KD = d.n_kv_heads * d.head_dim;
+    p.cap = hp.cap;
+    p.chunk = hp.kv_chunk;
+    p.max_splits = hp.max_splits;
+    p.qk_norm = d.qk_norm;
+    p.paged = d.kv_layout == MK_KV_PAGED;
+    p.kv_block = d.kv_layout == MK_KV_PAGED ? d.kv_block : 1;
+    p.max_blocks = d.max_blocks_per_seq;
+    p.eps = d.rms_eps;
+    p.scale = (float)(1.0 / std::sqrt((double)d.head_dim));
+    p.epoch = pl->epoch;
+    p.n_workers = hp.workers;
+    p.jit_on = hp.jit;
+    p.persistent = d.opts.mode == MK_PERSISTENT ? 1 : 0;
+    p.jit_mask = hp.jit_ring_cap - 1;
+    p.mb_mask = hp.mb_cap - 1;
+    const int wd = d.opts.watchdog_ms > 0 ? d.opts.watchdog_ms : 2000;
+    p.watchdog_ticks = (uint64_t)wd * 100000ull;
+    return p;
+}
+
+int check_step_args(mk_plan* pl, const mk_weights* w, const mk_kv_cache* kv, const int32_t* seq_lens, const void* in,
+                    const void* out) {
+    if (!pl) return set_err("null plan"), MK_ERR_ARG;
+    if (pl->host_only) return set_err("host-only plan cannot run steps"), MK_ERR_STATE;
+    const mk_model_desc& d = pl->hp.desc;
+    if (!w || !kv || !seq_lens || !in || !out) return set_err("null argument"), MK_ERR_ARG;
+    if (w->n_layers != d.n_layers || !w->layers) return set_err("weights.n_layers does not match the plan"), MK_ERR_ARG;
+    if (!kv->k || !kv->v) return set_err("null KV cache pointer"), MK_ERR_ARG;
+    if (d.kv_layout == MK_KV_PAGED && !kv->block_table) return set_err("paged plan needs a block table"), MK_ERR_ARG;
+    if (!d.hidden_io && (!w->embed || !w->lm_head || !w->final_norm))
+        return set_err("embed, lm_head and final_norm are required"), MK_ERR_ARG;
+    for (int l = 0; l < d.n_layers; ++l) {
+        const mk_layer_weights& lw = w->layers[l];
+        if (!lw.attn_norm || !lw.wq || !lw.wk || !lw.wv || !lw.wo || !lw.mlp_norm || !lw.w_gate || !lw.w_up || !lw.w_down)
+            return set_err("null weight pointer in layer " + std::to_string(l)), MK_ERR_ARG;
+        if (d.qk_norm && (!lw.q_norm || !lw.k_norm)) return set_err("qk_norm needs q_norm and k_norm"), MK_ERR_ARG;
+    }
+    return MK_OK;
+}
+
+// pointer table re-upload only when a pointer changed (a captured or cached
+// launch must never run with stale pointers)
+int sync_pointer_table(mk_plan* pl, const mk_weights* w, hipStream_t st) {
+    const int L = pl->hp.desc.n_layers;
+    bool same = (int)pl->cached_lw.size() == L &&
+                std::memcmp(pl->cached_lw.data(), w->layers, sizeof(LayerPtrs) * L) == 0;
+    if (same) return MK_OK;
+    if (!hip_ok(hipStreamSynchronize(st), "hipStreamSynchronize")) return MK_ERR_HIP;
+    std::memcpy(pl->h_lw_pinned, w->layers, sizeof(LayerPtrs) * L);
+    if (!hip_ok(hipMemcpyAsync(pl->d_lw, pl->h_lw_pinned, sizeof(LayerPtrs) * L, hipMemcpyHostToDevice, st),
+                "hipMemcpyAsync(pointer table)"))
+        return MK_ERR_HIP;
+    pl->cached_lw.assign((const LayerPtrs*)w->layers, (const LayerPtrs*)w->layers + L);
+    return MK_OK;
+}
+
+int launch_step(mk_plan* pl, const mk_weights* w, const mk_kv_cache* kv, const int32_t* tokens, const int32_t* seq_lens,
+                const float* x_in, float* out, hipStream_t st) {
+    if (!hip_ok(hipSetDevice(pl->device), "hipSetDevice")) return MK_ERR_HIP;
+    int rc = sync_pointer_table(pl, w, st);
+    if (rc) return rc;
+    KParams p = make_params(pl, w, kv, tokens, seq_lens, x_in, out);
+    const HostPlan& hp = pl->hp;
+    if (hp.desc.opts.mode == MK_PERSISTENT) {
+        void* args[] = {&p};
+        if (!hip_ok(hipLaunchCooperativeKernel(persistent_kernel(pl), dim3(hp.workers + hp.sched_wgs), dim3(kThreads), args,
+                                               pl->lds_bytes_persistent, st),
+                    "hipLaunchCooperativeKernel"))
+            return MK_ERR_HIP;
+        pl->epoch++;
+        return MK_OK;
+    }
+    for (int lv = 0; lv < hp.n_levels; ++lv) {
+        const int op = hp.level_op[lv];
+        if (op == OP_ATTN) {
+            int layer = hp.level_layer[lv];
+            void* args[] = {&p, &layer};
+            const int grid = hp.desc.batch * hp.desc.n_kv_heads * hp.max_splits;
+            if (!hip_ok(hipLaunchKernel(attn_kernel(pl), dim3(grid), dim3(kThreads), args, pl->lds_bytes, st),
+                        "hipLaunchKernel(attention level)"))
+                return MK_ERR_HIP;
+        } else {
+            const int n = hp.level_off[lv + 1] - hp.level_off[lv];
+            if (n == 0) continue;
+            const int32_t* ids = pl->d_level_tasks + hp.level_off[lv];
+            void* args[] = {&p, (void*)&ids};
+            if (!hip_ok(hipLaunchKernel(level_kernel(pl), dim3(n), dim3(kThreads), args, pl->lds_bytes, st),
+                        "hipLaunchKernel(level)"))
+                return MK_ERR_HIP;
+        }
+    }
+    return MK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mk_last_error(void) { return g_err.c_str(); }
+
+mk_plan* mk_build_graph(const mk_model_desc* desc) {
+    if (!desc) {
+        set_err("null desc");
+        return nullptr;
+    }
+    mk_plan* pl = new mk_plan();
+    pl->host_only = desc->opts.host_only != 0;
+    int cus = desc->opts.device_cus > 0 ? desc->opts.device_cus : 256;
+    if (!pl->host_only) {
+        hipDeviceProp_t prop;
+        if (!hip_ok(hipGetDevice(&pl->device), "hipGetDevice") ||
+            !hip_ok(hipGetDeviceProperties(&prop, pl->device), "hipGetDeviceProperties")) {
+            delete pl;
+            return nullptr;
+        }
+        cus = prop.multiProcessorCount;
+        if (!prop.cooperativeLaunch && desc->opts.mode == MK_PERSISTENT) {
+            set_err("device does not support cooperative launch");
+            delete pl;
+            return nullptr;
+        }
+    }
+    pl->cus = cus;
+    std::string err;
+    if (!build_host_plan(*desc, cus, pl->hp, err) || !verify_plan(pl->hp, err)) {
+        set_err(err);
+        delete pl;
+        return nullptr;
+    }
+    if (pl->host_only) return pl;
+    if (!upload_plan(pl)) {
+        mk_destroy_plan(pl);
+        return nullptr;
+    }
+    return pl;
+}
+
+void mk_destroy_plan(mk_plan* pl) {
+    if (!pl) return;
+    if (!pl->host_only) {
+        (void)hipSetDevice(pl->device);
+        (void)hipDeviceSynchronize();
+        if (pl->dmem) (void)hipFree(pl->dmem);
+        if (pl->h_lw_pinned) (void)hipHostFree(pl->h_lw_pinned);
+    }
+    delete pl;
+}
+
+int mk_plan_query(const mk_plan* pl, mk_plan_info* info) {
+    if (!pl || !info) return set_err("null argument"), MK_ERR_ARG;
+    const HostPlan& hp = pl->hp;
+    std::memset(info, 0, sizeof(*info));
+    info->workers = hp.workers;
+    info->sched_waves = hp.sched_wgs * kWaves;
+    info->n_aot_tasks = (int32_t)hp.tasks.size();
+    info->n_events = (int32_t)hp.events.size();
+    info->n_levels = hp.n_levels;
+    info->max_jit_tasks = hp.max_jit_tasks;
+    info->kv_chunk = hp.kv_chunk;
+    info->max_splits = hp.max_splits;
+    for (int i = 0; i < 8 && i < kNumOps; ++i) info->tasks_per_op[i] = hp.tasks_per_op[i];
+    info->weight_bytes_per_step = hp.weight_bytes;
+    info->kv_bytes_per_token = hp.kv_bytes_per_token;
+    info->device_bytes = (int64_t)pl->dbytes;
+    info->jit = hp.jit;
+    info->mode = hp.desc.opts.mode;
+    info->host_only = pl->host_only ? 1 : 0;
+    return MK_OK;
+}
+
+int mk_decode_step(mk_plan* pl, const mk_weights* w, const mk_kv_cache* kv, const int32_t* tokens,
+                   const int32_t* seq_lens, float* logits, void* stream) {
+    int rc = check_step_args(pl, w, kv, seq_lens, tokens, logits);
+    if (rc) return rc;
+    if (pl->hp.desc.hidden_io) return set_err("hidden_io plan: use mk_decode_step_hidden"), MK_ERR_STATE;
+    return launch_step(pl, w, kv, tokens, seq_lens, nullptr, logits, (hipStream_t)stream);
+}
+
+int mk_decode_step_hidden(mk_plan* pl, const mk_weights* w, const mk_kv_cache* kv, const float* x_in,
+                          const int32_t* seq_lens, float* x_out, void* stream) {
+    int rc = check_step_args(pl, w, kv, seq_lens, x_in, x_out);
+    if (rc) return rc;
+    if (!pl->hp.desc.hidden_io) return set_err("token plan: use mk_decode_step"), MK_ERR_STATE;
+    if ((const void*)x_in == (const void*)x_out) return set_err("x_in and x_out must not alias"), MK_ERR_ARG;
+    return launch_step(pl, w, kv, nullptr, seq_lens, x_in, x_out, (hipStream_t)stream);
+}
+
+int mk_get_device_error(mk_plan* pl, void* stream) {
+    if (!pl) return set_err("null plan"), MK_ERR_ARG;
+    if (pl->host_only) return set_err("host-only plan"), MK_ERR_STATE;
+    hipStream_t st = (hipStream_t)stream;
+    if (!hip_ok(hipSetDevice(pl->device), "hipSetDevice") || !hip_ok(hipStreamSynchronize(st), "hipStreamSynchronize"))
+        return MK_ERR_HIP;
+    Ctrl c;
+    if (!hip_ok(hipMemcpy(&c, pl->d_ctrl, sizeof(Ctrl), hipMemcpyDeviceToHost), "hipMemcpy(error word)")) return MK_ERR_HIP;
+    const int bits = (int)c.error;
+    if (bits) {
+        if (bits & MK_ERR_TIMEOUT) {
+            // counters are inconsistent after an aborted step: restart from epoch 0
+            if (!hip_ok(hipMemset(pl->dmem + pl->ctrl_off, 0, pl->ctrl_bytes), "hipMemset(reset)")) return MK_ERR_HIP;
+            pl->epoch = 0;
+        } else {
+            uint32_t z = 0;
+            if (!hip_ok(hipMemcpy(&pl->d_ctrl->error, &z, sizeof(z), hipMemcpyHostToDevice), "hipMemcpy(clear)"))
+                return MK_ERR_HIP;
+        }
+    }
+    return bits;
+}
+
+int mk_argmax(const mk_plan* pl, const float* logits, int32_t* out_tokens, void* stream) {
+    if (!pl || !logits || !out_tokens) return set_err("null argument"), MK_ERR_ARG;
+    if (pl->host_only) return set_err("host-only plan"), MK_ERR_STATE;
+    if (pl->hp.desc.hidden_io) return set_err("hidden_io plan has no logits"), MK_ERR_STATE;
+    hipLaunchKernelGGL(k_argmax, dim3(pl->hp.desc.batch), dim3(kThreads), 0, (hipStream_t)stream, logits,
+                       pl->hp.desc.vocab, out_tokens);
+    if (!hip_ok(hipGetLastError(), "k_argmax launch")) return MK_ERR_HIP;
+    return MK_OK;
+}
+
+int mk_plan_verify(const mk_plan* pl) {
+    if (!pl) return set_err("null plan"), MK_ERR_ARG;
+    std::string err;
+    if (!verify_plan(pl->hp, err)) return set_err(err), MK_ERR_STATE;
+    return MK_OK;
+}
+
+int mk_plan_dry_run(const mk_plan* pl, int n_threads, uint64_t seed, int drop_task, int timeout_ms,
+                    const int32_t* seq_lens_host) {
+    if (!pl) return set_err("null plan"), MK_ERR_ARG;
+    std::string err;
+    if (!dry_run(pl->hp, n_threads, seed, drop_task, timeout_ms, seq_lens_host, err)) return set_err(err), MK_ERR_STATE;
+    return MK_OK;
+}
+
+}  // extern "C"
