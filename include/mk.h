@@ -64,7 +64,7 @@ enum mk_device_error {
  *  sched_wgs     scheduler workgroups of 4 waves each (default 4 -> 16 waves).
  *  jit           attention launch: 0 = default (JIT), 1 = JIT through the
  *                scheduler waves, 2 = AOT with the maximum split count queued.
- *  kv_chunk      KV positions per attention split task (default 256; a
+ *  kv_chunk      KV positions per attention split task (default 128; a
  *                multiple of 16).
  *  watchdog_ms   bound on every spin wait of the persistent kernel
  *                (default 2000).
@@ -74,6 +74,10 @@ enum mk_device_error {
  *  device_cus    CU count to plan for when host_only (default 256).
  *  debug_extra_required  for fault tests: adds this many to the required
  *                count of event `debug_event` so its waiters time out.
+ *  trace         records per worker kept by the in-kernel task trace (0 =
+ *                off). Each record holds the task, the worker, and the
+ *                real-time-clock ticks (100 MHz) at wait start, ready and
+ *                done; read them with mk_plan_trace.
  */
 typedef struct mk_exec_opts {
     int32_t mode;
@@ -86,7 +90,8 @@ typedef struct mk_exec_opts {
     int32_t device_cus;
     int32_t debug_event;
     int32_t debug_extra_required;
-    int32_t reserved[6];
+    int32_t trace;
+    int32_t reserved[5];
 } mk_exec_opts;
 
 /*
@@ -233,6 +238,32 @@ int mk_plan_verify(const mk_plan* plan);
  */
 int mk_plan_dry_run(const mk_plan* plan, int n_threads, uint64_t seed, int drop_task, int timeout_ms,
                     const int32_t* seq_lens_host);
+
+/*
+ * One task-trace record (opts.trace > 0). kind: 0 AOT task (id = task
+ * index in the plan), 1 JIT attention task (id = layer << 24 | (b*Hkv+g) << 12
+ * | split, fields truncated). t_wait: the worker started waiting for the
+ * task's event; t_ready: the event was satisfied (JIT: task popped);
+ * t_done: outputs written and the completion signalled; t_a, t_b: phase
+ * marks inside the task body. Ticks of the 100 MHz device real-time clock.
+ */
+typedef struct mk_trace_rec {
+    int32_t kind;
+    int32_t id;
+    int32_t worker;
+    int32_t op;
+    uint64_t t_wait, t_ready, t_done;
+    uint64_t t_a, t_b; /* task-defined phase marks (GEMV: operands ready, rows done;
+                          attention: prologue done, partial written); 0 if unset */
+} mk_trace_rec;
+
+/*
+ * Copy the trace of the last persistent step to host memory `out` (room
+ * for `max_records`). Synchronises `stream`. Returns the number of records
+ * written (records of workers that overflowed their share are dropped), or
+ * a negative mk_status (MK_ERR_STATE if the plan was built without trace).
+ */
+int mk_plan_trace(const mk_plan* plan, mk_trace_rec* out, int64_t max_records, void* stream);
 
 #ifdef __cplusplus
 }

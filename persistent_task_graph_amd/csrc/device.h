@@ -29,7 +29,10 @@ struct KParams {
     const EventRec* evrec;
     uint32_t* ev;
     uint32_t* arrive;  // [B * Hkv] last-arrival counters (self-resetting)
-    RingSlot* jit;
+    RingSlot* inbox;         // [workers][inbox_mask + 1] JIT tasks dealt to each worker
+    int64_t* inbox_tail;     // [workers] producer positions
+    int64_t* inbox_head;     // [workers] consumer positions (kept across launches)
+    const int32_t* elig;     // workers that receive JIT tasks
     RingSlot* mb;
     Ctrl* ctrl;
     const float2* rope;  // [cap][D/2] (cos, sin)
@@ -44,6 +47,7 @@ struct KParams {
     float* logits;
     // weights
     const LayerPtrs* lw;
+    const void* zero;  // zero-filled buffer of at least the largest K (stays cached)
     const void* embed;
     const void* final_norm;
     const void* lm_head;
@@ -63,10 +67,16 @@ struct KParams {
     int n_workers;
     int jit_on;
     int persistent;  // 1: events are signalled (persistent mode)
-    int jit_mask;
+    int inbox_mask;
+    int n_elig;
     int mb_mask;
     uint64_t watchdog_ticks;  // 100 MHz ticks
+    // optional task trace: per worker `trace_cap` records, count in trace_n
+    mk_trace_rec* trace;
+    int32_t* trace_n;
+    int trace_cap;
 };
+
 
 // ---------------------------------------------------------------- numerics
 
@@ -149,9 +159,56 @@ __device__ __forceinline__ int64_t ld_acquire64(const int64_t* p) {
 __device__ __forceinline__ int64_t ld_relaxed64(const int64_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
-__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
+// Coherence between workgroups without L2-wide fences. On this part an
+// agent-scope release fence writes back the whole L2 and an acquire
+// invalidates it (several microseconds each), so data that one workgroup
+// hands to another within a step moves with agent-coherent (sc1) accesses
+// instead: the producer stores with st_co, waits for its stores to
+// complete (wait_stores), then bumps the event counter with a relaxed
+// atomic; the consumer polls the counter, then reads with ld_co / sc1
+// buffer loads, which do not hit stale cache lines. Weights and the KV
+// cache positions read within a step were written before the launch and
+// use ordinary cached loads.
+constexpr int kSC1 = 16;  // cache-policy bit of agent-coherent buffer accesses
+__device__ __forceinline__ float ld_co(const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ int ld_co(const int* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ void st_co(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ void st_co(int* p, int v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
 __device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
+
+// phase marks for the task trace: thread 0 keeps them in shared memory
+__device__ __forceinline__ void trace_mark(const KParams& p, uint64_t* marks, int i) {
+    if (p.trace && threadIdx.x == 0) marks[i] = now_ticks();
+}
+
+// ---------------------------------------------------------------- buffer loads
+// Raw buffer resources (base, size) in SGPRs with 32-bit lane offsets: a
+// load whose offset is past `size` returns zero and touches no memory, which
+// pads tails and unused rows for free.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr uint32_t kOOB = 0x80000000u;  // an offset past every resource
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+// agent-coherent variant for data written earlier in the same step
+__device__ __forceinline__ uint4 buf_load16_co(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kSC1);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// One weight row as seen by a GEMV: resource of its matrix tile and the
+// byte offset of the row inside it.
+struct RowRef {
+    __amdgpu_buffer_rsrc_t r;
+    uint32_t soff;
+};
 
 __device__ __forceinline__ void raise_error(Ctrl* c, uint32_t bits) {
     __hip_atomic_fetch_or(&c->error, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -8,18 +8,16 @@
 namespace mk {
 namespace {  // kernels get internal linkage: each instantiation unit registers its own
 
-// ---------------------------------------------------------------- JIT ring
+// ---------------------------------------------------------------- JIT inbox
 
-// Pop one ready attention task (FIFO). Only thread 0 of a worker calls it.
-__device__ __forceinline__ bool jit_try_pop(const KParams& p, int& layer, int& bg, int& split) {
-    const int64_t h = ld_relaxed64(&p.ctrl->jit_head);
-    RingSlot* sl = &p.jit[h & p.jit_mask];
-    if (ld_acquire64(&sl->tag) != h + 1) return false;
-    const int p0 = sl->p0, p1 = sl->p1;
-    int64_t expect = h;
-    if (!__hip_atomic_compare_exchange_strong(&p.ctrl->jit_head, &expect, h + 1, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT))
-        return false;
+// Pop the next attention task dealt to this worker (single consumer: only
+// thread 0 of the owning workgroup reads its inbox; `head` lives in a
+// register and is written back when the workgroup exits).
+__device__ __forceinline__ bool inbox_try_pop(const KParams& p, int64_t& head, int& layer, int& bg, int& split) {
+    const RingSlot* sl = &p.inbox[(int64_t)blockIdx.x * (p.inbox_mask + 1) + (head & p.inbox_mask)];
+    if (ld_relaxed64(&sl->tag) != head + 1) return false;
+    const int p0 = ld_co(&sl->p0), p1 = ld_co(&sl->p1);
+    head++;
     layer = p0 >> 16;
     bg = p0 & 0xFFFF;
     split = p1;
@@ -42,8 +40,8 @@ __device__ __forceinline__ void scheduler_wave(const KParams& p) {
             else if (aborted(p.ctrl)) status = 3;
             else {
                 RingSlot* sl = &p.mb[h & p.mb_mask];
-                if (ld_acquire64(&sl->tag) == h + 1) {
-                    const int l = sl->p0;
+                if (ld_relaxed64(&sl->tag) == h + 1) {
+                    const int l = ld_co(&sl->p0);
                     int64_t e = h;
                     if (__hip_atomic_compare_exchange_strong(&p.ctrl->mb_head, &e, h + 1, __ATOMIC_RELAXED,
                                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
@@ -72,38 +70,72 @@ __device__ __forceinline__ void scheduler_wave(const KParams& p) {
             const int ns = ovf ? 1 : (pos + 1 + p.chunk - 1) / p.chunk;
             total += ns * p.Hkv;
         }
-        int64_t base = 0;
+        // deal the tasks round-robin to the eligible workers' inboxes,
+        // continuing where the previous expansion stopped
+        int64_t start = 0;
         if (lane == 0)
-            base = __hip_atomic_fetch_add(&p.ctrl->jit_tail, (int64_t)total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        base = __shfl(base, 0, 64);
-        int off = 0;
-        for (int b = 0; b < p.B; ++b) {
-            const int pos = p.seq_lens[b];
-            const bool ovf = pos < 0 || pos + 1 > p.cap;
-            const int ns = ovf ? 1 : (pos + 1 + p.chunk - 1) / p.chunk;
-            const int nb = ns * p.Hkv;
-            for (int i = lane; i < nb; i += 64) {
-                const int g = i / ns, sp = i % ns;
-                const int64_t q = base + off + i;
-                RingSlot* sl = &p.jit[q & p.jit_mask];
-                sl->p0 = (layer << 16) | (b * p.Hkv + g);
-                sl->p1 = sp;
-                __hip_atomic_store(&sl->tag, q + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            start = __hip_atomic_fetch_add(&p.ctrl->rr, (int64_t)total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        start = __shfl(start, 0, 64);
+        for (int i = lane; i < total; i += 64) {
+            int b = 0, off = 0, ns = 1;
+            for (;; ++b) {
+                const int pos = p.seq_lens[b];
+                const bool ovf = pos < 0 || pos + 1 > p.cap;
+                ns = ovf ? 1 : (pos + 1 + p.chunk - 1) / p.chunk;
+                if (i < off + ns * p.Hkv || b == p.B - 1) break;
+                off += ns * p.Hkv;
             }
-            off += nb;
+            const int local = i - off, g = local / ns, sp = local % ns;
+            const int w = p.elig[(start + i) % p.n_elig];
+            const int64_t q = __hip_atomic_fetch_add(&p.inbox_tail[w], (int64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            RingSlot* sl = &p.inbox[(int64_t)w * (p.inbox_mask + 1) + (q & p.inbox_mask)];
+            st_co(&sl->p0, (layer << 16) | (b * p.Hkv + g));
+            st_co(&sl->p1, sp);
+            wait_stores();
+            __hip_atomic_store(&sl->tag, q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
 
 // ---------------------------------------------------------------- worker
 
+// task trace (thread 0 only)
+__device__ __forceinline__ void trace_put(const KParams& p, const Lds& s, int kind, int id, int op, uint64_t tw,
+                                          uint64_t tr) {
+    if (!p.trace || threadIdx.x != 0) return;
+    const int w = blockIdx.x;
+    const int i = p.trace_n[w];
+    if (i < p.trace_cap) {
+        mk_trace_rec r;
+        r.kind = kind;
+        r.id = id;
+        r.worker = w;
+        r.op = op;
+        r.t_wait = tw;
+        r.t_ready = tr;
+        r.t_done = now_ticks();
+        r.t_a = s.marks[0];
+        r.t_b = s.marks[1];
+        p.trace[(int64_t)w * p.trace_cap + i] = r;
+    }
+    p.trace_n[w] = i + 1;
+    s.marks[0] = s.marks[1] = 0;
+}
+
 template <typename WT, int NB>
 __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s) {
     const int w = blockIdx.x;
     const int qb = p.qoff[w], qe = p.qoff[w + 1];
     const uint32_t ep1 = p.epoch + 1u;
+    if (p.trace && threadIdx.x == 0) {
+        p.trace_n[w] = 0;
+        s.marks[0] = s.marks[1] = 0;
+    }
+    int64_t head = (threadIdx.x == 0 && p.jit_on) ? p.inbox_head[w] : 0;
     for (int qi = qb; qi < qe; ++qi) {
-        const TaskRec t = p.tasks[p.queue[qi]];
+        const int tid_task = p.queue[qi];
+        const TaskRec t = p.tasks[tid_task];
+        const uint64_t tw = p.trace ? now_ticks() : 0;
         if (t.wait_ev >= 0) {
             const uint32_t target = p.evrec[t.wait_ev].required * ep1;
             uint64_t t0 = now_ticks();
@@ -115,7 +147,7 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s) {
                     else if (aborted(p.ctrl)) cmd = 3;
                     else {
                         int jl, jbg, js;
-                        if (p.jit_on && jit_try_pop(p, jl, jbg, js)) {
+                        if (p.jit_on && inbox_try_pop(p, head, jl, jbg, js)) {
                             cmd = 1;
                             s.cmd[1] = jl;
                             s.cmd[2] = jbg;
@@ -132,24 +164,30 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s) {
                 const int jl = s.cmd[1], jbg = s.cmd[2], js = s.cmd[3];
                 __syncthreads();
                 if (cmd == 0) break;
-                if (cmd == 3) return;
+                if (cmd == 3) {
+                    if (threadIdx.x == 0 && p.jit_on) p.inbox_head[w] = head;
+                    return;
+                }
                 if (cmd == 1) {
-                    fence_acquire();
+                    const uint64_t tj = p.trace ? now_ticks() : 0;
                     attention_task<WT>(p, jl, jbg, js, s);
+                    trace_put(p, s, 1, (jl << 24) | ((jbg & 0xFFF) << 12) | (js & 0xFFF), OP_ATTN, tj, tj);
                     t0 = now_ticks();
                 } else {
                     __builtin_amdgcn_s_sleep(1);
                 }
             }
-            fence_acquire();
         }
+        const uint64_t tr = p.trace ? now_ticks() : 0;
         if (t.op == OP_ATTN) {
             attention_task<WT>(p, t.layer, t.a0, t.a1, s);
-            continue;
+        } else {
+            run_gemv_task<WT, NB>(p, t, s);
+            signal_event(p, t.sig_ev, s);
         }
-        run_gemv_task<WT, NB>(p, t, s);
-        signal_event(p, t.sig_ev, s);
+        trace_put(p, s, 0, tid_task, t.op, tw, tr);
     }
+    if (threadIdx.x == 0 && p.jit_on) p.inbox_head[w] = head;
 }
 
 extern __shared__ float mk_dyn_lds[];

@@ -63,10 +63,9 @@ struct Ctrl {
     uint32_t error;      // sticky mk_device_error bits
     uint32_t abort;      // set when any wait times out; all loops exit
     uint32_t pad0[14];
-    int64_t jit_tail;    // next JIT position to reserve (64 B apart from the head)
+    int64_t rr;          // round-robin position for dealing JIT tasks to worker inboxes
     int64_t pad1[7];
-    int64_t jit_head;    // next JIT position to pop
-    int64_t pad2[7];
+    int64_t pad2[8];
     int64_t mb_tail;     // mailbox reserve position
     int64_t pad3[7];
     int64_t mb_head;     // mailbox pop position
@@ -92,8 +91,9 @@ struct HostPlan {
     std::vector<int32_t> level_tasks;
     std::vector<uint8_t> level_op;   // op of each level
     std::vector<uint16_t> level_layer;
-    int jit_ring_cap = 0;  // power of two
-    int mb_cap = 0;        // power of two
+    int inbox_cap = 0;  // JIT inbox slots per worker (power of two)
+    int mb_cap = 0;     // power of two
+    std::vector<int32_t> jit_elig;  // workers that may receive JIT tasks
     int max_jit_tasks = 0;
     int tasks_per_op[kNumOps] = {0};
     int64_t weight_bytes = 0;

@@ -86,7 +86,7 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
         return fail(err, "workers + sched_wgs must be in [2, CU count] (one workgroup per CU)");
     if (o.jit < 0 || o.jit > 2) return fail(err, "opts.jit must be 0, 1 or 2");
     p.jit = (o.jit == 2) ? 0 : 1;
-    p.kv_chunk = o.kv_chunk > 0 ? o.kv_chunk : 256;
+    p.kv_chunk = o.kv_chunk > 0 ? o.kv_chunk : 128;
     if (p.kv_chunk % 16 || p.kv_chunk > 4096) return fail(err, "kv_chunk must be a multiple of 16, at most 4096");
     if (p.kv_chunk * (d.n_heads / d.n_kv_heads) > 16384) return fail(err, "kv_chunk * (n_heads / n_kv_heads) must be <= 16384");
     p.cap = d.max_seq_len;
@@ -184,7 +184,19 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
     const int64_t per_layer_jit = (int64_t)B * Hkv * p.max_splits;
     if (per_layer_jit > (1 << 26)) return fail(err, "too many attention tasks per layer");
     p.max_jit_tasks = (int)per_layer_jit;
-    p.jit_ring_cap = next_pow2(std::max<int>(64, (int)per_layer_jit));
+    // JIT tasks are dealt round-robin to workers that still have an AOT task
+    // after the last attention level: such a worker is bound to wait on an
+    // event that depends on the attention, and drains its inbox meanwhile
+    int last_attn = -1;
+    for (int lv = 0; lv < p.n_levels; ++lv)
+        if (p.level_op[lv] == OP_ATTN) last_attn = lv;
+    for (int w = 0; w < W; ++w) {
+        bool ok = false;
+        for (int i = p.queue_off[w]; i < p.queue_off[w + 1] && !ok; ++i) ok = p.tasks[p.queue[i]].level > last_attn;
+        if (ok) p.jit_elig.push_back(w);
+    }
+    if (p.jit && p.jit_elig.empty()) return fail(err, "no worker can receive JIT tasks");
+    p.inbox_cap = next_pow2((int)std::max<int64_t>(16, per_layer_jit / std::max<size_t>(1, p.jit_elig.size()) + 2));
     p.mb_cap = next_pow2(std::max(16, L));
 
     const int64_t es = d.weight_dtype == MK_BF16 ? 2 : 4;
@@ -286,9 +298,11 @@ struct DryState {
     std::vector<std::atomic<uint32_t>> ev;
     std::vector<std::atomic<uint32_t>> arrive;
     std::vector<std::atomic<uint64_t>> partial;  // [B*Hkv][max_splits]
-    std::vector<RingSlot> jit;
-    std::vector<std::atomic<int64_t>> jit_tag;
-    std::atomic<int64_t> jit_tail{0}, jit_head{0};
+    std::vector<RingSlot> jit;                     // [workers][inbox_cap]
+    std::vector<std::atomic<int64_t>> jit_tag;     // [workers][inbox_cap]
+    std::vector<std::atomic<int64_t>> jit_tail;    // per worker
+    std::vector<int64_t> jit_head;                 // per worker (single consumer)
+    std::atomic<int64_t> rr{0};
     std::vector<std::atomic<int64_t>> mb_tag;
     std::vector<int32_t> mb_payload;
     std::atomic<int64_t> mb_tail{0}, mb_head{0};
@@ -364,9 +378,12 @@ bool dry_run(const HostPlan& p, int n_threads, uint64_t seed, int drop_task, int
     s.arrive = std::vector<std::atomic<uint32_t>>(d.batch * d.n_kv_heads);
     for (auto& a : s.arrive) a.store(0);
     s.partial = std::vector<std::atomic<uint64_t>>((size_t)d.batch * d.n_kv_heads * p.max_splits);
-    s.jit.resize(p.jit_ring_cap);
-    s.jit_tag = std::vector<std::atomic<int64_t>>(p.jit_ring_cap);
+    s.jit.resize((size_t)p.workers * p.inbox_cap);
+    s.jit_tag = std::vector<std::atomic<int64_t>>((size_t)p.workers * p.inbox_cap);
     for (auto& t : s.jit_tag) t.store(0);
+    s.jit_tail = std::vector<std::atomic<int64_t>>(p.workers);
+    for (auto& t : s.jit_tail) t.store(0);
+    s.jit_head.assign(p.workers, 0);
     s.mb_tag = std::vector<std::atomic<int64_t>>(p.mb_cap);
     for (auto& t : s.mb_tag) t.store(0);
     s.mb_payload.assign(p.mb_cap, 0);
@@ -397,15 +414,14 @@ bool dry_run(const HostPlan& p, int n_threads, uint64_t seed, int drop_task, int
             if (p.level_op[lv] == OP_ATTN && p.level_layer[lv] == layer) return lv;
         return -1;
     };
-    auto try_pop_jit = [&](int& layer, int& bg, int& split) {
-        int64_t h = s.jit_head.load(std::memory_order_acquire);
-        RingSlot& sl = s.jit[h % p.jit_ring_cap];
-        if (s.jit_tag[h % p.jit_ring_cap].load(std::memory_order_acquire) != h + 1) return false;
-        int p0 = sl.p0, p1 = sl.p1;
-        if (!s.jit_head.compare_exchange_strong(h, h + 1)) return false;
-        layer = p0 >> 16;
-        bg = p0 & 0xFFFF;
-        split = p1;
+    auto try_pop_jit = [&](int w, int& layer, int& bg, int& split) {
+        const int64_t h = s.jit_head[w];
+        const size_t slot = (size_t)w * p.inbox_cap + (size_t)(h % p.inbox_cap);
+        if (s.jit_tag[slot].load(std::memory_order_acquire) != h + 1) return false;
+        layer = s.jit[slot].p0 >> 16;
+        bg = s.jit[slot].p0 & 0xFFFF;
+        split = s.jit[slot].p1;
+        s.jit_head[w] = h + 1;
         return true;
     };
     auto run_jit = [&](int layer, int bg, int split, std::mt19937_64& rng) {
@@ -430,15 +446,21 @@ bool dry_run(const HostPlan& p, int n_threads, uint64_t seed, int drop_task, int
                 int layer = s.mb_payload[h % p.mb_cap];
                 if (!s.mb_head.compare_exchange_strong(h, h + 1)) continue;
                 std::this_thread::sleep_for(std::chrono::microseconds(rng() % 30));
+                int64_t total = 0;
+                for (int b = 0; b < d.batch; ++b) total += (int64_t)d.n_kv_heads * n_splits_for(s.seq[b] + 1, p.kv_chunk);
+                const int64_t start = s.rr.fetch_add(total);
+                int64_t i = 0;
+                const int64_t ne = (int64_t)p.jit_elig.size();
                 for (int b = 0; b < d.batch; ++b) {
                     int ns = n_splits_for(s.seq[b] + 1, p.kv_chunk);
                     for (int g = 0; g < d.n_kv_heads; ++g)
-                        for (int sp = 0; sp < ns; ++sp) {
-                            int64_t pos = s.jit_tail.fetch_add(1);
-                            RingSlot& sl = s.jit[pos % p.jit_ring_cap];
-                            sl.p0 = (layer << 16) | (b * d.n_kv_heads + g);
-                            sl.p1 = sp;
-                            s.jit_tag[pos % p.jit_ring_cap].store(pos + 1, std::memory_order_release);
+                        for (int sp = 0; sp < ns; ++sp, ++i) {
+                            const int w = p.jit_elig[(size_t)((start + i) % ne)];
+                            int64_t pos = s.jit_tail[w].fetch_add(1);
+                            const size_t slot = (size_t)w * p.inbox_cap + (size_t)(pos % p.inbox_cap);
+                            s.jit[slot].p0 = (layer << 16) | (b * d.n_kv_heads + g);
+                            s.jit[slot].p1 = sp;
+                            s.jit_tag[slot].store(pos + 1, std::memory_order_release);
                         }
                 }
             }
@@ -483,18 +505,21 @@ bool dry_run(const HostPlan& p, int n_threads, uint64_t seed, int drop_task, int
                     signal(t.sig_ev);
                 }
                 if (!progressed) {
-                    int layer, bg, sp;
-                    if (p.jit && try_pop_jit(layer, bg, sp)) run_jit(layer, bg, sp, rng);
-                    else std::this_thread::yield();
+                    bool ran = false;
+                    for (size_t k = 0; k < mine.size() && p.jit; ++k) {
+                        int layer, bg, sp;
+                        if (try_pop_jit(mine[k], layer, bg, sp)) {
+                            run_jit(layer, bg, sp, rng);
+                            ran = true;
+                        }
+                    }
+                    if (!ran) std::this_thread::yield();
                 }
             }
         });
     }
     for (auto& t : th) t.join();
-    if (p.jit) {
-        s.abort.store(s.abort.load() | 0);  // scheduler exits on its own once every message is popped
-        sched.join();
-    }
+    if (p.jit) sched.join();  // the scheduler exits once every message is popped (or on abort)
     if (!s.abort.load())
         for (int l = 0; l < d.n_layers; ++l)
             if (s.ev[ev_attn(l)].load() != p.events[ev_attn(l)].required)

@@ -28,28 +28,37 @@
 
 namespace mk {
 
-// argmax over each logits row, lowest index on ties
-__global__ __launch_bounds__(kThreads) void k_argmax(const float* logits, int V, int32_t* out) {
+// argmax over each logits row, lowest index on ties. grid (kArgBlocks, B):
+// every block reduces a contiguous slice; the last block of a row to finish
+// (arrival counter, self-resetting) reduces the slice winners in order.
+constexpr int kArgBlocks = 64;
+
+__device__ __forceinline__ void argmax_merge(float& best, int& bi, float ov, int oi) {
+    if (ov > best || (ov == best && oi < bi)) {
+        best = ov;
+        bi = oi;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_argmax(const float* logits, int V, int32_t* out, float* pv, int32_t* pi,
+                                                     uint32_t* cnt) {
     __shared__ float sv[kWaves];
     __shared__ int si[kWaves];
-    const float* row = logits + (int64_t)blockIdx.x * V;
+    __shared__ int last;
+    const int b = blockIdx.y;
+    const float* row = logits + (int64_t)b * V;
+    const int per = (V + kArgBlocks - 1) / kArgBlocks;
+    const int i0 = blockIdx.x * per, i1 = min(V, i0 + per);
     float best = -INFINITY;
     int bi = V;
-    for (int i = threadIdx.x; i < V; i += kThreads) {
+    for (int i = i0 + (int)threadIdx.x; i < i1; i += kThreads) {
         const float v = row[i];
-        if (v > best) {  // strict: the first (lowest) index wins ties; NaN never wins
+        if (v > best) {  // strict: lowest index wins ties; NaN never wins
             best = v;
             bi = i;
         }
     }
-    for (int o = 32; o >= 1; o >>= 1) {
-        const float ov = __shfl_xor(best, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
-        if (ov > best || (ov == best && oi < bi)) {
-            best = ov;
-            bi = oi;
-        }
-    }
+    for (int o = 32; o >= 1; o >>= 1) argmax_merge(best, bi, __shfl_xor(best, o, 64), __shfl_xor(bi, o, 64));
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (lane == 0) {
         sv[wave] = best;
@@ -57,13 +66,20 @@ __global__ __launch_bounds__(kThreads) void k_argmax(const float* logits, int V,
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        for (int w = 1; w < kWaves; ++w)
-            if (sv[w] > best || (sv[w] == best && si[w] < bi)) {
-                best = sv[w];
-                bi = si[w];
-            }
-        out[blockIdx.x] = bi < V ? bi : 0;
+        for (int w = 1; w < kWaves; ++w) argmax_merge(best, bi, sv[w], si[w]);
+        st_co(&pv[b * kArgBlocks + blockIdx.x], best);
+        st_co(&pi[b * kArgBlocks + blockIdx.x], bi);
+        wait_stores();
+        const uint32_t old = __hip_atomic_fetch_add(&cnt[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = (old + 1u == (uint32_t)kArgBlocks);
     }
+    __syncthreads();
+    if (!last || threadIdx.x != 0) return;
+    best = -INFINITY;
+    bi = V;
+    for (int k = 0; k < kArgBlocks; ++k) argmax_merge(best, bi, ld_co(&pv[b * kArgBlocks + k]), ld_co(&pi[b * kArgBlocks + k]));
+    out[b] = bi < V ? bi : 0;
+    __hip_atomic_store(&cnt[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace mk
@@ -88,7 +104,11 @@ struct mk_plan {
     EventRec* d_evrec = nullptr;
     uint32_t* d_ev = nullptr;
     uint32_t* d_arrive = nullptr;
-    RingSlot* d_jit = nullptr;
+    RingSlot* d_inbox = nullptr;
+    int64_t* d_inbox_tail = nullptr;
+    int64_t* d_inbox_head = nullptr;
+    int32_t* d_elig = nullptr;
+    void* d_zero = nullptr;
     RingSlot* d_mb = nullptr;
     Ctrl* d_ctrl = nullptr;
     float2* d_rope = nullptr;
@@ -97,6 +117,12 @@ struct mk_plan {
     float* d_x0 = nullptr;
     float* d_xfinal = nullptr;
     LayerPtrs* d_lw = nullptr;
+    float* d_argv = nullptr;
+    int32_t* d_argi = nullptr;
+    uint32_t* d_argc = nullptr;
+    mk_trace_rec* d_trace = nullptr;
+    int32_t* d_trace_n = nullptr;
+    int trace_cap = 0;
     int64_t act_stride = 0, off_qkv = 0, off_attn = 0, off_xmid = 0, off_h = 0, off_xnext = 0;
     size_t ctrl_off = 0, ev_off = 0, arrive_off = 0, jit_off = 0, mb_off = 0, ctrl_bytes = 0;
     // state
@@ -174,15 +200,25 @@ bool upload_plan(mk_plan* pl) {
     // zero-initialised control area: events, arrivals, rings, ctrl
     Region r_ev = take(sizeof(uint32_t) * hp.events.size());
     Region r_arr = take(sizeof(uint32_t) * (size_t)B * Hkv);
-    Region r_jit = take(sizeof(RingSlot) * (size_t)hp.jit_ring_cap);
+    Region r_inbox = take(sizeof(RingSlot) * (size_t)hp.workers * hp.inbox_cap);
+    Region r_itail = take(sizeof(int64_t) * (size_t)hp.workers);
+    Region r_ihead = take(sizeof(int64_t) * (size_t)hp.workers);
     Region r_mb = take(sizeof(RingSlot) * (size_t)hp.mb_cap);
     Region r_ctrl = take(sizeof(Ctrl));
     Region r_rope = take(sizeof(float2) * (size_t)hp.cap * (D / 2));
-    Region r_part = take(sizeof(float) * (size_t)B * Hkv * hp.max_splits * (G * D + 2 * G));
+    Region r_part = take(sizeof(float) * (size_t)B * Hkv * hp.max_splits * attn_rec(G, D));
     Region r_act = take(sizeof(float) * (size_t)L * pl->act_stride);
     Region r_x0 = take(sizeof(float) * (size_t)B * H);
     Region r_xf = take(sizeof(float) * (size_t)B * H);
     Region r_lw = take(sizeof(LayerPtrs) * L);
+    Region r_zero = take(64 * 1024);
+    Region r_elig = take(sizeof(int32_t) * std::max<size_t>(1, hp.jit_elig.size()));
+    Region r_argv = take(sizeof(float) * (size_t)B * kArgBlocks);
+    Region r_argi = take(sizeof(int32_t) * (size_t)B * kArgBlocks);
+    Region r_argc = take(sizeof(uint32_t) * (size_t)B);
+    pl->trace_cap = d.opts.trace > 0 ? d.opts.trace : 0;
+    Region r_tr = take(sizeof(mk_trace_rec) * (size_t)hp.workers * pl->trace_cap);
+    Region r_trn = take(sizeof(int32_t) * (size_t)hp.workers);
     pl->dbytes = align_up(at, 256);
     if (!hip_ok(hipSetDevice(pl->device), "hipSetDevice")) return false;
     if (!hip_ok(hipMalloc((void**)&pl->dmem, pl->dbytes), "hipMalloc(plan)")) return false;
@@ -195,7 +231,9 @@ bool upload_plan(mk_plan* pl) {
     pl->d_evrec = (EventRec*)(m + r_evrec.off);
     pl->d_ev = (uint32_t*)(m + r_ev.off);
     pl->d_arrive = (uint32_t*)(m + r_arr.off);
-    pl->d_jit = (RingSlot*)(m + r_jit.off);
+    pl->d_inbox = (RingSlot*)(m + r_inbox.off);
+    pl->d_inbox_tail = (int64_t*)(m + r_itail.off);
+    pl->d_inbox_head = (int64_t*)(m + r_ihead.off);
     pl->d_mb = (RingSlot*)(m + r_mb.off);
     pl->d_ctrl = (Ctrl*)(m + r_ctrl.off);
     pl->d_rope = (float2*)(m + r_rope.off);
@@ -204,6 +242,13 @@ bool upload_plan(mk_plan* pl) {
     pl->d_x0 = (float*)(m + r_x0.off);
     pl->d_xfinal = (float*)(m + r_xf.off);
     pl->d_lw = (LayerPtrs*)(m + r_lw.off);
+    pl->d_elig = (int32_t*)(m + r_elig.off);
+    pl->d_zero = m + r_zero.off;
+    pl->d_argv = (float*)(m + r_argv.off);
+    pl->d_argi = (int32_t*)(m + r_argi.off);
+    pl->d_argc = (uint32_t*)(m + r_argc.off);
+    pl->d_trace = pl->trace_cap ? (mk_trace_rec*)(m + r_tr.off) : nullptr;
+    pl->d_trace_n = (int32_t*)(m + r_trn.off);
     pl->ctrl_off = r_ev.off;
     pl->ctrl_bytes = r_ctrl.off + r_ctrl.bytes - r_ev.off;
     auto up = [&](void* dst, const void* src, size_t n) {
@@ -214,6 +259,7 @@ bool upload_plan(mk_plan* pl) {
     if (!up(pl->d_queue, hp.queue.data(), sizeof(int32_t) * hp.queue.size())) return false;
     if (!up(pl->d_level_tasks, hp.level_tasks.data(), sizeof(int32_t) * hp.level_tasks.size())) return false;
     if (!up(pl->d_evrec, hp.events.data(), sizeof(EventRec) * hp.events.size())) return false;
+    if (!up(pl->d_elig, hp.jit_elig.data(), sizeof(int32_t) * hp.jit_elig.size())) return false;
     // RoPE table: theta_i = pos * base^(-2i/D), cos/sin in double, stored as float
     std::vector<float2> rope((size_t)hp.cap * (D / 2));
     for (int pos = 0; pos < hp.cap; ++pos)
@@ -263,7 +309,10 @@ KParams make_params(const mk_plan* pl, const mk_weights* w, const mk_kv_cache* k
     p.evrec = pl->d_evrec;
     p.ev = pl->d_ev;
     p.arrive = pl->d_arrive;
-    p.jit = pl->d_jit;
+    p.inbox = pl->d_inbox;
+    p.inbox_tail = pl->d_inbox_tail;
+    p.inbox_head = pl->d_inbox_head;
+    p.elig = pl->d_elig;
     p.mb = pl->d_mb;
     p.ctrl = pl->d_ctrl;
     p.rope = pl->d_rope;
@@ -287,6 +336,7 @@ KParams make_params(const mk_plan* pl, const mk_weights* w, const mk_kv_cache* k
         p.logits = out;
     }
     p.lw = pl->d_lw;
+    p.zero = pl->d_zero;
     p.embed = w->embed;
     p.final_norm = w->final_norm;
     p.lm_head = w->lm_head;
@@ -319,10 +369,14 @@ KParams make_params(const mk_plan* pl, const mk_weights* w, const mk_kv_cache* k
     p.n_workers = hp.workers;
     p.jit_on = hp.jit;
     p.persistent = d.opts.mode == MK_PERSISTENT ? 1 : 0;
-    p.jit_mask = hp.jit_ring_cap - 1;
+    p.inbox_mask = hp.inbox_cap - 1;
+    p.n_elig = (int)hp.jit_elig.size();
     p.mb_mask = hp.mb_cap - 1;
     const int wd = d.opts.watchdog_ms > 0 ? d.opts.watchdog_ms : 2000;
     p.watchdog_ticks = (uint64_t)wd * 100000ull;
+    p.trace = pl->d_trace;
+    p.trace_n = pl->d_trace_n;
+    p.trace_cap = pl->trace_cap;
     return p;
 }
 
@@ -520,10 +574,29 @@ int mk_argmax(const mk_plan* pl, const float* logits, int32_t* out_tokens, void*
     if (!pl || !logits || !out_tokens) return set_err("null argument"), MK_ERR_ARG;
     if (pl->host_only) return set_err("host-only plan"), MK_ERR_STATE;
     if (pl->hp.desc.hidden_io) return set_err("hidden_io plan has no logits"), MK_ERR_STATE;
-    hipLaunchKernelGGL(k_argmax, dim3(pl->hp.desc.batch), dim3(kThreads), 0, (hipStream_t)stream, logits,
-                       pl->hp.desc.vocab, out_tokens);
+    hipLaunchKernelGGL(k_argmax, dim3(kArgBlocks, pl->hp.desc.batch), dim3(kThreads), 0, (hipStream_t)stream, logits,
+                       pl->hp.desc.vocab, out_tokens, pl->d_argv, pl->d_argi, pl->d_argc);
     if (!hip_ok(hipGetLastError(), "k_argmax launch")) return MK_ERR_HIP;
     return MK_OK;
+}
+
+int mk_plan_trace(const mk_plan* pl, mk_trace_rec* out, int64_t max_records, void* stream) {
+    if (!pl || (!out && max_records > 0)) return set_err("null argument"), MK_ERR_ARG;
+    if (pl->host_only || !pl->d_trace) return set_err("plan built without trace"), MK_ERR_STATE;
+    if (!hip_ok(hipSetDevice(pl->device), "hipSetDevice") ||
+        !hip_ok(hipStreamSynchronize((hipStream_t)stream), "hipStreamSynchronize"))
+        return MK_ERR_HIP;
+    const int W = pl->hp.workers;
+    std::vector<int32_t> n(W);
+    std::vector<mk_trace_rec> all((size_t)W * pl->trace_cap);
+    if (!hip_ok(hipMemcpy(n.data(), pl->d_trace_n, sizeof(int32_t) * W, hipMemcpyDeviceToHost), "hipMemcpy(trace)") ||
+        !hip_ok(hipMemcpy(all.data(), pl->d_trace, sizeof(mk_trace_rec) * all.size(), hipMemcpyDeviceToHost),
+                "hipMemcpy(trace)"))
+        return MK_ERR_HIP;
+    int64_t k = 0;
+    for (int w = 0; w < W; ++w)
+        for (int i = 0; i < std::min(n[w], pl->trace_cap) && k < max_records; ++i) out[k++] = all[(size_t)w * pl->trace_cap + i];
+    return (int)k;
 }
 
 int mk_plan_verify(const mk_plan* pl) {

@@ -21,9 +21,14 @@ struct Lds {
     float* p;     // G * chunk: scores, then probabilities
     float* acc;   // kWaves * 8 * 128: P.V partials per wave
     float* ml;    // 2 * 8: (m, l) per head
+    float* cmb;   // kCmbSplits * (8 * 128 + 16): partials staged for the combine
+    uint64_t* marks;  // 2 trace phase marks
 };
 
-__host__ __device__ constexpr int lds_floats_fixed() { return 64 + 16 + 16 + kWaves * 256 * 4 + 8 * 128 + 2 * 128 + kWaves * 8 * 128 + 16; }
+constexpr int kCmbSplits = 8;  // splits merged per staged chunk
+__host__ __device__ constexpr int lds_floats_fixed() {
+    return 64 + 16 + 16 + 4 + kWaves * 256 * 4 + 8 * 128 + 2 * 128 + kWaves * 8 * 128 + 16 + kCmbSplits * (8 * 128 + 16);
+}
 __host__ __device__ inline int lds_bytes_for(int G, int chunk) { return 4 * (lds_floats_fixed() + G * chunk); }
 
 __device__ __forceinline__ Lds carve_lds(float* base, int G, int chunk) {
@@ -31,12 +36,14 @@ __device__ __forceinline__ Lds carve_lds(float* base, int G, int chunk) {
     float* p = base;
     s.red = p; p += 64;
     s.cmd = (int*)p; p += 16;
+    s.marks = (uint64_t*)p; p += 4;
     s.rstd = p; p += 16;
     s.part = p; p += kWaves * 256 * 4;
     s.q = p; p += 8 * 128;
     s.kn = p; p += 2 * 128;
     s.acc = p; p += kWaves * 8 * 128;
     s.ml = p; p += 16;
+    s.cmb = p; p += kCmbSplits * (8 * 128 + 16);
     s.p = p;
     (void)G; (void)chunk;
     return s;
@@ -58,12 +65,15 @@ template <int NB>
 __device__ __forceinline__ void block_rstd(const float* x, int ldx, int K, int B, float eps, const Lds& s) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     float ss[NB];
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)(B * ldx) * 4u);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         ss[b] = 0.f;
         if (b < B)
             for (int k = tid * 4; k < K; k += kThreads * 4) {
-                const float4 v = *(const float4*)(x + (int64_t)b * ldx + k);
+                const uint4 u = buf_load16_co(xr, (uint32_t)(b * ldx + k) * 4u, 0);
+                const float4 v = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
+                                             __uint_as_float(u.w));
                 ss[b] += v.x * v.x;
                 ss[b] += v.y * v.y;
                 ss[b] += v.z * v.z;
@@ -90,111 +100,169 @@ __device__ __forceinline__ void block_rstd(const float* x, int ldx, int K, int B
 // registers; each wave reduces its partial dot products with a butterfly,
 // and the four wave partials are added in wave order. Output row r gets
 //   y[b, r] = (sum_w sum_lane sum_seg sum_e W[r,k] * g[k] * x[b,k]) * rstd[b].
-// NSW = segments per wave (compile time), U = rows in flight per wave.
+// NSW = segments per wave (compile time), U = rows per group. Weight loads
+// are double-buffered: group i+1 is in flight while group i is consumed.
+// Rows past the tile and segments past K load through an out-of-range
+// offset (zeros, no memory traffic), so every load is issued unconditionally.
 template <typename WT, int NB, int NSW, int U, bool DUAL, typename RowFn, typename OutFn>
-__device__ __forceinline__ void gemv_ksplit(int r0, int r1, int K, const float* x, int ldx, int B, const WT* gain, RowFn rowp,
-                            OutFn out, const Lds& s) {
+__device__ __forceinline__ void gemv_ksplit(int r0, int r1, int K, const float* x, int ldx, int B, const WT* gain,
+                                            float eps, RowFn rowp, OutFn out, const Lds& s, bool tr) {
     using V = Vec16<WT>;
     constexpr int E = V::N, SEG = 64 * E;
+    constexpr int NM = DUAL ? 2 : 1;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nseg = (K + SEG - 1) / SEG;
-    float xr[NSW][NB][E];
-    int kof[NSW];
-    bool kval[NSW];
+    uint32_t voff[NSW];
+    bool kvalid[NSW];
 #pragma unroll
     for (int j = 0; j < NSW; ++j) {
-        const int sg = wave + kWaves * j;
-        kof[j] = sg * SEG + lane * E;
-        kval[j] = sg < nseg && kof[j] < K;
-        float g[E];
-        if (gain && kval[j]) V::widen(*(const uint4*)(gain + kof[j]), g);
-        else
+        const int k = (wave + kWaves * j) * SEG + lane * E;
+        kvalid[j] = wave + kWaves * j < nseg && k < K;
+        voff[j] = kvalid[j] ? (uint32_t)k * (uint32_t)sizeof(WT) : kOOB;
+    }
+    constexpr int WIN = 4096 / (kWaves * NM * NB);  // rows per LDS window
+    auto load = [&](uint4 (&w)[U][NM][NSW], int r, int rend) {
 #pragma unroll
-            for (int e = 0; e < E; ++e) g[e] = 1.f;
+        for (int u = 0; u < U; ++u) {
+            const bool rv = r + u < rend;
+            RowRef rf[2];
+            rowp(rv ? r + u : rend - 1, rf[0], rf[1]);
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+#pragma unroll
+                for (int j = 0; j < NSW; ++j) w[u][m][j] = buf_load16(rf[m].r, rv ? voff[j] : kOOB, rf[m].soff);
+        }
+    };
+    // the first weight group goes out before the (latency-bound) x loads
+    uint4 wa[U][NM][NSW], wb[U][NM][NSW];
+    load(wa, r0, min(r0 + WIN, r1));
+
+    // x (agent-coherent: written earlier in this step) and the norm gain
+    const __amdgpu_buffer_rsrc_t xr_rs = make_rsrc(x, (uint32_t)(B * ldx) * 4u);
+    const __amdgpu_buffer_rsrc_t g_rs = make_rsrc(gain, gain ? (uint32_t)K * (uint32_t)sizeof(WT) : 0u);
+    float xr[NSW][NB][E];
+#pragma unroll
+    for (int j = 0; j < NSW; ++j)
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
+            const uint32_t xo = (kvalid[j] && b < B) ? (uint32_t)(b * ldx) * 4u + voff[j] / (uint32_t)sizeof(WT) * 4u : kOOB;
 #pragma unroll
             for (int e = 0; e < E; e += 4) {
-                float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (kval[j] && b < B) v = *(const float4*)(x + (int64_t)b * ldx + kof[j] + e);
-                xr[j][b][e + 0] = v.x * g[e + 0];
-                xr[j][b][e + 1] = v.y * g[e + 1];
-                xr[j][b][e + 2] = v.z * g[e + 2];
-                xr[j][b][e + 3] = v.w * g[e + 3];
+                const uint4 v = buf_load16_co(xr_rs, xo, (uint32_t)e * 4u);
+                xr[j][b][e + 0] = __uint_as_float(v.x);
+                xr[j][b][e + 1] = __uint_as_float(v.y);
+                xr[j][b][e + 2] = __uint_as_float(v.z);
+                xr[j][b][e + 3] = __uint_as_float(v.w);
             }
         }
+    float g[NSW][E];
+#pragma unroll
+    for (int j = 0; j < NSW; ++j) {
+        if (gain) V::widen(buf_load16(g_rs, voff[j], 0), g[j]);
+        else
+#pragma unroll
+            for (int e = 0; e < E; ++e) g[j][e] = 1.f;
     }
-    constexpr int NM = DUAL ? 2 : 1;
-    for (int rg = r0; rg < r1; rg += 256) {
-        const int rend = min(rg + 256, r1);
-        for (int r = rg; r < rend; r += U) {
-            uint4 w[U][NM][NSW];
+    if (gain) {
+        // RMSNorm statistic: the four waves' segments cover K exactly once;
+        // lane sums in (segment, element) order, butterfly, then waves in order
+        float ss[NB];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int row = min(r + u, rend - 1);
-                const WT* pr[2];
-                rowp(row, pr[0], pr[1]);
+        for (int b = 0; b < NB; ++b) {
+            ss[b] = 0.f;
 #pragma unroll
-                for (int m = 0; m < NM; ++m)
+            for (int j = 0; j < NSW; ++j)
 #pragma unroll
-                    for (int j = 0; j < NSW; ++j)
-                        w[u][m][j] = kval[j] ? *(const uint4*)(pr[m] + kof[j]) : make_uint4(0, 0, 0, 0);
-            }
+                for (int e = 0; e < E; ++e) ss[b] += xr[j][b][e] * xr[j][b][e];
+            ss[b] = wave_sum(ss[b]);
+        }
+        if (lane == 0)
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
+            for (int b = 0; b < NB; ++b) s.red[wave * 16 + b] = ss[b];
+        __syncthreads();
+        if (tid < NB) {
+            float t = s.red[tid];
 #pragma unroll
-                for (int m = 0; m < NM; ++m) {
-                    float acc[NB];
+            for (int w = 1; w < kWaves; ++w) t += s.red[w * 16 + tid];
+            s.rstd[tid] = 1.0f / sqrtf(t / (float)K + eps);
+        }
+        // s.rstd is read by `out` only after the window barrier below
+    }
+    if (tr && tid == 0) s.marks[0] = now_ticks();
 #pragma unroll
-                    for (int b = 0; b < NB; ++b) acc[b] = 0.f;
+    for (int j = 0; j < NSW; ++j)
 #pragma unroll
-                    for (int j = 0; j < NSW; ++j) {
-                        float wf[E];
-                        V::widen(w[u][m][j], wf);
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
-                        for (int e = 0; e < E; ++e)
+            for (int e = 0; e < E; ++e) xr[j][b][e] = xr[j][b][e] * g[j][e];
+
+    auto consume = [&](const uint4 (&w)[U][NM][NSW], int r, int rend, int rg) {
 #pragma unroll
-                            for (int b = 0; b < NB; ++b) acc[b] = fmaf(wf[e], xr[j][b][e], acc[b]);
-                    }
+        for (int u = 0; u < U; ++u) {
 #pragma unroll
-                    for (int b = 0; b < NB; ++b) {
-                        const float v = wave_sum(acc[b]);
-                        if (lane == 0 && r + u < rend) s.part[((wave * 256) + (r + u - rg)) * 2 * NB + m * NB + b] = v;
-                    }
+            for (int m = 0; m < NM; ++m) {
+                float acc[NB];
+#pragma unroll
+                for (int b = 0; b < NB; ++b) acc[b] = 0.f;
+#pragma unroll
+                for (int j = 0; j < NSW; ++j) {
+                    float wf[E];
+                    V::widen(w[u][m][j], wf);
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+#pragma unroll
+                        for (int b = 0; b < NB; ++b) acc[b] = fmaf(wf[e], xr[j][b][e], acc[b]);
+                }
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const float v = wave_sum(acc[b]);
+                    if (lane == 0 && r + u < rend) s.part[((wave * WIN) + (r + u - rg)) * NM * NB + m * NB + b] = v;
                 }
             }
         }
+    };
+    for (int rg = r0; rg < r1; rg += WIN) {
+        const int rend = min(rg + WIN, r1);
+        if (rg != r0) load(wa, rg, rend);
+        for (int r = rg; r < rend; r += 2 * U) {
+            load(wb, r + U, rend);
+            consume(wa, r, rend, rg);
+            load(wa, r + 2 * U, rend);
+            consume(wb, r + U, rend, rg);
+        }
+        if (tr && tid == 0) s.marks[1] = now_ticks();
         __syncthreads();
         for (int i = tid; i < (rend - rg) * NB; i += kThreads) {
             const int rr = i / NB, b = i % NB;
-            float t[2];
+            float t[2] = {0.f, 0.f};
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
-                float a = s.part[(rr)*2 * NB + m * NB + b];
+                float a = s.part[rr * NM * NB + m * NB + b];
 #pragma unroll
-                for (int wv = 1; wv < kWaves; ++wv) a += s.part[((wv * 256) + rr) * 2 * NB + m * NB + b];
+                for (int wv = 1; wv < kWaves; ++wv) a += s.part[((wv * WIN) + rr) * NM * NB + m * NB + b];
                 t[m] = a;
             }
-            if (b < B) out(rg + rr, b, t[0], DUAL ? t[1] : 0.f);
+            if (b < B) out(rg + rr, b, t[0], t[1]);
         }
         __syncthreads();
     }
 }
 
 // ---------------------------------------------------------------- GEMV (B >= 3)
-// One row per wave at a time, K across the lanes, x read from the cache.
+// One row per wave at a time, K across the lanes, x read through the cache.
 // The per-row arithmetic (lane partial sums over segments, butterfly) is
 // fixed by the shape, so the result does not depend on the task tiling.
 template <typename WT, int NB, bool DUAL, typename RowFn, typename OutFn>
-__device__ __forceinline__ void gemv_rowwave(int r0, int r1, int K, const float* x, int ldx, int B, const WT* gain, RowFn rowp,
-                             OutFn out) {
+__device__ __forceinline__ void gemv_rowwave(int r0, int r1, int K, const float* x, int ldx, int B, const WT* gain,
+                                             RowFn rowp, OutFn out) {
     using V = Vec16<WT>;
     constexpr int E = V::N, SEG = 64 * E;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     constexpr int NM = DUAL ? 2 : 1;
+    const __amdgpu_buffer_rsrc_t x_rs = make_rsrc(x, (uint32_t)(B * ldx) * 4u);
     for (int r = r0 + wave; r < r1; r += kWaves) {
-        const WT* pr[2];
-        rowp(r, pr[0], pr[1]);
+        RowRef rf[2];
+        rowp(r, rf[0], rf[1]);
         float acc[NM][NB];
 #pragma unroll
         for (int m = 0; m < NM; ++m)
@@ -204,7 +272,7 @@ __device__ __forceinline__ void gemv_rowwave(int r0, int r1, int K, const float*
         for (int k = lane * E; k < K; k += SEG) {
             uint4 w[NM];
 #pragma unroll
-            for (int m = 0; m < NM; ++m) w[m] = *(const uint4*)(pr[m] + k);
+            for (int m = 0; m < NM; ++m) w[m] = buf_load16(rf[m].r, (uint32_t)k * (uint32_t)sizeof(WT), rf[m].soff);
             float g[E];
             if (gain) V::widen(*(const uint4*)(gain + k), g);
             else
@@ -219,11 +287,11 @@ __device__ __forceinline__ void gemv_rowwave(int r0, int r1, int K, const float*
                 float xv[E];
 #pragma unroll
                 for (int e = 0; e < E; e += 4) {
-                    const float4 v = *(const float4*)(x + (int64_t)b * ldx + k + e);
-                    xv[e] = v.x * g[e];
-                    xv[e + 1] = v.y * g[e + 1];
-                    xv[e + 2] = v.z * g[e + 2];
-                    xv[e + 3] = v.w * g[e + 3];
+                    const uint4 v = buf_load16_co(x_rs, (uint32_t)(b * ldx + k + e) * 4u, 0);
+                    xv[e] = __uint_as_float(v.x) * g[e];
+                    xv[e + 1] = __uint_as_float(v.y) * g[e + 1];
+                    xv[e + 2] = __uint_as_float(v.z) * g[e + 2];
+                    xv[e + 3] = __uint_as_float(v.w) * g[e + 3];
                 }
 #pragma unroll
                 for (int m = 0; m < NM; ++m)
@@ -236,7 +304,10 @@ __device__ __forceinline__ void gemv_rowwave(int r0, int r1, int K, const float*
         for (int b = 0; b < NB; ++b) {
             const float a0 = wave_sum(acc[0][b]);
             const float a1 = DUAL ? wave_sum(acc[NM - 1][b]) : 0.f;
-            if (lane == b) { t0 = a0; t1 = a1; }
+            if (lane == b) {
+                t0 = a0;
+                t1 = a1;
+            }
         }
         if (lane < B) out(r, lane, t0, t1);
     }
@@ -244,20 +315,42 @@ __device__ __forceinline__ void gemv_rowwave(int r0, int r1, int K, const float*
 
 template <typename WT, int NB, bool DUAL, typename RowFn, typename OutFn>
 __device__ __forceinline__ void gemv_dispatch(int r0, int r1, int K, const float* x, int ldx, int B, const WT* gain,
-                                              RowFn rowp, OutFn out, const Lds& s) {
+                                              float eps, RowFn rowp, OutFn out, const Lds& s, bool tr) {
     if constexpr (NB <= 2) {
         constexpr int SEG = 64 * Vec16<WT>::N;
+        constexpr int D2 = DUAL ? 2 : 1;
         const int nsw = ((K + SEG - 1) / SEG + kWaves - 1) / kWaves;
-        if (nsw <= 1) gemv_ksplit<WT, NB, 1, 16, DUAL>(r0, r1, K, x, ldx, B, gain, rowp, out, s);
-        else if (nsw <= 2) gemv_ksplit<WT, NB, 2, 16 / (DUAL ? 2 : 1), DUAL>(r0, r1, K, x, ldx, B, gain, rowp, out, s);
-        else if (nsw <= 4) gemv_ksplit<WT, NB, 4, 8 / (DUAL ? 2 : 1), DUAL>(r0, r1, K, x, ldx, B, gain, rowp, out, s);
-        else if (nsw <= 6) gemv_ksplit<WT, NB, 6, 4 / (DUAL ? 2 : 1), DUAL>(r0, r1, K, x, ldx, B, gain, rowp, out, s);
-        else gemv_ksplit<WT, NB, 8, 4 / (DUAL ? 2 : 1), DUAL>(r0, r1, K, x, ldx, B, gain, rowp, out, s);
+        // rows per group so that one buffer holds at most 16 16-byte loads
+        // per lane: two buffers then fit in 128 VGPRs
+        if (nsw <= 1) gemv_ksplit<WT, NB, 1, 16 / D2, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr);
+        else if (nsw <= 2) gemv_ksplit<WT, NB, 2, 8 / D2, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr);
+        else if (nsw <= 4) gemv_ksplit<WT, NB, 4, 4 / D2, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr);
+        else if (nsw <= 6) gemv_ksplit<WT, NB, 6, 2 / D2, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr);
+        else gemv_ksplit<WT, NB, 8, 2 / D2, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr);
     } else {
-        (void)s;
+        if (gain) block_rstd<NB>(x, ldx, K, B, eps, s);
         gemv_rowwave<WT, NB, DUAL>(r0, r1, K, x, ldx, B, gain, rowp, out);
     }
 }
+
+// Buffer resource over rows [lo, hi) of a row-major matrix with K columns
+// (rows clipped to [0, rows)); row r is at byte (r - lo) * K * es.
+template <typename WT>
+struct MatTile {
+    __amdgpu_buffer_rsrc_t r;
+    int lo;
+    uint32_t rowbytes;
+    __device__ __forceinline__ MatTile(const WT* m, int K, int rows, int lo_, int hi_) {
+        lo = max(0, min(lo_, rows));
+        const int hi = max(lo, min(hi_, rows));
+        rowbytes = (uint32_t)K * (uint32_t)sizeof(WT);
+        r = make_rsrc(m + (int64_t)lo * K, (uint32_t)(hi - lo) * rowbytes);
+    }
+    __device__ __forceinline__ void row(int rr, RowRef& o) const {
+        o.r = r;
+        o.soff = (uint32_t)(rr - lo) * rowbytes;
+    }
+};
 
 // ---------------------------------------------------------------- GEMV tasks
 
@@ -276,25 +369,26 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
                     if (r == r0) raise_error(p.ctrl, MK_ERR_TOKEN);
                     tok = 0;
                 }
-                p.x0_w[(int64_t)b * H + r] = load_scalar<WT>(E, (int64_t)tok * H + r);
+                st_co(&p.x0_w[(int64_t)b * H + r], load_scalar<WT>(E, (int64_t)tok * H + r));
             }
             break;
         }
         case OP_QKV: {
             const LayerPtrs w = p.lw[l];
             const float* x = layer_in(p, l);
-            block_rstd<NB>(x, H, H, B, p.eps, s);
             const int QD = p.QD, KD = p.KD, ld = QD + 2 * KD;
-            const WT* wq = (const WT*)w.wq;
-            const WT* wk = (const WT*)w.wk;
-            const WT* wv = (const WT*)w.wv;
+            const MatTile<WT> tq((const WT*)w.wq, H, QD, r0, r1);
+            const MatTile<WT> tk((const WT*)w.wk, H, KD, r0 - QD, r1 - QD);
+            const MatTile<WT> tv((const WT*)w.wv, H, KD, r0 - QD - KD, r1 - QD - KD);
             float* o = layer_buf(p, l, p.off_qkv);
-            auto rowp = [&](int r, const WT*& a, const WT*& b2) {
-                a = r < QD ? wq + (int64_t)r * H : (r < QD + KD ? wk + (int64_t)(r - QD) * H : wv + (int64_t)(r - QD - KD) * H);
+            auto rowp = [&](int r, RowRef& a, RowRef& b2) {
+                if (r < QD) tq.row(r, a);
+                else if (r < QD + KD) tk.row(r - QD, a);
+                else tv.row(r - QD - KD, a);
                 b2 = a;
             };
-            auto out = [&](int r, int b, float v, float) { o[(int64_t)b * ld + r] = v * s.rstd[b]; };
-            gemv_dispatch<WT, NB, false>(r0, r1, H, x, H, B, (const WT*)w.attn_norm, rowp, out, s);
+            auto out = [&](int r, int b, float v, float) { st_co(&o[(int64_t)b * ld + r], v * s.rstd[b]); };
+            gemv_dispatch<WT, NB, false>(r0, r1, H, x, H, B, (const WT*)w.attn_norm, p.eps, rowp, out, s, p.trace != nullptr);
             break;
         }
         case OP_O: {
@@ -302,34 +396,33 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
             const float* a = layer_buf(p, l, p.off_attn);
             const float* xin = layer_in(p, l);
             float* o = layer_buf(p, l, p.off_xmid);
-            const WT* wo = (const WT*)w.wo;
             const int K = p.QD;
-            auto rowp = [&](int r, const WT*& a0, const WT*& b2) { a0 = wo + (int64_t)r * K; b2 = a0; };
+            const MatTile<WT> to((const WT*)w.wo, K, H, r0, r1);
+            auto rowp = [&](int r, RowRef& a0, RowRef& b2) { to.row(r, a0); b2 = a0; };
             auto out = [&](int r, int b, float v, float) {
                 const int64_t i = (int64_t)b * H + r;
-                o[i] = xin[i] + v;
+                st_co(&o[i], ld_co(&xin[i]) + v);
             };
-            gemv_dispatch<WT, NB, false>(r0, r1, K, a, K, B, (const WT*)nullptr, rowp, out, s);
+            gemv_dispatch<WT, NB, false>(r0, r1, K, a, K, B, (const WT*)nullptr, p.eps, rowp, out, s, p.trace != nullptr);
             break;
         }
         case OP_GATEUP: {
             const LayerPtrs w = p.lw[l];
             const float* x = layer_buf(p, l, p.off_xmid);
-            block_rstd<NB>(x, H, H, B, p.eps, s);
             float* o = layer_buf(p, l, p.off_h);
-            const WT* wg = (const WT*)w.w_gate;
-            const WT* wu = (const WT*)w.w_up;
             const int F = p.F;
-            auto rowp = [&](int r, const WT*& a0, const WT*& b2) {
-                a0 = wg + (int64_t)r * H;
-                b2 = wu + (int64_t)r * H;
+            const MatTile<WT> tg((const WT*)w.w_gate, H, F, r0, r1);
+            const MatTile<WT> tu((const WT*)w.w_up, H, F, r0, r1);
+            auto rowp = [&](int r, RowRef& a0, RowRef& b2) {
+                tg.row(r, a0);
+                tu.row(r, b2);
             };
             auto out = [&](int r, int b, float g, float u) {
                 const float rs = s.rstd[b];
                 const float gg = g * rs, uu = u * rs;
-                o[(int64_t)b * F + r] = (gg / (1.0f + __expf(-gg))) * uu;
+                st_co(&o[(int64_t)b * F + r], (gg / (1.0f + __expf(-gg))) * uu);
             };
-            gemv_dispatch<WT, NB, true>(r0, r1, H, x, H, B, (const WT*)w.mlp_norm, rowp, out, s);
+            gemv_dispatch<WT, NB, true>(r0, r1, H, x, H, B, (const WT*)w.mlp_norm, p.eps, rowp, out, s, p.trace != nullptr);
             break;
         }
         case OP_DOWN: {
@@ -337,25 +430,24 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
             const float* h = layer_buf(p, l, p.off_h);
             const float* xm = layer_buf(p, l, p.off_xmid);
             float* o = layer_out(p, l);
-            const WT* wd = (const WT*)w.w_down;
             const int F = p.F;
-            auto rowp = [&](int r, const WT*& a0, const WT*& b2) { a0 = wd + (int64_t)r * F; b2 = a0; };
+            const MatTile<WT> td((const WT*)w.w_down, F, H, r0, r1);
+            auto rowp = [&](int r, RowRef& a0, RowRef& b2) { td.row(r, a0); b2 = a0; };
             auto out = [&](int r, int b, float v, float) {
                 const int64_t i = (int64_t)b * H + r;
-                o[i] = xm[i] + v;
+                st_co(&o[i], ld_co(&xm[i]) + v);
             };
-            gemv_dispatch<WT, NB, false>(r0, r1, F, h, F, B, (const WT*)nullptr, rowp, out, s);
+            gemv_dispatch<WT, NB, false>(r0, r1, F, h, F, B, (const WT*)nullptr, p.eps, rowp, out, s, p.trace != nullptr);
             break;
         }
         case OP_LM: {
             const float* x = p.x_final;
-            block_rstd<NB>(x, H, H, B, p.eps, s);
-            const WT* wl = (const WT*)p.lm_head;
             float* o = p.logits;
             const int V = p.V;
-            auto rowp = [&](int r, const WT*& a0, const WT*& b2) { a0 = wl + (int64_t)r * H; b2 = a0; };
-            auto out = [&](int r, int b, float v, float) { o[(int64_t)b * V + r] = v * s.rstd[b]; };
-            gemv_dispatch<WT, NB, false>(r0, r1, H, x, H, B, (const WT*)p.final_norm, rowp, out, s);
+            const MatTile<WT> tl((const WT*)p.lm_head, H, V, r0, r1);
+            auto rowp = [&](int r, RowRef& a0, RowRef& b2) { tl.row(r, a0); b2 = a0; };
+            auto out = [&](int r, int b, float v, float) { o[(int64_t)b * V + r] = v * s.rstd[b]; };  // read after the launch
+            gemv_dispatch<WT, NB, false>(r0, r1, H, x, H, B, (const WT*)p.final_norm, p.eps, rowp, out, s, p.trace != nullptr);
             break;
         }
         default: break;
@@ -369,20 +461,19 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
 // The arrival that completes a JIT-triggering event posts a message to the
 // scheduler mailbox (§2.2: the data-dependent successor is launched JIT).
 __device__ __forceinline__ void signal_event(const KParams& p, int e, const Lds& s) {
-    fence_release();
+    wait_stores();  // this thread's agent-coherent stores have completed
     __syncthreads();
     if (threadIdx.x == 0 && e >= 0) {
-        const uint32_t old = __hip_atomic_fetch_add(&p.ev[e], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t old = __hip_atomic_fetch_add(&p.ev[e], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const EventRec er = p.evrec[e];
         if (er.jit_layer >= 0 && old + 1u == er.required * (p.epoch + 1u)) {
-            // the completing arrival forwards every producer's writes to the
-            // scheduler: acquire what the earlier releases published first
-            fence_acquire();
+            // the completing arrival posts "expand attention of this layer"
             const int64_t pos = __hip_atomic_fetch_add(&p.ctrl->mb_tail, (int64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             RingSlot* sl = &p.mb[pos & p.mb_mask];
-            sl->p0 = er.jit_layer;
-            sl->p1 = 0;
-            __hip_atomic_store(&sl->tag, pos + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            st_co(&sl->p0, er.jit_layer);
+            st_co(&sl->p1, 0);
+            wait_stores();
+            __hip_atomic_store(&sl->tag, pos + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
     (void)s;
@@ -427,10 +518,13 @@ __device__ __forceinline__ void head_norm_rope(float* v, int D, const WT* gain, 
 
 // One split of the split-KV decode attention for (layer, b, g, split):
 // positions [split*C, min((split+1)*C, pos+1)). Writes the split's partial
-// (m, l, acc) and, if it is the last to arrive for (b, g), combines all
+// (acc, m, l) and, if it is the last to arrive for (b, g), merges all
 // splits in split order and (persistent mode) signals the layer's
 // attention event. The split that holds position pos first normalises,
 // rotates and appends the new k and v (rounded to the cache type).
+// Partial record: acc[G*D], m[h] at G*D + h, l[h] at G*D + 8 + h.
+__host__ __device__ constexpr int attn_rec(int G, int D) { return G * D + 16; }
+
 template <typename WT>
 __device__ __forceinline__ void attention_task(const KParams& p, int l, int bg, int split, const Lds& s) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -446,76 +540,105 @@ __device__ __forceinline__ void attention_task(const KParams& p, int l, int bg, 
     const LayerPtrs& lw = p.lw[l];
 
     if (overflow) {
-        for (int i = tid; i < G * D; i += kThreads) out[i] = 0.f;
+        for (int i = tid; i < G * D; i += kThreads) st_co(&out[i], 0.f);
         if (tid == 0) raise_error(p.ctrl, MK_ERR_KV_OVERFLOW);
         if (p.persistent) signal_event(p, ev_attn(l), s);
         return;
     }
     const int j0 = split * C, j1 = min(j0 + C, keys);
     const bool owner = (j1 == keys);
+    const int n = j1 - j0;
+
+    // K/V rows of this split: lane (rr, cc) holds 16 bytes of row
+    // j = it*per_it + wave*ppw + rr. The first batch of K and V is requested
+    // before anything else (it depends on nothing computed here).
+    using VK = Vec16<WT>;
+    constexpr int E = VK::N;
+    constexpr int NIT = 8;
+    const int lpr = D / E;            // lanes per K row
+    const int ppw = 64 / lpr;         // rows per wave per load
+    const int per_it = kWaves * ppw;  // rows per workgroup iteration
+    const int sub = per_it * NIT;     // rows per batch
+    const int rr = lane / lpr, cc = lane % lpr;
+    const WT* kbase = (const WT*)p.kv_k;
+    const WT* vbase = (const WT*)p.kv_v;
+    const uint4 z4 = make_uint4(0, 0, 0, 0);
+    uint4 kr[NIT], vr[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int j = it * per_it + wave * ppw + rr;
+        const int jj = j0 + j;
+        const bool ld = j < n && jj != pos;
+        const int64_t off = ld ? kv_offset(p, l, b, g, jj) + cc * E : 0;
+        kr[it] = ld ? *(const uint4*)(kbase + off) : z4;
+        vr[it] = ld ? *(const uint4*)(vbase + off) : z4;
+    }
+
+    // 1. query heads of this group: norm + RoPE into LDS
     const float2* rope_row = p.rope + (int64_t)pos * (D / 2);
     const WT* qn = (const WT*)lw.q_norm;
     const WT* kn = (const WT*)lw.k_norm;
-
-    // 1. query heads of this group: norm + RoPE into LDS
     for (int hh = wave; hh < G; hh += kWaves) {
         float v[2];
-        const int per = D / 64;
-        for (int i = 0; i < per; ++i) v[i] = qkv[(int64_t)(g * G + hh) * D + lane + 64 * i];
+        v[0] = ld_co(&qkv[(int64_t)(g * G + hh) * D + lane]);
+        v[1] = D > 64 ? ld_co(&qkv[(int64_t)(g * G + hh) * D + lane + 64]) : 0.f;
         head_norm_rope<WT>(v, D, qn, p.qk_norm != 0, p.eps, rope_row);
-        for (int i = 0; i < per; ++i) s.q[hh * D + lane + 64 * i] = v[i];
+        s.q[hh * D + lane] = v[0];
+        if (D > 64) s.q[hh * D + lane + 64] = v[1];
     }
     // 2. owner: new k (norm + RoPE) and v, rounded to the cache type, appended
     if (owner && wave < 2) {
         float v[2];
-        const int per = D / 64;
         const int64_t base = wave == 0 ? (int64_t)p.QD + (int64_t)g * D : (int64_t)p.QD + p.KD + (int64_t)g * D;
-        for (int i = 0; i < per; ++i) v[i] = qkv[base + lane + 64 * i];
+        v[0] = ld_co(&qkv[base + lane]);
+        v[1] = D > 64 ? ld_co(&qkv[base + lane + 64]) : 0.f;
         if (wave == 0) head_norm_rope<WT>(v, D, kn, p.qk_norm != 0, p.eps, rope_row);
         WT* dst = (WT*)(wave == 0 ? p.kv_k : p.kv_v) + kv_offset(p, l, b, g, pos);
-        for (int i = 0; i < per; ++i) {
+        for (int i = 0; i < D / 64; ++i) {
             const WT c = from_float<WT>(v[i]);
             dst[lane + 64 * i] = c;
             s.kn[wave * 128 + lane + 64 * i] = to_float<WT>(c);
         }
     }
     __syncthreads();
+    trace_mark(p, s.marks, 0);
 
     // 3. scores s_j = (q_h . k_j) * scale for j in [j0, j1)
-    using VK = Vec16<WT>;
-    constexpr int E = VK::N;
-    const int lpr = D / E;          // lanes per K row
-    const int ppw = 64 / lpr;       // rows per wave load
-    const int rr = lane / lpr, cc = lane % lpr;
-    const int n = j1 - j0;
     float qreg[8][E];
 #pragma unroll
     for (int hh = 0; hh < 8; ++hh)
 #pragma unroll
         for (int e = 0; e < E; ++e) qreg[hh][e] = hh < G ? s.q[hh * D + cc * E + e] : 0.f;
-    const WT* kbase = (const WT*)p.kv_k;
-    for (int j = wave * ppw + rr; j - rr < n; j += kWaves * ppw) {
-        const int jj = j0 + j;
-        float kf[E];
-        const bool valid = j < n;
-        if (valid && jj == pos) {
+    for (int base = 0; base < n; base += sub) {
+        if (base > 0) {
 #pragma unroll
-            for (int e = 0; e < E; ++e) kf[e] = s.kn[cc * E + e];
-        } else if (valid) {
-            const uint4 kv = *(const uint4*)(kbase + kv_offset(p, l, b, g, jj) + cc * E);
-            VK::widen(kv, kf);
-        } else {
-#pragma unroll
-            for (int e = 0; e < E; ++e) kf[e] = 0.f;
+            for (int it = 0; it < NIT; ++it) {
+                const int j = base + it * per_it + wave * ppw + rr;
+                const int jj = j0 + j;
+                const bool ld = j < n && jj != pos;
+                kr[it] = ld ? *(const uint4*)(kbase + (ld ? kv_offset(p, l, b, g, jj) + cc * E : 0)) : z4;
+            }
         }
 #pragma unroll
-        for (int hh = 0; hh < 8; ++hh) {
-            if (hh >= G) break;
-            float d = 0.f;
+        for (int it = 0; it < NIT; ++it) {
+            const int j = base + it * per_it + wave * ppw + rr;
+            const bool valid = j < n;
+            float kf[E];
+            if (valid && j0 + j == pos) {
 #pragma unroll
-            for (int e = 0; e < E; ++e) d = fmaf(qreg[hh][e], kf[e], d);
-            for (int o = lpr / 2; o >= 1; o >>= 1) d += __shfl_xor(d, o, 64);
-            if (valid && cc == 0) s.p[hh * C + j] = d * p.scale;
+                for (int e = 0; e < E; ++e) kf[e] = s.kn[cc * E + e];
+            } else {
+                VK::widen(kr[it], kf);
+            }
+#pragma unroll
+            for (int hh = 0; hh < 8; ++hh) {
+                if (hh >= G) continue;
+                float d = 0.f;
+#pragma unroll
+                for (int e = 0; e < E; ++e) d = fmaf(qreg[hh][e], kf[e], d);
+                for (int o = lpr / 2; o >= 1; o >>= 1) d += __shfl_xor(d, o, 64);
+                if (valid && cc == 0) s.p[hh * C + j] = d * p.scale;
+            }
         }
     }
     __syncthreads();
@@ -539,35 +662,46 @@ __device__ __forceinline__ void attention_task(const KParams& p, int l, int bg, 
     }
     __syncthreads();
 
-    // 5. acc[h][d] = sum_j p[h][j] V[j][d]
-    const WT* vbase = (const WT*)p.kv_v;
+    // 5. acc[h][d] = sum_j p[h][j] V[j][d] (first batch of V already loaded)
     float acc[8][E];
 #pragma unroll
     for (int hh = 0; hh < 8; ++hh)
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[hh][e] = 0.f;
-    for (int j = wave * ppw + rr; j < n; j += kWaves * ppw) {
-        const int jj = j0 + j;
-        float vf[E];
-        if (jj == pos) {
+    for (int base = 0; base < n; base += sub) {
+        if (base > 0) {
 #pragma unroll
-            for (int e = 0; e < E; ++e) vf[e] = s.kn[128 + cc * E + e];
-        } else {
-            const uint4 vv = *(const uint4*)(vbase + kv_offset(p, l, b, g, jj) + cc * E);
-            VK::widen(vv, vf);
+            for (int it = 0; it < NIT; ++it) {
+                const int j = base + it * per_it + wave * ppw + rr;
+                const int jj = j0 + j;
+                const bool ld = j < n && jj != pos;
+                vr[it] = ld ? *(const uint4*)(vbase + (ld ? kv_offset(p, l, b, g, jj) + cc * E : 0)) : z4;
+            }
         }
 #pragma unroll
-        for (int hh = 0; hh < 8; ++hh) {
-            if (hh >= G) break;
-            const float pj = s.p[hh * C + j];
+        for (int it = 0; it < NIT; ++it) {
+            const int j = base + it * per_it + wave * ppw + rr;
+            if (j >= n) continue;
+            float vf[E];
+            if (j0 + j == pos) {
 #pragma unroll
-            for (int e = 0; e < E; ++e) acc[hh][e] = fmaf(pj, vf[e], acc[hh][e]);
+                for (int e = 0; e < E; ++e) vf[e] = s.kn[128 + cc * E + e];
+            } else {
+                VK::widen(vr[it], vf);
+            }
+#pragma unroll
+            for (int hh = 0; hh < 8; ++hh) {
+                if (hh >= G) continue;
+                const float pj = s.p[hh * C + j];
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[hh][e] = fmaf(pj, vf[e], acc[hh][e]);
+            }
         }
     }
     // reduce over the row groups of the wave (lanes with equal cc)
 #pragma unroll
     for (int hh = 0; hh < 8; ++hh) {
-        if (hh >= G) break;
+        if (hh >= G) continue;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             float v = acc[hh][e];
@@ -578,49 +712,79 @@ __device__ __forceinline__ void attention_task(const KParams& p, int l, int bg, 
     if (rr == 0) {
 #pragma unroll
         for (int hh = 0; hh < 8; ++hh) {
-            if (hh >= G) break;
+            if (hh >= G) continue;
 #pragma unroll
             for (int e = 0; e < E; ++e) s.acc[(wave * 8 + hh) * 128 + cc * E + e] = acc[hh][e];
         }
     }
     __syncthreads();
 
-    // 6. partial record: acc[G*D], then m[G], l[G]
-    const int rec = G * D + 2 * G;
+    // 6. partial record
+    const int rec = attn_rec(G, D);
     float* part = p.partials + ((int64_t)bg * p.max_splits + split) * rec;
     for (int i = tid; i < G * D; i += kThreads) {
         const int hh = i / D, d = i % D;
         float a = s.acc[hh * 128 + d];
         for (int w = 1; w < kWaves; ++w) a += s.acc[(w * 8 + hh) * 128 + d];
-        part[i] = a;
+        st_co(&part[i], a);
     }
-    if (tid < 2 * G) part[G * D + tid] = s.ml[tid];  // interleaved (m, l) pairs
+    if (tid < G) {
+        st_co(&part[G * D + tid], s.ml[2 * tid]);
+        st_co(&part[G * D + 8 + tid], s.ml[2 * tid + 1]);
+    }
 
-    // 7. last arrival combines the splits in split order
-    fence_release();
+    // 7. last arrival merges the splits in split order
+    wait_stores();
+    trace_mark(p, s.marks, 1);
     __syncthreads();
     if (tid == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(&p.arrive[bg], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t old = __hip_atomic_fetch_add(&p.arrive[bg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s.cmd[8] = (old + 1u == (uint32_t)ns) ? 1 : 0;
     }
     __syncthreads();
     const bool last = s.cmd[8] != 0;
     __syncthreads();
     if (!last) return;
-    fence_acquire();
     const float* part0 = p.partials + (int64_t)bg * p.max_splits * rec;
-    for (int i = tid; i < G * D; i += kThreads) {
-        const int hh = i / D;
-        float M = -INFINITY;
-        for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, part0[(int64_t)sp * rec + G * D + 2 * hh]);
-        float num = 0.f, den = 0.f;
-        for (int sp = 0; sp < ns; ++sp) {
-            const float* pr = part0 + (int64_t)sp * rec;
-            const float wgt = __expf(pr[G * D + 2 * hh] - M);
-            den = fmaf(wgt, pr[G * D + 2 * hh + 1], den);
-            num = fmaf(wgt, pr[i], num);
+    const __amdgpu_buffer_rsrc_t prs = make_rsrc(part0, (uint32_t)(ns * rec) * 4u);
+    const int q4 = rec / 4;  // 16-byte chunks per record
+    // running (M, num, den) per output element, merged split by split:
+    //   M' = max(M, m_s); num = num e^{M-M'} + acc_s e^{m_s-M'}; den likewise with l_s
+    float M[4], num[4], den[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        M[k] = -INFINITY;
+        num[k] = 0.f;
+        den[k] = 0.f;
+    }
+    for (int c0 = 0; c0 < ns; c0 += kCmbSplits) {
+        const int nc = min(kCmbSplits, ns - c0);
+        for (int i = tid; i < nc * q4; i += kThreads) {
+            const uint4 v = buf_load16_co(prs, (uint32_t)((c0 * q4 + i) * 16), 0);
+            *(uint4*)(s.cmb + i * 4) = v;
         }
-        out[i] = num / den;
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int i = tid + k * kThreads;
+            if (i >= G * D) continue;
+            const int hh = i / D;
+            for (int sp = 0; sp < nc; ++sp) {
+                const float* r = s.cmb + sp * rec;
+                const float ms = r[G * D + hh], ls = r[G * D + 8 + hh], as = r[i];
+                const float Mn = fmaxf(M[k], ms);
+                const float co = __expf(M[k] - Mn), cn = __expf(ms - Mn);
+                num[k] = num[k] * co + as * cn;
+                den[k] = den[k] * co + ls * cn;
+                M[k] = Mn;
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int i = tid + k * kThreads;
+        if (i < G * D) st_co(&out[i], num[k] / den[k]);
     }
     if (tid == 0) __hip_atomic_store(&p.arrive[bg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (p.persistent) signal_event(p, ev_attn(l), s);

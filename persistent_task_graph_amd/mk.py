@@ -23,13 +23,15 @@ MK_ERR_TOKEN, MK_ERR_KV_OVERFLOW, MK_ERR_TIMEOUT = 1, 2, 4
 OP_QKV, OP_O, OP_GATEUP, OP_DOWN, OP_LM, OP_ATTN, OP_EMBED = 1, 2, 3, 4, 5, 6, 7
 
 EXPORTS = ["mk_build_graph", "mk_destroy_plan", "mk_last_error", "mk_plan_query", "mk_decode_step",
-           "mk_decode_step_hidden", "mk_get_device_error", "mk_argmax", "mk_plan_verify", "mk_plan_dry_run"]
+           "mk_decode_step_hidden", "mk_get_device_error", "mk_argmax", "mk_plan_verify", "mk_plan_dry_run",
+           "mk_plan_trace"]
 
 
 class ExecOpts(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("mode", "workers", "sched_wgs", "jit", "kv_chunk", "watchdog_ms",
-                                               "host_only", "device_cus", "debug_event", "debug_extra_required")] + \
-               [("reserved", ctypes.c_int32 * 6)]
+                                               "host_only", "device_cus", "debug_event", "debug_extra_required",
+                                               "trace")] + \
+               [("reserved", ctypes.c_int32 * 5)]
 
 
 class ModelDesc(ctypes.Structure):
@@ -55,6 +57,11 @@ class Weights(ctypes.Structure):
 class KVCache(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("layer_stride", ctypes.c_int64),
                 ("block_table", ctypes.c_void_p)]
+
+
+class TraceRec(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("kind", "id", "worker", "op")] + \
+               [(n, ctypes.c_uint64) for n in ("t_wait", "t_ready", "t_done", "t_a", "t_b")]
 
 
 class PlanInfo(ctypes.Structure):
@@ -93,8 +100,9 @@ def lib() -> ctypes.CDLL:
         L.mk_argmax.argtypes = [vp, vp, vp, vp]
         L.mk_plan_verify.argtypes = [vp]
         L.mk_plan_dry_run.argtypes = [vp, i32, ctypes.c_uint64, i32, i32, vp]
+        L.mk_plan_trace.argtypes = [vp, vp, ctypes.c_int64, vp]
         for f in ("mk_plan_query", "mk_decode_step", "mk_decode_step_hidden", "mk_get_device_error", "mk_argmax",
-                  "mk_plan_verify", "mk_plan_dry_run"):
+                  "mk_plan_verify", "mk_plan_dry_run", "mk_plan_trace"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -204,6 +212,17 @@ class Plan:
 
     def device_error(self, stream=None) -> int:
         return _check(lib().mk_get_device_error(self._h, _stream(stream)), "mk_get_device_error")
+
+    def trace(self, max_records: int = 1 << 20, stream=None):
+        """Task trace of the last persistent step as a numpy structured array."""
+        import numpy as np
+
+        buf = (TraceRec * max_records)()
+        n = _check(lib().mk_plan_trace(self._h, ctypes.cast(buf, ctypes.c_void_p), max_records, _stream(stream)),
+                   "mk_plan_trace")
+        dt = np.dtype([("kind", "<i4"), ("id", "<i4"), ("worker", "<i4"), ("op", "<i4"), ("t_wait", "<u8"),
+                       ("t_ready", "<u8"), ("t_done", "<u8"), ("t_a", "<u8"), ("t_b", "<u8")])
+        return np.frombuffer(bytes(buf)[: n * ctypes.sizeof(TraceRec)], dtype=dt).copy()
 
     def argmax(self, logits, out_tokens, stream=None) -> None:
         _check(lib().mk_argmax(self._h, _ptr(logits), _ptr(out_tokens), _stream(stream)), "mk_argmax")

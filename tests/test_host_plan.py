@@ -26,7 +26,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     hdr = open(os.path.join(ROOT, "include", "mk.h")).read()
-    declared = set(re.findall(r"\b(mk_[a-z_]+)\s*\(", hdr))
+    declared = set(re.findall(r"^(?:int|void|const char\*|mk_plan\*)\s+(mk_[a-z_]+)\s*\(", hdr, re.M))
     assert set(mk.EXPORTS) == declared
     for name in declared:
         assert hasattr(lib, name), name
