@@ -74,6 +74,11 @@ enum mk_device_error {
  *  device_cus    CU count to plan for when host_only (default 256).
  *  debug_extra_required  for fault tests: adds this many to the required
  *                count of event `debug_event` so its waiters time out.
+ *  prefetch_kb   KB of the next GEMV task's weights each worker pulls into
+ *                L2 before that task's event fires (default 64; -1 = off).
+ *  lds_stream    1: at batch 1 with bf16 weights, the persistent kernel streams
+ *                weight pages through a per-wave LDS ring filled by
+ *                direct-to-LDS buffer loads (experimental; same results).
  *  trace         records per worker kept by the in-kernel task trace (0 =
  *                off). Each record holds the task, the worker, and the
  *                real-time-clock ticks (100 MHz) at wait start, ready and
@@ -91,7 +96,9 @@ typedef struct mk_exec_opts {
     int32_t debug_event;
     int32_t debug_extra_required;
     int32_t trace;
-    int32_t reserved[5];
+    int32_t prefetch_kb;
+    int32_t lds_stream;
+    int32_t reserved[3];
 } mk_exec_opts;
 
 /*

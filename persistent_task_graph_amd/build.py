@@ -19,7 +19,8 @@ ARCH = os.environ.get("MK_OFFLOAD_ARCH", "gfx950")
 # (weight type, batch tile) so the instantiations build in parallel
 UNITS = [("runtime.hip", []), ("plan.cpp", [])] + \
     [("kernels.hip", ["-DMK_WT_BF16", "-DMK_NB=%d" % nb]) for nb in (1, 2, 4, 8, 16)] + \
-    [("kernels.hip", ["-DMK_WT_F32", "-DMK_NB=%d" % nb]) for nb in (1, 2, 4)]
+    [("kernels.hip", ["-DMK_WT_F32", "-DMK_NB=%d" % nb]) for nb in (1, 2, 4)] + \
+    [("kernels.hip", ["-DMK_WT_BF16", "-DMK_NB=1", "-DMK_LDS_STREAM"])]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

@@ -11,7 +11,7 @@ namespace mk {
 
 using bf16_t = uint16_t;
 
-constexpr int kThreads = 256;  // one workgroup = 4 wave64
+constexpr int kThreads = 256;  // one workgroup = 4 wave64 (one per SIMD)
 constexpr int kWaves = kThreads / 64;
 
 // Per-layer weight pointers (same layout as mk_layer_weights).
@@ -71,6 +71,7 @@ struct KParams {
     int n_elig;
     int mb_mask;
     uint64_t watchdog_ticks;  // 100 MHz ticks
+    int prefetch_kb;          // next-task weight bytes pulled into L2 per worker (KB)
     // optional task trace: per worker `trace_cap` records, count in trace_n
     mk_trace_rec* trace;
     int32_t* trace_n;

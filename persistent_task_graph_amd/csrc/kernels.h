@@ -8,6 +8,7 @@ enum KernelKind { KK_PERSISTENT = 0, KK_LEVEL_GEMV = 1, KK_LEVEL_ATTN = 2 };
 
 extern "C" {
 void* mk_kernels_bf16_1(int kind);
+void* mk_kernels_bf16_1s(int kind);
 void* mk_kernels_bf16_2(int kind);
 void* mk_kernels_bf16_4(int kind);
 void* mk_kernels_bf16_8(int kind);

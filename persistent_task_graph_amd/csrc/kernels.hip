@@ -1,5 +1,6 @@
 // One instantiation unit of the device kernels: compiled once per weight
-// type (MK_WT_BF16 or MK_WT_F32) and batch tile MK_NB.
+// type (MK_WT_BF16 or MK_WT_F32) and batch tile MK_NB; MK_LDS_STREAM selects
+// the batch-1 variant that streams weights through an LDS page ring.
 #include "megakernel.h"
 #include "kernels.h"
 
@@ -17,7 +18,12 @@
 #endif
 
 #define MK_CAT3(a, b, c) a##b##_##c
+#define MK_CAT4(a, b, c, d) a##b##_##c##d
+#ifdef MK_LDS_STREAM
+#define MK_NAME(tag, nb) MK_CAT4(mk_kernels_, tag, nb, s)
+#else
 #define MK_NAME(tag, nb) MK_CAT3(mk_kernels_, tag, nb)
+#endif
 
 extern "C" void* MK_NAME(MK_TAG, MK_NB)(int kind) {
     switch (kind) {

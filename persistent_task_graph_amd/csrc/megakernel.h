@@ -3,7 +3,15 @@
 // tile) so the instantiations build in parallel.
 #pragma once
 
-#include "tasks.h"
+#include "stream.h"
+
+namespace mk {
+#ifdef MK_LDS_STREAM
+constexpr bool kLdsStream = true;
+#else
+constexpr bool kLdsStream = false;
+#endif
+}  // namespace mk
 
 namespace mk {
 namespace {  // kernels get internal linkage: each instantiation unit registers its own
@@ -123,15 +131,28 @@ __device__ __forceinline__ void trace_put(const KParams& p, const Lds& s, int ki
 }
 
 template <typename WT, int NB>
-__device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s) {
+__device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s, uint4* ring_mem) {
     const int w = blockIdx.x;
     const int qb = p.qoff[w], qe = p.qoff[w + 1];
     const uint32_t ep1 = p.epoch + 1u;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     if (p.trace && threadIdx.x == 0) {
         p.trace_n[w] = 0;
         s.marks[0] = s.marks[1] = 0;
     }
     int64_t head = (threadIdx.x == 0 && p.jit_on) ? p.inbox_head[w] : 0;
+    // optional batch-1 variant: weight pages stream through a per-wave LDS
+    // ring fed by direct-to-LDS loads (stream.h) instead of registers
+    constexpr bool kStream = kLdsStream && NB == 1;
+    Stream st;
+    const uint4* ring = ring_mem + wave * kRingPages * 64;
+    if constexpr (kStream) {
+        st.issued = st.consumed = 0;
+        st.ldone = false;
+        st.ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)ring;
+        loader_seek<WT>(p, st, qb, qe, wave);
+        loader_fill<WT>(p, st, 0, qe, wave, lane);
+    }
     for (int qi = qb; qi < qe; ++qi) {
         const int tid_task = p.queue[qi];
         const TaskRec t = p.tasks[tid_task];
@@ -166,6 +187,7 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s) {
                 if (cmd == 0) break;
                 if (cmd == 3) {
                     if (threadIdx.x == 0 && p.jit_on) p.inbox_head[w] = head;
+                    if constexpr (kStream) wait_vm<0>();
                     return;
                 }
                 if (cmd == 1) {
@@ -182,12 +204,20 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s) {
         if (t.op == OP_ATTN) {
             attention_task<WT>(p, t.layer, t.a0, t.a1, s);
         } else {
-            run_gemv_task<WT, NB>(p, t, s);
+            if constexpr (kStream) {
+                if (is_streamed(t.op)) run_stream_task<WT>(p, st, ring, qe, t, s);
+                else if (t.op == OP_EMBED) embed_task<WT>(p, t);
+            } else {
+                run_gemv_task<WT, NB>(p, t, s);
+            }
             signal_event(p, t.sig_ev, s);
         }
+        if constexpr (!kStream)
+            if (qi + 1 < qe) prefetch_task<WT>(p, p.tasks[p.queue[qi + 1]]);
         trace_put(p, s, 0, tid_task, t.op, tw, tr);
     }
     if (threadIdx.x == 0 && p.jit_on) p.inbox_head[w] = head;
+    if constexpr (kStream) wait_vm<0>();
 }
 
 extern __shared__ float mk_dyn_lds[];
@@ -196,10 +226,16 @@ template <typename WT, int NB>
 __global__ __launch_bounds__(kThreads) void k_persistent(KParams p) {
     const Lds s = carve_lds(mk_dyn_lds, p.Hq / p.Hkv, p.chunk);
     if ((int)blockIdx.x >= p.n_workers) {
-        if (p.jit_on) scheduler_wave(p);
+        // four scheduler waves per scheduler workgroup
+        if (p.jit_on && (threadIdx.x >> 6) < 4) scheduler_wave(p);
         return;
     }
-    worker_loop<WT, NB>(p, s);
+    if constexpr (kLdsStream && NB == 1) {
+        __shared__ __attribute__((aligned(1024))) uint4 ring_mem[kWaves * kRingPages * 64];
+        worker_loop<WT, NB>(p, s, ring_mem);
+    } else {
+        worker_loop<WT, NB>(p, s, nullptr);
+    }
 }
 
 template <typename WT, int NB>

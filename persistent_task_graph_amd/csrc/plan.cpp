@@ -85,6 +85,7 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
     if (p.workers < 1 || p.workers + p.sched_wgs > device_cus)
         return fail(err, "workers + sched_wgs must be in [2, CU count] (one workgroup per CU)");
     if (o.jit < 0 || o.jit > 2) return fail(err, "opts.jit must be 0, 1 or 2");
+    if (o.lds_stream < 0 || o.lds_stream > 1) return fail(err, "opts.lds_stream must be 0 or 1");
     p.jit = (o.jit == 2) ? 0 : 1;
     p.kv_chunk = o.kv_chunk > 0 ? o.kv_chunk : 128;
     if (p.kv_chunk % 16 || p.kv_chunk > 4096) return fail(err, "kv_chunk must be a multiple of 16, at most 4096");

@@ -153,7 +153,7 @@ void* kernel_for(const mk_plan* pl, int kind) {
     const int nb = nb_for(pl->hp.desc.batch);
     if (pl->hp.desc.weight_dtype == MK_BF16) {
         switch (nb) {
-            case 1: return mk_kernels_bf16_1(kind);
+            case 1: return pl->hp.desc.opts.lds_stream == 1 ? mk_kernels_bf16_1s(kind) : mk_kernels_bf16_1(kind);
             case 2: return mk_kernels_bf16_2(kind);
             case 4: return mk_kernels_bf16_4(kind);
             case 8: return mk_kernels_bf16_8(kind);
@@ -271,7 +271,10 @@ bool upload_plan(mk_plan* pl) {
     if (!hip_ok(hipHostMalloc((void**)&pl->h_lw_pinned, sizeof(LayerPtrs) * L, hipHostMallocDefault), "hipHostMalloc"))
         return false;
     pl->lds_bytes = lds_bytes_for(G, hp.kv_chunk);
-    pl->lds_bytes_persistent = std::max(pl->lds_bytes, 82 * 1024);  // > half the CU's LDS: one workgroup per CU
+    // one workgroup per CU: the LDS-ring variant's static page ring already
+    // takes more than half of the CU's LDS; other kernels reserve it dynamically
+    const bool ring = nb_for(d.batch) == 1 && d.weight_dtype == MK_BF16 && d.opts.lds_stream == 1;
+    pl->lds_bytes_persistent = ring ? pl->lds_bytes : std::max(pl->lds_bytes, 82 * 1024);
     if (pl->lds_bytes_persistent > 160 * 1024) {
         set_err("LDS need exceeds 160 KB (reduce kv_chunk)");
         return false;
@@ -374,6 +377,7 @@ KParams make_params(const mk_plan* pl, const mk_weights* w, const mk_kv_cache* k
     p.mb_mask = hp.mb_cap - 1;
     const int wd = d.opts.watchdog_ms > 0 ? d.opts.watchdog_ms : 2000;
     p.watchdog_ticks = (uint64_t)wd * 100000ull;
+    p.prefetch_kb = d.opts.prefetch_kb == 0 ? 64 : (d.opts.prefetch_kb < 0 ? 0 : d.opts.prefetch_kb);
     p.trace = pl->d_trace;
     p.trace_n = pl->d_trace_n;
     p.trace_cap = pl->trace_cap;
@@ -513,7 +517,7 @@ int mk_plan_query(const mk_plan* pl, mk_plan_info* info) {
     const HostPlan& hp = pl->hp;
     std::memset(info, 0, sizeof(*info));
     info->workers = hp.workers;
-    info->sched_waves = hp.sched_wgs * kWaves;
+    info->sched_waves = hp.sched_wgs * 4;
     info->n_aot_tasks = (int32_t)hp.tasks.size();
     info->n_events = (int32_t)hp.events.size();
     info->n_levels = hp.n_levels;

@@ -12,10 +12,10 @@ namespace mk {
 // ---------------------------------------------------------------- LDS layout
 // Carved from one dynamic shared buffer; sizes in floats.
 struct Lds {
-    float* red;   // 64: reductions / broadcast
+    float* red;   // kWaves * 16: reductions / broadcast
     int* cmd;     // 16 ints
     float* rstd;  // 16
-    float* part;  // kWaves * 256 * 4: GEMV cross-wave partial sums (2 matrices x 2 rows)
+    float* part;  // kPartFloats: GEMV cross-wave partial sums
     float* q;     // 8 * 128: rotated query heads of one KV group
     float* kn;    // 2 * 128: new k, v (rounded to the cache type)
     float* p;     // G * chunk: scores, then probabilities
@@ -25,20 +25,21 @@ struct Lds {
     uint64_t* marks;  // 2 trace phase marks
 };
 
-constexpr int kCmbSplits = 8;  // splits merged per staged chunk
+constexpr int kCmbSplits = 4;  // splits merged per staged chunk
+constexpr int kPartFloats = 4096;  // GEMV cross-wave partial sums
 __host__ __device__ constexpr int lds_floats_fixed() {
-    return 64 + 16 + 16 + 4 + kWaves * 256 * 4 + 8 * 128 + 2 * 128 + kWaves * 8 * 128 + 16 + kCmbSplits * (8 * 128 + 16);
+    return kWaves * 16 + 16 + 16 + 4 + kPartFloats + 8 * 128 + 2 * 128 + kWaves * 8 * 128 + 16 + kCmbSplits * (8 * 128 + 16);
 }
 __host__ __device__ inline int lds_bytes_for(int G, int chunk) { return 4 * (lds_floats_fixed() + G * chunk); }
 
 __device__ __forceinline__ Lds carve_lds(float* base, int G, int chunk) {
     Lds s;
     float* p = base;
-    s.red = p; p += 64;
+    s.red = p; p += kWaves * 16;
     s.cmd = (int*)p; p += 16;
     s.marks = (uint64_t*)p; p += 4;
     s.rstd = p; p += 16;
-    s.part = p; p += kWaves * 256 * 4;
+    s.part = p; p += kPartFloats;
     s.q = p; p += 8 * 128;
     s.kn = p; p += 2 * 128;
     s.acc = p; p += kWaves * 8 * 128;
@@ -120,7 +121,7 @@ __device__ __forceinline__ void gemv_ksplit(int r0, int r1, int K, const float* 
         kvalid[j] = wave + kWaves * j < nseg && k < K;
         voff[j] = kvalid[j] ? (uint32_t)k * (uint32_t)sizeof(WT) : kOOB;
     }
-    constexpr int WIN = 4096 / (kWaves * NM * NB);  // rows per LDS window
+    constexpr int WIN = kPartFloats / (kWaves * NM * NB);  // rows per LDS window
     auto load = [&](uint4 (&w)[U][NM][NSW], int r, int rend) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -320,10 +321,11 @@ __device__ __forceinline__ void gemv_dispatch(int r0, int r1, int K, const float
         constexpr int SEG = 64 * Vec16<WT>::N;
         constexpr int D2 = DUAL ? 2 : 1;
         const int nsw = ((K + SEG - 1) / SEG + kWaves - 1) / kWaves;
-        // rows per group so that one buffer holds at most 16 16-byte loads
+        // rows per group so that one buffer holds about 16 16-byte loads
         // per lane: two buffers then fit in 128 VGPRs
         if (nsw <= 1) gemv_ksplit<WT, NB, 1, 16 / D2, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr);
         else if (nsw <= 2) gemv_ksplit<WT, NB, 2, 8 / D2, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr);
+        else if (nsw <= 3) gemv_ksplit<WT, NB, 3, 5 / D2, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr);
         else if (nsw <= 4) gemv_ksplit<WT, NB, 4, 4 / D2, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr);
         else if (nsw <= 6) gemv_ksplit<WT, NB, 6, 2 / D2, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr);
         else gemv_ksplit<WT, NB, 8, 2 / D2, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr);
@@ -354,25 +356,29 @@ struct MatTile {
 
 // ---------------------------------------------------------------- GEMV tasks
 
+// x_0[b, r] = E[token_b, r] for rows [a0, a1) (token ids outside the
+// vocabulary raise MK_ERR_TOKEN and read row 0)
+template <typename WT>
+__device__ __forceinline__ void embed_task(const KParams& p, const TaskRec& t) {
+    const WT* E = (const WT*)p.embed;
+    const int H = p.H, B = p.B, r0 = t.a0, n = t.a1 - t.a0;
+    for (int i = threadIdx.x; i < n * B; i += kThreads) {
+        const int b = i / n, r = r0 + i % n;
+        int tok = p.tokens[b];
+        if (tok < 0 || tok >= p.V) {
+            if (r == r0) raise_error(p.ctrl, MK_ERR_TOKEN);
+            tok = 0;
+        }
+        st_co(&p.x0_w[(int64_t)b * H + r], load_scalar<WT>(E, (int64_t)tok * H + r));
+    }
+}
+
 template <typename WT, int NB>
 __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t, const Lds& s) {
     const int l = t.layer, B = p.B, H = p.H;
     const int r0 = t.a0, r1 = t.a1;
     switch (t.op) {
-        case OP_EMBED: {
-            const WT* E = (const WT*)p.embed;
-            const int n = r1 - r0;
-            for (int i = threadIdx.x; i < n * B; i += kThreads) {
-                const int b = i / n, r = r0 + i % n;
-                int tok = p.tokens[b];
-                if (tok < 0 || tok >= p.V) {
-                    if (r == r0) raise_error(p.ctrl, MK_ERR_TOKEN);
-                    tok = 0;
-                }
-                st_co(&p.x0_w[(int64_t)b * H + r], load_scalar<WT>(E, (int64_t)tok * H + r));
-            }
-            break;
-        }
+        case OP_EMBED: embed_task<WT>(p, t); break;
         case OP_QKV: {
             const LayerPtrs w = p.lw[l];
             const float* x = layer_in(p, l);
@@ -479,6 +485,51 @@ __device__ __forceinline__ void signal_event(const KParams& p, int e, const Lds&
     (void)s;
 }
 
+// ---------------------------------------------------------------- next-task prefetch
+// The weights are static, so the next GEMV task's leading rows can be
+// fetched before its event fires (the MPK article's preload phase, §3.2):
+// waves 1..3 issue direct-to-LDS loads of up to `kb` KB of them into a
+// scratch LDS slot that is never read. The lines land in this XCD's L2,
+// keeping HBM busy across the level boundary; the task body's own loads
+// then hit L2. Wave 0 (which polls the next event) issues nothing.
+__shared__ __attribute__((aligned(16))) uint4 mk_prefetch_sink[kWaves][64];
+
+__device__ __forceinline__ void prefetch_rows(const void* m, int K, int es, int rows, int r0, int r1, int kb, int wave,
+                                              int lane) {
+    r0 = max(0, min(r0, rows));
+    r1 = max(r0, min(r1, rows));
+    const uint32_t bytes = (uint32_t)(r1 - r0) * (uint32_t)K * (uint32_t)es;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc((const char*)m + (int64_t)r0 * K * es, bytes);
+    const uint32_t n = min(bytes, (uint32_t)kb * 1024u) / 1024u;
+    for (uint32_t i = (uint32_t)(wave - 1); i < n; i += kWaves - 1)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)&mk_prefetch_sink[wave][0], 16,
+                                                 lane * 16, i * 1024u, 0, 0);
+}
+
+template <typename WT>
+__device__ __forceinline__ void prefetch_task(const KParams& p, const TaskRec& t) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (wave == 0 || p.prefetch_kb <= 0) return;
+    const int es = (int)sizeof(WT), l = t.layer, H = p.H, kb = p.prefetch_kb;
+    switch (t.op) {
+        case OP_QKV: {
+            const LayerPtrs& w = p.lw[l];
+            if (t.a0 < p.QD) prefetch_rows(w.wq, H, es, p.QD, t.a0, t.a1, kb, wave, lane);
+            else if (t.a0 < p.QD + p.KD) prefetch_rows(w.wk, H, es, p.KD, t.a0 - p.QD, t.a1 - p.QD, kb, wave, lane);
+            else prefetch_rows(w.wv, H, es, p.KD, t.a0 - p.QD - p.KD, t.a1 - p.QD - p.KD, kb, wave, lane);
+            break;
+        }
+        case OP_O: prefetch_rows(p.lw[l].wo, p.QD, es, H, t.a0, t.a1, kb, wave, lane); break;
+        case OP_GATEUP:
+            prefetch_rows(p.lw[l].w_gate, H, es, p.F, t.a0, t.a1, kb / 2, wave, lane);
+            prefetch_rows(p.lw[l].w_up, H, es, p.F, t.a0, t.a1, kb / 2, wave, lane);
+            break;
+        case OP_DOWN: prefetch_rows(p.lw[l].w_down, p.F, es, H, t.a0, t.a1, kb, wave, lane); break;
+        case OP_LM: prefetch_rows(p.lm_head, H, es, p.V, t.a0, t.a1, kb, wave, lane); break;
+        default: break;
+    }
+}
+
 // ---------------------------------------------------------------- attention
 
 __device__ __forceinline__ int64_t kv_offset(const KParams& p, int l, int b, int g, int pos) {
@@ -554,24 +605,57 @@ __device__ __forceinline__ void attention_task(const KParams& p, int l, int bg, 
     // before anything else (it depends on nothing computed here).
     using VK = Vec16<WT>;
     constexpr int E = VK::N;
-    constexpr int NIT = 8;
+    constexpr int NIT = 32 / kWaves > 0 ? 32 / kWaves : 1;  // workgroup iterations per batch
     const int lpr = D / E;            // lanes per K row
     const int ppw = 64 / lpr;         // rows per wave per load
     const int per_it = kWaves * ppw;  // rows per workgroup iteration
     const int sub = per_it * NIT;     // rows per batch
     const int rr = lane / lpr, cc = lane % lpr;
-    const WT* kbase = (const WT*)p.kv_k;
-    const WT* vbase = (const WT*)p.kv_v;
-    const uint4 z4 = make_uint4(0, 0, 0, 0);
-    uint4 kr[NIT], vr[NIT];
+    // K/V of this (layer, b, g) through buffer resources; row jj of the split
+    // at byte row_off(jj); rows past the split (or the new row, which comes
+    // from LDS) load through an out-of-range offset: no branches around loads
+    const int es = (int)sizeof(WT);
+    const int64_t lbase = (int64_t)l * p.kv_layer_stride;
+    __amdgpu_buffer_rsrc_t krs, vrs;
+    if (!p.paged) {
+        const int64_t seq = lbase + (int64_t)(b * Hkv + g) * p.cap * D;
+        krs = make_rsrc((const WT*)p.kv_k + seq, (uint32_t)p.cap * (uint32_t)(D * es));
+        vrs = make_rsrc((const WT*)p.kv_v + seq, (uint32_t)p.cap * (uint32_t)(D * es));
+    } else {
+        krs = make_rsrc((const WT*)p.kv_k + lbase, (uint32_t)(p.kv_layer_stride * es));
+        vrs = make_rsrc((const WT*)p.kv_v + lbase, (uint32_t)(p.kv_layer_stride * es));
+    }
+    const int32_t* btab = p.paged ? p.block_table + (int64_t)b * p.max_blocks : nullptr;
+    // byte offsets of this lane's 16 bytes for NIT rows starting at `base`
+    auto row_offsets = [&](int base, uint32_t (&ro)[NIT]) {
+        int blk[NIT];
+        if (p.paged) {
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-        const int j = it * per_it + wave * ppw + rr;
-        const int jj = j0 + j;
-        const bool ld = j < n && jj != pos;
-        const int64_t off = ld ? kv_offset(p, l, b, g, jj) + cc * E : 0;
-        kr[it] = ld ? *(const uint4*)(kbase + off) : z4;
-        vr[it] = ld ? *(const uint4*)(vbase + off) : z4;
+            for (int it = 0; it < NIT; ++it) {
+                const int j = base + it * per_it + wave * ppw + rr;
+                blk[it] = j < n ? btab[(j0 + j) / p.kv_block] : 0;
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int j = base + it * per_it + wave * ppw + rr;
+            const int jj = j0 + j;
+            uint32_t o;
+            if (p.paged) o = (uint32_t)(((blk[it] * Hkv + g) * p.kv_block + jj % p.kv_block) * D * es);
+            else o = (uint32_t)(jj * D * es);
+            ro[it] = (j < n && jj != pos) ? o + (uint32_t)(cc * 16) : kOOB;
+        }
+    };
+    uint4 kr[NIT], vr[NIT];
+    {
+        uint32_t ro[NIT];
+        row_offsets(0, ro);
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            kr[it] = buf_load16(krs, ro[it], 0);
+            vr[it] = buf_load16(vrs, ro[it], 0);
+        }
+        asm volatile("" ::: "memory");  // keep the bulk loads ahead of the small ones below
     }
 
     // 1. query heads of this group: norm + RoPE into LDS
@@ -611,13 +695,10 @@ __device__ __forceinline__ void attention_task(const KParams& p, int l, int bg, 
         for (int e = 0; e < E; ++e) qreg[hh][e] = hh < G ? s.q[hh * D + cc * E + e] : 0.f;
     for (int base = 0; base < n; base += sub) {
         if (base > 0) {
+            uint32_t ro[NIT];
+            row_offsets(base, ro);
 #pragma unroll
-            for (int it = 0; it < NIT; ++it) {
-                const int j = base + it * per_it + wave * ppw + rr;
-                const int jj = j0 + j;
-                const bool ld = j < n && jj != pos;
-                kr[it] = ld ? *(const uint4*)(kbase + (ld ? kv_offset(p, l, b, g, jj) + cc * E : 0)) : z4;
-            }
+            for (int it = 0; it < NIT; ++it) kr[it] = buf_load16(krs, ro[it], 0);
         }
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
@@ -670,13 +751,10 @@ __device__ __forceinline__ void attention_task(const KParams& p, int l, int bg, 
         for (int e = 0; e < E; ++e) acc[hh][e] = 0.f;
     for (int base = 0; base < n; base += sub) {
         if (base > 0) {
+            uint32_t ro[NIT];
+            row_offsets(base, ro);
 #pragma unroll
-            for (int it = 0; it < NIT; ++it) {
-                const int j = base + it * per_it + wave * ppw + rr;
-                const int jj = j0 + j;
-                const bool ld = j < n && jj != pos;
-                vr[it] = ld ? *(const uint4*)(vbase + (ld ? kv_offset(p, l, b, g, jj) + cc * E : 0)) : z4;
-            }
+            for (int it = 0; it < NIT; ++it) vr[it] = buf_load16(vrs, ro[it], 0);
         }
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {

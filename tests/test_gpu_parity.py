@@ -145,6 +145,17 @@ def test_mid_modes_bitwise(mid_weights):
         _bitwise(a, o)
 
 
+def test_mid_b1_variants_bitwise(mid_weights):
+    log("mid bf16 B=1: register GEMV vs LDS-ring streaming vs kernel-per-op vs no prefetch")
+    s = make_setup(MID, 1, [517], 540, weights=mid_weights)
+    a, _ = _logits_seq(s, 3)
+    b, _ = _logits_seq(s, 3, lds_stream=1)
+    c, _ = _logits_seq(s, 3, mode=1)
+    d, _ = _logits_seq(s, 3, prefetch_kb=-1)
+    for o in (b, c, d):
+        _bitwise(a, o)
+
+
 def test_mid_paged_equals_contiguous(mid_weights):
     log("mid bf16: paged (identity and permuted tables) vs contiguous, B=4")
     B, lens, cap = 4, [17, 250, 64, 129], 300
