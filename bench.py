@@ -27,6 +27,38 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "persistent_decode_q8b_b1_hbm_traffic.md")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the device sources (name + bytes, sorted by name)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "persistent_task_graph_amd", "csrc")
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".h", ".hip", ".cpp")):
+            h.update(name.encode())
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the batch-1 megakernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when that summary is
+    missing or was taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            kv = dict(l.split(":", 1) for l in f.read().splitlines() if l.startswith(("source_sha256:", "traffic_bytes_per_launch:")))
+    except OSError:
+        return None
+    if kv.get("source_sha256", "").strip() != kernel_source_hash():
+        return None
+    try:
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def log(*a):
@@ -48,6 +80,9 @@ def parse():
     ap.add_argument("--kv-chunk", type=int, default=0)
     ap.add_argument("--workers", type=int, default=0)
     ap.add_argument("--quick", action="store_true", help="tiny prompt, few steps (profiling runs)")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                    help="run one plain elementwise copy (torch.neg) of MIB MiB of fp32 first, untimed: the "
+                         "known-size kernel that scales the FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
 
 
@@ -66,6 +101,14 @@ def main():
 
     torch.cuda.set_device(0)
     dev = "cuda"
+    if args.copy_calib > 0:
+        n = args.copy_calib * (1 << 20) // 4
+        xs = torch.ones(n, dtype=torch.float32, device=dev)
+        ys = torch.empty_like(xs)
+        torch.cuda.synchronize()
+        torch.neg(xs, out=ys)
+        torch.cuda.synchronize()
+        del xs, ys
     shape = synth.Q8B
     wl = synth.WORKLOADS["q8b_b1"]
     t0 = time.time()
@@ -162,7 +205,7 @@ def main():
                       "p99": round(float(np.percentile(k_ms, 99)), 4)},
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(),
             "kernel": "persistent decode-step megakernel (one launch per step)",
             "bytes_per_launch": int(avg_bytes),
         },
