@@ -138,16 +138,50 @@ __device__ __forceinline__ bf16_t from_float<bf16_t>(float f) { return f32_to_bf
 template <>
 __device__ __forceinline__ float from_float<float>(float f) { return f; }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+// ---------------------------------------------------------------- lane reductions
+// Sums and maxima over aligned groups of N lanes through DPP lane selects,
+// which stay inside the VALU (no LDS crossbar round trip): two quad_perm
+// swaps reduce groups of 4, the half-row mirror (lane i <-> 7 - i) and the
+// row mirror (i <-> 15 - i) extend that to 8 and 16 lanes. The four rows of
+// a wave meet through readlane. The pairing is symmetric, so every lane of
+// a group ends with the bitwise-same value. Call with all lanes active.
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror
+constexpr int kDppMirror = 0x140;      // row_mirror
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_sel(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float read_lane(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group size");
+    if constexpr (N >= 2) v += dpp_sel<kDppXor1>(v);
+    if constexpr (N >= 4) v += dpp_sel<kDppXor2>(v);
+    if constexpr (N >= 8) v += dpp_sel<kDppHalfMirror>(v);
+    if constexpr (N >= 16) v += dpp_sel<kDppMirror>(v);
+    if constexpr (N == 32) v += __shfl_xor(v, 16, 64);
+    if constexpr (N == 64) v = (read_lane(v, 0) + read_lane(v, 16)) + (read_lane(v, 32) + read_lane(v, 48));
     return v;
 }
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+    static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group size");
+    if constexpr (N >= 2) v = fmaxf(v, dpp_sel<kDppXor1>(v));
+    if constexpr (N >= 4) v = fmaxf(v, dpp_sel<kDppXor2>(v));
+    if constexpr (N >= 8) v = fmaxf(v, dpp_sel<kDppHalfMirror>(v));
+    if constexpr (N >= 16) v = fmaxf(v, dpp_sel<kDppMirror>(v));
+    if constexpr (N == 32) v = fmaxf(v, __shfl_xor(v, 16, 64));
+    if constexpr (N == 64) v = fmaxf(fmaxf(read_lane(v, 0), read_lane(v, 16)), fmaxf(read_lane(v, 32), read_lane(v, 48)));
     return v;
 }
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
+__device__ __forceinline__ float wave_max(float v) { return group_max<64>(v); }
 
 // ---------------------------------------------------------------- memory model
 

@@ -157,53 +157,69 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s, uint
         const int tid_task = p.queue[qi];
         const TaskRec t = p.tasks[tid_task];
         const uint64_t tw = p.trace ? now_ticks() : 0;
-        if (t.wait_ev >= 0) {
-            const uint32_t target = p.evrec[t.wait_ev].required * ep1;
-            uint64_t t0 = now_ticks();
-            for (;;) {
+        uint64_t tr = tw;
+        // Wait for the task's event, running JIT attention tasks from this
+        // worker's inbox meanwhile. An AOT attention task runs through the
+        // same call once its event has fired, so the (large) attention body
+        // is expanded at one site only.
+        bool waiting = t.wait_ev >= 0, aot_attn = t.op == OP_ATTN;
+        const uint32_t target = waiting ? p.evrec[t.wait_ev].required * ep1 : 0u;
+        uint64_t t0 = now_ticks();
+        for (;;) {
+            int cmd = 0, jl = t.layer, jbg = t.a0, js = t.a1;
+            if (waiting) {
                 if (threadIdx.x == 0) {
-                    int cmd = 2;
-                    const uint32_t c = ld_relaxed(&p.ev[t.wait_ev]);
-                    if ((int32_t)(c - target) >= 0) cmd = 0;
-                    else if (aborted(p.ctrl)) cmd = 3;
+                    int c = 2;
+                    const uint32_t v = ld_relaxed(&p.ev[t.wait_ev]);
+                    if ((int32_t)(v - target) >= 0) c = 0;
+                    else if (aborted(p.ctrl)) c = 3;
                     else {
-                        int jl, jbg, js;
-                        if (p.jit_on && inbox_try_pop(p, head, jl, jbg, js)) {
-                            cmd = 1;
-                            s.cmd[1] = jl;
-                            s.cmd[2] = jbg;
-                            s.cmd[3] = js;
+                        int a, bb, cc;
+                        if (p.jit_on && inbox_try_pop(p, head, a, bb, cc)) {
+                            c = 1;
+                            s.cmd[1] = a;
+                            s.cmd[2] = bb;
+                            s.cmd[3] = cc;
                         } else if (now_ticks() - t0 > p.watchdog_ticks) {
                             raise_abort(p.ctrl);
-                            cmd = 3;
+                            c = 3;
                         }
                     }
-                    s.cmd[0] = cmd;
+                    s.cmd[0] = c;
                 }
                 __syncthreads();
-                const int cmd = s.cmd[0];
-                const int jl = s.cmd[1], jbg = s.cmd[2], js = s.cmd[3];
+                cmd = s.cmd[0];
+                if (cmd == 1) {
+                    jl = s.cmd[1];
+                    jbg = s.cmd[2];
+                    js = s.cmd[3];
+                }
                 __syncthreads();
-                if (cmd == 0) break;
                 if (cmd == 3) {
                     if (threadIdx.x == 0 && p.jit_on) p.inbox_head[w] = head;
                     if constexpr (kStream) wait_vm<0>();
                     return;
                 }
-                if (cmd == 1) {
-                    const uint64_t tj = p.trace ? now_ticks() : 0;
-                    attention_task<WT>(p, jl, jbg, js, s);
-                    trace_put(p, s, 1, (jl << 24) | ((jbg & 0xFFF) << 12) | (js & 0xFFF), OP_ATTN, tj, tj);
-                    t0 = now_ticks();
-                } else {
+                if (cmd == 2) {
                     __builtin_amdgcn_s_sleep(1);
+                    continue;
+                }
+                if (cmd == 0) {
+                    waiting = false;
+                    if (p.trace) tr = now_ticks();
                 }
             }
+            if (cmd == 0) {
+                if (!aot_attn) break;
+                aot_attn = false;
+            }
+            const uint64_t tj = p.trace ? now_ticks() : 0;
+            attention_task<WT>(p, jl, jbg, js, s);
+            if (cmd == 0) break;  // that was this AOT attention task
+            trace_put(p, s, 1, (jl << 24) | ((jbg & 0xFFF) << 12) | (js & 0xFFF), OP_ATTN, tj, tj);
+            t0 = now_ticks();
         }
-        const uint64_t tr = p.trace ? now_ticks() : 0;
-        if (t.op == OP_ATTN) {
-            attention_task<WT>(p, t.layer, t.a0, t.a1, s);
-        } else {
+        if (t.op != OP_ATTN) {
             if constexpr (kStream) {
                 if (is_streamed(t.op)) run_stream_task<WT>(p, st, ring, qe, t, s);
                 else if (t.op == OP_EMBED) embed_task<WT>(p, t);

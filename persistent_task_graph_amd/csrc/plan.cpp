@@ -89,7 +89,11 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
     p.jit = (o.jit == 2) ? 0 : 1;
     p.kv_chunk = o.kv_chunk > 0 ? o.kv_chunk : 128;
     if (p.kv_chunk % 16 || p.kv_chunk > 4096) return fail(err, "kv_chunk must be a multiple of 16, at most 4096");
-    if (p.kv_chunk * (d.n_heads / d.n_kv_heads) > 16384) return fail(err, "kv_chunk * (n_heads / n_kv_heads) must be <= 16384");
+    {
+        const int G = d.n_heads / d.n_kv_heads, gp = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
+        if (p.kv_chunk * gp > 16384)
+            return fail(err, "kv_chunk * (n_heads / n_kv_heads rounded up to a power of two) must be <= 16384");
+    }
     p.cap = d.max_seq_len;
     p.max_splits = n_splits_for(p.cap, p.kv_chunk);
     if (p.max_splits > 65535) return fail(err, "too many splits per sequence");

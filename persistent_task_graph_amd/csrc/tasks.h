@@ -18,7 +18,7 @@ struct Lds {
     float* part;  // kPartFloats: GEMV cross-wave partial sums
     float* q;     // 8 * 128: rotated query heads of one KV group
     float* kn;    // 2 * 128: new k, v (rounded to the cache type)
-    float* p;     // G * chunk: scores, then probabilities
+    float* p;     // GP * chunk: scores, then probabilities (GP = G rounded up to 1, 2, 4 or 8)
     float* acc;   // kWaves * 8 * 128: P.V partials per wave
     float* ml;    // 2 * 8: (m, l) per head
     float* cmb;   // kCmbSplits * (8 * 128 + 16): partials staged for the combine
@@ -30,7 +30,10 @@ constexpr int kPartFloats = 4096;  // GEMV cross-wave partial sums
 __host__ __device__ constexpr int lds_floats_fixed() {
     return kWaves * 16 + 16 + 16 + 4 + kPartFloats + 8 * 128 + 2 * 128 + kWaves * 8 * 128 + 16 + kCmbSplits * (8 * 128 + 16);
 }
-__host__ __device__ inline int lds_bytes_for(int G, int chunk) { return 4 * (lds_floats_fixed() + G * chunk); }
+__host__ __device__ inline int lds_bytes_for(int G, int chunk) {
+    const int gp = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
+    return 4 * (lds_floats_fixed() + gp * chunk);
+}
 
 __device__ __forceinline__ Lds carve_lds(float* base, int G, int chunk) {
     Lds s;
@@ -540,18 +543,20 @@ __device__ __forceinline__ int64_t kv_offset(const KParams& p, int l, int b, int
 
 // RMSNorm over one head (D = 64 or 128) held by a wave as D/64 values per
 // lane (element j in lane j % 64, slot j / 64), then rotate-half RoPE.
-template <typename WT>
-__device__ __forceinline__ void head_norm_rope(float* v, int D, const WT* gain, bool norm, float eps, const float2* rope_row) {
+template <typename WT, int D>
+__device__ __forceinline__ void head_norm_rope(float (&v)[2], const WT* gain, bool norm, float eps, const float2* rope_row) {
     const int lane = threadIdx.x & 63;
-    const int per = D / 64;
+    constexpr int per = D / 64;
     if (norm) {
         float ss = 0.f;
+#pragma unroll
         for (int i = 0; i < per; ++i) ss += v[i] * v[i];
         ss = wave_sum(ss);
         const float rs = 1.0f / sqrtf(ss / (float)D + eps);
+#pragma unroll
         for (int i = 0; i < per; ++i) v[i] = (v[i] * rs) * load_scalar<WT>(gain, lane + 64 * i);
     }
-    if (per == 2) {
+    if constexpr (per == 2) {
         // pair (lane, lane + 64) sits in one lane
         const float2 cs = rope_row[lane];
         const float a = v[0], b = v[1];
@@ -574,12 +579,16 @@ __device__ __forceinline__ void head_norm_rope(float* v, int D, const WT* gain, 
 // attention event. The split that holds position pos first normalises,
 // rotates and appends the new k and v (rounded to the cache type).
 // Partial record: acc[G*D], m[h] at G*D + h, l[h] at G*D + 8 + h.
+// D (head size) and GP (query heads per KV head rounded up to a power of
+// two) are compile-time so that every lane loop and reduction unrolls;
+// heads G..GP-1 are computed on zeros and never stored.
 __host__ __device__ constexpr int attn_rec(int G, int D) { return G * D + 16; }
+__host__ __device__ constexpr int attn_gp(int G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8; }
 
-template <typename WT>
-__device__ __forceinline__ void attention_task(const KParams& p, int l, int bg, int split, const Lds& s) {
+template <typename WT, int D, int GP>
+__device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, int split, const Lds& s) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int Hkv = p.Hkv, D = p.D, G = p.Hq / p.Hkv, C = p.chunk;
+    const int Hkv = p.Hkv, G = p.Hq / p.Hkv, C = p.chunk;
     const int b = bg / Hkv, g = bg % Hkv;
     const int pos = p.seq_lens[b];
     const bool overflow = pos < 0 || pos + 1 > p.cap;
@@ -600,21 +609,43 @@ __device__ __forceinline__ void attention_task(const KParams& p, int l, int bg, 
     const bool owner = (j1 == keys);
     const int n = j1 - j0;
 
+    // 0. this wave's query heads (and, in the owner, the new k / v) are
+    // requested first: they are few and gate the prologue, while the bulk
+    // K/V loads issued next stay in flight behind them
+    constexpr int QPW = (GP + kWaves - 1) / kWaves;  // query heads per wave
+    float qv[QPW][2];
+#pragma unroll
+    for (int i = 0; i < QPW; ++i) {
+        const int hh = wave + i * kWaves;
+        qv[i][0] = qv[i][1] = 0.f;
+        if (hh < G) {
+            qv[i][0] = ld_co(&qkv[(int64_t)(g * G + hh) * D + lane]);
+            if constexpr (D > 64) qv[i][1] = ld_co(&qkv[(int64_t)(g * G + hh) * D + lane + 64]);
+        }
+    }
+    float nv[2] = {0.f, 0.f};
+    const bool appender = owner && wave < 2;
+    if (appender) {
+        const int64_t base = wave == 0 ? (int64_t)p.QD + (int64_t)g * D : (int64_t)p.QD + p.KD + (int64_t)g * D;
+        nv[0] = ld_co(&qkv[base + lane]);
+        if constexpr (D > 64) nv[1] = ld_co(&qkv[base + lane + 64]);
+    }
+    asm volatile("" ::: "memory");
+
     // K/V rows of this split: lane (rr, cc) holds 16 bytes of row
-    // j = it*per_it + wave*ppw + rr. The first batch of K and V is requested
-    // before anything else (it depends on nothing computed here).
+    // j = it*PER_IT + wave*PPW + rr; one batch covers SUB rows.
     using VK = Vec16<WT>;
     constexpr int E = VK::N;
-    constexpr int NIT = 32 / kWaves > 0 ? 32 / kWaves : 1;  // workgroup iterations per batch
-    const int lpr = D / E;            // lanes per K row
-    const int ppw = 64 / lpr;         // rows per wave per load
-    const int per_it = kWaves * ppw;  // rows per workgroup iteration
-    const int sub = per_it * NIT;     // rows per batch
-    const int rr = lane / lpr, cc = lane % lpr;
-    // K/V of this (layer, b, g) through buffer resources; row jj of the split
-    // at byte row_off(jj); rows past the split (or the new row, which comes
-    // from LDS) load through an out-of-range offset: no branches around loads
-    const int es = (int)sizeof(WT);
+    constexpr int LPR = D / E;             // lanes per K row
+    constexpr int PPW = 64 / LPR;          // rows per wave per load
+    constexpr int PER_IT = kWaves * PPW;   // rows per workgroup iteration
+    constexpr int NIT = 32 / kWaves;       // iterations per batch
+    constexpr int SUB = PER_IT * NIT;      // rows per batch
+    const int rr = lane / LPR, cc = lane % LPR;
+    // K/V of this (layer, b, g) through buffer resources; rows past the split
+    // (or the new row, which comes from LDS) load through an out-of-range
+    // offset: no branches around loads
+    constexpr int es = (int)sizeof(WT);
     const int64_t lbase = (int64_t)l * p.kv_layer_stride;
     __amdgpu_buffer_rsrc_t krs, vrs;
     if (!p.paged) {
@@ -632,13 +663,13 @@ __device__ __forceinline__ void attention_task(const KParams& p, int l, int bg, 
         if (p.paged) {
 #pragma unroll
             for (int it = 0; it < NIT; ++it) {
-                const int j = base + it * per_it + wave * ppw + rr;
+                const int j = base + it * PER_IT + wave * PPW + rr;
                 blk[it] = j < n ? btab[(j0 + j) / p.kv_block] : 0;
             }
         }
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
-            const int j = base + it * per_it + wave * ppw + rr;
+            const int j = base + it * PER_IT + wave * PPW + rr;
             const int jj = j0 + j;
             uint32_t o;
             if (p.paged) o = (uint32_t)(((blk[it] * Hkv + g) * p.kv_block + jj % p.kv_block) * D * es);
@@ -655,31 +686,27 @@ __device__ __forceinline__ void attention_task(const KParams& p, int l, int bg, 
             kr[it] = buf_load16(krs, ro[it], 0);
             vr[it] = buf_load16(vrs, ro[it], 0);
         }
-        asm volatile("" ::: "memory");  // keep the bulk loads ahead of the small ones below
     }
 
     // 1. query heads of this group: norm + RoPE into LDS
     const float2* rope_row = p.rope + (int64_t)pos * (D / 2);
-    const WT* qn = (const WT*)lw.q_norm;
-    const WT* kn = (const WT*)lw.k_norm;
-    for (int hh = wave; hh < G; hh += kWaves) {
-        float v[2];
-        v[0] = ld_co(&qkv[(int64_t)(g * G + hh) * D + lane]);
-        v[1] = D > 64 ? ld_co(&qkv[(int64_t)(g * G + hh) * D + lane + 64]) : 0.f;
-        head_norm_rope<WT>(v, D, qn, p.qk_norm != 0, p.eps, rope_row);
-        s.q[hh * D + lane] = v[0];
-        if (D > 64) s.q[hh * D + lane + 64] = v[1];
+    const bool qkn = p.qk_norm != 0;
+#pragma unroll
+    for (int i = 0; i < QPW; ++i) {
+        const int hh = wave + i * kWaves;
+        if (hh < G) {
+            head_norm_rope<WT, D>(qv[i], (const WT*)lw.q_norm, qkn, p.eps, rope_row);
+            s.q[hh * D + lane] = qv[i][0];
+            if constexpr (D > 64) s.q[hh * D + lane + 64] = qv[i][1];
+        }
     }
     // 2. owner: new k (norm + RoPE) and v, rounded to the cache type, appended
-    if (owner && wave < 2) {
-        float v[2];
-        const int64_t base = wave == 0 ? (int64_t)p.QD + (int64_t)g * D : (int64_t)p.QD + p.KD + (int64_t)g * D;
-        v[0] = ld_co(&qkv[base + lane]);
-        v[1] = D > 64 ? ld_co(&qkv[base + lane + 64]) : 0.f;
-        if (wave == 0) head_norm_rope<WT>(v, D, kn, p.qk_norm != 0, p.eps, rope_row);
+    if (appender) {
+        if (wave == 0) head_norm_rope<WT, D>(nv, (const WT*)lw.k_norm, qkn, p.eps, rope_row);
         WT* dst = (WT*)(wave == 0 ? p.kv_k : p.kv_v) + kv_offset(p, l, b, g, pos);
+#pragma unroll
         for (int i = 0; i < D / 64; ++i) {
-            const WT c = from_float<WT>(v[i]);
+            const WT c = from_float<WT>(nv[i]);
             dst[lane + 64 * i] = c;
             s.kn[wave * 128 + lane + 64 * i] = to_float<WT>(c);
         }
@@ -688,12 +715,12 @@ __device__ __forceinline__ void attention_task(const KParams& p, int l, int bg, 
     trace_mark(p, s.marks, 0);
 
     // 3. scores s_j = (q_h . k_j) * scale for j in [j0, j1)
-    float qreg[8][E];
+    float qreg[GP][E];
 #pragma unroll
-    for (int hh = 0; hh < 8; ++hh)
+    for (int hh = 0; hh < GP; ++hh)
 #pragma unroll
         for (int e = 0; e < E; ++e) qreg[hh][e] = hh < G ? s.q[hh * D + cc * E + e] : 0.f;
-    for (int base = 0; base < n; base += sub) {
+    for (int base = 0; base < n; base += SUB) {
         if (base > 0) {
             uint32_t ro[NIT];
             row_offsets(base, ro);
@@ -702,7 +729,7 @@ __device__ __forceinline__ void attention_task(const KParams& p, int l, int bg, 
         }
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
-            const int j = base + it * per_it + wave * ppw + rr;
+            const int j = base + it * PER_IT + wave * PPW + rr;
             const bool valid = j < n;
             float kf[E];
             if (valid && j0 + j == pos) {
@@ -711,14 +738,19 @@ __device__ __forceinline__ void attention_task(const KParams& p, int l, int bg, 
             } else {
                 VK::widen(kr[it], kf);
             }
+            float d[GP];
 #pragma unroll
-            for (int hh = 0; hh < 8; ++hh) {
-                if (hh >= G) continue;
-                float d = 0.f;
+            for (int hh = 0; hh < GP; ++hh) {
+                d[hh] = 0.f;
 #pragma unroll
-                for (int e = 0; e < E; ++e) d = fmaf(qreg[hh][e], kf[e], d);
-                for (int o = lpr / 2; o >= 1; o >>= 1) d += __shfl_xor(d, o, 64);
-                if (valid && cc == 0) s.p[hh * C + j] = d * p.scale;
+                for (int e = 0; e < E; ++e) d[hh] = fmaf(qreg[hh][e], kf[e], d[hh]);
+            }
+#pragma unroll
+            for (int hh = 0; hh < GP; ++hh) d[hh] = group_sum<LPR>(d[hh]);
+            if (valid && cc == 0) {
+#pragma unroll
+                for (int hh = 0; hh < GP; ++hh)
+                    if (hh < G) s.p[hh * C + j] = d[hh] * p.scale;
             }
         }
     }
@@ -744,12 +776,12 @@ __device__ __forceinline__ void attention_task(const KParams& p, int l, int bg, 
     __syncthreads();
 
     // 5. acc[h][d] = sum_j p[h][j] V[j][d] (first batch of V already loaded)
-    float acc[8][E];
+    float acc[GP][E];
 #pragma unroll
-    for (int hh = 0; hh < 8; ++hh)
+    for (int hh = 0; hh < GP; ++hh)
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[hh][e] = 0.f;
-    for (int base = 0; base < n; base += sub) {
+    for (int base = 0; base < n; base += SUB) {
         if (base > 0) {
             uint32_t ro[NIT];
             row_offsets(base, ro);
@@ -758,19 +790,19 @@ __device__ __forceinline__ void attention_task(const KParams& p, int l, int bg, 
         }
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
-            const int j = base + it * per_it + wave * ppw + rr;
-            if (j >= n) continue;
+            const int j = base + it * PER_IT + wave * PPW + rr;
+            const bool valid = j < n;
             float vf[E];
-            if (j0 + j == pos) {
+            if (valid && j0 + j == pos) {
 #pragma unroll
                 for (int e = 0; e < E; ++e) vf[e] = s.kn[128 + cc * E + e];
             } else {
                 VK::widen(vr[it], vf);
             }
+            const int jc = valid ? j : 0;
 #pragma unroll
-            for (int hh = 0; hh < 8; ++hh) {
-                if (hh >= G) continue;
-                const float pj = s.p[hh * C + j];
+            for (int hh = 0; hh < GP; ++hh) {
+                const float pj = (valid && hh < G) ? s.p[hh * C + jc] : 0.f;
 #pragma unroll
                 for (int e = 0; e < E; ++e) acc[hh][e] = fmaf(pj, vf[e], acc[hh][e]);
             }
@@ -778,18 +810,15 @@ __device__ __forceinline__ void attention_task(const KParams& p, int l, int bg, 
     }
     // reduce over the row groups of the wave (lanes with equal cc)
 #pragma unroll
-    for (int hh = 0; hh < 8; ++hh) {
-        if (hh >= G) continue;
+    for (int hh = 0; hh < GP; ++hh)
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            float v = acc[hh][e];
-            for (int o = lpr; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
-            acc[hh][e] = v;
+#pragma unroll
+            for (int o = LPR; o < 64; o <<= 1) acc[hh][e] += __shfl_xor(acc[hh][e], o, 64);
         }
-    }
     if (rr == 0) {
 #pragma unroll
-        for (int hh = 0; hh < 8; ++hh) {
+        for (int hh = 0; hh < GP; ++hh) {
             if (hh >= G) continue;
 #pragma unroll
             for (int e = 0; e < E; ++e) s.acc[(wave * 8 + hh) * 128 + cc * E + e] = acc[hh][e];
@@ -866,6 +895,21 @@ __device__ __forceinline__ void attention_task(const KParams& p, int l, int bg, 
     }
     if (tid == 0) __hip_atomic_store(&p.arrive[bg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (p.persistent) signal_event(p, ev_attn(l), s);
+}
+
+template <typename WT, int D>
+__device__ __forceinline__ void attention_task_d(const KParams& p, int l, int bg, int split, const Lds& s) {
+    switch (attn_gp(p.Hq / p.Hkv)) {
+        case 1: attention_body<WT, D, 1>(p, l, bg, split, s); break;
+        case 2: attention_body<WT, D, 2>(p, l, bg, split, s); break;
+        case 4: attention_body<WT, D, 4>(p, l, bg, split, s); break;
+        default: attention_body<WT, D, 8>(p, l, bg, split, s); break;
+    }
+}
+template <typename WT>
+__device__ __forceinline__ void attention_task(const KParams& p, int l, int bg, int split, const Lds& s) {
+    if (p.D == 128) attention_task_d<WT, 128>(p, l, bg, split, s);
+    else attention_task_d<WT, 64>(p, l, bg, split, s);
 }
 
 }  // namespace mk
