@@ -74,8 +74,10 @@ enum mk_device_error {
  *  device_cus    CU count to plan for when host_only (default 256).
  *  debug_extra_required  for fault tests: adds this many to the required
  *                count of event `debug_event` so its waiters time out.
- *  prefetch_kb   KB of the next GEMV task's weights each worker pulls into
- *                L2 before that task's event fires (default 64; -1 = off).
+ *  prefetch_kb   KB of the next GEMV task's weights each worker pulls toward
+ *                the chip (L2 / memory-side cache) while it waits for that
+ *                task's event, issued in small slices between polls
+ *                (default 256; -1 = off).
  *  lds_stream    1: at batch 1 with bf16 weights, the persistent kernel streams
  *                weight pages through a per-wave LDS ring filled by
  *                direct-to-LDS buffer loads (experimental; same results).
@@ -251,7 +253,7 @@ int mk_plan_dry_run(const mk_plan* plan, int n_threads, uint64_t seed, int drop_
  * index in the plan), 1 JIT attention task (id = layer << 24 | (b*Hkv+g) << 12
  * | split, fields truncated). t_wait: the worker started waiting for the
  * task's event; t_ready: the event was satisfied (JIT: task popped);
- * t_done: outputs written and the completion signalled; t_a, t_b: phase
+ * t_done: outputs written and the completion signalled; t_a .. t_d: phase
  * marks inside the task body. Ticks of the 100 MHz device real-time clock.
  */
 typedef struct mk_trace_rec {
@@ -260,8 +262,10 @@ typedef struct mk_trace_rec {
     int32_t worker;
     int32_t op;
     uint64_t t_wait, t_ready, t_done;
-    uint64_t t_a, t_b; /* task-defined phase marks (GEMV: operands ready, rows done;
-                          attention: prologue done, partial written); 0 if unset */
+    uint64_t t_a, t_b, t_c, t_d; /* task-defined phase marks, 0 if unset. GEMV: operands
+                                    ready, rows done, outputs stored, stores complete;
+                                    attention: prologue done, partial written, -, stores
+                                    complete (last arrival only) */
 } mk_trace_rec;
 
 /*

@@ -124,10 +124,12 @@ __device__ __forceinline__ void trace_put(const KParams& p, const Lds& s, int ki
         r.t_done = now_ticks();
         r.t_a = s.marks[0];
         r.t_b = s.marks[1];
+        r.t_c = s.marks[2];
+        r.t_d = s.marks[3];
         p.trace[(int64_t)w * p.trace_cap + i] = r;
     }
     p.trace_n[w] = i + 1;
-    s.marks[0] = s.marks[1] = 0;
+    s.marks[0] = s.marks[1] = s.marks[2] = s.marks[3] = 0;
 }
 
 template <typename WT, int NB>
@@ -138,7 +140,7 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s, uint
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     if (p.trace && threadIdx.x == 0) {
         p.trace_n[w] = 0;
-        s.marks[0] = s.marks[1] = 0;
+        s.marks[0] = s.marks[1] = s.marks[2] = s.marks[3] = 0;
     }
     int64_t head = (threadIdx.x == 0 && p.jit_on) ? p.inbox_head[w] : 0;
     // optional batch-1 variant: weight pages stream through a per-wave LDS
@@ -153,9 +155,19 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s, uint
         loader_seek<WT>(p, st, qb, qe, wave);
         loader_fill<WT>(p, st, 0, qe, wave, lane);
     }
+    Prefetch pf;
+    pf.next = pf.end = 0;
+    if constexpr (!kStream)
+        if (qb < qe) pf = prefetch_setup<WT>(p, p.tasks[p.queue[qb]]);
+    Prefetch pf_next;
+    pf_next.next = pf_next.end = 0;
     for (int qi = qb; qi < qe; ++qi) {
         const int tid_task = p.queue[qi];
         const TaskRec t = p.tasks[tid_task];
+        // the next task's weight cursor is looked up now, off the critical
+        // path (its table reads complete while this task waits and runs)
+        if constexpr (!kStream)
+            if (qi + 1 < qe) pf_next = prefetch_setup<WT>(p, p.tasks[p.queue[qi + 1]]);
         const uint64_t tw = p.trace ? now_ticks() : 0;
         uint64_t tr = tw;
         // Wait for the task's event, running JIT attention tasks from this
@@ -201,6 +213,7 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s, uint
                     return;
                 }
                 if (cmd == 2) {
+                    if constexpr (!kStream) prefetch_step(pf);
                     __builtin_amdgcn_s_sleep(1);
                     continue;
                 }
@@ -228,8 +241,12 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s, uint
             }
             signal_event(p, t.sig_ev, s);
         }
-        if constexpr (!kStream)
-            if (qi + 1 < qe) prefetch_task<WT>(p, p.tasks[p.queue[qi + 1]]);
+        if constexpr (!kStream) {
+            if (qi + 1 < qe) {
+                pf = pf_next;
+                prefetch_step(pf);
+            }
+        }
         trace_put(p, s, 0, tid_task, t.op, tw, tr);
     }
     if (threadIdx.x == 0 && p.jit_on) p.inbox_head[w] = head;

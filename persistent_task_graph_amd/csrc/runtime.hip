@@ -377,7 +377,7 @@ KParams make_params(const mk_plan* pl, const mk_weights* w, const mk_kv_cache* k
     p.mb_mask = hp.mb_cap - 1;
     const int wd = d.opts.watchdog_ms > 0 ? d.opts.watchdog_ms : 2000;
     p.watchdog_ticks = (uint64_t)wd * 100000ull;
-    p.prefetch_kb = d.opts.prefetch_kb == 0 ? 64 : (d.opts.prefetch_kb < 0 ? 0 : d.opts.prefetch_kb);
+    p.prefetch_kb = d.opts.prefetch_kb == 0 ? 256 : (d.opts.prefetch_kb < 0 ? 0 : d.opts.prefetch_kb);
     p.trace = pl->d_trace;
     p.trace_n = pl->d_trace_n;
     p.trace_cap = pl->trace_cap;

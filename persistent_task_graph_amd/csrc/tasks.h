@@ -22,13 +22,13 @@ struct Lds {
     float* acc;   // kWaves * 8 * 128: P.V partials per wave
     float* ml;    // 2 * 8: (m, l) per head
     float* cmb;   // kCmbSplits * (8 * 128 + 16): partials staged for the combine
-    uint64_t* marks;  // 2 trace phase marks
+    uint64_t* marks;  // 4 trace phase marks
 };
 
 constexpr int kCmbSplits = 4;  // splits merged per staged chunk
 constexpr int kPartFloats = 4096;  // GEMV cross-wave partial sums
 __host__ __device__ constexpr int lds_floats_fixed() {
-    return kWaves * 16 + 16 + 16 + 4 + kPartFloats + 8 * 128 + 2 * 128 + kWaves * 8 * 128 + 16 + kCmbSplits * (8 * 128 + 16);
+    return kWaves * 16 + 16 + 16 + 8 + kPartFloats + 8 * 128 + 2 * 128 + kWaves * 8 * 128 + 16 + kCmbSplits * (8 * 128 + 16);
 }
 __host__ __device__ inline int lds_bytes_for(int G, int chunk) {
     const int gp = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
@@ -40,7 +40,7 @@ __device__ __forceinline__ Lds carve_lds(float* base, int G, int chunk) {
     float* p = base;
     s.red = p; p += kWaves * 16;
     s.cmd = (int*)p; p += 16;
-    s.marks = (uint64_t*)p; p += 4;
+    s.marks = (uint64_t*)p; p += 8;
     s.rstd = p; p += 16;
     s.part = p; p += kPartFloats;
     s.q = p; p += 8 * 128;
@@ -324,13 +324,15 @@ __device__ __forceinline__ void gemv_dispatch(int r0, int r1, int K, const float
         constexpr int SEG = 64 * Vec16<WT>::N;
         constexpr int D2 = DUAL ? 2 : 1;
         const int nsw = ((K + SEG - 1) / SEG + kWaves - 1) / kWaves;
-        // rows per group so that one buffer holds about 16 16-byte loads
-        // per lane: two buffers then fit in 128 VGPRs
+        // rows per group: small groups keep the fully unrolled loop short,
+        // which measured faster than deeper groups for every task size here
+        // (instruction fetch and fixed latencies dominate short tasks; the
+        // stream of a long task is bound by HBM either way)
         if (nsw <= 1) gemv_ksplit<WT, NB, 1, 16 / D2, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr);
-        else if (nsw <= 2) gemv_ksplit<WT, NB, 2, 8 / D2, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr);
+        else if (nsw <= 2) gemv_ksplit<WT, NB, 2, 2 / D2, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr);
         else if (nsw <= 3) gemv_ksplit<WT, NB, 3, 5 / D2, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr);
         else if (nsw <= 4) gemv_ksplit<WT, NB, 4, 4 / D2, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr);
-        else if (nsw <= 6) gemv_ksplit<WT, NB, 6, 2 / D2, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr);
+        else if (nsw <= 6) gemv_ksplit<WT, NB, 6, 1, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr);
         else gemv_ksplit<WT, NB, 8, 2 / D2, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr);
     } else {
         if (gain) block_rstd<NB>(x, ldx, K, B, eps, s);
@@ -461,6 +463,7 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
         }
         default: break;
     }
+    trace_mark(p, s.marks, 2);
 }
 
 // ---------------------------------------------------------------- signalling
@@ -471,11 +474,17 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
 // scheduler mailbox (§2.2: the data-dependent successor is launched JIT).
 __device__ __forceinline__ void signal_event(const KParams& p, int e, const Lds& s) {
     wait_stores();  // this thread's agent-coherent stores have completed
+    trace_mark(p, s.marks, 3);
     __syncthreads();
     if (threadIdx.x == 0 && e >= 0) {
-        const uint32_t old = __hip_atomic_fetch_add(&p.ev[e], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const EventRec er = p.evrec[e];
-        if (er.jit_layer >= 0 && old + 1u == er.required * (p.epoch + 1u)) {
+        if (er.jit_layer < 0) {
+            // no one acts on the count here: the add needs no return trip
+            __hip_atomic_fetch_add(&p.ev[e], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+        const uint32_t old = __hip_atomic_fetch_add(&p.ev[e], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (old + 1u == er.required * (p.epoch + 1u)) {
             // the completing arrival posts "expand attention of this layer"
             const int64_t pos = __hip_atomic_fetch_add(&p.ctrl->mb_tail, (int64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             RingSlot* sl = &p.mb[pos & p.mb_mask];
@@ -485,52 +494,86 @@ __device__ __forceinline__ void signal_event(const KParams& p, int e, const Lds&
             __hip_atomic_store(&sl->tag, pos + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    (void)s;
 }
 
 // ---------------------------------------------------------------- next-task prefetch
-// The weights are static, so the next GEMV task's leading rows can be
-// fetched before its event fires (the MPK article's preload phase, §3.2):
-// waves 1..3 issue direct-to-LDS loads of up to `kb` KB of them into a
-// scratch LDS slot that is never read. The lines land in this XCD's L2,
-// keeping HBM busy across the level boundary; the task body's own loads
-// then hit L2. Wave 0 (which polls the next event) issues nothing.
+// The weights are static, so a worker can pull its next GEMV task's rows
+// toward the chip before that task's event fires (the MPK article's
+// preload phase, section 3.2): HBM stays busy across level boundaries and
+// the task body's own loads then hit L2 or the memory-side cache. Loads go
+// direct-to-LDS into a scratch slot that is never read, so they hold no
+// registers. They are issued in slices (kPrefetchSlice KB per wave) between
+// polls of the event, never as one burst, so that the poll loop is not held
+// up by a full load queue.
 __shared__ __attribute__((aligned(16))) uint4 mk_prefetch_sink[kWaves][64];
+constexpr int kPrefetchSlice = 6;
 
-__device__ __forceinline__ void prefetch_rows(const void* m, int K, int es, int rows, int r0, int r1, int kb, int wave,
-                                              int lane) {
+struct Prefetch {
+    __amdgpu_buffer_rsrc_t a, b;  // one or two weight segments (gate and up interleave)
+    uint32_t kb_a, kb_b;          // segment sizes in KB (rounded up)
+    uint32_t next, end;           // next KB index to issue, total KB to issue
+};
+
+__device__ __forceinline__ void prefetch_segment(const void* m, int K, int es, int rows, int r0, int r1,
+                                                 __amdgpu_buffer_rsrc_t& rs, uint32_t& kb) {
     r0 = max(0, min(r0, rows));
     r1 = max(r0, min(r1, rows));
     const uint32_t bytes = (uint32_t)(r1 - r0) * (uint32_t)K * (uint32_t)es;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc((const char*)m + (int64_t)r0 * K * es, bytes);
-    const uint32_t n = min(bytes, (uint32_t)kb * 1024u) / 1024u;
-    for (uint32_t i = (uint32_t)(wave - 1); i < n; i += kWaves - 1)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)&mk_prefetch_sink[wave][0], 16,
-                                                 lane * 16, i * 1024u, 0, 0);
+    rs = make_rsrc((const char*)m + (int64_t)r0 * K * es, bytes);
+    kb = (bytes + 1023u) / 1024u;
 }
 
+// Cursor over the next task's weights (empty for attention / embedding or
+// when prefetching is off).
 template <typename WT>
-__device__ __forceinline__ void prefetch_task(const KParams& p, const TaskRec& t) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    if (wave == 0 || p.prefetch_kb <= 0) return;
-    const int es = (int)sizeof(WT), l = t.layer, H = p.H, kb = p.prefetch_kb;
+__device__ __forceinline__ Prefetch prefetch_setup(const KParams& p, const TaskRec& t) {
+    Prefetch f;
+    f.kb_a = f.kb_b = 0;
+    f.next = f.end = 0;
+    f.a = f.b = make_rsrc(p.zero, 0);
+    if (p.prefetch_kb <= 0) return f;
+    const int es = (int)sizeof(WT), l = t.layer, H = p.H;
     switch (t.op) {
         case OP_QKV: {
             const LayerPtrs& w = p.lw[l];
-            if (t.a0 < p.QD) prefetch_rows(w.wq, H, es, p.QD, t.a0, t.a1, kb, wave, lane);
-            else if (t.a0 < p.QD + p.KD) prefetch_rows(w.wk, H, es, p.KD, t.a0 - p.QD, t.a1 - p.QD, kb, wave, lane);
-            else prefetch_rows(w.wv, H, es, p.KD, t.a0 - p.QD - p.KD, t.a1 - p.QD - p.KD, kb, wave, lane);
+            if (t.a0 < p.QD) prefetch_segment(w.wq, H, es, p.QD, t.a0, t.a1, f.a, f.kb_a);
+            else if (t.a0 < p.QD + p.KD) prefetch_segment(w.wk, H, es, p.KD, t.a0 - p.QD, t.a1 - p.QD, f.a, f.kb_a);
+            else prefetch_segment(w.wv, H, es, p.KD, t.a0 - p.QD - p.KD, t.a1 - p.QD - p.KD, f.a, f.kb_a);
             break;
         }
-        case OP_O: prefetch_rows(p.lw[l].wo, p.QD, es, H, t.a0, t.a1, kb, wave, lane); break;
+        case OP_O: prefetch_segment(p.lw[l].wo, p.QD, es, H, t.a0, t.a1, f.a, f.kb_a); break;
         case OP_GATEUP:
-            prefetch_rows(p.lw[l].w_gate, H, es, p.F, t.a0, t.a1, kb / 2, wave, lane);
-            prefetch_rows(p.lw[l].w_up, H, es, p.F, t.a0, t.a1, kb / 2, wave, lane);
+            prefetch_segment(p.lw[l].w_gate, H, es, p.F, t.a0, t.a1, f.a, f.kb_a);
+            prefetch_segment(p.lw[l].w_up, H, es, p.F, t.a0, t.a1, f.b, f.kb_b);
             break;
-        case OP_DOWN: prefetch_rows(p.lw[l].w_down, p.F, es, H, t.a0, t.a1, kb, wave, lane); break;
-        case OP_LM: prefetch_rows(p.lm_head, H, es, p.V, t.a0, t.a1, kb, wave, lane); break;
+        case OP_DOWN: prefetch_segment(p.lw[l].w_down, p.F, es, H, t.a0, t.a1, f.a, f.kb_a); break;
+        case OP_LM: prefetch_segment(p.lm_head, H, es, p.V, t.a0, t.a1, f.a, f.kb_a); break;
         default: break;
     }
+    f.end = min(f.kb_a + f.kb_b, (uint32_t)p.prefetch_kb);
+    return f;
+}
+
+// Issue the next slice: each wave takes every kWaves-th KB. With two
+// segments, KB i of the stream is KB i/2 of segment (i & 1). Offsets past a
+// segment are out of range for its resource and fetch nothing.
+__device__ __forceinline__ void prefetch_step(Prefetch& f) {
+    if (f.next >= f.end) return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    auto* sink = (__attribute__((address_space(3))) void*)&mk_prefetch_sink[wave][0];
+#pragma unroll
+    for (int k = 0; k < kPrefetchSlice; ++k) {
+        const uint32_t i = f.next + (uint32_t)(k * kWaves + wave);
+        if (i >= f.end) break;
+        if (f.kb_b == 0) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(f.a, sink, 16, lane * 16, i * 1024u, 0, 0);
+        } else {
+            const uint32_t o = (i >> 1) * 1024u;
+            if (i & 1) __builtin_amdgcn_raw_ptr_buffer_load_lds(f.b, sink, 16, lane * 16, o, 0, 0);
+            else __builtin_amdgcn_raw_ptr_buffer_load_lds(f.a, sink, 16, lane * 16, o, 0, 0);
+        }
+    }
+    f.next += (uint32_t)(kPrefetchSlice * kWaves);
 }
 
 // ---------------------------------------------------------------- attention

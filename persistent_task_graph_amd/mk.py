@@ -61,7 +61,7 @@ class KVCache(ctypes.Structure):
 
 class TraceRec(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("kind", "id", "worker", "op")] + \
-               [(n, ctypes.c_uint64) for n in ("t_wait", "t_ready", "t_done", "t_a", "t_b")]
+               [(n, ctypes.c_uint64) for n in ("t_wait", "t_ready", "t_done", "t_a", "t_b", "t_c", "t_d")]
 
 
 class PlanInfo(ctypes.Structure):
@@ -221,7 +221,8 @@ class Plan:
         n = _check(lib().mk_plan_trace(self._h, ctypes.cast(buf, ctypes.c_void_p), max_records, _stream(stream)),
                    "mk_plan_trace")
         dt = np.dtype([("kind", "<i4"), ("id", "<i4"), ("worker", "<i4"), ("op", "<i4"), ("t_wait", "<u8"),
-                       ("t_ready", "<u8"), ("t_done", "<u8"), ("t_a", "<u8"), ("t_b", "<u8")])
+                       ("t_ready", "<u8"), ("t_done", "<u8"), ("t_a", "<u8"), ("t_b", "<u8"),
+                       ("t_c", "<u8"), ("t_d", "<u8")])
         return np.frombuffer(bytes(buf)[: n * ctypes.sizeof(TraceRec)], dtype=dt).copy()
 
     def argmax(self, logits, out_tokens, stream=None) -> None:
