@@ -264,8 +264,8 @@ typedef struct mk_trace_rec {
     uint64_t t_wait, t_ready, t_done;
     uint64_t t_a, t_b, t_c, t_d; /* task-defined phase marks, 0 if unset. GEMV: operands
                                     ready, rows done, outputs stored, stores complete;
-                                    attention: prologue done, partial written, -, stores
-                                    complete (last arrival only) */
+                                    attention: prologue done, scores done, P.V done,
+                                    partial stored */
 } mk_trace_rec;
 
 /*

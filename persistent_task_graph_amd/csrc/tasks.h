@@ -799,6 +799,7 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
     }
     __syncthreads();
 
+    trace_mark(p, s.marks, 1);
     // 4. per-head max and exp-sum over this split (fixed strides and tree)
     for (int hh = wave; hh < G; hh += kWaves) {
         float m = -INFINITY;
@@ -869,6 +870,7 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
     }
     __syncthreads();
 
+    trace_mark(p, s.marks, 2);
     // 6. partial record
     const int rec = attn_rec(G, D);
     float* part = p.partials + ((int64_t)bg * p.max_splits + split) * rec;
@@ -885,7 +887,7 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
 
     // 7. last arrival merges the splits in split order
     wait_stores();
-    trace_mark(p, s.marks, 1);
+    trace_mark(p, s.marks, 3);
     __syncthreads();
     if (tid == 0) {
         const uint32_t old = __hip_atomic_fetch_add(&p.arrive[bg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
