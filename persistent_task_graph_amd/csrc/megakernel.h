@@ -253,7 +253,7 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s, uint
     if constexpr (kStream) wait_vm<0>();
 }
 
-extern __shared__ float mk_dyn_lds[];
+extern __shared__ __attribute__((aligned(16))) float mk_dyn_lds[];
 
 template <typename WT, int NB>
 __global__ __launch_bounds__(kThreads) void k_persistent(KParams p) {

@@ -5,6 +5,8 @@
 // runs it), no floating-point atomics are used, and contraction is off.
 #pragma once
 
+#include <type_traits>
+
 #include "device.h"
 
 namespace mk {
@@ -26,7 +28,7 @@ struct Lds {
 };
 
 constexpr int kCmbSplits = 4;  // splits merged per staged chunk
-constexpr int kPartFloats = 4096;  // GEMV cross-wave partial sums
+constexpr int kPartFloats = 8192;  // GEMV cross-wave partial sums
 __host__ __device__ constexpr int lds_floats_fixed() {
     return kWaves * 16 + 16 + 16 + 8 + kPartFloats + 8 * 128 + 2 * 128 + kWaves * 8 * 128 + 16 + kCmbSplits * (8 * 128 + 16);
 }
@@ -345,11 +347,12 @@ __device__ __forceinline__ void gemv_dispatch(int r0, int r1, int K, const float
 template <typename WT>
 struct MatTile {
     __amdgpu_buffer_rsrc_t r;
-    int lo;
+    int lo, n;
     uint32_t rowbytes;
     __device__ __forceinline__ MatTile(const WT* m, int K, int rows, int lo_, int hi_) {
         lo = max(0, min(lo_, rows));
         const int hi = max(lo, min(hi_, rows));
+        n = hi - lo;
         rowbytes = (uint32_t)K * (uint32_t)sizeof(WT);
         r = make_rsrc(m + (int64_t)lo * K, (uint32_t)(hi - lo) * rowbytes);
     }
@@ -358,6 +361,240 @@ struct MatTile {
         o.soff = (uint32_t)(rr - lo) * rowbytes;
     }
 };
+
+// ---------------------------------------------------------------- GEMV on MFMA (bf16, B >= 3)
+// With a batch of several sequences the GEMV is a thin matrix product
+// Y[r][b] = sum_k W[r][k] xg[b][k] (xg = x * norm gain), done here on the
+// 16x16x32 bf16 matrix cores: a 16-row weight tile is the A operand (lane
+// l holds 8 consecutive k of row l % 16), the batch is the N dimension.
+// The fp32 activations are split into two bf16 terms, xg = hi + lo with
+// lo = bf16(xg - hi), and both are multiplied, so the product keeps about
+// 16 significant bits of xg (error ~2^-17 relative) instead of bf16's 8.
+// x is staged through LDS a piece of 256 k at a time (converted once per
+// workgroup, laid out as the MFMA B operand); within a piece wave w takes
+// the 64 consecutive k [64w, 64w + 64), so each weight row is read as whole
+// 128-byte lines. Weight loads of the next piece are in flight while the
+// current one is multiplied. Each wave's partial tiles are added across
+// waves in wave order through LDS. A task's rows are taken in passes of
+// TMAX tiles (x is staged again per pass); rows past a segment and k past
+// K load through an out-of-range offset (zeros, no traffic).
+typedef __bf16 mk_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float mk_f32x4 __attribute__((ext_vector_type(4)));
+
+// one run of output rows backed by one matrix (two for gate/up)
+struct MSeg {
+    __amdgpu_buffer_rsrc_t a, b;  // rows [0, n) of the matrix (matrices)
+    int n;                        // rows in the run
+    int out0;                     // output row of the run's first row
+};
+
+__device__ __forceinline__ mk_f32x4 mfma_bf16(const uint4& a, const uint4& b, mk_f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mk_bf16x8, a), __builtin_bit_cast(mk_bf16x8, b), c,
+                                                   0, 0, 0);
+}
+
+constexpr int kMfmaPieceK = 256;                      // k staged per piece
+constexpr int kMfmaStageU4 = (kMfmaPieceK / 32) * 128;  // uint4 per staged piece (hi + lo)
+
+template <int NB, bool DUAL, int TMAX, int NSEG, typename OutFn>
+__device__ __forceinline__ void gemv_mfma(const MSeg (&seg)[NSEG], int K, const float* x, int ldx, int B,
+                                          const bf16_t* gain, float eps, OutFn out, const Lds& s, bool tr) {
+    constexpr int NM = DUAL ? 2 : 1;
+    static_assert(kWaves * TMAX * NM * 256 <= kPartFloats, "partial tiles exceed the LDS window");
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lk = lane >> 4;
+    const uint32_t rowbytes = (uint32_t)K * 2u;
+    const int npiece = (K + kMfmaPieceK - 1) / kMfmaPieceK;
+    uint4* stage = reinterpret_cast<uint4*>(s.q);  // 2 x kMfmaStageU4 (aliases the attention scratch)
+    const __amdgpu_buffer_rsrc_t xr_rs = make_rsrc(x, (uint32_t)(B * ldx) * 4u);
+    const __amdgpu_buffer_rsrc_t g_rs = make_rsrc(gain, gain ? rowbytes : 0u);
+
+    // staging: thread tid converts units (b = tid % 16, 8-k group tid/16 and
+    // tid/16 + 16) of each piece
+    const int fb = tid & 15;
+    float ss = 0.f;  // sum of x^2 over this thread's k (for the norm statistic)
+    struct Fill {
+        uint4 x[2][2];
+        uint4 g[2];
+    };
+    auto fill_load = [&](Fill& f, int pc) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int k = pc * kMfmaPieceK + ((tid >> 4) + 16 * u) * 8;
+            const bool ok = fb < B && k < K && pc < npiece;
+            const uint32_t xo = ok ? (uint32_t)(fb * ldx + k) * 4u : kOOB;
+            f.x[u][0] = buf_load16_co(xr_rs, xo, 0);
+            f.x[u][1] = buf_load16_co(xr_rs, xo, 16);
+            f.g[u] = buf_load16(g_rs, (k < K && pc < npiece) ? (uint32_t)k * 2u : kOOB, 0);
+        }
+    };
+    auto fill_store = [&](const Fill& f, int buf, bool stat) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int grp = (tid >> 4) + 16 * u;  // 8-k group within the piece
+            float xv[8], gv[8];
+            xv[0] = __uint_as_float(f.x[u][0].x); xv[1] = __uint_as_float(f.x[u][0].y);
+            xv[2] = __uint_as_float(f.x[u][0].z); xv[3] = __uint_as_float(f.x[u][0].w);
+            xv[4] = __uint_as_float(f.x[u][1].x); xv[5] = __uint_as_float(f.x[u][1].y);
+            xv[6] = __uint_as_float(f.x[u][1].z); xv[7] = __uint_as_float(f.x[u][1].w);
+            if (gain) Vec16<bf16_t>::widen(f.g[u], gv);
+            else
+#pragma unroll
+                for (int e = 0; e < 8; ++e) gv[e] = 1.f;
+            uint32_t hw[4], lw[4];
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                if (stat) {
+                    ss += xv[e] * xv[e];
+                    ss += xv[e + 1] * xv[e + 1];
+                }
+                const float a0 = xv[e] * gv[e], a1 = xv[e + 1] * gv[e + 1];
+                const bf16_t h0 = f32_to_bf16(a0), h1 = f32_to_bf16(a1);
+                const bf16_t l0 = f32_to_bf16(a0 - __uint_as_float((uint32_t)h0 << 16));
+                const bf16_t l1 = f32_to_bf16(a1 - __uint_as_float((uint32_t)h1 << 16));
+                hw[e / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+                lw[e / 2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+            }
+            // B operand of chunk grp/4: lane (grp % 4) * 16 + b holds k 8*(grp%4)..+8 of batch b
+            uint4* st = stage + buf * kMfmaStageU4 + (grp >> 2) * 128 + (grp & 3) * 16 + fb;
+            st[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            st[64] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        }
+    };
+
+    // tiles of the task: segment by segment, 16 rows each
+    int ntile = 0;
+#pragma unroll
+    for (int q = 0; q < NSEG; ++q) ntile += (seg[q].n + 15) >> 4;
+
+    for (int t0 = 0; t0 < ntile; t0 += TMAX) {
+        // this pass's tile table (uniform): resources, row offset, valid rows, output row
+        __amdgpu_buffer_rsrc_t ta[TMAX], tb[TMAX];
+        uint32_t tsoff[TMAX];
+        int tval[TMAX], tout[TMAX];
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t) {
+            // segment q holding task tile t0 + t, and the tile's index gt in it
+            int gt = t0 + t, q = NSEG;
+#pragma unroll
+            for (int qq = 0; qq < NSEG; ++qq) {
+                const int nt = (seg[qq].n + 15) >> 4;
+                if (q == NSEG) {
+                    if (gt < nt) q = qq;
+                    else gt -= nt;
+                }
+            }
+            ta[t] = seg[0].a;
+            tb[t] = seg[0].b;
+            tsoff[t] = 0;
+            tval[t] = 0;
+            tout[t] = 0;
+#pragma unroll
+            for (int qq = 0; qq < NSEG; ++qq)
+                if (q == qq) {
+                    ta[t] = seg[qq].a;
+                    tb[t] = seg[qq].b;
+                    tsoff[t] = (uint32_t)(gt * 16) * rowbytes;
+                    tval[t] = min(16, seg[qq].n - gt * 16);
+                    tout[t] = seg[qq].out0 + gt * 16;
+                }
+        }
+        // per-lane weight offsets: row li of the tile, k of this wave's two chunks
+        auto w_load = [&](uint4 (&w)[TMAX][NM][2], int pc) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const int k = pc * kMfmaPieceK + wave * 64 + c * 32 + lk * 8;
+                const bool kok = k < K && pc < npiece;
+#pragma unroll
+                for (int t = 0; t < TMAX; ++t) {
+                    const uint32_t vo = (kok && li < tval[t]) ? (uint32_t)li * rowbytes + (uint32_t)k * 2u : kOOB;
+                    w[t][0][c] = buf_load16(ta[t], vo, tsoff[t]);
+                    if constexpr (DUAL) w[t][1][c] = buf_load16(tb[t], vo, tsoff[t]);
+                }
+            }
+        };
+        mk_f32x4 acc[TMAX][NM];
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t)
+#pragma unroll
+            for (int m = 0; m < NM; ++m) acc[t][m] = mk_f32x4{0.f, 0.f, 0.f, 0.f};
+        auto compute = [&](const uint4 (&w)[TMAX][NM][2], int buf) {
+            const uint4* st = stage + buf * kMfmaStageU4 + (wave * 2) * 128 + lane;
+            const uint4 h0 = st[0], l0 = st[64], h1 = st[128], l1 = st[192];
+#pragma unroll
+            for (int t = 0; t < TMAX; ++t) {
+                if (t0 + t >= ntile) continue;
+#pragma unroll
+                for (int m = 0; m < NM; ++m) {
+                    acc[t][m] = mfma_bf16(w[t][m][0], h0, acc[t][m]);
+                    acc[t][m] = mfma_bf16(w[t][m][0], l0, acc[t][m]);
+                    acc[t][m] = mfma_bf16(w[t][m][1], h1, acc[t][m]);
+                    acc[t][m] = mfma_bf16(w[t][m][1], l1, acc[t][m]);
+                }
+            }
+        };
+        const bool stat = gain != nullptr && t0 == 0;
+        Fill fa, fbuf;
+        uint4 wa[TMAX][NM][2], wb[TMAX][NM][2];
+        fill_load(fa, 0);
+        w_load(wa, 0);
+        fill_store(fa, 0, stat);
+        __syncthreads();
+        if (tr && tid == 0 && t0 == 0) s.marks[0] = now_ticks();
+        for (int pc = 0; pc < npiece; pc += 2) {
+            fill_load(fbuf, pc + 1);
+            w_load(wb, pc + 1);
+            compute(wa, 0);
+            if (pc + 1 < npiece) fill_store(fbuf, 1, stat);
+            __syncthreads();
+            fill_load(fa, pc + 2);
+            w_load(wa, pc + 2);
+            if (pc + 1 < npiece) compute(wb, 1);
+            if (pc + 2 < npiece) fill_store(fa, 0, stat);
+            __syncthreads();
+        }
+        if (stat) {
+            // norm statistic: lanes b, b+16, b+32, b+48 of each wave, then waves in order
+            ss += __shfl_xor(ss, 16, 64);
+            ss += __shfl_xor(ss, 32, 64);
+            if (lane < 16) s.red[wave * 16 + lane] = ss;
+        }
+        // partial tiles: D layout, lane l holds rows 4*(l/16)+r of batch l % 16
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t)
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+                if (t0 + t < ntile)
+                    *reinterpret_cast<mk_f32x4*>(&s.part[((wave * TMAX + t) * NM + m) * 256 + lane * 4]) = acc[t][m];
+        __syncthreads();
+        if (stat && tid < 16) {
+            float tt = s.red[tid];
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w) tt += s.red[w * 16 + tid];
+            s.rstd[tid] = 1.0f / sqrtf(tt / (float)K + eps);
+        }
+        if (tr && tid == 0) s.marks[1] = now_ticks();
+        __syncthreads();
+        {
+            const int i = tid >> 4, b = tid & 15;  // row in tile, batch
+            const int pl = ((i >> 2) * 16 + b) * 4 + (i & 3);
+#pragma unroll
+            for (int t = 0; t < TMAX; ++t) {
+                if (t0 + t >= ntile) continue;
+                float v[NM];
+#pragma unroll
+                for (int m = 0; m < NM; ++m) {
+                    float a = s.part[(t * NM + m) * 256 + pl];
+#pragma unroll
+                    for (int w = 1; w < kWaves; ++w) a += s.part[((w * TMAX + t) * NM + m) * 256 + pl];
+                    v[m] = a;
+                }
+                if (i < tval[t] && b < B) out(tout[t] + i, b, v[0], v[NM - 1]);
+            }
+        }
+        __syncthreads();
+    }
+}
 
 // ---------------------------------------------------------------- GEMV tasks
 
@@ -380,6 +617,8 @@ __device__ __forceinline__ void embed_task(const KParams& p, const TaskRec& t) {
 
 template <typename WT, int NB>
 __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t, const Lds& s) {
+    // bf16 weights with more than two sequences run on the matrix cores
+    constexpr bool kMfma = std::is_same<WT, bf16_t>::value && NB >= 4;
     const int l = t.layer, B = p.B, H = p.H;
     const int r0 = t.a0, r1 = t.a1;
     switch (t.op) {
@@ -399,7 +638,12 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
                 b2 = a;
             };
             auto out = [&](int r, int b, float v, float) { st_co(&o[(int64_t)b * ld + r], v * s.rstd[b]); };
-            gemv_dispatch<WT, NB, false>(r0, r1, H, x, H, B, (const WT*)w.attn_norm, p.eps, rowp, out, s, p.trace != nullptr);
+            if constexpr (kMfma) {
+                const MSeg sg[3] = {{tq.r, tq.r, tq.n, tq.lo}, {tk.r, tk.r, tk.n, QD + tk.lo}, {tv.r, tv.r, tv.n, QD + KD + tv.lo}};
+                gemv_mfma<NB, false, 4>(sg, H, x, H, B, (const bf16_t*)w.attn_norm, p.eps, out, s, p.trace != nullptr);
+            } else {
+                gemv_dispatch<WT, NB, false>(r0, r1, H, x, H, B, (const WT*)w.attn_norm, p.eps, rowp, out, s, p.trace != nullptr);
+            }
             break;
         }
         case OP_O: {
@@ -414,7 +658,12 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
                 const int64_t i = (int64_t)b * H + r;
                 st_co(&o[i], ld_co(&xin[i]) + v);
             };
-            gemv_dispatch<WT, NB, false>(r0, r1, K, a, K, B, (const WT*)nullptr, p.eps, rowp, out, s, p.trace != nullptr);
+            if constexpr (kMfma) {
+                const MSeg sg[1] = {{to.r, to.r, to.n, to.lo}};
+                gemv_mfma<NB, false, 2>(sg, K, a, K, B, (const bf16_t*)nullptr, p.eps, out, s, p.trace != nullptr);
+            } else {
+                gemv_dispatch<WT, NB, false>(r0, r1, K, a, K, B, (const WT*)nullptr, p.eps, rowp, out, s, p.trace != nullptr);
+            }
             break;
         }
         case OP_GATEUP: {
@@ -433,7 +682,12 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
                 const float gg = g * rs, uu = u * rs;
                 st_co(&o[(int64_t)b * F + r], (gg / (1.0f + __expf(-gg))) * uu);
             };
-            gemv_dispatch<WT, NB, true>(r0, r1, H, x, H, B, (const WT*)w.mlp_norm, p.eps, rowp, out, s, p.trace != nullptr);
+            if constexpr (kMfma) {
+                const MSeg sg[1] = {{tg.r, tu.r, tg.n, tg.lo}};
+                gemv_mfma<NB, true, 4>(sg, H, x, H, B, (const bf16_t*)w.mlp_norm, p.eps, out, s, p.trace != nullptr);
+            } else {
+                gemv_dispatch<WT, NB, true>(r0, r1, H, x, H, B, (const WT*)w.mlp_norm, p.eps, rowp, out, s, p.trace != nullptr);
+            }
             break;
         }
         case OP_DOWN: {
@@ -448,7 +702,12 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
                 const int64_t i = (int64_t)b * H + r;
                 st_co(&o[i], ld_co(&xm[i]) + v);
             };
-            gemv_dispatch<WT, NB, false>(r0, r1, F, h, F, B, (const WT*)nullptr, p.eps, rowp, out, s, p.trace != nullptr);
+            if constexpr (kMfma) {
+                const MSeg sg[1] = {{td.r, td.r, td.n, td.lo}};
+                gemv_mfma<NB, false, 2>(sg, F, h, F, B, (const bf16_t*)nullptr, p.eps, out, s, p.trace != nullptr);
+            } else {
+                gemv_dispatch<WT, NB, false>(r0, r1, F, h, F, B, (const WT*)nullptr, p.eps, rowp, out, s, p.trace != nullptr);
+            }
             break;
         }
         case OP_LM: {
@@ -458,7 +717,12 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
             const MatTile<WT> tl((const WT*)p.lm_head, H, V, r0, r1);
             auto rowp = [&](int r, RowRef& a0, RowRef& b2) { tl.row(r, a0); b2 = a0; };
             auto out = [&](int r, int b, float v, float) { o[(int64_t)b * V + r] = v * s.rstd[b]; };  // read after the launch
-            gemv_dispatch<WT, NB, false>(r0, r1, H, x, H, B, (const WT*)p.final_norm, p.eps, rowp, out, s, p.trace != nullptr);
+            if constexpr (kMfma) {
+                const MSeg sg[1] = {{tl.r, tl.r, tl.n, tl.lo}};
+                gemv_mfma<NB, false, 8>(sg, H, x, H, B, (const bf16_t*)p.final_norm, p.eps, out, s, p.trace != nullptr);
+            } else {
+                gemv_dispatch<WT, NB, false>(r0, r1, H, x, H, B, (const WT*)p.final_norm, p.eps, rowp, out, s, p.trace != nullptr);
+            }
             break;
         }
         default: break;
