@@ -158,6 +158,27 @@ __device__ __forceinline__ float read_lane(float v, int lane) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
 
+// Sums across the rows of 16 lanes through the gfx950 row-swap instructions
+// (VALU, no LDS crossbar): with both operands equal, permlane16_swap returns
+// the even rows in its first result and the odd rows in its second, so their
+// sum is v[l] + v[l ^ 16] in every lane, added in the same order in both
+// lanes; permlane32_swap does the same for the two halves (l ^ 32).
+__device__ __forceinline__ float rows_sum16(float v) {
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+__device__ __forceinline__ float halves_sum32(float v) {
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+// the value of lane l ^ 32
+__device__ __forceinline__ float halves_partner(float v) {
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (unsigned)((threadIdx.x & 32) ? r[0] : r[1]));
+}
 template <int N>
 __device__ __forceinline__ float group_sum(float v) {
     static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group size");
@@ -165,7 +186,7 @@ __device__ __forceinline__ float group_sum(float v) {
     if constexpr (N >= 4) v += dpp_sel<kDppXor2>(v);
     if constexpr (N >= 8) v += dpp_sel<kDppHalfMirror>(v);
     if constexpr (N >= 16) v += dpp_sel<kDppMirror>(v);
-    if constexpr (N == 32) v += __shfl_xor(v, 16, 64);
+    if constexpr (N == 32) v = rows_sum16(v);
     if constexpr (N == 64) v = (read_lane(v, 0) + read_lane(v, 16)) + (read_lane(v, 32) + read_lane(v, 48));
     return v;
 }
@@ -176,10 +197,27 @@ __device__ __forceinline__ float group_max(float v) {
     if constexpr (N >= 4) v = fmaxf(v, dpp_sel<kDppXor2>(v));
     if constexpr (N >= 8) v = fmaxf(v, dpp_sel<kDppHalfMirror>(v));
     if constexpr (N >= 16) v = fmaxf(v, dpp_sel<kDppMirror>(v));
-    if constexpr (N == 32) v = fmaxf(v, __shfl_xor(v, 16, 64));
+    if constexpr (N == 32) {
+        const unsigned u = __builtin_bit_cast(unsigned, v);
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        v = fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+    }
     if constexpr (N == 64) v = fmaxf(fmaxf(read_lane(v, 0), read_lane(v, 16)), fmaxf(read_lane(v, 32), read_lane(v, 48)));
     return v;
 }
+constexpr int kDppRor8 = 0x128;  // row_ror:8 (lane l <- l ^ 8 inside a row of 16)
+
+// Sum over the lanes l' with l' % N == l % N (N = 8, 16 or 32): the lanes
+// that hold the same column position in each group of N.
+template <int N>
+__device__ __forceinline__ float column_sum(float v) {
+    static_assert(N == 8 || N == 16 || N == 32 || N == 64, "group size");
+    if constexpr (N == 8) v += dpp_sel<kDppRor8>(v);
+    if constexpr (N <= 16) v = rows_sum16(v);
+    if constexpr (N <= 32) v = halves_sum32(v);
+    return v;
+}
+
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 __device__ __forceinline__ float wave_max(float v) { return group_max<64>(v); }
 
@@ -237,6 +275,21 @@ __device__ __forceinline__ uint4 buf_load16_co(__amdgpu_buffer_rsrc_t r, uint32_
     const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kSC1);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
+
+// Activations (per-layer buffers written exactly once per step by other
+// workgroups, before the event their readers wait on) are read with plain,
+// L2-cacheable loads. This is safe because (1) the producers write them with
+// agent-coherent stores, which reach memory past every L2, (2) no workgroup
+// touches such a buffer before its event fires, so no L2 holds a line of it
+// from earlier in the step, and (3) each step starts with an agent-scope
+// acquire that drops every line cached in an earlier step. The other
+// workgroups of the same XCD then hit in the shared L2 instead of going to
+// memory, which matters when every worker reads the whole input vector.
+// Buffers reused within a step (attention partials, rings) keep coherent loads.
+__device__ __forceinline__ uint4 buf_load16_act(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return buf_load16(r, voff, soff);
+}
+__device__ __forceinline__ float ld_act(const float* p) { return *p; }
 
 // One weight row as seen by a GEMV: resource of its matrix tile and the
 // byte offset of the row inside it.

@@ -258,6 +258,9 @@ extern __shared__ __attribute__((aligned(16))) float mk_dyn_lds[];
 template <typename WT, int NB>
 __global__ __launch_bounds__(kThreads) void k_persistent(KParams p) {
     const Lds s = carve_lds(mk_dyn_lds, p.Hq / p.Hkv, p.chunk);
+    // drop L2 lines cached in earlier steps: activations are then read with
+    // plain loads (see buf_load16_act)
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if ((int)blockIdx.x >= p.n_workers) {
         // four scheduler waves per scheduler workgroup
         if (p.jit_on && (threadIdx.x >> 6) < 4) scheduler_wave(p);
@@ -272,6 +275,9 @@ __global__ __launch_bounds__(kThreads) void k_persistent(KParams p) {
 }
 
 template <typename WT, int NB>
+// Kernel-per-operator launches: the previous level's outputs are visible
+// through the launch's own acquire (the same guarantee ordinary stream-ordered
+// kernels rely on), so activations are read with plain loads here too.
 __global__ __launch_bounds__(kThreads) void k_level_gemv(KParams p, const int32_t* ids) {
     const Lds s = carve_lds(mk_dyn_lds, p.Hq / p.Hkv, p.chunk);
     const TaskRec t = p.tasks[ids[blockIdx.x]];

@@ -198,7 +198,7 @@ __device__ __forceinline__ void gemv_stream(const KParams& p, Stream& st, const 
         const bool kv = j < nsw && k < K;
 #pragma unroll
         for (int e = 0; e < E; e += 4) {
-            const uint4 v = buf_load16_co(xr_rs, kv ? (uint32_t)(k + e) * 4u : kOOB, 0);
+            const uint4 v = buf_load16_act(xr_rs, kv ? (uint32_t)(k + e) * 4u : kOOB, 0);
             xr[j][e + 0] = __uint_as_float(v.x);
             xr[j][e + 1] = __uint_as_float(v.y);
             xr[j][e + 2] = __uint_as_float(v.z);
@@ -332,7 +332,7 @@ __device__ __forceinline__ void run_stream_task(const KParams& p, Stream& st, co
         case OP_O: {
             const float* xin = layer_in(p, l);
             float* o = layer_buf(p, l, p.off_xmid);
-            auto out = [&](int r, int, float v, float) { st_co(&o[r], ld_co(&xin[r]) + v); };
+            auto out = [&](int r, int, float v, float) { st_co(&o[r], ld_act(&xin[r]) + v); };
             gemv_stream_dispatch<WT, false>(p, st, ring, qe, r0, r1, p.QD, layer_buf(p, l, p.off_attn), (const WT*)nullptr,
                                             out, s);
             break;
@@ -352,7 +352,7 @@ __device__ __forceinline__ void run_stream_task(const KParams& p, Stream& st, co
         case OP_DOWN: {
             const float* xm = layer_buf(p, l, p.off_xmid);
             float* o = layer_out(p, l);
-            auto out = [&](int r, int, float v, float) { st_co(&o[r], ld_co(&xm[r]) + v); };
+            auto out = [&](int r, int, float v, float) { st_co(&o[r], ld_act(&xm[r]) + v); };
             gemv_stream_dispatch<WT, false>(p, st, ring, qe, r0, r1, p.F, layer_buf(p, l, p.off_h), (const WT*)nullptr,
                                             out, s);
             break;

@@ -77,7 +77,7 @@ __device__ __forceinline__ void block_rstd(const float* x, int ldx, int K, int B
         ss[b] = 0.f;
         if (b < B)
             for (int k = tid * 4; k < K; k += kThreads * 4) {
-                const uint4 u = buf_load16_co(xr, (uint32_t)(b * ldx + k) * 4u, 0);
+                const uint4 u = buf_load16_act(xr, (uint32_t)(b * ldx + k) * 4u, 0);
                 const float4 v = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
                                              __uint_as_float(u.w));
                 ss[b] += v.x * v.x;
@@ -154,7 +154,7 @@ __device__ __forceinline__ void gemv_ksplit(int r0, int r1, int K, const float* 
             const uint32_t xo = (kvalid[j] && b < B) ? (uint32_t)(b * ldx) * 4u + voff[j] / (uint32_t)sizeof(WT) * 4u : kOOB;
 #pragma unroll
             for (int e = 0; e < E; e += 4) {
-                const uint4 v = buf_load16_co(xr_rs, xo, (uint32_t)e * 4u);
+                const uint4 v = buf_load16_act(xr_rs, xo, (uint32_t)e * 4u);
                 xr[j][b][e + 0] = __uint_as_float(v.x);
                 xr[j][b][e + 1] = __uint_as_float(v.y);
                 xr[j][b][e + 2] = __uint_as_float(v.z);
@@ -293,7 +293,7 @@ __device__ __forceinline__ void gemv_rowwave(int r0, int r1, int K, const float*
                 float xv[E];
 #pragma unroll
                 for (int e = 0; e < E; e += 4) {
-                    const uint4 v = buf_load16_co(x_rs, (uint32_t)(b * ldx + k + e) * 4u, 0);
+                    const uint4 v = buf_load16_act(x_rs, (uint32_t)(b * ldx + k + e) * 4u, 0);
                     xv[e] = __uint_as_float(v.x) * g[e];
                     xv[e + 1] = __uint_as_float(v.y) * g[e + 1];
                     xv[e + 2] = __uint_as_float(v.z) * g[e + 2];
@@ -366,18 +366,19 @@ struct MatTile {
 // With a batch of several sequences the GEMV is a thin matrix product
 // Y[r][b] = sum_k W[r][k] xg[b][k] (xg = x * norm gain), done here on the
 // 16x16x32 bf16 matrix cores: a 16-row weight tile is the A operand (lane
-// l holds 8 consecutive k of row l % 16), the batch is the N dimension.
-// The fp32 activations are split into two bf16 terms, xg = hi + lo with
-// lo = bf16(xg - hi), and both are multiplied, so the product keeps about
-// 16 significant bits of xg (error ~2^-17 relative) instead of bf16's 8.
-// x is staged through LDS a piece of 256 k at a time (converted once per
-// workgroup, laid out as the MFMA B operand); within a piece wave w takes
-// the 64 consecutive k [64w, 64w + 64), so each weight row is read as whole
-// 128-byte lines. Weight loads of the next piece are in flight while the
-// current one is multiplied. Each wave's partial tiles are added across
-// waves in wave order through LDS. A task's rows are taken in passes of
-// TMAX tiles (x is staged again per pass); rows past a segment and k past
-// K load through an out-of-range offset (zeros, no traffic).
+// l holds 8 consecutive k of row l % 16), the batch is the N dimension
+// (lane l holds the same 8 k of sequence l % 16). The fp32 activations are
+// split into two bf16 terms, xg = hi + lo with lo = bf16(xg - hi), and both
+// are multiplied, so the product keeps about 16 significant bits of xg
+// (relative error ~2^-17) instead of bf16's 8.
+// K is cut into 64-k blocks dealt to the waves round-robin (block j to wave
+// j % 4); a block is two MFMA k-steps, so every weight row is read in whole
+// 128-byte lines, and each wave loads and converts only its own x values:
+// no LDS staging and no barrier inside the loop. Weights and x of the next
+// block are in flight while the current one is multiplied. The four waves'
+// partial tiles are added in wave order through LDS. A task's rows are
+// taken in passes of TMAX tiles; rows past a run and k past K load through
+// an out-of-range offset (zeros, no traffic).
 typedef __bf16 mk_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float mk_f32x4 __attribute__((ext_vector_type(4)));
 
@@ -388,13 +389,9 @@ struct MSeg {
     int out0;                     // output row of the run's first row
 };
 
-__device__ __forceinline__ mk_f32x4 mfma_bf16(const uint4& a, const uint4& b, mk_f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mk_bf16x8, a), __builtin_bit_cast(mk_bf16x8, b), c,
-                                                   0, 0, 0);
+__device__ __forceinline__ mk_f32x4 mfma_bf16(const uint4& a, const mk_bf16x8& b, mk_f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mk_bf16x8, a), b, c, 0, 0, 0);
 }
-
-constexpr int kMfmaPieceK = 256;                      // k staged per piece
-constexpr int kMfmaStageU4 = (kMfmaPieceK / 32) * 128;  // uint4 per staged piece (hi + lo)
 
 template <int NB, bool DUAL, int TMAX, int NSEG, typename OutFn>
 __device__ __forceinline__ void gemv_mfma(const MSeg (&seg)[NSEG], int K, const float* x, int ldx, int B,
@@ -404,69 +401,17 @@ __device__ __forceinline__ void gemv_mfma(const MSeg (&seg)[NSEG], int K, const 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lk = lane >> 4;
     const uint32_t rowbytes = (uint32_t)K * 2u;
-    const int npiece = (K + kMfmaPieceK - 1) / kMfmaPieceK;
-    uint4* stage = reinterpret_cast<uint4*>(s.q);  // 2 x kMfmaStageU4 (aliases the attention scratch)
+    const int nblk = (K + 63) >> 6;
+    const int nmine = (nblk - wave + kWaves - 1) / kWaves;  // blocks of this wave
     const __amdgpu_buffer_rsrc_t xr_rs = make_rsrc(x, (uint32_t)(B * ldx) * 4u);
     const __amdgpu_buffer_rsrc_t g_rs = make_rsrc(gain, gain ? rowbytes : 0u);
+    const bool bok = li < B;
 
-    // staging: thread tid converts units (b = tid % 16, 8-k group tid/16 and
-    // tid/16 + 16) of each piece
-    const int fb = tid & 15;
-    float ss = 0.f;  // sum of x^2 over this thread's k (for the norm statistic)
-    struct Fill {
-        uint4 x[2][2];
-        uint4 g[2];
-    };
-    auto fill_load = [&](Fill& f, int pc) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int k = pc * kMfmaPieceK + ((tid >> 4) + 16 * u) * 8;
-            const bool ok = fb < B && k < K && pc < npiece;
-            const uint32_t xo = ok ? (uint32_t)(fb * ldx + k) * 4u : kOOB;
-            f.x[u][0] = buf_load16_co(xr_rs, xo, 0);
-            f.x[u][1] = buf_load16_co(xr_rs, xo, 16);
-            f.g[u] = buf_load16(g_rs, (k < K && pc < npiece) ? (uint32_t)k * 2u : kOOB, 0);
-        }
-    };
-    auto fill_store = [&](const Fill& f, int buf, bool stat) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int grp = (tid >> 4) + 16 * u;  // 8-k group within the piece
-            float xv[8], gv[8];
-            xv[0] = __uint_as_float(f.x[u][0].x); xv[1] = __uint_as_float(f.x[u][0].y);
-            xv[2] = __uint_as_float(f.x[u][0].z); xv[3] = __uint_as_float(f.x[u][0].w);
-            xv[4] = __uint_as_float(f.x[u][1].x); xv[5] = __uint_as_float(f.x[u][1].y);
-            xv[6] = __uint_as_float(f.x[u][1].z); xv[7] = __uint_as_float(f.x[u][1].w);
-            if (gain) Vec16<bf16_t>::widen(f.g[u], gv);
-            else
-#pragma unroll
-                for (int e = 0; e < 8; ++e) gv[e] = 1.f;
-            uint32_t hw[4], lw[4];
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                if (stat) {
-                    ss += xv[e] * xv[e];
-                    ss += xv[e + 1] * xv[e + 1];
-                }
-                const float a0 = xv[e] * gv[e], a1 = xv[e + 1] * gv[e + 1];
-                const bf16_t h0 = f32_to_bf16(a0), h1 = f32_to_bf16(a1);
-                const bf16_t l0 = f32_to_bf16(a0 - __uint_as_float((uint32_t)h0 << 16));
-                const bf16_t l1 = f32_to_bf16(a1 - __uint_as_float((uint32_t)h1 << 16));
-                hw[e / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-                lw[e / 2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-            }
-            // B operand of chunk grp/4: lane (grp % 4) * 16 + b holds k 8*(grp%4)..+8 of batch b
-            uint4* st = stage + buf * kMfmaStageU4 + (grp >> 2) * 128 + (grp & 3) * 16 + fb;
-            st[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-            st[64] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-        }
-    };
-
-    // tiles of the task: segment by segment, 16 rows each
     int ntile = 0;
 #pragma unroll
     for (int q = 0; q < NSEG; ++q) ntile += (seg[q].n + 15) >> 4;
 
+    float ss = 0.f;  // sum of x^2 over this lane's (sequence li, k) values
     for (int t0 = 0; t0 < ntile; t0 += TMAX) {
         // this pass's tile table (uniform): resources, row offset, valid rows, output row
         __amdgpu_buffer_rsrc_t ta[TMAX], tb[TMAX];
@@ -474,7 +419,7 @@ __device__ __forceinline__ void gemv_mfma(const MSeg (&seg)[NSEG], int K, const 
         int tval[TMAX], tout[TMAX];
 #pragma unroll
         for (int t = 0; t < TMAX; ++t) {
-            // segment q holding task tile t0 + t, and the tile's index gt in it
+            // run q holding task tile t0 + t, and the tile's index gt in it
             int gt = t0 + t, q = NSEG;
 #pragma unroll
             for (int qq = 0; qq < NSEG; ++qq) {
@@ -499,18 +444,27 @@ __device__ __forceinline__ void gemv_mfma(const MSeg (&seg)[NSEG], int K, const 
                     tout[t] = seg[qq].out0 + gt * 16;
                 }
         }
-        // per-lane weight offsets: row li of the tile, k of this wave's two chunks
-        auto w_load = [&](uint4 (&w)[TMAX][NM][2], int pc) {
+        struct Stage {
+            uint4 w[TMAX][NM][2];
+            uint4 x[2][2];
+            uint4 g[2];
+        };
+        // block i of this wave: k = 64 * (wave + 4 i) + 32 c + 8 lk
+        auto load = [&](Stage& st, int i) {
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
-                const int k = pc * kMfmaPieceK + wave * 64 + c * 32 + lk * 8;
-                const bool kok = k < K && pc < npiece;
+                const int k = ((wave + kWaves * i) << 6) + c * 32 + lk * 8;
+                const bool kok = k < K && i < nmine;
+                const uint32_t xo = (kok && bok) ? (uint32_t)(li * ldx + k) * 4u : kOOB;
 #pragma unroll
                 for (int t = 0; t < TMAX; ++t) {
                     const uint32_t vo = (kok && li < tval[t]) ? (uint32_t)li * rowbytes + (uint32_t)k * 2u : kOOB;
-                    w[t][0][c] = buf_load16(ta[t], vo, tsoff[t]);
-                    if constexpr (DUAL) w[t][1][c] = buf_load16(tb[t], vo, tsoff[t]);
+                    st.w[t][0][c] = buf_load16(ta[t], vo, tsoff[t]);
+                    if constexpr (DUAL) st.w[t][1][c] = buf_load16(tb[t], vo, tsoff[t]);
                 }
+                st.x[c][0] = buf_load16_act(xr_rs, xo, 0);
+                st.x[c][1] = buf_load16_act(xr_rs, xo, 16);
+                st.g[c] = buf_load16(g_rs, kok ? (uint32_t)k * 2u : kOOB, 0);
             }
         };
         mk_f32x4 acc[TMAX][NM];
@@ -518,48 +472,55 @@ __device__ __forceinline__ void gemv_mfma(const MSeg (&seg)[NSEG], int K, const 
         for (int t = 0; t < TMAX; ++t)
 #pragma unroll
             for (int m = 0; m < NM; ++m) acc[t][m] = mk_f32x4{0.f, 0.f, 0.f, 0.f};
-        auto compute = [&](const uint4 (&w)[TMAX][NM][2], int buf) {
-            const uint4* st = stage + buf * kMfmaStageU4 + (wave * 2) * 128 + lane;
-            const uint4 h0 = st[0], l0 = st[64], h1 = st[128], l1 = st[192];
+        const bool stat = gain != nullptr && t0 == 0;
+        auto compute = [&](const Stage& st) {
 #pragma unroll
-            for (int t = 0; t < TMAX; ++t) {
-                if (t0 + t >= ntile) continue;
+            for (int c = 0; c < 2; ++c) {
+                float xv[8], gv[8];
+                xv[0] = __uint_as_float(st.x[c][0].x); xv[1] = __uint_as_float(st.x[c][0].y);
+                xv[2] = __uint_as_float(st.x[c][0].z); xv[3] = __uint_as_float(st.x[c][0].w);
+                xv[4] = __uint_as_float(st.x[c][1].x); xv[5] = __uint_as_float(st.x[c][1].y);
+                xv[6] = __uint_as_float(st.x[c][1].z); xv[7] = __uint_as_float(st.x[c][1].w);
+                if (gain) Vec16<bf16_t>::widen(st.g[c], gv);
+                else
 #pragma unroll
-                for (int m = 0; m < NM; ++m) {
-                    acc[t][m] = mfma_bf16(w[t][m][0], h0, acc[t][m]);
-                    acc[t][m] = mfma_bf16(w[t][m][0], l0, acc[t][m]);
-                    acc[t][m] = mfma_bf16(w[t][m][1], h1, acc[t][m]);
-                    acc[t][m] = mfma_bf16(w[t][m][1], l1, acc[t][m]);
+                    for (int e = 0; e < 8; ++e) gv[e] = 1.f;
+                // hardware round-to-nearest-even conversions (v_cvt_pk_bf16_f32)
+                mk_bf16x8 hi, lo;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    if (stat) ss += xv[e] * xv[e];
+                    const float a = xv[e] * gv[e];
+                    const __bf16 h = (__bf16)a;
+                    hi[e] = h;
+                    lo[e] = (__bf16)(a - (float)h);
+                }
+#pragma unroll
+                for (int t = 0; t < TMAX; ++t) {
+                    if (t0 + t >= ntile) continue;
+#pragma unroll
+                    for (int m = 0; m < NM; ++m) {
+                        acc[t][m] = mfma_bf16(st.w[t][m][c], hi, acc[t][m]);
+                        acc[t][m] = mfma_bf16(st.w[t][m][c], lo, acc[t][m]);
+                    }
                 }
             }
         };
-        const bool stat = gain != nullptr && t0 == 0;
-        Fill fa, fbuf;
-        uint4 wa[TMAX][NM][2], wb[TMAX][NM][2];
-        fill_load(fa, 0);
-        w_load(wa, 0);
-        fill_store(fa, 0, stat);
-        __syncthreads();
+        Stage sa, sb;
+        load(sa, 0);
         if (tr && tid == 0 && t0 == 0) s.marks[0] = now_ticks();
-        for (int pc = 0; pc < npiece; pc += 2) {
-            fill_load(fbuf, pc + 1);
-            w_load(wb, pc + 1);
-            compute(wa, 0);
-            if (pc + 1 < npiece) fill_store(fbuf, 1, stat);
-            __syncthreads();
-            fill_load(fa, pc + 2);
-            w_load(wa, pc + 2);
-            if (pc + 1 < npiece) compute(wb, 1);
-            if (pc + 2 < npiece) fill_store(fa, 0, stat);
-            __syncthreads();
+        for (int i = 0; i < nmine; i += 2) {
+            load(sb, i + 1);
+            compute(sa);
+            load(sa, i + 2);
+            if (i + 1 < nmine) compute(sb);
         }
         if (stat) {
             // norm statistic: lanes b, b+16, b+32, b+48 of each wave, then waves in order
-            ss += __shfl_xor(ss, 16, 64);
-            ss += __shfl_xor(ss, 32, 64);
+            ss = column_sum<16>(ss);
             if (lane < 16) s.red[wave * 16 + lane] = ss;
         }
-        // partial tiles: D layout, lane l holds rows 4*(l/16)+r of batch l % 16
+        // partial tiles: D layout, lane l holds rows 4*(l/16)+r of sequence l % 16
 #pragma unroll
         for (int t = 0; t < TMAX; ++t)
 #pragma unroll
@@ -576,7 +537,7 @@ __device__ __forceinline__ void gemv_mfma(const MSeg (&seg)[NSEG], int K, const 
         if (tr && tid == 0) s.marks[1] = now_ticks();
         __syncthreads();
         {
-            const int i = tid >> 4, b = tid & 15;  // row in tile, batch
+            const int i = tid >> 4, b = tid & 15;  // row in tile, sequence
             const int pl = ((i >> 2) * 16 + b) * 4 + (i & 3);
 #pragma unroll
             for (int t = 0; t < TMAX; ++t) {
@@ -656,7 +617,7 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
             auto rowp = [&](int r, RowRef& a0, RowRef& b2) { to.row(r, a0); b2 = a0; };
             auto out = [&](int r, int b, float v, float) {
                 const int64_t i = (int64_t)b * H + r;
-                st_co(&o[i], ld_co(&xin[i]) + v);
+                st_co(&o[i], ld_act(&xin[i]) + v);
             };
             if constexpr (kMfma) {
                 const MSeg sg[1] = {{to.r, to.r, to.n, to.lo}};
@@ -700,7 +661,7 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
             auto rowp = [&](int r, RowRef& a0, RowRef& b2) { td.row(r, a0); b2 = a0; };
             auto out = [&](int r, int b, float v, float) {
                 const int64_t i = (int64_t)b * H + r;
-                st_co(&o[i], ld_co(&xm[i]) + v);
+                st_co(&o[i], ld_act(&xm[i]) + v);
             };
             if constexpr (kMfma) {
                 const MSeg sg[1] = {{td.r, td.r, td.n, td.lo}};
@@ -849,9 +810,11 @@ __device__ __forceinline__ int64_t kv_offset(const KParams& p, int l, int b, int
 }
 
 // RMSNorm over one head (D = 64 or 128) held by a wave as D/64 values per
-// lane (element j in lane j % 64, slot j / 64), then rotate-half RoPE.
-template <typename WT, int D>
-__device__ __forceinline__ void head_norm_rope(float (&v)[2], const WT* gain, bool norm, float eps, const float2* rope_row) {
+// lane (element j in lane j % 64, slot j / 64), then rotate-half RoPE. The
+// gains g (same slots) and this lane's (cos, sin) are loaded by the caller
+// ahead of time.
+template <int D>
+__device__ __forceinline__ void head_norm_rope(float (&v)[2], const float (&g)[2], bool norm, float eps, float2 cs) {
     const int lane = threadIdx.x & 63;
     constexpr int per = D / 64;
     if (norm) {
@@ -861,19 +824,16 @@ __device__ __forceinline__ void head_norm_rope(float (&v)[2], const WT* gain, bo
         ss = wave_sum(ss);
         const float rs = 1.0f / sqrtf(ss / (float)D + eps);
 #pragma unroll
-        for (int i = 0; i < per; ++i) v[i] = (v[i] * rs) * load_scalar<WT>(gain, lane + 64 * i);
+        for (int i = 0; i < per; ++i) v[i] = (v[i] * rs) * g[i];
     }
     if constexpr (per == 2) {
         // pair (lane, lane + 64) sits in one lane
-        const float2 cs = rope_row[lane];
         const float a = v[0], b = v[1];
         v[0] = a * cs.x - b * cs.y;
         v[1] = b * cs.x + a * cs.y;
     } else {
         // D = 64: pair (i, i + 32) spans lanes i and i + 32
-        const float other = __shfl_xor(v[0], 32, 64);
-        const int i = lane & 31;
-        const float2 cs = rope_row[i];
+        const float other = halves_partner(v[0]);
         if (lane < 32) v[0] = v[0] * cs.x - other * cs.y;
         else v[0] = v[0] * cs.x + other * cs.y;
     }
@@ -926,17 +886,28 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
         const int hh = wave + i * kWaves;
         qv[i][0] = qv[i][1] = 0.f;
         if (hh < G) {
-            qv[i][0] = ld_co(&qkv[(int64_t)(g * G + hh) * D + lane]);
-            if constexpr (D > 64) qv[i][1] = ld_co(&qkv[(int64_t)(g * G + hh) * D + lane + 64]);
+            qv[i][0] = ld_act(&qkv[(int64_t)(g * G + hh) * D + lane]);
+            if constexpr (D > 64) qv[i][1] = ld_act(&qkv[(int64_t)(g * G + hh) * D + lane + 64]);
         }
     }
     float nv[2] = {0.f, 0.f};
     const bool appender = owner && wave < 2;
     if (appender) {
         const int64_t base = wave == 0 ? (int64_t)p.QD + (int64_t)g * D : (int64_t)p.QD + p.KD + (int64_t)g * D;
-        nv[0] = ld_co(&qkv[base + lane]);
-        if constexpr (D > 64) nv[1] = ld_co(&qkv[base + lane + 64]);
+        nv[0] = ld_act(&qkv[base + lane]);
+        if constexpr (D > 64) nv[1] = ld_act(&qkv[base + lane + 64]);
     }
+    // norm gains and this lane's RoPE factors, needed as soon as q arrives
+    const bool qkn = p.qk_norm != 0;
+    float gq[2] = {1.f, 1.f}, gk[2] = {1.f, 1.f};
+    if (qkn) {
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i) {
+            gq[i] = load_scalar<WT>((const WT*)lw.q_norm, lane + 64 * i);
+            gk[i] = load_scalar<WT>((const WT*)lw.k_norm, lane + 64 * i);
+        }
+    }
+    const float2 cs = p.rope[(int64_t)pos * (D / 2) + (D == 128 ? lane : (lane & 31))];
     asm volatile("" ::: "memory");
 
     // K/V rows of this split: lane (rr, cc) holds 16 bytes of row
@@ -996,20 +967,18 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
     }
 
     // 1. query heads of this group: norm + RoPE into LDS
-    const float2* rope_row = p.rope + (int64_t)pos * (D / 2);
-    const bool qkn = p.qk_norm != 0;
 #pragma unroll
     for (int i = 0; i < QPW; ++i) {
         const int hh = wave + i * kWaves;
         if (hh < G) {
-            head_norm_rope<WT, D>(qv[i], (const WT*)lw.q_norm, qkn, p.eps, rope_row);
+            head_norm_rope<D>(qv[i], gq, qkn, p.eps, cs);
             s.q[hh * D + lane] = qv[i][0];
             if constexpr (D > 64) s.q[hh * D + lane + 64] = qv[i][1];
         }
     }
     // 2. owner: new k (norm + RoPE) and v, rounded to the cache type, appended
     if (appender) {
-        if (wave == 0) head_norm_rope<WT, D>(nv, (const WT*)lw.k_norm, qkn, p.eps, rope_row);
+        if (wave == 0) head_norm_rope<D>(nv, gk, qkn, p.eps, cs);
         WT* dst = (WT*)(wave == 0 ? p.kv_k : p.kv_v) + kv_offset(p, l, b, g, pos);
 #pragma unroll
         for (int i = 0; i < D / 64; ++i) {
@@ -1055,9 +1024,9 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
 #pragma unroll
             for (int hh = 0; hh < GP; ++hh) d[hh] = group_sum<LPR>(d[hh]);
             if (valid && cc == 0) {
+                // probabilities are kept row-major, GP heads per key
 #pragma unroll
-                for (int hh = 0; hh < GP; ++hh)
-                    if (hh < G) s.p[hh * C + j] = d[hh] * p.scale;
+                for (int hh = 0; hh < GP; ++hh) s.p[j * GP + hh] = d[hh] * p.scale;
             }
         }
     }
@@ -1067,12 +1036,12 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
     // 4. per-head max and exp-sum over this split (fixed strides and tree)
     for (int hh = wave; hh < G; hh += kWaves) {
         float m = -INFINITY;
-        for (int j = lane; j < n; j += 64) m = fmaxf(m, s.p[hh * C + j]);
+        for (int j = lane; j < n; j += 64) m = fmaxf(m, s.p[j * GP + hh]);
         m = wave_max(m);
         float sum = 0.f;
         for (int j = lane; j < n; j += 64) {
-            const float e = __expf(s.p[hh * C + j] - m);
-            s.p[hh * C + j] = e;
+            const float e = __expf(s.p[j * GP + hh] - m);
+            s.p[j * GP + hh] = e;
             sum += e;
         }
         sum = wave_sum(sum);
@@ -1108,9 +1077,12 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
                 VK::widen(vr[it], vf);
             }
             const int jc = valid ? j : 0;
+            float pr[GP];
+#pragma unroll
+            for (int hh = 0; hh < GP; ++hh) pr[hh] = s.p[jc * GP + hh];
 #pragma unroll
             for (int hh = 0; hh < GP; ++hh) {
-                const float pj = (valid && hh < G) ? s.p[hh * C + jc] : 0.f;
+                const float pj = (valid && hh < G) ? pr[hh] : 0.f;
 #pragma unroll
                 for (int e = 0; e < E; ++e) acc[hh][e] = fmaf(pj, vf[e], acc[hh][e]);
             }
@@ -1121,8 +1093,7 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
     for (int hh = 0; hh < GP; ++hh)
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-#pragma unroll
-            for (int o = LPR; o < 64; o <<= 1) acc[hh][e] += __shfl_xor(acc[hh][e], o, 64);
+            acc[hh][e] = column_sum<LPR>(acc[hh][e]);
         }
     if (rr == 0) {
 #pragma unroll
