@@ -243,26 +243,28 @@ def seq_lengths(wl: Workload, seed: int = SEED_LENGTHS) -> np.ndarray:
     raise ValueError(kind)
 
 
-def kv_contents(shape: ModelShape, lengths: np.ndarray, capacity: int, seed: int = SEED_KV) -> List[Dict[str, np.ndarray]]:
-    """Per sequence: k, v arrays [n_layers, n_kv_heads, capacity, head_dim] (cache dtype).
-
-    Positions < length hold N(0, 1) values; the rest are zero.
-    """
-    out = []
+def kv_sequence(shape: ModelShape, b: int, n: int, capacity: int, seed: int = SEED_KV) -> Dict[str, np.ndarray]:
+    """KV cache of sequence b of a workload: k, v arrays [n_layers, n_kv_heads,
+    capacity, head_dim] (cache dtype); positions < n hold N(0, 1) values, the
+    rest are zero. The random stream depends on (b, layer, head, k/v) only, so
+    one sequence can be generated without the others."""
     L, Hkv, D = shape.n_layers, shape.n_kv_heads, shape.head_dim
     dt = np.uint16 if shape.kv_dtype == "bf16" else np.float32
-    for b, n in enumerate(lengths):
-        n = int(n)
-        seq = {}
-        for kind, kid in (("k", 0), ("v", 1)):
-            arr = np.zeros((L, Hkv, capacity, D), dtype=dt)
-            for l in range(L):
-                for h in range(Hkv):
-                    stream = ((b * 4096 + l) * 256 + h) * 2 + kid
-                    arr[l, h, :n] = normal(seed, stream, (n, D), 1.0, shape.kv_dtype)
-            seq[kind] = arr
-        out.append(seq)
-    return out
+    n = int(n)
+    seq = {}
+    for kind, kid in (("k", 0), ("v", 1)):
+        arr = np.zeros((L, Hkv, capacity, D), dtype=dt)
+        for l in range(L):
+            for h in range(Hkv):
+                stream = ((b * 4096 + l) * 256 + h) * 2 + kid
+                arr[l, h, :n] = normal(seed, stream, (n, D), 1.0, shape.kv_dtype)
+        seq[kind] = arr
+    return seq
+
+
+def kv_contents(shape: ModelShape, lengths: np.ndarray, capacity: int, seed: int = SEED_KV) -> List[Dict[str, np.ndarray]]:
+    """Per sequence b: kv_sequence(shape, b, lengths[b], capacity)."""
+    return [kv_sequence(shape, b, int(n), capacity, seed) for b, n in enumerate(lengths)]
 
 
 def tokens(wl: Workload, n: Optional[int] = None, seed: int = SEED_TOKENS, stream: int = 0) -> np.ndarray:
