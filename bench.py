@@ -6,8 +6,10 @@ Workload (the headline): the 36-layer Qwen3-8B-shaped decoder (hidden 4096,
 prefilled by teacher-forced decode steps (outside the timed region), then
 greedy decode. One timed step = one mk_decode_step (the whole step in one
 persistent launch) + mk_argmax + the caller's seq_lens increment.
-A second line of numbers (reported inside the same JSON object) covers the
-same model at batch 16 with KV lengths log-uniform in [32, 4096].
+Further numbers, reported inside the same JSON object: the same model at
+batch 16 with KV lengths log-uniform in [32, 4096] (`batch16`), at batch 8
+with a paged cache and KV lengths uniform in [4096, 16384] (`batch8_paged`),
+and one 8B-shaped layer with hidden-state input/output (`layer8b`).
 
 Printed: ONE JSON line with tok/s (value), ms/step, HBM roofline of the
 megakernel (algorithmic bytes / average launch time from HIP events on the
@@ -73,6 +75,9 @@ def parse():
     ap.add_argument("--prompt", type=int, default=1024, help="prefill length (teacher-forced steps)")
     ap.add_argument("--no-b16", action="store_true", help="skip the batch-16 measurement")
     ap.add_argument("--b16-steps", type=int, default=64)
+    ap.add_argument("--no-paged", action="store_true", help="skip the paged batch-8 long-context measurement")
+    ap.add_argument("--paged-steps", type=int, default=32)
+    ap.add_argument("--no-layer", action="store_true", help="skip the single-layer measurement")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--mode", type=int, default=0, help="0 persistent, 1 kernel-per-op")
@@ -92,7 +97,7 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     if args.quick:
-        args.prompt, args.steps, args.warmup, args.b16_steps = 64, 8, 2, 8
+        args.prompt, args.steps, args.warmup, args.b16_steps, args.paged_steps = 64, 8, 2, 8, 4
 
     import torch
 
@@ -255,6 +260,99 @@ def main():
         }
         plan16.close()
         del kv16
+
+    # ---------------------------------------------------------------- batch 8, paged, long context
+    if not args.no_paged:
+        wl8 = synth.WORKLOADS["q8b_b8_paged"]
+        B8, st8 = wl8.batch, args.paged_steps
+        lens8 = synth.seq_lengths(wl8)
+        cap8 = int(lens8.max()) + args.warmup + st8 + 8
+        table8 = synth.block_table([cap8] * B8, wl8.kv_block)
+        t0 = time.time()
+        kv8 = harness.DeviceKV(shape, B8, cap8, paged=True, block=wl8.kv_block, block_table=table8)
+        # cache contents: seeded N(0,1) drawn on the device (timing does not
+        # depend on the values; the parity tests use the host generator)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(synth.SEED_KV)
+        for t in (kv8.k, kv8.v):
+            for l in range(t.shape[0]):
+                t[l].copy_(torch.randn(t[l].shape, generator=gen, device=dev).to(torch.bfloat16).view(torch.int16))
+        torch.cuda.synchronize()
+        log("B=8 paged KV ready in %.1fs (%d blocks)" % (time.time() - t0, kv8.n_blocks))
+        plan8 = harness.build_plan(shape, B8, cap8, paged=True, block=wl8.kv_block, max_blocks=table8.shape[1], **opts)
+        d_tok8 = torch.from_numpy(synth.tokens(wl8)).to(dev)
+        d_len8 = torch.from_numpy(lens8.astype(np.int32)).to(dev)
+        logits8 = torch.empty((B8, shape.vocab), dtype=torch.float32, device=dev)
+        run(args.warmup, plan8, kv8, d_tok8, d_len8, logits8)
+        torch.cuda.synchronize()
+        l8 = d_len8.cpu().numpy().copy()
+        ev8 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(st8)]
+        e0.record(st)
+        run(st8, plan8, kv8, d_tok8, d_len8, logits8, ev8)
+        e1.record(st)
+        torch.cuda.synchronize()
+        err = plan8.device_error()
+        if err:
+            raise SystemExit("device error %d during paged batch-8 steps" % err)
+        t8 = e0.elapsed_time(e1)
+        k8 = np.array([a.elapsed_time(b) for a, b in ev8])
+        b8_bytes = float(np.mean([harness.step_bytes(shape, (l8 + i).tolist(), B8) for i in range(st8)]))
+        ach8 = b8_bytes / (k8.mean() * 1e-3) / 1e9
+        tok8 = B8 * st8 / (t8 * 1e-3)
+        log("B=8 paged: %.3f ms/step (kernel avg %.3f), %.1f tok/s, %.0f GB/s = %.1f%%"
+            % (t8 / st8, k8.mean(), tok8, ach8, 100 * ach8 / PEAK_HBM_GBS))
+        result["batch8_paged"] = {
+            "workload": "q8b_b8_paged: same model, batch 8, paged KV (16-token blocks, permuted block table), "
+                        "KV lengths uniform in [4096, 16384] (seeded)",
+            "value": round(tok8, 2), "unit": "tokens/s", "ms_per_step": round(t8 / st8, 4),
+            "kernel_ms_mean": round(float(k8.mean()), 4), "hbm_gbs": round(ach8, 1),
+            "hbm_frac": round(ach8 / PEAK_HBM_GBS, 4), "bytes_per_launch": int(b8_bytes),
+        }
+        plan8.close()
+        del kv8
+
+    # ---------------------------------------------------------------- one 8B layer, hidden I/O
+    if not args.no_layer:
+        wlL = synth.WORKLOADS["layer8b"]
+        shL = wlL.shape
+        lensL = synth.seq_lengths(wlL)
+        stL = wlL.steps
+        capL = int(lensL.max()) + args.warmup + stL + 8
+        dmL = harness.DeviceModel(shL, synth.model_weights(shL), dev)
+        kvL = harness.DeviceKV(shL, 1, capL)
+        cL = synth.kv_sequence(shL, 0, int(lensL[0]), capL)
+        kvL.load_sequence(0, cL["k"], cL["v"], int(lensL[0]))
+        planL = harness.build_plan(shL, 1, capL, **opts)
+        xs = [torch.from_numpy(synth.hidden_inputs(shL, 1, t)).to(dev) for t in range(args.warmup + stL)]
+        xo = torch.empty((1, shL.hidden), dtype=torch.float32, device=dev)
+        d_lenL = torch.from_numpy(lensL.astype(np.int32)).to(dev)
+        for t in range(args.warmup):
+            planL.step_hidden(dmL.struct, kvL.struct, xs[t], d_lenL, xo)
+            d_lenL += 1
+        torch.cuda.synchronize()
+        l0 = int(d_lenL.item())
+        evL = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(stL)]
+        for t in range(stL):
+            evL[t][0].record(st)
+            planL.step_hidden(dmL.struct, kvL.struct, xs[args.warmup + t], d_lenL, xo)
+            evL[t][1].record(st)
+            d_lenL += 1
+        torch.cuda.synchronize()
+        if planL.device_error():
+            raise SystemExit("device error during single-layer steps")
+        kL = np.array([a.elapsed_time(b) for a, b in evL])
+        bL = float(np.mean([harness.step_bytes(shL, [l0 + i], 1) for i in range(stL)]))
+        achL = bL / (kL.mean() * 1e-3) / 1e9
+        log("layer8b: %.2f us/layer-step (median %.2f), %.0f GB/s = %.1f%%"
+            % (kL.mean() * 1e3, np.median(kL) * 1e3, achL, 100 * achL / PEAK_HBM_GBS))
+        result["layer8b"] = {
+            "workload": "layer8b: one Qwen3-8B-shaped decoder layer, hidden state in/out, batch 1, KV 512 -> 576",
+            "value": round(float(kL.mean()) * 1e3, 2), "unit": "us/layer-step",
+            "median_us": round(float(np.median(kL)) * 1e3, 2), "hbm_gbs": round(achL, 1),
+            "hbm_frac": round(achL / PEAK_HBM_GBS, 4), "bytes_per_launch": int(bL),
+            "note": "386 MB of weights per step; the 256 MB memory-side cache holds part of them between steps",
+        }
+        planL.close()
 
     # ---------------------------------------------------------------- CPU oracle sample
     if not args.no_cpu:

@@ -65,7 +65,12 @@ enum mk_device_error {
  *  jit           attention launch: 0 = default (JIT), 1 = JIT through the
  *                scheduler waves, 2 = AOT with the maximum split count queued.
  *  kv_chunk      KV positions per attention split task (default 128; a
- *                multiple of 16).
+ *                multiple of 16). In a step whose sequences would need more
+ *                than 4 split tasks per worker, the chunk doubles (up to
+ *                kv_chunk_max) until they do not; the rule depends only on
+ *                seq_lens, so every mode computes the same splits.
+ *  kv_chunk_max  upper bound of that doubling (default 1024, lowered to fit
+ *                LDS; set it equal to kv_chunk to keep the chunk fixed).
  *  watchdog_ms   bound on every spin wait of the persistent kernel
  *                (default 2000).
  *  host_only     1: build the task graph on the host only (no HIP calls);
@@ -100,7 +105,8 @@ typedef struct mk_exec_opts {
     int32_t trace;
     int32_t prefetch_kb;
     int32_t lds_stream;
-    int32_t reserved[3];
+    int32_t kv_chunk_max;
+    int32_t reserved[2];
 } mk_exec_opts;
 
 /*

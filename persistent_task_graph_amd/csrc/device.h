@@ -61,6 +61,7 @@ struct KParams {
     const int32_t* seq_lens;
     // shape
     int B, H, Hq, Hkv, D, F, V, L, QD, KD, cap, chunk, max_splits, qk_norm, paged, kv_block, max_blocks;
+    int chunk_max, attn_target;  // per-step attention chunk rule (attn_chunk_for)
     float eps, scale;
     // schedule
     uint32_t epoch;

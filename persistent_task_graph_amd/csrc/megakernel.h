@@ -71,11 +71,12 @@ __device__ __forceinline__ void scheduler_wave(const KParams& p) {
         layer = __shfl(layer, 0, 64);
         t0 = now_ticks();
         // expand: tasks (b, g, s) for every sequence, in sequence order
+        const int chunk = attn_chunk(p);
         int total = 0;
         for (int b = 0; b < p.B; ++b) {
             const int pos = p.seq_lens[b];
             const bool ovf = pos < 0 || pos + 1 > p.cap;
-            const int ns = ovf ? 1 : (pos + 1 + p.chunk - 1) / p.chunk;
+            const int ns = ovf ? 1 : (pos + 1 + chunk - 1) / chunk;
             total += ns * p.Hkv;
         }
         // deal the tasks round-robin to the eligible workers' inboxes,
@@ -89,7 +90,7 @@ __device__ __forceinline__ void scheduler_wave(const KParams& p) {
             for (;; ++b) {
                 const int pos = p.seq_lens[b];
                 const bool ovf = pos < 0 || pos + 1 > p.cap;
-                ns = ovf ? 1 : (pos + 1 + p.chunk - 1) / p.chunk;
+                ns = ovf ? 1 : (pos + 1 + chunk - 1) / chunk;
                 if (i < off + ns * p.Hkv || b == p.B - 1) break;
                 off += ns * p.Hkv;
             }

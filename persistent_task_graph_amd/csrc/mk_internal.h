@@ -79,7 +79,9 @@ struct HostPlan {
     int workers = 0;
     int sched_wgs = 0;
     int jit = 1;  // 1 JIT, 0 AOT attention
-    int kv_chunk = 256;
+    int kv_chunk = 256;     // base keys per split (sizes the partial records)
+    int kv_chunk_max = 256; // largest per-step chunk (sizes the score buffer)
+    int attn_target = 0;    // split tasks per step above which the chunk doubles
     int max_splits = 0;
     int n_levels = 0;
     int cap = 0;  // KV positions per sequence
@@ -122,5 +124,25 @@ MK_HD inline int ev_down(int l) { return 5 * l + 4; }
 MK_HD inline int ev_embed(int n_layers) { return 5 * n_layers; }
 
 MK_HD inline int n_splits_for(int keys, int chunk) { return (keys + chunk - 1) / chunk; }
+
+// Keys per attention split in one step: the plan's chunk c0, doubled while
+// the step would create more than `target` split tasks and the doubled chunk
+// stays within `cmax`. It depends only on the sequence lengths (len(b) =
+// tokens cached before the step), so every execution mode and every task of
+// the step derives the same splits, and hence the same bits.
+template <typename LenFn>
+MK_HD inline int attn_chunk_for(LenFn len, int B, int Hkv, int c0, int cmax, int target) {
+    int c = c0;
+    while (2 * c <= cmax) {
+        long long total = 0;
+        for (int b = 0; b < B; ++b) {
+            const int L = len(b);
+            total += (long long)Hkv * n_splits_for(L < 0 ? 1 : L + 1, c);
+        }
+        if (total <= (long long)target) break;
+        c *= 2;
+    }
+    return c;
+}
 
 }  // namespace mk

@@ -96,6 +96,18 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
     }
     p.cap = d.max_seq_len;
     p.max_splits = n_splits_for(p.cap, p.kv_chunk);
+    {
+        // the per-step chunk may grow to cmax (score buffer: GP * cmax floats)
+        const int G = d.n_heads / d.n_kv_heads, gp = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
+        int cmax = o.kv_chunk_max > 0 ? o.kv_chunk_max : 1024;
+        cmax = std::min(cmax, 16384 / gp);
+        if (o.kv_chunk_max > 0 && (o.kv_chunk_max < p.kv_chunk || o.kv_chunk_max % p.kv_chunk))
+            return fail(err, "opts.kv_chunk_max must be a multiple of kv_chunk");
+        int c = p.kv_chunk;
+        while (2 * c <= cmax) c *= 2;
+        p.kv_chunk_max = c;
+        p.attn_target = 4 * p.workers;
+    }
     if (p.max_splits > 65535) return fail(err, "too many splits per sequence");
 
     const int L = d.n_layers, W = p.workers, B = d.batch, Hkv = d.n_kv_heads;
@@ -318,6 +330,12 @@ struct DryState {
     explicit DryState(const HostPlan& pl) : p(pl) {}
 };
 
+int step_chunk(const DryState& s) {
+    const HostPlan& p = s.p;
+    return attn_chunk_for([&](int b) { return s.seq[b]; }, p.desc.batch, p.desc.n_kv_heads, p.kv_chunk, p.kv_chunk_max,
+                          p.attn_target);
+}
+
 uint64_t level_input_sum(DryState& s, int lv) {
     uint64_t h = 0;
     for (auto& v : s.out[lv]) h += v.load(std::memory_order_acquire);
@@ -344,7 +362,7 @@ bool run_attn(DryState& s, int layer, int bg, int split, int lv) {
     const HostPlan& p = s.p;
     int b = bg / p.desc.n_kv_heads;
     int keys = s.seq[b] + 1;
-    int ns = n_splits_for(keys, p.kv_chunk);
+    int ns = n_splits_for(keys, step_chunk(s));
     if (split >= ns) return false;  // reserved but unused (AOT mode)
     uint64_t sum = level_input_sum(s, lv - 1);
     s.partial[(size_t)bg * p.max_splits + split].store(mix64(sum ^ ((uint64_t)bg << 20) ^ (uint64_t)split),
@@ -452,12 +470,12 @@ bool dry_run(const HostPlan& p, int n_threads, uint64_t seed, int drop_task, int
                 if (!s.mb_head.compare_exchange_strong(h, h + 1)) continue;
                 std::this_thread::sleep_for(std::chrono::microseconds(rng() % 30));
                 int64_t total = 0;
-                for (int b = 0; b < d.batch; ++b) total += (int64_t)d.n_kv_heads * n_splits_for(s.seq[b] + 1, p.kv_chunk);
+                for (int b = 0; b < d.batch; ++b) total += (int64_t)d.n_kv_heads * n_splits_for(s.seq[b] + 1, step_chunk(s));
                 const int64_t start = s.rr.fetch_add(total);
                 int64_t i = 0;
                 const int64_t ne = (int64_t)p.jit_elig.size();
                 for (int b = 0; b < d.batch; ++b) {
-                    int ns = n_splits_for(s.seq[b] + 1, p.kv_chunk);
+                    int ns = n_splits_for(s.seq[b] + 1, step_chunk(s));
                     for (int g = 0; g < d.n_kv_heads; ++g)
                         for (int sp = 0; sp < ns; ++sp, ++i) {
                             const int w = p.jit_elig[(size_t)((start + i) % ne)];
@@ -542,7 +560,7 @@ bool dry_run(const HostPlan& p, int n_threads, uint64_t seed, int drop_task, int
         }
         if (p.level_op[lv] == OP_ATTN) {
             for (int bg = 0; bg < d.batch * d.n_kv_heads; ++bg) {
-                int ns = n_splits_for(s.seq[bg / d.n_kv_heads] + 1, p.kv_chunk);
+                int ns = n_splits_for(s.seq[bg / d.n_kv_heads] + 1, step_chunk(s));
                 uint64_t c = 0;
                 for (int i = 0; i < ns; ++i) c = mix64(c ^ mix64(sum ^ ((uint64_t)bg << 20) ^ (uint64_t)i));
                 ref[lv][bg] = c;

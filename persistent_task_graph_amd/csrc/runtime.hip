@@ -270,7 +270,7 @@ bool upload_plan(mk_plan* pl) {
     if (!up(pl->d_rope, rope.data(), sizeof(float2) * rope.size())) return false;
     if (!hip_ok(hipHostMalloc((void**)&pl->h_lw_pinned, sizeof(LayerPtrs) * L, hipHostMallocDefault), "hipHostMalloc"))
         return false;
-    pl->lds_bytes = lds_bytes_for(G, hp.kv_chunk);
+    pl->lds_bytes = lds_bytes_for(G, hp.kv_chunk_max);
     // one workgroup per CU: the LDS-ring variant's static page ring already
     // takes more than half of the CU's LDS; other kernels reserve it dynamically
     const bool ring = nb_for(d.batch) == 1 && d.weight_dtype == MK_BF16 && d.opts.lds_stream == 1;
@@ -361,6 +361,8 @@ KParams make_params(const mk_plan* pl, const mk_weights* w, const mk_kv_cache* k
     p.KD = d.n_kv_heads * d.head_dim;
     p.cap = hp.cap;
     p.chunk = hp.kv_chunk;
+    p.chunk_max = hp.kv_chunk_max;
+    p.attn_target = hp.attn_target;
     p.max_splits = hp.max_splits;
     p.qk_norm = d.qk_norm;
     p.paged = d.kv_layout == MK_KV_PAGED;

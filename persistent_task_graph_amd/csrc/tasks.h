@@ -57,6 +57,11 @@ __device__ __forceinline__ Lds carve_lds(float* base, int G, int chunk) {
 
 // ---------------------------------------------------------------- activations
 
+// keys per attention split in this step (the same for every task and mode)
+__device__ __forceinline__ int attn_chunk(const KParams& p) {
+    return attn_chunk_for([&](int b) { return p.seq_lens[b]; }, p.B, p.Hkv, p.chunk, p.chunk_max, p.attn_target);
+}
+
 __device__ __forceinline__ float* layer_buf(const KParams& p, int l, int64_t off) { return p.act + l * p.act_stride + off; }
 __device__ __forceinline__ const float* layer_in(const KParams& p, int l) {
     return l == 0 ? p.x0 : (l == p.L ? p.x_final : layer_buf(p, l - 1, p.off_xnext));
@@ -855,7 +860,7 @@ __host__ __device__ constexpr int attn_gp(int G) { return G <= 1 ? 1 : G <= 2 ? 
 template <typename WT, int D, int GP>
 __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, int split, const Lds& s) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int Hkv = p.Hkv, G = p.Hq / p.Hkv, C = p.chunk;
+    const int Hkv = p.Hkv, G = p.Hq / p.Hkv, C = attn_chunk(p);
     const int b = bg / Hkv, g = bg % Hkv;
     const int pos = p.seq_lens[b];
     const bool overflow = pos < 0 || pos + 1 > p.cap;
@@ -917,7 +922,7 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
     constexpr int LPR = D / E;             // lanes per K row
     constexpr int PPW = 64 / LPR;          // rows per wave per load
     constexpr int PER_IT = kWaves * PPW;   // rows per workgroup iteration
-    constexpr int NIT = 32 / kWaves;       // iterations per batch
+    constexpr int NIT = (GP >= 8 ? 16 : 32) / kWaves;  // iterations per batch (fewer registers for 8 heads)
     constexpr int SUB = PER_IT * NIT;      // rows per batch
     const int rr = lane / LPR, cc = lane % LPR;
     // K/V of this (layer, b, g) through buffer resources; rows past the split
@@ -955,6 +960,9 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
             ro[it] = (j < n && jj != pos) ? o + (uint32_t)(cc * 16) : kOOB;
         }
     };
+    // a split of one batch (the common case) requests its V with its K; a
+    // longer split streams K, then V, batch by batch (below)
+    const bool one_batch = n <= SUB;
     uint4 kr[NIT], vr[NIT];
     {
         uint32_t ro[NIT];
@@ -962,7 +970,7 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
             kr[it] = buf_load16(krs, ro[it], 0);
-            vr[it] = buf_load16(vrs, ro[it], 0);
+            vr[it] = buf_load16(vrs, one_batch ? ro[it] : kOOB, 0);
         }
     }
 
@@ -996,13 +1004,14 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
     for (int hh = 0; hh < GP; ++hh)
 #pragma unroll
         for (int e = 0; e < E; ++e) qreg[hh][e] = hh < G ? s.q[hh * D + cc * E + e] : 0.f;
-    for (int base = 0; base < n; base += SUB) {
-        if (base > 0) {
-            uint32_t ro[NIT];
-            row_offsets(base, ro);
+    // rows of a batch into registers (rows at or past n fetch nothing)
+    auto load_rows = [&](uint4 (&dst)[NIT], __amdgpu_buffer_rsrc_t rs, int base) {
+        uint32_t ro[NIT];
+        row_offsets(base, ro);
 #pragma unroll
-            for (int it = 0; it < NIT; ++it) kr[it] = buf_load16(krs, ro[it], 0);
-        }
+        for (int it = 0; it < NIT; ++it) dst[it] = buf_load16(rs, ro[it], 0);
+    };
+    auto score_batch = [&](const uint4 (&kk)[NIT], int base) {
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
             const int j = base + it * PER_IT + wave * PPW + rr;
@@ -1012,7 +1021,7 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
 #pragma unroll
                 for (int e = 0; e < E; ++e) kf[e] = s.kn[cc * E + e];
             } else {
-                VK::widen(kr[it], kf);
+                VK::widen(kk[it], kf);
             }
             float d[GP];
 #pragma unroll
@@ -1028,6 +1037,19 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
 #pragma unroll
                 for (int hh = 0; hh < GP; ++hh) s.p[j * GP + hh] = d[hh] * p.scale;
             }
+        }
+    };
+    // batches alternate between two register sets: the next batch is in
+    // flight while the current one is used
+    if (one_batch) {
+        score_batch(kr, 0);
+    } else {
+        uint4 kb[NIT];
+        for (int base = 0; base < n; base += 2 * SUB) {
+            load_rows(kb, krs, base + SUB);
+            score_batch(kr, base);
+            load_rows(kr, krs, base + 2 * SUB);
+            if (base + SUB < n) score_batch(kb, base + SUB);
         }
     }
     __syncthreads();
@@ -1058,13 +1080,7 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
     for (int hh = 0; hh < GP; ++hh)
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[hh][e] = 0.f;
-    for (int base = 0; base < n; base += SUB) {
-        if (base > 0) {
-            uint32_t ro[NIT];
-            row_offsets(base, ro);
-#pragma unroll
-            for (int it = 0; it < NIT; ++it) vr[it] = buf_load16(vrs, ro[it], 0);
-        }
+    auto pv_batch = [&](const uint4 (&vv)[NIT], int base) {
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
             const int j = base + it * PER_IT + wave * PPW + rr;
@@ -1074,7 +1090,7 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
 #pragma unroll
                 for (int e = 0; e < E; ++e) vf[e] = s.kn[128 + cc * E + e];
             } else {
-                VK::widen(vr[it], vf);
+                VK::widen(vv[it], vf);
             }
             const int jc = valid ? j : 0;
             float pr[GP];
@@ -1086,6 +1102,18 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
 #pragma unroll
                 for (int e = 0; e < E; ++e) acc[hh][e] = fmaf(pj, vf[e], acc[hh][e]);
             }
+        }
+    };
+    if (one_batch) {
+        pv_batch(vr, 0);
+    } else {
+        load_rows(vr, vrs, 0);
+        uint4 vb[NIT];
+        for (int base = 0; base < n; base += 2 * SUB) {
+            load_rows(vb, vrs, base + SUB);
+            pv_batch(vr, base);
+            load_rows(vr, vrs, base + 2 * SUB);
+            if (base + SUB < n) pv_batch(vb, base + SUB);
         }
     }
     // reduce over the row groups of the wave (lanes with equal cc)
