@@ -66,7 +66,7 @@ enum mk_device_error {
  *                scheduler waves, 2 = AOT with the maximum split count queued.
  *  kv_chunk      KV positions per attention split task (default 128; a
  *                multiple of 16). In a step whose sequences would need more
- *                than 4 split tasks per worker, the chunk doubles (up to
+ *                than 256 split tasks, the chunk doubles (up to
  *                kv_chunk_max) until they do not; the rule depends only on
  *                seq_lens, so every mode computes the same splits.
  *  kv_chunk_max  upper bound of that doubling (default 1024, lowered to fit

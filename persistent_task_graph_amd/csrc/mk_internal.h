@@ -125,6 +125,11 @@ MK_HD inline int ev_embed(int n_layers) { return 5 * n_layers; }
 
 MK_HD inline int n_splits_for(int keys, int chunk) { return (keys + chunk - 1) / chunk; }
 
+// Split tasks per step above which the attention chunk doubles: about one
+// per CU of the device. A constant (not the worker count), so that results
+// do not depend on how many workers a plan uses.
+constexpr int kAttnSplitTarget = 256;
+
 // Keys per attention split in one step: the plan's chunk c0, doubled while
 // the step would create more than `target` split tasks and the doubled chunk
 // stays within `cmax`. It depends only on the sequence lengths (len(b) =

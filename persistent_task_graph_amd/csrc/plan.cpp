@@ -106,7 +106,7 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
         int c = p.kv_chunk;
         while (2 * c <= cmax) c *= 2;
         p.kv_chunk_max = c;
-        p.attn_target = 4 * p.workers;
+        p.attn_target = kAttnSplitTarget;
     }
     if (p.max_splits > 65535) return fail(err, "too many splits per sequence");
 

@@ -285,7 +285,7 @@ bool upload_plan(mk_plan* pl) {
     if (!hip_ok(hipFuncSetAttribute(kp, hipFuncAttributeMaxDynamicSharedMemorySize, pl->lds_bytes_persistent),
                 "hipFuncSetAttribute(persistent)"))
         return false;
-    if (!hip_ok(hipFuncSetAttribute(kl, hipFuncAttributeMaxDynamicSharedMemorySize, pl->lds_bytes), "hipFuncSetAttribute"))
+    if (!hip_ok(hipFuncSetAttribute(kl, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes_gemv()), "hipFuncSetAttribute"))
         return false;
     if (!hip_ok(hipFuncSetAttribute(ka, hipFuncAttributeMaxDynamicSharedMemorySize, pl->lds_bytes), "hipFuncSetAttribute"))
         return false;
@@ -452,7 +452,7 @@ int launch_step(mk_plan* pl, const mk_weights* w, const mk_kv_cache* kv, const i
             if (n == 0) continue;
             const int32_t* ids = pl->d_level_tasks + hp.level_off[lv];
             void* args[] = {&p, (void*)&ids};
-            if (!hip_ok(hipLaunchKernel(level_kernel(pl), dim3(n), dim3(kThreads), args, pl->lds_bytes, st),
+            if (!hip_ok(hipLaunchKernel(level_kernel(pl), dim3(n), dim3(kThreads), args, lds_bytes_gemv(), st),
                         "hipLaunchKernel(level)"))
                 return MK_ERR_HIP;
         }

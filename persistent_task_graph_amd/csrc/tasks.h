@@ -32,6 +32,8 @@ constexpr int kPartFloats = 8192;  // GEMV cross-wave partial sums
 __host__ __device__ constexpr int lds_floats_fixed() {
     return kWaves * 16 + 16 + 16 + 8 + kPartFloats + 8 * 128 + 2 * 128 + kWaves * 8 * 128 + 16 + kCmbSplits * (8 * 128 + 16);
 }
+// GEMV and embedding tasks touch only the regions up to the partial sums
+__host__ __device__ constexpr int lds_bytes_gemv() { return 4 * (kWaves * 16 + 16 + 16 + 8 + kPartFloats); }
 __host__ __device__ inline int lds_bytes_for(int G, int chunk) {
     const int gp = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
     return 4 * (lds_floats_fixed() + gp * chunk);

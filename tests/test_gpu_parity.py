@@ -146,25 +146,28 @@ def test_mid_modes_bitwise(mid_weights):
 
 
 def test_mid_adaptive_chunk_matches_oracle_and_modes(mid_weights):
-    # 8 workers -> at most 32 split tasks per step before the chunk doubles:
-    # lengths 300 and 700 at a base chunk of 64 grow the chunk to 512
-    log("mid bf16: per-step chunk growth (workers=8, chunk 64 -> 512), B=2")
-    s = make_setup(MID, 2, [300, 700], 720, weights=mid_weights)
-    opts = dict(kv_chunk=64, workers=8)
+    # more than 256 split tasks in a step double the chunk: these 4 sequences
+    # need 2864 splits at a base chunk of 16, 368 at 128 and 184 at 256, so
+    # the chunk grows to 256 whatever the worker count
+    log("mid bf16: per-step chunk growth (chunk 16 -> 256), B=4")
+    s = make_setup(MID, 4, [1000, 1500, 1999, 1200], 2010, weights=mid_weights)
+    opts = dict(kv_chunk=16, workers=64)
     plan = plan_for(s, **opts)
     kv = device_kv(s)
-    out, err = run_gpu(s, plan, kv, _tokens(MID, 2, 11), 2)
+    out, err = run_gpu(s, plan, kv, _tokens(MID, 4, 11), 2)
     assert err == 0
     plan.close()
     orc, _ = run_oracle(s, out)
     worst, agree = compare(out, orc)
     log("  max|d|/std = %.3g, top-1 = %.3f" % (worst, agree))
     assert worst <= 2e-2 and agree >= 0.99
-    b, _ = _logits_seq(s, 2, tokens=_tokens(MID, 2, 11), mode=1, **opts)
-    c, _ = _logits_seq(s, 2, tokens=_tokens(MID, 2, 11), jit=2, **opts)
-    d, _ = _logits_seq(s, 2, tokens=_tokens(MID, 2, 11), kv_chunk=64, kv_chunk_max=64, workers=8)
+    b, _ = _logits_seq(s, 2, tokens=_tokens(MID, 4, 11), mode=1, **opts)
+    c, _ = _logits_seq(s, 2, tokens=_tokens(MID, 4, 11), jit=2, **opts)
+    e, _ = _logits_seq(s, 2, tokens=_tokens(MID, 4, 11), kv_chunk=16)  # default worker count: same chunk
+    d, _ = _logits_seq(s, 2, tokens=_tokens(MID, 4, 11), kv_chunk=16, kv_chunk_max=16, workers=64)
     _bitwise(out, b)
     _bitwise(out, c)
+    _bitwise(out, e)
     # a fixed chunk splits the keys differently: same values within tolerance, other bits
     worst_d = max(float(np.abs(x[1] - y[1]).max()) / float(y[1].std()) for x, y in zip(out, d))
     assert worst_d <= 2e-2
