@@ -69,8 +69,8 @@ enum mk_device_error {
  *                than 256 split tasks, the chunk doubles (up to
  *                kv_chunk_max) until they do not; the rule depends only on
  *                seq_lens, so every mode computes the same splits.
- *  kv_chunk_max  upper bound of that doubling (default 1024, lowered to fit
- *                LDS; set it equal to kv_chunk to keep the chunk fixed).
+ *  kv_chunk_max  upper bound of that doubling (default 1024, at most 16384;
+ *                set it equal to kv_chunk to keep the chunk fixed).
  *  watchdog_ms   bound on every spin wait of the persistent kernel
  *                (default 2000).
  *  host_only     1: build the task graph on the host only (no HIP calls);
@@ -270,8 +270,8 @@ typedef struct mk_trace_rec {
     uint64_t t_wait, t_ready, t_done;
     uint64_t t_a, t_b, t_c, t_d; /* task-defined phase marks, 0 if unset. GEMV: operands
                                     ready, rows done, outputs stored, stores complete;
-                                    attention: prologue done, scores done, P.V done,
-                                    partial stored */
+                                    attention: prologue done, K/V pass done, waves
+                                    merged into LDS, partial stored */
 } mk_trace_rec;
 
 /*

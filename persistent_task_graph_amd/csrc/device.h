@@ -219,6 +219,24 @@ __device__ __forceinline__ float column_sum(float v) {
     return v;
 }
 
+// Maximum over the same lanes as column_sum.
+template <int N>
+__device__ __forceinline__ float column_max(float v) {
+    static_assert(N == 8 || N == 16 || N == 32 || N == 64, "group size");
+    if constexpr (N == 8) v = fmaxf(v, dpp_sel<kDppRor8>(v));
+    if constexpr (N <= 16) {
+        const unsigned u = __builtin_bit_cast(unsigned, v);
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        v = fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+    }
+    if constexpr (N <= 32) {
+        const unsigned u = __builtin_bit_cast(unsigned, v);
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        v = fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+    }
+    return v;
+}
+
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 __device__ __forceinline__ float wave_max(float v) { return group_max<64>(v); }
 

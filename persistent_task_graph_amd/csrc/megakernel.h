@@ -37,6 +37,7 @@ __device__ __forceinline__ bool inbox_try_pop(const KParams& p, int64_t& head, i
 __device__ __forceinline__ void scheduler_wave(const KParams& p) {
     const int lane = threadIdx.x & 63;
     const int64_t want = (int64_t)p.L * (int64_t)(p.epoch + 1u);  // mailbox messages consumed by step end
+    const int chunk = attn_chunk(p);
     uint64_t t0 = now_ticks();
     for (;;) {
         int64_t h = 0;
@@ -71,7 +72,6 @@ __device__ __forceinline__ void scheduler_wave(const KParams& p) {
         layer = __shfl(layer, 0, 64);
         t0 = now_ticks();
         // expand: tasks (b, g, s) for every sequence, in sequence order
-        const int chunk = attn_chunk(p);
         int total = 0;
         for (int b = 0; b < p.B; ++b) {
             const int pos = p.seq_lens[b];
@@ -144,6 +144,7 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s, uint
         s.marks[0] = s.marks[1] = s.marks[2] = s.marks[3] = 0;
     }
     int64_t head = (threadIdx.x == 0 && p.jit_on) ? p.inbox_head[w] : 0;
+    int chunk = 0;  // the step's attention chunk, found before the first attention task
     // optional batch-1 variant: weight pages stream through a per-wave LDS
     // ring fed by direct-to-LDS loads (stream.h) instead of registers
     constexpr bool kStream = kLdsStream && NB == 1;
@@ -228,7 +229,8 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s, uint
                 aot_attn = false;
             }
             const uint64_t tj = p.trace ? now_ticks() : 0;
-            attention_task<WT>(p, jl, jbg, js, s);
+            if (chunk == 0) chunk = attn_chunk(p);
+            attention_task<WT>(p, jl, jbg, js, chunk, s);
             if (cmd == 0) break;  // that was this AOT attention task
             trace_put(p, s, 1, (jl << 24) | ((jbg & 0xFFF) << 12) | (js & 0xFFF), OP_ATTN, tj, tj);
             t0 = now_ticks();
@@ -258,7 +260,7 @@ extern __shared__ __attribute__((aligned(16))) float mk_dyn_lds[];
 
 template <typename WT, int NB>
 __global__ __launch_bounds__(kThreads) void k_persistent(KParams p) {
-    const Lds s = carve_lds(mk_dyn_lds, p.Hq / p.Hkv, p.chunk);
+    const Lds s = carve_lds(mk_dyn_lds);
     // drop L2 lines cached in earlier steps: activations are then read with
     // plain loads (see buf_load16_act)
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -280,16 +282,16 @@ template <typename WT, int NB>
 // through the launch's own acquire (the same guarantee ordinary stream-ordered
 // kernels rely on), so activations are read with plain loads here too.
 __global__ __launch_bounds__(kThreads) void k_level_gemv(KParams p, const int32_t* ids) {
-    const Lds s = carve_lds(mk_dyn_lds, p.Hq / p.Hkv, p.chunk);
+    const Lds s = carve_lds(mk_dyn_lds);
     const TaskRec t = p.tasks[ids[blockIdx.x]];
     run_gemv_task<WT, NB>(p, t, s);
 }
 
 template <typename WT>
 __global__ __launch_bounds__(kThreads) void k_level_attn(KParams p, int layer) {
-    const Lds s = carve_lds(mk_dyn_lds, p.Hq / p.Hkv, p.chunk);
+    const Lds s = carve_lds(mk_dyn_lds);
     const int bg = blockIdx.x / p.max_splits, sp = blockIdx.x % p.max_splits;
-    attention_task<WT>(p, layer, bg, sp, s);
+    attention_task<WT>(p, layer, bg, sp, attn_chunk(p), s);
 }
 
 }  // namespace

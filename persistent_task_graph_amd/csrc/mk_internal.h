@@ -125,29 +125,32 @@ MK_HD inline int ev_embed(int n_layers) { return 5 * n_layers; }
 
 MK_HD inline int n_splits_for(int keys, int chunk) { return (keys + chunk - 1) / chunk; }
 
-// Split tasks per step above which the attention chunk doubles: about one
-// per CU of the device. A constant (not the worker count), so that results
-// do not depend on how many workers a plan uses.
-constexpr int kAttnSplitTarget = 256;
+// Split tasks per step that the attention chunk is sized for: a little
+// under one per worker of a 256-CU device (252 workers), so that a step's
+// split tasks run in one round. A constant (not the worker count), so that
+// results do not depend on how many workers a plan uses.
+constexpr int kAttnSplitTarget = 240;
 
-// Keys per attention split in one step: the plan's chunk c0, doubled while
-// the step would create more than `target` split tasks and the doubled chunk
-// stays within `cmax`. It depends only on the sequence lengths (len(b) =
-// tokens cached before the step), so every execution mode and every task of
-// the step derives the same splits, and hence the same bits.
-template <typename LenFn>
-MK_HD inline int attn_chunk_for(LenFn len, int B, int Hkv, int c0, int cmax, int target) {
-    int c = c0;
-    while (2 * c <= cmax) {
-        long long total = 0;
-        for (int b = 0; b < B; ++b) {
-            const int L = len(b);
-            total += (long long)Hkv * n_splits_for(L < 0 ? 1 : L + 1, c);
-        }
-        if (total <= (long long)target) break;
-        c *= 2;
+// Keys per attention split in one step: the smallest multiple of 16 in
+// [c0, cmax] for which the step's split tasks, total(c) = sum over b of
+// Hkv * ceil(keys_b / c), number at most `target` (cmax if none does).
+// total(c) never grows with c, so a bisection finds it. It depends only on
+// the sequence lengths, so every execution mode and every task of the step
+// derives the same splits, and hence the same bits. c0 and cmax are
+// multiples of 16.
+template <typename TotalFn>
+MK_HD inline int attn_chunk_search(TotalFn total, int c0, int cmax, int target) {
+    if (cmax <= c0 || total(c0) <= (long long)target) return c0;
+    if (total(cmax) > (long long)target) return cmax;
+    int lo = c0, hi = cmax;  // total(lo) > target >= total(hi)
+    while (hi - lo > 16) {
+        const int mid = lo + ((hi - lo) / 32) * 16;
+        if (total(mid) <= (long long)target) hi = mid;
+        else lo = mid;
     }
-    return c;
+    return hi;
 }
+// keys counted for sequence length L (tokens cached before the step)
+MK_HD inline int attn_keys(int L) { return L < 0 ? 1 : L + 1; }
 
 }  // namespace mk

@@ -89,23 +89,14 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
     p.jit = (o.jit == 2) ? 0 : 1;
     p.kv_chunk = o.kv_chunk > 0 ? o.kv_chunk : 128;
     if (p.kv_chunk % 16 || p.kv_chunk > 4096) return fail(err, "kv_chunk must be a multiple of 16, at most 4096");
-    {
-        const int G = d.n_heads / d.n_kv_heads, gp = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
-        if (p.kv_chunk * gp > 16384)
-            return fail(err, "kv_chunk * (n_heads / n_kv_heads rounded up to a power of two) must be <= 16384");
-    }
     p.cap = d.max_seq_len;
     p.max_splits = n_splits_for(p.cap, p.kv_chunk);
     {
-        // the per-step chunk may grow to cmax (score buffer: GP * cmax floats)
-        const int G = d.n_heads / d.n_kv_heads, gp = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
-        int cmax = o.kv_chunk_max > 0 ? o.kv_chunk_max : 1024;
-        cmax = std::min(cmax, 16384 / gp);
-        if (o.kv_chunk_max > 0 && (o.kv_chunk_max < p.kv_chunk || o.kv_chunk_max % p.kv_chunk))
-            return fail(err, "opts.kv_chunk_max must be a multiple of kv_chunk");
-        int c = p.kv_chunk;
-        while (2 * c <= cmax) c *= 2;
-        p.kv_chunk_max = c;
+        // the per-step chunk may grow to cmax (a paged split stages its
+        // block-table entries, cmax / kv_block + 2 ints, in LDS)
+        if (o.kv_chunk_max > 0 && (o.kv_chunk_max < p.kv_chunk || o.kv_chunk_max % 16 || o.kv_chunk_max > 16384))
+            return fail(err, "opts.kv_chunk_max must be a multiple of 16 in [kv_chunk, 16384]");
+        p.kv_chunk_max = o.kv_chunk_max > 0 ? o.kv_chunk_max : std::max(p.kv_chunk, 4096);
         p.attn_target = kAttnSplitTarget;
     }
     if (p.max_splits > 65535) return fail(err, "too many splits per sequence");
@@ -332,8 +323,13 @@ struct DryState {
 
 int step_chunk(const DryState& s) {
     const HostPlan& p = s.p;
-    return attn_chunk_for([&](int b) { return s.seq[b]; }, p.desc.batch, p.desc.n_kv_heads, p.kv_chunk, p.kv_chunk_max,
-                          p.attn_target);
+    const int B = p.desc.batch, Hkv = p.desc.n_kv_heads;
+    auto total = [&](int c) {
+        long long t = 0;
+        for (int b = 0; b < B; ++b) t += (long long)Hkv * n_splits_for(attn_keys(s.seq[b]), c);
+        return t;
+    };
+    return attn_chunk_search(total, p.kv_chunk, p.kv_chunk_max, p.attn_target);
 }
 
 uint64_t level_input_sum(DryState& s, int lv) {

@@ -270,7 +270,7 @@ bool upload_plan(mk_plan* pl) {
     if (!up(pl->d_rope, rope.data(), sizeof(float2) * rope.size())) return false;
     if (!hip_ok(hipHostMalloc((void**)&pl->h_lw_pinned, sizeof(LayerPtrs) * L, hipHostMallocDefault), "hipHostMalloc"))
         return false;
-    pl->lds_bytes = lds_bytes_for(G, hp.kv_chunk_max);
+    pl->lds_bytes = lds_bytes_for(hp.kv_chunk_max, d.kv_layout == MK_KV_PAGED ? d.kv_block : 1, d.kv_layout == MK_KV_PAGED);
     // one workgroup per CU: the LDS-ring variant's static page ring already
     // takes more than half of the CU's LDS; other kernels reserve it dynamically
     const bool ring = nb_for(d.batch) == 1 && d.weight_dtype == MK_BF16 && d.opts.lds_stream == 1;

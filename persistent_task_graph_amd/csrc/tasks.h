@@ -12,56 +12,71 @@
 namespace mk {
 
 // ---------------------------------------------------------------- LDS layout
-// Carved from one dynamic shared buffer; sizes in floats.
+// Carved from one dynamic shared buffer; sizes in floats. A workgroup runs
+// one task at a time, so the GEMV partial sums and the attention regions
+// share one union after the common header.
 struct Lds {
     float* red;   // kWaves * 16: reductions / broadcast
     int* cmd;     // 16 ints
     float* rstd;  // 16
-    float* part;  // kPartFloats: GEMV cross-wave partial sums
+    float* part;  // kPartFloats: GEMV cross-wave partial sums (union member)
     float* q;     // 8 * 128: rotated query heads of one KV group
     float* kn;    // 2 * 128: new k, v (rounded to the cache type)
-    float* p;     // GP * chunk: scores, then probabilities (GP = G rounded up to 1, 2, 4 or 8)
     float* acc;   // kWaves * 8 * 128: P.V partials per wave
-    float* ml;    // 2 * 8: (m, l) per head
+    float* wml;   // kWaves * 16: per wave (m[8], l[8])
+    float* ml;    // 2 * 8: (m, l) per head of the split
     float* cmb;   // kCmbSplits * (8 * 128 + 16): partials staged for the combine
+    int* btab;    // paged cache: block-table entries of the split
     uint64_t* marks;  // 4 trace phase marks
 };
 
 constexpr int kCmbSplits = 4;  // splits merged per staged chunk
 constexpr int kPartFloats = 8192;  // GEMV cross-wave partial sums
-__host__ __device__ constexpr int lds_floats_fixed() {
-    return kWaves * 16 + 16 + 16 + 8 + kPartFloats + 8 * 128 + 2 * 128 + kWaves * 8 * 128 + 16 + kCmbSplits * (8 * 128 + 16);
-}
-// GEMV and embedding tasks touch only the regions up to the partial sums
-__host__ __device__ constexpr int lds_bytes_gemv() { return 4 * (kWaves * 16 + 16 + 16 + 8 + kPartFloats); }
-__host__ __device__ inline int lds_bytes_for(int G, int chunk) {
-    const int gp = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
-    return 4 * (lds_floats_fixed() + gp * chunk);
+constexpr int kLdsHeader = kWaves * 16 + 16 + 16 + 8;
+constexpr int kAttnFloats = 8 * 128 + 2 * 128 + kWaves * 8 * 128 + kWaves * 16 + 16 + kCmbSplits * (8 * 128 + 16);
+// GEMV and embedding tasks touch only the header and the partial sums
+__host__ __device__ constexpr int lds_bytes_gemv() { return 4 * (kLdsHeader + kPartFloats); }
+// block-table entries one split of `chunk` keys can span
+__host__ __device__ constexpr int attn_btab_ints(int chunk, int kv_block) { return chunk / kv_block + 2; }
+__host__ __device__ inline int lds_bytes_for(int chunk_max, int kv_block, bool paged) {
+    const int attn = kAttnFloats + (paged ? attn_btab_ints(chunk_max, kv_block) : 0);
+    return 4 * (kLdsHeader + (attn > kPartFloats ? attn : kPartFloats));
 }
 
-__device__ __forceinline__ Lds carve_lds(float* base, int G, int chunk) {
+__device__ __forceinline__ Lds carve_lds(float* base) {
     Lds s;
     float* p = base;
     s.red = p; p += kWaves * 16;
     s.cmd = (int*)p; p += 16;
     s.marks = (uint64_t*)p; p += 8;
     s.rstd = p; p += 16;
-    s.part = p; p += kPartFloats;
+    s.part = p;  // the attention regions below overlay the partial sums
     s.q = p; p += 8 * 128;
     s.kn = p; p += 2 * 128;
     s.acc = p; p += kWaves * 8 * 128;
+    s.wml = p; p += kWaves * 16;
     s.ml = p; p += 16;
     s.cmb = p; p += kCmbSplits * (8 * 128 + 16);
-    s.p = p;
-    (void)G; (void)chunk;
+    s.btab = (int*)p;
     return s;
 }
 
 // ---------------------------------------------------------------- activations
 
-// keys per attention split in this step (the same for every task and mode)
+// Keys per attention split in this step (the same for every task and mode).
+// Evaluated by one whole wave: lane i holds sequence i (and i + 64, ...),
+// and the split counts are summed exactly across the wave.
 __device__ __forceinline__ int attn_chunk(const KParams& p) {
-    return attn_chunk_for([&](int b) { return p.seq_lens[b]; }, p.B, p.Hkv, p.chunk, p.chunk_max, p.attn_target);
+    const int lane = threadIdx.x & 63;
+    const int k0 = lane < p.B ? attn_keys(p.seq_lens[lane]) : 0;
+    auto total = [&](int c) {
+        int t = k0 > 0 ? n_splits_for(k0, c) : 0;
+        for (int b = lane + 64; b < p.B; b += 64) t += n_splits_for(attn_keys(p.seq_lens[b]), c);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
+        return (long long)t * p.Hkv;
+    };
+    return attn_chunk_search(total, p.chunk, p.chunk_max, p.attn_target);
 }
 
 __device__ __forceinline__ float* layer_buf(const KParams& p, int l, int64_t off) { return p.act + l * p.act_stride + off; }
@@ -860,32 +875,15 @@ __host__ __device__ constexpr int attn_rec(int G, int D) { return G * D + 16; }
 __host__ __device__ constexpr int attn_gp(int G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8; }
 
 template <typename WT, int D, int GP>
-__device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, int split, const Lds& s) {
+__device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, int split, int C, const Lds& s) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int Hkv = p.Hkv, G = p.Hq / p.Hkv, C = attn_chunk(p);
+    const int Hkv = p.Hkv, G = p.Hq / p.Hkv;
     const int b = bg / Hkv, g = bg % Hkv;
-    const int pos = p.seq_lens[b];
-    const bool overflow = pos < 0 || pos + 1 > p.cap;
-    const int keys = pos + 1;
-    const int ns = overflow ? 1 : (keys + C - 1) / C;
-    if (split >= ns) return;  // reserved AOT slot beyond this sequence's length
-    float* out = layer_buf(p, l, p.off_attn) + (int64_t)b * p.QD + (int64_t)g * G * D;
     const float* qkv = layer_buf(p, l, p.off_qkv) + (int64_t)b * (p.QD + 2 * p.KD);
     const LayerPtrs& lw = p.lw[l];
-
-    if (overflow) {
-        for (int i = tid; i < G * D; i += kThreads) st_co(&out[i], 0.f);
-        if (tid == 0) raise_error(p.ctrl, MK_ERR_KV_OVERFLOW);
-        if (p.persistent) signal_event(p, ev_attn(l), s);
-        return;
-    }
-    const int j0 = split * C, j1 = min(j0 + C, keys);
-    const bool owner = (j1 == keys);
-    const int n = j1 - j0;
-
-    // 0. this wave's query heads (and, in the owner, the new k / v) are
-    // requested first: they are few and gate the prologue, while the bulk
-    // K/V loads issued next stay in flight behind them
+    // 0. this wave's query heads, the new k (wave 0) and v (wave 1), and the
+    // norm gains are requested first: their addresses do not depend on the
+    // sequence length, so they are in flight while it is read
     constexpr int QPW = (GP + kWaves - 1) / kWaves;  // query heads per wave
     float qv[QPW][2];
 #pragma unroll
@@ -898,13 +896,11 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
         }
     }
     float nv[2] = {0.f, 0.f};
-    const bool appender = owner && wave < 2;
-    if (appender) {
+    if (wave < 2) {
         const int64_t base = wave == 0 ? (int64_t)p.QD + (int64_t)g * D : (int64_t)p.QD + p.KD + (int64_t)g * D;
         nv[0] = ld_act(&qkv[base + lane]);
         if constexpr (D > 64) nv[1] = ld_act(&qkv[base + lane + 64]);
     }
-    // norm gains and this lane's RoPE factors, needed as soon as q arrives
     const bool qkn = p.qk_norm != 0;
     float gq[2] = {1.f, 1.f}, gk[2] = {1.f, 1.f};
     if (qkn) {
@@ -914,6 +910,25 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
             gk[i] = load_scalar<WT>((const WT*)lw.k_norm, lane + 64 * i);
         }
     }
+
+    const int pos = p.seq_lens[b];
+    const bool overflow = pos < 0 || pos + 1 > p.cap;
+    const int keys = pos + 1;
+    const int ns = overflow ? 1 : (keys + C - 1) / C;
+    if (split >= ns) return;  // reserved AOT slot beyond this sequence's length
+    float* out = layer_buf(p, l, p.off_attn) + (int64_t)b * p.QD + (int64_t)g * G * D;
+
+    if (overflow) {
+        for (int i = tid; i < G * D; i += kThreads) st_co(&out[i], 0.f);
+        if (tid == 0) raise_error(p.ctrl, MK_ERR_KV_OVERFLOW);
+        if (p.persistent) signal_event(p, ev_attn(l), s);
+        return;
+    }
+    const int j0 = split * C, j1 = min(j0 + C, keys);
+    const bool owner = (j1 == keys);
+    const int n = j1 - j0;
+    const bool appender = owner && wave < 2;
+    // this lane's RoPE factors at position pos
     const float2 cs = p.rope[(int64_t)pos * (D / 2) + (D == 128 ? lane : (lane & 31))];
     asm volatile("" ::: "memory");
 
@@ -942,14 +957,23 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
         vrs = make_rsrc((const WT*)p.kv_v + lbase, (uint32_t)(p.kv_layer_stride * es));
     }
     const int32_t* btab = p.paged ? p.block_table + (int64_t)b * p.max_blocks : nullptr;
+    // the split's block-table entries are staged in LDS for the batches after
+    // the first (visible after the prologue barrier), so that a batch's K/V
+    // requests never wait behind a block-table load
+    const int blk0 = p.paged ? j0 / p.kv_block : 0;
+    if (p.paged) {
+        const int nblk = (j1 - 1) / p.kv_block - blk0 + 1;
+        for (int i = tid; i < nblk; i += kThreads) s.btab[i] = btab[blk0 + i];
+    }
     // byte offsets of this lane's 16 bytes for NIT rows starting at `base`
-    auto row_offsets = [&](int base, uint32_t (&ro)[NIT]) {
+    auto row_offsets = [&](int base, uint32_t (&ro)[NIT], bool staged) {
         int blk[NIT];
         if (p.paged) {
 #pragma unroll
             for (int it = 0; it < NIT; ++it) {
                 const int j = base + it * PER_IT + wave * PPW + rr;
-                blk[it] = j < n ? btab[(j0 + j) / p.kv_block] : 0;
+                const int bi = (j0 + j) / p.kv_block;
+                blk[it] = j < n ? (staged ? s.btab[bi - blk0] : btab[bi]) : 0;
             }
         }
 #pragma unroll
@@ -962,17 +986,16 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
             ro[it] = (j < n && jj != pos) ? o + (uint32_t)(cc * 16) : kOOB;
         }
     };
-    // a split of one batch (the common case) requests its V with its K; a
-    // longer split streams K, then V, batch by batch (below)
+    // the first batch of K and V rows is requested before the prologue's math
     const bool one_batch = n <= SUB;
     uint4 kr[NIT], vr[NIT];
     {
         uint32_t ro[NIT];
-        row_offsets(0, ro);
+        row_offsets(0, ro, false);
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
             kr[it] = buf_load16(krs, ro[it], 0);
-            vr[it] = buf_load16(vrs, one_batch ? ro[it] : kOOB, 0);
+            vr[it] = buf_load16(vrs, ro[it], 0);
         }
     }
 
@@ -1000,20 +1023,36 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
     __syncthreads();
     trace_mark(p, s.marks, 0);
 
-    // 3. scores s_j = (q_h . k_j) * scale for j in [j0, j1)
-    float qreg[GP][E];
-#pragma unroll
-    for (int hh = 0; hh < GP; ++hh)
-#pragma unroll
-        for (int e = 0; e < E; ++e) qreg[hh][e] = hh < G ? s.q[hh * D + cc * E + e] : 0.f;
-    // rows of a batch into registers (rows at or past n fetch nothing)
-    auto load_rows = [&](uint4 (&dst)[NIT], __amdgpu_buffer_rsrc_t rs, int base) {
+    // K and V rows of a batch into registers (rows at or past n fetch nothing)
+    auto load_kv = [&](uint4 (&kd)[NIT], uint4 (&vd)[NIT], int base) {
         uint32_t ro[NIT];
-        row_offsets(base, ro);
+        row_offsets(base, ro, true);
 #pragma unroll
-        for (int it = 0; it < NIT; ++it) dst[it] = buf_load16(rs, ro[it], 0);
+        for (int it = 0; it < NIT; ++it) {
+            kd[it] = buf_load16(krs, ro[it], 0);
+            vd[it] = buf_load16(vrs, ro[it], 0);
+        }
     };
-    auto score_batch = [&](const uint4 (&kk)[NIT], int base) {
+    // 3. one pass over the split's keys with a running (max, sum, acc) per
+    // head in each wave: the K and V rows of a batch are requested together,
+    // one batch ahead of the one in use. Lanes (rr, cc) of row group rr hold
+    // the full score of their row after the group sum, which is exactly the
+    // probability their P.V update needs, so scores never leave registers.
+    // The running max is wave-uniform (maxed over the row groups), which
+    // keeps every lane's acc on one scale; the four waves merge at the end.
+    float acc[GP][E], lsum[GP], mrun[GP];
+#pragma unroll
+    for (int hh = 0; hh < GP; ++hh) {
+        lsum[hh] = 0.f;
+        mrun[hh] = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[hh][e] = 0.f;
+    }
+    auto process = [&](const uint4 (&kk)[NIT], const uint4 (&vv)[NIT], int base) {
+        float d[NIT][GP];
+        float bm[GP];
+#pragma unroll
+        for (int hh = 0; hh < GP; ++hh) bm[hh] = -INFINITY;
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
             const int j = base + it * PER_IT + wave * PPW + rr;
@@ -1025,106 +1064,66 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
             } else {
                 VK::widen(kk[it], kf);
             }
-            float d[GP];
 #pragma unroll
             for (int hh = 0; hh < GP; ++hh) {
-                d[hh] = 0.f;
+                float t = 0.f;
 #pragma unroll
-                for (int e = 0; e < E; ++e) d[hh] = fmaf(qreg[hh][e], kf[e], d[hh]);
-            }
-#pragma unroll
-            for (int hh = 0; hh < GP; ++hh) d[hh] = group_sum<LPR>(d[hh]);
-            if (valid && cc == 0) {
-                // probabilities are kept row-major, GP heads per key
-#pragma unroll
-                for (int hh = 0; hh < GP; ++hh) s.p[j * GP + hh] = d[hh] * p.scale;
+                for (int e = 0; e < E; ++e) t = fmaf(s.q[hh * D + cc * E + e], kf[e], t);
+                t = group_sum<LPR>(t) * p.scale;
+                d[it][hh] = valid ? t : -INFINITY;
+                bm[hh] = fmaxf(bm[hh], d[it][hh]);
             }
         }
-    };
-    // batches alternate between two register sets: the next batch is in
-    // flight while the current one is used
-    if (one_batch) {
-        score_batch(kr, 0);
-    } else {
-        uint4 kb[NIT];
-        for (int base = 0; base < n; base += 2 * SUB) {
-            load_rows(kb, krs, base + SUB);
-            score_batch(kr, base);
-            load_rows(kr, krs, base + 2 * SUB);
-            if (base + SUB < n) score_batch(kb, base + SUB);
-        }
-    }
-    __syncthreads();
-
-    trace_mark(p, s.marks, 1);
-    // 4. per-head max and exp-sum over this split (fixed strides and tree)
-    for (int hh = wave; hh < G; hh += kWaves) {
-        float m = -INFINITY;
-        for (int j = lane; j < n; j += 64) m = fmaxf(m, s.p[j * GP + hh]);
-        m = wave_max(m);
-        float sum = 0.f;
-        for (int j = lane; j < n; j += 64) {
-            const float e = __expf(s.p[j * GP + hh] - m);
-            s.p[j * GP + hh] = e;
-            sum += e;
-        }
-        sum = wave_sum(sum);
-        if (lane == 0) {
-            s.ml[2 * hh] = m;
-            s.ml[2 * hh + 1] = sum;
-        }
-    }
-    __syncthreads();
-
-    // 5. acc[h][d] = sum_j p[h][j] V[j][d] (first batch of V already loaded)
-    float acc[GP][E];
+        float mz[GP];
 #pragma unroll
-    for (int hh = 0; hh < GP; ++hh)
+        for (int hh = 0; hh < GP; ++hh) {
+            const float mn = fmaxf(mrun[hh], column_max<LPR>(bm[hh]));
+            // mn is -inf only while this wave has seen no key: nothing to scale
+            const float corr = mn == -INFINITY ? 1.f : __expf(mrun[hh] - mn);
+            mz[hh] = mn == -INFINITY ? 0.f : mn;
+            lsum[hh] *= corr;
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[hh][e] = 0.f;
-    auto pv_batch = [&](const uint4 (&vv)[NIT], int base) {
+            for (int e = 0; e < E; ++e) acc[hh][e] *= corr;
+            mrun[hh] = mn;
+        }
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
             const int j = base + it * PER_IT + wave * PPW + rr;
-            const bool valid = j < n;
             float vf[E];
-            if (valid && j0 + j == pos) {
+            if (j < n && j0 + j == pos) {
 #pragma unroll
                 for (int e = 0; e < E; ++e) vf[e] = s.kn[128 + cc * E + e];
             } else {
-                VK::widen(vv[it], vf);
+                VK::widen(vv[it], vf);  // rows past the split loaded zeros
             }
-            const int jc = valid ? j : 0;
-            float pr[GP];
-#pragma unroll
-            for (int hh = 0; hh < GP; ++hh) pr[hh] = s.p[jc * GP + hh];
 #pragma unroll
             for (int hh = 0; hh < GP; ++hh) {
-                const float pj = (valid && hh < G) ? pr[hh] : 0.f;
+                const float pj = __expf(d[it][hh] - mz[hh]);  // exp(-inf) = 0 past the split
+                lsum[hh] += pj;
 #pragma unroll
                 for (int e = 0; e < E; ++e) acc[hh][e] = fmaf(pj, vf[e], acc[hh][e]);
             }
         }
     };
     if (one_batch) {
-        pv_batch(vr, 0);
+        process(kr, vr, 0);
     } else {
-        load_rows(vr, vrs, 0);
-        uint4 vb[NIT];
+        uint4 kb[NIT], vb[NIT];
         for (int base = 0; base < n; base += 2 * SUB) {
-            load_rows(vb, vrs, base + SUB);
-            pv_batch(vr, base);
-            load_rows(vr, vrs, base + 2 * SUB);
-            if (base + SUB < n) pv_batch(vb, base + SUB);
+            load_kv(kb, vb, base + SUB);
+            process(kr, vr, base);
+            load_kv(kr, vr, base + 2 * SUB);
+            if (base + SUB < n) process(kb, vb, base + SUB);
         }
     }
-    // reduce over the row groups of the wave (lanes with equal cc)
+    trace_mark(p, s.marks, 1);
+    // 4. this wave's (m, l, acc): sums over its row groups (lanes with equal cc)
 #pragma unroll
-    for (int hh = 0; hh < GP; ++hh)
+    for (int hh = 0; hh < GP; ++hh) {
+        lsum[hh] = column_sum<LPR>(lsum[hh]);
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            acc[hh][e] = column_sum<LPR>(acc[hh][e]);
-        }
+        for (int e = 0; e < E; ++e) acc[hh][e] = column_sum<LPR>(acc[hh][e]);
+    }
     if (rr == 0) {
 #pragma unroll
         for (int hh = 0; hh < GP; ++hh) {
@@ -1133,24 +1132,45 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
             for (int e = 0; e < E; ++e) s.acc[(wave * 8 + hh) * 128 + cc * E + e] = acc[hh][e];
         }
     }
+    if (lane == 0) {
+#pragma unroll
+        for (int hh = 0; hh < GP; ++hh) {
+            if (hh >= G) continue;
+            s.wml[wave * 16 + hh] = mrun[hh];
+            s.wml[wave * 16 + 8 + hh] = lsum[hh];
+        }
+    }
     __syncthreads();
 
     trace_mark(p, s.marks, 2);
-    // 6. partial record
+    // 5. partial record: the waves merged in wave order on the split's max
     const int rec = attn_rec(G, D);
     float* part = p.partials + ((int64_t)bg * p.max_splits + split) * rec;
+    auto wave_scale = [&](int w, int hh, float M) {
+        const float m = s.wml[w * 16 + hh];
+        return m == -INFINITY ? 0.f : __expf(m - M);
+    };
+    auto split_max = [&](int hh) {
+        float M = s.wml[hh];
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s.wml[w * 16 + hh]);
+        return M;  // finite: the split holds at least one key
+    };
     for (int i = tid; i < G * D; i += kThreads) {
         const int hh = i / D, d = i % D;
-        float a = s.acc[hh * 128 + d];
-        for (int w = 1; w < kWaves; ++w) a += s.acc[(w * 8 + hh) * 128 + d];
+        const float M = split_max(hh);
+        float a = s.acc[hh * 128 + d] * wave_scale(0, hh, M);
+        for (int w = 1; w < kWaves; ++w) a = fmaf(s.acc[(w * 8 + hh) * 128 + d], wave_scale(w, hh, M), a);
         st_co(&part[i], a);
     }
     if (tid < G) {
-        st_co(&part[G * D + tid], s.ml[2 * tid]);
-        st_co(&part[G * D + 8 + tid], s.ml[2 * tid + 1]);
+        const float M = split_max(tid);
+        float L = s.wml[8 + tid] * wave_scale(0, tid, M);
+        for (int w = 1; w < kWaves; ++w) L = fmaf(s.wml[w * 16 + 8 + tid], wave_scale(w, tid, M), L);
+        st_co(&part[G * D + tid], M);
+        st_co(&part[G * D + 8 + tid], L);
     }
 
-    // 7. last arrival merges the splits in split order
+    // 6. last arrival merges the splits in split order
     wait_stores();
     trace_mark(p, s.marks, 3);
     __syncthreads();
@@ -1208,18 +1228,19 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
 }
 
 template <typename WT, int D>
-__device__ __forceinline__ void attention_task_d(const KParams& p, int l, int bg, int split, const Lds& s) {
+__device__ __forceinline__ void attention_task_d(const KParams& p, int l, int bg, int split, int C, const Lds& s) {
     switch (attn_gp(p.Hq / p.Hkv)) {
-        case 1: attention_body<WT, D, 1>(p, l, bg, split, s); break;
-        case 2: attention_body<WT, D, 2>(p, l, bg, split, s); break;
-        case 4: attention_body<WT, D, 4>(p, l, bg, split, s); break;
-        default: attention_body<WT, D, 8>(p, l, bg, split, s); break;
+        case 1: attention_body<WT, D, 1>(p, l, bg, split, C, s); break;
+        case 2: attention_body<WT, D, 2>(p, l, bg, split, C, s); break;
+        case 4: attention_body<WT, D, 4>(p, l, bg, split, C, s); break;
+        default: attention_body<WT, D, 8>(p, l, bg, split, C, s); break;
     }
 }
+// C: the step's chunk, attn_chunk(p)
 template <typename WT>
-__device__ __forceinline__ void attention_task(const KParams& p, int l, int bg, int split, const Lds& s) {
-    if (p.D == 128) attention_task_d<WT, 128>(p, l, bg, split, s);
-    else attention_task_d<WT, 64>(p, l, bg, split, s);
+__device__ __forceinline__ void attention_task(const KParams& p, int l, int bg, int split, int C, const Lds& s) {
+    if (p.D == 128) attention_task_d<WT, 128>(p, l, bg, split, C, s);
+    else attention_task_d<WT, 64>(p, l, bg, split, C, s);
 }
 
 }  // namespace mk

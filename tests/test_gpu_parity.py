@@ -146,10 +146,11 @@ def test_mid_modes_bitwise(mid_weights):
 
 
 def test_mid_adaptive_chunk_matches_oracle_and_modes(mid_weights):
-    # more than 256 split tasks in a step double the chunk: these 4 sequences
-    # need 2864 splits at a base chunk of 16, 368 at 128 and 184 at 256, so
-    # the chunk grows to 256 whatever the worker count
-    log("mid bf16: per-step chunk growth (chunk 16 -> 256), B=4")
+    # the step's chunk is the smallest multiple of 16 giving at most 240 split
+    # tasks: these 4 sequences (8 KV heads) need 2864 splits at a base chunk
+    # of 16, 256 at 192 and 232 at 208, so the chunk becomes 208 whatever the
+    # worker count
+    log("mid bf16: per-step chunk growth (chunk 16 -> 208), B=4")
     s = make_setup(MID, 4, [1000, 1500, 1999, 1200], 2010, weights=mid_weights)
     opts = dict(kv_chunk=16, workers=64)
     plan = plan_for(s, **opts)
