@@ -65,12 +65,14 @@ enum mk_device_error {
  *  jit           attention launch: 0 = default (JIT), 1 = JIT through the
  *                scheduler waves, 2 = AOT with the maximum split count queued.
  *  kv_chunk      KV positions per attention split task (default 128; a
- *                multiple of 16). In a step whose sequences would need more
- *                than 256 split tasks, the chunk doubles (up to
- *                kv_chunk_max) until they do not; the rule depends only on
- *                seq_lens, so every mode computes the same splits.
- *  kv_chunk_max  upper bound of that doubling (default 1024, at most 16384;
- *                set it equal to kv_chunk to keep the chunk fixed).
+ *                multiple of 16). Each step uses the smallest multiple of 16
+ *                from kv_chunk up to kv_chunk_max for which the step has at
+ *                most 240 split tasks (kv_chunk_max if none does); the rule
+ *                depends only on seq_lens, so every mode computes the same
+ *                splits.
+ *  kv_chunk_max  upper bound of that chunk (default 4096, at most 16384, a
+ *                multiple of 16; set it equal to kv_chunk to keep the chunk
+ *                fixed).
  *  watchdog_ms   bound on every spin wait of the persistent kernel
  *                (default 2000).
  *  host_only     1: build the task graph on the host only (no HIP calls);

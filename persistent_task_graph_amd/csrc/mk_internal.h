@@ -80,7 +80,7 @@ struct HostPlan {
     int sched_wgs = 0;
     int jit = 1;  // 1 JIT, 0 AOT attention
     int kv_chunk = 256;     // base keys per split (sizes the partial records)
-    int kv_chunk_max = 256; // largest per-step chunk (sizes the score buffer)
+    int kv_chunk_max = 4096; // largest per-step chunk
     int attn_target = 0;    // split tasks per step above which the chunk doubles
     int max_splits = 0;
     int n_levels = 0;
