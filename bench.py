@@ -78,6 +78,9 @@ def parse():
     ap.add_argument("--no-paged", action="store_true", help="skip the paged batch-8 long-context measurement")
     ap.add_argument("--paged-steps", type=int, default=32)
     ap.add_argument("--no-layer", action="store_true", help="skip the single-layer measurement")
+    ap.add_argument("--no-ablation", action="store_true",
+                    help="skip the JIT-scheduler and kernel-per-op step times at batch 1 and 16")
+    ap.add_argument("--ablation-steps", type=int, default=32)
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--mode", type=int, default=0, help="0 persistent, 1 kernel-per-op")
@@ -127,7 +130,8 @@ def main():
 
     # ---------------------------------------------------------------- batch 1
     B = 1
-    cap = args.prompt + args.warmup + args.steps + 8
+    n_abl = 0 if args.no_ablation else 2 * (args.ablation_steps + 4)
+    cap = args.prompt + args.warmup + args.steps + n_abl + 8
     kv = harness.DeviceKV(shape, B, cap)
     plan = harness.build_plan(shape, B, cap, **opts)
     info = plan.info()
@@ -159,6 +163,24 @@ def main():
             plan.argmax(logits, d_tok)
             d_len += 1
 
+    def ablation(Bn, capn, kv, d_tok, d_len, logits):
+        """ms/step of the same step with JIT attention through the scheduler
+        waves, and in kernel-per-operator mode (same results, bitwise)."""
+        out = {"kv_len_start": int(d_len[0].item())}
+        for name, o in (("jit_scheduler", dict(opts, jit=1)), ("kernel_per_op", dict(opts, mode=1))):
+            pl = harness.build_plan(shape, Bn, capn, **o)
+            run(4, pl, kv, d_tok, d_len, logits)
+            torch.cuda.synchronize()
+            e0.record(st)
+            run(args.ablation_steps, pl, kv, d_tok, d_len, logits)
+            e1.record(st)
+            torch.cuda.synchronize()
+            if pl.device_error():
+                raise SystemExit("device error in the %s ablation" % name)
+            out[name + "_ms_per_step"] = round(e0.elapsed_time(e1) / args.ablation_steps, 4)
+            pl.close()
+        return out
+
     run(args.warmup, plan, kv, d_tok, d_len, logits)
     torch.cuda.synchronize()
     len0 = int(d_len.item())
@@ -184,6 +206,10 @@ def main():
     log("B=1: %.3f ms/step (kernel avg %.3f, median %.3f, p99 %.3f), %.1f tok/s, %.0f GB/s = %.1f%% of 8 TB/s"
         % (ms_per_step, k_avg, np.median(k_ms), np.percentile(k_ms, 99), tok_s, achieved, 100 * achieved / PEAK_HBM_GBS))
     plan.close()
+    abl1 = None
+    if not args.no_ablation:
+        abl1 = ablation(B, cap, kv, d_tok, d_len, logits)
+        log("B=1 ablation: %s" % abl1)
     del kv
 
     result = {
@@ -204,7 +230,7 @@ def main():
                         % args.prompt,
             "batch": B, "kv_len_start": len0, "mode": "persistent" if args.mode == 0 else "kernel_per_op",
             "workers": info.workers, "sched_waves": info.sched_waves, "kv_chunk": info.kv_chunk,
-            "jit": bool(info.jit),
+            "attention": "JIT (scheduler waves)" if info.jit else "AOT slots",
         },
         "kernel_ms": {"mean": round(k_avg, 4), "median": round(float(np.median(k_ms)), 4),
                       "p99": round(float(np.percentile(k_ms, 99)), 4)},
@@ -215,13 +241,15 @@ def main():
             "bytes_per_launch": int(avg_bytes),
         },
     }
+    if abl1 is not None:
+        result["ablation_b1"] = abl1
 
     # ---------------------------------------------------------------- batch 16
     if not args.no_b16:
         wl16 = synth.WORKLOADS["q8b_b16"]
         B16 = wl16.batch
         lens = synth.seq_lengths(wl16)
-        cap16 = int(lens.max()) + args.warmup + args.b16_steps + 8
+        cap16 = int(lens.max()) + args.warmup + args.b16_steps + n_abl + 8
         t0 = time.time()
         kv16 = harness.DeviceKV(shape, B16, cap16)
         caches = synth.kv_contents(shape, lens, int(lens.max()) + 1)
@@ -259,6 +287,9 @@ def main():
             "hbm_frac": round(ach16 / PEAK_HBM_GBS, 4), "bytes_per_launch": int(b16_bytes),
         }
         plan16.close()
+        if not args.no_ablation:
+            result["batch16"]["ablation"] = ablation(B16, cap16, kv16, d_tok16, d_len16, logits16)
+            log("B=16 ablation: %s" % result["batch16"]["ablation"])
         del kv16
 
     # ---------------------------------------------------------------- batch 8, paged, long context

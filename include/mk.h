@@ -60,10 +60,18 @@ enum mk_device_error {
  * Execution options. Zero means "default" for every field.
  *  mode          MK_PERSISTENT (default) or MK_KERNEL_PER_OP (one launch per
  *                task-graph level, same task bodies, bit-identical results).
- *  workers       worker workgroups, one per CU (default: CU count - 4).
- *  sched_wgs     scheduler workgroups of 4 waves each (default 4 -> 16 waves).
- *  jit           attention launch: 0 = default (JIT), 1 = JIT through the
- *                scheduler waves, 2 = AOT with the maximum split count queued.
+ *  workers       worker workgroups, one per CU (default: CU count - sched_wgs).
+ *  sched_wgs     scheduler workgroups of 4 waves each, JIT mode only (default
+ *                4 -> 16 waves; 0 in AOT mode).
+ *  jit           attention launch: 0 = default (AOT), 1 = JIT: the last QKV
+ *                task of a layer posts it to a mailbox, the scheduler waves
+ *                expand its split tasks from seq_lens and deal them into the
+ *                workers' inboxes, 2 = AOT: each layer queues one attention
+ *                slot per split task a step can have (min(240, batch *
+ *                n_kv_heads * max splits), or batch * n_kv_heads *
+ *                ceil(max_seq_len / kv_chunk_max) if larger) on the
+ *                workers; once the layer's QKV event fires, slot i runs
+ *                split task i of the step in (b, g, split) order, if any.
  *  kv_chunk      KV positions per attention split task (default 128; a
  *                multiple of 16). Each step uses the smallest multiple of 16
  *                from kv_chunk up to kv_chunk_max for which the step has at

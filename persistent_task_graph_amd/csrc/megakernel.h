@@ -177,6 +177,19 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s, uint
         // same call once its event has fired, so the (large) attention body
         // is expanded at one site only.
         bool waiting = t.wait_ev >= 0, aot_attn = t.op == OP_ATTN;
+        // an AOT attention slot runs split task t.a0 of the step, found from
+        // seq_lens before it waits and handed to the run below through LDS
+        // (past the poll loop's barriers); bg = -1 marks a slot the step
+        // leaves empty
+        if (aot_attn) {
+            if (chunk == 0) chunk = attn_chunk(p);
+            int abg, asp;
+            if (!attn_locate(p, chunk, t.a0, abg, asp)) abg = -1;
+            if (threadIdx.x == 0) {
+                s.cmd[12] = abg;
+                s.cmd[13] = asp;
+            }
+        }
         const uint32_t target = waiting ? p.evrec[t.wait_ev].required * ep1 : 0u;
         uint64_t t0 = now_ticks();
         for (;;) {
@@ -227,6 +240,9 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s, uint
             if (cmd == 0) {
                 if (!aot_attn) break;
                 aot_attn = false;
+                jbg = s.cmd[12];
+                js = s.cmd[13];
+                if (jbg < 0) break;
             }
             const uint64_t tj = p.trace ? now_ticks() : 0;
             if (chunk == 0) chunk = attn_chunk(p);

@@ -150,6 +150,17 @@ MK_HD inline int attn_chunk_search(TotalFn total, int c0, int cmax, int target) 
     }
     return hi;
 }
+// AOT attention slots per layer, one per split task a step can have: a
+// step's chunk gives at most kAttnSplitTarget tasks unless it is capped at
+// kv_chunk_max, where a sequence has at most ceil(cap / kv_chunk_max) splits
+template <typename Plan>
+inline int aot_attn_slots(const Plan& p) {
+    const long long bg = (long long)p.desc.batch * p.desc.n_kv_heads;
+    const long long most = bg * p.max_splits;
+    const long long capped = bg * ((p.cap + p.kv_chunk_max - 1) / p.kv_chunk_max);
+    const long long target = most < kAttnSplitTarget ? most : kAttnSplitTarget;
+    return (int)(capped > target ? capped : target);
+}
 // keys counted for sequence length L (tokens cached before the step)
 MK_HD inline int attn_keys(int L) { return L < 0 ? 1 : L + 1; }
 

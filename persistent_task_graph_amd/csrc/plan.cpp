@@ -80,13 +80,15 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
     if (device_cus < 2) return fail(err, "device has too few CUs");
     p = HostPlan();
     p.desc = d;
-    p.sched_wgs = o.sched_wgs > 0 ? o.sched_wgs : 4;
+    if (o.jit < 0 || o.jit > 2) return fail(err, "opts.jit must be 0, 1 or 2");
+    p.jit = (o.jit == 1) ? 1 : 0;  // default: AOT attention slots
+    // scheduler workgroups exist only to deal JIT attention; without them
+    // every CU is a worker
+    p.sched_wgs = p.jit ? (o.sched_wgs > 0 ? o.sched_wgs : 4) : 0;
     p.workers = o.workers > 0 ? o.workers : device_cus - p.sched_wgs;
     if (p.workers < 1 || p.workers + p.sched_wgs > device_cus)
-        return fail(err, "workers + sched_wgs must be in [2, CU count] (one workgroup per CU)");
-    if (o.jit < 0 || o.jit > 2) return fail(err, "opts.jit must be 0, 1 or 2");
+        return fail(err, "workers + sched_wgs must be in [1, CU count] (one workgroup per CU)");
     if (o.lds_stream < 0 || o.lds_stream > 1) return fail(err, "opts.lds_stream must be 0 or 1");
-    p.jit = (o.jit == 2) ? 0 : 1;
     p.kv_chunk = o.kv_chunk > 0 ? o.kv_chunk : 128;
     if (p.kv_chunk % 16 || p.kv_chunk > 4096) return fail(err, "kv_chunk must be a multiple of 16, at most 4096");
     p.cap = d.max_seq_len;
@@ -150,23 +152,25 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
         if (p.jit) {
             p.events[ev_qkv(l)].jit_layer = l;
         } else {
-            for (int bg = 0; bg < B * Hkv; ++bg)
-                for (int s = 0; s < p.max_splits; ++s) {
-                    TaskRec t{};
-                    t.op = OP_ATTN;
-                    t.layer = (uint16_t)l;
-                    t.a0 = bg;
-                    t.a1 = s;
-                    t.wait_ev = ev_qkv(l);
-                    t.sig_ev = ev_attn(l);
-                    t.level = level;
-                    int id = (int)p.tasks.size();
-                    p.tasks.push_back(t);
-                    p.level_tasks.push_back(id);
-                    q[rot].push_back(id);
-                    rot = (rot + 1) % W;
-                    p.tasks_per_op[OP_ATTN]++;
-                }
+            // AOT: slot i runs split task i of the step in (b, g, split)
+            // order, found from seq_lens when it runs
+            const int S = aot_attn_slots(p);
+            for (int i = 0; i < S; ++i) {
+                TaskRec t{};
+                t.op = OP_ATTN;
+                t.layer = (uint16_t)l;
+                t.a0 = i;
+                t.a1 = S;
+                t.wait_ev = ev_qkv(l);
+                t.sig_ev = ev_attn(l);
+                t.level = level;
+                int id = (int)p.tasks.size();
+                p.tasks.push_back(t);
+                p.level_tasks.push_back(id);
+                q[rot].push_back(id);
+                rot = (rot + 1) % W;
+                p.tasks_per_op[OP_ATTN]++;
+            }
         }
         p.events[ev_attn(l)].required = (uint32_t)(B * Hkv);
         level++;
@@ -280,7 +284,7 @@ bool verify_plan(const HostPlan& p, std::string& err) {
         for (int lv = 0; lv < p.n_levels; ++lv) {
             if (p.level_op[lv] != OP_ATTN) continue;
             int n = p.level_off[lv + 1] - p.level_off[lv];
-            if (n != d.batch * d.n_kv_heads * p.max_splits) return fail(err, "AOT attention level incomplete");
+            if (n != aot_attn_slots(p)) return fail(err, "AOT attention level incomplete");
         }
     }
     return true;
@@ -352,6 +356,21 @@ void run_gemv(DryState& s, const TaskRec& t) {
     uint64_t sum = in >= 0 ? level_input_sum(s, in) : 0x1234;
     for (int r = t.a0; r < t.a1; ++r)
         s.out[t.level][r].store(mix64(sum ^ ((uint64_t)t.level << 40) ^ (uint64_t)r), std::memory_order_release);
+}
+
+// split task k of the step in (b, g, split) order, if the step has one
+bool locate_split(const DryState& s, int C, int k, int& bg, int& split) {
+    const HostPlan& p = s.p;
+    for (int b = 0; b < p.desc.batch; ++b) {
+        const int ns = n_splits_for(s.seq[b] + 1, C), cnt = ns * p.desc.n_kv_heads;
+        if (k < cnt) {
+            bg = b * p.desc.n_kv_heads + k / ns;
+            split = k % ns;
+            return true;
+        }
+        k -= cnt;
+    }
+    return false;
 }
 
 bool run_attn(DryState& s, int layer, int bg, int split, int lv) {
@@ -516,7 +535,9 @@ bool dry_run(const HostPlan& p, int n_threads, uint64_t seed, int drop_task, int
                     if (cur[k] >= p.queue_off[w + 1]) left--;
                     progressed = true;
                     if (t.op == OP_ATTN) {
-                        if (run_attn(s, t.layer, t.a0, t.a1, t.level)) signal(t.sig_ev);
+                        int bg, sp;
+                        if (locate_split(s, step_chunk(s), t.a0, bg, sp) && run_attn(s, t.layer, bg, sp, t.level))
+                            signal(t.sig_ev);
                         continue;
                     }
                     run_gemv(s, t);

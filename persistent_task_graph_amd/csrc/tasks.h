@@ -79,6 +79,23 @@ __device__ __forceinline__ int attn_chunk(const KParams& p) {
     return attn_chunk_search(total, p.chunk, p.chunk_max, p.attn_target);
 }
 
+// Split task k of the step, counted in (b, g, split) order, for chunk C:
+// its (b * Hkv + g, split), or false when the step has fewer tasks.
+// Uniform across the workgroup (scalar loads of seq_lens).
+__device__ __forceinline__ bool attn_locate(const KParams& p, int C, int k, int& bg, int& split) {
+    for (int b = 0; b < p.B; ++b) {
+        const int pos = p.seq_lens[b];
+        const int ns = (pos < 0 || pos + 1 > p.cap) ? 1 : (pos + C) / C;
+        if (k < ns * p.Hkv) {
+            bg = b * p.Hkv + k / ns;
+            split = k % ns;
+            return true;
+        }
+        k -= ns * p.Hkv;
+    }
+    return false;
+}
+
 __device__ __forceinline__ float* layer_buf(const KParams& p, int l, int64_t off) { return p.act + l * p.act_stride + off; }
 __device__ __forceinline__ const float* layer_in(const KParams& p, int l) {
     return l == 0 ? p.x0 : (l == p.L ? p.x_final : layer_buf(p, l - 1, p.off_xnext));

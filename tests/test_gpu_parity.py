@@ -83,9 +83,9 @@ def test_tiny_worker_count_invariance(tiny, workers):
 
 
 def test_tiny_jit_vs_aot_and_repeat(tiny):
-    log("tiny: JIT vs AOT attention, repeat run")
+    log("tiny: AOT (default) vs JIT attention, repeat run")
     a, _ = _logits_seq(tiny, 6, kv_chunk=16)
-    b, _ = _logits_seq(tiny, 6, kv_chunk=16, jit=2)
+    b, _ = _logits_seq(tiny, 6, kv_chunk=16, jit=1)
     c, _ = _logits_seq(tiny, 6, kv_chunk=16)
     _bitwise(a, b)
     _bitwise(a, c)
@@ -135,11 +135,11 @@ def test_mid_bf16_matches_oracle(mid_weights, B, lens, chunk):
 
 
 def test_mid_modes_bitwise(mid_weights):
-    log("mid bf16: persistent vs kernel-per-op vs AOT vs workers=37, B=2")
+    log("mid bf16: persistent vs kernel-per-op vs JIT vs workers=37, B=2")
     s = make_setup(MID, 2, [100, 333], 400, weights=mid_weights)
     a, _ = _logits_seq(s, 3, kv_chunk=64)
     b, _ = _logits_seq(s, 3, kv_chunk=64, mode=1)
-    c, _ = _logits_seq(s, 3, kv_chunk=64, jit=2)
+    c, _ = _logits_seq(s, 3, kv_chunk=64, jit=1)
     d, _ = _logits_seq(s, 3, kv_chunk=64, workers=37)
     for o in (b, c, d):
         _bitwise(a, o)
@@ -163,7 +163,7 @@ def test_mid_adaptive_chunk_matches_oracle_and_modes(mid_weights):
     log("  max|d|/std = %.3g, top-1 = %.3f" % (worst, agree))
     assert worst <= 2e-2 and agree >= 0.99
     b, _ = _logits_seq(s, 2, tokens=_tokens(MID, 4, 11), mode=1, **opts)
-    c, _ = _logits_seq(s, 2, tokens=_tokens(MID, 4, 11), jit=2, **opts)
+    c, _ = _logits_seq(s, 2, tokens=_tokens(MID, 4, 11), jit=1, **opts)
     e, _ = _logits_seq(s, 2, tokens=_tokens(MID, 4, 11), kv_chunk=16)  # default worker count: same chunk
     d, _ = _logits_seq(s, 2, tokens=_tokens(MID, 4, 11), kv_chunk=16, kv_chunk_max=16, workers=64)
     _bitwise(out, b)

@@ -44,14 +44,19 @@ def test_workload_plans_verify(lib, name):
     p = _plan(wl.shape, wl.batch, wl.capacity(), paged=wl.paged)
     p.verify()
     inf = p.info()
-    assert inf.workers == 252 and inf.sched_waves == 16
+    assert inf.workers == 256 and inf.sched_waves == 0  # AOT attention: no scheduler CUs
     assert inf.weight_bytes_per_step == wl.shape.step_weight_bytes()
     L = wl.shape.n_layers
     assert inf.n_levels == 5 * L + (2 if wl.shape.embed_head else 0)
     # one GEMV task per worker per operator (rows >= workers)
     for op in (mk.OP_QKV, mk.OP_O, mk.OP_GATEUP, mk.OP_DOWN):
-        assert inf.tasks_per_op[op] == L * min(252, 1 << 30)
-    assert inf.tasks_per_op[mk.OP_ATTN] == 0  # JIT by default
+        assert inf.tasks_per_op[op] == L * 256
+    assert inf.tasks_per_op[mk.OP_ATTN] > 0  # AOT attention slots by default
+    j = _plan(wl.shape, wl.batch, wl.capacity(), paged=wl.paged, jit=1)
+    j.verify()
+    ji = j.info()
+    assert ji.workers == 252 and ji.sched_waves == 16
+    assert ji.tasks_per_op[mk.OP_ATTN] == 0  # JIT: created on the device
 
 
 def test_eight_b_step_bytes_match_definition(lib):
@@ -80,7 +85,7 @@ def test_dry_run_full_model_default_workers(lib):
 
 def test_dry_run_dropped_producer_times_out(lib):
     shape = replace(synth.Q8B, n_layers=2)
-    p = _plan(shape, 1, 256, workers=8)
+    p = _plan(shape, 1, 256, workers=8, jit=1)  # task 20 is then a GEMV task
     rc = p.dry_run(n_threads=4, seed=1, drop_task=20, timeout_ms=500, seq_lens=[10])
     assert rc == mk.MK_ERR_STATE and "timeout" in mk.last_error()
 
@@ -117,9 +122,27 @@ def test_step_on_host_only_plan_is_state_error(lib):
     assert rc == mk.MK_ERR_STATE
 
 
-def test_aot_attention_reserves_max_splits(lib):
+def test_aot_attention_slots(lib):
+    # one slot per split task a step can have: at most 240 while the chunk can
+    # still grow, else every split at kv_chunk_max
     p = _plan(synth.TINY, 1, 48, jit=2, kv_chunk=16)
     inf = p.info()
     assert inf.max_splits == 3
     assert inf.tasks_per_op[mk.OP_ATTN] == 2 * 4 * 3
     p.verify()
+    p = _plan(replace(synth.Q8B, n_layers=2), 16, 4200, jit=2, kv_chunk=128)
+    inf = p.info()
+    assert inf.max_splits == 33
+    assert inf.tasks_per_op[mk.OP_ATTN] == 2 * 16 * 8 * 2  # 4200 keys need 2 splits of 4096
+    p.verify()
+    p = _plan(replace(synth.Q8B, n_layers=2), 4, 1024, jit=2, kv_chunk=128)
+    assert p.info().tasks_per_op[mk.OP_ATTN] == 2 * 240
+    p.verify()
+
+
+def test_aot_slots_dry_run_capped_chunk(lib):
+    # the chunk capped at kv_chunk_max: more than 240 split tasks, one slot each
+    shape = replace(synth.Q8B, n_layers=2)
+    p = _plan(shape, 16, 4200, jit=2, workers=24, kv_chunk=64, kv_chunk_max=64)
+    seq = [4000] * 16  # 16 * 8 * 63 split tasks per layer
+    assert p.dry_run(n_threads=6, seed=5, timeout_ms=60000, seq_lens=seq) == 0, mk.last_error()
