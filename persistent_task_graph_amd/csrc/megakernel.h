@@ -185,6 +185,7 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s, uint
             if (chunk == 0) chunk = attn_chunk(p);
             int abg, asp;
             if (!attn_locate(p, chunk, t.a0, abg, asp)) abg = -1;
+            else if constexpr (!kStream) pf = attn_prefetch_setup<WT>(p, t.layer, abg, asp, chunk);
             if (threadIdx.x == 0) {
                 s.cmd[12] = abg;
                 s.cmd[13] = asp;

@@ -818,6 +818,31 @@ __device__ __forceinline__ Prefetch prefetch_setup(const KParams& p, const TaskR
     return f;
 }
 
+// Cursor over the cached K and V rows of an attention split (contiguous
+// cache only): the rows before position pos are fixed for the step, so a slot
+// can pull them toward the chip while it waits for the layer's QKV event.
+// Row pos is appended by this step and never read from memory by it.
+template <typename WT>
+__device__ __forceinline__ Prefetch attn_prefetch_setup(const KParams& p, int l, int bg, int split, int C) {
+    Prefetch f;
+    f.kb_a = f.kb_b = 0;
+    f.next = f.end = 0;
+    f.a = f.b = make_rsrc(p.zero, 0);
+    if (p.prefetch_kb <= 0 || p.paged) return f;
+    const int b = bg / p.Hkv, g = bg % p.Hkv;
+    const int pos = p.seq_lens[b];
+    if (pos < 0 || pos + 1 > p.cap) return f;
+    const int j0 = split * C, j1 = min(j0 + C, pos);
+    if (j1 <= j0) return f;
+    const int64_t off = (int64_t)l * p.kv_layer_stride + ((int64_t)(b * p.Hkv + g) * p.cap + j0) * p.D;
+    const uint32_t bytes = (uint32_t)(j1 - j0) * (uint32_t)p.D * (uint32_t)sizeof(WT);
+    f.a = make_rsrc((const WT*)p.kv_k + off, bytes);
+    f.b = make_rsrc((const WT*)p.kv_v + off, bytes);
+    f.kb_a = f.kb_b = (bytes + 1023u) / 1024u;
+    f.end = min(f.kb_a + f.kb_b, (uint32_t)p.prefetch_kb);
+    return f;
+}
+
 // Issue the next slice: each wave takes every kWaves-th KB. With two
 // segments, KB i of the stream is KB i/2 of segment (i & 1). Offsets past a
 // segment are out of range for its resource and fetch nothing.
@@ -1172,19 +1197,31 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
         for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s.wml[w * 16 + hh]);
         return M;  // finite: the split holds at least one key
     };
-    for (int i = tid; i < G * D; i += kThreads) {
-        const int hh = i / D, d = i % D;
-        const float M = split_max(hh);
-        float a = s.acc[hh * 128 + d] * wave_scale(0, hh, M);
-        for (int w = 1; w < kWaves; ++w) a = fmaf(s.acc[(w * 8 + hh) * 128 + d], wave_scale(w, hh, M), a);
-        st_co(&part[i], a);
-    }
     if (tid < G) {
         const float M = split_max(tid);
         float L = s.wml[8 + tid] * wave_scale(0, tid, M);
         for (int w = 1; w < kWaves; ++w) L = fmaf(s.wml[w * 16 + 8 + tid], wave_scale(w, tid, M), L);
-        st_co(&part[G * D + tid], M);
-        st_co(&part[G * D + 8 + tid], L);
+        s.ml[2 * tid] = M;
+        s.ml[2 * tid + 1] = L;
+        if (ns > 1) {
+            st_co(&part[G * D + tid], M);
+            st_co(&part[G * D + 8 + tid], L);
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < G * D; i += kThreads) {
+        const int hh = i / D, d = i % D;
+        const float M = s.ml[2 * hh];
+        float a = s.acc[hh * 128 + d] * wave_scale(0, hh, M);
+        for (int w = 1; w < kWaves; ++w) a = fmaf(s.acc[(w * 8 + hh) * 128 + d], wave_scale(w, hh, M), a);
+        // a sequence of one split is its own combine: the merge below would
+        // compute a * e^0 / (l * e^0), the same bits
+        if (ns == 1) st_co(&out[i], a / s.ml[2 * hh + 1]);
+        else st_co(&part[i], a);
+    }
+    if (ns == 1) {
+        if (p.persistent) signal_event(p, ev_attn(l), s);
+        return;
     }
 
     // 6. last arrival merges the splits in split order
