@@ -432,7 +432,7 @@ __device__ __forceinline__ mk_f32x4 mfma_bf16(const uint4& a, const mk_bf16x8& b
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mk_bf16x8, a), b, c, 0, 0, 0);
 }
 
-template <int NB, bool DUAL, int TMAX, int NSEG, typename OutFn>
+template <int NB, bool DUAL, int TMAX, int NSEG, typename OutFn, int NST = 2>
 __device__ __forceinline__ void gemv_mfma(const MSeg (&seg)[NSEG], int K, const float* x, int ldx, int B,
                                           const bf16_t* gain, float eps, OutFn out, const Lds& s, bool tr) {
     constexpr int NM = DUAL ? 2 : 1;
@@ -545,14 +545,30 @@ __device__ __forceinline__ void gemv_mfma(const MSeg (&seg)[NSEG], int K, const 
                 }
             }
         };
-        Stage sa, sb;
-        load(sa, 0);
-        if (tr && tid == 0 && t0 == 0) s.marks[0] = now_ticks();
-        for (int i = 0; i < nmine; i += 2) {
-            load(sb, i + 1);
-            compute(sa);
-            load(sa, i + 2);
-            if (i + 1 < nmine) compute(sb);
+        if constexpr (NST == 2) {
+            Stage sa, sb;
+            load(sa, 0);
+            if (tr && tid == 0 && t0 == 0) s.marks[0] = now_ticks();
+            for (int i = 0; i < nmine; i += 2) {
+                load(sb, i + 1);
+                compute(sa);
+                load(sa, i + 2);
+                if (i + 1 < nmine) compute(sb);
+            }
+        } else {
+            // three stages: two blocks in flight while one is multiplied
+            Stage sa, sb, sc;
+            load(sa, 0);
+            load(sb, 1);
+            if (tr && tid == 0 && t0 == 0) s.marks[0] = now_ticks();
+            for (int i = 0; i < nmine; i += 3) {
+                load(sc, i + 2);
+                compute(sa);
+                load(sa, i + 3);
+                if (i + 1 < nmine) compute(sb);
+                load(sb, i + 4);
+                if (i + 2 < nmine) compute(sc);
+            }
         }
         if (stat) {
             // norm statistic: lanes b, b+16, b+32, b+48 of each wave, then waves in order
@@ -660,7 +676,7 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
             };
             if constexpr (kMfma) {
                 const MSeg sg[1] = {{to.r, to.r, to.n, to.lo}};
-                gemv_mfma<NB, false, 2>(sg, K, a, K, B, (const bf16_t*)nullptr, p.eps, out, s, p.trace != nullptr);
+                gemv_mfma<NB, false, 2, 1, decltype(out), 3>(sg, K, a, K, B, (const bf16_t*)nullptr, p.eps, out, s, p.trace != nullptr);
             } else {
                 gemv_dispatch<WT, NB, false>(r0, r1, K, a, K, B, (const WT*)nullptr, p.eps, rowp, out, s, p.trace != nullptr);
             }
@@ -704,7 +720,7 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
             };
             if constexpr (kMfma) {
                 const MSeg sg[1] = {{td.r, td.r, td.n, td.lo}};
-                gemv_mfma<NB, false, 2>(sg, F, h, F, B, (const bf16_t*)nullptr, p.eps, out, s, p.trace != nullptr);
+                gemv_mfma<NB, false, 2, 1, decltype(out), 3>(sg, F, h, F, B, (const bf16_t*)nullptr, p.eps, out, s, p.trace != nullptr);
             } else {
                 gemv_dispatch<WT, NB, false>(r0, r1, F, h, F, B, (const WT*)nullptr, p.eps, rowp, out, s, p.trace != nullptr);
             }
