@@ -26,6 +26,7 @@ struct Lds {
     float* wml;   // kWaves * 16: per wave (m[8], l[8])
     float* ml;    // 2 * 8: (m, l) per head of the split
     float* cmb;   // kCmbSplits * (8 * 128 + 16): partials staged for the combine
+    float* pt;    // kWaves * 32 * 8: attention probabilities per wave [row][head]
     int* btab;    // paged cache: block-table entries of the split
     uint64_t* marks;  // 4 trace phase marks
 };
@@ -33,7 +34,8 @@ struct Lds {
 constexpr int kCmbSplits = 4;  // splits merged per staged chunk
 constexpr int kPartFloats = 8192;  // GEMV cross-wave partial sums
 constexpr int kLdsHeader = kWaves * 16 + 16 + 16 + 8;
-constexpr int kAttnFloats = 8 * 128 + 2 * 128 + kWaves * 8 * 128 + kWaves * 16 + 16 + kCmbSplits * (8 * 128 + 16);
+constexpr int kAttnFloats = 8 * 128 + 2 * 128 + kWaves * 8 * 128 + kWaves * 16 + 16 + kCmbSplits * (8 * 128 + 16) +
+                            kWaves * 32 * 8;
 // GEMV and embedding tasks touch only the header and the partial sums
 __host__ __device__ constexpr int lds_bytes_gemv() { return 4 * (kLdsHeader + kPartFloats); }
 // block-table entries one split of `chunk` keys can span
@@ -57,6 +59,7 @@ __device__ __forceinline__ Lds carve_lds(float* base) {
     s.wml = p; p += kWaves * 16;
     s.ml = p; p += 16;
     s.cmb = p; p += kCmbSplits * (8 * 128 + 16);
+    s.pt = p; p += kWaves * 32 * 8;
     s.btab = (int*)p;
     return s;
 }
@@ -990,16 +993,26 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
     const float2 cs = p.rope[(int64_t)pos * (D / 2) + (D == 128 ? lane : (lane & 31))];
     asm volatile("" ::: "memory");
 
-    // K/V rows of this split: lane (rr, cc) holds 16 bytes of row
-    // j = it*PER_IT + wave*PPW + rr; one batch covers SUB rows.
+    // K/V rows of this split. V (and, for an fp32 cache, K) is held in the
+    // lane layout of the P.V update: lane (rr, cc) holds 16 bytes (column
+    // segment cc) of one row per load. With a bf16 cache the scores run on the
+    // 16x16x32 matrix cores and K is loaded in their operand layout instead:
+    // lane l holds row l % 16 of a 16-row tile and 16 * KS contiguous bytes of
+    // it (dims 8*KS*(l/16) ..), the query dims permuted the same way.
     using VK = Vec16<WT>;
     constexpr int E = VK::N;
-    constexpr int LPR = D / E;             // lanes per K row
+    constexpr int LPR = D / E;             // lanes per row in the P.V layout
     constexpr int PPW = 64 / LPR;          // rows per wave per load
     constexpr int PER_IT = kWaves * PPW;   // rows per workgroup iteration
-    constexpr int NIT = (GP >= 8 ? 16 : 32) / kWaves;  // iterations per batch (fewer registers for 8 heads)
-    constexpr int SUB = PER_IT * NIT;      // rows per batch
+    constexpr bool kMf = std::is_same<WT, bf16_t>::value;
+    constexpr int WR = 16;                 // rows per wave per batch in the matrix-core layout (16-row tiles)
+    constexpr int NT = WR / 16;            // tiles per wave per batch
+    constexpr int KS = D / 32;             // MFMA k-steps per row
+    constexpr int NIT = kMf ? WR / PPW : (GP >= 8 ? 16 : 32) / kWaves;  // V loads per lane per batch
+    constexpr int NK = kMf ? NT * KS : NIT;                             // K loads per lane per batch
+    constexpr int SUB = kMf ? kWaves * WR : PER_IT * NIT;               // rows per batch
     const int rr = lane / LPR, cc = lane % LPR;
+    const int li = lane & 15, lg = lane >> 4;  // matrix-core row and k group
     // K/V of this (layer, b, g) through buffer resources; rows past the split
     // (or the new row, which comes from LDS) load through an out-of-range
     // offset: no branches around loads
@@ -1023,39 +1036,43 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
         const int nblk = (j1 - 1) / p.kv_block - blk0 + 1;
         for (int i = tid; i < nblk; i += kThreads) s.btab[i] = btab[blk0 + i];
     }
-    // byte offsets of this lane's 16 bytes for NIT rows starting at `base`
-    auto row_offsets = [&](int base, uint32_t (&ro)[NIT], bool staged) {
-        int blk[NIT];
+    // byte offset of row j of the split (plus `add`), or out of range for
+    // rows past the split and for the new row
+    auto row_off = [&](int j, uint32_t add, bool staged) -> uint32_t {
+        const int jj = j0 + j;
+        if (j >= n || jj == pos) return kOOB;
+        uint32_t o;
         if (p.paged) {
+            const int bi = jj / p.kv_block;
+            const int blk = staged ? s.btab[bi - blk0] : btab[bi];
+            o = (uint32_t)(((blk * Hkv + g) * p.kv_block + jj % p.kv_block) * D * es);
+        } else {
+            o = (uint32_t)(jj * D * es);
+        }
+        return o + add;
+    };
+    // row of the split that V load `it` of this lane holds in a batch at `base`
+    auto vrow = [&](int base, int it) {
+        return kMf ? base + wave * WR + it * PPW + rr : base + it * PER_IT + wave * PPW + rr;
+    };
+    // K and V rows of a batch into registers (rows at or past n fetch nothing)
+    auto load_kv = [&](uint4 (&kd)[NK], uint4 (&vd)[NIT], int base, bool staged) {
 #pragma unroll
-            for (int it = 0; it < NIT; ++it) {
-                const int j = base + it * PER_IT + wave * PPW + rr;
-                const int bi = (j0 + j) / p.kv_block;
-                blk[it] = j < n ? (staged ? s.btab[bi - blk0] : btab[bi]) : 0;
+        for (int q = 0; q < NK; ++q) {
+            if constexpr (kMf) {
+                const int j = base + wave * WR + 16 * (q / KS) + li;
+                kd[q] = buf_load16(krs, row_off(j, (uint32_t)(16 * (KS * lg + q % KS)), staged), 0);
+            } else {
+                kd[q] = buf_load16(krs, row_off(vrow(base, q), (uint32_t)(cc * 16), staged), 0);
             }
         }
 #pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-            const int j = base + it * PER_IT + wave * PPW + rr;
-            const int jj = j0 + j;
-            uint32_t o;
-            if (p.paged) o = (uint32_t)(((blk[it] * Hkv + g) * p.kv_block + jj % p.kv_block) * D * es);
-            else o = (uint32_t)(jj * D * es);
-            ro[it] = (j < n && jj != pos) ? o + (uint32_t)(cc * 16) : kOOB;
-        }
+        for (int it = 0; it < NIT; ++it) vd[it] = buf_load16(vrs, row_off(vrow(base, it), (uint32_t)(cc * 16), staged), 0);
     };
     // the first batch of K and V rows is requested before the prologue's math
     const bool one_batch = n <= SUB;
-    uint4 kr[NIT], vr[NIT];
-    {
-        uint32_t ro[NIT];
-        row_offsets(0, ro, false);
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-            kr[it] = buf_load16(krs, ro[it], 0);
-            vr[it] = buf_load16(vrs, ro[it], 0);
-        }
-    }
+    uint4 kr[NK], vr[NIT];
+    load_kv(kr, vr, 0, false);
 
     // 1. query heads of this group: norm + RoPE into LDS
 #pragma unroll
@@ -1081,23 +1098,11 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
     __syncthreads();
     trace_mark(p, s.marks, 0);
 
-    // K and V rows of a batch into registers (rows at or past n fetch nothing)
-    auto load_kv = [&](uint4 (&kd)[NIT], uint4 (&vd)[NIT], int base) {
-        uint32_t ro[NIT];
-        row_offsets(base, ro, true);
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-            kd[it] = buf_load16(krs, ro[it], 0);
-            vd[it] = buf_load16(vrs, ro[it], 0);
-        }
-    };
     // 3. one pass over the split's keys with a running (max, sum, acc) per
     // head in each wave: the K and V rows of a batch are requested together,
-    // one batch ahead of the one in use. Lanes (rr, cc) of row group rr hold
-    // the full score of their row after the group sum, which is exactly the
-    // probability their P.V update needs, so scores never leave registers.
-    // The running max is wave-uniform (maxed over the row groups), which
-    // keeps every lane's acc on one scale; the four waves merge at the end.
+    // one batch ahead of the one in use. The running max of a head is the
+    // same in every lane of the wave, which keeps every lane's acc on one
+    // scale; the four waves merge at the end.
     float acc[GP][E], lsum[GP], mrun[GP];
 #pragma unroll
     for (int hh = 0; hh < GP; ++hh) {
@@ -1106,7 +1111,9 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[hh][e] = 0.f;
     }
-    auto process = [&](const uint4 (&kk)[NIT], const uint4 (&vv)[NIT], int base) {
+    // fp32 cache: lanes (rr, cc) of row group rr hold the full score of their
+    // row after the group sum, which is the probability their P.V update needs
+    auto process_valu = [&](const uint4 (&kk)[NK], const uint4 (&vv)[NIT], int base) {
         float d[NIT][GP];
         float bm[GP];
 #pragma unroll
@@ -1163,14 +1170,112 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
             }
         }
     };
+    // bf16 cache: scores on the matrix cores. Query heads are the 16 columns
+    // (heads past G are zeros), split hi + lo into bf16 like the GEMV
+    // activations; each wave scores its 16-row tiles, keeps the online
+    // softmax on the result tiles (lane l: rows 4*(l/16) + r, head l % 16)
+    // and hands the probabilities to its P.V lanes through LDS.
+    mk_bf16x8 qh[KS], ql[KS];
+    if constexpr (kMf) {
+#pragma unroll
+        for (int q = 0; q < KS; ++q)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float v = li < G ? s.q[li * D + 8 * KS * lg + 8 * q + e] : 0.f;
+                const __bf16 h = (__bf16)v;
+                qh[q][e] = h;
+                ql[q][e] = (__bf16)(v - (float)h);
+            }
+    }
+    float* pw = s.pt + wave * (WR * 8);  // this wave's probabilities [row][head]
+    float mlane = -INFINITY;             // running max of head li, as mrun[li]
+    auto process_mf = [&](const uint4 (&kk)[NK], const uint4 (&vv)[NIT], int base) {
+        mk_f32x4 sc[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            sc[t] = mk_f32x4{0.f, 0.f, 0.f, 0.f};
+            const int j = base + wave * WR + 16 * t + li;
+            const bool nw = j < n && j0 + j == pos;  // the new row's k comes from LDS
+#pragma unroll
+            for (int q = 0; q < KS; ++q) {
+                uint4 a = kk[t * KS + q];
+                if (nw) {
+                    mk_bf16x8 kb;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) kb[e] = (__bf16)s.kn[8 * KS * lg + 8 * q + e];
+                    a = __builtin_bit_cast(uint4, kb);
+                }
+                sc[t] = mfma_bf16(a, qh[q], sc[t]);
+                sc[t] = mfma_bf16(a, ql[q], sc[t]);
+            }
+        }
+        // scale, mask rows past the split, batch max of head li
+        float bm = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = base + wave * WR + 16 * t + 4 * lg + r;
+                sc[t][r] = j < n ? sc[t][r] * p.scale : -INFINITY;
+                bm = fmaxf(bm, sc[t][r]);
+            }
+        bm = column_max<16>(bm);
+        float mz[GP];
+#pragma unroll
+        for (int hh = 0; hh < GP; ++hh) {
+            const float mn = fmaxf(mrun[hh], read_lane(bm, hh));
+            // mn is -inf only while this wave has seen no key: nothing to scale
+            const float corr = mn == -INFINITY ? 1.f : __expf(mrun[hh] - mn);
+            mz[hh] = mn == -INFINITY ? 0.f : mn;
+            lsum[hh] *= corr;
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[hh][e] *= corr;
+            mrun[hh] = mn;
+        }
+        mlane = fmaxf(mlane, bm);
+        const float mzl = mlane == -INFINITY ? 0.f : mlane;
+        if (li < GP) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) pw[(16 * t + 4 * lg + r) * 8 + li] = __expf(sc[t][r] - mzl);  // 0 past the split
+        }
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int jw = it * PPW + rr;  // row within the wave's WR
+            const int j = base + wave * WR + jw;
+            float vf[E];
+            if (j < n && j0 + j == pos) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) vf[e] = s.kn[128 + cc * E + e];
+            } else {
+                VK::widen(vv[it], vf);  // rows past the split loaded zeros
+            }
+#pragma unroll
+            for (int hh = 0; hh < GP; ++hh) {
+                const float pj = pw[jw * 8 + hh];
+                lsum[hh] += pj;
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[hh][e] = fmaf(pj, vf[e], acc[hh][e]);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
+    };
+    auto process = [&](const uint4 (&kk)[NK], const uint4 (&vv)[NIT], int base) {
+        if constexpr (kMf) process_mf(kk, vv, base);
+        else process_valu(kk, vv, base);
+    };
     if (one_batch) {
         process(kr, vr, 0);
     } else {
-        uint4 kb[NIT], vb[NIT];
+        uint4 kb[NK], vb[NIT];
         for (int base = 0; base < n; base += 2 * SUB) {
-            load_kv(kb, vb, base + SUB);
+            load_kv(kb, vb, base + SUB, true);
             process(kr, vr, base);
-            load_kv(kr, vr, base + 2 * SUB);
+            load_kv(kr, vr, base + 2 * SUB, true);
             if (base + SUB < n) process(kb, vb, base + SUB);
         }
     }
