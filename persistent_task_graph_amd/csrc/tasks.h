@@ -997,8 +997,8 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
     // lane layout of the P.V update: lane (rr, cc) holds 16 bytes (column
     // segment cc) of one row per load. With a bf16 cache the scores run on the
     // 16x16x32 matrix cores and K is loaded in their operand layout instead:
-    // lane l holds row l % 16 of a 16-row tile and 16 * KS contiguous bytes of
-    // it (dims 8*KS*(l/16) ..), the query dims permuted the same way.
+    // for k-step q, lane l holds dims 32 q + 8 (l/16) .. + 7 of row l % 16 of
+    // a 16-row tile, so one load covers 64 contiguous bytes of each row.
     using VK = Vec16<WT>;
     constexpr int E = VK::N;
     constexpr int LPR = D / E;             // lanes per row in the P.V layout
@@ -1061,7 +1061,7 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
         for (int q = 0; q < NK; ++q) {
             if constexpr (kMf) {
                 const int j = base + wave * WR + 16 * (q / KS) + li;
-                kd[q] = buf_load16(krs, row_off(j, (uint32_t)(16 * (KS * lg + q % KS)), staged), 0);
+                kd[q] = buf_load16(krs, row_off(j, (uint32_t)(16 * (4 * (q % KS) + lg)), staged), 0);
             } else {
                 kd[q] = buf_load16(krs, row_off(vrow(base, q), (uint32_t)(cc * 16), staged), 0);
             }
@@ -1181,7 +1181,7 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
         for (int q = 0; q < KS; ++q)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float v = li < G ? s.q[li * D + 8 * KS * lg + 8 * q + e] : 0.f;
+                const float v = li < G ? s.q[li * D + 32 * q + 8 * lg + e] : 0.f;
                 const __bf16 h = (__bf16)v;
                 qh[q][e] = h;
                 ql[q][e] = (__bf16)(v - (float)h);
@@ -1202,7 +1202,7 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
                 if (nw) {
                     mk_bf16x8 kb;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) kb[e] = (__bf16)s.kn[8 * KS * lg + 8 * q + e];
+                    for (int e = 0; e < 8; ++e) kb[e] = (__bf16)s.kn[32 * q + 8 * lg + e];
                     a = __builtin_bit_cast(uint4, kb);
                 }
                 sc[t] = mfma_bf16(a, qh[q], sc[t]);
