@@ -154,14 +154,13 @@ def main():
         raise SystemExit("device error %d during prefill" % err)
 
     def run(n, plan, kv, d_tok, d_len, logits, events=None):
+        # greedy decode: each launch also writes the next tokens and advances the lengths
         for i in range(n):
             if events is not None:
                 events[i][0].record(st)
-            plan.step(dm.struct, kv.struct, d_tok, d_len, logits)
+            plan.step_greedy(dm.struct, kv.struct, d_tok, d_len, logits)
             if events is not None:
                 events[i][1].record(st)
-            plan.argmax(logits, d_tok)
-            d_len += 1
 
     def ablation(Bn, capn, kv, d_tok, d_len, logits):
         """ms/step of the same step with JIT attention through the scheduler

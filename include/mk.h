@@ -225,6 +225,17 @@ int mk_decode_step(mk_plan* plan, const mk_weights* weights, const mk_kv_cache* 
                    const int32_t* seq_lens, float* logits, void* stream);
 
 /*
+ * One decode step with the greedy choice fused into it: as mk_decode_step,
+ * and then, in the same launch, tokens[b] is overwritten with the argmax of
+ * logits[b] (lowest index on ties, NaN never chosen, as mk_argmax) and
+ * seq_lens[b] is incremented, ready for the next step. The argmax is folded
+ * into the LM-head tasks; the last of them writes tokens and seq_lens after
+ * every reader of the step's lengths has finished. Not for hidden_io plans.
+ */
+int mk_decode_step_greedy(mk_plan* plan, const mk_weights* weights, const mk_kv_cache* kv, int32_t* tokens,
+                          int32_t* seq_lens, float* logits, void* stream);
+
+/*
  * Hidden-state variant for hidden_io plans: x_in, x_out are device float
  * [batch, hidden] (they may not alias); otherwise as mk_decode_step.
  */

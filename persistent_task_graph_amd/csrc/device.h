@@ -73,6 +73,11 @@ struct KParams {
     int mb_mask;
     uint64_t watchdog_ticks;  // 100 MHz ticks
     int prefetch_kb;          // next-task weight bytes pulled into L2 per worker (KB)
+    int32_t* greedy_tokens;   // greedy step: next token of each sequence written here (else null)
+    int32_t* greedy_lens;     // greedy step: each sequence's length advanced here
+    unsigned long long* amax; // [B] packed (value, index) argmax keys; zero between steps
+    uint32_t* lm_done;        // LM-head tasks finished in this step (reset by the last)
+    int n_lm_tasks;
     // optional task trace: per worker `trace_cap` records, count in trace_n
     mk_trace_rec* trace;
     int32_t* trace_n;

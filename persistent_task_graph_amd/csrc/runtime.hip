@@ -104,6 +104,8 @@ struct mk_plan {
     EventRec* d_evrec = nullptr;
     uint32_t* d_ev = nullptr;
     uint32_t* d_arrive = nullptr;
+    unsigned long long* d_amax = nullptr;  // greedy step: per-sequence argmax keys
+    uint32_t* d_lm_done = nullptr;         // greedy step: LM tasks finished
     RingSlot* d_inbox = nullptr;
     int64_t* d_inbox_tail = nullptr;
     int64_t* d_inbox_head = nullptr;
@@ -200,6 +202,8 @@ bool upload_plan(mk_plan* pl) {
     // zero-initialised control area: events, arrivals, rings, ctrl
     Region r_ev = take(sizeof(uint32_t) * hp.events.size());
     Region r_arr = take(sizeof(uint32_t) * (size_t)B * Hkv);
+    Region r_amax = take(sizeof(unsigned long long) * (size_t)B);
+    Region r_lmd = take(sizeof(uint32_t));
     Region r_inbox = take(sizeof(RingSlot) * (size_t)hp.workers * hp.inbox_cap);
     Region r_itail = take(sizeof(int64_t) * (size_t)hp.workers);
     Region r_ihead = take(sizeof(int64_t) * (size_t)hp.workers);
@@ -231,6 +235,8 @@ bool upload_plan(mk_plan* pl) {
     pl->d_evrec = (EventRec*)(m + r_evrec.off);
     pl->d_ev = (uint32_t*)(m + r_ev.off);
     pl->d_arrive = (uint32_t*)(m + r_arr.off);
+    pl->d_amax = (unsigned long long*)(m + r_amax.off);
+    pl->d_lm_done = (uint32_t*)(m + r_lmd.off);
     pl->d_inbox = (RingSlot*)(m + r_inbox.off);
     pl->d_inbox_tail = (int64_t*)(m + r_itail.off);
     pl->d_inbox_head = (int64_t*)(m + r_ihead.off);
@@ -312,6 +318,9 @@ KParams make_params(const mk_plan* pl, const mk_weights* w, const mk_kv_cache* k
     p.evrec = pl->d_evrec;
     p.ev = pl->d_ev;
     p.arrive = pl->d_arrive;
+    p.amax = pl->d_amax;
+    p.lm_done = pl->d_lm_done;
+    p.n_lm_tasks = hp.tasks_per_op[OP_LM];
     p.inbox = pl->d_inbox;
     p.inbox_tail = pl->d_inbox_tail;
     p.inbox_head = pl->d_inbox_head;
@@ -423,11 +432,14 @@ int sync_pointer_table(mk_plan* pl, const mk_weights* w, hipStream_t st) {
 }
 
 int launch_step(mk_plan* pl, const mk_weights* w, const mk_kv_cache* kv, const int32_t* tokens, const int32_t* seq_lens,
-                const float* x_in, float* out, hipStream_t st) {
+                const float* x_in, float* out, hipStream_t st, int32_t* greedy_tokens = nullptr,
+                int32_t* greedy_lens = nullptr) {
     if (!hip_ok(hipSetDevice(pl->device), "hipSetDevice")) return MK_ERR_HIP;
     int rc = sync_pointer_table(pl, w, st);
     if (rc) return rc;
     KParams p = make_params(pl, w, kv, tokens, seq_lens, x_in, out);
+    p.greedy_tokens = greedy_tokens;
+    p.greedy_lens = greedy_lens;
     const HostPlan& hp = pl->hp;
     if (hp.desc.opts.mode == MK_PERSISTENT) {
         void* args[] = {&p};
@@ -542,6 +554,14 @@ int mk_decode_step(mk_plan* pl, const mk_weights* w, const mk_kv_cache* kv, cons
     if (rc) return rc;
     if (pl->hp.desc.hidden_io) return set_err("hidden_io plan: use mk_decode_step_hidden"), MK_ERR_STATE;
     return launch_step(pl, w, kv, tokens, seq_lens, nullptr, logits, (hipStream_t)stream);
+}
+
+int mk_decode_step_greedy(mk_plan* pl, const mk_weights* w, const mk_kv_cache* kv, int32_t* tokens,
+                          int32_t* seq_lens, float* logits, void* stream) {
+    int rc = check_step_args(pl, w, kv, seq_lens, tokens, logits);
+    if (rc) return rc;
+    if (pl->hp.desc.hidden_io) return set_err("hidden_io plan has no logits"), MK_ERR_STATE;
+    return launch_step(pl, w, kv, tokens, seq_lens, nullptr, logits, (hipStream_t)stream, tokens, seq_lens);
 }
 
 int mk_decode_step_hidden(mk_plan* pl, const mk_weights* w, const mk_kv_cache* kv, const float* x_in,

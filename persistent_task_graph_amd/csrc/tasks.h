@@ -634,6 +634,58 @@ __device__ __forceinline__ void embed_task(const KParams& p, const TaskRec& t) {
     }
 }
 
+// ---------------------------------------------------------------- greedy step
+
+// Orderable key of logit v at vocabulary index i: a larger value wins, and
+// on equal values the lower index (-0 counts as +0; NaN is never passed).
+__device__ __forceinline__ unsigned long long argmax_key(float v, int i) {
+    const uint32_t u = __float_as_uint(v + 0.0f);
+    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((unsigned long long)o << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)i);
+}
+
+// Greedy step, after an LM-head task has stored logit rows [r0, r1): fold
+// them into each sequence's argmax key; the task that finishes the LM head
+// last turns the keys into the next tokens and advances the lengths (every
+// attention task of the step, the only other reader of the lengths, has
+// finished before the LM head starts). Same choice as k_argmax.
+__device__ __forceinline__ void lm_greedy(const KParams& p, int r0, int r1, const Lds& s) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    wait_stores();
+    __syncthreads();
+    // wave w folds sequences w, w + 4, ... (no workgroup barrier per sequence)
+    for (int b = wave; b < p.B; b += kWaves) {
+        const float* row = p.logits + (int64_t)b * p.V;
+        unsigned long long k = 0;  // 0: no candidate (all NaN)
+        for (int c = r0; c < r1; c += 16 * 64) {
+            // all of a lane's loads of the chunk are in flight together
+            float v[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int r = c + 64 * i + lane;
+                v[i] = r < r1 ? row[r] : __builtin_nanf("");
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (v[i] == v[i]) k = max(k, argmax_key(v[i], c + 64 * i + lane));
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) k = max(k, (unsigned long long)__shfl_xor((long long)k, o, 64));
+        if (lane == 0 && k) __hip_atomic_fetch_max(&p.amax[b], k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    wait_stores();  // the maxima are performed before this task counts as done
+    __syncthreads();
+    if (tid != 0) return;
+    const uint32_t old = __hip_atomic_fetch_add(p.lm_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old + 1u != (uint32_t)p.n_lm_tasks) return;
+    for (int b = 0; b < p.B; ++b) {
+        const unsigned long long k = __hip_atomic_exchange(&p.amax[b], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        p.greedy_tokens[b] = k ? (int32_t)(0xFFFFFFFFu - (uint32_t)k) : 0;
+        p.greedy_lens[b] += 1;
+    }
+    __hip_atomic_store(p.lm_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <typename WT, int NB>
 __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t, const Lds& s) {
     // bf16 weights with more than two sequences run on the matrix cores
@@ -742,6 +794,7 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
             } else {
                 gemv_dispatch<WT, NB, false>(r0, r1, H, x, H, B, (const WT*)p.final_norm, p.eps, rowp, out, s, p.trace != nullptr);
             }
+            if (p.greedy_tokens) lm_greedy(p, r0, r1, s);
             break;
         }
         default: break;

@@ -23,7 +23,7 @@ MK_ERR_TOKEN, MK_ERR_KV_OVERFLOW, MK_ERR_TIMEOUT = 1, 2, 4
 OP_QKV, OP_O, OP_GATEUP, OP_DOWN, OP_LM, OP_ATTN, OP_EMBED = 1, 2, 3, 4, 5, 6, 7
 
 EXPORTS = ["mk_build_graph", "mk_destroy_plan", "mk_last_error", "mk_plan_query", "mk_decode_step",
-           "mk_decode_step_hidden", "mk_get_device_error", "mk_argmax", "mk_plan_verify", "mk_plan_dry_run",
+           "mk_decode_step_greedy", "mk_decode_step_hidden", "mk_get_device_error", "mk_argmax", "mk_plan_verify", "mk_plan_dry_run",
            "mk_plan_trace"]
 
 
@@ -95,14 +95,15 @@ def lib() -> ctypes.CDLL:
         L.mk_last_error.restype = ctypes.c_char_p
         L.mk_plan_query.argtypes = [vp, P(PlanInfo)]
         L.mk_decode_step.argtypes = [vp, P(Weights), P(KVCache), vp, vp, vp, vp]
+        L.mk_decode_step_greedy.argtypes = [vp, P(Weights), P(KVCache), vp, vp, vp, vp]
         L.mk_decode_step_hidden.argtypes = [vp, P(Weights), P(KVCache), vp, vp, vp, vp]
         L.mk_get_device_error.argtypes = [vp, vp]
         L.mk_argmax.argtypes = [vp, vp, vp, vp]
         L.mk_plan_verify.argtypes = [vp]
         L.mk_plan_dry_run.argtypes = [vp, i32, ctypes.c_uint64, i32, i32, vp]
         L.mk_plan_trace.argtypes = [vp, vp, ctypes.c_int64, vp]
-        for f in ("mk_plan_query", "mk_decode_step", "mk_decode_step_hidden", "mk_get_device_error", "mk_argmax",
-                  "mk_plan_verify", "mk_plan_dry_run", "mk_plan_trace"):
+        for f in ("mk_plan_query", "mk_decode_step", "mk_decode_step_greedy", "mk_decode_step_hidden",
+                  "mk_get_device_error", "mk_argmax", "mk_plan_verify", "mk_plan_dry_run", "mk_plan_trace"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -205,6 +206,11 @@ class Plan:
     def step(self, weights: "Weights", kv: "KVCache", tokens, seq_lens, logits, stream=None) -> None:
         _check(lib().mk_decode_step(self._h, ctypes.byref(weights), ctypes.byref(kv), _ptr(tokens), _ptr(seq_lens),
                                     _ptr(logits), _stream(stream)), "mk_decode_step")
+
+    def step_greedy(self, weights: "Weights", kv: "KVCache", tokens, seq_lens, logits, stream=None) -> None:
+        """One step; tokens become the greedy next tokens and seq_lens advance by one, in the same launch."""
+        _check(lib().mk_decode_step_greedy(self._h, ctypes.byref(weights), ctypes.byref(kv), _ptr(tokens),
+                                           _ptr(seq_lens), _ptr(logits), _stream(stream)), "mk_decode_step_greedy")
 
     def step_hidden(self, weights: "Weights", kv: "KVCache", x_in, seq_lens, x_out, stream=None) -> None:
         _check(lib().mk_decode_step_hidden(self._h, ctypes.byref(weights), ctypes.byref(kv), _ptr(x_in),

@@ -199,6 +199,48 @@ def test_mid_paged_equals_contiguous(mid_weights):
         _bitwise(a, b)
 
 
+def _greedy_seq(s, steps, tokens0, **opts):
+    """Decode with the fused greedy entry point; per step (tokens fed, logits, next tokens) and final lengths."""
+    import torch
+
+    plan = plan_for(s, **opts)
+    kv = device_kv(s)
+    tok = torch.from_numpy(tokens0.astype(np.int32)).cuda()
+    d_len = torch.from_numpy(s.lens.astype(np.int32)).cuda()
+    logits = torch.empty((s.B, s.shape.vocab), dtype=torch.float32, device="cuda")
+    out = []
+    for _ in range(steps):
+        fed = tok.cpu().numpy().copy()
+        plan.step_greedy(s.dm.struct, kv.struct, tok, d_len, logits)
+        out.append((fed, logits.cpu().numpy().copy(), tok.cpu().numpy().copy()))
+    torch.cuda.synchronize()
+    assert plan.device_error() == 0
+    plan.close()
+    return out, d_len.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", ["tiny", "mid3", "mid3_per_op", "mid16_jit"])
+def test_greedy_step_equals_step_argmax_increment(tiny, mid_weights, case):
+    # the fused step gives the logits, tokens and lengths of step + argmax + increment
+    if case == "tiny":
+        s, opts, steps = tiny, {}, 6
+    else:
+        B = 16 if case == "mid16_jit" else 3
+        lens = [0, 300, 77] if B == 3 else [int(x) for x in np.linspace(1, 500, B)]
+        s = make_setup(MID, B, lens, 520, weights=mid_weights)
+        opts = {"mode": 1} if case == "mid3_per_op" else ({"jit": 1} if case == "mid16_jit" else {})
+        steps = 3
+    log("greedy step vs step + argmax + increment: %s" % case)
+    t0 = _tokens(s.shape, s.B, 5)
+    a, _ = _logits_seq(s, steps, tokens=t0, **opts)
+    g, lens = _greedy_seq(s, steps, t0, **opts)
+    for (ta, la, na), (tg, lg, ng) in zip(a, g):
+        assert np.array_equal(ta, tg)
+        assert np.array_equal(la.view(np.uint32), lg.view(np.uint32))
+        assert np.array_equal(na, ng)
+    assert np.array_equal(lens, s.lens + steps)
+
+
 def test_device_errors_token_and_overflow(tiny):
     import torch
 
