@@ -31,7 +31,7 @@ struct Lds {
     uint64_t* marks;  // 4 trace phase marks
 };
 
-constexpr int kCmbSplits = 4;  // splits merged per staged chunk
+constexpr int kCmbSplits = 16;  // splits merged per staged chunk (one load round for up to 16)
 constexpr int kPartFloats = 8192;  // GEMV cross-wave partial sums
 constexpr int kLdsHeader = kWaves * 16 + 16 + 16 + 8;
 constexpr int kAttnFloats = 8 * 128 + 2 * 128 + kWaves * 8 * 128 + kWaves * 16 + 16 + kCmbSplits * (8 * 128 + 16) +
@@ -1424,9 +1424,19 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
     }
     for (int c0 = 0; c0 < ns; c0 += kCmbSplits) {
         const int nc = min(kCmbSplits, ns - c0);
-        for (int i = tid; i < nc * q4; i += kThreads) {
-            const uint4 v = buf_load16_co(prs, (uint32_t)((c0 * q4 + i) * 16), 0);
-            *(uint4*)(s.cmb + i * 4) = v;
+        // up to 8 loads of a thread in flight before its LDS stores
+        for (int i0 = tid; i0 < nc * q4; i0 += 8 * kThreads) {
+            uint4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + u * kThreads;
+                v[u] = buf_load16_co(prs, i < nc * q4 ? (uint32_t)((c0 * q4 + i) * 16) : kOOB, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + u * kThreads;
+                if (i < nc * q4) *(uint4*)(s.cmb + i * 4) = v[u];
+            }
         }
         __syncthreads();
 #pragma unroll
