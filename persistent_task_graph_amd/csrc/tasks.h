@@ -1192,17 +1192,25 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
                 bm[hh] = fmaxf(bm[hh], d[it][hh]);
             }
         }
-        float mz[GP];
+        float mz[GP], corr[GP];
+        bool grew = false;  // some head's running max rose (uniform over the wave)
 #pragma unroll
         for (int hh = 0; hh < GP; ++hh) {
             const float mn = fmaxf(mrun[hh], column_max<LPR>(bm[hh]));
             // mn is -inf only while this wave has seen no key: nothing to scale
-            const float corr = mn == -INFINITY ? 1.f : __expf(mrun[hh] - mn);
+            corr[hh] = mn == -INFINITY ? 1.f : __expf(mrun[hh] - mn);
             mz[hh] = mn == -INFINITY ? 0.f : mn;
-            lsum[hh] *= corr;
-#pragma unroll
-            for (int e = 0; e < E; ++e) acc[hh][e] *= corr;
+            grew |= mn != mrun[hh];
             mrun[hh] = mn;
+        }
+        // an unchanged max scales by exactly e^0 = 1: skipping it keeps the bits
+        if (grew) {
+#pragma unroll
+            for (int hh = 0; hh < GP; ++hh) {
+                lsum[hh] *= corr[hh];
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[hh][e] *= corr[hh];
+            }
         }
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
@@ -1273,17 +1281,25 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
                 bm = fmaxf(bm, sc[t][r]);
             }
         bm = column_max<16>(bm);
-        float mz[GP];
+        float mz[GP], corr[GP];
+        bool grew = false;  // some head's running max rose (uniform over the wave)
 #pragma unroll
         for (int hh = 0; hh < GP; ++hh) {
             const float mn = fmaxf(mrun[hh], read_lane(bm, hh));
             // mn is -inf only while this wave has seen no key: nothing to scale
-            const float corr = mn == -INFINITY ? 1.f : __expf(mrun[hh] - mn);
+            corr[hh] = mn == -INFINITY ? 1.f : __expf(mrun[hh] - mn);
             mz[hh] = mn == -INFINITY ? 0.f : mn;
-            lsum[hh] *= corr;
-#pragma unroll
-            for (int e = 0; e < E; ++e) acc[hh][e] *= corr;
+            grew |= mn != mrun[hh];
             mrun[hh] = mn;
+        }
+        // an unchanged max scales by exactly e^0 = 1: skipping it keeps the bits
+        if (grew) {
+#pragma unroll
+            for (int hh = 0; hh < GP; ++hh) {
+                lsum[hh] *= corr[hh];
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[hh][e] *= corr[hh];
+            }
         }
         mlane = fmaxf(mlane, bm);
         const float mzl = mlane == -INFINITY ? 0.f : mlane;
