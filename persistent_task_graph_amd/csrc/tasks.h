@@ -1254,7 +1254,8 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
         mk_f32x4 sc[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            sc[t] = mk_f32x4{0.f, 0.f, 0.f, 0.f};
+            // the hi and lo query terms accumulate in two independent chains
+            mk_f32x4 sh = mk_f32x4{0.f, 0.f, 0.f, 0.f}, sl = sh;
             const int j = base + wave * WR + 16 * t + li;
             const bool nw = j < n && j0 + j == pos;  // the new row's k comes from LDS
 #pragma unroll
@@ -1266,9 +1267,10 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
                     for (int e = 0; e < 8; ++e) kb[e] = (__bf16)s.kn[32 * q + 8 * lg + e];
                     a = __builtin_bit_cast(uint4, kb);
                 }
-                sc[t] = mfma_bf16(a, qh[q], sc[t]);
-                sc[t] = mfma_bf16(a, ql[q], sc[t]);
+                sh = mfma_bf16(a, qh[q], sh);
+                sl = mfma_bf16(a, ql[q], sl);
             }
+            sc[t] = sh + sl;
         }
         // scale, mask rows past the split, batch max of head li
         float bm = -INFINITY;
