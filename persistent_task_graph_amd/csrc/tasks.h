@@ -711,7 +711,7 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
             auto out = [&](int r, int b, float v, float) { st_co(&o[(int64_t)b * ld + r], v * s.rstd[b]); };
             if constexpr (kMfma) {
                 const MSeg sg[3] = {{tq.r, tq.r, tq.n, tq.lo}, {tk.r, tk.r, tk.n, QD + tk.lo}, {tv.r, tv.r, tv.n, QD + KD + tv.lo}};
-                gemv_mfma<NB, false, 4>(sg, H, x, H, B, (const bf16_t*)w.attn_norm, p.eps, out, s, p.trace != nullptr);
+                gemv_mfma<NB, false, 2>(sg, H, x, H, B, (const bf16_t*)w.attn_norm, p.eps, out, s, p.trace != nullptr);
             } else {
                 gemv_dispatch<WT, NB, false>(r0, r1, H, x, H, B, (const WT*)w.attn_norm, p.eps, rowp, out, s, p.trace != nullptr);
             }
@@ -731,7 +731,7 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
             };
             if constexpr (kMfma) {
                 const MSeg sg[1] = {{to.r, to.r, to.n, to.lo}};
-                gemv_mfma<NB, false, 2, 1, decltype(out), 3>(sg, K, a, K, B, (const bf16_t*)nullptr, p.eps, out, s, p.trace != nullptr);
+                gemv_mfma<NB, false, 1, 1, decltype(out), 3>(sg, K, a, K, B, (const bf16_t*)nullptr, p.eps, out, s, p.trace != nullptr);
             } else {
                 gemv_dispatch<WT, NB, false>(r0, r1, K, a, K, B, (const WT*)nullptr, p.eps, rowp, out, s, p.trace != nullptr);
             }
@@ -755,7 +755,7 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
             };
             if constexpr (kMfma) {
                 const MSeg sg[1] = {{tg.r, tu.r, tg.n, tg.lo}};
-                gemv_mfma<NB, true, 4>(sg, H, x, H, B, (const bf16_t*)w.mlp_norm, p.eps, out, s, p.trace != nullptr);
+                gemv_mfma<NB, true, 3>(sg, H, x, H, B, (const bf16_t*)w.mlp_norm, p.eps, out, s, p.trace != nullptr);
             } else {
                 gemv_dispatch<WT, NB, true>(r0, r1, H, x, H, B, (const WT*)w.mlp_norm, p.eps, rowp, out, s, p.trace != nullptr);
             }
@@ -775,7 +775,7 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
             };
             if constexpr (kMfma) {
                 const MSeg sg[1] = {{td.r, td.r, td.n, td.lo}};
-                gemv_mfma<NB, false, 2, 1, decltype(out), 3>(sg, F, h, F, B, (const bf16_t*)nullptr, p.eps, out, s, p.trace != nullptr);
+                gemv_mfma<NB, false, 1, 1, decltype(out), 3>(sg, F, h, F, B, (const bf16_t*)nullptr, p.eps, out, s, p.trace != nullptr);
             } else {
                 gemv_dispatch<WT, NB, false>(r0, r1, F, h, F, B, (const WT*)nullptr, p.eps, rowp, out, s, p.trace != nullptr);
             }
