@@ -649,7 +649,7 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, int i) {
 // last turns the keys into the next tokens and advances the lengths (every
 // attention task of the step, the only other reader of the lengths, has
 // finished before the LM head starts). Same choice as k_argmax.
-__device__ __forceinline__ void lm_greedy(const KParams& p, int r0, int r1, const Lds& s) {
+__device__ __forceinline__ void lm_greedy(const KParams& p, int r0, int r1) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     wait_stores();
     __syncthreads();
@@ -794,7 +794,7 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
             } else {
                 gemv_dispatch<WT, NB, false>(r0, r1, H, x, H, B, (const WT*)p.final_norm, p.eps, rowp, out, s, p.trace != nullptr);
             }
-            if (p.greedy_tokens) lm_greedy(p, r0, r1, s);
+            if (p.greedy_tokens) lm_greedy(p, r0, r1);
             break;
         }
         default: break;
