@@ -1,5 +1,5 @@
 """Host-side tests of the C ABI (no GPU): the library loads and exports every
-symbol of include/mk.h; task graphs for every workload verify; the host
+symbol of include/mk.h, and the binding raises when it is missing; task graphs for every workload verify; the host
 dry run of the persistent protocol matches a sequential evaluation under
 random delays and thread counts; fault injection times out instead of
 hanging; invalid descriptions are rejected with a message."""
@@ -30,6 +30,14 @@ def test_exports_every_declared_symbol(lib):
     assert set(mk.EXPORTS) == declared
     for name in declared:
         assert hasattr(lib, name), name
+
+
+def test_missing_library_raises(monkeypatch, tmp_path):
+    # no CPU fallback: without the built library the binding refuses to run
+    monkeypatch.setattr(mk, "LIB_PATH", str(tmp_path / "libmk.so"))
+    monkeypatch.setattr(mk, "_lib", None)
+    with pytest.raises(mk.MKError, match="not built"):
+        mk.lib()
 
 
 def _plan(shape, batch, cap, **kw):
