@@ -1,8 +1,9 @@
 """Host-side tests of the C ABI (no GPU): the library loads and exports every
-symbol of include/mk.h, and the binding raises when it is missing; task graphs for every workload verify; the host
-dry run of the persistent protocol matches a sequential evaluation under
-random delays and thread counts; fault injection times out instead of
-hanging; invalid descriptions are rejected with a message."""
+symbol of include/mk.h, and the binding raises when it is missing; task
+graphs for every workload verify; the host dry run of the persistent
+protocol matches a sequential evaluation under random delays and thread
+counts; fault injection times out instead of hanging; invalid descriptions
+are rejected with a message."""
 import ctypes
 import os
 import re
