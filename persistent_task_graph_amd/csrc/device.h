@@ -20,6 +20,17 @@ struct LayerPtrs {
 };
 static_assert(sizeof(LayerPtrs) == sizeof(mk_layer_weights), "LayerPtrs layout");
 
+// Each event counter is kept as up to kEvPlanesMax partial counts, one
+// 128-byte aligned plane each; its value is the sum of the planes (mod 2^32).
+// A kernel instance for batch NB uses ev_planes(NB) of them: GEMV producers
+// spread their arrivals over those planes, so that the 256 arrivals of one
+// event do not all queue on one address, and a waiter sums them. At batch
+// 8 and 16 that is faster; at smaller batches the waiters' extra polling
+// loads cost more than it saves, and one plane is used.
+constexpr int kEvPlanesMax = 8;
+__host__ __device__ constexpr int ev_planes(int nb) { return nb >= 8 ? kEvPlanesMax : 1; }
+__host__ __device__ constexpr int ev_plane_stride(int n_events) { return (n_events + 31) / 32 * 32; }
+
 // Everything a task body needs; passed by value to every kernel.
 struct KParams {
     // task graph
@@ -27,7 +38,8 @@ struct KParams {
     const int32_t* qoff;
     const int32_t* queue;
     const EventRec* evrec;
-    uint32_t* ev;
+    uint32_t* ev;      // [kEvPlanesMax][ev_stride] partial counts
+    int ev_stride;
     uint32_t* arrive;  // [B * Hkv] last-arrival counters (self-resetting)
     RingSlot* inbox;         // [workers][inbox_mask + 1] JIT tasks dealt to each worker
     int64_t* inbox_tail;     // [workers] producer positions

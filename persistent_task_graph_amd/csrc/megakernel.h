@@ -138,6 +138,7 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s, uint
     const int w = blockIdx.x;
     const int qb = p.qoff[w], qe = p.qoff[w + 1];
     const uint32_t ep1 = p.epoch + 1u;
+    constexpr int NP = ev_planes(NB);  // event-count planes this instance uses
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     if (p.trace && threadIdx.x == 0) {
         p.trace_n[w] = 0;
@@ -198,7 +199,9 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s, uint
             if (waiting) {
                 if (threadIdx.x == 0) {
                     int c = 2;
-                    const uint32_t v = ld_relaxed(&p.ev[t.wait_ev]);
+                    uint32_t v = 0;
+#pragma unroll
+                    for (int j = 0; j < NP; ++j) v += ld_relaxed(&p.ev[j * p.ev_stride + t.wait_ev]);
                     if ((int32_t)(v - target) >= 0) c = 0;
                     else if (aborted(p.ctrl)) c = 3;
                     else {
@@ -259,7 +262,7 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s, uint
             } else {
                 run_gemv_task<WT, NB>(p, t, s);
             }
-            signal_event(p, t.sig_ev, s);
+            signal_event(p, t.sig_ev, s, (int)blockIdx.x & (NP - 1));
         }
         if constexpr (!kStream) {
             if (qi + 1 < qe) {

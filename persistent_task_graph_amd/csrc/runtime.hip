@@ -200,7 +200,7 @@ bool upload_plan(mk_plan* pl) {
     Region r_lvl = take(sizeof(int32_t) * std::max<size_t>(1, hp.level_tasks.size()));
     Region r_evrec = take(sizeof(EventRec) * hp.events.size());
     // zero-initialised control area: events, arrivals, rings, ctrl
-    Region r_ev = take(sizeof(uint32_t) * hp.events.size());
+    Region r_ev = take(sizeof(uint32_t) * (size_t)ev_plane_stride((int)hp.events.size()) * kEvPlanesMax);
     Region r_arr = take(sizeof(uint32_t) * (size_t)B * Hkv);
     Region r_amax = take(sizeof(unsigned long long) * (size_t)B);
     Region r_lmd = take(sizeof(uint32_t));
@@ -317,6 +317,7 @@ KParams make_params(const mk_plan* pl, const mk_weights* w, const mk_kv_cache* k
     p.queue = pl->d_queue;
     p.evrec = pl->d_evrec;
     p.ev = pl->d_ev;
+    p.ev_stride = ev_plane_stride((int)hp.events.size());
     p.arrive = pl->d_arrive;
     p.amax = pl->d_amax;
     p.lm_done = pl->d_lm_done;

@@ -805,10 +805,11 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
 // ---------------------------------------------------------------- signalling
 
 // Make this workgroup's writes visible device-wide, then count one
-// arrival on event e (MPK article §2.1: trigger_count / required_count).
+// arrival on event e (MPK article §2.1: trigger_count / required_count), in
+// partial-count plane `plane` (below the waiters' plane count).
 // The arrival that completes a JIT-triggering event posts a message to the
 // scheduler mailbox (§2.2: the data-dependent successor is launched JIT).
-__device__ __forceinline__ void signal_event(const KParams& p, int e, const Lds& s) {
+__device__ __forceinline__ void signal_event(const KParams& p, int e, const Lds& s, int plane = 0) {
     wait_stores();  // this thread's agent-coherent stores have completed
     trace_mark(p, s.marks, 3);
     __syncthreads();
@@ -816,9 +817,10 @@ __device__ __forceinline__ void signal_event(const KParams& p, int e, const Lds&
         const EventRec er = p.evrec[e];
         if (er.jit_layer < 0) {
             // no one acts on the count here: the add needs no return trip
-            __hip_atomic_fetch_add(&p.ev[e], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(&p.ev[plane * p.ev_stride + e], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             return;
         }
+        // the completing arrival must see the whole count: plane 0 only
         const uint32_t old = __hip_atomic_fetch_add(&p.ev[e], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (old + 1u == er.required * (p.epoch + 1u)) {
             // the completing arrival posts "expand attention of this layer"
