@@ -22,9 +22,10 @@ static_assert(sizeof(LayerPtrs) == sizeof(mk_layer_weights), "LayerPtrs layout")
 
 // Each event counter is kept as up to kEvPlanesMax partial counts, one
 // 128-byte aligned plane each; its value is the sum of the planes (mod 2^32).
-// A kernel instance for batch NB uses ev_planes(NB) of them: GEMV producers
-// spread their arrivals over those planes, so that the 256 arrivals of one
-// event do not all queue on one address, and a waiter sums them. At batch
+// A kernel instance for batch NB uses ev_planes(NB) of them: GEMV and
+// attention producers spread their arrivals over those planes, so that the
+// arrivals of one event do not all queue on one address, and a waiter sums
+// them. At batch
 // 8 and 16 that is faster; at smaller batches the waiters' extra polling
 // loads cost more than it saves, and one plane is used.
 constexpr int kEvPlanesMax = 8;

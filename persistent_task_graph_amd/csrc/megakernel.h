@@ -250,7 +250,7 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s, uint
             }
             const uint64_t tj = p.trace ? now_ticks() : 0;
             if (chunk == 0) chunk = attn_chunk(p);
-            attention_task<WT>(p, jl, jbg, js, chunk, s);
+            attention_task<WT>(p, jl, jbg, js, chunk, s, (int)blockIdx.x & (NP - 1));
             if (cmd == 0) break;  // that was this AOT attention task
             trace_put(p, s, 1, (jl << 24) | ((jbg & 0xFFF) << 12) | (js & 0xFFF), OP_ATTN, tj, tj);
             t0 = now_ticks();

@@ -991,7 +991,8 @@ __host__ __device__ constexpr int attn_rec(int G, int D) { return G * D + 16; }
 __host__ __device__ constexpr int attn_gp(int G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8; }
 
 template <typename WT, int D, int GP>
-__device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, int split, int C, const Lds& s) {
+__device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, int split, int C, const Lds& s,
+                                               int ev_plane) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int Hkv = p.Hkv, G = p.Hq / p.Hkv;
     const int b = bg / Hkv, g = bg % Hkv;
@@ -1037,7 +1038,7 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
     if (overflow) {
         for (int i = tid; i < G * D; i += kThreads) st_co(&out[i], 0.f);
         if (tid == 0) raise_error(p.ctrl, MK_ERR_KV_OVERFLOW);
-        if (p.persistent) signal_event(p, ev_attn(l), s);
+        if (p.persistent) signal_event(p, ev_attn(l), s, ev_plane);
         return;
     }
     const int j0 = split * C, j1 = min(j0 + C, keys);
@@ -1414,7 +1415,7 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
         else st_co(&part[i], a);
     }
     if (ns == 1) {
-        if (p.persistent) signal_event(p, ev_attn(l), s);
+        if (p.persistent) signal_event(p, ev_attn(l), s, ev_plane);
         return;
     }
 
@@ -1482,23 +1483,26 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
         if (i < G * D) st_co(&out[i], num[k] / den[k]);
     }
     if (tid == 0) __hip_atomic_store(&p.arrive[bg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (p.persistent) signal_event(p, ev_attn(l), s);
+    if (p.persistent) signal_event(p, ev_attn(l), s, ev_plane);
 }
 
 template <typename WT, int D>
-__device__ __forceinline__ void attention_task_d(const KParams& p, int l, int bg, int split, int C, const Lds& s) {
+__device__ __forceinline__ void attention_task_d(const KParams& p, int l, int bg, int split, int C, const Lds& s,
+                                                 int ev_plane) {
     switch (attn_gp(p.Hq / p.Hkv)) {
-        case 1: attention_body<WT, D, 1>(p, l, bg, split, C, s); break;
-        case 2: attention_body<WT, D, 2>(p, l, bg, split, C, s); break;
-        case 4: attention_body<WT, D, 4>(p, l, bg, split, C, s); break;
-        default: attention_body<WT, D, 8>(p, l, bg, split, C, s); break;
+        case 1: attention_body<WT, D, 1>(p, l, bg, split, C, s, ev_plane); break;
+        case 2: attention_body<WT, D, 2>(p, l, bg, split, C, s, ev_plane); break;
+        case 4: attention_body<WT, D, 4>(p, l, bg, split, C, s, ev_plane); break;
+        default: attention_body<WT, D, 8>(p, l, bg, split, C, s, ev_plane); break;
     }
 }
-// C: the step's chunk, attn_chunk(p)
+// C: the step's chunk, attn_chunk(p); ev_plane: the attention-done count
+// plane this workgroup adds to
 template <typename WT>
-__device__ __forceinline__ void attention_task(const KParams& p, int l, int bg, int split, int C, const Lds& s) {
-    if (p.D == 128) attention_task_d<WT, 128>(p, l, bg, split, C, s);
-    else attention_task_d<WT, 64>(p, l, bg, split, C, s);
+__device__ __forceinline__ void attention_task(const KParams& p, int l, int bg, int split, int C, const Lds& s,
+                                               int ev_plane = 0) {
+    if (p.D == 128) attention_task_d<WT, 128>(p, l, bg, split, C, s, ev_plane);
+    else attention_task_d<WT, 64>(p, l, bg, split, C, s, ev_plane);
 }
 
 }  // namespace mk
