@@ -53,7 +53,9 @@ enum mk_status {
 enum mk_device_error {
     MK_ERR_TOKEN = 1,       /* a token id outside [0, vocab): that row used token 0 */
     MK_ERR_KV_OVERFLOW = 2, /* seq_lens[b] + 1 exceeds the KV capacity: that row's attention output is zero */
-    MK_ERR_TIMEOUT = 4      /* a bounded wait in the persistent kernel expired; all workgroups exited */
+    MK_ERR_TIMEOUT = 4,     /* a bounded wait in the persistent kernel expired; all workgroups exited */
+    MK_ERR_BLOCK_TABLE = 8  /* a paged block-table entry outside the pool (see mk_kv_cache): those
+                               positions read as zeros and the new row is not stored */
 };
 
 /*
@@ -127,9 +129,11 @@ typedef struct mk_exec_opts {
  *  weight_dtype, kv_dtype: MK_BF16 or MK_F32 (bf16 weights need a bf16 cache
  *  and f32 weights an f32 cache).
  *  max_seq_len: KV capacity per sequence in positions. Contiguous layout:
- *  the cache holds [layer][batch][kv_head][max_seq_len][head_dim]. Paged
- *  layout: positions are reached through a block table (see mk_kv_cache)
- *  and max_seq_len bounds seq_lens[b] + 1.
+ *  the cache holds [layer][batch][kv_head][max_seq_len][head_dim], and one
+ *  sequence's span max_seq_len * head_dim * element size must be below
+ *  2 GiB (attention addresses it with 32-bit byte offsets). Paged layout:
+ *  positions are reached through a block table (see mk_kv_cache) and
+ *  max_seq_len bounds seq_lens[b] + 1.
  *  hidden_io: 1 = no embedding and no LM head; steps read and write hidden
  *  states (mk_decode_step_hidden).
  */
@@ -171,10 +175,18 @@ typedef struct mk_weights {
  * KV cache (device memory, caller-owned, elements of kv_dtype).
  *  layer_stride: elements from one layer's cache to the next.
  *  Contiguous: element (l, b, h, p, d) at
- *    l*layer_stride + ((b*n_kv_heads + h)*max_seq_len + p)*head_dim + d.
- *  Paged: block_table is device int32 [batch, max_blocks_per_seq]; position
- *  p of sequence b lives in physical block blk = block_table[b][p / kv_block]
- *  at l*layer_stride + ((blk*n_kv_heads + h)*kv_block + p % kv_block)*head_dim + d.
+ *    l*layer_stride + ((b*n_kv_heads + h)*max_seq_len + p)*head_dim + d;
+ *    layer_stride >= batch*n_kv_heads*max_seq_len*head_dim.
+ *  Paged (the MPK article's paged memory, §3.1, applied to the cache):
+ *    block_table is device int32 [batch, max_blocks_per_seq]; position p of
+ *    sequence b lives in physical block blk = block_table[b][p / kv_block]
+ *    at l*layer_stride + ((blk*n_kv_heads + h)*kv_block + p % kv_block)*head_dim + d.
+ *    layer_stride is a multiple of n_kv_heads*kv_block*head_dim, so a layer
+ *    holds layer_stride / (n_kv_heads*kv_block*head_dim) blocks (the pool),
+ *    and layer_stride * element size must be below 2 GiB (32-bit offsets);
+ *    the steps reject other strides with MK_ERR_ARG. Entries outside
+ *    [0, pool) are caught on the device: MK_ERR_BLOCK_TABLE, nothing is
+ *    read from or written to such a block.
  */
 typedef struct mk_kv_cache {
     void* k;
@@ -194,24 +206,49 @@ typedef struct mk_plan_info {
 } mk_plan_info;
 
 /*
- * Build the task graph for `desc` (MPK article §2.1: the graph becomes one
- * kernel; §2.2: classify_task; §5.1: workers = CUs - 4, 16 scheduler
- * waves) and upload its tables. Returns NULL on error (see mk_last_error).
- * The plan owns its tables, activations, partials, rings and error word.
+ * Build the task graph for `desc` and upload its tables. Defining passages:
+ * the MPK article (devpress.csdn.net) §2.1 "Mega-Kernel执行模型" (each
+ * operator becomes tile tasks linked by events, and the whole graph one
+ * kernel), §2.2 "混合任务启动机制" (classify_task: JIT for data-dependent
+ * operators, AOT otherwise), §4.2 (one pre-built graph per batch size) and
+ * §5.1 "参数配置建议" (workers = CUs - 4, 16 scheduler warps).
+ * Returns NULL on error (see mk_last_error). The plan owns its tables,
+ * activations, partials, rings and error word (device memory allocated
+ * here, once).
  */
 mk_plan* mk_build_graph(const mk_model_desc* desc);
 
-/* Free a plan and its device memory (waits for the device). NULL is a no-op. */
+/*
+ * Free a plan and its device memory. Waits for the device first. NULL is a
+ * no-op. The pages define no teardown; the plan's memory is released here
+ * because mk_build_graph allocated it.
+ */
 void mk_destroy_plan(mk_plan* plan);
 
-/* Message for the last error on the calling thread ("" if none). */
+/*
+ * Message for the last error on the calling thread ("" if none). The pages
+ * define no error reporting; errors stay inside the C ABI as status codes
+ * and this thread-local text.
+ */
 const char* mk_last_error(void);
 
-/* Fill `info` (host). */
+/*
+ * Fill `info` (host memory) with the plan's task counts per operator, its
+ * event and level counts and its bytes per step: the quantities of the MPK
+ * article's task graph (§2.1 TaskDesc / Event) and of the decode step's
+ * memory-bound cost (Ada-MK summary, gist.science, "Methodik" 2: decode is
+ * IO-bound). Returns MK_OK or MK_ERR_ARG.
+ */
 int mk_plan_query(const mk_plan* plan, mk_plan_info* info);
 
 /*
- * Enqueue one decode step on `stream`.
+ * Enqueue one decode step on `stream`: embedding, every decoder layer
+ * (RMSNorm, QKV, QK-norm, RoPE, KV append, attention, O, SwiGLU MLP) and
+ * the final norm and LM head, as one persistent launch (the MPK article,
+ * §2.1 "Mega-Kernel执行模型"; the layer as Attention then MLP, §1), or, with
+ * opts.mode = MK_KERNEL_PER_OP, as one launch per task-graph level (§1, the
+ * execution model the article replaces, kept as the one-switch fallback of
+ * the pgsm.cn essay, §5.3 "回滚预案").
  *  tokens   device int32 [batch]: the new token of each sequence.
  *  seq_lens device int32 [batch]: positions already cached. The step writes
  *           K/V at index seq_lens[b] and attends over seq_lens[b] + 1 keys.
@@ -229,15 +266,21 @@ int mk_decode_step(mk_plan* plan, const mk_weights* weights, const mk_kv_cache* 
  * and then, in the same launch, tokens[b] is overwritten with the argmax of
  * logits[b] (lowest index on ties, NaN never chosen, as mk_argmax) and
  * seq_lens[b] is incremented, ready for the next step. The argmax is folded
- * into the LM-head tasks; the last of them writes tokens and seq_lens after
- * every reader of the step's lengths has finished. Not for hidden_io plans.
+ * into the LM-head tasks; tokens and seq_lens are written once every reader
+ * of the step's lengths has finished (persistent mode: the last worker to
+ * leave its queue; kernel-per-op: the last LM-head task). Not for hidden_io
+ * plans. Defining passage: the MPK article §2.1 (the next token is produced
+ * inside the single launch, so the host only re-launches), §1 (per-launch
+ * cost of 5-20 us).
  */
 int mk_decode_step_greedy(mk_plan* plan, const mk_weights* weights, const mk_kv_cache* kv, int32_t* tokens,
                           int32_t* seq_lens, float* logits, void* stream);
 
 /*
  * Hidden-state variant for hidden_io plans: x_in, x_out are device float
- * [batch, hidden] (they may not alias); otherwise as mk_decode_step.
+ * [batch, hidden] (they may not alias); otherwise as mk_decode_step. It runs
+ * the decoder layers only (the Ada-MK summary, gist.science, "Methodik" 1:
+ * the Transformer decoder, with the LM head as a separate part).
  */
 int mk_decode_step_hidden(mk_plan* plan, const mk_weights* weights, const mk_kv_cache* kv, const float* x_in,
                           const int32_t* seq_lens, float* x_out, void* stream);
@@ -245,18 +288,27 @@ int mk_decode_step_hidden(mk_plan* plan, const mk_weights* weights, const mk_kv_
 /*
  * Synchronise `stream`, return the sticky device error bits (0 if none) and
  * clear them. After MK_ERR_TIMEOUT the plan's event counters are reset so
- * the next step starts clean. Negative on a HIP failure.
+ * the next step starts clean. Negative on a HIP failure. The pages define no
+ * device error path; a single persistent launch cannot return one, so the
+ * kernel sets bits in a word the plan owns and this call reads them (the
+ * checks behind them are the caller-data checks of the pgsm.cn essay's
+ * production list, §5.3, done on the device).
  */
 int mk_get_device_error(mk_plan* plan, void* stream);
 
 /*
  * Greedy next token: out_tokens[b] = argmax_v logits[b, v] (lowest index on
- * ties). logits device float [batch, vocab]; out_tokens device int32 [batch].
+ * ties, NaN never chosen). logits device float [batch, vocab]; out_tokens
+ * device int32 [batch]. Its own launch, using the plan's scratch. Defining
+ * passage: greedy decoding of the next token after the LM head (the Ada-MK
+ * summary, gist.science, "Methodik" 1 and "Experimentelle Ergebnisse": the
+ * decode phase generates one token per step).
  */
 int mk_argmax(const mk_plan* plan, const float* logits, int32_t* out_tokens, void* stream);
 
 /*
- * Host-side checks of a plan's task graph: every output row covered
+ * Host-side checks of a plan's task graph (the MPK article §2.1: tasks,
+ * events with required counts): every output row covered
  * exactly once per op, events' required counts equal their producer
  * counts, every queue sorted by level, no task waits on an event of its
  * own or a later level. Returns MK_OK or MK_ERR_STATE with a message.
@@ -264,7 +316,8 @@ int mk_argmax(const mk_plan* plan, const float* logits, int32_t* out_tokens, voi
 int mk_plan_verify(const mk_plan* plan);
 
 /*
- * Host dry run of the persistent schedule: `n_threads` host threads play
+ * Host dry run of the persistent schedule (the MPK article §2.1-2.2: AOT
+ * queues, event waits, JIT dispatch): `n_threads` host threads play
  * the workers (AOT queues, event waits, JIT ring drained while waiting)
  * with random delays from `seed`, each task computing an integer checksum
  * of its inputs. Compares against a sequential topological evaluation.
@@ -297,7 +350,8 @@ typedef struct mk_trace_rec {
 
 /*
  * Copy the trace of the last persistent step to host memory `out` (room
- * for `max_records`). Synchronises `stream`. Returns the number of records
+ * for `max_records`; the pages' timing breakdown of task phases, MPK §3.2,
+ * measured per task here). Synchronises `stream`. Returns the number of records
  * written (records of workers that overflowed their share are dropped), or
  * a negative mk_status (MK_ERR_STATE if the plan was built without trace).
  */

@@ -69,6 +69,7 @@ struct KParams {
     void* kv_v;
     int64_t kv_layer_stride;
     const int32_t* block_table;
+    int n_pool_blocks;  // paged: physical blocks per layer (layer_stride / (Hkv * kv_block * D))
     // step inputs
     const int32_t* tokens;
     const int32_t* seq_lens;
@@ -89,7 +90,8 @@ struct KParams {
     int32_t* greedy_tokens;   // greedy step: next token of each sequence written here (else null)
     int32_t* greedy_lens;     // greedy step: each sequence's length advanced here
     unsigned long long* amax; // [B] packed (value, index) argmax keys; zero between steps
-    uint32_t* lm_done;        // LM-head tasks finished in this step (reset by the last)
+    uint32_t* lm_done;        // kernel-per-op greedy step: LM-head tasks finished (reset by the last)
+    uint32_t* exit_cnt;       // persistent greedy step: workers that left their queue (reset by the last)
     int n_lm_tasks;
     // optional task trace: per worker `trace_cap` records, count in trace_n
     mk_trace_rec* trace;

@@ -274,6 +274,19 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s, uint
     }
     if (threadIdx.x == 0 && p.jit_on) p.inbox_head[w] = head;
     if constexpr (kStream) wait_vm<0>();
+    if (p.greedy_tokens) {
+        // greedy step: the last worker to leave its queue writes the next
+        // tokens and advances the lengths; no worker reads them after this
+        wait_stores();
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const uint32_t old = __hip_atomic_fetch_add(p.exit_cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (old + 1u == (uint32_t)p.n_workers) {
+                greedy_finish(p);
+                __hip_atomic_store(p.exit_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
 }
 
 extern __shared__ __attribute__((aligned(16))) float mk_dyn_lds[];

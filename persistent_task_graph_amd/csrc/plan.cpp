@@ -67,6 +67,10 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
             return fail(err, "hidden, ffn and n_heads*head_dim must be <= " + std::to_string(kmax));
     }
     if (d.max_seq_len < 1 || d.max_seq_len > (1 << 22)) return fail(err, "max_seq_len must be in [1, 4M]");
+    if (d.kv_layout == MK_KV_CONTIGUOUS &&
+        (int64_t)d.max_seq_len * d.head_dim * (d.kv_dtype == MK_BF16 ? 2 : 4) >= ((int64_t)1 << 31))
+        return fail(err, "contiguous KV: one sequence's span (max_seq_len * head_dim * element size) must be "
+                         "smaller than 2 GiB (32-bit buffer offsets)");
     if (!(d.rms_eps >= 0.f) || !(d.rope_base > 1.f)) return fail(err, "rms_eps must be >= 0 and rope_base > 1");
     if (d.kv_layout != MK_KV_CONTIGUOUS && d.kv_layout != MK_KV_PAGED) return fail(err, "bad kv_layout");
     if (d.kv_layout == MK_KV_PAGED) {

@@ -105,7 +105,8 @@ struct mk_plan {
     uint32_t* d_ev = nullptr;
     uint32_t* d_arrive = nullptr;
     unsigned long long* d_amax = nullptr;  // greedy step: per-sequence argmax keys
-    uint32_t* d_lm_done = nullptr;         // greedy step: LM tasks finished
+    uint32_t* d_lm_done = nullptr;         // greedy step: LM tasks finished (kernel-per-op)
+    uint32_t* d_exit_cnt = nullptr;        // greedy step: workers done (persistent)
     RingSlot* d_inbox = nullptr;
     int64_t* d_inbox_tail = nullptr;
     int64_t* d_inbox_head = nullptr;
@@ -204,6 +205,7 @@ bool upload_plan(mk_plan* pl) {
     Region r_arr = take(sizeof(uint32_t) * (size_t)B * Hkv);
     Region r_amax = take(sizeof(unsigned long long) * (size_t)B);
     Region r_lmd = take(sizeof(uint32_t));
+    Region r_exit = take(sizeof(uint32_t));
     Region r_inbox = take(sizeof(RingSlot) * (size_t)hp.workers * hp.inbox_cap);
     Region r_itail = take(sizeof(int64_t) * (size_t)hp.workers);
     Region r_ihead = take(sizeof(int64_t) * (size_t)hp.workers);
@@ -237,6 +239,7 @@ bool upload_plan(mk_plan* pl) {
     pl->d_arrive = (uint32_t*)(m + r_arr.off);
     pl->d_amax = (unsigned long long*)(m + r_amax.off);
     pl->d_lm_done = (uint32_t*)(m + r_lmd.off);
+    pl->d_exit_cnt = (uint32_t*)(m + r_exit.off);
     pl->d_inbox = (RingSlot*)(m + r_inbox.off);
     pl->d_inbox_tail = (int64_t*)(m + r_itail.off);
     pl->d_inbox_head = (int64_t*)(m + r_ihead.off);
@@ -321,6 +324,7 @@ KParams make_params(const mk_plan* pl, const mk_weights* w, const mk_kv_cache* k
     p.arrive = pl->d_arrive;
     p.amax = pl->d_amax;
     p.lm_done = pl->d_lm_done;
+    p.exit_cnt = pl->d_exit_cnt;
     p.n_lm_tasks = hp.tasks_per_op[OP_LM];
     p.inbox = pl->d_inbox;
     p.inbox_tail = pl->d_inbox_tail;
@@ -357,6 +361,9 @@ KParams make_params(const mk_plan* pl, const mk_weights* w, const mk_kv_cache* k
     p.kv_v = kv->v;
     p.kv_layer_stride = kv->layer_stride;
     p.block_table = kv->block_table;
+    p.n_pool_blocks = d.kv_layout == MK_KV_PAGED
+                          ? (int)(kv->layer_stride / ((int64_t)d.n_kv_heads * d.kv_block * d.head_dim))
+                          : 0;
     p.tokens = tokens;
     p.seq_lens = seq_lens;
     p.B = d.batch;
@@ -396,15 +403,33 @@ KParams make_params(const mk_plan* pl, const mk_weights* w, const mk_kv_cache* k
     return p;
 }
 
+// Arguments are checked before the plan's state, so that a host-only plan
+// reports a bad argument the same way a device plan does.
 int check_step_args(mk_plan* pl, const mk_weights* w, const mk_kv_cache* kv, const int32_t* seq_lens, const void* in,
                     const void* out) {
     if (!pl) return set_err("null plan"), MK_ERR_ARG;
-    if (pl->host_only) return set_err("host-only plan cannot run steps"), MK_ERR_STATE;
     const mk_model_desc& d = pl->hp.desc;
     if (!w || !kv || !seq_lens || !in || !out) return set_err("null argument"), MK_ERR_ARG;
     if (w->n_layers != d.n_layers || !w->layers) return set_err("weights.n_layers does not match the plan"), MK_ERR_ARG;
     if (!kv->k || !kv->v) return set_err("null KV cache pointer"), MK_ERR_ARG;
     if (d.kv_layout == MK_KV_PAGED && !kv->block_table) return set_err("paged plan needs a block table"), MK_ERR_ARG;
+    {
+        // attention reads K/V through buffer resources with 32-bit byte
+        // offsets: a contiguous sequence span (checked at build) or a paged
+        // layer must stay below 2^31 bytes
+        const int64_t es = d.kv_dtype == MK_BF16 ? 2 : 4;
+        const int64_t blk = (int64_t)d.n_kv_heads * d.kv_block * d.head_dim;
+        if (d.kv_layout == MK_KV_PAGED) {
+            if (kv->layer_stride < blk || kv->layer_stride % blk)
+                return set_err("paged KV: layer_stride must be a positive multiple of n_kv_heads * kv_block * head_dim"),
+                       MK_ERR_ARG;
+            if (kv->layer_stride * es >= ((int64_t)1 << 31))
+                return set_err("paged KV: one layer's pool must be smaller than 2 GiB (32-bit buffer offsets)"), MK_ERR_ARG;
+        } else if (kv->layer_stride < (int64_t)d.batch * d.n_kv_heads * d.max_seq_len * d.head_dim) {
+            return set_err("contiguous KV: layer_stride is smaller than batch * n_kv_heads * max_seq_len * head_dim"),
+                   MK_ERR_ARG;
+        }
+    }
     if (!d.hidden_io && (!w->embed || !w->lm_head || !w->final_norm))
         return set_err("embed, lm_head and final_norm are required"), MK_ERR_ARG;
     for (int l = 0; l < d.n_layers; ++l) {
@@ -413,6 +438,7 @@ int check_step_args(mk_plan* pl, const mk_weights* w, const mk_kv_cache* kv, con
             return set_err("null weight pointer in layer " + std::to_string(l)), MK_ERR_ARG;
         if (d.qk_norm && (!lw.q_norm || !lw.k_norm)) return set_err("qk_norm needs q_norm and k_norm"), MK_ERR_ARG;
     }
+    if (pl->host_only) return set_err("host-only plan cannot run steps"), MK_ERR_STATE;
     return MK_OK;
 }
 

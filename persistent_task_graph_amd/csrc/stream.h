@@ -361,6 +361,7 @@ __device__ __forceinline__ void run_stream_task(const KParams& p, Stream& st, co
             float* o = p.logits;
             auto out = [&](int r, int, float v, float) { o[r] = v * s.rstd[0]; };
             gemv_stream_dispatch<WT, false>(p, st, ring, qe, r0, r1, H, p.x_final, (const WT*)p.final_norm, out, s);
+            if (p.greedy_tokens) lm_greedy(p, r0, r1);
             break;
         }
         default: break;

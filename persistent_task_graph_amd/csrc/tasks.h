@@ -644,11 +644,24 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, int i) {
     return ((unsigned long long)o << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)i);
 }
 
+// Greedy step, end: turn each sequence's argmax key into its next token,
+// reset the key and advance the sequence's length. Runs once per step, on
+// one thread, after every reader of the step's lengths has finished.
+__device__ __forceinline__ void greedy_finish(const KParams& p) {
+    for (int b = 0; b < p.B; ++b) {
+        const unsigned long long k = __hip_atomic_exchange(&p.amax[b], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        p.greedy_tokens[b] = k ? (int32_t)(0xFFFFFFFFu - (uint32_t)k) : 0;
+        p.greedy_lens[b] += 1;
+    }
+}
+
 // Greedy step, after an LM-head task has stored logit rows [r0, r1): fold
-// them into each sequence's argmax key; the task that finishes the LM head
-// last turns the keys into the next tokens and advances the lengths (every
-// attention task of the step, the only other reader of the lengths, has
-// finished before the LM head starts). Same choice as k_argmax.
+// them into each sequence's argmax key (same choice as k_argmax). The keys
+// become tokens in greedy_finish, called when the lengths have no reader
+// left: in the persistent kernel by the last worker to leave its queue (an
+// AOT attention slot that the step leaves empty still reads the lengths,
+// and a worker holding one may come late), in kernel-per-op mode by the last
+// LM-head task (every earlier launch has ended by then).
 __device__ __forceinline__ void lm_greedy(const KParams& p, int r0, int r1) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     wait_stores();
@@ -675,14 +688,10 @@ __device__ __forceinline__ void lm_greedy(const KParams& p, int r0, int r1) {
     }
     wait_stores();  // the maxima are performed before this task counts as done
     __syncthreads();
-    if (tid != 0) return;
+    if (p.persistent || tid != 0) return;
     const uint32_t old = __hip_atomic_fetch_add(p.lm_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old + 1u != (uint32_t)p.n_lm_tasks) return;
-    for (int b = 0; b < p.B; ++b) {
-        const unsigned long long k = __hip_atomic_exchange(&p.amax[b], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        p.greedy_tokens[b] = k ? (int32_t)(0xFFFFFFFFu - (uint32_t)k) : 0;
-        p.greedy_lens[b] += 1;
-    }
+    greedy_finish(p);
     __hip_atomic_store(p.lm_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -941,9 +950,13 @@ __device__ __forceinline__ void prefetch_step(Prefetch& f) {
 
 // ---------------------------------------------------------------- attention
 
+// Element offset of (layer l, sequence b, KV head g, position pos) in the
+// cache, or -1 for a paged position whose block-table entry lies outside
+// the pool (the entry is the caller's data: it is checked, not trusted).
 __device__ __forceinline__ int64_t kv_offset(const KParams& p, int l, int b, int g, int pos) {
     if (!p.paged) return (int64_t)l * p.kv_layer_stride + ((int64_t)(b * p.Hkv + g) * p.cap + pos) * p.D;
     const int blk = p.block_table[(int64_t)b * p.max_blocks + pos / p.kv_block];
+    if ((unsigned)blk >= (unsigned)p.n_pool_blocks) return -1;
     return (int64_t)l * p.kv_layer_stride + ((int64_t)blk * p.Hkv + g) * p.kv_block * p.D + (int64_t)(pos % p.kv_block) * p.D;
 }
 
@@ -1090,10 +1103,17 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
     const int blk0 = p.paged ? j0 / p.kv_block : 0;
     if (p.paged) {
         const int nblk = (j1 - 1) / p.kv_block - blk0 + 1;
-        for (int i = tid; i < nblk; i += kThreads) s.btab[i] = btab[blk0 + i];
+        for (int i = tid; i < nblk; i += kThreads) {
+            const int e = btab[blk0 + i];
+            // an entry outside the pool reads zeros (and is reported)
+            if ((unsigned)e >= (unsigned)p.n_pool_blocks) raise_error(p.ctrl, MK_ERR_BLOCK_TABLE);
+            s.btab[i] = e;
+        }
     }
     // byte offset of row j of the split (plus `add`), or out of range for
-    // rows past the split and for the new row
+    // rows past the split, for the new row and for blocks outside the pool.
+    // In range, every offset is below 2^31 bytes (the plan and the step
+    // check that a sequence's contiguous span, or a paged layer, is smaller).
     auto row_off = [&](int j, uint32_t add, bool staged) -> uint32_t {
         const int jj = j0 + j;
         if (j >= n || jj == pos) return kOOB;
@@ -1101,6 +1121,7 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
         if (p.paged) {
             const int bi = jj / p.kv_block;
             const int blk = staged ? s.btab[bi - blk0] : btab[bi];
+            if ((unsigned)blk >= (unsigned)p.n_pool_blocks) return kOOB;
             o = (uint32_t)(((blk * Hkv + g) * p.kv_block + jj % p.kv_block) * D * es);
         } else {
             o = (uint32_t)(jj * D * es);
@@ -1143,11 +1164,13 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
     // 2. owner: new k (norm + RoPE) and v, rounded to the cache type, appended
     if (appender) {
         if (wave == 0) head_norm_rope<D>(nv, gk, qkn, p.eps, cs);
-        WT* dst = (WT*)(wave == 0 ? p.kv_k : p.kv_v) + kv_offset(p, l, b, g, pos);
+        const int64_t off = kv_offset(p, l, b, g, pos);
+        if (off < 0 && lane == 0 && wave == 0) raise_error(p.ctrl, MK_ERR_BLOCK_TABLE);
+        WT* dst = (WT*)(wave == 0 ? p.kv_k : p.kv_v) + (off < 0 ? 0 : off);
 #pragma unroll
         for (int i = 0; i < D / 64; ++i) {
             const WT c = from_float<WT>(nv[i]);
-            dst[lane + 64 * i] = c;
+            if (off >= 0) dst[lane + 64 * i] = c;  // a bad block-table entry: nothing is written
             s.kn[wave * 128 + lane + 64 * i] = to_float<WT>(c);
         }
     }

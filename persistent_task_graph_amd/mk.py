@@ -6,8 +6,11 @@ there is no CPU fallback.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
+import sys
+import weakref
 from typing import Optional, Sequence
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -17,7 +20,7 @@ MK_F32, MK_BF16 = 0, 1
 MK_KV_CONTIGUOUS, MK_KV_PAGED = 0, 1
 MK_PERSISTENT, MK_KERNEL_PER_OP = 0, 1
 MK_OK, MK_ERR_ARG, MK_ERR_HIP, MK_ERR_UNSUPPORTED, MK_ERR_STATE = 0, -1, -2, -3, -4
-MK_ERR_TOKEN, MK_ERR_KV_OVERFLOW, MK_ERR_TIMEOUT = 1, 2, 4
+MK_ERR_TOKEN, MK_ERR_KV_OVERFLOW, MK_ERR_TIMEOUT, MK_ERR_BLOCK_TABLE = 1, 2, 4, 8
 
 # operator ids (mk_plan_info.tasks_per_op index)
 OP_QKV, OP_O, OP_GATEUP, OP_DOWN, OP_LM, OP_ATTN, OP_EMBED = 1, 2, 3, 4, 5, 6, 7
@@ -161,6 +164,18 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
+_live_plans: "weakref.WeakSet[Plan]" = weakref.WeakSet()
+
+
+@atexit.register
+def _close_live_plans() -> None:
+    # free every plan while the HIP runtime is still up: atexit handlers run
+    # before the interpreter tears modules down, and before the C runtime's
+    # exit handlers (a profiler's among them) run
+    for pl in list(_live_plans):
+        pl.close()
+
+
 class Plan:
     """Owns one mk_plan (task graph + device tables)."""
 
@@ -170,6 +185,7 @@ class Plan:
         if not h:
             raise MKError("mk_build_graph failed: " + last_error())
         self._h = h
+        _live_plans.add(self)
 
     @property
     def handle(self) -> int:
@@ -181,6 +197,11 @@ class Plan:
             self._h = None
 
     def __del__(self):
+        # no HIP call once the interpreter is finalizing: the plan was freed
+        # by the atexit hook, or the process is ending and the driver takes
+        # the memory back
+        if sys.is_finalizing():
+            return
         try:
             self.close()
         except Exception:

@@ -8,7 +8,10 @@ from fixed seeds, with the shapes and value distributions of the workloads
 
 Random numbers come from the counter-based generator in ``synth.c``
 (SplitMix64 words, Box-Muller normals), so results do not depend on the
-thread count. Norm gains are 1.0 (the N(0, 0.02) draw applies to matrices).
+thread count. Norm gains are 1.0 for the workloads (the N(0, 0.02) draw
+applies to matrices); tests that must tell one gain vector from another ask
+for ``gains="random"``: every gain vector (attention, MLP, final, per-head q
+and k) then holds its own seeded draw from 1 + N(0, 0.25).
 """
 from __future__ import annotations
 
@@ -195,36 +198,66 @@ WORKLOADS: Dict[str, Workload] = {
 _MATS = ["wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down"]
 _STREAM_EMBED = 1_000_001
 _STREAM_LM = 1_000_002
+_STREAM_FINAL_GAIN = 1_000_003
+# gain vector ids inside one layer (stream = layer * 32 + 16 + id)
+_GAINS = ["attn_norm", "mlp_norm", "q_norm", "k_norm"]
+GAIN_STD = 0.25
 
 
-def _gain(n: int, wdtype: str) -> np.ndarray:
+def _gain(n: int, wdtype: str, gains: str = "unit", seed: int = SEED_WEIGHTS, stream: int = 0) -> np.ndarray:
+    """Norm gain vector: all ones ('unit') or a seeded 1 + N(0, GAIN_STD) draw ('random')."""
+    if gains == "random":
+        return normal(seed, stream, (n,), GAIN_STD, wdtype, mean=1.0)
+    if gains != "unit":
+        raise ValueError(gains)
     if wdtype == "bf16":
         return np.full(n, BF16_ONE, dtype=np.uint16)
     return np.ones(n, dtype=np.float32)
 
 
-def layer_weights(shape: ModelShape, layer: int, seed: int = SEED_WEIGHTS, std: float = 0.02) -> Dict[str, np.ndarray]:
+def layer_weights(shape: ModelShape, layer: int, seed: int = SEED_WEIGHTS, std: float = 0.02,
+                  gains: str = "unit") -> Dict[str, np.ndarray]:
     H, F, D = shape.hidden, shape.ffn, shape.head_dim
     dims = {"wq": (shape.qdim, H), "wk": (shape.kvdim, H), "wv": (shape.kvdim, H), "wo": (H, shape.qdim),
             "w_gate": (F, H), "w_up": (F, H), "w_down": (H, F)}
     out = {}
     for i, name in enumerate(_MATS):
         out[name] = normal(seed, layer * 32 + i, dims[name], std, shape.wdtype)
-    out["attn_norm"] = _gain(H, shape.wdtype)
-    out["mlp_norm"] = _gain(H, shape.wdtype)
-    if shape.qk_norm:
-        out["q_norm"] = _gain(D, shape.wdtype)
-        out["k_norm"] = _gain(D, shape.wdtype)
+    names = ["attn_norm", "mlp_norm"] + (["q_norm", "k_norm"] if shape.qk_norm else [])
+    for name in names:
+        n = D if name in ("q_norm", "k_norm") else H
+        out[name] = _gain(n, shape.wdtype, gains, seed, layer * 32 + 16 + _GAINS.index(name))
     return out
 
 
-def model_weights(shape: ModelShape, seed: int = SEED_WEIGHTS, std: float = 0.02) -> Dict[str, object]:
-    w: Dict[str, object] = {"layers": [layer_weights(shape, l, seed, std) for l in range(shape.n_layers)]}
+def model_weights(shape: ModelShape, seed: int = SEED_WEIGHTS, std: float = 0.02, gains: str = "unit") -> Dict[str, object]:
+    """Weights of a model: matrices N(0, std); norm gains per `gains` ('unit' or 'random')."""
+    w: Dict[str, object] = {"layers": [layer_weights(shape, l, seed, std, gains) for l in range(shape.n_layers)]}
     if shape.embed_head:
         w["embed"] = normal(seed, _STREAM_EMBED, (shape.vocab, shape.hidden), std, shape.wdtype)
         w["lm_head"] = normal(seed, _STREAM_LM, (shape.vocab, shape.hidden), std, shape.wdtype)
-        w["final_norm"] = _gain(shape.hidden, shape.wdtype)
+        w["final_norm"] = _gain(shape.hidden, shape.wdtype, gains, seed, _STREAM_FINAL_GAIN)
     return w
+
+
+def with_gains(shape: ModelShape, weights: Dict[str, object], gains: str = "random",
+               seed: int = SEED_WEIGHTS) -> Dict[str, object]:
+    """Shallow copy of `weights` whose norm gains are replaced by the `gains`
+    draw (the same vectors model_weights(shape, seed, gains=gains) makes);
+    the matrices are shared, not copied."""
+    H, D = shape.hidden, shape.head_dim
+    out: Dict[str, object] = {k: v for k, v in weights.items() if k != "layers"}
+    layers = []
+    for l, lw in enumerate(weights["layers"]):
+        nl = dict(lw)
+        for name in ["attn_norm", "mlp_norm"] + (["q_norm", "k_norm"] if shape.qk_norm else []):
+            n = D if name in ("q_norm", "k_norm") else H
+            nl[name] = _gain(n, shape.wdtype, gains, seed, l * 32 + 16 + _GAINS.index(name))
+        layers.append(nl)
+    out["layers"] = layers
+    if shape.embed_head:
+        out["final_norm"] = _gain(H, shape.wdtype, gains, seed, _STREAM_FINAL_GAIN)
+    return out
 
 
 def seq_lengths(wl: Workload, seed: int = SEED_LENGTHS) -> np.ndarray:

@@ -5,8 +5,10 @@ oracle on sampled outputs.
   output element is compared, and the appended K/V rows are checked;
 - the 36-layer 8B-shaped model at batch 1: a teacher-forced prefill from an
   empty cache followed by greedy steps, all logits compared each step;
+- the same model at batch 1 from the benchmarked state (1024 cached random
+  keys): 100 greedy steps, the oracle teacher-forced on the GPU's tokens;
 - the same model at batch 16 with log-uniform KV lengths: two sampled
-  sequences compared over two steps;
+  sequences compared over two steps, and four sequences over eight steps;
 - the same model at batch 8 with the paged cache and KV lengths in
   [4096, 16384]: the shortest sequence compared over two steps (the other
   sequences' cache blocks hold seeded device-side N(0,1) values; sequences
@@ -84,13 +86,18 @@ def _check_rows(out, orc, caches, lens, rows):
     return worst, agree / total
 
 
-def test_layer8b_hidden_every_step_matches_oracle():
+@pytest.mark.parametrize("gains", ["unit", "random"])
+def test_layer8b_hidden_every_step_matches_oracle(gains):
+    # unit gains: the workload as benchmarked; random gains: every gain vector
+    # (attention, MLP, per-head q and k) differs, so a swapped or missing gain,
+    # or QK-norm after RoPE, would fail
     wl = synth.WORKLOADS["layer8b"]
-    shape, B, steps = wl.shape, wl.batch, wl.steps
+    shape, B = wl.shape, wl.batch
+    steps = wl.steps if gains == "unit" else 16
     lens = synth.seq_lengths(wl)
     cap = wl.capacity()
-    log("layer8b: one 8B-shaped layer, hidden I/O, KV %d, %d steps" % (int(lens[0]), steps))
-    w = synth.model_weights(shape)
+    log("layer8b: one 8B-shaped layer, hidden I/O, KV %d, %d steps, %s gains" % (int(lens[0]), steps, gains))
+    w = synth.model_weights(shape, gains=gains)
     dm = harness.DeviceModel(shape, w)
     caches = [synth.kv_sequence(shape, b, int(lens[b]), cap) for b in range(B)]
     kv = harness.DeviceKV(shape, B, cap)
@@ -207,6 +214,58 @@ def test_q8b_b8_paged_long_context_sampled_row_matches_oracle(q8b):
     out = _decode(plan, dm, kv, synth.tokens(wl), lens, steps, shape)
     worst, agree = _check_rows(out, orc, {b0: c}, lens, [b0])
     log("  max|d|/std = %.3g, top-1 = %.3f" % (worst, agree))
+    assert worst <= TOL
+    assert agree >= 0.99
+    plan.close()
+
+
+def test_q8b_b1_bench_state_100_greedy_steps_top1(q8b):
+    # the benchmarked batch-1 state: 1024 cached N(0,1) keys per layer and
+    # head, then 100 greedy GPU steps; the oracle starts from the same cache
+    # and is fed the GPU's tokens. Every step's logits are compared, and the
+    # oracle's argmax must equal the GPU's token on >= 99 of the 100 steps.
+    w, dm, orc = q8b
+    shape = synth.Q8B
+    L0, steps = 1024, 100
+    cap = L0 + steps + 8
+    log("q8b B=1: %d cached keys, %d greedy steps, oracle teacher-forced" % (L0, steps))
+    t0 = time.time()
+    cache = synth.kv_sequence(shape, 0, L0, cap)
+    kv = harness.DeviceKV(shape, 1, cap)
+    kv.load_sequence(0, cache["k"], cache["v"], L0)
+    plan = harness.build_plan(shape, 1, cap)
+    out = _decode(plan, dm, kv, synth.tokens(synth.WORKLOADS["q8b_b1"]), [L0], steps, shape)
+    log("  GPU done in %.1fs" % (time.time() - t0))
+    worst, agree = _check_rows(out, orc, [cache], [L0], [0])
+    log("  max|d|/std = %.3g, top-1 = %.3f over %d row-steps (%.1fs)" % (worst, agree, steps, time.time() - t0))
+    assert worst <= TOL
+    assert agree >= 0.99
+    plan.close()
+
+
+def test_q8b_b16_32_row_steps_top1(q8b):
+    # batch 16 with log-uniform lengths: four sequences (shortest, longest and
+    # two between) over eight greedy steps, 32 row-steps in all
+    w, dm, orc = q8b
+    wl = synth.WORKLOADS["q8b_b16"]
+    shape, B = wl.shape, wl.batch
+    lens = synth.seq_lengths(wl)
+    steps = 8
+    cap = int(lens.max()) + steps + 8
+    order = np.argsort(lens)
+    rows = sorted({int(order[0]), int(order[5]), int(order[10]), int(order[-1])})
+    log("q8b B=16: rows %s (lengths %s), %d steps" % (rows, [int(lens[b]) for b in rows], steps))
+    kv = harness.DeviceKV(shape, B, cap)
+    caches = {}
+    for b in range(B):
+        c = synth.kv_sequence(shape, b, int(lens[b]), cap)
+        kv.load_sequence(b, c["k"], c["v"], int(lens[b]))
+        if b in rows:
+            caches[b] = c
+    plan = harness.build_plan(shape, B, cap)
+    out = _decode(plan, dm, kv, synth.tokens(wl, stream=3), lens, steps, shape)
+    worst, agree = _check_rows(out, orc, caches, lens, rows)
+    log("  max|d|/std = %.3g, top-1 = %.3f over %d row-steps" % (worst, agree, steps * len(rows)))
     assert worst <= TOL
     assert agree >= 0.99
     plan.close()

@@ -117,13 +117,18 @@ def test_mid_bf16_matches_oracle(mid_weights, B, lens, chunk):
     log("  max|d|/std = %.3g, top-1 = %.3f" % (worst, agree))
     assert worst <= 2e-2
     assert agree >= 0.99
-    # cached positions are untouched (bit-identical); the two appended rows
-    # agree with the oracle's to one bf16 ulp plus the fp32-vs-fp64 error of
-    # the projection, which is relative to the head vector's scale (RoPE can
-    # cancel an element down to near zero)
+    _check_appended(s, kv, caches, rows, 2)
+    plan.close()
+
+
+def _check_appended(s, kv, caches, rows, steps):
+    """Cached positions are untouched (bit-identical); the appended rows agree
+    with the oracle's to one bf16 ulp plus the fp32-vs-fp64 error of the
+    projection, which is relative to the head vector's scale (RoPE can cancel
+    an element down to near zero)."""
     for b in rows:
         L0 = int(s.lens[b])
-        n = L0 + 2
+        n = L0 + steps
         k, v = kv.read_sequence(b, n)
         for got, ref in ((k, caches[b]["k"][:, :, :n]), (v, caches[b]["v"][:, :, :n])):
             assert np.array_equal(got[:, :, :L0], ref[:, :, :L0])
@@ -131,6 +136,55 @@ def test_mid_bf16_matches_oracle(mid_weights, B, lens, chunk):
             r = synth.bf16_to_f32(np.ascontiguousarray(ref[:, :, L0:])).astype(np.float64)
             rms = np.sqrt(np.mean(r * r, axis=-1, keepdims=True))
             assert np.all(np.abs(g - r) <= 2 ** -7 * np.maximum(np.abs(g), np.abs(r)) + 1e-4 * rms)
+
+
+# Seeded non-unit gains, different for every gain vector (attention, MLP,
+# final, per-head q and k): a kernel that read the wrong gain vector, no
+# gain, or applied QK-norm after RoPE fails these (with unit gains it would
+# not: RoPE keeps a head's RMS).
+@pytest.fixture(scope="module")
+def mid_weights_g(mid_weights):
+    return synth.with_gains(MID, mid_weights, "random")
+
+
+def test_tiny_random_gains_matches_oracle():
+    wl = synth.WORKLOADS["tiny"]
+    log("tiny: random gains, 8 greedy steps")
+    w = synth.model_weights(wl.shape, gains="random")
+    s = make_setup(wl.shape, wl.batch, synth.seq_lengths(wl), wl.capacity(), weights=w)
+    plan = plan_for(s)
+    kv = device_kv(s)
+    out, err = run_gpu(s, plan, kv, _tokens(s.shape, s.B), 8)
+    assert err == 0
+    orc, _ = run_oracle(s, out)
+    worst, agree = compare(out, orc)
+    log("  max|d|/std = %.3g, top-1 = %.3f" % (worst, agree))
+    assert worst <= 1e-3 and agree >= 0.99
+    plan.close()
+
+
+@pytest.mark.parametrize("B,lens,paged", [
+    (1, [300], False),
+    (3, [5, 129, 700], False),
+    (16, list(range(3, 16 * 37, 37)), False),
+    (4, [17, 250, 64, 129], True),
+])
+def test_mid_random_gains_match_oracle(mid_weights_g, B, lens, paged):
+    log("mid bf16, random gains: B=%d lens=%s paged=%s" % (B, lens, paged))
+    cap = max(lens) + 8
+    table = synth.block_table([cap] * B, 16) if paged else None
+    s = make_setup(MID, B, lens, cap, weights=mid_weights_g, paged=paged, table=table)
+    plan = plan_for(s, kv_chunk=64)
+    kv = device_kv(s)
+    out, err = run_gpu(s, plan, kv, _tokens(MID, B, 9), 2)
+    assert err == 0
+    rows = list(range(B)) if B <= 8 else [0, 7, 15]
+    orc, caches = run_oracle(s, out, rows=rows)
+    worst, agree = compare(out, orc, rows=rows)
+    log("  max|d|/std = %.3g, top-1 = %.3f" % (worst, agree))
+    assert worst <= 2e-2
+    assert agree >= 0.99
+    _check_appended(s, kv, caches, rows, 2)
     plan.close()
 
 
@@ -143,6 +197,26 @@ def test_mid_modes_bitwise(mid_weights):
     d, _ = _logits_seq(s, 3, kv_chunk=64, workers=37)
     for o in (b, c, d):
         _bitwise(a, o)
+
+
+@pytest.mark.parametrize("B,paged", [(8, False), (16, False), (8, True)])
+def test_mid_modes_bitwise_large_batch(mid_weights, B, paged):
+    # the batch-8 and batch-16 kernel instances spread event arrivals over
+    # eight count planes; the persistent step (AOT slots and JIT through the
+    # scheduler waves) must still give the kernel-per-op bits exactly
+    lens = [int(v) for v in np.linspace(0, 900, B)]
+    log("mid bf16: persistent vs kernel-per-op vs JIT, B=%d paged=%s lens=%s" % (B, paged, lens))
+    cap = max(lens) + 8
+    table = synth.block_table([cap] * B, 16) if paged else None
+    s = make_setup(MID, B, lens, cap, weights=mid_weights, paged=paged, table=table)
+    t0 = _tokens(MID, B, 3)
+    a, _ = _logits_seq(s, 3, tokens=t0)
+    b, _ = _logits_seq(s, 3, tokens=t0, mode=1)
+    c, _ = _logits_seq(s, 3, tokens=t0, jit=1)
+    for o in (b, c):
+        _bitwise(a, o)
+        for (ta, la, na), (to, lo, no) in zip(a, o):
+            assert np.array_equal(na, no)
 
 
 def test_mid_adaptive_chunk_matches_oracle_and_modes(mid_weights):
@@ -274,3 +348,34 @@ def test_watchdog_times_out_instead_of_hanging(tiny):
     d_len = torch.from_numpy(s.lens.astype(np.int32)).cuda()
     plan.step(s.dm.struct, kv.struct, tok, d_len, logits)
     assert plan.device_error() & 4
+
+
+def test_block_table_entry_outside_pool_is_reported(mid_weights):
+    # a paged block-table entry past the pool or negative: the kernel's range
+    # checks read zeros for those positions, store nothing for the new row and
+    # raise MK_ERR_BLOCK_TABLE; with the table restored the next step is clean
+    import torch
+
+    from persistent_task_graph_amd import mk
+
+    B, lens, cap = 2, [40, 70], 100
+    table = synth.block_table([cap] * B, 16)
+    s = make_setup(MID, B, lens, cap, weights=mid_weights, paged=True, table=table)
+    plan = plan_for(s)
+    kv = device_kv(s)
+    pool = kv.n_blocks
+    good = kv.table.clone()
+    kv.table[0, 40 // 16] = pool + 100  # the block holding sequence 0's new row
+    kv.table[1, 1] = -7                 # a cached block of sequence 1
+    log("paged block table with entries outside the pool (pool %d)" % pool)
+    logits = torch.empty((B, MID.vocab), dtype=torch.float32, device="cuda")
+    tok = torch.from_numpy(_tokens(MID, B, 1)).cuda()
+    d_len = torch.from_numpy(s.lens.astype(np.int32)).cuda()
+    plan.step(s.dm.struct, kv.struct, tok, d_len, logits)
+    err = plan.device_error()
+    assert err & mk.MK_ERR_BLOCK_TABLE and not err & ~mk.MK_ERR_BLOCK_TABLE
+    assert torch.isfinite(logits).all()
+    kv.table.copy_(good)
+    plan.step(s.dm.struct, kv.struct, tok, d_len, logits)
+    assert plan.device_error() == 0
+    plan.close()

@@ -124,11 +124,14 @@ def test_bad_desc_rejected(lib, field, value, msg):
 
 
 def test_step_on_host_only_plan_is_state_error(lib):
+    # arguments are checked first (null weight pointers: MK_ERR_ARG), then the
+    # plan's state (host-only: MK_ERR_STATE)
     p = _plan(synth.TINY, 1, 64)
     w = mk.make_weights([{}] * 2, 1, 1, 1)
-    kv = mk.make_kv(1, 1, 0)
+    kv = mk.make_kv(1, 1, 1 * 4 * 64 * 64)
     rc = lib.mk_decode_step(p.handle, ctypes.byref(w), ctypes.byref(kv), 1, 1, 1, None)
-    assert rc == mk.MK_ERR_STATE
+    assert rc == mk.MK_ERR_ARG
+    assert _fake_step(p, synth.TINY, 1 * 4 * 64 * 64, False) == mk.MK_ERR_STATE
 
 
 def test_aot_attention_slots(lib):
@@ -155,3 +158,47 @@ def test_aot_slots_dry_run_capped_chunk(lib):
     p = _plan(shape, 16, 4200, jit=2, workers=24, kv_chunk=64, kv_chunk_max=64)
     seq = [4000] * 16  # 16 * 8 * 63 split tasks per layer
     assert p.dry_run(n_threads=6, seed=5, timeout_ms=60000, seq_lens=seq) == 0, mk.last_error()
+
+
+# ---------------------------------------------------------------- 32-bit K/V offsets
+# Attention addresses K/V with 32-bit byte offsets inside buffer resources,
+# and uses 2^31 as the out-of-range offset: a contiguous sequence span and a
+# paged layer must both stay below 2 GiB. Larger layouts are refused.
+
+def _fake_step(plan, shape, layer_stride, paged):
+    """mk_decode_step on a host-only plan with fake (never dereferenced) device pointers."""
+    fake = 0x1000
+    lw = [{n: fake for n in mk.LAYER_FIELDS} for _ in range(shape.n_layers)]
+    w = mk.make_weights(lw, fake, fake, fake)
+    kv = mk.make_kv(fake, fake, layer_stride, fake if paged else None)
+    return mk.lib().mk_decode_step(plan.handle, ctypes.byref(w), ctypes.byref(kv), fake, fake, fake, None)
+
+
+def test_contiguous_span_of_2gib_rejected_at_build(lib):
+    shape = synth.ModelShape(n_layers=1, hidden=1024, n_heads=8, n_kv_heads=8, head_dim=128, ffn=2048, vocab=100,
+                             wdtype="f32", kv_dtype="f32")
+    # fp32, head_dim 128: 4M positions span exactly 2 GiB
+    with pytest.raises(mk.MKError, match="2 GiB"):
+        _plan(shape, 1, 1 << 22)
+    _plan(shape, 1, (1 << 22) - 1).verify()
+    _plan(synth.Q8B, 1, 1 << 22).verify()  # bf16: 1 GiB
+
+
+def test_paged_layer_of_2gib_rejected_at_step(lib):
+    shape = replace(synth.Q8B, n_layers=2)
+    blk = shape.n_kv_heads * 16 * shape.head_dim  # elements per physical block and layer
+    p = _plan(shape, 16, 1 << 22, paged=True)
+    max_blocks = ((1 << 31) - 1) // (2 * blk)  # largest pool under 2 GiB per layer
+    assert _fake_step(p, shape, max_blocks * blk, True) == mk.MK_ERR_STATE  # arguments fine, plan host-only
+    assert _fake_step(p, shape, (max_blocks + 1) * blk, True) == mk.MK_ERR_ARG
+    assert "2 GiB" in mk.last_error()
+    assert _fake_step(p, shape, blk + 1, True) == mk.MK_ERR_ARG  # not a whole number of blocks
+    assert "multiple" in mk.last_error()
+
+
+def test_contiguous_layer_stride_too_small_rejected(lib):
+    shape = replace(synth.Q8B, n_layers=2)
+    p = _plan(shape, 4, 1000)
+    need = 4 * shape.n_kv_heads * 1000 * shape.head_dim
+    assert _fake_step(p, shape, need, False) == mk.MK_ERR_STATE
+    assert _fake_step(p, shape, need - 1, False) == mk.MK_ERR_ARG

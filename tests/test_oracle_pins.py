@@ -327,3 +327,209 @@ def test_layer_matches_float64_composition_of_pinned_primitives():
     up = lw["w_up"].astype(np.float64) @ xn
     x2 = x1 + lw["w_down"].astype(np.float64) @ (gt * expit(gt) * up)
     np.testing.assert_allclose(y, x2, rtol=2e-5, atol=2e-5)
+
+
+# ----------------------------------------------------------------- norm gains: routing and order
+# With unit gains a swap of two gain vectors, or QK-norm applied after RoPE
+# (RoPE keeps a head's RMS), changes nothing. The pins below use seeded
+# non-unit gains, different for every vector, or gains that are zero
+# except where a closed form needs them.
+
+def _f64_layer(shape, lw, cache_ref, x, pos, order="norm_then_rope"):
+    """float64 decoder layer in numpy; `order` chooses where QK-norm sits."""
+    D, Hq, Hkv = shape.head_dim, shape.n_heads, shape.n_kv_heads
+    xd = x.astype(np.float64)
+
+    def g(name):
+        return lw[name].astype(np.float64)
+
+    def rms(v, gain):
+        return v / np.sqrt(np.mean(v * v) + shape.eps) * gain
+
+    def rot(v, p):
+        h = D // 2
+        th = p * shape.rope_base ** (-2.0 * np.arange(h) / D)
+        a, b = v[:h], v[h:]
+        return np.concatenate([a * np.cos(th) - b * np.sin(th), b * np.cos(th) + a * np.sin(th)])
+
+    def head(v, gain):
+        if order == "norm_then_rope":
+            return rot(rms(v, gain), pos)
+        return rms(rot(v, pos), gain)
+
+    xn = rms(xd, g("attn_norm"))
+    q = (g("wq") @ xn).reshape(Hq, D)
+    k = (g("wk") @ xn).reshape(Hkv, D)
+    v = (g("wv") @ xn).reshape(Hkv, D)
+    q = np.stack([head(q[h], g("q_norm")) for h in range(Hq)])
+    k = np.stack([head(k[h], g("k_norm")) for h in range(Hkv)])
+    K = cache_ref["k"][0].astype(np.float64)
+    V = cache_ref["v"][0].astype(np.float64)
+    K[:, pos] = k
+    V[:, pos] = v
+    att = []
+    for h in range(Hq):
+        grp = h * Hkv // Hq
+        s = K[grp, : pos + 1] @ q[h] / math.sqrt(D)
+        att.append(softmax(s) @ V[grp, : pos + 1])
+    x1 = xd + g("wo") @ np.concatenate(att)
+    xn = rms(x1, g("mlp_norm"))
+    gt = g("w_gate") @ xn
+    up = g("w_up") @ xn
+    return x1 + g("w_down") @ (gt * expit(gt) * up), k
+
+
+def test_random_gains_are_distinct_per_vector_and_layer():
+    # the seeded gain draws differ between vectors and layers (else a swap
+    # of two of them could not be seen)
+    shape = _tiny_shape(n_layers=2)
+    w = synth.model_weights(shape, seed=7, gains="random")
+    vecs = [w["final_norm"]] + [lw[n] for lw in w["layers"] for n in ("attn_norm", "mlp_norm", "q_norm", "k_norm")]
+    for i in range(len(vecs)):
+        assert np.all(np.isfinite(vecs[i])) and abs(float(np.std(vecs[i])) - synth.GAIN_STD) < 0.12
+        for j in range(i):
+            n = min(vecs[i].size, vecs[j].size)
+            assert not np.array_equal(vecs[i][:n], vecs[j][:n])
+
+
+def test_layer_with_distinct_gains_matches_float64_composition_and_rejects_planted_mistakes():
+    # the layer with different non-unit gains everywhere equals the float64
+    # composition with R3's order (QK-norm, then RoPE); the same composition
+    # with the two norms' places exchanged, and the oracle fed swapped gain
+    # vectors, both land far outside the tolerance
+    shape = _tiny_shape()
+    w = synth.model_weights(shape, seed=7, std=0.2, gains="random")
+    lw = w["layers"][0]
+    pos = 5
+    cache = _cache(shape, 8, pos)
+    ref_cache = {k: cache[k].copy() for k in cache}
+    x = f32(RNG.normal(size=shape.hidden))
+    y = oracle.Oracle(shape, w).layer_forward(0, cache, pos, x)
+    want, k_new = _f64_layer(shape, lw, ref_cache, x, pos)
+    scale = float(np.abs(want - x).max())
+    np.testing.assert_allclose(y, want, rtol=2e-5, atol=2e-5)
+    np.testing.assert_allclose(cache["k"][0, :, pos], k_new, rtol=2e-5, atol=2e-6)
+    # norm after RoPE: the appended keys and the layer output change
+    wrong, k_wrong = _f64_layer(shape, lw, ref_cache, x, pos, order="rope_then_norm")
+    assert float(np.abs(cache["k"][0, :, pos] - k_wrong).max()) > 1e-2
+    assert float(np.abs(y - wrong).max()) > 1e-3 * scale
+    # planted in the oracle's inputs: swapped q/k gains, swapped attn/mlp gains
+    for a, b in (("q_norm", "k_norm"), ("attn_norm", "mlp_norm")):
+        wp = {"layers": [dict(lw)]}
+        wp["layers"][0][a], wp["layers"][0][b] = lw[b], lw[a]
+        c2 = {k: ref_cache[k].copy() for k in ref_cache}
+        yp = oracle.Oracle(shape, wp).layer_forward(0, c2, pos, x)
+        assert float(np.abs(yp - want).max()) > 1e-3 * scale, (a, b)
+
+
+def test_appended_key_is_normed_then_rotated():
+    # k at position p equals R(p) applied to k at position 0 (RoPE at 0 is
+    # the identity), with the same x and weights. That holds when QK-norm
+    # comes before RoPE; with a non-uniform k gain, norm after RoPE breaks it.
+    shape = _tiny_shape()
+    w = synth.model_weights(shape, seed=9, std=0.2, gains="random")
+    o = oracle.Oracle(shape, w)
+    x = f32(RNG.normal(size=shape.hidden))
+    c0 = _cache(shape, 16, 0)
+    o.layer_forward(0, c0, 0, x)
+    for p in (1, 7, 13):
+        cp = _cache(shape, 16, p)
+        o.layer_forward(0, cp, p, x)
+        for g in range(shape.n_kv_heads):
+            want = oracle.rope(c0["k"][0, g, 0], p, shape.rope_base)
+            np.testing.assert_allclose(cp["k"][0, g, p], want, rtol=1e-5, atol=1e-6)
+            # the value row is not rotated
+            np.testing.assert_array_equal(cp["v"][0, g, p], c0["v"][0, g, 0])
+    # and at p = 0 the key row is the closed form g_k * a / rms(a), a = W_k xn
+    xd = x.astype(np.float64)
+    xn = xd / np.sqrt(np.mean(xd * xd) + shape.eps) * w["layers"][0]["attn_norm"]
+    a = (w["layers"][0]["wk"].astype(np.float64) @ xn).reshape(shape.n_kv_heads, shape.head_dim)
+    gk = w["layers"][0]["k_norm"].astype(np.float64)
+    want0 = gk * a / np.sqrt(np.mean(a * a, axis=1, keepdims=True) + shape.eps)
+    np.testing.assert_allclose(c0["k"][0, :, 0], want0, rtol=1e-5, atol=1e-6)
+
+
+def test_attention_gain_feeds_qkv_and_mlp_gain_feeds_the_mlp():
+    # zero gains give closed forms that a swap of the two vectors breaks:
+    #  (1) mlp gain 0 and W_o = 0: attention adds nothing, the MLP sees a zero
+    #      vector and adds silu(0) * 0 = 0, so the layer is the identity;
+    #  (2) attention gain 0 except one channel c: the appended value row is
+    #      column c of W_v times g_c x_c / rms(x)
+    shape = _tiny_shape(qk_norm=False)
+    w = synth.model_weights(shape, seed=11, std=0.2, gains="random")
+    lw = w["layers"][0]
+    x = f32(RNG.normal(size=shape.hidden))
+    pos = 4
+    w1 = {"layers": [dict(lw)]}
+    w1["layers"][0]["mlp_norm"] = np.zeros_like(lw["mlp_norm"])
+    w1["layers"][0]["wo"] = np.zeros_like(lw["wo"])
+    y = oracle.Oracle(shape, w1).layer_forward(0, _cache(shape, 8, pos), pos, x)
+    np.testing.assert_array_equal(y, x)
+    w1s = {"layers": [dict(w1["layers"][0])]}
+    w1s["layers"][0]["attn_norm"], w1s["layers"][0]["mlp_norm"] = w1["layers"][0]["mlp_norm"], lw["attn_norm"]
+    ys = oracle.Oracle(shape, w1s).layer_forward(0, _cache(shape, 8, pos), pos, x)
+    assert not np.array_equal(ys, x)
+    c = 13
+    w2 = {"layers": [dict(lw)]}
+    ga = np.zeros_like(lw["attn_norm"])
+    ga[c] = lw["attn_norm"][c]
+    w2["layers"][0]["attn_norm"] = ga
+    cache = _cache(shape, 8, pos)
+    oracle.Oracle(shape, w2).layer_forward(0, cache, pos, x)
+    xd = x.astype(np.float64)
+    s = float(ga[c]) * xd[c] / math.sqrt(np.mean(xd * xd) + shape.eps)
+    want = (lw["wv"][:, c].astype(np.float64) * s).reshape(shape.n_kv_heads, shape.head_dim)
+    np.testing.assert_allclose(cache["v"][0, :, pos], want, rtol=1e-6, atol=1e-7)
+
+
+def test_zero_q_gain_gives_uniform_attention_and_zero_k_gain_a_zero_key():
+    # H = Hq * D, so W_o = I and W_d = 0 expose the attention output: y = x + att.
+    #  (1) q gain 0: every score is 0, each head returns the mean of its group's
+    #      value rows 0..pos (the appended row included);
+    #  (2) k gain 0: the appended key row is exactly zero.
+    # Swapping the q and k gain vectors breaks both.
+    shape = _tiny_shape()
+    H = shape.hidden
+    assert shape.n_heads * shape.head_dim == H
+    w = synth.model_weights(shape, seed=13, std=0.2, gains="random")
+    lw = dict(w["layers"][0])
+    lw["wo"] = np.eye(H, dtype=np.float32)
+    lw["w_down"] = np.zeros_like(lw["w_down"])
+    lw["q_norm"] = np.zeros_like(lw["q_norm"])
+    pos = 6
+    x = f32(RNG.normal(size=H) * 0.1)
+    cache = _cache(shape, 8, pos)
+    y = oracle.Oracle(shape, {"layers": [lw]}).layer_forward(0, cache, pos, x)
+    G = shape.n_heads // shape.n_kv_heads
+    V = cache["v"][0].astype(np.float64)
+    want = np.concatenate([V[h // G, : pos + 1].mean(axis=0) for h in range(shape.n_heads)])
+    np.testing.assert_allclose(y, x.astype(np.float64) + want, rtol=1e-5, atol=1e-6)
+    lk = dict(w["layers"][0])
+    lk["k_norm"] = np.zeros_like(lk["k_norm"])
+    ck = _cache(shape, 8, pos)
+    oracle.Oracle(shape, {"layers": [lk]}).layer_forward(0, ck, pos, x)
+    assert not np.any(ck["k"][0, :, pos])
+    ls = dict(lk)
+    ls["q_norm"], ls["k_norm"] = lk["k_norm"], lk["q_norm"]  # swapped: the key gets the nonzero gain
+    cs = _cache(shape, 8, pos)
+    oracle.Oracle(shape, {"layers": [ls]}).layer_forward(0, cs, pos, x)
+    assert np.any(cs["k"][0, :, pos])
+
+
+def test_final_gain_closed_form_with_one_channel():
+    # W_o = W_d = 0 keep x = E[tok]; a final gain that is zero except channel c
+    # gives logits = W_lm[:, c] * g_c * x_c / rms(x)
+    shape = _tiny_shape(n_layers=2)
+    w = synth.model_weights(shape, seed=17, std=0.2, gains="random")
+    for lw in w["layers"]:
+        lw["wo"][:] = 0
+        lw["w_down"][:] = 0
+    c = 21
+    gf = np.zeros_like(w["final_norm"])
+    gf[c] = w["final_norm"][c]
+    w["final_norm"] = gf
+    tok = 17
+    logits = oracle.Oracle(shape, w).model_forward(_cache(shape, 8, 3), tok, 3)
+    x = w["embed"][tok].astype(np.float64)
+    s = float(gf[c]) * x[c] / math.sqrt(np.mean(x * x) + shape.eps)
+    np.testing.assert_allclose(logits, w["lm_head"][:, c].astype(np.float64) * s, rtol=1e-6, atol=1e-7)
