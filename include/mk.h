@@ -307,6 +307,24 @@ int mk_get_device_error(mk_plan* plan, void* stream);
 int mk_argmax(const mk_plan* plan, const float* logits, int32_t* out_tokens, void* stream);
 
 /*
+ * mk_argmax without a plan and without any allocation, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. Same result as mk_argmax:
+ * out_tokens[b] = argmax_v logits[b, v], lowest index on ties, NaN never
+ * chosen (0 for a row with no number).
+ *  logits     device float [batch, vocab]; out_tokens device int32 [batch].
+ *  batch      1 .. 256 (larger: MK_ERR_ARG, nothing launched); vocab >= 1.
+ *  Runs on the current device; `stream` must belong to it.
+ * Its scratch (the 64 slice winners of each row, 128 KB at most) is a fixed
+ * array in the library's device memory, one per GPU, held until the process
+ * ends; its address is looked up with hipGetSymbolAddress on the first call
+ * on each device. Two launches, stream-ordered; the scratch needs no
+ * clearing. Calls that overlap on one GPU (different streams, or several
+ * host threads) share that array and race: serialise them.
+ */
+int mk_argmax_noalloc(const float* logits, int32_t batch, int32_t vocab, int32_t* out_tokens, void* stream);
+
+/*
  * Host-side checks of a plan's task graph (the MPK article §2.1: tasks,
  * events with required counts): every output row covered
  * exactly once per op, events' required counts equal their producer

@@ -40,17 +40,16 @@ __device__ __forceinline__ void argmax_merge(float& best, int& bi, float ov, int
     }
 }
 
-__global__ __launch_bounds__(kThreads) void k_argmax(const float* logits, int V, int32_t* out, float* pv, int32_t* pi,
-                                                     uint32_t* cnt) {
+// Winner (value, index) of slice blockIdx.x of row b; valid in thread 0.
+// best = -inf with index V when the slice holds no number.
+__device__ __forceinline__ void argmax_slice(const float* logits, int V, int b, float& best, int& bi) {
     __shared__ float sv[kWaves];
     __shared__ int si[kWaves];
-    __shared__ int last;
-    const int b = blockIdx.y;
     const float* row = logits + (int64_t)b * V;
     const int per = (V + kArgBlocks - 1) / kArgBlocks;
     const int i0 = blockIdx.x * per, i1 = min(V, i0 + per);
-    float best = -INFINITY;
-    int bi = V;
+    best = -INFINITY;
+    bi = V;
     for (int i = i0 + (int)threadIdx.x; i < i1; i += kThreads) {
         const float v = row[i];
         if (v > best) {  // strict: lowest index wins ties; NaN never wins
@@ -65,8 +64,18 @@ __global__ __launch_bounds__(kThreads) void k_argmax(const float* logits, int V,
         si[wave] = bi;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (threadIdx.x == 0)
         for (int w = 1; w < kWaves; ++w) argmax_merge(best, bi, sv[w], si[w]);
+}
+
+__global__ __launch_bounds__(kThreads) void k_argmax(const float* logits, int V, int32_t* out, float* pv, int32_t* pi,
+                                                     uint32_t* cnt) {
+    __shared__ int last;
+    const int b = blockIdx.y;
+    float best;
+    int bi;
+    argmax_slice(logits, V, b, best, bi);
+    if (threadIdx.x == 0) {
         st_co(&pv[b * kArgBlocks + blockIdx.x], best);
         st_co(&pi[b * kArgBlocks + blockIdx.x], bi);
         wait_stores();
@@ -81,6 +90,41 @@ __global__ __launch_bounds__(kThreads) void k_argmax(const float* logits, int V,
     out[b] = bi < V ? bi : 0;
     __hip_atomic_store(&cnt[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// ---------------------------------------------------------------- argmax without allocation
+// The slice winners of mk_argmax_noalloc live in this fixed array: one per
+// device, for callers that cannot allocate. It is written by k_argmax_part
+// and read by k_argmax_final, in stream order, so nothing in it has to start
+// at zero. Host code never passes `scratch` itself to a kernel (in host code
+// the name is a stand-in, not a device address): it passes the address that
+// hipGetSymbolAddress returned for the current device.
+constexpr int kNoAllocMaxRows = 256;
+struct ArgmaxScratch {
+    float v[kNoAllocMaxRows * kArgBlocks];
+    int32_t i[kNoAllocMaxRows * kArgBlocks];
+};
+static __device__ __align__(256) ArgmaxScratch scratch;
+
+__global__ __launch_bounds__(kThreads) void k_argmax_part(const float* logits, int V, ArgmaxScratch* sc) {
+    const int b = blockIdx.y;
+    float best;
+    int bi;
+    argmax_slice(logits, V, b, best, bi);
+    if (threadIdx.x == 0) {
+        sc->v[b * kArgBlocks + blockIdx.x] = best;
+        sc->i[b * kArgBlocks + blockIdx.x] = bi;
+    }
+}
+
+// one wave per row: the slice winners in slice order, lowest index on ties
+__global__ __launch_bounds__(64) void k_argmax_final(const ArgmaxScratch* sc, int V, int32_t* out) {
+    const int b = blockIdx.x, lane = threadIdx.x;
+    float best = sc->v[b * kArgBlocks + lane];
+    int bi = sc->i[b * kArgBlocks + lane];
+    for (int o = 32; o >= 1; o >>= 1) argmax_merge(best, bi, __shfl_xor(best, o, 64), __shfl_xor(bi, o, 64));
+    if (lane == 0) out[b] = bi < V ? bi : 0;
+}
+static_assert(kArgBlocks == 64, "k_argmax_final reduces one slice winner per lane");
 
 }  // namespace mk
 
@@ -630,6 +674,36 @@ int mk_argmax(const mk_plan* pl, const float* logits, int32_t* out_tokens, void*
     hipLaunchKernelGGL(k_argmax, dim3(kArgBlocks, pl->hp.desc.batch), dim3(kThreads), 0, (hipStream_t)stream, logits,
                        pl->hp.desc.vocab, out_tokens, pl->d_argv, pl->d_argi, pl->d_argc);
     if (!hip_ok(hipGetLastError(), "k_argmax launch")) return MK_ERR_HIP;
+    return MK_OK;
+}
+
+int mk_argmax_noalloc(const float* logits, int32_t batch, int32_t vocab, int32_t* out_tokens, void* stream) {
+    if (!logits || !out_tokens) return set_err("null argument"), MK_ERR_ARG;
+    if (batch < 1 || batch > kNoAllocMaxRows)
+        return set_err("mk_argmax_noalloc: batch must be in [1, " + std::to_string(kNoAllocMaxRows) + "]"), MK_ERR_ARG;
+    if (vocab < 1) return set_err("mk_argmax_noalloc: vocab must be positive"), MK_ERR_ARG;
+    // the array's address on the current device, looked up once per device
+    static std::mutex mu;
+    static std::vector<void*> addr;
+    int dev = 0;
+    if (!hip_ok(hipGetDevice(&dev), "hipGetDevice")) return MK_ERR_HIP;
+    void* ptr = nullptr;
+    {
+        std::lock_guard<std::mutex> g(mu);
+        if ((int)addr.size() <= dev) addr.resize(dev + 1, nullptr);
+        if (!addr[dev]) {
+            void* a = nullptr;
+            if (!hip_ok(hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)")) return MK_ERR_HIP;
+            addr[dev] = a;
+        }
+        ptr = addr[dev];
+    }
+    ArgmaxScratch* sc = (ArgmaxScratch*)ptr;
+    hipStream_t st = (hipStream_t)stream;
+    hipLaunchKernelGGL(k_argmax_part, dim3(kArgBlocks, batch), dim3(kThreads), 0, st, logits, vocab, sc);
+    if (!hip_ok(hipGetLastError(), "k_argmax_part launch")) return MK_ERR_HIP;
+    hipLaunchKernelGGL(k_argmax_final, dim3(batch), dim3(64), 0, st, (const ArgmaxScratch*)sc, vocab, out_tokens);
+    if (!hip_ok(hipGetLastError(), "k_argmax_final launch")) return MK_ERR_HIP;
     return MK_OK;
 }
 

@@ -27,7 +27,7 @@ OP_QKV, OP_O, OP_GATEUP, OP_DOWN, OP_LM, OP_ATTN, OP_EMBED = 1, 2, 3, 4, 5, 6, 7
 
 EXPORTS = ["mk_build_graph", "mk_destroy_plan", "mk_last_error", "mk_plan_query", "mk_decode_step",
            "mk_decode_step_greedy", "mk_decode_step_hidden", "mk_get_device_error", "mk_argmax", "mk_plan_verify", "mk_plan_dry_run",
-           "mk_plan_trace"]
+           "mk_plan_trace", "mk_argmax_noalloc"]
 
 
 class ExecOpts(ctypes.Structure):
@@ -105,7 +105,8 @@ def lib() -> ctypes.CDLL:
         L.mk_plan_verify.argtypes = [vp]
         L.mk_plan_dry_run.argtypes = [vp, i32, ctypes.c_uint64, i32, i32, vp]
         L.mk_plan_trace.argtypes = [vp, vp, ctypes.c_int64, vp]
-        for f in ("mk_plan_query", "mk_decode_step", "mk_decode_step_greedy", "mk_decode_step_hidden",
+        L.mk_argmax_noalloc.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp, vp]
+        for f in ("mk_argmax_noalloc", "mk_plan_query", "mk_decode_step", "mk_decode_step_greedy", "mk_decode_step_hidden",
                   "mk_get_device_error", "mk_argmax", "mk_plan_verify", "mk_plan_dry_run", "mk_plan_trace"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -254,6 +255,12 @@ class Plan:
 
     def argmax(self, logits, out_tokens, stream=None) -> None:
         _check(lib().mk_argmax(self._h, _ptr(logits), _ptr(out_tokens), _stream(stream)), "mk_argmax")
+
+
+def argmax_noalloc(logits, out_tokens, batch: int, vocab: int, stream=None) -> None:
+    """mk_argmax_noalloc: greedy tokens of `batch` rows of `vocab` logits, no plan, no allocation."""
+    _check(lib().mk_argmax_noalloc(_ptr(logits), int(batch), int(vocab), _ptr(out_tokens), _stream(stream)),
+           "mk_argmax_noalloc")
 
 
 def make_weights(layer_ptrs, embed=None, final_norm=None, lm_head=None) -> Weights:
