@@ -4,12 +4,18 @@ Workload (the headline): the 36-layer Qwen3-8B-shaped decoder (hidden 4096,
 32 query / 8 KV heads of 128, SwiGLU 12288, vocab 151936, bf16 weights
 ~N(0, 0.02) from a fixed seed), batch 1, a prompt of 1024 random token ids
 prefilled by teacher-forced decode steps (outside the timed region), then
-greedy decode. One timed step = one mk_decode_step (the whole step in one
-persistent launch) + mk_argmax + the caller's seq_lens increment.
+greedy decode. One timed step = one mk_decode_step_greedy launch: the
+whole step, the greedy argmax and the seq_lens increment in one persistent
+launch.
 Further numbers, reported inside the same JSON object: the same model at
 batch 16 with KV lengths log-uniform in [32, 4096] (`batch16`), at batch 8
 with a paged cache and KV lengths uniform in [4096, 16384] (`batch8_paged`),
-and one 8B-shaped layer with hidden-state input/output (`layer8b`).
+one 8B-shaped layer with hidden-state input/output, rotating over three
+weight copies so that the weights come from HBM (`layer8b`), and the tiny
+fp32 two-layer model (`tiny`, latency-bound: us/step only).
+--phases B prints instead a per-operator summary of the in-kernel task
+trace (where a step's time goes) at batch B; --cpu-extended times the oracle
+on the first steps of the batch-16 and paged workloads (all rows).
 
 Printed: ONE JSON line with tok/s (value), ms/step, HBM roofline of the
 megakernel (algorithmic bytes / average launch time from HIP events on the
@@ -87,11 +93,29 @@ def parse():
     ap.add_argument("--jit", type=int, default=0)
     ap.add_argument("--kv-chunk", type=int, default=0)
     ap.add_argument("--workers", type=int, default=0)
+    ap.add_argument("--lds-preload", type=int, default=0, help="1: preload GEMV rows into LDS pages (batch <= 2)")
     ap.add_argument("--quick", action="store_true", help="tiny prompt, few steps (profiling runs)")
+    ap.add_argument("--no-tiny", action="store_true", help="skip the tiny-model step time")
+    ap.add_argument("--phases", type=int, default=0, metavar="B",
+                    help="print the per-operator task-trace summary of the 8B model at batch B (1, 16 or 8 = paged) "
+                         "and exit")
+    ap.add_argument("--cpu-extended", action="store_true",
+                    help="time the oracle on all rows of the first steps of the batch-16 and paged workloads and exit")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="run one plain elementwise copy (torch.neg) of MIB MiB of fp32 first, untimed: the "
                          "known-size kernel that scales the FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -99,6 +123,12 @@ def main():
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.cpu_extended:
+        cpu_extended(args)
+        return
+    if args.phases:
+        phases(args)
+        return
     if args.quick:
         args.prompt, args.steps, args.warmup, args.b16_steps, args.paged_steps = 64, 8, 2, 8, 4
 
@@ -126,7 +156,8 @@ def main():
     dm = harness.DeviceModel(shape, weights, dev)
     torch.cuda.synchronize()
     log("weights uploaded in %.1fs" % (time.time() - t0))
-    opts = dict(mode=args.mode, jit=args.jit, kv_chunk=args.kv_chunk, workers=args.workers)
+    opts = dict(mode=args.mode, jit=args.jit, kv_chunk=args.kv_chunk, workers=args.workers,
+                lds_preload=args.lds_preload)
 
     # ---------------------------------------------------------------- batch 1
     B = 1
@@ -348,7 +379,11 @@ def main():
         lensL = synth.seq_lengths(wlL)
         stL = wlL.steps
         capL = int(lensL.max()) + args.warmup + stL + 8
-        dmL = harness.DeviceModel(shL, synth.model_weights(shL), dev)
+        # three copies of the layer's weights (1.16 GB), used in turn: a step
+        # never finds its weights in the 256 MB memory-side cache, so the
+        # rate is an HBM rate (the copies are equal: results do not change)
+        wL = synth.model_weights(shL)
+        dmLs = [harness.DeviceModel(shL, wL, dev) for _ in range(3)]
         kvL = harness.DeviceKV(shL, 1, capL)
         cL = synth.kv_sequence(shL, 0, int(lensL[0]), capL)
         kvL.load_sequence(0, cL["k"], cL["v"], int(lensL[0]))
@@ -357,14 +392,14 @@ def main():
         xo = torch.empty((1, shL.hidden), dtype=torch.float32, device=dev)
         d_lenL = torch.from_numpy(lensL.astype(np.int32)).to(dev)
         for t in range(args.warmup):
-            planL.step_hidden(dmL.struct, kvL.struct, xs[t], d_lenL, xo)
+            planL.step_hidden(dmLs[t % 3].struct, kvL.struct, xs[t], d_lenL, xo)
             d_lenL += 1
         torch.cuda.synchronize()
         l0 = int(d_lenL.item())
         evL = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(stL)]
         for t in range(stL):
             evL[t][0].record(st)
-            planL.step_hidden(dmL.struct, kvL.struct, xs[args.warmup + t], d_lenL, xo)
+            planL.step_hidden(dmLs[t % 3].struct, kvL.struct, xs[args.warmup + t], d_lenL, xo)
             evL[t][1].record(st)
             d_lenL += 1
         torch.cuda.synchronize()
@@ -380,9 +415,49 @@ def main():
             "value": round(float(kL.mean()) * 1e3, 2), "unit": "us/layer-step",
             "median_us": round(float(np.median(kL)) * 1e3, 2), "hbm_gbs": round(achL, 1),
             "hbm_frac": round(achL / PEAK_HBM_GBS, 4), "bytes_per_launch": int(bL),
-            "note": "386 MB of weights per step; the 256 MB memory-side cache holds part of them between steps",
+            "note": "386 MB of weights per step, three weight copies used in turn (1.16 GB): each step reads its "
+                    "weights from HBM, not from the 256 MB memory-side cache",
         }
         planL.close()
+        del dmLs
+
+    # ---------------------------------------------------------------- tiny fp32 model (latency-bound)
+    if not args.no_tiny:
+        wlT = synth.WORKLOADS["tiny"]
+        shT = wlT.shape
+        capT = wlT.capacity() + args.warmup + 8
+        lensT = synth.seq_lengths(wlT)
+        dmT = harness.DeviceModel(shT, synth.model_weights(shT), dev)
+        kvT = harness.DeviceKV(shT, 1, capT)
+        cT = synth.kv_sequence(shT, 0, int(lensT[0]), capT)
+        kvT.load_sequence(0, cT["k"], cT["v"], int(lensT[0]))
+        planT = harness.build_plan(shT, 1, capT)
+        d_tokT = torch.from_numpy(synth.tokens(wlT)).to(dev)
+        d_lenT = torch.from_numpy(lensT.astype(np.int32)).to(dev)
+        logitsT = torch.empty((1, shT.vocab), dtype=torch.float32, device=dev)
+        for _ in range(args.warmup):
+            planT.step_greedy(dmT.struct, kvT.struct, d_tokT, d_lenT, logitsT)
+        torch.cuda.synchronize()
+        evT = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(wlT.steps)]
+        e0.record(st)
+        for t in range(wlT.steps):
+            evT[t][0].record(st)
+            planT.step_greedy(dmT.struct, kvT.struct, d_tokT, d_lenT, logitsT)
+            evT[t][1].record(st)
+        e1.record(st)
+        torch.cuda.synchronize()
+        if planT.device_error():
+            raise SystemExit("device error during tiny-model steps")
+        kT = np.array([a.elapsed_time(b) for a, b in evT])
+        log("tiny: %.1f us/step (kernel median %.1f us)" % (e0.elapsed_time(e1) / wlT.steps * 1e3, np.median(kT) * 1e3))
+        result["tiny"] = {
+            "workload": "tiny: 2-layer fp32 decoder (hidden 256, 4 heads x 64, FFN 1024, vocab 1024), batch 1, "
+                        "KV 32 + warm-up, %d greedy steps" % wlT.steps,
+            "value": round(e0.elapsed_time(e1) / wlT.steps * 1e3, 2), "unit": "us/step",
+            "kernel_us_median": round(float(np.median(kT)) * 1e3, 2),
+            "note": "about 9.4 MB per step, held in caches: latency-bound, no HBM fraction",
+        }
+        planT.close()
 
     # ---------------------------------------------------------------- CPU oracle sample
     if not args.no_cpu:
@@ -407,10 +482,146 @@ def main():
             "value": round(n / dt, 4), "unit": "tokens/s", "cores": oracle.get_threads(), "kind": "oracle",
             "sample": "%d greedy decode steps of the same 36-layer model, batch 1, KV length %d..%d "
                       "(random N(0,1) KV), plain C oracle with OpenMP over output rows" % (n, kvlen, kvlen + n - 1),
+            "cpu_model": cpu_model(),
         }
         log("CPU oracle: %d steps in %.1fs (%.3f tok/s, %d threads)" % (n, dt, n / dt, oracle.get_threads()))
+        del orc, cache
+        # the oracle on one thread: the tiny model (all 16 steps) and the
+        # single 8B layer (8 steps)
+        oracle.set_threads(1)
+        single = {}
+        for name, nsteps in (("tiny", 16), ("layer8b", 8)):
+            wlS = synth.WORKLOADS[name]
+            shS = wlS.shape
+            wS = synth.model_weights(shS)
+            orcS = oracle.Oracle(shS, wS)
+            L0 = int(synth.seq_lengths(wlS)[0])
+            cS = synth.kv_sequence(shS, 0, L0, L0 + nsteps + 1)
+            t0 = time.time()
+            tokS = int(synth.tokens(wlS)[0])
+            for i in range(nsteps):
+                if shS.embed_head:
+                    tokS = int(np.argmax(orcS.model_forward(cS, tokS, L0 + i)))
+                else:
+                    orcS.hidden_forward(cS, L0 + i, synth.hidden_inputs(shS, 1, i)[0])
+            dtS = time.time() - t0
+            unit = "ms/step" if shS.embed_head else "ms/layer-step"
+            single[name] = {"value": round(dtS / nsteps * 1e3, 3), "unit": unit, "steps": nsteps}
+            log("CPU oracle, 1 thread, %s: %.3f %s" % (name, dtS / nsteps * 1e3, unit))
+        oracle.set_threads(threads)
+        result["cpu_baseline"]["single_thread"] = single
 
     print(json.dumps(result), flush=True)
+
+
+def cpu_extended(args):
+    """The oracle on all host cores for the first steps of the batch-16 and
+    paged batch-8 workloads, every row (no GPU involved)."""
+    import oracle
+    import synth
+
+    shape = synth.Q8B
+    threads = len(os.sched_getaffinity(0))
+    oracle.set_threads(threads)
+    orc = oracle.Oracle(shape, synth.model_weights(shape))
+    out = {"cpu_model": cpu_model(), "cores": oracle.get_threads()}
+    for name in ("q8b_b16", "q8b_b8_paged"):
+        wl = synth.WORKLOADS[name]
+        lens = synth.seq_lengths(wl)
+        toks = synth.tokens(wl)
+        steps = 8
+        t_all = 0.0
+        for b in range(wl.batch):
+            c = synth.kv_sequence(shape, b, int(lens[b]), int(lens[b]) + steps + 1)
+            tok = int(toks[b])
+            t0 = time.time()
+            for i in range(steps):
+                tok = int(np.argmax(orc.model_forward(c, tok, int(lens[b]) + i)))
+            t_all += time.time() - t0
+            del c
+        out[name] = {"rows": wl.batch, "steps": steps, "seconds": round(t_all, 2),
+                     "s_per_step": round(t_all / steps, 3), "tokens_per_s": round(wl.batch * steps / t_all, 3)}
+        log("CPU oracle %s: %d rows x %d steps in %.1fs" % (name, wl.batch, steps, t_all))
+    print(json.dumps({"cpu_oracle_extended": out}), flush=True)
+
+
+def phases(args):
+    """Per-operator summary of the in-kernel task trace of the 8B model: for
+    each operator, the mean over layers of the level's span (first task ready
+    to last task done) and the mean per-task times between the trace marks."""
+    import torch
+
+    import synth
+    from persistent_task_graph_amd import harness, mk
+
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    shape = synth.Q8B
+    name = {1: "q8b_b1", 16: "q8b_b16", 8: "q8b_b8_paged"}[args.phases]
+    wl = synth.WORKLOADS[name]
+    B = wl.batch
+    lens = synth.seq_lengths(wl)
+    if name == "q8b_b1":
+        lens = np.array([1100])
+    cap = int(lens.max()) + 16
+    dm = harness.DeviceModel(shape, synth.model_weights(shape), dev)
+    table = synth.block_table([cap] * B, wl.kv_block) if wl.paged else None
+    kv = harness.DeviceKV(shape, B, cap, paged=wl.paged, block=wl.kv_block, block_table=table)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(synth.SEED_KV)
+    for t in (kv.k, kv.v):
+        for l in range(t.shape[0]):
+            t[l].copy_(torch.randn(t[l].shape, generator=gen, device=dev).to(torch.bfloat16).view(torch.int16))
+    plan = harness.build_plan(shape, B, cap, paged=wl.paged, block=wl.kv_block,
+                              max_blocks=table.shape[1] if table is not None else 0, trace=4096,
+                              mode=args.mode, jit=args.jit, kv_chunk=args.kv_chunk, workers=args.workers,
+                              lds_preload=args.lds_preload)
+    d_tok = torch.from_numpy(synth.tokens(wl)).to(dev)
+    d_len = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    logits = torch.empty((B, shape.vocab), dtype=torch.float32, device=dev)
+    for _ in range(4):
+        plan.step_greedy(dm.struct, kv.struct, d_tok, d_len, logits)
+    torch.cuda.synchronize()
+    tr = plan.trace()
+    if plan.device_error():
+        raise SystemExit("device error in the traced steps")
+    ops = {mk.OP_EMBED: "embed", mk.OP_QKV: "qkv", mk.OP_ATTN: "attention", mk.OP_O: "o_proj",
+           mk.OP_GATEUP: "gate_up", mk.OP_DOWN: "down", mk.OP_LM: "lm_head"}
+    t0 = int(tr["t_wait"].min())
+    rows = {}
+    for op, nm in ops.items():
+        r = tr[tr["op"] == op]
+        if op == mk.OP_ATTN:
+            r = r[r["t_a"] > 0]  # slots the step left empty run no body
+        if len(r) == 0:
+            continue
+        # tasks of one level share the layer; group by layer through the task id
+        # order within the step: the trace holds one step, so group by t_ready clusters
+        ready = (r["t_ready"].astype(np.int64) - t0) / 100.0  # us (100 MHz ticks)
+        done = (r["t_done"].astype(np.int64) - t0) / 100.0
+        per_task = done - ready
+        rows[nm] = {"tasks": int(len(r)), "task_us_mean": round(float(per_task.mean()), 2),
+                    "task_us_p90": round(float(np.percentile(per_task, 90)), 2)}
+        # per-layer operators: the level's span, first task ready to last task
+        # done (the tasks of one layer's level are consecutive in ready order)
+        nl = shape.n_layers if nm not in ("embed", "lm_head") else 1
+        if len(r) % nl == 0:
+            order = np.argsort(ready)
+            k = len(r) // nl
+            spans = [float(done[order[i * k:(i + 1) * k]].max() - ready[order[i * k:(i + 1) * k]].min())
+                     for i in range(nl)]
+            rows[nm]["level_span_us_mean"] = round(float(np.mean(spans)), 2)
+        for a, b, key in (("t_ready", "t_a", "to_mark_a"), ("t_a", "t_b", "a_to_b"), ("t_b", "t_c", "b_to_c"),
+                          ("t_c", "t_d", "c_to_d"), ("t_d", "t_done", "d_to_done")):
+            m = (r[a] > 0) & (r[b] > 0)
+            if m.any():
+                rows[nm][key + "_us"] = round(float(((r[b][m].astype(np.int64) - r[a][m].astype(np.int64)) / 100.0).mean()), 2)
+    step_us = (int(tr["t_done"].max()) - t0) / 100.0
+    out = {"workload": name, "batch": B, "step_us_traced": round(step_us, 1), "per_op": rows,
+           "marks": {"gemv": "a operands ready, b rows done, c outputs stored, d stores complete",
+                     "attention": "a prologue done, b K/V pass done, c waves merged, d partial stored"}}
+    print(json.dumps(out, indent=1), flush=True)
+    plan.close()
 
 
 if __name__ == "__main__":

@@ -102,6 +102,13 @@ enum mk_device_error {
  *                off). Each record holds the task, the worker, and the
  *                real-time-clock ticks (100 MHz) at wait start, ready and
  *                done; read them with mk_plan_trace.
+ *  lds_preload   1: in persistent mode with ahead-of-time attention and
+ *                batch <= 2, a worker waiting for a GEMV task's event copies
+ *                the task's first rows (up to 30 KB per wave) into LDS pages
+ *                with direct-to-LDS loads and the task reads them from there
+ *                (the MPK article's paged shared memory, §3.1, and preload
+ *                during the wait, §3.2; same results). 0 (default): off; the
+ *                L2 prefetch of prefetch_kb measured faster.
  */
 typedef struct mk_exec_opts {
     int32_t mode;
@@ -118,7 +125,8 @@ typedef struct mk_exec_opts {
     int32_t prefetch_kb;
     int32_t lds_stream;
     int32_t kv_chunk_max;
-    int32_t reserved[2];
+    int32_t lds_preload;
+    int32_t reserved[1];
 } mk_exec_opts;
 
 /*

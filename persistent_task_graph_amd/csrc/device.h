@@ -87,6 +87,7 @@ struct KParams {
     int mb_mask;
     uint64_t watchdog_ticks;  // 100 MHz ticks
     int prefetch_kb;          // next-task weight bytes pulled into L2 per worker (KB)
+    int pre_slots;            // LDS preload slots per wave for the awaited GEMV task (0: off)
     int32_t* greedy_tokens;   // greedy step: next token of each sequence written here (else null)
     int32_t* greedy_lens;     // greedy step: each sequence's length advanced here
     unsigned long long* amax; // [B] packed (value, index) argmax keys; zero between steps

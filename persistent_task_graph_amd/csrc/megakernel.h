@@ -167,6 +167,8 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s, uint
     for (int qi = qb; qi < qe; ++qi) {
         const int tid_task = p.queue[qi];
         const TaskRec t = p.tasks[tid_task];
+        // the layer's weight pointers are read now, not after the event fires
+        const LayerPtrs lwt = p.lw[t.layer];
         // the next task's weight cursor is looked up now, off the critical
         // path (its table reads complete while this task waits and runs)
         if constexpr (!kStream)
@@ -192,6 +194,12 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s, uint
                 s.cmd[13] = asp;
             }
         }
+        // a GEMV task's first rows go to the LDS preload slots while it waits
+        if constexpr (!kStream && NB <= 2)
+            if (p.pre_slots > 0) {
+                preload_setup<WT>(p, t, s);
+                preload_step<WT>(s);
+            }
         const uint32_t target = waiting ? p.evrec[t.wait_ev].required * ep1 : 0u;
         uint64_t t0 = now_ticks();
         for (;;) {
@@ -232,7 +240,11 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s, uint
                     return;
                 }
                 if (cmd == 2) {
-                    if constexpr (!kStream) prefetch_step(pf);
+                    if constexpr (!kStream) {
+                        if constexpr (NB <= 2)
+                            if (p.pre_slots > 0) preload_step<WT>(s);
+                        prefetch_step(pf);
+                    }
                     __builtin_amdgcn_s_sleep(1);
                     continue;
                 }
@@ -260,7 +272,7 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s, uint
                 if (is_streamed(t.op)) run_stream_task<WT>(p, st, ring, qe, t, s);
                 else if (t.op == OP_EMBED) embed_task<WT>(p, t);
             } else {
-                run_gemv_task<WT, NB>(p, t, s);
+                run_gemv_task<WT, NB>(p, t, s, lwt, (NB <= 2 && p.pre_slots > 0) ? preload_done_rows(s) : 0);
             }
             signal_event(p, t.sig_ev, s, (int)blockIdx.x & (NP - 1));
         }
@@ -317,7 +329,8 @@ template <typename WT, int NB>
 __global__ __launch_bounds__(kThreads) void k_level_gemv(KParams p, const int32_t* ids) {
     const Lds s = carve_lds(mk_dyn_lds);
     const TaskRec t = p.tasks[ids[blockIdx.x]];
-    run_gemv_task<WT, NB>(p, t, s);
+    const LayerPtrs lwt = p.lw[t.layer];
+    run_gemv_task<WT, NB>(p, t, s, lwt);
 }
 
 template <typename WT>

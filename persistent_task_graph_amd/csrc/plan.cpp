@@ -93,6 +93,7 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
     if (p.workers < 1 || p.workers + p.sched_wgs > device_cus)
         return fail(err, "workers + sched_wgs must be in [1, CU count] (one workgroup per CU)");
     if (o.lds_stream < 0 || o.lds_stream > 1) return fail(err, "opts.lds_stream must be 0 or 1");
+    if (o.lds_preload < 0 || o.lds_preload > 1) return fail(err, "opts.lds_preload must be 0 (off) or 1 (on)");
     p.kv_chunk = o.kv_chunk > 0 ? o.kv_chunk : 128;
     if (p.kv_chunk % 16 || p.kv_chunk > 4096) return fail(err, "kv_chunk must be a multiple of 16, at most 4096");
     p.cap = d.max_seq_len;

@@ -217,6 +217,15 @@ void* persistent_kernel(const mk_plan* pl) { return kernel_for(pl, KK_PERSISTENT
 void* level_kernel(const mk_plan* pl) { return kernel_for(pl, KK_LEVEL_GEMV); }
 void* attn_kernel(const mk_plan* pl) { return kernel_for(pl, KK_LEVEL_ATTN); }
 
+// LDS preload of the awaited GEMV task's first rows (opts.lds_preload = 1):
+// persistent mode with ahead-of-time queues (no JIT task may run in the
+// wait), the batch <= 2 GEMV, not the LDS-ring variant
+bool lds_preload_on(const mk_plan* pl) {
+    const mk_model_desc& d = pl->hp.desc;
+    return d.opts.mode == MK_PERSISTENT && !pl->hp.jit && nb_for(d.batch) <= 2 && d.opts.lds_stream != 1 &&
+           d.opts.lds_preload == 1;
+}
+
 bool upload_plan(mk_plan* pl) {
     const HostPlan& hp = pl->hp;
     const mk_model_desc& d = hp.desc;
@@ -328,8 +337,10 @@ bool upload_plan(mk_plan* pl) {
     // takes more than half of the CU's LDS; other kernels reserve it dynamically
     const bool ring = nb_for(d.batch) == 1 && d.weight_dtype == MK_BF16 && d.opts.lds_stream == 1;
     pl->lds_bytes_persistent = ring ? pl->lds_bytes : std::max(pl->lds_bytes, 82 * 1024);
-    if (pl->lds_bytes_persistent > 160 * 1024) {
-        set_err("LDS need exceeds 160 KB (reduce kv_chunk)");
+    if (lds_preload_on(pl)) pl->lds_bytes_persistent = std::max(pl->lds_bytes_persistent, lds_bytes_preload());
+    // 160 KB per CU, less the statically declared prefetch sink (4 KB)
+    if (pl->lds_bytes_persistent > 156 * 1024) {
+        set_err("LDS need exceeds 156 KB of dynamic LDS (reduce kv_chunk_max)");
         return false;
     }
     void* kp = persistent_kernel(pl);
@@ -441,6 +452,7 @@ KParams make_params(const mk_plan* pl, const mk_weights* w, const mk_kv_cache* k
     const int wd = d.opts.watchdog_ms > 0 ? d.opts.watchdog_ms : 2000;
     p.watchdog_ticks = (uint64_t)wd * 100000ull;
     p.prefetch_kb = d.opts.prefetch_kb == 0 ? 256 : (d.opts.prefetch_kb < 0 ? 0 : d.opts.prefetch_kb);
+    p.pre_slots = lds_preload_on(pl) ? kPreSlots : 0;
     p.trace = pl->d_trace;
     p.trace_n = pl->d_trace_n;
     p.trace_cap = pl->trace_cap;

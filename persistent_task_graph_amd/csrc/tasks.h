@@ -29,15 +29,25 @@ struct Lds {
     float* pt;    // kWaves * 32 * 8: attention probabilities per wave [row][head]
     int* btab;    // paged cache: block-table entries of the split
     uint64_t* marks;  // 4 trace phase marks
+    uint4* pre;   // kWaves * kPreSlots: next GEMV task's weights preloaded while waiting
+    int* pst;     // kWaves * kPstInts: each wave's preload cursor
 };
 
 constexpr int kCmbSplits = 16;  // splits merged per staged chunk (one load round for up to 16)
 constexpr int kPartFloats = 8192;  // GEMV cross-wave partial sums
-constexpr int kLdsHeader = kWaves * 16 + 16 + 16 + 8;
+constexpr int kPstInts = 24;  // preload cursor of one wave (ints)
+constexpr int kLdsHeader = kWaves * 16 + 16 + 16 + 8 + kWaves * kPstInts;
 constexpr int kAttnFloats = 8 * 128 + 2 * 128 + kWaves * 8 * 128 + kWaves * 16 + 16 + kCmbSplits * (8 * 128 + 16) +
                             kWaves * 32 * 8;
 // GEMV and embedding tasks touch only the header and the partial sums
 __host__ __device__ constexpr int lds_bytes_gemv() { return 4 * (kLdsHeader + kPartFloats); }
+// Preload pages: after the partial sums, 1 KB slots per wave, each holding
+// one wave-wide 16-byte-per-lane load of the next GEMV task's weights (the
+// MPK article's paged shared memory, §3.1, filled during the wait, §3.2).
+// They overlay the attention regions, which no task uses while a worker
+// waits for a GEMV event (ahead-of-time queues only).
+constexpr int kPreSlots = 30;
+__host__ __device__ constexpr int lds_bytes_preload() { return lds_bytes_gemv() + kWaves * kPreSlots * 1024; }
 // block-table entries one split of `chunk` keys can span
 __host__ __device__ constexpr int attn_btab_ints(int chunk, int kv_block) { return chunk / kv_block + 2; }
 __host__ __device__ inline int lds_bytes_for(int chunk_max, int kv_block, bool paged) {
@@ -52,6 +62,7 @@ __device__ __forceinline__ Lds carve_lds(float* base) {
     s.cmd = (int*)p; p += 16;
     s.marks = (uint64_t*)p; p += 8;
     s.rstd = p; p += 16;
+    s.pst = (int*)p; p += kWaves * kPstInts;
     s.part = p;  // the attention regions below overlay the partial sums
     s.q = p; p += 8 * 128;
     s.kn = p; p += 2 * 128;
@@ -61,6 +72,7 @@ __device__ __forceinline__ Lds carve_lds(float* base) {
     s.cmb = p; p += kCmbSplits * (8 * 128 + 16);
     s.pt = p; p += kWaves * 32 * 8;
     s.btab = (int*)p;
+    s.pre = (uint4*)(s.part + kPartFloats);
     return s;
 }
 
@@ -152,9 +164,13 @@ __device__ __forceinline__ void block_rstd(const float* x, int ldx, int K, int B
 // are double-buffered: group i+1 is in flight while group i is consumed.
 // Rows past the tile and segments past K load through an out-of-range
 // offset (zeros, no memory traffic), so every load is issued unconditionally.
+// The first pre_rows rows of the task may already sit in this wave's LDS
+// preload slots (slot (r - r0) * NM * NSW + m * NSW + j holds what the load
+// of row r, matrix m, segment j would return); they are read from there,
+// the arithmetic is the same.
 template <typename WT, int NB, int NSW, int U, bool DUAL, typename RowFn, typename OutFn>
 __device__ __forceinline__ void gemv_ksplit(int r0, int r1, int K, const float* x, int ldx, int B, const WT* gain,
-                                            float eps, RowFn rowp, OutFn out, const Lds& s, bool tr) {
+                                            float eps, RowFn rowp, OutFn out, const Lds& s, bool tr, int pre_rows) {
     using V = Vec16<WT>;
     constexpr int E = V::N, SEG = 64 * E;
     constexpr int NM = DUAL ? 2 : 1;
@@ -181,9 +197,30 @@ __device__ __forceinline__ void gemv_ksplit(int r0, int r1, int K, const float* 
                 for (int j = 0; j < NSW; ++j) w[u][m][j] = buf_load16(rf[m].r, rv ? voff[j] : kOOB, rf[m].soff);
         }
     };
+    // preloaded rows [r0, rp) lie in the first window; their DMA loads were
+    // issued while the worker waited and have landed once this wave's loads
+    // are complete
+    const int rp = r0 + min(pre_rows, min(WIN, r1 - r0));
+    if (rp > r0) __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */
+    typedef __attribute__((address_space(3))) const u32x4 lds_u4;
+    lds_u4* pre = (lds_u4*)(s.pre + wave * (kPreSlots * 64));
+    auto lds_load = [&](uint4 (&w)[U][NM][NSW], int r, int rend) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+#pragma unroll
+                for (int j = 0; j < NSW; ++j) {
+                    // rows past rend and k past K read slot 0 and use zeros
+                    const bool ok = r + u < rend && kvalid[j];
+                    const int n = ok ? ((r + u - r0) * NM + m) * NSW + j : 0;
+                    const u32x4 v = pre[n * 64 + lane];
+                    w[u][m][j] = ok ? make_uint4(v.x, v.y, v.z, v.w) : make_uint4(0u, 0u, 0u, 0u);
+                }
+    };
     // the first weight group goes out before the (latency-bound) x loads
     uint4 wa[U][NM][NSW], wb[U][NM][NSW];
-    load(wa, r0, min(r0 + WIN, r1));
+    load(wa, rp, min(r0 + WIN, r1));
 
     // x (agent-coherent: written earlier in this step) and the norm gain
     const __amdgpu_buffer_rsrc_t xr_rs = make_rsrc(x, (uint32_t)(B * ldx) * 4u);
@@ -272,7 +309,15 @@ __device__ __forceinline__ void gemv_ksplit(int r0, int r1, int K, const float* 
     for (int rg = r0; rg < r1; rg += WIN) {
         const int rend = min(rg + WIN, r1);
         if (rg != r0) load(wa, rg, rend);
-        for (int r = rg; r < rend; r += 2 * U) {
+        int rs = rg;
+        if (rg == r0 && rp > r0) {
+            for (int r = r0; r < rp; r += U) {
+                lds_load(wb, r, rp);
+                consume(wb, r, rp, rg);
+            }
+            rs = rp;
+        }
+        for (int r = rs; r < rend; r += 2 * U) {
             load(wb, r + U, rend);
             consume(wa, r, rend, rg);
             load(wa, r + 2 * U, rend);
@@ -361,23 +406,32 @@ __device__ __forceinline__ void gemv_rowwave(int r0, int r1, int K, const float*
     }
 }
 
+// segments per wave per row of the B <= 2 GEMV for K inputs of type WT
+// (the template instance gemv_dispatch picks; the preload uses the same)
+template <typename WT>
+__host__ __device__ constexpr int ksplit_nsw(int K) {
+    constexpr int SEG = 64 * (16 / (int)sizeof(WT));
+    const int n = ((K + SEG - 1) / SEG + kWaves - 1) / kWaves;
+    return n <= 4 ? (n < 1 ? 1 : n) : (n <= 6 ? 6 : 8);
+}
+
 template <typename WT, int NB, bool DUAL, typename RowFn, typename OutFn>
 __device__ __forceinline__ void gemv_dispatch(int r0, int r1, int K, const float* x, int ldx, int B, const WT* gain,
-                                              float eps, RowFn rowp, OutFn out, const Lds& s, bool tr) {
+                                              float eps, RowFn rowp, OutFn out, const Lds& s, bool tr,
+                                              int pre_rows = 0) {
     if constexpr (NB <= 2) {
-        constexpr int SEG = 64 * Vec16<WT>::N;
         constexpr int D2 = DUAL ? 2 : 1;
-        const int nsw = ((K + SEG - 1) / SEG + kWaves - 1) / kWaves;
+        const int nsw = ksplit_nsw<WT>(K);
         // rows per group: small groups keep the fully unrolled loop short,
         // which measured faster than deeper groups for every task size here
         // (instruction fetch and fixed latencies dominate short tasks; the
         // stream of a long task is bound by HBM either way)
-        if (nsw <= 1) gemv_ksplit<WT, NB, 1, 16 / D2, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr);
-        else if (nsw <= 2) gemv_ksplit<WT, NB, 2, 2 / D2, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr);
-        else if (nsw <= 3) gemv_ksplit<WT, NB, 3, 5 / D2, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr);
-        else if (nsw <= 4) gemv_ksplit<WT, NB, 4, 4 / D2, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr);
-        else if (nsw <= 6) gemv_ksplit<WT, NB, 6, 1, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr);
-        else gemv_ksplit<WT, NB, 8, 2 / D2, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr);
+        if (nsw <= 1) gemv_ksplit<WT, NB, 1, 16 / D2, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr, pre_rows);
+        else if (nsw <= 2) gemv_ksplit<WT, NB, 2, 2 / D2, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr, pre_rows);
+        else if (nsw <= 3) gemv_ksplit<WT, NB, 3, 5 / D2, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr, pre_rows);
+        else if (nsw <= 4) gemv_ksplit<WT, NB, 4, 4 / D2, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr, pre_rows);
+        else if (nsw <= 6) gemv_ksplit<WT, NB, 6, 1, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr, pre_rows);
+        else gemv_ksplit<WT, NB, 8, 2 / D2, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr, pre_rows);
     } else {
         if (gain) block_rstd<NB>(x, ldx, K, B, eps, s);
         gemv_rowwave<WT, NB, DUAL>(r0, r1, K, x, ldx, B, gain, rowp, out);
@@ -695,8 +749,12 @@ __device__ __forceinline__ void lm_greedy(const KParams& p, int r0, int r1) {
     __hip_atomic_store(p.lm_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// w: the task's layer pointers, p.lw[t.layer] (the worker reads them before
+// the task's event fires). pre_rows: leading rows of the task whose weights
+// were preloaded into this worker's LDS slots (batch <= 2 only; 0 otherwise).
 template <typename WT, int NB>
-__device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t, const Lds& s) {
+__device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t, const Lds& s, const LayerPtrs& w,
+                                              int pre_rows = 0) {
     // bf16 weights with more than two sequences run on the matrix cores
     constexpr bool kMfma = std::is_same<WT, bf16_t>::value && NB >= 4;
     const int l = t.layer, B = p.B, H = p.H;
@@ -704,7 +762,6 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
     switch (t.op) {
         case OP_EMBED: embed_task<WT>(p, t); break;
         case OP_QKV: {
-            const LayerPtrs w = p.lw[l];
             const float* x = layer_in(p, l);
             const int QD = p.QD, KD = p.KD, ld = QD + 2 * KD;
             const MatTile<WT> tq((const WT*)w.wq, H, QD, r0, r1);
@@ -722,12 +779,11 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
                 const MSeg sg[3] = {{tq.r, tq.r, tq.n, tq.lo}, {tk.r, tk.r, tk.n, QD + tk.lo}, {tv.r, tv.r, tv.n, QD + KD + tv.lo}};
                 gemv_mfma<NB, false, 2>(sg, H, x, H, B, (const bf16_t*)w.attn_norm, p.eps, out, s, p.trace != nullptr);
             } else {
-                gemv_dispatch<WT, NB, false>(r0, r1, H, x, H, B, (const WT*)w.attn_norm, p.eps, rowp, out, s, p.trace != nullptr);
+                gemv_dispatch<WT, NB, false>(r0, r1, H, x, H, B, (const WT*)w.attn_norm, p.eps, rowp, out, s, p.trace != nullptr, pre_rows);
             }
             break;
         }
         case OP_O: {
-            const LayerPtrs w = p.lw[l];
             const float* a = layer_buf(p, l, p.off_attn);
             const float* xin = layer_in(p, l);
             float* o = layer_buf(p, l, p.off_xmid);
@@ -742,12 +798,11 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
                 const MSeg sg[1] = {{to.r, to.r, to.n, to.lo}};
                 gemv_mfma<NB, false, 1, 1, decltype(out), 3>(sg, K, a, K, B, (const bf16_t*)nullptr, p.eps, out, s, p.trace != nullptr);
             } else {
-                gemv_dispatch<WT, NB, false>(r0, r1, K, a, K, B, (const WT*)nullptr, p.eps, rowp, out, s, p.trace != nullptr);
+                gemv_dispatch<WT, NB, false>(r0, r1, K, a, K, B, (const WT*)nullptr, p.eps, rowp, out, s, p.trace != nullptr, pre_rows);
             }
             break;
         }
         case OP_GATEUP: {
-            const LayerPtrs w = p.lw[l];
             const float* x = layer_buf(p, l, p.off_xmid);
             float* o = layer_buf(p, l, p.off_h);
             const int F = p.F;
@@ -766,12 +821,11 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
                 const MSeg sg[1] = {{tg.r, tu.r, tg.n, tg.lo}};
                 gemv_mfma<NB, true, 3>(sg, H, x, H, B, (const bf16_t*)w.mlp_norm, p.eps, out, s, p.trace != nullptr);
             } else {
-                gemv_dispatch<WT, NB, true>(r0, r1, H, x, H, B, (const WT*)w.mlp_norm, p.eps, rowp, out, s, p.trace != nullptr);
+                gemv_dispatch<WT, NB, true>(r0, r1, H, x, H, B, (const WT*)w.mlp_norm, p.eps, rowp, out, s, p.trace != nullptr, pre_rows);
             }
             break;
         }
         case OP_DOWN: {
-            const LayerPtrs w = p.lw[l];
             const float* h = layer_buf(p, l, p.off_h);
             const float* xm = layer_buf(p, l, p.off_xmid);
             float* o = layer_out(p, l);
@@ -786,7 +840,7 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
                 const MSeg sg[1] = {{td.r, td.r, td.n, td.lo}};
                 gemv_mfma<NB, false, 1, 1, decltype(out), 3>(sg, F, h, F, B, (const bf16_t*)nullptr, p.eps, out, s, p.trace != nullptr);
             } else {
-                gemv_dispatch<WT, NB, false>(r0, r1, F, h, F, B, (const WT*)nullptr, p.eps, rowp, out, s, p.trace != nullptr);
+                gemv_dispatch<WT, NB, false>(r0, r1, F, h, F, B, (const WT*)nullptr, p.eps, rowp, out, s, p.trace != nullptr, pre_rows);
             }
             break;
         }
@@ -801,7 +855,7 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
                 const MSeg sg[1] = {{tl.r, tl.r, tl.n, tl.lo}};
                 gemv_mfma<NB, false, 8>(sg, H, x, H, B, (const bf16_t*)p.final_norm, p.eps, out, s, p.trace != nullptr);
             } else {
-                gemv_dispatch<WT, NB, false>(r0, r1, H, x, H, B, (const WT*)p.final_norm, p.eps, rowp, out, s, p.trace != nullptr);
+                gemv_dispatch<WT, NB, false>(r0, r1, H, x, H, B, (const WT*)p.final_norm, p.eps, rowp, out, s, p.trace != nullptr, pre_rows);
             }
             if (p.greedy_tokens) lm_greedy(p, r0, r1);
             break;
@@ -841,6 +895,151 @@ __device__ __forceinline__ void signal_event(const KParams& p, int e, const Lds&
             __hip_atomic_store(&sl->tag, pos + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
+}
+
+// ---------------------------------------------------------------- LDS preload (batch <= 2 GEMV)
+// While a worker waits for a GEMV task's event it copies the task's first
+// rows into its LDS preload slots with direct-to-LDS loads: wave w issues
+// exactly the loads its own part of the task would issue (row r, matrix m,
+// segment j: 16 bytes per lane at k = (w + 4 j) * SEG + lane * E), one slot
+// per load, in the task's order. The task then reads those rows from LDS.
+// Whole rows only, so every wave preloads the same rows.
+// The cursor of each wave lives in LDS (s.pst), not in registers: the
+// worker loop holds little state across the large task bodies, and a
+// cursor in registers spilled to scratch, whose reloads inside the poll
+// loop would wait for every load in flight. Layout (ints): next, end, r, m,
+// j, nm, nsw, nseg, K, rowbytes, lim0, lim1, then three 64-bit matrix bases
+// (rows [0, lim0), [lim0, lim1), [lim1, ..); QKV q, k, v; gate/up: gate, up).
+enum { PS_NEXT, PS_END, PS_R, PS_M, PS_J, PS_NM, PS_NSW, PS_NSEG, PS_K, PS_ROWB, PS_LIM0, PS_LIM1, PS_B0, PS_B1 = PS_B0 + 2,
+       PS_B2 = PS_B1 + 2 };
+static_assert(PS_B2 + 2 <= kPstInts, "preload cursor size");
+
+__device__ __forceinline__ bool preload_op(int op) {
+    return op == OP_QKV || op == OP_O || op == OP_GATEUP || op == OP_DOWN || op == OP_LM;
+}
+
+// inputs per row of a GEMV op's matrix
+__device__ __forceinline__ int gemv_k(const KParams& p, int op) {
+    return op == OP_O ? p.QD : (op == OP_DOWN ? p.F : p.H);
+}
+
+// rows of task t that the preload covers (0 if it does not apply: the plan
+// sets pre_slots only for batch <= 2 with ahead-of-time queues)
+template <typename WT>
+__device__ __forceinline__ int preload_rows(const KParams& p, const TaskRec& t) {
+    if (p.pre_slots <= 0 || !preload_op(t.op) || t.wait_ev < 0) return 0;
+    const int nm = t.op == OP_GATEUP ? 2 : 1;
+    const int per_row = nm * ksplit_nsw<WT>(gemv_k(p, t.op));
+    return min(t.a1 - t.a0, p.pre_slots / per_row);
+}
+
+__device__ __forceinline__ int rfl(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ const char* ps_ptr(const int* st, int i) {
+    const uint32_t lo = (uint32_t)rfl(st[i]), hi = (uint32_t)rfl(st[i + 1]);
+    return (const char*)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ void ps_put_ptr(int* st, int i, const void* v) {
+    st[i] = (int)(uint32_t)(uint64_t)v;
+    st[i + 1] = (int)(uint32_t)((uint64_t)v >> 32);
+}
+
+// Set this wave's cursor for task t (an empty cursor for tasks the preload
+// does not cover). Lane 0 writes; the wave reads it back in order.
+template <typename WT>
+__device__ __forceinline__ void preload_setup(const KParams& p, const TaskRec& t, const Lds& s) {
+    const int wave = threadIdx.x >> 6;
+    int* st = s.pst + wave * kPstInts;
+    const int rows = preload_rows<WT>(p, t);
+    if ((threadIdx.x & 63) != 0) return;
+    st[PS_NEXT] = 0;
+    if (rows <= 0) {
+        st[PS_END] = 0;
+        return;
+    }
+    const int K = gemv_k(p, t.op), nm = t.op == OP_GATEUP ? 2 : 1, nsw = ksplit_nsw<WT>(K);
+    const uint32_t rowbytes = (uint32_t)K * (uint32_t)sizeof(WT);
+    st[PS_END] = rows * nm * nsw;
+    st[PS_R] = t.a0;
+    st[PS_M] = 0;
+    st[PS_J] = 0;
+    st[PS_NM] = nm;
+    st[PS_NSW] = nsw;
+    st[PS_NSEG] = (K + 64 * Vec16<WT>::N - 1) / (64 * Vec16<WT>::N);
+    st[PS_K] = K;
+    st[PS_ROWB] = (int)rowbytes;
+    st[PS_LIM0] = st[PS_LIM1] = 1 << 30;
+    const LayerPtrs& w = p.lw[t.layer];
+    const char *b0 = nullptr, *b1 = nullptr, *b2 = nullptr;
+    switch (t.op) {
+        case OP_QKV:
+            b0 = (const char*)w.wq;
+            b1 = (const char*)w.wk - (int64_t)p.QD * rowbytes;
+            b2 = (const char*)w.wv - (int64_t)(p.QD + p.KD) * rowbytes;
+            st[PS_LIM0] = p.QD;
+            st[PS_LIM1] = p.QD + p.KD;
+            break;
+        case OP_O: b0 = (const char*)w.wo; break;
+        case OP_GATEUP:
+            b0 = (const char*)w.w_gate;
+            b1 = (const char*)w.w_up;
+            break;
+        case OP_DOWN: b0 = (const char*)w.w_down; break;
+        default: b0 = (const char*)p.lm_head; break;
+    }
+    ps_put_ptr(st, PS_B0, b0);
+    ps_put_ptr(st, PS_B1, b1);
+    ps_put_ptr(st, PS_B2, b2);
+}
+
+constexpr int kPreSlice = 6;  // slots per wave issued between two polls
+
+template <typename WT>
+__device__ __forceinline__ void preload_step(const Lds& s) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    int* st = s.pst + wave * kPstInts;
+    int next = rfl(st[PS_NEXT]);
+    const int end = rfl(st[PS_END]);
+    if (next >= end) return;
+    constexpr int E = Vec16<WT>::N;
+    int r = rfl(st[PS_R]), m = rfl(st[PS_M]), j = rfl(st[PS_J]);
+    const int nm = rfl(st[PS_NM]), nsw = rfl(st[PS_NSW]), nseg = rfl(st[PS_NSEG]), K = rfl(st[PS_K]);
+    const uint32_t rowbytes = (uint32_t)rfl(st[PS_ROWB]);
+    const int lim0 = rfl(st[PS_LIM0]), lim1 = rfl(st[PS_LIM1]);
+    const char *b0 = ps_ptr(st, PS_B0), *b1 = ps_ptr(st, PS_B1), *b2 = ps_ptr(st, PS_B2);
+    uint4* slots = s.pre + wave * (kPreSlots * 64);
+    for (int k = 0; k < kPreSlice && next < end; ++k) {
+        const int seg = wave + kWaves * j;
+        if (seg < nseg) {  // past the last segment the task loads zeros itself
+            const int kk = seg * 64 * E + lane * E;
+            const uint32_t voff = kk < K ? (uint32_t)kk * (uint32_t)sizeof(WT) : kOOB;
+            // gate/up: matrix m; QKV: the matrix holding row r
+            const char* b = nm == 2 ? (m ? b1 : b0) : (r < lim0 ? b0 : (r < lim1 ? b1 : b2));
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(b + (int64_t)r * rowbytes, rowbytes);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(slots + next * 64),
+                                                     16, voff, 0, 0, 0);
+        }
+        next++;
+        if (++j == nsw) {
+            j = 0;
+            if (++m == nm) {
+                m = 0;
+                r++;
+            }
+        }
+    }
+    if (lane == 0) {
+        st[PS_NEXT] = next;
+        st[PS_R] = r;
+        st[PS_M] = m;
+        st[PS_J] = j;
+    }
+}
+
+// rows of the task whose slots every wave has issued
+__device__ __forceinline__ int preload_done_rows(const Lds& s) {
+    const int* st = s.pst + (threadIdx.x >> 6) * kPstInts;
+    const int end = rfl(st[PS_END]);
+    return end > 0 ? rfl(st[PS_NEXT]) / (rfl(st[PS_NM]) * rfl(st[PS_NSW])) : 0;
 }
 
 // ---------------------------------------------------------------- next-task prefetch
@@ -898,6 +1097,13 @@ __device__ __forceinline__ Prefetch prefetch_setup(const KParams& p, const TaskR
         default: break;
     }
     f.end = min(f.kb_a + f.kb_b, (uint32_t)p.prefetch_kb);
+    // rows going to the LDS preload slots are not pulled into L2 as well
+    // (KB i of the stream is KB i/2 of segment i & 1 when there are two)
+    const int lds_rows = preload_rows<WT>(p, t);
+    if (lds_rows > 0) {
+        const uint32_t kb = (uint32_t)lds_rows * (uint32_t)gemv_k(p, t.op) * (uint32_t)es / 1024u * (f.kb_b ? 2u : 1u);
+        f.next = min(kb, f.end);
+    }
     return f;
 }
 

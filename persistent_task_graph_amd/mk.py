@@ -33,8 +33,8 @@ EXPORTS = ["mk_build_graph", "mk_destroy_plan", "mk_last_error", "mk_plan_query"
 class ExecOpts(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("mode", "workers", "sched_wgs", "jit", "kv_chunk", "watchdog_ms",
                                                "host_only", "device_cus", "debug_event", "debug_extra_required",
-                                               "trace", "prefetch_kb", "lds_stream", "kv_chunk_max")] + \
-               [("reserved", ctypes.c_int32 * 2)]
+                                               "trace", "prefetch_kb", "lds_stream", "kv_chunk_max", "lds_preload")] + \
+               [("reserved", ctypes.c_int32 * 1)]
 
 
 class ModelDesc(ctypes.Structure):

@@ -248,14 +248,16 @@ def test_mid_adaptive_chunk_matches_oracle_and_modes(mid_weights):
     assert worst_d <= 2e-2
 
 
-def test_mid_b1_variants_bitwise(mid_weights):
-    log("mid bf16 B=1: register GEMV vs LDS-ring streaming vs kernel-per-op vs no prefetch")
-    s = make_setup(MID, 1, [517], 540, weights=mid_weights)
+@pytest.mark.parametrize("B", [1, 2])
+def test_mid_b1_variants_bitwise(mid_weights, B):
+    log("mid bf16 B=%d: register GEMV vs LDS preload vs LDS-ring streaming vs kernel-per-op vs no prefetch" % B)
+    s = make_setup(MID, B, [517, 300][:B], 540, weights=mid_weights)
     a, _ = _logits_seq(s, 3)
-    b, _ = _logits_seq(s, 3, lds_stream=1)
-    c, _ = _logits_seq(s, 3, mode=1)
-    d, _ = _logits_seq(s, 3, prefetch_kb=-1)
-    for o in (b, c, d):
+    variants = [dict(lds_preload=1), dict(mode=1), dict(prefetch_kb=-1), dict(lds_preload=1, prefetch_kb=-1)]
+    if B == 1:
+        variants.append(dict(lds_stream=1))
+    for v in variants:
+        o, _ = _logits_seq(s, 3, **v)
         _bitwise(a, o)
 
 
