@@ -87,6 +87,8 @@ def parse():
     ap.add_argument("--no-ablation", action="store_true",
                     help="skip the JIT-scheduler and kernel-per-op step times at batch 1 and 16")
     ap.add_argument("--ablation-steps", type=int, default=32)
+    ap.add_argument("--multi-step", type=int, default=16, metavar="N",
+                    help="also time the batch-1 decode with N greedy steps per launch (0: skip)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--mode", type=int, default=0, help="0 persistent, 1 kernel-per-op")
@@ -162,7 +164,8 @@ def main():
     # ---------------------------------------------------------------- batch 1
     B = 1
     n_abl = 0 if args.no_ablation else 2 * (args.ablation_steps + 4)
-    cap = args.prompt + args.warmup + args.steps + n_abl + 8
+    n_multi = 0 if args.multi_step <= 0 else args.multi_step * (1 + max(1, args.steps // args.multi_step))
+    cap = args.prompt + args.warmup + args.steps + n_abl + n_multi + 8
     kv = harness.DeviceKV(shape, B, cap)
     plan = harness.build_plan(shape, B, cap, **opts)
     info = plan.info()
@@ -235,6 +238,30 @@ def main():
     tok_s = B * args.steps / (total_ms * 1e-3)
     log("B=1: %.3f ms/step (kernel avg %.3f, median %.3f, p99 %.3f), %.1f tok/s, %.0f GB/s = %.1f%% of 8 TB/s"
         % (ms_per_step, k_avg, np.median(k_ms), np.percentile(k_ms, 99), tok_s, achieved, 100 * achieved / PEAK_HBM_GBS))
+    multi = None
+    if args.multi_step > 0:
+        # the same decode with N greedy steps per launch (tokens and lengths
+        # fed forward on the device): one warm-up launch, then the timed ones
+        N = args.multi_step
+        nl = max(1, args.steps // N)
+        out_tok = torch.empty((N, B), dtype=torch.int32, device=dev)
+        plan.steps_greedy(dm.struct, kv.struct, d_tok, d_len, logits, N, out_tok)
+        torch.cuda.synchronize()
+        lenm = int(d_len.item())
+        e0.record(st)
+        for _ in range(nl):
+            plan.steps_greedy(dm.struct, kv.struct, d_tok, d_len, logits, N, out_tok)
+        e1.record(st)
+        torch.cuda.synchronize()
+        if plan.device_error():
+            raise SystemExit("device error in the multi-step launches")
+        ms_m = e0.elapsed_time(e1) / (nl * N)
+        bytes_m = float(np.mean([harness.step_bytes(shape, [lenm + i], B) for i in range(nl * N)]))
+        multi = {"steps_per_launch": N, "launches": nl, "ms_per_step": round(ms_m, 4),
+                 "value": round(B / (ms_m * 1e-3), 2), "unit": "tokens/s", "kv_len_start": lenm,
+                 "hbm_gbs": round(bytes_m / (ms_m * 1e-3) / 1e9, 1),
+                 "hbm_frac": round(bytes_m / (ms_m * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        log("B=1, %d steps per launch: %.3f ms/step, %.1f tok/s" % (N, ms_m, B / (ms_m * 1e-3)))
     plan.close()
     abl1 = None
     if not args.no_ablation:
@@ -273,6 +300,8 @@ def main():
     }
     if abl1 is not None:
         result["ablation_b1"] = abl1
+    if multi is not None:
+        result["multi_step_b1"] = multi
 
     # ---------------------------------------------------------------- batch 16
     if not args.no_b16:

@@ -285,6 +285,29 @@ int mk_decode_step_greedy(mk_plan* plan, const mk_weights* weights, const mk_kv_
                           int32_t* seq_lens, float* logits, void* stream);
 
 /*
+ * n_steps greedy decode steps in one persistent launch: the same as calling
+ * mk_decode_step_greedy n_steps times (same tokens, lengths and, for the
+ * last step, logits, bit for bit), with the next token fed to the next step
+ * on the device and the events' epochs advanced there (the MPK article,
+ * §2.1: the whole computation in one kernel, no per-step launch, §1).
+ *  tokens, seq_lens  as mk_decode_step_greedy; on return they hold the last
+ *                    step's tokens and seq_lens[b] + n_steps.
+ *  logits            device float [batch, vocab]: the last step's logits.
+ *  n_steps           1 .. 4096 (MK_ERR_ARG outside). Every step must fit the
+ *                    KV capacity (seq_lens[b] + n_steps <= max_seq_len), else
+ *                    the device reports MK_ERR_KV_OVERFLOW for those steps.
+ *  out_tokens        device int32 [n_steps, batch] or NULL: step s's tokens
+ *                    at out_tokens[s * batch + b].
+ * Persistent mode needs ahead-of-time attention (opts.jit 0 or 2) and no
+ * lds_stream for n_steps > 1 (MK_ERR_UNSUPPORTED otherwise); kernel-per-op
+ * mode runs the steps as consecutive level launches. Between two steps every
+ * worker waits at a device-wide step barrier released by the last worker to
+ * finish the step, which writes that step's tokens and lengths.
+ */
+int mk_decode_steps_greedy(mk_plan* plan, const mk_weights* weights, const mk_kv_cache* kv, int32_t* tokens,
+                           int32_t* seq_lens, float* logits, int32_t n_steps, int32_t* out_tokens, void* stream);
+
+/*
  * Hidden-state variant for hidden_io plans: x_in, x_out are device float
  * [batch, hidden] (they may not alias); otherwise as mk_decode_step. It runs
  * the decoder layers only (the Ada-MK summary, gist.science, "Methodik" 1:

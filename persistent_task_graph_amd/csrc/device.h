@@ -90,6 +90,8 @@ struct KParams {
     int pre_slots;            // LDS preload slots per wave for the awaited GEMV task (0: off)
     int32_t* greedy_tokens;   // greedy step: next token of each sequence written here (else null)
     int32_t* greedy_lens;     // greedy step: each sequence's length advanced here
+    int32_t* out_tokens;      // greedy steps: step s's tokens at [s * B, s * B + B) (or null)
+    int n_steps;              // greedy decode steps this launch runs (1 unless multi-step)
     unsigned long long* amax; // [B] packed (value, index) argmax keys; zero between steps
     uint32_t* lm_done;        // kernel-per-op greedy step: LM-head tasks finished (reset by the last)
     uint32_t* exit_cnt;       // persistent greedy step: workers that left their queue (reset by the last)
@@ -288,6 +290,7 @@ __device__ __forceinline__ float ld_co(const float* p) { return __hip_atomic_loa
 __device__ __forceinline__ int ld_co(const int* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 __device__ __forceinline__ void st_co(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 __device__ __forceinline__ void st_co(int* p, int v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ void st_co(uint16_t* p, uint16_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
 __device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
 

@@ -137,7 +137,6 @@ template <typename WT, int NB>
 __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s, uint4* ring_mem) {
     const int w = blockIdx.x;
     const int qb = p.qoff[w], qe = p.qoff[w + 1];
-    const uint32_t ep1 = p.epoch + 1u;
     constexpr int NP = ev_planes(NB);  // event-count planes this instance uses
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     if (p.trace && threadIdx.x == 0) {
@@ -145,7 +144,6 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s, uint
         s.marks[0] = s.marks[1] = s.marks[2] = s.marks[3] = 0;
     }
     int64_t head = (threadIdx.x == 0 && p.jit_on) ? p.inbox_head[w] : 0;
-    int chunk = 0;  // the step's attention chunk, found before the first attention task
     // optional batch-1 variant: weight pages stream through a per-wave LDS
     // ring fed by direct-to-LDS loads (stream.h) instead of registers
     constexpr bool kStream = kLdsStream && NB == 1;
@@ -158,6 +156,12 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s, uint
         loader_seek<WT>(p, st, qb, qe, wave);
         loader_fill<WT>(p, st, 0, qe, wave, lane);
     }
+    // Several greedy decode steps may run in one launch (the MPK article,
+    // §2.1: the whole computation in one kernel): step s waits on events at
+    // epoch + s and starts once step s - 1 has written its tokens and lengths.
+    for (int step = 0; step < p.n_steps; ++step) {
+    const uint32_t ep1 = p.epoch + (uint32_t)step + 1u;
+    int chunk = 0;  // the step's attention chunk, found before the first attention task
     Prefetch pf;
     pf.next = pf.end = 0;
     if constexpr (!kStream)
@@ -284,21 +288,45 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s, uint
         }
         trace_put(p, s, 0, tid_task, t.op, tw, tr);
     }
-    if (threadIdx.x == 0 && p.jit_on) p.inbox_head[w] = head;
-    if constexpr (kStream) wait_vm<0>();
     if (p.greedy_tokens) {
         // greedy step: the last worker to leave its queue writes the next
-        // tokens and advances the lengths; no worker reads them after this
+        // tokens and advances the lengths (no worker reads them any more in
+        // this step), then releases the step
         wait_stores();
         __syncthreads();
         if (threadIdx.x == 0) {
             const uint32_t old = __hip_atomic_fetch_add(p.exit_cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (old + 1u == (uint32_t)p.n_workers) {
-                greedy_finish(p);
+                greedy_finish(p, step);
                 __hip_atomic_store(p.exit_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                wait_stores();
+                __hip_atomic_store(&p.ctrl->step_done, ep1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
+        if (step + 1 < p.n_steps) {
+            // step barrier: wait for the release, then drop cached lines of
+            // this launch's earlier steps (activations, tokens, lengths) as
+            // the kernel entry does for earlier launches
+            if (threadIdx.x == 0) {
+                const uint64_t tb = now_ticks();
+                int c = 0;
+                while ((int32_t)(ld_relaxed(&p.ctrl->step_done) - ep1) < 0) {
+                    if (aborted(p.ctrl)) { c = 1; break; }
+                    if (now_ticks() - tb > p.watchdog_ticks) { raise_abort(p.ctrl); c = 1; break; }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                s.cmd[0] = c;
+            }
+            __syncthreads();
+            const int c = s.cmd[0];
+            __syncthreads();
+            if (c) break;
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
     }
+    }  // step
+    if (threadIdx.x == 0 && p.jit_on) p.inbox_head[w] = head;
+    if constexpr (kStream) wait_vm<0>();
 }
 
 extern __shared__ __attribute__((aligned(16))) float mk_dyn_lds[];

@@ -62,7 +62,9 @@ struct RingSlot {
 struct Ctrl {
     uint32_t error;      // sticky mk_device_error bits
     uint32_t abort;      // set when any wait times out; all loops exit
-    uint32_t pad0[14];
+    uint32_t pad00[14];
+    uint32_t step_done;  // greedy steps: epoch + 1 of the last step whose tokens and lengths are written
+    uint32_t pad0[15];
     int64_t rr;          // round-robin position for dealing JIT tasks to worker inboxes
     int64_t pad1[7];
     int64_t pad2[8];

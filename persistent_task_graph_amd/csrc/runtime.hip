@@ -194,6 +194,8 @@ bool hip_ok(hipError_t e, const char* what) {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+constexpr int kMaxStepsPerLaunch = 4096;
+
 int nb_for(int B) { return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : B <= 8 ? 8 : 16; }
 
 void* kernel_for(const mk_plan* pl, int kind) {
@@ -370,6 +372,7 @@ KParams make_params(const mk_plan* pl, const mk_weights* w, const mk_kv_cache* k
     const HostPlan& hp = pl->hp;
     const mk_model_desc& d = hp.desc;
     KParams p{};
+    p.n_steps = 1;
     p.tasks = pl->d_tasks;
     p.qoff = pl->d_qoff;
     p.queue = pl->d_queue;
@@ -514,15 +517,19 @@ int sync_pointer_table(mk_plan* pl, const mk_weights* w, hipStream_t st) {
     return MK_OK;
 }
 
+// One step (n_steps = 1) or, with the greedy choice, n_steps greedy steps:
+// one persistent launch, or n_steps rounds of kernel-per-op level launches.
 int launch_step(mk_plan* pl, const mk_weights* w, const mk_kv_cache* kv, const int32_t* tokens, const int32_t* seq_lens,
                 const float* x_in, float* out, hipStream_t st, int32_t* greedy_tokens = nullptr,
-                int32_t* greedy_lens = nullptr) {
+                int32_t* greedy_lens = nullptr, int n_steps = 1, int32_t* out_tokens = nullptr) {
     if (!hip_ok(hipSetDevice(pl->device), "hipSetDevice")) return MK_ERR_HIP;
     int rc = sync_pointer_table(pl, w, st);
     if (rc) return rc;
     KParams p = make_params(pl, w, kv, tokens, seq_lens, x_in, out);
     p.greedy_tokens = greedy_tokens;
     p.greedy_lens = greedy_lens;
+    p.out_tokens = out_tokens;
+    p.n_steps = n_steps;
     const HostPlan& hp = pl->hp;
     if (hp.desc.opts.mode == MK_PERSISTENT) {
         void* args[] = {&p};
@@ -530,9 +537,12 @@ int launch_step(mk_plan* pl, const mk_weights* w, const mk_kv_cache* kv, const i
                                                pl->lds_bytes_persistent, st),
                     "hipLaunchCooperativeKernel"))
             return MK_ERR_HIP;
-        pl->epoch++;
+        pl->epoch += (uint32_t)n_steps;
         return MK_OK;
     }
+    p.n_steps = 1;
+    for (int step = 0; step < n_steps; ++step) {
+    p.out_tokens = out_tokens ? out_tokens + (int64_t)step * hp.desc.batch : nullptr;
     for (int lv = 0; lv < hp.n_levels; ++lv) {
         const int op = hp.level_op[lv];
         if (op == OP_ATTN) {
@@ -552,6 +562,7 @@ int launch_step(mk_plan* pl, const mk_weights* w, const mk_kv_cache* kv, const i
                 return MK_ERR_HIP;
         }
     }
+    }  // step
     return MK_OK;
 }
 
@@ -645,6 +656,20 @@ int mk_decode_step_greedy(mk_plan* pl, const mk_weights* w, const mk_kv_cache* k
     if (rc) return rc;
     if (pl->hp.desc.hidden_io) return set_err("hidden_io plan has no logits"), MK_ERR_STATE;
     return launch_step(pl, w, kv, tokens, seq_lens, nullptr, logits, (hipStream_t)stream, tokens, seq_lens);
+}
+
+int mk_decode_steps_greedy(mk_plan* pl, const mk_weights* w, const mk_kv_cache* kv, int32_t* tokens,
+                           int32_t* seq_lens, float* logits, int32_t n_steps, int32_t* out_tokens, void* stream) {
+    int rc = check_step_args(pl, w, kv, seq_lens, tokens, logits);
+    if (rc) return rc;
+    if (pl->hp.desc.hidden_io) return set_err("hidden_io plan has no logits"), MK_ERR_STATE;
+    if (n_steps < 1 || n_steps > kMaxStepsPerLaunch)
+        return set_err("n_steps must be in [1, " + std::to_string(kMaxStepsPerLaunch) + "]"), MK_ERR_ARG;
+    if (pl->hp.desc.opts.mode == MK_PERSISTENT && n_steps > 1 && (pl->hp.jit || pl->hp.desc.opts.lds_stream == 1))
+        return set_err("several steps per launch need ahead-of-time attention (opts.jit 0 or 2, no lds_stream)"),
+               MK_ERR_UNSUPPORTED;
+    return launch_step(pl, w, kv, tokens, seq_lens, nullptr, logits, (hipStream_t)stream, tokens, seq_lens, n_steps,
+                       out_tokens);
 }
 
 int mk_decode_step_hidden(mk_plan* pl, const mk_weights* w, const mk_kv_cache* kv, const float* x_in,

@@ -699,13 +699,18 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, int i) {
 }
 
 // Greedy step, end: turn each sequence's argmax key into its next token,
-// reset the key and advance the sequence's length. Runs once per step, on
-// one thread, after every reader of the step's lengths has finished.
-__device__ __forceinline__ void greedy_finish(const KParams& p) {
+// reset the key and advance the sequence's length; step `step` of a
+// multi-step launch also records the tokens in out_tokens. Runs once per
+// step, on one thread, after every reader of the step's lengths has
+// finished. Agent-coherent stores: the next step of the same launch reads
+// tokens and lengths on other CUs.
+__device__ __forceinline__ void greedy_finish(const KParams& p, int step) {
     for (int b = 0; b < p.B; ++b) {
         const unsigned long long k = __hip_atomic_exchange(&p.amax[b], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        p.greedy_tokens[b] = k ? (int32_t)(0xFFFFFFFFu - (uint32_t)k) : 0;
-        p.greedy_lens[b] += 1;
+        const int32_t tok = k ? (int32_t)(0xFFFFFFFFu - (uint32_t)k) : 0;
+        st_co(&p.greedy_tokens[b], tok);
+        st_co(&p.greedy_lens[b], __hip_atomic_load(&p.greedy_lens[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1);
+        if (p.out_tokens) p.out_tokens[(int64_t)step * p.B + b] = tok;
     }
 }
 
@@ -745,7 +750,7 @@ __device__ __forceinline__ void lm_greedy(const KParams& p, int r0, int r1) {
     if (p.persistent || tid != 0) return;
     const uint32_t old = __hip_atomic_fetch_add(p.lm_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old + 1u != (uint32_t)p.n_lm_tasks) return;
-    greedy_finish(p);
+    greedy_finish(p, 0);
     __hip_atomic_store(p.lm_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -1376,7 +1381,9 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
 #pragma unroll
         for (int i = 0; i < D / 64; ++i) {
             const WT c = from_float<WT>(nv[i]);
-            if (off >= 0) dst[lane + 64 * i] = c;  // a bad block-table entry: nothing is written
+            // agent-coherent: a later step of the same launch may read the row on
+            // another CU (a bad block-table entry: nothing is written)
+            if (off >= 0) st_co(&dst[lane + 64 * i], c);
             s.kn[wave * 128 + lane + 64 * i] = to_float<WT>(c);
         }
     }

@@ -27,7 +27,7 @@ OP_QKV, OP_O, OP_GATEUP, OP_DOWN, OP_LM, OP_ATTN, OP_EMBED = 1, 2, 3, 4, 5, 6, 7
 
 EXPORTS = ["mk_build_graph", "mk_destroy_plan", "mk_last_error", "mk_plan_query", "mk_decode_step",
            "mk_decode_step_greedy", "mk_decode_step_hidden", "mk_get_device_error", "mk_argmax", "mk_plan_verify", "mk_plan_dry_run",
-           "mk_plan_trace", "mk_argmax_noalloc"]
+           "mk_plan_trace", "mk_argmax_noalloc", "mk_decode_steps_greedy"]
 
 
 class ExecOpts(ctypes.Structure):
@@ -106,7 +106,8 @@ def lib() -> ctypes.CDLL:
         L.mk_plan_dry_run.argtypes = [vp, i32, ctypes.c_uint64, i32, i32, vp]
         L.mk_plan_trace.argtypes = [vp, vp, ctypes.c_int64, vp]
         L.mk_argmax_noalloc.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp, vp]
-        for f in ("mk_argmax_noalloc", "mk_plan_query", "mk_decode_step", "mk_decode_step_greedy", "mk_decode_step_hidden",
+        L.mk_decode_steps_greedy.argtypes = [vp, P(Weights), P(KVCache), vp, vp, vp, ctypes.c_int32, vp, vp]
+        for f in ("mk_argmax_noalloc", "mk_decode_steps_greedy", "mk_plan_query", "mk_decode_step", "mk_decode_step_greedy", "mk_decode_step_hidden",
                   "mk_get_device_error", "mk_argmax", "mk_plan_verify", "mk_plan_dry_run", "mk_plan_trace"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -233,6 +234,13 @@ class Plan:
         """One step; tokens become the greedy next tokens and seq_lens advance by one, in the same launch."""
         _check(lib().mk_decode_step_greedy(self._h, ctypes.byref(weights), ctypes.byref(kv), _ptr(tokens),
                                            _ptr(seq_lens), _ptr(logits), _stream(stream)), "mk_decode_step_greedy")
+
+    def steps_greedy(self, weights: "Weights", kv: "KVCache", tokens, seq_lens, logits, n_steps: int,
+                     out_tokens=None, stream=None) -> None:
+        """n_steps greedy steps in one launch; out_tokens [n_steps, batch] receives each step's tokens."""
+        _check(lib().mk_decode_steps_greedy(self._h, ctypes.byref(weights), ctypes.byref(kv), _ptr(tokens),
+                                            _ptr(seq_lens), _ptr(logits), int(n_steps), _ptr(out_tokens),
+                                            _stream(stream)), "mk_decode_steps_greedy")
 
     def step_hidden(self, weights: "Weights", kv: "KVCache", x_in, seq_lens, x_out, stream=None) -> None:
         _check(lib().mk_decode_step_hidden(self._h, ctypes.byref(weights), ctypes.byref(kv), _ptr(x_in),

@@ -381,3 +381,43 @@ def test_block_table_entry_outside_pool_is_reported(mid_weights):
     plan.step(s.dm.struct, kv.struct, tok, d_len, logits)
     assert plan.device_error() == 0
     plan.close()
+
+
+@pytest.mark.parametrize("case", ["tiny", "mid3", "mid16", "mid4_paged", "mid3_per_op"])
+def test_multi_step_launch_equals_repeated_greedy_steps(tiny, mid_weights, case):
+    # n greedy steps in one launch give, bit for bit, the tokens of each step,
+    # the final lengths and the last step's logits of n separate greedy steps
+    import torch
+
+    opts = {}
+    if case == "tiny":
+        s, n = tiny, 6
+    else:
+        B = int("".join(ch for ch in case[3:] if ch.isdigit()))
+        paged = case.endswith("paged")
+        lens = [int(v) for v in np.linspace(3, 700, B)]
+        cap = max(lens) + 16
+        table = synth.block_table([cap] * B, 16) if paged else None
+        s = make_setup(MID, B, lens, cap, weights=mid_weights, paged=paged, table=table)
+        n = 4 if B < 16 else 3
+        if case.endswith("per_op"):
+            opts = {"mode": 1}
+    log("multi-step launch vs %d greedy steps: %s" % (n, case))
+    t0 = _tokens(s.shape, s.B, 6)
+    ref, ref_lens = _greedy_seq(s, n, t0, **opts)
+    plan = plan_for(s, **opts)
+    kv = device_kv(s)
+    tok = torch.from_numpy(t0.astype(np.int32)).cuda()
+    d_len = torch.from_numpy(s.lens.astype(np.int32)).cuda()
+    logits = torch.empty((s.B, s.shape.vocab), dtype=torch.float32, device="cuda")
+    out = torch.full((n, s.B), -1, dtype=torch.int32, device="cuda")
+    plan.steps_greedy(s.dm.struct, kv.struct, tok, d_len, logits, n, out)
+    torch.cuda.synchronize()
+    assert plan.device_error() == 0
+    got = out.cpu().numpy()
+    for i, (fed, lg, nxt) in enumerate(ref):
+        assert np.array_equal(got[i], nxt), (i, got[i], nxt)
+    assert np.array_equal(tok.cpu().numpy(), ref[-1][2])
+    assert np.array_equal(d_len.cpu().numpy(), ref_lens)
+    assert np.array_equal(logits.cpu().numpy().view(np.uint32), ref[-1][1].view(np.uint32))
+    plan.close()
