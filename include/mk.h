@@ -109,6 +109,17 @@ enum mk_device_error {
  *                (the MPK article's paged shared memory, §3.1, and preload
  *                during the wait, §3.2; same results). 0 (default): off; the
  *                L2 prefetch of prefetch_kb measured faster.
+ *  schedule      0 (default): the event runtime above. 1: static schedule
+ *                (the Ada-MK articles, gist.science "Methodik" 1, zingnex.cn
+ *                技术二: offline search, fixed execution path): the planner
+ *                searches the task count of every GEMV operator and the
+ *                attention split length under a cost model, layer by layer
+ *                with pruning, places tasks longest first on the least-loaded
+ *                worker and fixes every attention split task to its
+ *                (sequence, KV head, split) of the whole capacity; kv_chunk
+ *                and kv_chunk_max are replaced by the searched length. Same
+ *                task bodies: the bits of the event runtime at that length.
+ *                Not with jit = 1.
  */
 typedef struct mk_exec_opts {
     int32_t mode;
@@ -126,7 +137,7 @@ typedef struct mk_exec_opts {
     int32_t lds_stream;
     int32_t kv_chunk_max;
     int32_t lds_preload;
-    int32_t reserved[1];
+    int32_t schedule;
 } mk_exec_opts;
 
 /*
@@ -210,7 +221,8 @@ typedef struct mk_plan_info {
     int64_t weight_bytes_per_step; /* weight bytes one step streams (matrices, gains, LM head) */
     int64_t kv_bytes_per_token;    /* K + V bytes per cached position over all layers */
     int64_t device_bytes;          /* device memory the plan owns */
-    int32_t jit, mode, host_only, reserved;
+    int32_t jit, mode, host_only, schedule;
+    double predicted_layer_us;     /* static schedule: the cost model's time of one layer (0 otherwise) */
 } mk_plan_info;
 
 /*

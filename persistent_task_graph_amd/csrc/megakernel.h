@@ -190,8 +190,8 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s, uint
         // leaves empty
         if (aot_attn) {
             if (chunk == 0) chunk = attn_chunk(p);
-            int abg, asp;
-            if (!attn_locate(p, chunk, t.a0, abg, asp)) abg = -1;
+            int abg = t.a0, asp = t.a1;  // a static-schedule task carries its split
+            if (!(t.flags & kTaskStaticAttn) && !attn_locate(p, chunk, t.a0, abg, asp)) abg = -1;
             else if constexpr (!kStream) pf = attn_prefetch_setup<WT>(p, t.layer, abg, asp, chunk);
             if (threadIdx.x == 0) {
                 s.cmd[12] = abg;

@@ -41,6 +41,9 @@ struct TaskRec {
     int32_t pad[2];
 };
 static_assert(sizeof(TaskRec) == 32, "TaskRec size");
+// TaskRec.flags: an attention task of the static schedule, fixed to
+// (b * n_kv_heads + g = a0, split = a1)
+constexpr uint8_t kTaskStaticAttn = 1;
 
 // Event record (the article's Event, §2.1): the counter itself lives in a
 // separate uint32 array and only grows; step e is complete for this event
@@ -81,6 +84,8 @@ struct HostPlan {
     int workers = 0;
     int sched_wgs = 0;
     int jit = 1;  // 1 JIT, 0 AOT attention
+    int schedule = 0;  // 0 event runtime, 1 static (searched) schedule
+    double predicted_layer_us = 0;  // static schedule: cost-model time of one layer
     int kv_chunk = 256;     // base keys per split (sizes the partial records)
     int kv_chunk_max = 4096; // largest per-step chunk
     int attn_target = 0;    // split tasks per step above which the chunk doubles

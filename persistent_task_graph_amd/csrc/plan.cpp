@@ -45,6 +45,132 @@ static int64_t op_rows(const mk_model_desc& d, int op) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Static schedule (opts.schedule = 1): an offline search fixes the tiling and
+// the per-worker task order before any step runs (the Ada-MK articles,
+// gist.science "Methodik" 1 and zingnex.cn 技术二: a DAG-level offline search
+// with pruning, searched layer by layer under a cost model, whose result is
+// frozen so that no runtime scheduling decision remains). Here the searched
+// variables are the number of tasks of each GEMV operator (their rows are cut
+// evenly, in 16-row tiles on the matrix-core path) and the attention split
+// length, which must cover the plan's whole KV capacity because the split
+// tasks are placed before any sequence length is known; tasks are placed on
+// workers longest first onto the least-loaded worker (LPT). The task bodies
+// are the event runtime's, so the two give the same bits at the same split
+// length.
+//
+// Cost model (microseconds; calibrated on the per-operator trace of the 8B
+// model on one MI355X): a GEMV task costs a fixed kLamGemv (event seen,
+// operands issued, cross-wave reduction, stores, completion signal) plus its
+// weight bytes at kRateW per worker plus the activation bytes it reads at
+// kRateAct (once per pass of its matrix-core tiles); an attention split task
+// costs kLamAttn plus its K/V bytes at kRateKV; every level adds one event
+// hop kHop. A level lasts as long as its most loaded worker.
+namespace {
+constexpr double kLamGemv = 4.5, kRateW = 28000.0, kRateAct = 60000.0;  // us, bytes/us
+constexpr double kLamAttn = 9.0, kRateKV = 20000.0, kHop = 2.0;
+
+struct StaticChoice {
+    int tasks[kNumOps] = {0};  // tasks per GEMV operator
+    int chunk = 0;             // attention split length
+    double predicted_us = 0;   // cost-model time of one layer
+};
+
+// cost of the most loaded worker when `costs` are placed longest first
+double lpt_span(std::vector<double> costs, int W) {
+    std::sort(costs.begin(), costs.end(), [](double a, double b) { return a > b; });
+    std::vector<double> load(W, 0.0);
+    double span = 0;
+    for (double c : costs) {
+        int best = 0;
+        for (int w = 1; w < W; ++w)
+            if (load[w] < load[best]) best = w;
+        load[best] += c;
+        span = std::max(span, load[best]);
+    }
+    return span;
+}
+
+// rows cut evenly into n tasks; on the matrix-core path (batch >= 3, bf16)
+// the cuts fall on 16-row tile boundaries
+std::vector<std::pair<int, int>> cut_rows(int64_t rows, int64_t n, bool tiles) {
+    std::vector<std::pair<int, int>> r;
+    const int64_t unit = tiles ? 16 : 1;
+    const int64_t units = (rows + unit - 1) / unit;
+    n = std::max<int64_t>(1, std::min(n, units));
+    for (int64_t i = 0; i < n; ++i) {
+        const int64_t a = std::min(rows, i * units / n * unit), b = std::min(rows, (i + 1) * units / n * unit);
+        if (b > a) r.push_back({(int)a, (int)b});
+    }
+    return r;
+}
+
+// matrix-core tiles a task runs per pass (the task bodies' fixed counts)
+int mfma_tiles_per_pass(int op) { return op == OP_QKV ? 2 : op == OP_GATEUP ? 3 : op == OP_LM ? 8 : 1; }
+
+double gemv_level_cost(const mk_model_desc& d, int op, int n, int W) {
+    const int64_t rows = op_rows(d, op);
+    const int64_t K = op == OP_O ? (int64_t)d.n_heads * d.head_dim : op == OP_DOWN ? d.ffn : d.hidden;
+    const int es = d.weight_dtype == MK_BF16 ? 2 : 4, nm = op == OP_GATEUP ? 2 : 1;
+    const bool mf = d.weight_dtype == MK_BF16 && d.batch >= 3;
+    std::vector<double> c;
+    for (auto& r : cut_rows(rows, n, mf)) {
+        const int64_t nr = r.second - r.first;
+        const int passes = mf ? (int)(((nr + 15) / 16 + mfma_tiles_per_pass(op) - 1) / mfma_tiles_per_pass(op)) : 1;
+        c.push_back(kLamGemv + (double)(nr * K * es * nm) / kRateW + (double)(passes * d.batch * K * 4) / kRateAct);
+    }
+    return lpt_span(c, W) + kHop;
+}
+
+double attn_level_cost(const mk_model_desc& d, int cap, int C, int W) {
+    const int64_t splits = (cap + C - 1) / C;
+    const int es = d.kv_dtype == MK_BF16 ? 2 : 4;
+    std::vector<double> c((size_t)((int64_t)d.batch * d.n_kv_heads * splits),
+                          kLamAttn + (double)C * 2 * d.head_dim * es / kRateKV);
+    return lpt_span(c, W) + kHop;
+}
+
+// layered search: every layer has the same shape, so one layer's operators
+// are searched (each independently, levels being separated by events) and
+// the choice is used for all; a candidate whose lower bound (its bytes spread
+// evenly over every worker) cannot beat the best so far is pruned
+StaticChoice search_static(const mk_model_desc& d, int W, int cap, int chunk_min, int chunk_max) {
+    StaticChoice ch;
+    const int ops[] = {OP_QKV, OP_O, OP_GATEUP, OP_DOWN, OP_LM};
+    const double frac[] = {0.25, 0.5, 0.75, 1.0, 1.25, 1.5, 2.0, 3.0};
+    for (int op : ops) {
+        if (op == OP_LM && d.hidden_io) continue;
+        const int64_t rows = op_rows(d, op);
+        double best = 1e300;
+        int best_n = (int)std::min<int64_t>(W, rows);
+        for (double f : frac) {
+            const int n = (int)std::max<int64_t>(1, std::min<int64_t>(rows, (int64_t)(f * W)));
+            const int64_t K = op == OP_O ? (int64_t)d.n_heads * d.head_dim : op == OP_DOWN ? d.ffn : d.hidden;
+            const double lb = kLamGemv + (double)rows * K * (d.weight_dtype == MK_BF16 ? 2 : 4) *
+                                             (op == OP_GATEUP ? 2 : 1) / W / kRateW + kHop;
+            if (lb >= best) continue;  // pruned
+            const double c = gemv_level_cost(d, op, n, W);
+            if (c < best) {
+                best = c;
+                best_n = n;
+            }
+        }
+        ch.tasks[op] = best_n;
+        if (op != OP_LM) ch.predicted_us += best;
+    }
+    double best = 1e300;
+    for (int C = chunk_min; C <= chunk_max; C *= 2) {
+        const double c = attn_level_cost(d, cap, C, W);
+        if (c < best) {
+            best = c;
+            ch.chunk = C;
+        }
+    }
+    ch.predicted_us += best;
+    return ch;
+}
+}  // namespace
+
 bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::string& err) {
     // ---- validation
     if (d.n_layers < 1 || d.n_layers > 1024) return fail(err, "n_layers must be in [1, 1024]");
@@ -85,7 +211,10 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
     p = HostPlan();
     p.desc = d;
     if (o.jit < 0 || o.jit > 2) return fail(err, "opts.jit must be 0, 1 or 2");
+    if (o.schedule < 0 || o.schedule > 1) return fail(err, "opts.schedule must be 0 (event runtime) or 1 (static)");
+    if (o.schedule == 1 && o.jit == 1) return fail(err, "the static schedule has no JIT attention (opts.jit 0 or 2)");
     p.jit = (o.jit == 1) ? 1 : 0;  // default: AOT attention slots
+    p.schedule = o.schedule;
     // scheduler workgroups exist only to deal JIT attention; without them
     // every CU is a worker
     p.sched_wgs = p.jit ? (o.sched_wgs > 0 ? o.sched_wgs : 4) : 0;
@@ -107,6 +236,15 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
         p.attn_target = kAttnSplitTarget;
     }
     if (p.max_splits > 65535) return fail(err, "too many splits per sequence");
+    StaticChoice sc;
+    if (p.schedule == 1) {
+        // the split length is fixed for every step: chunk = chunk_max = the searched C
+        const int cmin = std::max(64, p.kv_chunk);
+        sc = search_static(d, p.workers, p.cap, cmin, std::max(cmin, std::min(p.kv_chunk_max, 4096)));
+        p.kv_chunk = p.kv_chunk_max = sc.chunk;
+        p.max_splits = n_splits_for(p.cap, p.kv_chunk);
+        p.predicted_layer_us = sc.predicted_us;
+    }
 
     const int L = d.n_layers, W = p.workers, B = d.batch, Hkv = d.n_kv_heads;
     p.events.assign(5 * L + 1, EventRec{0, -1});
@@ -119,8 +257,57 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
         p.level_layer.push_back((uint16_t)layer);
         p.level_off.push_back((int32_t)p.level_tasks.size());
     };
+    // static schedule: tasks placed longest first onto the least-loaded worker
+    // of the level (ties to the lowest index after the rotation)
+    auto lpt_place = [&](const std::vector<int>& ids, const std::vector<double>& cost) {
+        std::vector<int> order(ids.size());
+        for (size_t i = 0; i < order.size(); ++i) order[i] = (int)i;
+        std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return cost[a] > cost[b]; });
+        std::vector<double> load(W, 0.0);
+        std::vector<std::vector<int>> per(W);
+        for (int i : order) {
+            int best = rot;
+            for (int k = 1; k < W; ++k) {
+                const int w = (rot + k) % W;
+                if (load[w] < load[best]) best = w;
+            }
+            load[best] += cost[i];
+            per[best].push_back(ids[i]);
+        }
+        for (int w = 0; w < W; ++w) {
+            std::sort(per[w].begin(), per[w].end());
+            for (int id : per[w]) q[w].push_back(id);
+        }
+        rot = (rot + (int)ids.size()) % W;
+    };
     auto add_gemv = [&](int op, int layer, int wait, int sig, int min_rows) {
         const int64_t rows = op_rows(d, op);
+        if (p.schedule == 1 && op != OP_EMBED) {
+            const bool mf = d.weight_dtype == MK_BF16 && d.batch >= 3;
+            add_level(op, layer);
+            std::vector<int> ids;
+            std::vector<double> cost;
+            for (auto& r : cut_rows(rows, sc.tasks[op], mf)) {
+                TaskRec t{};
+                t.op = (uint8_t)op;
+                t.layer = (uint16_t)layer;
+                t.a0 = r.first;
+                t.a1 = r.second;
+                t.wait_ev = wait;
+                t.sig_ev = sig;
+                t.level = level;
+                const int id = (int)p.tasks.size();
+                p.tasks.push_back(t);
+                p.level_tasks.push_back(id);
+                ids.push_back(id);
+                cost.push_back((double)(r.second - r.first));
+                if (sig >= 0) p.events[sig].required++;
+                p.tasks_per_op[op]++;
+            }
+            lpt_place(ids, cost);
+            level++;
+            return;
+        }
         int64_t nt = std::min<int64_t>(W, (rows + min_rows - 1) / min_rows);
         add_level(op, layer);
         for (int64_t i = 0; i < nt; ++i) {
@@ -156,6 +343,31 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
         add_level(OP_ATTN, l);
         if (p.jit) {
             p.events[ev_qkv(l)].jit_layer = l;
+        } else if (p.schedule == 1) {
+            // static: one task per (sequence, KV head, split) of the capacity,
+            // its identity fixed in the record; splits past a sequence's
+            // length end at once
+            std::vector<int> ids;
+            std::vector<double> cost;
+            for (int bg = 0; bg < B * Hkv; ++bg)
+                for (int sp = 0; sp < p.max_splits; ++sp) {
+                    TaskRec t{};
+                    t.op = OP_ATTN;
+                    t.flags = kTaskStaticAttn;
+                    t.layer = (uint16_t)l;
+                    t.a0 = bg;
+                    t.a1 = sp;
+                    t.wait_ev = ev_qkv(l);
+                    t.sig_ev = ev_attn(l);
+                    t.level = level;
+                    const int id = (int)p.tasks.size();
+                    p.tasks.push_back(t);
+                    p.level_tasks.push_back(id);
+                    ids.push_back(id);
+                    cost.push_back(1.0);
+                    p.tasks_per_op[OP_ATTN]++;
+                }
+            lpt_place(ids, cost);
         } else {
             // AOT: slot i runs split task i of the step in (b, g, split)
             // order, found from seq_lens when it runs
@@ -286,10 +498,11 @@ bool verify_plan(const HostPlan& p, std::string& err) {
         if (at != op_rows(d, op)) return fail(err, "rows not fully covered at level " + std::to_string(lv));
     }
     if (!p.jit) {
+        const int want = p.schedule == 1 ? d.batch * d.n_kv_heads * p.max_splits : aot_attn_slots(p);
         for (int lv = 0; lv < p.n_levels; ++lv) {
             if (p.level_op[lv] != OP_ATTN) continue;
             int n = p.level_off[lv + 1] - p.level_off[lv];
-            if (n != aot_attn_slots(p)) return fail(err, "AOT attention level incomplete");
+            if (n != want) return fail(err, "AOT attention level incomplete");
         }
     }
     return true;
@@ -540,9 +753,9 @@ bool dry_run(const HostPlan& p, int n_threads, uint64_t seed, int drop_task, int
                     if (cur[k] >= p.queue_off[w + 1]) left--;
                     progressed = true;
                     if (t.op == OP_ATTN) {
-                        int bg, sp;
-                        if (locate_split(s, step_chunk(s), t.a0, bg, sp) && run_attn(s, t.layer, bg, sp, t.level))
-                            signal(t.sig_ev);
+                        int bg = t.a0, sp = t.a1;
+                        const bool located = (t.flags & kTaskStaticAttn) || locate_split(s, step_chunk(s), t.a0, bg, sp);
+                        if (located && run_attn(s, t.layer, bg, sp, t.level)) signal(t.sig_ev);
                         continue;
                     }
                     run_gemv(s, t);

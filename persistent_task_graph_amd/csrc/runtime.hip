@@ -639,6 +639,8 @@ int mk_plan_query(const mk_plan* pl, mk_plan_info* info) {
     info->jit = hp.jit;
     info->mode = hp.desc.opts.mode;
     info->host_only = pl->host_only ? 1 : 0;
+    info->schedule = hp.schedule;
+    info->predicted_layer_us = hp.predicted_layer_us;
     return MK_OK;
 }
 

@@ -33,8 +33,8 @@ EXPORTS = ["mk_build_graph", "mk_destroy_plan", "mk_last_error", "mk_plan_query"
 class ExecOpts(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("mode", "workers", "sched_wgs", "jit", "kv_chunk", "watchdog_ms",
                                                "host_only", "device_cus", "debug_event", "debug_extra_required",
-                                               "trace", "prefetch_kb", "lds_stream", "kv_chunk_max", "lds_preload")] + \
-               [("reserved", ctypes.c_int32 * 1)]
+                                               "trace", "prefetch_kb", "lds_stream", "kv_chunk_max", "lds_preload",
+                                               "schedule")]
 
 
 class ModelDesc(ctypes.Structure):
@@ -72,7 +72,8 @@ class PlanInfo(ctypes.Structure):
                                                "max_jit_tasks", "kv_chunk", "max_splits")] + \
                [("tasks_per_op", ctypes.c_int32 * 8)] + \
                [(n, ctypes.c_int64) for n in ("weight_bytes_per_step", "kv_bytes_per_token", "device_bytes")] + \
-               [(n, ctypes.c_int32) for n in ("jit", "mode", "host_only", "reserved")]
+               [(n, ctypes.c_int32) for n in ("jit", "mode", "host_only", "schedule")] + \
+               [("predicted_layer_us", ctypes.c_double)]
 
 
 _lib = None

@@ -421,3 +421,29 @@ def test_multi_step_launch_equals_repeated_greedy_steps(tiny, mid_weights, case)
     assert np.array_equal(d_len.cpu().numpy(), ref_lens)
     assert np.array_equal(logits.cpu().numpy().view(np.uint32), ref[-1][1].view(np.uint32))
     plan.close()
+
+
+@pytest.mark.parametrize("B,paged", [(1, False), (4, False), (16, False), (4, True)])
+def test_static_schedule_equals_event_runtime(mid_weights, B, paged):
+    # the static (searched) schedule runs the event runtime's task bodies: at
+    # the same attention split length the logits are the same bits
+    from persistent_task_graph_amd import harness
+
+    lens = [int(v) for v in np.linspace(5, 900, B)]
+    cap = max(lens) + 8
+    table = synth.block_table([cap] * B, 16) if paged else None
+    s = make_setup(MID, B, lens, cap, weights=mid_weights, paged=paged, table=table)
+    info = plan_for(s, schedule=1).info()
+    C = int(info.kv_chunk)
+    log("static schedule vs event runtime: B=%d paged=%s, split length %d, GEMV tasks %s"
+        % (B, paged, C, list(info.tasks_per_op)))
+    t0 = _tokens(MID, B, 8)
+    a, _ = _logits_seq(s, 3, tokens=t0, schedule=1)
+    b, _ = _logits_seq(s, 3, tokens=t0, kv_chunk=C, kv_chunk_max=C)
+    _bitwise(a, b)
+    if B == 16:
+        rows = [0, 15]
+        orc, _ = run_oracle(s, a, rows=rows)
+        worst, agree = compare(a, orc, rows=rows)
+        log("  static schedule vs oracle: max|d|/std = %.3g, top-1 = %.3f" % (worst, agree))
+        assert worst <= 2e-2 and agree >= 0.99

@@ -202,3 +202,26 @@ def test_contiguous_layer_stride_too_small_rejected(lib):
     need = 4 * shape.n_kv_heads * 1000 * shape.head_dim
     assert _fake_step(p, shape, need, False) == mk.MK_ERR_STATE
     assert _fake_step(p, shape, need - 1, False) == mk.MK_ERR_ARG
+
+
+# ---------------------------------------------------------------- static schedule
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_static_schedule_plans_verify_and_dry_run(lib, name):
+    # the searched plan covers every row once, fixes every attention split of
+    # the capacity, replays correctly on host threads, and is deterministic
+    wl = synth.WORKLOADS[name]
+    p = _plan(wl.shape, wl.batch, wl.capacity(), paged=wl.paged, schedule=1)
+    p.verify()
+    inf = p.info()
+    assert inf.schedule == 1 and inf.jit == 0 and inf.predicted_layer_us > 0
+    assert inf.tasks_per_op[mk.OP_ATTN] == wl.shape.n_layers * wl.batch * wl.shape.n_kv_heads * inf.max_splits
+    assert inf.max_splits == -(-wl.capacity() // inf.kv_chunk)
+    lens = [int(v) for v in synth.seq_lengths(wl)]
+    assert p.dry_run(n_threads=6, seed=11, seq_lens=lens) == 0
+    q = _plan(wl.shape, wl.batch, wl.capacity(), paged=wl.paged, schedule=1).info()
+    assert list(q.tasks_per_op) == list(inf.tasks_per_op) and q.kv_chunk == inf.kv_chunk
+
+
+def test_static_schedule_rejects_jit(lib):
+    with pytest.raises(mk.MKError, match="static schedule"):
+        _plan(synth.TINY, 1, 64, schedule=1, jit=1)
