@@ -649,7 +649,9 @@ __device__ __forceinline__ void gemv_mfma(const MSeg (&seg)[NSEG], int K, const 
         if (tr && tid == 0) s.marks[1] = now_ticks();
         __syncthreads();
         {
-            const int i = tid >> 4, b = tid & 15;  // row in tile, sequence
+            // row in tile, sequence: 16 consecutive lanes store 16 consecutive
+            // rows of one sequence, so their 4-byte stores merge into one write
+            const int i = tid & 15, b = tid >> 4;
             const int pl = ((i >> 2) * 16 + b) * 4 + (i & 3);
 #pragma unroll
             for (int t = 0; t < TMAX; ++t) {
