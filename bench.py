@@ -98,6 +98,8 @@ def parse():
     ap.add_argument("--lds-preload", type=int, default=0, help="1: preload GEMV rows into LDS pages (batch <= 2)")
     ap.add_argument("--quick", action="store_true", help="tiny prompt, few steps (profiling runs)")
     ap.add_argument("--no-tiny", action="store_true", help="skip the tiny-model step time")
+    ap.add_argument("--no-w4", action="store_true", help="skip the 4-bit-weight (W4A16) batch-1 measurement")
+    ap.add_argument("--w4-steps", type=int, default=64)
     ap.add_argument("--phases", type=int, default=0, metavar="B",
                     help="print the per-operator task-trace summary of the 8B model at batch B (1, 16 or 8 = paged) "
                          "and exit")
@@ -451,6 +453,55 @@ def main():
         }
         planL.close()
         del dmLs
+
+    # ---------------------------------------------------------------- 4-bit layer matrices (W4A16), batch 1
+    if not args.no_w4:
+        del dm
+        torch.cuda.empty_cache()
+        wl4 = synth.WORKLOADS["q8b_w4_b1"]
+        sh4 = wl4.shape
+        t0 = time.time()
+        dm4 = harness.DeviceModel(sh4, synth.model_weights(sh4), dev)
+        L04 = int(synth.seq_lengths(wl4)[0])
+        cap4 = L04 + args.warmup + args.w4_steps + 8
+        kv4 = harness.DeviceKV(sh4, 1, cap4)
+        c4 = synth.kv_sequence(sh4, 0, L04, cap4)
+        kv4.load_sequence(0, c4["k"], c4["v"], L04)
+        del c4
+        log("W4 model ready in %.1fs" % (time.time() - t0))
+        plan4 = harness.build_plan(sh4, 1, cap4, **opts)
+        d_tok4 = torch.from_numpy(synth.tokens(wl4)).to(dev)
+        d_len4 = torch.full((1,), L04, dtype=torch.int32, device=dev)
+        logits4 = torch.empty((1, sh4.vocab), dtype=torch.float32, device=dev)
+        for _ in range(args.warmup):
+            plan4.step_greedy(dm4.struct, kv4.struct, d_tok4, d_len4, logits4)
+        torch.cuda.synchronize()
+        l4 = int(d_len4.item())
+        ev4 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.w4_steps)]
+        e0.record(st)
+        for i in range(args.w4_steps):
+            ev4[i][0].record(st)
+            plan4.step_greedy(dm4.struct, kv4.struct, d_tok4, d_len4, logits4)
+            ev4[i][1].record(st)
+        e1.record(st)
+        torch.cuda.synchronize()
+        if plan4.device_error():
+            raise SystemExit("device error during W4 steps")
+        t4 = e0.elapsed_time(e1)
+        k4 = np.array([a.elapsed_time(b) for a, b in ev4])
+        b4 = float(np.mean([harness.step_bytes(sh4, [l4 + i], 1) for i in range(args.w4_steps)]))
+        ach4 = b4 / (k4.mean() * 1e-3) / 1e9
+        log("W4 B=1: %.3f ms/step (kernel avg %.3f), %.1f tok/s, %.0f GB/s = %.1f%%"
+            % (t4 / args.w4_steps, k4.mean(), args.w4_steps / (t4 * 1e-3), ach4, 100 * ach4 / PEAK_HBM_GBS))
+        result["w4_b1"] = {
+            "workload": "q8b_w4_b1: the same 36-layer model with 4-bit layer matrices (group 128, bf16 scales; bf16 "
+                        "embedding and LM head), batch 1, 1024 cached random keys, greedy decode",
+            "value": round(args.w4_steps / (t4 * 1e-3), 2), "unit": "tokens/s",
+            "ms_per_step": round(t4 / args.w4_steps, 4), "kernel_ms_mean": round(float(k4.mean()), 4),
+            "hbm_gbs": round(ach4, 1), "hbm_frac": round(ach4 / PEAK_HBM_GBS, 4), "bytes_per_launch": int(b4),
+        }
+        plan4.close()
+        del dm4, kv4
 
     # ---------------------------------------------------------------- tiny fp32 model (latency-bound)
     if not args.no_tiny:

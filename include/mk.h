@@ -37,7 +37,7 @@ extern "C" {
 
 typedef struct mk_plan mk_plan;
 
-enum mk_dtype { MK_F32 = 0, MK_BF16 = 1 };
+enum mk_dtype { MK_F32 = 0, MK_BF16 = 1, MK_W4 = 2 };
 enum mk_kv_layout { MK_KV_CONTIGUOUS = 0, MK_KV_PAGED = 1 };
 enum mk_exec_mode { MK_PERSISTENT = 0, MK_KERNEL_PER_OP = 1 };
 
@@ -146,7 +146,14 @@ typedef struct mk_exec_opts {
  *  hidden % 8 == 0; head_dim in {64, 128}; n_heads % n_kv_heads == 0;
  *  n_heads / n_kv_heads <= 8; 1 <= batch <= 16.
  *  weight_dtype, kv_dtype: MK_BF16 or MK_F32 (bf16 weights need a bf16 cache
- *  and f32 weights an f32 cache).
+ *  and f32 weights an f32 cache), or weight_dtype MK_W4 with a bf16 cache:
+ *  4-bit layer matrices (the Ada-MK summary's W4A16, gist.science
+ *  "Hauptbeiträge" 4), batch <= 2, hidden, ffn and n_heads * head_dim
+ *  multiples of 1024 and at most 12288. Each W4 matrix [rows, K] is one
+ *  buffer: 4-bit codes in row order, two per byte (low nibble first),
+ *  rows * K / 2 bytes; then, from that size rounded up to 256 bytes, one
+ *  bf16 scale per 128 inputs of a row, [rows][K / 128]; the weight is
+ *  (code - 8) * scale. Norm gains, embedding and LM head stay bf16.
  *  max_seq_len: KV capacity per sequence in positions. Contiguous layout:
  *  the cache holds [layer][batch][kv_head][max_seq_len][head_dim], and one
  *  sequence's span max_seq_len * head_dim * element size must be below

@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-F32, BF16 = 0, 1
+F32, BF16, W4 = 0, 1, 2
 
 
 def build(force: bool = False) -> str:
@@ -35,7 +35,8 @@ class _Cfg(ctypes.Structure):
     _fields_ = [("n_layers", ctypes.c_int), ("hidden", ctypes.c_int), ("n_heads", ctypes.c_int),
                 ("n_kv_heads", ctypes.c_int), ("head_dim", ctypes.c_int), ("ffn", ctypes.c_int),
                 ("vocab", ctypes.c_int), ("qk_norm", ctypes.c_int), ("wtype", ctypes.c_int),
-                ("kvtype", ctypes.c_int), ("eps", ctypes.c_double), ("rope_base", ctypes.c_double)]
+                ("mtype", ctypes.c_int), ("kvtype", ctypes.c_int), ("eps", ctypes.c_double),
+                ("rope_base", ctypes.c_double)]
 
 
 _LAYER_FIELDS = ["attn_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo", "mlp_norm", "w_gate", "w_up", "w_down"]
@@ -98,13 +99,20 @@ def rmsnorm(x: np.ndarray, gain: np.ndarray, eps: float = 1e-6) -> np.ndarray:
     return y
 
 
-def matvec(W: np.ndarray, x: np.ndarray) -> np.ndarray:
+def matvec(W: np.ndarray, x: np.ndarray, w4_shape=None) -> np.ndarray:
+    """y = W x. W: [rows, cols] float32 / bf16 bits, or a W4 buffer (uint8,
+    one dimension) with w4_shape = (rows, cols)."""
     W = _c(W)
     x = _c(np.ascontiguousarray(x, dtype=np.float32))
-    rows, cols = W.shape
+    if w4_shape is not None:
+        rows, cols = w4_shape
+        t = W4
+    else:
+        rows, cols = W.shape
+        t = _tcode(W)
     assert x.size == cols
     y = np.empty(rows, dtype=np.float32)
-    _load().orc_matvec(W.ctypes.data, _tcode(W), rows, cols, x.ctypes.data, y.ctypes.data)
+    _load().orc_matvec(W.ctypes.data, t, rows, cols, x.ctypes.data, y.ctypes.data)
     return y
 
 
@@ -145,6 +153,8 @@ class Oracle:
     Caches are per sequence: dict(k=[n_layers, Hkv, cap, D], v=...).
     """
 
+    _MATS = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
+
     def __init__(self, shape, weights: Dict):
         self.shape = shape
         self.w = weights
@@ -152,6 +162,7 @@ class Oracle:
         self._keep = []
         self._layers = (_Layer * len(layers))()
         wt = None
+        w4 = getattr(shape, "wdtype", "") == "w4"
         for li, lw in enumerate(layers):
             for name in _LAYER_FIELDS:
                 a = lw.get(name)
@@ -160,15 +171,19 @@ class Oracle:
                     continue
                 a = _c(a)
                 self._keep.append(a)
-                t = _tcode(a)
-                wt = t if wt is None else wt
-                if t != wt:
-                    raise TypeError("mixed weight types")
+                if w4 and name in self._MATS:
+                    if a.dtype != np.uint8 or a.ndim != 1:
+                        raise TypeError("W4 matrices are one-dimensional uint8 buffers")
+                else:
+                    t = _tcode(a)
+                    wt = t if wt is None else wt
+                    if t != wt:
+                        raise TypeError("mixed weight types")
                 setattr(self._layers[li], name, a.ctypes.data)
         self.wtype = wt
         self.cfg = _Cfg(shape.n_layers, shape.hidden, shape.n_heads, shape.n_kv_heads, shape.head_dim, shape.ffn,
-                        shape.vocab, int(bool(shape.qk_norm)), wt, BF16 if shape.kv_dtype == "bf16" else F32,
-                        float(shape.eps), float(shape.rope_base))
+                        shape.vocab, int(bool(shape.qk_norm)), wt, W4 if w4 else wt,
+                        BF16 if shape.kv_dtype == "bf16" else F32, float(shape.eps), float(shape.rope_base))
 
     def _check_cache(self, cache):
         k, v = _c(cache["k"]), _c(cache["v"])

@@ -34,7 +34,18 @@
 #include <omp.h>
 #endif
 
-enum { ORC_F32 = 0, ORC_BF16 = 1 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_W4 = 2 };
+
+/*
+ * W4 matrices (weight-only 4-bit quantisation, the Ada-MK summary's W4A16,
+ * gist.science "Hauptbeiträge" 4; the pages fix no format, so: symmetric
+ * 4-bit codes with offset 8 and one bf16 scale per group of 128 inputs of a
+ * row). One buffer per [rows, cols] matrix: the codes, rows * cols / 2
+ * bytes, element (r, c) in byte (r * cols + c) / 2, low nibble for even c,
+ * high nibble for odd c; then, from byte rows * cols / 2 rounded up to 256,
+ * the scales, bf16 [rows][cols / 128]. The weight is (code - 8) * scale.
+ */
+
 
 static inline float bf16_to_f32(uint16_t h) {
     uint32_t b = (uint32_t)h << 16;
@@ -49,6 +60,17 @@ static inline uint16_t f32_to_bf16_rne(float f) {
     if ((b & 0x7F800000u) == 0x7F800000u && (b & 0x007FFFFFu)) return (uint16_t)((b >> 16) | 0x40u);
     b += 0x7FFFu + ((b >> 16) & 1u);
     return (uint16_t)(b >> 16);
+}
+
+static inline size_t w4_scale_offset(int rows, int cols) { return (((size_t)rows * cols / 2) + 255) / 256 * 256; }
+
+/* weight (r, c) of a W4 matrix, dequantised exactly */
+static inline double w4_elem(const void* W, int rows, int cols, int r, int c) {
+    const uint8_t* q = (const uint8_t*)W;
+    const size_t i = (size_t)r * cols + c;
+    const int code = (c & 1) ? (q[i / 2] >> 4) : (q[i / 2] & 15);
+    const uint16_t* sc = (const uint16_t*)((const char*)W + w4_scale_offset(rows, cols));
+    return (double)(code - 8) * (double)bf16_to_f32(sc[(size_t)r * (cols / 128) + c / 128]);
 }
 
 /* element i of a weight/cache array of either type, widened exactly */
@@ -87,7 +109,9 @@ void orc_matvec(const void* W, int wtype, int rows, int cols, const float* x, fl
     for (int r = 0; r < rows; ++r) {
         double acc = 0.0;
         const int64_t base = (int64_t)r * cols;
-        if (wtype == ORC_BF16) {
+        if (wtype == ORC_W4) {
+            for (int c = 0; c < cols; ++c) acc += w4_elem(W, rows, cols, r, c) * (double)x[c];
+        } else if (wtype == ORC_BF16) {
             const uint16_t* w = (const uint16_t*)W + base;
             for (int c = 0; c < cols; ++c) acc += (double)bf16_to_f32(w[c]) * (double)x[c];
         } else {
@@ -152,6 +176,7 @@ typedef struct {
     int n_layers, hidden, n_heads, n_kv_heads, head_dim, ffn, vocab;
     int qk_norm;  /* per-head RMSNorm of q and k before RoPE */
     int wtype;    /* ORC_F32 / ORC_BF16 for every weight and gain */
+    int mtype;    /* type of the layer matrices: wtype, or ORC_W4 (gains, embedding and LM head stay wtype) */
     int kvtype;   /* cache element type */
     double eps, rope_base;
 } orc_cfg;
@@ -193,9 +218,9 @@ void orc_layer_forward(const orc_cfg* c, const orc_layer* w, void* kc, void* vc,
 
     /* attention block */
     orc_rmsnorm(x, H, w->attn_norm, c->wtype, c->eps, xn);
-    orc_matvec(w->wq, c->wtype, QD, H, xn, q);
-    orc_matvec(w->wk, c->wtype, KD, H, xn, k);
-    orc_matvec(w->wv, c->wtype, KD, H, xn, v);
+    orc_matvec(w->wq, c->mtype, QD, H, xn, q);
+    orc_matvec(w->wk, c->mtype, KD, H, xn, k);
+    orc_matvec(w->wv, c->mtype, KD, H, xn, v);
     for (int h = 0; h < Hq; ++h) {
         if (c->qk_norm) {
             orc_rmsnorm(q + h * D, D, w->q_norm, c->wtype, c->eps, tmp);
@@ -221,15 +246,15 @@ void orc_layer_forward(const orc_cfg* c, const orc_layer* w, void* kc, void* vc,
         const char* Vh = (const char*)vc + (size_t)hk * cap * D * es;
         orc_attention_head(q + h * D, Kh, Vh, c->kvtype, pos + 1, D, att + h * D, NULL);
     }
-    orc_matvec(w->wo, c->wtype, H, QD, att, y);
+    orc_matvec(w->wo, c->mtype, H, QD, att, y);
     for (int i = 0; i < H; ++i) x[i] = (float)((double)x[i] + (double)y[i]);
 
     /* MLP block */
     orc_rmsnorm(x, H, w->mlp_norm, c->wtype, c->eps, xn);
-    orc_matvec(w->w_gate, c->wtype, F, H, xn, g);
-    orc_matvec(w->w_up, c->wtype, F, H, xn, u);
+    orc_matvec(w->w_gate, c->mtype, F, H, xn, g);
+    orc_matvec(w->w_up, c->mtype, F, H, xn, u);
     orc_swiglu(g, u, F, xn);
-    orc_matvec(w->w_down, c->wtype, H, F, xn, y);
+    orc_matvec(w->w_down, c->mtype, H, F, xn, y);
     for (int i = 0; i < H; ++i) x[i] = (float)((double)x[i] + (double)y[i]);
 
     free(xn); free(q); free(k); free(v); free(att); free(y); free(g); free(u); free(tmp);

@@ -183,11 +183,21 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
     if (d.ffn < 8 || d.ffn % 8) return fail(err, "ffn must be a positive multiple of 8");
     if (!d.hidden_io && (d.vocab < 1)) return fail(err, "vocab must be positive");
     if (d.batch < 1 || d.batch > 16) return fail(err, "batch must be in [1, 16]");
-    if (d.weight_dtype != MK_BF16 && d.weight_dtype != MK_F32) return fail(err, "weight_dtype must be MK_BF16 or MK_F32");
-    if (d.kv_dtype != d.weight_dtype) return fail(err, "kv_dtype must equal weight_dtype (bf16/bf16 or f32/f32)");
+    if (d.weight_dtype != MK_BF16 && d.weight_dtype != MK_F32 && d.weight_dtype != MK_W4)
+        return fail(err, "weight_dtype must be MK_BF16, MK_F32 or MK_W4");
+    if (d.weight_dtype == MK_W4) {
+        if (d.kv_dtype != MK_BF16) return fail(err, "W4 weights need a bf16 KV cache");
+        if (d.batch > 2) return fail(err, "W4 weights support batch <= 2");
+        if (d.opts.lds_stream == 1) return fail(err, "W4 weights do not support lds_stream");
+        const int64_t ks[3] = {d.hidden, d.ffn, (int64_t)d.n_heads * d.head_dim};
+        for (int64_t k : ks)
+            if (k % 1024 || k > 12288) return fail(err, "W4: hidden, ffn and n_heads*head_dim must be multiples of 1024, at most 12288");
+    } else if (d.kv_dtype != d.weight_dtype) {
+        return fail(err, "kv_dtype must equal weight_dtype (bf16/bf16 or f32/f32)");
+    }
     if (d.weight_dtype == MK_F32 && d.batch > 4) return fail(err, "f32 weights support batch <= 4");
     {
-        const int64_t seg = d.weight_dtype == MK_BF16 ? 512 : 256;
+        const int64_t seg = d.weight_dtype == MK_F32 ? 256 : 512;
         const int64_t kmax = 4 * 8 * seg;  // four waves x eight 16-byte segments per lane
         if (d.hidden > kmax || d.ffn > kmax || (int64_t)d.n_heads * d.head_dim > kmax)
             return fail(err, "hidden, ffn and n_heads*head_dim must be <= " + std::to_string(kmax));
@@ -428,9 +438,15 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
     p.inbox_cap = next_pow2((int)std::max<int64_t>(16, per_layer_jit / std::max<size_t>(1, p.jit_elig.size()) + 2));
     p.mb_cap = next_pow2(std::max(16, L));
 
-    const int64_t es = d.weight_dtype == MK_BF16 ? 2 : 4;
+    const int64_t es = d.weight_dtype == MK_F32 ? 4 : 2;
     const int64_t H = d.hidden, F = d.ffn, QD = (int64_t)d.n_heads * d.head_dim, KD = (int64_t)Hkv * d.head_dim;
     int64_t layer = ((QD + 2 * KD) * H + H * QD + 3 * F * H + 2 * H + (d.qk_norm ? 2 * d.head_dim : 0)) * es;
+    if (d.weight_dtype == MK_W4) {
+        // codes (K / 2 bytes per row) and scales (2 bytes per 128 inputs); gains bf16
+        const int64_t dims[7][2] = {{QD, H}, {KD, H}, {KD, H}, {H, QD}, {F, H}, {F, H}, {H, F}};
+        layer = (2 * H + (d.qk_norm ? 2 * d.head_dim : 0)) * 2;
+        for (auto& rc : dims) layer += rc[0] * rc[1] / 2 + rc[0] * (rc[1] / 128) * 2;
+    }
     p.weight_bytes = L * layer + (d.hidden_io ? 0 : ((int64_t)d.vocab * H + H) * es);
     p.kv_bytes_per_token = (int64_t)L * 2 * KD * (d.kv_dtype == MK_BF16 ? 2 : 4);
     return true;

@@ -200,7 +200,7 @@ int nb_for(int B) { return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : B <= 8 ? 8 : 1
 
 void* kernel_for(const mk_plan* pl, int kind) {
     const int nb = nb_for(pl->hp.desc.batch);
-    if (pl->hp.desc.weight_dtype == MK_BF16) {
+    if (pl->hp.desc.weight_dtype == MK_BF16 || pl->hp.desc.weight_dtype == MK_W4) {
         switch (nb) {
             case 1: return pl->hp.desc.opts.lds_stream == 1 ? mk_kernels_bf16_1s(kind) : mk_kernels_bf16_1(kind);
             case 2: return mk_kernels_bf16_2(kind);
@@ -225,7 +225,7 @@ void* attn_kernel(const mk_plan* pl) { return kernel_for(pl, KK_LEVEL_ATTN); }
 bool lds_preload_on(const mk_plan* pl) {
     const mk_model_desc& d = pl->hp.desc;
     return d.opts.mode == MK_PERSISTENT && !pl->hp.jit && nb_for(d.batch) <= 2 && d.opts.lds_stream != 1 &&
-           d.opts.lds_preload == 1;
+           d.opts.lds_preload == 1 && d.weight_dtype != MK_W4;
 }
 
 bool upload_plan(mk_plan* pl) {
@@ -337,7 +337,7 @@ bool upload_plan(mk_plan* pl) {
     pl->lds_bytes = lds_bytes_for(hp.kv_chunk_max, d.kv_layout == MK_KV_PAGED ? d.kv_block : 1, d.kv_layout == MK_KV_PAGED);
     // one workgroup per CU: the LDS-ring variant's static page ring already
     // takes more than half of the CU's LDS; other kernels reserve it dynamically
-    const bool ring = nb_for(d.batch) == 1 && d.weight_dtype == MK_BF16 && d.opts.lds_stream == 1;
+    const bool ring = nb_for(d.batch) == 1 && d.weight_dtype != MK_F32 && d.opts.lds_stream == 1;
     pl->lds_bytes_persistent = ring ? pl->lds_bytes : std::max(pl->lds_bytes, 82 * 1024);
     if (lds_preload_on(pl)) pl->lds_bytes_persistent = std::max(pl->lds_bytes_persistent, lds_bytes_preload());
     // 160 KB per CU, less the statically declared prefetch sink (4 KB)
@@ -456,6 +456,7 @@ KParams make_params(const mk_plan* pl, const mk_weights* w, const mk_kv_cache* k
     p.watchdog_ticks = (uint64_t)wd * 100000ull;
     p.prefetch_kb = d.opts.prefetch_kb == 0 ? 256 : (d.opts.prefetch_kb < 0 ? 0 : d.opts.prefetch_kb);
     p.pre_slots = lds_preload_on(pl) ? kPreSlots : 0;
+    p.w4 = d.weight_dtype == MK_W4 ? 1 : 0;
     p.trace = pl->d_trace;
     p.trace_n = pl->d_trace_n;
     p.trace_cap = pl->trace_cap;

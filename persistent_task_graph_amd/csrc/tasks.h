@@ -406,6 +406,237 @@ __device__ __forceinline__ void gemv_rowwave(int r0, int r1, int K, const float*
     }
 }
 
+// ---------------------------------------------------------------- GEMV with 4-bit weights (B <= 2)
+// W4 matrix buffer (one per [rows, K] matrix): 4-bit codes in row order, two
+// per byte (low nibble first), rows * K / 2 bytes; then, from that size
+// rounded up to 256 bytes, one bf16 scale per 128 inputs of a row. The
+// weight is (code - 8) * scale.
+constexpr int kW4Group = 128;
+__host__ __device__ constexpr int64_t w4_scale_offset(int64_t rows, int64_t K) { return (rows * K / 2 + 255) / 256 * 256; }
+
+// v & m computed where the compiler cannot see the result's zero bits
+__device__ __forceinline__ uint32_t opaque_and(uint32_t v, uint32_t m) {
+    uint32_t r;
+    asm volatile("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(v), "v"(m));
+    return r;
+}
+
+// One W4 matrix tile: codes and scales of rows [lo, lo + n)
+struct W4Tile {
+    __amdgpu_buffer_rsrc_t q, sc;
+    int lo, n;
+    uint32_t qrow, srow;  // bytes per row of codes, of scales
+};
+__device__ __forceinline__ W4Tile w4_tile(const void* m, int K, int rows, int lo_, int hi_) {
+    W4Tile t;
+    t.lo = max(0, min(lo_, rows));
+    const int hi = max(t.lo, min(hi_, rows));
+    t.n = hi - t.lo;
+    t.qrow = (uint32_t)K / 2u;
+    t.srow = (uint32_t)(K / kW4Group) * 2u;
+    const char* base = (const char*)m;
+    t.q = make_rsrc(base + (int64_t)t.lo * t.qrow, (uint32_t)t.n * t.qrow);
+    t.sc = make_rsrc(base + w4_scale_offset(rows, K) + (int64_t)t.lo * t.srow, (uint32_t)t.n * t.srow);
+    return t;
+}
+
+// Same shape as gemv_ksplit: K in segments of 1024 inputs (64 lanes x 16
+// codes, one 8-byte load per lane), segment s to wave s % 4; each lane keeps
+// its 16 inputs (times the norm gain) and their sum in registers. A lane's
+// 16 codes share one scale, so its part of row r is
+//   scale * (sum_e code_e * x_e - 8 * sum_e x_e),
+// summed over its segments, then over the wave (butterfly) and the waves
+// in order. Rows past the tile and inputs past K load zeros (out of range).
+// RowFn(r) gives the tile holding row r (and the second matrix's, for DUAL).
+template <int NB, int NSW, int U, bool DUAL, typename RowFn, typename OutFn>
+__device__ __forceinline__ void gemv_w4(int r0, int r1, int K, const float* x, int ldx, int B, const bf16_t* gain,
+                                        float eps, RowFn rowp, OutFn out, const Lds& s, bool tr) {
+    constexpr int E = 16, SEG = 64 * E;
+    constexpr int NM = DUAL ? 2 : 1;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nseg = (K + SEG - 1) / SEG;
+    uint32_t qoff[NSW], soff[NSW];
+    bool kvalid[NSW];
+#pragma unroll
+    for (int j = 0; j < NSW; ++j) {
+        const int k = (wave + kWaves * j) * SEG + lane * E;
+        kvalid[j] = wave + kWaves * j < nseg && k < K;
+        qoff[j] = kvalid[j] ? (uint32_t)k / 2u : kOOB;
+        soff[j] = kvalid[j] ? (uint32_t)(k / kW4Group) * 2u : kOOB;
+    }
+    constexpr int WIN = kPartFloats / (kWaves * NM * NB);
+    struct Row {
+        uint2 q[NM][NSW];
+        uint32_t sc[NM][NSW];
+    };
+    auto load = [&](Row (&w)[U], int r, int rend) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool rv = r + u < rend;
+            W4Tile ta, tb;
+            int rr;  // the row inside its tile
+            rowp(rv ? r + u : rend - 1, ta, tb, rr);
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                const W4Tile& t = m == 0 ? ta : tb;
+#pragma unroll
+                for (int j = 0; j < NSW; ++j) {
+                    const uint32_t qo = rv ? qoff[j] : kOOB, so = rv ? soff[j] : kOOB;
+                    const auto v = __builtin_amdgcn_raw_buffer_load_b64(t.q, qo, (uint32_t)rr * t.qrow, 0);
+                    w[u].q[m][j] = make_uint2((uint32_t)v[0], (uint32_t)v[1]);
+                    w[u].sc[m][j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(t.sc, so, (uint32_t)rr * t.srow, 0);
+                }
+            }
+        }
+    };
+    Row wa[U], wb[U];
+    load(wa, r0, min(r0 + WIN, r1));
+
+    const __amdgpu_buffer_rsrc_t xr_rs = make_rsrc(x, (uint32_t)(B * ldx) * 4u);
+    const __amdgpu_buffer_rsrc_t g_rs = make_rsrc(gain, gain ? (uint32_t)K * 2u : 0u);
+    float xr[NSW][NB][E];
+#pragma unroll
+    for (int j = 0; j < NSW; ++j)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const uint32_t xo = (kvalid[j] && b < B) ? (uint32_t)(b * ldx + (wave + kWaves * j) * SEG + lane * E) * 4u : kOOB;
+#pragma unroll
+            for (int e = 0; e < E; e += 4) {
+                const uint4 v = buf_load16_act(xr_rs, xo, (uint32_t)e * 4u);
+                xr[j][b][e + 0] = __uint_as_float(v.x);
+                xr[j][b][e + 1] = __uint_as_float(v.y);
+                xr[j][b][e + 2] = __uint_as_float(v.z);
+                xr[j][b][e + 3] = __uint_as_float(v.w);
+            }
+        }
+    float g[NSW][E];
+#pragma unroll
+    for (int j = 0; j < NSW; ++j) {
+        if (gain) {
+            const uint32_t go = kvalid[j] ? (uint32_t)((wave + kWaves * j) * SEG + lane * E) * 2u : kOOB;
+            Vec16<bf16_t>::widen(buf_load16(g_rs, go, 0), &g[j][0]);
+            Vec16<bf16_t>::widen(buf_load16(g_rs, go, 16), &g[j][8]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) g[j][e] = 1.f;
+        }
+    }
+    if (gain) {
+        float ss[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            ss[b] = 0.f;
+#pragma unroll
+            for (int j = 0; j < NSW; ++j)
+#pragma unroll
+                for (int e = 0; e < E; ++e) ss[b] += xr[j][b][e] * xr[j][b][e];
+            ss[b] = wave_sum(ss[b]);
+        }
+        if (lane == 0)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) s.red[wave * 16 + b] = ss[b];
+        __syncthreads();
+        if (tid < NB) {
+            float t = s.red[tid];
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w) t += s.red[w * 16 + tid];
+            s.rstd[tid] = 1.0f / sqrtf(t / (float)K + eps);
+        }
+    }
+    if (tr && tid == 0) s.marks[0] = now_ticks();
+    float sx[NSW][NB];  // sum of the lane's 16 inputs (times the gain)
+#pragma unroll
+    for (int j = 0; j < NSW; ++j)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            float t = 0.f;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                xr[j][b][e] = xr[j][b][e] * g[j][e];
+                t += xr[j][b][e];
+            }
+            sx[j][b] = t;
+        }
+
+    auto consume = [&](const Row (&w)[U], int r, int rend, int rg) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                float acc[NB];
+#pragma unroll
+                for (int b = 0; b < NB; ++b) acc[b] = 0.f;
+#pragma unroll
+                for (int j = 0; j < NSW; ++j) {
+                    // codes 0..15 of the lane: byte i of the 8 holds codes 2i, 2i + 1.
+                    // The masks are opaque to the compiler, so each masked byte
+                    // converts with one v_cvt_f32_ubyte{0..3} (it would otherwise
+                    // fold mask and shift into a bit-field extract plus a convert)
+                    const uint32_t lo0 = opaque_and(w[u].q[m][j].x, 0x0F0F0F0Fu);
+                    const uint32_t hi0 = opaque_and(w[u].q[m][j].x >> 4, 0x0F0F0F0Fu);
+                    const uint32_t lo1 = opaque_and(w[u].q[m][j].y, 0x0F0F0F0Fu);
+                    const uint32_t hi1 = opaque_and(w[u].q[m][j].y >> 4, 0x0F0F0F0Fu);
+                    float c[E];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        c[2 * i] = (float)((lo0 >> (8 * i)) & 0xFFu);
+                        c[2 * i + 1] = (float)((hi0 >> (8 * i)) & 0xFFu);
+                        c[8 + 2 * i] = (float)((lo1 >> (8 * i)) & 0xFFu);
+                        c[8 + 2 * i + 1] = (float)((hi1 >> (8 * i)) & 0xFFu);
+                    }
+                    const float sc = __uint_as_float(w[u].sc[m][j] << 16);
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) {
+                        float d = 0.f;
+#pragma unroll
+                        for (int e = 0; e < E; ++e) d = fmaf(c[e], xr[j][b][e], d);
+                        acc[b] = fmaf(sc, fmaf(-8.0f, sx[j][b], d), acc[b]);
+                    }
+                }
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const float v = wave_sum(acc[b]);
+                    if (lane == 0 && r + u < rend) s.part[((wave * WIN) + (r + u - rg)) * NM * NB + m * NB + b] = v;
+                }
+            }
+        }
+    };
+    for (int rg = r0; rg < r1; rg += WIN) {
+        const int rend = min(rg + WIN, r1);
+        if (rg != r0) load(wa, rg, rend);
+        for (int r = rg; r < rend; r += 2 * U) {
+            load(wb, r + U, rend);
+            consume(wa, r, rend, rg);
+            load(wa, r + 2 * U, rend);
+            consume(wb, r + U, rend, rg);
+        }
+        if (tr && tid == 0) s.marks[1] = now_ticks();
+        __syncthreads();
+        for (int i = tid; i < (rend - rg) * NB; i += kThreads) {
+            const int rr = i / NB, b = i % NB;
+            float t[2] = {0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                float a = s.part[rr * NM * NB + m * NB + b];
+#pragma unroll
+                for (int wv = 1; wv < kWaves; ++wv) a += s.part[((wv * WIN) + rr) * NM * NB + m * NB + b];
+                t[m] = a;
+            }
+            if (b < B) out(rg + rr, b, t[0], t[1]);
+        }
+        __syncthreads();
+    }
+}
+
+template <int NB, bool DUAL, typename RowFn, typename OutFn>
+__device__ __forceinline__ void gemv_w4_dispatch(int r0, int r1, int K, const float* x, int ldx, int B, const bf16_t* gain,
+                                                 float eps, RowFn rowp, OutFn out, const Lds& s, bool tr) {
+    const int nsw = (K / 1024 + kWaves - 1) / kWaves;
+    if (nsw <= 1) gemv_w4<NB, 1, 2, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr);
+    else if (nsw <= 2) gemv_w4<NB, 2, 2, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr);
+    else gemv_w4<NB, 3, 1, DUAL>(r0, r1, K, x, ldx, B, gain, eps, rowp, out, s, tr);
+}
+
 // segments per wave per row of the B <= 2 GEMV for K inputs of type WT
 // (the template instance gemv_dispatch picks; the preload uses the same)
 template <typename WT>
@@ -756,12 +987,87 @@ __device__ __forceinline__ void lm_greedy(const KParams& p, int r0, int r1) {
     __hip_atomic_store(p.lm_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// A GEMV task of a plan whose layer matrices are W4 (batch <= 2); the LM
+// head and the embedding stay bf16 and take the ordinary path.
+template <int NB>
+__device__ __forceinline__ void run_w4_task(const KParams& p, const TaskRec& t, const Lds& s, const LayerPtrs& w) {
+    const int l = t.layer, B = p.B, H = p.H, r0 = t.a0, r1 = t.a1;
+    const bool tr = p.trace != nullptr;
+    switch (t.op) {
+        case OP_QKV: {
+            const float* x = layer_in(p, l);
+            const int QD = p.QD, KD = p.KD, ld = QD + 2 * KD;
+            const W4Tile tq = w4_tile(w.wq, H, QD, r0, r1), tk = w4_tile(w.wk, H, KD, r0 - QD, r1 - QD),
+                         tv = w4_tile(w.wv, H, KD, r0 - QD - KD, r1 - QD - KD);
+            float* o = layer_buf(p, l, p.off_qkv);
+            auto rowp = [&](int r, W4Tile& a, W4Tile& b2, int& rr) {
+                if (r < QD) { a = tq; rr = r - tq.lo; }
+                else if (r < QD + KD) { a = tk; rr = r - QD - tk.lo; }
+                else { a = tv; rr = r - QD - KD - tv.lo; }
+                b2 = a;
+            };
+            auto out = [&](int r, int b, float v, float) { st_co(&o[(int64_t)b * ld + r], v * s.rstd[b]); };
+            gemv_w4_dispatch<NB, false>(r0, r1, H, x, H, B, (const bf16_t*)w.attn_norm, p.eps, rowp, out, s, tr);
+            break;
+        }
+        case OP_O: {
+            const float* a = layer_buf(p, l, p.off_attn);
+            const float* xin = layer_in(p, l);
+            float* o = layer_buf(p, l, p.off_xmid);
+            const W4Tile to = w4_tile(w.wo, p.QD, H, r0, r1);
+            auto rowp = [&](int r, W4Tile& a0, W4Tile& b2, int& rr) { a0 = b2 = to; rr = r - to.lo; };
+            auto out = [&](int r, int b, float v, float) {
+                const int64_t i = (int64_t)b * H + r;
+                st_co(&o[i], ld_act(&xin[i]) + v);
+            };
+            gemv_w4_dispatch<NB, false>(r0, r1, p.QD, a, p.QD, B, (const bf16_t*)nullptr, p.eps, rowp, out, s, tr);
+            break;
+        }
+        case OP_GATEUP: {
+            const float* x = layer_buf(p, l, p.off_xmid);
+            float* o = layer_buf(p, l, p.off_h);
+            const int F = p.F;
+            const W4Tile tg = w4_tile(w.w_gate, H, F, r0, r1), tu = w4_tile(w.w_up, H, F, r0, r1);
+            auto rowp = [&](int r, W4Tile& a0, W4Tile& b2, int& rr) { a0 = tg; b2 = tu; rr = r - tg.lo; };
+            auto out = [&](int r, int b, float g, float u) {
+                const float rs = s.rstd[b];
+                const float gg = g * rs, uu = u * rs;
+                st_co(&o[(int64_t)b * F + r], (gg / (1.0f + __expf(-gg))) * uu);
+            };
+            gemv_w4_dispatch<NB, true>(r0, r1, H, x, H, B, (const bf16_t*)w.mlp_norm, p.eps, rowp, out, s, tr);
+            break;
+        }
+        case OP_DOWN: {
+            const float* h = layer_buf(p, l, p.off_h);
+            const float* xm = layer_buf(p, l, p.off_xmid);
+            float* o = layer_out(p, l);
+            const W4Tile td = w4_tile(w.w_down, p.F, H, r0, r1);
+            auto rowp = [&](int r, W4Tile& a0, W4Tile& b2, int& rr) { a0 = b2 = td; rr = r - td.lo; };
+            auto out = [&](int r, int b, float v, float) {
+                const int64_t i = (int64_t)b * H + r;
+                st_co(&o[i], ld_act(&xm[i]) + v);
+            };
+            gemv_w4_dispatch<NB, false>(r0, r1, p.F, h, p.F, B, (const bf16_t*)nullptr, p.eps, rowp, out, s, tr);
+            break;
+        }
+        default: break;
+    }
+    trace_mark(p, s.marks, 2);
+}
+
 // w: the task's layer pointers, p.lw[t.layer] (the worker reads them before
 // the task's event fires). pre_rows: leading rows of the task whose weights
 // were preloaded into this worker's LDS slots (batch <= 2 only; 0 otherwise).
 template <typename WT, int NB>
 __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t, const Lds& s, const LayerPtrs& w,
                                               int pre_rows = 0) {
+    // 4-bit layer matrices (batch <= 2)
+    if constexpr (std::is_same<WT, bf16_t>::value && NB <= 2) {
+        if (p.w4 && t.op != OP_LM && t.op != OP_EMBED) {
+            run_w4_task<NB>(p, t, s, w);
+            return;
+        }
+    }
     // bf16 weights with more than two sequences run on the matrix cores
     constexpr bool kMfma = std::is_same<WT, bf16_t>::value && NB >= 4;
     const int l = t.layer, B = p.B, H = p.H;
@@ -1085,21 +1391,25 @@ __device__ __forceinline__ Prefetch prefetch_setup(const KParams& p, const TaskR
     f.next = f.end = 0;
     f.a = f.b = make_rsrc(p.zero, 0);
     if (p.prefetch_kb <= 0) return f;
-    const int es = (int)sizeof(WT), l = t.layer, H = p.H;
+    // a W4 layer matrix streams K / 2 bytes of codes per row (its scales,
+    // 1/64 of that, are not prefetched): the same cursor with halved K
+    const bool w4m = p.w4 && t.op != OP_LM && t.op != OP_EMBED;
+    const int es = w4m ? 1 : (int)sizeof(WT), l = t.layer, H = p.H;
+    const int kh = w4m ? p.H / 2 : p.H, kq = w4m ? p.QD / 2 : p.QD, kf = w4m ? p.F / 2 : p.F;  // row lengths in elements of size es
     switch (t.op) {
         case OP_QKV: {
             const LayerPtrs& w = p.lw[l];
-            if (t.a0 < p.QD) prefetch_segment(w.wq, H, es, p.QD, t.a0, t.a1, f.a, f.kb_a);
-            else if (t.a0 < p.QD + p.KD) prefetch_segment(w.wk, H, es, p.KD, t.a0 - p.QD, t.a1 - p.QD, f.a, f.kb_a);
-            else prefetch_segment(w.wv, H, es, p.KD, t.a0 - p.QD - p.KD, t.a1 - p.QD - p.KD, f.a, f.kb_a);
+            if (t.a0 < p.QD) prefetch_segment(w.wq, kh, es, p.QD, t.a0, t.a1, f.a, f.kb_a);
+            else if (t.a0 < p.QD + p.KD) prefetch_segment(w.wk, kh, es, p.KD, t.a0 - p.QD, t.a1 - p.QD, f.a, f.kb_a);
+            else prefetch_segment(w.wv, kh, es, p.KD, t.a0 - p.QD - p.KD, t.a1 - p.QD - p.KD, f.a, f.kb_a);
             break;
         }
-        case OP_O: prefetch_segment(p.lw[l].wo, p.QD, es, H, t.a0, t.a1, f.a, f.kb_a); break;
+        case OP_O: prefetch_segment(p.lw[l].wo, kq, es, H, t.a0, t.a1, f.a, f.kb_a); break;
         case OP_GATEUP:
-            prefetch_segment(p.lw[l].w_gate, H, es, p.F, t.a0, t.a1, f.a, f.kb_a);
-            prefetch_segment(p.lw[l].w_up, H, es, p.F, t.a0, t.a1, f.b, f.kb_b);
+            prefetch_segment(p.lw[l].w_gate, kh, es, p.F, t.a0, t.a1, f.a, f.kb_a);
+            prefetch_segment(p.lw[l].w_up, kh, es, p.F, t.a0, t.a1, f.b, f.kb_b);
             break;
-        case OP_DOWN: prefetch_segment(p.lw[l].w_down, p.F, es, H, t.a0, t.a1, f.a, f.kb_a); break;
+        case OP_DOWN: prefetch_segment(p.lw[l].w_down, kf, es, H, t.a0, t.a1, f.a, f.kb_a); break;
         case OP_LM: prefetch_segment(p.lm_head, H, es, p.V, t.a0, t.a1, f.a, f.kb_a); break;
         default: break;
     }

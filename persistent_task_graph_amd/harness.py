@@ -128,7 +128,7 @@ def step_bytes(shape, seq_lens: Sequence[int], batch: int) -> int:
     b += kvtok * sum(int(l) + 1 for l in seq_lens)  # reads
     b += kvtok * batch  # appends
     if shape.embed_head:
-        wes = 2 if shape.wdtype == "bf16" else 4
+        wes = 4 if shape.wdtype == "f32" else 2
         b += batch * shape.hidden * wes + batch * shape.vocab * 4
     else:
         b += 2 * batch * shape.hidden * 4

@@ -16,7 +16,7 @@ from typing import Optional, Sequence
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmk.so")
 
-MK_F32, MK_BF16 = 0, 1
+MK_F32, MK_BF16, MK_W4 = 0, 1, 2
 MK_KV_CONTIGUOUS, MK_KV_PAGED = 0, 1
 MK_PERSISTENT, MK_KERNEL_PER_OP = 0, 1
 MK_OK, MK_ERR_ARG, MK_ERR_HIP, MK_ERR_UNSUPPORTED, MK_ERR_STATE = 0, -1, -2, -3, -4
@@ -133,7 +133,7 @@ def make_desc(shape, batch: int, max_seq_len: int, *, paged: bool = False, kv_bl
     d.head_dim, d.ffn, d.vocab = shape.head_dim, shape.ffn, shape.vocab
     d.rms_eps, d.rope_base = shape.eps, shape.rope_base
     d.qk_norm = int(bool(shape.qk_norm))
-    d.weight_dtype = MK_BF16 if shape.wdtype == "bf16" else MK_F32
+    d.weight_dtype = {"bf16": MK_BF16, "f32": MK_F32, "w4": MK_W4}[shape.wdtype]
     d.kv_dtype = MK_BF16 if shape.kv_dtype == "bf16" else MK_F32
     d.batch = batch
     d.max_seq_len = max_seq_len

@@ -60,6 +60,7 @@ def _load():
         lib.synth_normal_bf16.argtypes = [u64, u64, dbl, dbl, i64, vp]
         lib.synth_uniform_int.argtypes = [u64, u64, i64, i64, i64, vp]
         lib.synth_uniform_f64.argtypes = [u64, u64, i64, vp]
+        lib.synth_codes_u4.argtypes = [u64, u64, i64, vp]
         _lib = lib
     return _lib
 
@@ -95,6 +96,47 @@ def uniform01(seed: int, stream: int, n: int) -> np.ndarray:
     return out
 
 
+# ----------------------------------------------------------------------------
+# 4-bit weight matrices (W4A16)
+#
+# One buffer per [rows, cols] matrix: the 4-bit codes in row order, two per
+# byte (low nibble first), rows * cols / 2 bytes; then, from that size
+# rounded up to 256 bytes, one bf16 scale per group of W4_GROUP inputs of a
+# row, [rows][cols / W4_GROUP]. The weight is (code - 8) * scale.
+W4_GROUP = 128
+# scale of the codes so the weights have about the standard deviation of the
+# bf16 matrices: (code - 8) is uniform on [-8, 7], standard deviation 4.61
+W4_SCALE_PER_STD = 1.0 / 4.6098
+
+
+def w4_scale_offset(rows: int, cols: int) -> int:
+    return (rows * cols // 2 + 255) // 256 * 256
+
+
+def w4_matrix(seed: int, stream: int, rows: int, cols: int, std: float = 0.02) -> np.ndarray:
+    """Seeded W4 matrix buffer: uniform codes; scales |N(1, 0.25)| * std / 4.61 in bf16."""
+    assert cols % W4_GROUP == 0 and cols % 2 == 0
+    off = w4_scale_offset(rows, cols)
+    buf = np.zeros(off + rows * (cols // W4_GROUP) * 2, dtype=np.uint8)
+    _load().synth_codes_u4(seed, stream, rows * cols // 2, buf.ctypes.data)
+    sc = normal(seed, stream + (1 << 40), (rows * (cols // W4_GROUP),), 0.25, "f32", mean=1.0)
+    sc = np.abs(sc) * np.float32(std * W4_SCALE_PER_STD)
+    buf[off:] = f32_to_bf16(sc).view(np.uint8)
+    return buf
+
+
+def w4_dequant(buf: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """float64 [rows, cols] weights of a W4 buffer (for tests)."""
+    q = buf[: rows * cols // 2]
+    codes = np.empty(rows * cols, dtype=np.int64)
+    codes[0::2] = q & 15
+    codes[1::2] = q >> 4
+    off = w4_scale_offset(rows, cols)
+    sc = bf16_to_f32(buf[off: off + rows * (cols // W4_GROUP) * 2].view(np.uint16)).astype(np.float64)
+    w = (codes.reshape(rows, cols) - 8).astype(np.float64)
+    return w * np.repeat(sc.reshape(rows, cols // W4_GROUP), W4_GROUP, axis=1)
+
+
 def bf16_to_f32(a: np.ndarray) -> np.ndarray:
     """Exact widening of bf16 bit patterns (uint16) to float32."""
     return (a.astype(np.uint32) << 16).view(np.float32)
@@ -126,7 +168,7 @@ class ModelShape:
     eps: float = 1e-6
     rope_base: float = 10000.0
     qk_norm: bool = True
-    wdtype: str = "bf16"  # 'bf16' or 'f32'
+    wdtype: str = "bf16"  # 'bf16', 'f32', or 'w4' (4-bit layer matrices; gains, embedding, LM head bf16)
     kv_dtype: str = "bf16"
     embed_head: bool = True  # False: hidden-state in/out (one layer, no embedding / LM head)
 
@@ -144,15 +186,19 @@ class ModelShape:
         return 2 * self.kvdim * es
 
     def layer_weight_bytes(self) -> int:
-        es = 2 if self.wdtype == "bf16" else 4
+        es = 4 if self.wdtype == "f32" else 2
         H, F = self.hidden, self.ffn
-        mats = (self.qdim + 2 * self.kvdim) * H + H * self.qdim + 3 * F * H
         norms = 2 * H + (2 * self.head_dim if self.qk_norm else 0)
+        if self.wdtype == "w4":
+            dims = [(self.qdim, H), (self.kvdim, H), (self.kvdim, H), (H, self.qdim), (F, H), (F, H), (H, F)]
+            # codes and scales (the 256-byte alignment pad is not read)
+            return sum(r * c // 2 + r * (c // W4_GROUP) * 2 for r, c in dims) + norms * 2
+        mats = (self.qdim + 2 * self.kvdim) * H + H * self.qdim + 3 * F * H
         return (mats + norms) * es
 
     def step_weight_bytes(self) -> int:
         """Weight bytes one decode step streams (embedding rows not included)."""
-        es = 2 if self.wdtype == "bf16" else 4
+        es = 4 if self.wdtype == "f32" else 2
         b = self.n_layers * self.layer_weight_bytes()
         if self.embed_head:
             b += self.vocab * self.hidden * es + self.hidden * es
@@ -181,6 +227,7 @@ TINY = ModelShape(n_layers=2, hidden=256, n_heads=4, n_kv_heads=4, head_dim=64, 
                   qk_norm=False, wdtype="f32", kv_dtype="f32")
 Q8B = ModelShape(n_layers=36, hidden=4096, n_heads=32, n_kv_heads=8, head_dim=128, ffn=12288, vocab=151936)
 Q8B_LAYER = replace(Q8B, n_layers=1, embed_head=False)
+Q8B_W4 = replace(Q8B, wdtype="w4")
 
 WORKLOADS: Dict[str, Workload] = {
     "tiny": Workload("tiny", TINY, batch=1, steps=16, kv_len="fixed:32"),
@@ -188,6 +235,7 @@ WORKLOADS: Dict[str, Workload] = {
     "q8b_b1": Workload("q8b_b1", Q8B, batch=1, steps=128, kv_len="fixed:1024", prompt=1024),
     "q8b_b16": Workload("q8b_b16", Q8B, batch=16, steps=64, kv_len="loguniform:32:4096"),
     "q8b_b8_paged": Workload("q8b_b8_paged", Q8B, batch=8, steps=32, kv_len="uniform:4096:16384", paged=True),
+    "q8b_w4_b1": Workload("q8b_w4_b1", Q8B_W4, batch=1, steps=128, kv_len="fixed:1024"),
 }
 
 
@@ -222,11 +270,15 @@ def layer_weights(shape: ModelShape, layer: int, seed: int = SEED_WEIGHTS, std: 
             "w_gate": (F, H), "w_up": (F, H), "w_down": (H, F)}
     out = {}
     for i, name in enumerate(_MATS):
-        out[name] = normal(seed, layer * 32 + i, dims[name], std, shape.wdtype)
+        if shape.wdtype == "w4":
+            out[name] = w4_matrix(seed, layer * 32 + i, dims[name][0], dims[name][1], std)
+        else:
+            out[name] = normal(seed, layer * 32 + i, dims[name], std, shape.wdtype)
+    gt = "bf16" if shape.wdtype == "w4" else shape.wdtype
     names = ["attn_norm", "mlp_norm"] + (["q_norm", "k_norm"] if shape.qk_norm else [])
     for name in names:
         n = D if name in ("q_norm", "k_norm") else H
-        out[name] = _gain(n, shape.wdtype, gains, seed, layer * 32 + 16 + _GAINS.index(name))
+        out[name] = _gain(n, gt, gains, seed, layer * 32 + 16 + _GAINS.index(name))
     return out
 
 
@@ -234,9 +286,10 @@ def model_weights(shape: ModelShape, seed: int = SEED_WEIGHTS, std: float = 0.02
     """Weights of a model: matrices N(0, std); norm gains per `gains` ('unit' or 'random')."""
     w: Dict[str, object] = {"layers": [layer_weights(shape, l, seed, std, gains) for l in range(shape.n_layers)]}
     if shape.embed_head:
-        w["embed"] = normal(seed, _STREAM_EMBED, (shape.vocab, shape.hidden), std, shape.wdtype)
-        w["lm_head"] = normal(seed, _STREAM_LM, (shape.vocab, shape.hidden), std, shape.wdtype)
-        w["final_norm"] = _gain(shape.hidden, shape.wdtype, gains, seed, _STREAM_FINAL_GAIN)
+        et = "bf16" if shape.wdtype == "w4" else shape.wdtype
+        w["embed"] = normal(seed, _STREAM_EMBED, (shape.vocab, shape.hidden), std, et)
+        w["lm_head"] = normal(seed, _STREAM_LM, (shape.vocab, shape.hidden), std, et)
+        w["final_norm"] = _gain(shape.hidden, et, gains, seed, _STREAM_FINAL_GAIN)
     return w
 
 
@@ -250,13 +303,14 @@ def with_gains(shape: ModelShape, weights: Dict[str, object], gains: str = "rand
     layers = []
     for l, lw in enumerate(weights["layers"]):
         nl = dict(lw)
+        gt = "bf16" if shape.wdtype == "w4" else shape.wdtype
         for name in ["attn_norm", "mlp_norm"] + (["q_norm", "k_norm"] if shape.qk_norm else []):
             n = D if name in ("q_norm", "k_norm") else H
-            nl[name] = _gain(n, shape.wdtype, gains, seed, l * 32 + 16 + _GAINS.index(name))
+            nl[name] = _gain(n, gt, gains, seed, l * 32 + 16 + _GAINS.index(name))
         layers.append(nl)
     out["layers"] = layers
     if shape.embed_head:
-        out["final_norm"] = _gain(H, shape.wdtype, gains, seed, _STREAM_FINAL_GAIN)
+        out["final_norm"] = _gain(H, "bf16" if shape.wdtype == "w4" else shape.wdtype, gains, seed, _STREAM_FINAL_GAIN)
     return out
 
 

@@ -106,3 +106,15 @@ void synth_uniform_f64(uint64_t seed, uint64_t stream, int64_t n, double* out) {
 void synth_fill_u16(uint16_t v, int64_t n, uint16_t* out) {
     for (int64_t i = 0; i < n; ++i) out[i] = v;
 }
+
+/* n_bytes bytes of uniform 4-bit codes, two per byte: byte i holds code
+ * 2i in its low nibble and code 2i + 1 in its high nibble, each the top 4
+ * bits of its own word (the layout of the W4 matrices, codes in row order) */
+void synth_codes_u4(uint64_t seed, uint64_t stream, int64_t n_bytes, uint8_t* out) {
+    const uint64_t key = stream_key(seed, stream);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n_bytes; ++i) {
+        const uint64_t a = splitmix64(key + (uint64_t)(2 * i)), b = splitmix64(key + (uint64_t)(2 * i + 1));
+        out[i] = (uint8_t)((a >> 60) | ((b >> 60) << 4));
+    }
+}

@@ -269,3 +269,29 @@ def test_q8b_b16_32_row_steps_top1(q8b):
     assert worst <= TOL
     assert agree >= 0.99
     plan.close()
+
+
+def test_q8b_w4_b1_greedy_steps_match_oracle():
+    # the 36-layer model with 4-bit layer matrices (bf16 embedding and LM
+    # head), 1024 cached random keys, 6 greedy steps with the oracle
+    # teacher-forced on the GPU's tokens
+    import torch
+
+    shape = synth.Q8B_W4
+    L0, steps = 1024, 6
+    cap = L0 + steps + 8
+    t0 = time.time()
+    w = synth.model_weights(shape)
+    dm = harness.DeviceModel(shape, w)
+    orc = oracle.Oracle(shape, w)
+    log("q8b W4 B=1: weights in %.1fs; %d cached keys, %d greedy steps" % (time.time() - t0, L0, steps))
+    cache = synth.kv_sequence(shape, 0, L0, cap)
+    kv = harness.DeviceKV(shape, 1, cap)
+    kv.load_sequence(0, cache["k"], cache["v"], L0)
+    plan = harness.build_plan(shape, 1, cap)
+    out = _decode(plan, dm, kv, synth.tokens(synth.WORKLOADS["q8b_w4_b1"]), [L0], steps, shape)
+    worst, agree = _check_rows(out, orc, [cache], [L0], [0])
+    log("  max|d|/std = %.3g, top-1 = %.3f (%.1fs)" % (worst, agree, time.time() - t0))
+    assert worst <= TOL
+    assert agree >= 0.99
+    plan.close()

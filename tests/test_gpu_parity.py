@@ -447,3 +447,41 @@ def test_static_schedule_equals_event_runtime(mid_weights, B, paged):
         worst, agree = compare(a, orc, rows=rows)
         log("  static schedule vs oracle: max|d|/std = %.3g, top-1 = %.3f" % (worst, agree))
         assert worst <= 2e-2 and agree >= 0.99
+
+
+# ---------------------------------------------------------------- 4-bit weights (W4A16, batch <= 2)
+MID_W4 = replace(MID, wdtype="w4")
+
+
+@pytest.fixture(scope="module")
+def mid_w4_weights():
+    return synth.model_weights(MID_W4)
+
+
+@pytest.mark.parametrize("B,lens,gains", [(1, [300], "unit"), (2, [5, 700], "unit"), (1, [77], "random")])
+def test_mid_w4_matches_oracle(mid_w4_weights, B, lens, gains):
+    log("mid W4: B=%d lens=%s gains=%s" % (B, lens, gains))
+    w = mid_w4_weights if gains == "unit" else synth.with_gains(MID_W4, mid_w4_weights, "random")
+    cap = max(lens) + 8
+    s = make_setup(MID_W4, B, lens, cap, weights=w)
+    plan = plan_for(s)
+    kv = device_kv(s)
+    out, err = run_gpu(s, plan, kv, _tokens(MID_W4, B, 12), 2)
+    assert err == 0
+    orc, caches = run_oracle(s, out)
+    worst, agree = compare(out, orc)
+    log("  max|d|/std = %.3g, top-1 = %.3f" % (worst, agree))
+    assert worst <= 2e-2 and agree >= 0.99
+    _check_appended(s, kv, caches, list(range(B)), 2)
+    plan.close()
+
+
+def test_mid_w4_modes_bitwise(mid_w4_weights):
+    # persistent = kernel-per-op = no prefetch = static schedule; several steps per launch
+    log("mid W4 B=2: persistent vs kernel-per-op vs no prefetch vs static schedule")
+    s = make_setup(MID_W4, 2, [100, 333], 400, weights=mid_w4_weights)
+    t0 = _tokens(MID_W4, 2, 13)
+    a, _ = _logits_seq(s, 3, tokens=t0, kv_chunk=128, kv_chunk_max=128)
+    for o in (dict(mode=1), dict(prefetch_kb=-1), dict(schedule=1)):
+        b, _ = _logits_seq(s, 3, tokens=t0, kv_chunk=128, kv_chunk_max=128, **o)
+        _bitwise(a, b)

@@ -533,3 +533,68 @@ def test_final_gain_closed_form_with_one_channel():
     x = w["embed"][tok].astype(np.float64)
     s = float(gf[c]) * x[c] / math.sqrt(np.mean(x * x) + shape.eps)
     np.testing.assert_allclose(logits, w["lm_head"][:, c].astype(np.float64) * s, rtol=1e-6, atol=1e-7)
+
+
+# ----------------------------------------------------------------- 4-bit weights (W4A16)
+# Format: codes in row order, two per byte, low nibble first; from byte
+# rows * cols / 2 rounded up to 256, one bf16 scale per 128 inputs of a row;
+# the weight is (code - 8) * scale.
+
+def _w4_buffer(codes, scales):
+    rows, cols = codes.shape
+    off = synth.w4_scale_offset(rows, cols)
+    buf = np.zeros(off + scales.size * 2, dtype=np.uint8)
+    flat = codes.reshape(-1).astype(np.uint8)
+    buf[: rows * cols // 2] = flat[0::2] | (flat[1::2] << 4)
+    buf[off:] = synth.f32_to_bf16(scales.astype(np.float32).reshape(-1)).view(np.uint8)
+    return buf
+
+
+def test_w4_matvec_hand_example_nibble_order_and_groups():
+    # row 0: all codes 9 (weight +scale) with scale 0.5 in group 0, 0.25 in group 1
+    # row 1: codes alternate 0, 15 (weights -8s, +7s), scale 2 everywhere
+    # row 2: only column 0 nonzero (code 15 in the low nibble of byte 0)
+    rows, cols = 3, 256
+    codes = np.full((rows, cols), 8)
+    codes[0, :] = 9
+    codes[1, 0::2] = 0
+    codes[1, 1::2] = 15
+    codes[2, 0] = 15
+    scales = np.array([[0.5, 0.25], [2.0, 2.0], [1.0, 1.0]])
+    x = f32(RNG.normal(size=cols))
+    y = oracle.matvec(_w4_buffer(codes, scales), x, w4_shape=(rows, cols))
+    xd = x.astype(np.float64)
+    want = [0.5 * xd[:128].sum() + 0.25 * xd[128:].sum(),
+            2.0 * (-8.0 * xd[0::2].sum() + 7.0 * xd[1::2].sum()),
+            7.0 * xd[0]]
+    np.testing.assert_allclose(y, np.array(want, dtype=np.float32), rtol=1e-6, atol=1e-6)
+
+
+def test_w4_matvec_equals_float64_of_the_dequantised_matrix():
+    rows, cols = 40, 1024
+    buf = synth.w4_matrix(3, 9, rows, cols)
+    x = f32(RNG.normal(size=cols))
+    ref = synth.w4_dequant(buf, rows, cols) @ x.astype(np.float64)
+    np.testing.assert_allclose(oracle.matvec(buf, x, w4_shape=(rows, cols)), ref.astype(np.float32), rtol=1e-6,
+                               atol=1e-7)
+
+
+def test_w4_layer_equals_layer_on_dequantised_matrices():
+    # (code - 8) * bf16 scale is exact in fp32, so the layer with W4 matrices
+    # equals, bit for bit, the layer given the dequantised fp32 matrices and
+    # the same (bf16-valued) gains in fp32
+    shape = _tiny_shape(hidden=1024, n_heads=8, n_kv_heads=2, head_dim=128, ffn=1024, wdtype="w4", kv_dtype="bf16")
+    w = synth.model_weights(shape, seed=21, gains="random")
+    lw = w["layers"][0]
+    dims = {"wq": (1024, 1024), "wk": (256, 1024), "wv": (256, 1024), "wo": (1024, 1024), "w_gate": (1024, 1024),
+            "w_up": (1024, 1024), "w_down": (1024, 1024)}
+    f_shape = replace(shape, wdtype="f32")
+    lf = {k: (f32(synth.w4_dequant(v, *dims[k])) if k in dims else synth.bf16_to_f32(v)) for k, v in lw.items()}
+    pos = 7
+    ca = _cache(shape, 10, pos)
+    cb = {k: v.copy() for k, v in ca.items()}
+    x = f32(RNG.normal(size=shape.hidden))
+    ya = oracle.Oracle(shape, {"layers": [lw]}).layer_forward(0, ca, pos, x)
+    yb = oracle.Oracle(f_shape, {"layers": [lf]}).layer_forward(0, cb, pos, x)  # same bf16 cache
+    np.testing.assert_array_equal(ya, yb)
+    np.testing.assert_array_equal(ca["k"], cb["k"])
