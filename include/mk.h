@@ -120,6 +120,12 @@ enum mk_device_error {
  *                and kv_chunk_max are replaced by the searched length. Same
  *                task bodies: the bits of the event runtime at that length.
  *                Not with jit = 1.
+ *  prefill       1: a prompt-chunk plan for mk_prefill: the `batch` rows of a
+ *                step are consecutive positions of one sequence, all reading
+ *                and writing sequence 0's K/V; an append level (QK-norm,
+ *                RoPE, K/V store) runs between QKV and attention, so each
+ *                row's attention sees the rows before it. Ahead-of-time
+ *                attention only (not jit = 1); token input only.
  */
 typedef struct mk_exec_opts {
     int32_t mode;
@@ -138,6 +144,7 @@ typedef struct mk_exec_opts {
     int32_t kv_chunk_max;
     int32_t lds_preload;
     int32_t schedule;
+    int32_t prefill;
 } mk_exec_opts;
 
 /*
@@ -224,7 +231,8 @@ typedef struct mk_kv_cache {
 /* Plan summary (mk_plan_query). */
 typedef struct mk_plan_info {
     int32_t workers, sched_waves, n_aot_tasks, n_events, n_levels, max_jit_tasks, kv_chunk, max_splits;
-    int32_t tasks_per_op[8]; /* indexed by op: 1 QKV, 2 O, 3 gate/up, 4 down, 5 LM head, 6 attention (AOT) */
+    int32_t tasks_per_op[12]; /* indexed by op: 1 QKV, 2 O, 3 gate/up, 4 down, 5 LM head, 6 attention (AOT),
+                                 7 embedding, 8 append (prefill plans) */
     int64_t weight_bytes_per_step; /* weight bytes one step streams (matrices, gains, LM head) */
     int64_t kv_bytes_per_token;    /* K + V bytes per cached position over all layers */
     int64_t device_bytes;          /* device memory the plan owns */
@@ -325,6 +333,26 @@ int mk_decode_step_greedy(mk_plan* plan, const mk_weights* weights, const mk_kv_
  */
 int mk_decode_steps_greedy(mk_plan* plan, const mk_weights* weights, const mk_kv_cache* kv, int32_t* tokens,
                            int32_t* seq_lens, float* logits, int32_t n_steps, int32_t* out_tokens, void* stream);
+
+/*
+ * Prefill of T prompt tokens of one sequence through the decode runtime, a
+ * chunk of `batch` positions per persistent launch (the other half of the
+ * Ada-MK hybrid engine, zingnex.cn 技术三 and gist.science "Methodik" 2,
+ * here inside the same task-graph runtime): ceil(T / batch) launches of a
+ * plan built with opts.prefill = 1, instead of T decode steps.
+ *  tokens  device int32 [T]: the prompt, positions pos0 .. pos0 + T - 1.
+ *  pos0    positions already cached for the sequence (host int, >= 0);
+ *          pos0 + T <= max_seq_len.
+ *  kv      the sequence's cache: contiguous (sequence 0 of the layout) or
+ *          paged (row 0 of the block table).
+ *  logits  device float [vocab]: the logits after the last prompt token.
+ * The last chunk, if shorter, repeats its last position in the remaining
+ * rows; their appends store the same bits at the same place. The plan's own
+ * device memory holds the chunk's tokens, lengths and logits. Returns as
+ * mk_decode_step; MK_ERR_STATE for a plan without opts.prefill.
+ */
+int mk_prefill(mk_plan* plan, const mk_weights* weights, const mk_kv_cache* kv, const int32_t* tokens, int32_t pos0,
+               int32_t T, float* logits, void* stream);
 
 /*
  * Hidden-state variant for hidden_io plans: x_in, x_out are device float

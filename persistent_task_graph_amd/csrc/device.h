@@ -89,6 +89,7 @@ struct KParams {
     int prefetch_kb;          // next-task weight bytes pulled into L2 per worker (KB)
     int pre_slots;            // LDS preload slots per wave for the awaited GEMV task (0: off)
     int w4;                   // 1: the layer matrices are W4 buffers (batch <= 2); gains, embedding, LM head bf16
+    int prefill;              // 1: the batch rows are consecutive positions of sequence 0 (prompt chunk)
     int32_t* greedy_tokens;   // greedy step: next token of each sequence written here (else null)
     int32_t* greedy_lens;     // greedy step: each sequence's length advanced here
     int32_t* out_tokens;      // greedy steps: step s's tokens at [s * B, s * B + B) (or null)

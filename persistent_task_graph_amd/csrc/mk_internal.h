@@ -22,9 +22,10 @@ enum Op : uint8_t {
     OP_LM = 5,      // logits = W_lm . RMSNorm(x_final)        (AOT GEMV)
     OP_ATTN = 6,    // split-KV attention + last-arrival combine (JIT, or AOT fallback)
     OP_EMBED = 7,   // x_0 = E[token] (AOT row copy)
+    OP_APPEND = 8,  // prefill plans: QK-norm + RoPE + K/V store of rows (b, g), before attention
 };
 
-constexpr int kNumOps = 8;
+constexpr int kNumOps = 9;
 
 // Task record, 32 bytes (the MPK article's TaskDesc, §2.1, as our own
 // fixed-size record: operator, tile, the one event it waits on and the one
@@ -85,6 +86,7 @@ struct HostPlan {
     int sched_wgs = 0;
     int jit = 1;  // 1 JIT, 0 AOT attention
     int schedule = 0;  // 0 event runtime, 1 static (searched) schedule
+    int prefill = 0;   // 1: the batch rows are consecutive positions of one sequence (prompt chunks)
     double predicted_layer_us = 0;  // static schedule: cost-model time of one layer
     int kv_chunk = 256;     // base keys per split (sizes the partial records)
     int kv_chunk_max = 4096; // largest per-step chunk
@@ -129,6 +131,8 @@ MK_HD inline int ev_o(int l) { return 5 * l + 2; }
 MK_HD inline int ev_gateup(int l) { return 5 * l + 3; }
 MK_HD inline int ev_down(int l) { return 5 * l + 4; }
 MK_HD inline int ev_embed(int n_layers) { return 5 * n_layers; }
+// prefill plans: layer l's appends done
+MK_HD inline int ev_append(int l, int n_layers) { return 5 * n_layers + 1 + l; }
 
 MK_HD inline int n_splits_for(int keys, int chunk) { return (keys + chunk - 1) / chunk; }
 

@@ -41,6 +41,7 @@ static int64_t op_rows(const mk_model_desc& d, int op) {
         case OP_DOWN: return d.hidden;
         case OP_LM: return d.vocab;
         case OP_EMBED: return d.hidden;
+        case OP_APPEND: return (int64_t)d.batch * d.n_kv_heads;
         default: return 0;
     }
 }
@@ -225,6 +226,10 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
     if (o.schedule == 1 && o.jit == 1) return fail(err, "the static schedule has no JIT attention (opts.jit 0 or 2)");
     p.jit = (o.jit == 1) ? 1 : 0;  // default: AOT attention slots
     p.schedule = o.schedule;
+    if (o.prefill < 0 || o.prefill > 1) return fail(err, "opts.prefill must be 0 or 1");
+    p.prefill = o.prefill;
+    if (p.prefill && (o.jit == 1 || d.hidden_io))
+        return fail(err, "prefill plans need ahead-of-time attention and token input (no jit, no hidden_io)");
     // scheduler workgroups exist only to deal JIT attention; without them
     // every CU is a worker
     p.sched_wgs = p.jit ? (o.sched_wgs > 0 ? o.sched_wgs : 4) : 0;
@@ -257,7 +262,7 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
     }
 
     const int L = d.n_layers, W = p.workers, B = d.batch, Hkv = d.n_kv_heads;
-    p.events.assign(5 * L + 1, EventRec{0, -1});
+    p.events.assign(5 * L + 1 + (p.prefill ? L : 0), EventRec{0, -1});
     int rot = 0;
     std::vector<std::vector<int32_t>> q(W);
     int level = 0;
@@ -292,7 +297,7 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
     };
     auto add_gemv = [&](int op, int layer, int wait, int sig, int min_rows) {
         const int64_t rows = op_rows(d, op);
-        if (p.schedule == 1 && op != OP_EMBED) {
+        if (p.schedule == 1 && op != OP_EMBED && op != OP_APPEND) {
             const bool mf = d.weight_dtype == MK_BF16 && d.batch >= 3;
             add_level(op, layer);
             std::vector<int> ids;
@@ -348,6 +353,10 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
     }
     for (int l = 0; l < L; ++l) {
         add_gemv(OP_QKV, l, prev, ev_qkv(l), 1);
+        // prefill: the rows' keys and values are stored in a level of their
+        // own, so that every row's attention finds the rows before it
+        if (p.prefill) add_gemv(OP_APPEND, l, ev_qkv(l), ev_append(l, L), 1);
+        const int attn_wait = p.prefill ? ev_append(l, L) : ev_qkv(l);
         // attention: one level; tasks exist in AOT mode only (JIT tasks are
         // created on the device by the scheduler waves)
         add_level(OP_ATTN, l);
@@ -367,7 +376,7 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
                     t.layer = (uint16_t)l;
                     t.a0 = bg;
                     t.a1 = sp;
-                    t.wait_ev = ev_qkv(l);
+                    t.wait_ev = attn_wait;
                     t.sig_ev = ev_attn(l);
                     t.level = level;
                     const int id = (int)p.tasks.size();
@@ -388,7 +397,7 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
                 t.layer = (uint16_t)l;
                 t.a0 = i;
                 t.a1 = S;
-                t.wait_ev = ev_qkv(l);
+                t.wait_ev = attn_wait;
                 t.sig_ev = ev_attn(l);
                 t.level = level;
                 int id = (int)p.tasks.size();

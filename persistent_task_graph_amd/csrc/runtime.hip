@@ -126,6 +126,15 @@ __global__ __launch_bounds__(64) void k_argmax_final(const ArgmaxScratch* sc, in
 }
 static_assert(kArgBlocks == 64, "k_argmax_final reduces one slice winner per lane");
 
+// prefill chunk: row i takes prompt position min(i, n - 1) of the chunk
+__global__ void k_prefill_rows(const int32_t* tokens, int n, int pos, int B, int32_t* ptok, int32_t* plen) {
+    const int i = threadIdx.x;
+    if (i >= B) return;
+    const int j = i < n ? i : n - 1;
+    ptok[i] = tokens[j];
+    plen[i] = pos + j;
+}
+
 }  // namespace mk
 
 // ============================================================================
@@ -168,6 +177,9 @@ struct mk_plan {
     int32_t* d_argi = nullptr;
     uint32_t* d_argc = nullptr;
     mk_trace_rec* d_trace = nullptr;
+    int32_t* d_ptok = nullptr;   // prefill plans: the chunk's tokens
+    int32_t* d_plen = nullptr;   // prefill plans: the chunk's positions
+    float* d_plogits = nullptr;  // prefill plans: the chunk's logits [batch, vocab]
     int32_t* d_trace_n = nullptr;
     int trace_cap = 0;
     int64_t act_stride = 0, off_qkv = 0, off_attn = 0, off_xmid = 0, off_h = 0, off_xnext = 0;
@@ -280,6 +292,9 @@ bool upload_plan(mk_plan* pl) {
     pl->trace_cap = d.opts.trace > 0 ? d.opts.trace : 0;
     Region r_tr = take(sizeof(mk_trace_rec) * (size_t)hp.workers * pl->trace_cap);
     Region r_trn = take(sizeof(int32_t) * (size_t)hp.workers);
+    Region r_ptok = take(hp.prefill ? sizeof(int32_t) * (size_t)B : 0);
+    Region r_plen = take(hp.prefill ? sizeof(int32_t) * (size_t)B : 0);
+    Region r_plog = take(hp.prefill ? sizeof(float) * (size_t)B * d.vocab : 0);
     pl->dbytes = align_up(at, 256);
     if (!hip_ok(hipSetDevice(pl->device), "hipSetDevice")) return false;
     if (!hip_ok(hipMalloc((void**)&pl->dmem, pl->dbytes), "hipMalloc(plan)")) return false;
@@ -313,6 +328,11 @@ bool upload_plan(mk_plan* pl) {
     pl->d_argc = (uint32_t*)(m + r_argc.off);
     pl->d_trace = pl->trace_cap ? (mk_trace_rec*)(m + r_tr.off) : nullptr;
     pl->d_trace_n = (int32_t*)(m + r_trn.off);
+    if (hp.prefill) {
+        pl->d_ptok = (int32_t*)(m + r_ptok.off);
+        pl->d_plen = (int32_t*)(m + r_plen.off);
+        pl->d_plogits = (float*)(m + r_plog.off);
+    }
     pl->ctrl_off = r_ev.off;
     pl->ctrl_bytes = r_ctrl.off + r_ctrl.bytes - r_ev.off;
     auto up = [&](void* dst, const void* src, size_t n) {
@@ -457,6 +477,7 @@ KParams make_params(const mk_plan* pl, const mk_weights* w, const mk_kv_cache* k
     p.prefetch_kb = d.opts.prefetch_kb == 0 ? 256 : (d.opts.prefetch_kb < 0 ? 0 : d.opts.prefetch_kb);
     p.pre_slots = lds_preload_on(pl) ? kPreSlots : 0;
     p.w4 = d.weight_dtype == MK_W4 ? 1 : 0;
+    p.prefill = hp.prefill;
     p.trace = pl->d_trace;
     p.trace_n = pl->d_trace_n;
     p.trace_cap = pl->trace_cap;
@@ -485,8 +506,9 @@ int check_step_args(mk_plan* pl, const mk_weights* w, const mk_kv_cache* kv, con
                        MK_ERR_ARG;
             if (kv->layer_stride * es >= ((int64_t)1 << 31))
                 return set_err("paged KV: one layer's pool must be smaller than 2 GiB (32-bit buffer offsets)"), MK_ERR_ARG;
-        } else if (kv->layer_stride < (int64_t)d.batch * d.n_kv_heads * d.max_seq_len * d.head_dim) {
-            return set_err("contiguous KV: layer_stride is smaller than batch * n_kv_heads * max_seq_len * head_dim"),
+        } else if (kv->layer_stride < (int64_t)(pl->hp.prefill ? 1 : d.batch) * d.n_kv_heads * d.max_seq_len * d.head_dim) {
+            // a prefill plan's rows all use sequence 0
+            return set_err("contiguous KV: layer_stride is smaller than sequences * n_kv_heads * max_seq_len * head_dim"),
                    MK_ERR_ARG;
         }
     }
@@ -633,7 +655,7 @@ int mk_plan_query(const mk_plan* pl, mk_plan_info* info) {
     info->max_jit_tasks = hp.max_jit_tasks;
     info->kv_chunk = hp.kv_chunk;
     info->max_splits = hp.max_splits;
-    for (int i = 0; i < 8 && i < kNumOps; ++i) info->tasks_per_op[i] = hp.tasks_per_op[i];
+    for (int i = 0; i < 12 && i < kNumOps; ++i) info->tasks_per_op[i] = hp.tasks_per_op[i];
     info->weight_bytes_per_step = hp.weight_bytes;
     info->kv_bytes_per_token = hp.kv_bytes_per_token;
     info->device_bytes = (int64_t)pl->dbytes;
@@ -650,6 +672,7 @@ int mk_decode_step(mk_plan* pl, const mk_weights* w, const mk_kv_cache* kv, cons
     int rc = check_step_args(pl, w, kv, seq_lens, tokens, logits);
     if (rc) return rc;
     if (pl->hp.desc.hidden_io) return set_err("hidden_io plan: use mk_decode_step_hidden"), MK_ERR_STATE;
+    if (pl->hp.prefill) return set_err("prefill plan: use mk_prefill"), MK_ERR_STATE;
     return launch_step(pl, w, kv, tokens, seq_lens, nullptr, logits, (hipStream_t)stream);
 }
 
@@ -658,6 +681,7 @@ int mk_decode_step_greedy(mk_plan* pl, const mk_weights* w, const mk_kv_cache* k
     int rc = check_step_args(pl, w, kv, seq_lens, tokens, logits);
     if (rc) return rc;
     if (pl->hp.desc.hidden_io) return set_err("hidden_io plan has no logits"), MK_ERR_STATE;
+    if (pl->hp.prefill) return set_err("prefill plan: use mk_prefill"), MK_ERR_STATE;
     return launch_step(pl, w, kv, tokens, seq_lens, nullptr, logits, (hipStream_t)stream, tokens, seq_lens);
 }
 
@@ -666,6 +690,7 @@ int mk_decode_steps_greedy(mk_plan* pl, const mk_weights* w, const mk_kv_cache* 
     int rc = check_step_args(pl, w, kv, seq_lens, tokens, logits);
     if (rc) return rc;
     if (pl->hp.desc.hidden_io) return set_err("hidden_io plan has no logits"), MK_ERR_STATE;
+    if (pl->hp.prefill) return set_err("prefill plan: use mk_prefill"), MK_ERR_STATE;
     if (n_steps < 1 || n_steps > kMaxStepsPerLaunch)
         return set_err("n_steps must be in [1, " + std::to_string(kMaxStepsPerLaunch) + "]"), MK_ERR_ARG;
     if (pl->hp.desc.opts.mode == MK_PERSISTENT && n_steps > 1 && (pl->hp.jit || pl->hp.desc.opts.lds_stream == 1))
@@ -673,6 +698,33 @@ int mk_decode_steps_greedy(mk_plan* pl, const mk_weights* w, const mk_kv_cache* 
                MK_ERR_UNSUPPORTED;
     return launch_step(pl, w, kv, tokens, seq_lens, nullptr, logits, (hipStream_t)stream, tokens, seq_lens, n_steps,
                        out_tokens);
+}
+
+int mk_prefill(mk_plan* pl, const mk_weights* w, const mk_kv_cache* kv, const int32_t* tokens, int32_t pos0, int32_t T,
+               float* logits, void* stream) {
+    if (!pl) return set_err("null plan"), MK_ERR_ARG;
+    if (!tokens || !logits) return set_err("null argument"), MK_ERR_ARG;
+    const mk_model_desc& d = pl->hp.desc;
+    if (T < 1 || pos0 < 0 || (int64_t)pos0 + T > d.max_seq_len)
+        return set_err("prefill needs T >= 1, pos0 >= 0 and pos0 + T <= max_seq_len"), MK_ERR_ARG;
+    int rc = check_step_args(pl, w, kv, tokens, tokens, logits);
+    if (rc) return rc;
+    if (!pl->hp.prefill) return set_err("mk_prefill needs a plan built with opts.prefill = 1"), MK_ERR_STATE;
+    hipStream_t st = (hipStream_t)stream;
+    const int B = d.batch;
+    int n = 0;
+    for (int c = 0; c < T; c += B) {
+        n = std::min(B, T - c);
+        hipLaunchKernelGGL(k_prefill_rows, dim3(1), dim3(64), 0, st, tokens + c, n, pos0 + c, B, pl->d_ptok, pl->d_plen);
+        if (!hip_ok(hipGetLastError(), "k_prefill_rows launch")) return MK_ERR_HIP;
+        rc = launch_step(pl, w, kv, pl->d_ptok, pl->d_plen, nullptr, pl->d_plogits, st);
+        if (rc) return rc;
+    }
+    if (!hip_ok(hipMemcpyAsync(logits, pl->d_plogits + (size_t)(n - 1) * d.vocab, sizeof(float) * d.vocab,
+                               hipMemcpyDeviceToDevice, st),
+                "hipMemcpyAsync(prefill logits)"))
+        return MK_ERR_HIP;
+    return MK_OK;
 }
 
 int mk_decode_step_hidden(mk_plan* pl, const mk_weights* w, const mk_kv_cache* kv, const float* x_in,

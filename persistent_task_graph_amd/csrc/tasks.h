@@ -987,6 +987,82 @@ __device__ __forceinline__ void lm_greedy(const KParams& p, int r0, int r1) {
     __hip_atomic_store(p.lm_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Element offset of (layer l, sequence b, KV head g, position pos) in the
+// cache, or -1 for a paged position whose block-table entry lies outside
+// the pool (the entry is the caller's data: it is checked, not trusted).
+__device__ __forceinline__ int64_t kv_offset(const KParams& p, int l, int b, int g, int pos) {
+    if (p.prefill) b = 0;  // prefill plans: every row is a position of sequence 0
+    if (!p.paged) return (int64_t)l * p.kv_layer_stride + ((int64_t)(b * p.Hkv + g) * p.cap + pos) * p.D;
+    const int blk = p.block_table[(int64_t)b * p.max_blocks + pos / p.kv_block];
+    if ((unsigned)blk >= (unsigned)p.n_pool_blocks) return -1;
+    return (int64_t)l * p.kv_layer_stride + ((int64_t)blk * p.Hkv + g) * p.kv_block * p.D + (int64_t)(pos % p.kv_block) * p.D;
+}
+
+// RMSNorm over one head (D = 64 or 128) held by a wave as D/64 values per
+// lane (element j in lane j % 64, slot j / 64), then rotate-half RoPE. The
+// gains g (same slots) and this lane's (cos, sin) are loaded by the caller
+// ahead of time.
+template <int D>
+__device__ __forceinline__ void head_norm_rope(float (&v)[2], const float (&g)[2], bool norm, float eps, float2 cs) {
+    const int lane = threadIdx.x & 63;
+    constexpr int per = D / 64;
+    if (norm) {
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < per; ++i) ss += v[i] * v[i];
+        ss = wave_sum(ss);
+        const float rs = 1.0f / sqrtf(ss / (float)D + eps);
+#pragma unroll
+        for (int i = 0; i < per; ++i) v[i] = (v[i] * rs) * g[i];
+    }
+    if constexpr (per == 2) {
+        // pair (lane, lane + 64) sits in one lane
+        const float a = v[0], b = v[1];
+        v[0] = a * cs.x - b * cs.y;
+        v[1] = b * cs.x + a * cs.y;
+    } else {
+        // D = 64: pair (i, i + 32) spans lanes i and i + 32
+        const float other = halves_partner(v[0]);
+        if (lane < 32) v[0] = v[0] * cs.x - other * cs.y;
+        else v[0] = v[0] * cs.x + other * cs.y;
+    }
+}
+
+// Prefill plans: rows [a0, a1) of the append level, each (b, g) = (row of
+// the chunk, KV head): the new key (QK-norm, RoPE at seq_lens[b]) and value,
+// rounded to the cache type, stored at position seq_lens[b] of sequence 0
+// with agent-coherent stores (the attention level reads them on other CUs).
+// One wave per (b, g).
+template <typename WT, int D>
+__device__ __forceinline__ void append_rows(const KParams& p, const TaskRec& t, const LayerPtrs& w) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l = t.layer;
+    for (int bg = t.a0 + wave; bg < t.a1; bg += kWaves) {
+        const int b = bg / p.Hkv, g = bg % p.Hkv;
+        const int pos = p.seq_lens[b];
+        if (pos < 0 || pos + 1 > p.cap) continue;  // its attention task reports the overflow
+        const float* qkv = layer_buf(p, l, p.off_qkv) + (int64_t)b * (p.QD + 2 * p.KD);
+        float k[2] = {0.f, 0.f}, v[2] = {0.f, 0.f}, gk[2] = {1.f, 1.f};
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i) {
+            k[i] = ld_act(&qkv[(int64_t)p.QD + g * D + lane + 64 * i]);
+            v[i] = ld_act(&qkv[(int64_t)p.QD + p.KD + g * D + lane + 64 * i]);
+            if (p.qk_norm) gk[i] = load_scalar<WT>((const WT*)w.k_norm, lane + 64 * i);
+        }
+        const float2 cs = p.rope[(int64_t)pos * (D / 2) + (D == 128 ? lane : (lane & 31))];
+        head_norm_rope<D>(k, gk, p.qk_norm != 0, p.eps, cs);
+        const int64_t off = kv_offset(p, l, b, g, pos);
+        if (off < 0) {
+            if (lane == 0) raise_error(p.ctrl, MK_ERR_BLOCK_TABLE);
+            continue;
+        }
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i) {
+            st_co(&((WT*)p.kv_k)[off + lane + 64 * i], from_float<WT>(k[i]));
+            st_co(&((WT*)p.kv_v)[off + lane + 64 * i], from_float<WT>(v[i]));
+        }
+    }
+}
+
 // A GEMV task of a plan whose layer matrices are W4 (batch <= 2); the LM
 // head and the embedding stay bf16 and take the ordinary path.
 template <int NB>
@@ -1063,7 +1139,7 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
                                               int pre_rows = 0) {
     // 4-bit layer matrices (batch <= 2)
     if constexpr (std::is_same<WT, bf16_t>::value && NB <= 2) {
-        if (p.w4 && t.op != OP_LM && t.op != OP_EMBED) {
+        if (p.w4 && t.op != OP_LM && t.op != OP_EMBED && t.op != OP_APPEND) {
             run_w4_task<NB>(p, t, s, w);
             return;
         }
@@ -1074,6 +1150,10 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
     const int r0 = t.a0, r1 = t.a1;
     switch (t.op) {
         case OP_EMBED: embed_task<WT>(p, t); break;
+        case OP_APPEND:
+            if (p.D == 128) append_rows<WT, 128>(p, t, w);
+            else append_rows<WT, 64>(p, t, w);
+            break;
         case OP_QKV: {
             const float* x = layer_in(p, l);
             const int QD = p.QD, KD = p.KD, ld = QD + 2 * KD;
@@ -1434,7 +1514,9 @@ __device__ __forceinline__ Prefetch attn_prefetch_setup(const KParams& p, int l,
     f.kb_a = f.kb_b = 0;
     f.next = f.end = 0;
     f.a = f.b = make_rsrc(p.zero, 0);
-    if (p.prefetch_kb <= 0 || p.paged) return f;
+    // prefill: rows of this launch's chunk are stored by the append level,
+    // so nothing before the event may pull their lines into a cache
+    if (p.prefetch_kb <= 0 || p.paged || p.prefill) return f;
     const int b = bg / p.Hkv, g = bg % p.Hkv;
     const int pos = p.seq_lens[b];
     if (pos < 0 || pos + 1 > p.cap) return f;
@@ -1473,46 +1555,6 @@ __device__ __forceinline__ void prefetch_step(Prefetch& f) {
 
 // ---------------------------------------------------------------- attention
 
-// Element offset of (layer l, sequence b, KV head g, position pos) in the
-// cache, or -1 for a paged position whose block-table entry lies outside
-// the pool (the entry is the caller's data: it is checked, not trusted).
-__device__ __forceinline__ int64_t kv_offset(const KParams& p, int l, int b, int g, int pos) {
-    if (!p.paged) return (int64_t)l * p.kv_layer_stride + ((int64_t)(b * p.Hkv + g) * p.cap + pos) * p.D;
-    const int blk = p.block_table[(int64_t)b * p.max_blocks + pos / p.kv_block];
-    if ((unsigned)blk >= (unsigned)p.n_pool_blocks) return -1;
-    return (int64_t)l * p.kv_layer_stride + ((int64_t)blk * p.Hkv + g) * p.kv_block * p.D + (int64_t)(pos % p.kv_block) * p.D;
-}
-
-// RMSNorm over one head (D = 64 or 128) held by a wave as D/64 values per
-// lane (element j in lane j % 64, slot j / 64), then rotate-half RoPE. The
-// gains g (same slots) and this lane's (cos, sin) are loaded by the caller
-// ahead of time.
-template <int D>
-__device__ __forceinline__ void head_norm_rope(float (&v)[2], const float (&g)[2], bool norm, float eps, float2 cs) {
-    const int lane = threadIdx.x & 63;
-    constexpr int per = D / 64;
-    if (norm) {
-        float ss = 0.f;
-#pragma unroll
-        for (int i = 0; i < per; ++i) ss += v[i] * v[i];
-        ss = wave_sum(ss);
-        const float rs = 1.0f / sqrtf(ss / (float)D + eps);
-#pragma unroll
-        for (int i = 0; i < per; ++i) v[i] = (v[i] * rs) * g[i];
-    }
-    if constexpr (per == 2) {
-        // pair (lane, lane + 64) sits in one lane
-        const float a = v[0], b = v[1];
-        v[0] = a * cs.x - b * cs.y;
-        v[1] = b * cs.x + a * cs.y;
-    } else {
-        // D = 64: pair (i, i + 32) spans lanes i and i + 32
-        const float other = halves_partner(v[0]);
-        if (lane < 32) v[0] = v[0] * cs.x - other * cs.y;
-        else v[0] = v[0] * cs.x + other * cs.y;
-    }
-}
-
 // One split of the split-KV decode attention for (layer, b, g, split):
 // positions [split*C, min((split+1)*C, pos+1)). Writes the split's partial
 // (acc, m, l) and, if it is the last to arrive for (b, g), merges all
@@ -1532,6 +1574,10 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int Hkv = p.Hkv, G = p.Hq / p.Hkv;
     const int b = bg / Hkv, g = bg % Hkv;
+    // prefill plans: every row is a position of sequence 0 (shared K/V), and
+    // the row's own key and value were stored by the append level
+    const int bkv = p.prefill ? 0 : b;
+    const bool own_lds = !p.prefill;
     const float* qkv = layer_buf(p, l, p.off_qkv) + (int64_t)b * (p.QD + 2 * p.KD);
     const LayerPtrs& lw = p.lw[l];
     // 0. this wave's query heads, the new k (wave 0) and v (wave 1), and the
@@ -1580,7 +1626,7 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
     const int j0 = split * C, j1 = min(j0 + C, keys);
     const bool owner = (j1 == keys);
     const int n = j1 - j0;
-    const bool appender = owner && wave < 2;
+    const bool appender = own_lds && owner && wave < 2;
     // this lane's RoPE factors at position pos
     const float2 cs = p.rope[(int64_t)pos * (D / 2) + (D == 128 ? lane : (lane & 31))];
     asm volatile("" ::: "memory");
@@ -1612,14 +1658,14 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
     const int64_t lbase = (int64_t)l * p.kv_layer_stride;
     __amdgpu_buffer_rsrc_t krs, vrs;
     if (!p.paged) {
-        const int64_t seq = lbase + (int64_t)(b * Hkv + g) * p.cap * D;
+        const int64_t seq = lbase + (int64_t)(bkv * Hkv + g) * p.cap * D;
         krs = make_rsrc((const WT*)p.kv_k + seq, (uint32_t)p.cap * (uint32_t)(D * es));
         vrs = make_rsrc((const WT*)p.kv_v + seq, (uint32_t)p.cap * (uint32_t)(D * es));
     } else {
         krs = make_rsrc((const WT*)p.kv_k + lbase, (uint32_t)(p.kv_layer_stride * es));
         vrs = make_rsrc((const WT*)p.kv_v + lbase, (uint32_t)(p.kv_layer_stride * es));
     }
-    const int32_t* btab = p.paged ? p.block_table + (int64_t)b * p.max_blocks : nullptr;
+    const int32_t* btab = p.paged ? p.block_table + (int64_t)bkv * p.max_blocks : nullptr;
     // the split's block-table entries are staged in LDS for the batches after
     // the first (visible after the prologue barrier), so that a batch's K/V
     // requests never wait behind a block-table load
@@ -1639,7 +1685,7 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
     // check that a sequence's contiguous span, or a paged layer, is smaller).
     auto row_off = [&](int j, uint32_t add, bool staged) -> uint32_t {
         const int jj = j0 + j;
-        if (j >= n || jj == pos) return kOOB;
+        if (j >= n || (own_lds && jj == pos)) return kOOB;
         uint32_t o;
         if (p.paged) {
             const int bi = jj / p.kv_block;
@@ -1727,7 +1773,7 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
             const int j = base + it * PER_IT + wave * PPW + rr;
             const bool valid = j < n;
             float kf[E];
-            if (valid && j0 + j == pos) {
+            if (own_lds && valid && j0 + j == pos) {
 #pragma unroll
                 for (int e = 0; e < E; ++e) kf[e] = s.kn[cc * E + e];
             } else {
@@ -1767,7 +1813,7 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
         for (int it = 0; it < NIT; ++it) {
             const int j = base + it * PER_IT + wave * PPW + rr;
             float vf[E];
-            if (j < n && j0 + j == pos) {
+            if (own_lds && j < n && j0 + j == pos) {
 #pragma unroll
                 for (int e = 0; e < E; ++e) vf[e] = s.kn[128 + cc * E + e];
             } else {
@@ -1808,7 +1854,7 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
             // the hi and lo query terms accumulate in two independent chains
             mk_f32x4 sh = mk_f32x4{0.f, 0.f, 0.f, 0.f}, sl = sh;
             const int j = base + wave * WR + 16 * t + li;
-            const bool nw = j < n && j0 + j == pos;  // the new row's k comes from LDS
+            const bool nw = own_lds && j < n && j0 + j == pos;  // the new row's k comes from LDS
 #pragma unroll
             for (int q = 0; q < KS; ++q) {
                 uint4 a = kk[t * KS + q];
@@ -1869,7 +1915,7 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
             const int jw = it * PPW + rr;  // row within the wave's WR
             const int j = base + wave * WR + jw;
             float vf[E];
-            if (j < n && j0 + j == pos) {
+            if (own_lds && j < n && j0 + j == pos) {
 #pragma unroll
                 for (int e = 0; e < E; ++e) vf[e] = s.kn[128 + cc * E + e];
             } else {

@@ -23,18 +23,18 @@ MK_OK, MK_ERR_ARG, MK_ERR_HIP, MK_ERR_UNSUPPORTED, MK_ERR_STATE = 0, -1, -2, -3,
 MK_ERR_TOKEN, MK_ERR_KV_OVERFLOW, MK_ERR_TIMEOUT, MK_ERR_BLOCK_TABLE = 1, 2, 4, 8
 
 # operator ids (mk_plan_info.tasks_per_op index)
-OP_QKV, OP_O, OP_GATEUP, OP_DOWN, OP_LM, OP_ATTN, OP_EMBED = 1, 2, 3, 4, 5, 6, 7
+OP_QKV, OP_O, OP_GATEUP, OP_DOWN, OP_LM, OP_ATTN, OP_EMBED, OP_APPEND = 1, 2, 3, 4, 5, 6, 7, 8
 
 EXPORTS = ["mk_build_graph", "mk_destroy_plan", "mk_last_error", "mk_plan_query", "mk_decode_step",
            "mk_decode_step_greedy", "mk_decode_step_hidden", "mk_get_device_error", "mk_argmax", "mk_plan_verify", "mk_plan_dry_run",
-           "mk_plan_trace", "mk_argmax_noalloc", "mk_decode_steps_greedy"]
+           "mk_plan_trace", "mk_argmax_noalloc", "mk_decode_steps_greedy", "mk_prefill"]
 
 
 class ExecOpts(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("mode", "workers", "sched_wgs", "jit", "kv_chunk", "watchdog_ms",
                                                "host_only", "device_cus", "debug_event", "debug_extra_required",
                                                "trace", "prefetch_kb", "lds_stream", "kv_chunk_max", "lds_preload",
-                                               "schedule")]
+                                               "schedule", "prefill")]
 
 
 class ModelDesc(ctypes.Structure):
@@ -70,7 +70,7 @@ class TraceRec(ctypes.Structure):
 class PlanInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("workers", "sched_waves", "n_aot_tasks", "n_events", "n_levels",
                                                "max_jit_tasks", "kv_chunk", "max_splits")] + \
-               [("tasks_per_op", ctypes.c_int32 * 8)] + \
+               [("tasks_per_op", ctypes.c_int32 * 12)] + \
                [(n, ctypes.c_int64) for n in ("weight_bytes_per_step", "kv_bytes_per_token", "device_bytes")] + \
                [(n, ctypes.c_int32) for n in ("jit", "mode", "host_only", "schedule")] + \
                [("predicted_layer_us", ctypes.c_double)]
@@ -108,7 +108,8 @@ def lib() -> ctypes.CDLL:
         L.mk_plan_trace.argtypes = [vp, vp, ctypes.c_int64, vp]
         L.mk_argmax_noalloc.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp, vp]
         L.mk_decode_steps_greedy.argtypes = [vp, P(Weights), P(KVCache), vp, vp, vp, ctypes.c_int32, vp, vp]
-        for f in ("mk_argmax_noalloc", "mk_decode_steps_greedy", "mk_plan_query", "mk_decode_step", "mk_decode_step_greedy", "mk_decode_step_hidden",
+        L.mk_prefill.argtypes = [vp, P(Weights), P(KVCache), vp, ctypes.c_int32, ctypes.c_int32, vp, vp]
+        for f in ("mk_argmax_noalloc", "mk_decode_steps_greedy", "mk_prefill", "mk_plan_query", "mk_decode_step", "mk_decode_step_greedy", "mk_decode_step_hidden",
                   "mk_get_device_error", "mk_argmax", "mk_plan_verify", "mk_plan_dry_run", "mk_plan_trace"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -242,6 +243,11 @@ class Plan:
         _check(lib().mk_decode_steps_greedy(self._h, ctypes.byref(weights), ctypes.byref(kv), _ptr(tokens),
                                             _ptr(seq_lens), _ptr(logits), int(n_steps), _ptr(out_tokens),
                                             _stream(stream)), "mk_decode_steps_greedy")
+
+    def prefill(self, weights: "Weights", kv: "KVCache", tokens, pos0: int, T: int, logits, stream=None) -> None:
+        """T prompt tokens of one sequence, a chunk of `batch` positions per launch (plan built with prefill=1)."""
+        _check(lib().mk_prefill(self._h, ctypes.byref(weights), ctypes.byref(kv), _ptr(tokens), int(pos0), int(T),
+                                _ptr(logits), _stream(stream)), "mk_prefill")
 
     def step_hidden(self, weights: "Weights", kv: "KVCache", x_in, seq_lens, x_out, stream=None) -> None:
         _check(lib().mk_decode_step_hidden(self._h, ctypes.byref(weights), ctypes.byref(kv), _ptr(x_in),

@@ -118,3 +118,23 @@ def compare(gpu_out, orc_out, rows=None, tol_rel=2e-2):
             agree += int(np.sum(np.argmax(ref, axis=1) == nxt[rws]))
             total += len(rws)
     return worst, (agree / total if total else 1.0)
+
+
+def rows_vs_oracle_from_prefix(orc, cap, k_all, v_all, prompt, pos0, positions):
+    """For each position p: the oracle, given the GPU's K/V of positions < p,
+    computes position p; returns the worst (|gpu - oracle| - 2^-7 max(|gpu|,
+    |oracle|)) / rms(oracle row) over p's keys and values."""
+    worst = 0.0
+    L, Hkv, _, D = k_all.shape
+    for p in positions:
+        cache = {"k": np.zeros((L, Hkv, cap, D), np.uint16), "v": np.zeros((L, Hkv, cap, D), np.uint16)}
+        cache["k"][:, :, :p] = k_all[:, :, :p]
+        cache["v"][:, :, :p] = v_all[:, :, :p]
+        orc.model_forward(cache, int(prompt[p - pos0]), p)
+        for got, want in ((k_all[:, :, p], cache["k"][:, :, p]), (v_all[:, :, p], cache["v"][:, :, p])):
+            g = synth.bf16_to_f32(np.ascontiguousarray(got)).astype(np.float64)
+            r = synth.bf16_to_f32(np.ascontiguousarray(want)).astype(np.float64)
+            rms = np.sqrt(np.mean(r * r, axis=-1, keepdims=True))
+            excess = np.abs(g - r) - 2 ** -7 * np.maximum(np.abs(g), np.abs(r))
+            worst = max(worst, float((excess / rms).max()))
+    return worst

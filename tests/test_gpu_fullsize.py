@@ -26,7 +26,7 @@ import pytest
 import oracle
 import synth
 from persistent_task_graph_amd import harness
-from tests.gpu_util import log
+from tests.gpu_util import log, rows_vs_oracle_from_prefix
 
 pytestmark = pytest.mark.gpu
 
@@ -295,3 +295,43 @@ def test_q8b_w4_b1_greedy_steps_match_oracle():
     assert worst <= TOL
     assert agree >= 0.99
     plan.close()
+
+
+def test_q8b_prefill_1024_sampled_positions_match_oracle(q8b):
+    # the benchmarked prompt: 1024 positions in 64 prefill launches of 16
+    # positions each. At sampled positions p the oracle, given the GPU's cache
+    # of positions < p, recomputes position p's keys and values in every layer
+    # and, at the last position, the logits.
+    import torch
+
+    w, dm, orc = q8b
+    shape = synth.Q8B
+    T = 1024
+    cap = T + 8
+    log("q8b prefill: %d prompt tokens, chunks of 16, sampled positions vs oracle" % T)
+    prompt = synth.tokens(synth.WORKLOADS["q8b_b1"], n=T).reshape(-1).astype(np.int32)
+    kv = harness.DeviceKV(shape, 1, cap)
+    plan = harness.build_plan(shape, 16, cap, prefill=1)
+    logits = torch.empty(shape.vocab, dtype=torch.float32, device="cuda")
+    plan.prefill(dm.struct, kv.struct, torch.from_numpy(prompt).cuda(), 0, T, logits)
+    torch.cuda.synchronize()
+    assert plan.device_error() == 0
+    plan.close()
+    k_all, v_all = kv.read_sequence(0, T)
+    got_l = logits.cpu().numpy()
+    cache = synth.kv_sequence(shape, 0, 0, cap)
+    cache["k"][:, :, :T - 1] = k_all[:, :, :T - 1]
+    cache["v"][:, :, :T - 1] = v_all[:, :, :T - 1]
+    ref = orc.model_forward(cache, int(prompt[T - 1]), T - 1)
+    d = float(np.abs(got_l - ref).max()) / float(ref.std())
+    log("  last logits max|d|/std = %.3g, top-1 %d vs %d" % (d, int(np.argmax(got_l)), int(np.argmax(ref))))
+    assert d <= TOL
+    assert int(np.argmax(got_l)) == int(np.argmax(ref))
+    worst_kv = rows_vs_oracle_from_prefix(orc, cap, k_all, v_all, prompt, 0, (0, 15, 16, 517, T - 1))
+    log("  K/V rows: worst (|d| - 1 ulp) / rms = %.3g" % worst_kv)
+    # the file's bar, per row: at position 0 a single key's attention passes
+    # each layer's own value row through unaveraged, so the fp32-vs-fp64
+    # difference compounds over the 36 layers (about 8e-3 rms by the last
+    # layers; single-token decode steps show the same); later positions stay
+    # below 4e-4
+    assert worst_kv <= TOL

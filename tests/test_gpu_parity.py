@@ -12,8 +12,10 @@ from dataclasses import replace
 import numpy as np
 import pytest
 
+import oracle
 import synth
-from tests.gpu_util import compare, device_kv, log, make_setup, plan_for, run_gpu, run_oracle
+from tests.gpu_util import (compare, device_kv, log, make_setup, plan_for, rows_vs_oracle_from_prefix, run_gpu,
+                            run_oracle)
 
 pytestmark = pytest.mark.gpu
 
@@ -485,3 +487,102 @@ def test_mid_w4_modes_bitwise(mid_w4_weights):
     for o in (dict(mode=1), dict(prefetch_kb=-1), dict(schedule=1)):
         b, _ = _logits_seq(s, 3, tokens=t0, kv_chunk=128, kv_chunk_max=128, **o)
         _bitwise(a, b)
+
+
+# ---------------------------------------------------------------- prefill (prompt chunks through the runtime)
+# A prefill chunk of more than two positions runs its GEMVs on the matrix
+# cores with each fp32 activation split into two bf16 halves, x = hi + lo +
+# e with |e| <= 2^-17 |x|: a dot product over K = 4096 then errs by at most
+# 2^-17 sum|w x|, about 2^-17 (2/pi) sqrt(K) times its rms for random signs.
+HILO_TOL = 2.0 ** -17 * (2 / np.pi) * np.sqrt(4096)  # 3.1e-4
+def _prefill_case(mid_weights, B, pos0, T, paged=False, **opts):
+    """Prefill T prompt tokens after pos0 cached positions with a batch-B
+    prefill plan; returns (the setup, the device KV, the last logits, the
+    prompt)."""
+    import torch
+    from persistent_task_graph_amd import harness
+
+    cap = pos0 + T + 8
+    table = synth.block_table([cap], 16) if paged else None
+    s = make_setup(MID, 1, [pos0], cap, weights=mid_weights, paged=paged, table=table)
+    kv = device_kv(s)
+    mb = table.shape[1] if paged else 0
+    plan = harness.build_plan(MID, B, cap, paged=paged, max_blocks=mb, prefill=1, **opts)
+    prompt = synth.uniform_int(synth.SEED_TOKENS, 40 + pos0, 0, MID.vocab - 1, T).astype(np.int32)
+    d_tok = torch.from_numpy(prompt).cuda()
+    logits = torch.empty(MID.vocab, dtype=torch.float32, device="cuda")
+    plan.prefill(s.dm.struct, kv.struct, d_tok, pos0, T, logits)
+    torch.cuda.synchronize()
+    assert plan.device_error() == 0
+    plan.close()
+    return s, kv, logits.cpu().numpy(), prompt
+
+
+@pytest.mark.parametrize("B,pos0,T,paged,opts", [
+    (16, 0, 37, False, {}),                 # chunks of 16, 16 and a ragged 5
+    (16, 100, 20, False, {}),               # after a cached prefix
+    (16, 50, 19, True, {}),                 # paged: block-table row 0
+    (4, 7, 10, False, {"mode": 1}),         # kernel-per-op, chunks of 4
+    (16, 3, 21, False, {"schedule": 1}),    # static schedule
+])
+def test_prefill_matches_token_by_token_oracle(mid_weights, B, pos0, T, paged, opts):
+    # the prompt's keys and values and the logits after its last token agree
+    # with T single-token oracle steps (teacher forcing on the prompt)
+    log("prefill: chunk %d, pos0 %d, T %d, paged %s, %s" % (B, pos0, T, paged, opts))
+    s, kv, got, prompt = _prefill_case(mid_weights, B, pos0, T, paged, **opts)
+    orc = oracle.Oracle(MID, s.weights)
+    cache = {k: s.caches[0][k].copy() for k in ("k", "v")}
+    for i, tok in enumerate(prompt):
+        ref = orc.model_forward(cache, int(tok), pos0 + i)
+    d = float(np.abs(got - ref).max()) / float(ref.std())
+    log("  last logits max|d|/std = %.3g, top-1 %d vs %d" % (d, int(np.argmax(got)), int(np.argmax(ref))))
+    assert d <= 2e-2
+    assert int(np.argmax(got)) == int(np.argmax(ref))
+    # each prompt position's keys and values, recomputed by the oracle from
+    # the GPU's cache of the positions before it (so that one position's
+    # rounding does not carry into the next), agree to one bf16 ulp plus
+    # HILO_TOL * rms
+    k_all, v_all = kv.read_sequence(0, pos0 + T)
+    assert np.array_equal(k_all[:, :, :pos0], s.caches[0]["k"][:, :, :pos0])
+    assert np.array_equal(v_all[:, :, :pos0], s.caches[0]["v"][:, :, :pos0])
+    worst = rows_vs_oracle_from_prefix(orc, s.cap, k_all, v_all, prompt, pos0, range(pos0, pos0 + T))
+    log("  K/V rows: worst (|d| - 1 ulp) / rms = %.3g" % worst)
+    assert worst <= HILO_TOL
+
+
+
+def test_prefill_modes_bitwise(mid_weights):
+    # persistent and kernel-per-op run the same tasks: the same bits
+    log("prefill: persistent vs kernel-per-op, bitwise")
+    _, kv_a, a, _ = _prefill_case(mid_weights, 16, 30, 35)
+    _, kv_b, b, _ = _prefill_case(mid_weights, 16, 30, 35, mode=1)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    for x, y in zip(kv_a.read_sequence(0, 65), kv_b.read_sequence(0, 65)):
+        assert np.array_equal(x, y)
+
+
+def test_prefill_then_decode_continues(mid_weights):
+    # a decode plan picks up the prefilled cache: its first greedy steps agree
+    # with the oracle run over the whole prompt and the same tokens
+    import torch
+    from persistent_task_graph_amd import harness
+
+    log("prefill 24 tokens, then 3 batch-1 decode steps on the same cache")
+    s, kv, last, prompt = _prefill_case(mid_weights, 16, 0, 24)
+    orc = oracle.Oracle(MID, s.weights)
+    cache = {k: s.caches[0][k].copy() for k in ("k", "v")}
+    for i, tok in enumerate(prompt):
+        orc.model_forward(cache, int(tok), i)
+    plan = harness.build_plan(MID, 1, s.cap)
+    tok = torch.tensor([int(np.argmax(last))], dtype=torch.int32, device="cuda")
+    d_len = torch.tensor([len(prompt)], dtype=torch.int32, device="cuda")
+    logits = torch.empty((1, MID.vocab), dtype=torch.float32, device="cuda")
+    for t in range(3):
+        fed = int(tok.item())
+        plan.step_greedy(s.dm.struct, kv.struct, tok, d_len, logits)
+        ref = orc.model_forward(cache, fed, len(prompt) + t)
+        got = logits.cpu().numpy()[0]
+        assert float(np.abs(got - ref).max()) <= 2e-2 * float(ref.std())
+        assert int(tok.item()) == int(np.argmax(ref))
+    assert plan.device_error() == 0
+    plan.close()

@@ -225,3 +225,39 @@ def test_static_schedule_plans_verify_and_dry_run(lib, name):
 def test_static_schedule_rejects_jit(lib):
     with pytest.raises(mk.MKError, match="static schedule"):
         _plan(synth.TINY, 1, 64, schedule=1, jit=1)
+
+
+# ---------------------------------------------------------------- prefill plans
+@pytest.mark.parametrize("schedule", [0, 1])
+def test_prefill_plan_has_append_level(lib, schedule):
+    # one append task per (row, KV head) and layer, between QKV and attention;
+    # attention waits for the layer's appends
+    shape = replace(synth.Q8B, n_layers=3)
+    p = _plan(shape, 16, 2048, prefill=1, schedule=schedule)
+    p.verify()
+    inf = p.info()
+    assert inf.tasks_per_op[mk.OP_APPEND] == 3 * 16 * shape.n_kv_heads
+    assert inf.n_levels == 6 * 3 + 2
+    assert p.dry_run(n_threads=6, seed=2, seq_lens=list(range(100, 116))) == 0, mk.last_error()
+
+
+def test_prefill_plan_rejects_jit(lib):
+    with pytest.raises(mk.MKError, match="prefill"):
+        _plan(synth.TINY, 4, 64, prefill=1, jit=1)
+
+
+def test_prefill_entry_point_checks(lib):
+    p = _plan(synth.TINY, 4, 64, prefill=1)
+    fake = 0x1000
+    lw = [{n: fake for n in mk.LAYER_FIELDS} for _ in range(synth.TINY.n_layers)]
+    w = mk.make_weights(lw, fake, fake, fake)
+    stride = synth.TINY.n_kv_heads * 64 * synth.TINY.head_dim  # one sequence suffices
+    kv = mk.make_kv(fake, fake, stride)
+    call = lambda pos0, T: lib.mk_prefill(p.handle, ctypes.byref(w), ctypes.byref(kv), fake, pos0, T, fake, None)
+    assert call(0, 64) == mk.MK_ERR_STATE  # arguments fine, plan host-only
+    assert call(1, 64) == mk.MK_ERR_ARG and "max_seq_len" in mk.last_error()
+    assert call(0, 0) == mk.MK_ERR_ARG
+    assert call(-1, 4) == mk.MK_ERR_ARG
+    d = _plan(synth.TINY, 4, 64)  # a decode plan refuses prefill
+    kv4 = mk.make_kv(fake, fake, 4 * stride)
+    assert lib.mk_prefill(d.handle, ctypes.byref(w), ctypes.byref(kv4), fake, 0, 8, fake, None) == mk.MK_ERR_STATE
