@@ -60,7 +60,7 @@ def _load():
         lib.synth_normal_bf16.argtypes = [u64, u64, dbl, dbl, i64, vp]
         lib.synth_uniform_int.argtypes = [u64, u64, i64, i64, i64, vp]
         lib.synth_uniform_f64.argtypes = [u64, u64, i64, vp]
-        lib.synth_codes_u4.argtypes = [u64, u64, i64, vp]
+        lib.synth_codes_u4.argtypes = [u64, u64, dbl, i64, vp]
         _lib = lib
     return _lib
 
@@ -104,9 +104,12 @@ def uniform01(seed: int, stream: int, n: int) -> np.ndarray:
 # rounded up to 256 bytes, one bf16 scale per group of W4_GROUP inputs of a
 # row, [rows][cols / W4_GROUP]. The weight is (code - 8) * scale.
 W4_GROUP = 128
-# scale of the codes so the weights have about the standard deviation of the
-# bf16 matrices: (code - 8) is uniform on [-8, 7], standard deviation 4.61
-W4_SCALE_PER_STD = 1.0 / 4.6098
+# codes of N(0, 2.5^2) values rounded and clamped to [-8, 7] (offset 8):
+# (code - 8) then has mean -0.0013 and rms 2.5096 (exact sums over the
+# normal distribution), so scales of std / 2.5096 give the weights about the
+# standard deviation of the bf16 matrices
+W4_CODE_SIGMA = 2.5
+W4_SCALE_PER_STD = 1.0 / 2.5096
 
 
 def w4_scale_offset(rows: int, cols: int) -> int:
@@ -114,11 +117,14 @@ def w4_scale_offset(rows: int, cols: int) -> int:
 
 
 def w4_matrix(seed: int, stream: int, rows: int, cols: int, std: float = 0.02) -> np.ndarray:
-    """Seeded W4 matrix buffer: uniform codes; scales |N(1, 0.25)| * std / 4.61 in bf16."""
+    """Seeded W4 matrix buffer: codes of N(0, W4_CODE_SIGMA^2) values under
+    symmetric 4-bit quantization (offset 8, clamped to [0, 15]); group scales
+    |N(1, 0.25)| * std * W4_SCALE_PER_STD in bf16, so that the dequantized
+    matrix has rms about std and mean about zero."""
     assert cols % W4_GROUP == 0 and cols % 2 == 0
     off = w4_scale_offset(rows, cols)
     buf = np.zeros(off + rows * (cols // W4_GROUP) * 2, dtype=np.uint8)
-    _load().synth_codes_u4(seed, stream, rows * cols // 2, buf.ctypes.data)
+    _load().synth_codes_u4(seed, stream, W4_CODE_SIGMA, rows * cols // 2, buf.ctypes.data)
     sc = normal(seed, stream + (1 << 40), (rows * (cols // W4_GROUP),), 0.25, "f32", mean=1.0)
     sc = np.abs(sc) * np.float32(std * W4_SCALE_PER_STD)
     buf[off:] = f32_to_bf16(sc).view(np.uint8)

@@ -107,14 +107,22 @@ void synth_fill_u16(uint16_t v, int64_t n, uint16_t* out) {
     for (int64_t i = 0; i < n; ++i) out[i] = v;
 }
 
-/* n_bytes bytes of uniform 4-bit codes, two per byte: byte i holds code
- * 2i in its low nibble and code 2i + 1 in its high nibble, each the top 4
- * bits of its own word (the layout of the W4 matrices, codes in row order) */
-void synth_codes_u4(uint64_t seed, uint64_t stream, int64_t n_bytes, uint8_t* out) {
+/* n_bytes bytes of 4-bit codes, two per byte: byte i holds code 2i in its
+ * low nibble and code 2i + 1 in its high nibble (the layout of the W4
+ * matrices, codes in row order). The codes are those of Gaussian weights
+ * under symmetric 4-bit quantization: code = clamp(round(sigma * z) + 8,
+ * 0, 15), with z0, z1 of normal pair i for codes 2i and 2i + 1. Every
+ * code occurs (0 and 15 through the clamp), and the dequantized values
+ * (code - 8) have mean about zero. */
+void synth_codes_u4(uint64_t seed, uint64_t stream, double sigma, int64_t n_bytes, uint8_t* out) {
     const uint64_t key = stream_key(seed, stream);
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n_bytes; ++i) {
-        const uint64_t a = splitmix64(key + (uint64_t)(2 * i)), b = splitmix64(key + (uint64_t)(2 * i + 1));
-        out[i] = (uint8_t)((a >> 60) | ((b >> 60) << 4));
+        double z0, z1;
+        normal_pair(key, i, &z0, &z1);
+        long c0 = lround(sigma * z0) + 8, c1 = lround(sigma * z1) + 8;
+        c0 = c0 < 0 ? 0 : c0 > 15 ? 15 : c0;
+        c1 = c1 < 0 ? 0 : c1 > 15 ? 15 : c1;
+        out[i] = (uint8_t)(c0 | (c1 << 4));
     }
 }
