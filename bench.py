@@ -166,7 +166,7 @@ def main():
 
     # ---------------------------------------------------------------- batch 1
     B = 1
-    n_abl = 0 if args.no_ablation else 3 * (args.ablation_steps + 4)
+    n_abl = 0 if args.no_ablation else 4 * (args.ablation_steps + 4)
     n_multi = 0 if args.multi_step <= 0 else args.multi_step * (1 + max(1, args.steps // args.multi_step))
     cap = args.prompt + args.warmup + args.steps + n_abl + n_multi + 8
     kv = harness.DeviceKV(shape, B, cap)
@@ -217,11 +217,15 @@ def main():
 
     def ablation(Bn, capn, kv, d_tok, d_len, logits):
         """ms/step of the same step with JIT attention through the scheduler
-        waves, in kernel-per-operator mode (same results, bitwise), and with
-        the static (searched) schedule (its own fixed split length)."""
+        waves, with JIT attention expanded by the completing QKV arrival on
+        all workers, in kernel-per-operator mode (same results, bitwise), and
+        with the static (searched) schedule (its own fixed split length)."""
         out = {"kv_len_start": int(d_len[0].item())}
-        for name, o in (("jit_scheduler", dict(opts, jit=1)), ("kernel_per_op", dict(opts, mode=1)),
-                        ("static_schedule", dict(opts, schedule=1))):
+        runs = [("jit_scheduler", dict(opts, jit=1))]
+        if Bn >= 5:  # JIT expanded by the completing QKV arrival: the batch >= 8 instances
+            runs.append(("jit_inline", dict(opts, jit=3)))
+        runs += [("kernel_per_op", dict(opts, mode=1)), ("static_schedule", dict(opts, schedule=1))]
+        for name, o in runs:
             pl = harness.build_plan(shape, Bn, capn, **o)
             run(4, pl, kv, d_tok, d_len, logits)
             torch.cuda.synchronize()

@@ -73,7 +73,13 @@ enum mk_device_error {
  *                n_kv_heads * max splits), or batch * n_kv_heads *
  *                ceil(max_seq_len / kv_chunk_max) if larger) on the
  *                workers; once the layer's QKV event fires, slot i runs
- *                split task i of the step in (b, g, split) order, if any.
+ *                split task i of the step in (b, g, split) order, if any,
+ *                3 = JIT without scheduler waves: the QKV task whose arrival
+ *                completes the layer's QKV event expands the split tasks
+ *                (one wave) and deals them into the workers' inboxes; every
+ *                CU is a worker (the mixed launch of the MPK article, §2.2,
+ *                with the expansion moved from dedicated scheduler warps
+ *                into the completing producer). Batch >= 5 only.
  *  kv_chunk      KV positions per attention split task (default 128; a
  *                multiple of 16). Each step uses the smallest multiple of 16
  *                from kv_chunk up to kv_chunk_max for which the step has at

@@ -80,7 +80,7 @@ struct KParams {
     // schedule
     uint32_t epoch;
     int n_workers;
-    int jit_on;
+    int jit_on;  // 0 AOT, 1 JIT through scheduler waves, 2 JIT expanded by the completing QKV arrival
     int persistent;  // 1: events are signalled (persistent mode)
     int inbox_mask;
     int n_elig;

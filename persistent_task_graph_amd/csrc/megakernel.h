@@ -278,7 +278,16 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s, uint
             } else {
                 run_gemv_task<WT, NB>(p, t, s, lwt, (NB <= 2 && p.pre_slots > 0) ? preload_done_rows(s) : 0);
             }
-            signal_event(p, t.sig_ev, s, (int)blockIdx.x & (NP - 1));
+            // JIT expanded by the completing QKV arrival: batch >= 8
+            // instances only (the expansion code in the batch <= 4 loops
+            // costs those steps 1-3% even when it never runs)
+            bool signalled = false;
+            if constexpr (NB >= 8)
+                if (p.jit_on == 2) {
+                    signal_gemv_jit_inline(p, t.sig_ev, s, (int)blockIdx.x & (NP - 1));
+                    signalled = true;
+                }
+            if (!signalled) signal_event(p, t.sig_ev, s, (int)blockIdx.x & (NP - 1));
         }
         if constexpr (!kStream) {
             if (qi + 1 < qe) {

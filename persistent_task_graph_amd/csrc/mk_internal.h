@@ -85,6 +85,7 @@ struct HostPlan {
     int workers = 0;
     int sched_wgs = 0;
     int jit = 1;  // 1 JIT, 0 AOT attention
+    int jit_inline = 0;  // JIT expanded by the completing QKV arrival (no scheduler workgroups)
     int schedule = 0;  // 0 event runtime, 1 static (searched) schedule
     int prefill = 0;   // 1: the batch rows are consecutive positions of one sequence (prompt chunks)
     double predicted_layer_us = 0;  // static schedule: cost-model time of one layer

@@ -221,18 +221,22 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
     if (device_cus < 2) return fail(err, "device has too few CUs");
     p = HostPlan();
     p.desc = d;
-    if (o.jit < 0 || o.jit > 2) return fail(err, "opts.jit must be 0, 1 or 2");
+    if (o.jit < 0 || o.jit > 3) return fail(err, "opts.jit must be 0, 1, 2 or 3");
+    const bool jit_opt = o.jit == 1 || o.jit == 3;
     if (o.schedule < 0 || o.schedule > 1) return fail(err, "opts.schedule must be 0 (event runtime) or 1 (static)");
-    if (o.schedule == 1 && o.jit == 1) return fail(err, "the static schedule has no JIT attention (opts.jit 0 or 2)");
-    p.jit = (o.jit == 1) ? 1 : 0;  // default: AOT attention slots
+    if (o.schedule == 1 && jit_opt) return fail(err, "the static schedule has no JIT attention (opts.jit 0 or 2)");
+    p.jit = jit_opt ? 1 : 0;  // default: AOT attention slots
+    p.jit_inline = o.jit == 3 ? 1 : 0;
+    if (p.jit_inline && d.batch < 5)
+        return fail(err, "opts.jit = 3 needs batch >= 5 (the batch >= 8 kernel instances)");
     p.schedule = o.schedule;
     if (o.prefill < 0 || o.prefill > 1) return fail(err, "opts.prefill must be 0 or 1");
     p.prefill = o.prefill;
-    if (p.prefill && (o.jit == 1 || d.hidden_io))
+    if (p.prefill && (jit_opt || d.hidden_io))
         return fail(err, "prefill plans need ahead-of-time attention and token input (no jit, no hidden_io)");
     // scheduler workgroups exist only to deal JIT attention; without them
     // every CU is a worker
-    p.sched_wgs = p.jit ? (o.sched_wgs > 0 ? o.sched_wgs : 4) : 0;
+    p.sched_wgs = (p.jit && !p.jit_inline) ? (o.sched_wgs > 0 ? o.sched_wgs : 4) : 0;
     p.workers = o.workers > 0 ? o.workers : device_cus - p.sched_wgs;
     if (p.workers < 1 || p.workers + p.sched_wgs > device_cus)
         return fail(err, "workers + sched_wgs must be in [1, CU count] (one workgroup per CU)");
@@ -681,10 +685,36 @@ bool dry_run(const HostPlan& p, int n_threads, uint64_t seed, int drop_task, int
         }
         return false;
     };
+    // deal layer `layer`'s split tasks round-robin into the workers'
+    // inboxes (the scheduler's work, or the completing producer's with
+    // jit_inline)
+    auto expand = [&](int layer) {
+        int64_t total = 0;
+        for (int b = 0; b < d.batch; ++b) total += (int64_t)d.n_kv_heads * n_splits_for(s.seq[b] + 1, step_chunk(s));
+        const int64_t start = s.rr.fetch_add(total);
+        int64_t i = 0;
+        const int64_t ne = (int64_t)p.jit_elig.size();
+        for (int b = 0; b < d.batch; ++b) {
+            int ns = n_splits_for(s.seq[b] + 1, step_chunk(s));
+            for (int g = 0; g < d.n_kv_heads; ++g)
+                for (int sp = 0; sp < ns; ++sp, ++i) {
+                    const int w = p.jit_elig[(size_t)((start + i) % ne)];
+                    int64_t pos = s.jit_tail[w].fetch_add(1);
+                    const size_t slot = (size_t)w * p.inbox_cap + (size_t)(pos % p.inbox_cap);
+                    s.jit[slot].p0 = (layer << 16) | (b * d.n_kv_heads + g);
+                    s.jit[slot].p1 = sp;
+                    s.jit_tag[slot].store(pos + 1, std::memory_order_release);
+                }
+        }
+    };
     auto signal = [&](int e) {
         if (e < 0) return;
         uint32_t old = s.ev[e].fetch_add(1, std::memory_order_acq_rel);
         if (old + 1 == p.events[e].required && p.events[e].jit_layer >= 0) {
+            if (p.jit_inline) {
+                expand(p.events[e].jit_layer);
+                return;
+            }
             int64_t pos = s.mb_tail.fetch_add(1);
             s.mb_payload[pos % p.mb_cap] = p.events[e].jit_layer;
             s.mb_tag[pos % p.mb_cap].store(pos + 1, std::memory_order_release);
@@ -713,7 +743,7 @@ bool dry_run(const HostPlan& p, int n_threads, uint64_t seed, int drop_task, int
 
     // scheduler thread: pops the mailbox and expands attention tasks
     std::thread sched;
-    if (p.jit) {
+    if (p.jit && !p.jit_inline) {
         sched = std::thread([&]() {
             std::mt19937_64 rng(seed ^ 0xABCDEF);
             int64_t want = d.n_layers;
@@ -727,23 +757,7 @@ bool dry_run(const HostPlan& p, int n_threads, uint64_t seed, int drop_task, int
                 int layer = s.mb_payload[h % p.mb_cap];
                 if (!s.mb_head.compare_exchange_strong(h, h + 1)) continue;
                 std::this_thread::sleep_for(std::chrono::microseconds(rng() % 30));
-                int64_t total = 0;
-                for (int b = 0; b < d.batch; ++b) total += (int64_t)d.n_kv_heads * n_splits_for(s.seq[b] + 1, step_chunk(s));
-                const int64_t start = s.rr.fetch_add(total);
-                int64_t i = 0;
-                const int64_t ne = (int64_t)p.jit_elig.size();
-                for (int b = 0; b < d.batch; ++b) {
-                    int ns = n_splits_for(s.seq[b] + 1, step_chunk(s));
-                    for (int g = 0; g < d.n_kv_heads; ++g)
-                        for (int sp = 0; sp < ns; ++sp, ++i) {
-                            const int w = p.jit_elig[(size_t)((start + i) % ne)];
-                            int64_t pos = s.jit_tail[w].fetch_add(1);
-                            const size_t slot = (size_t)w * p.inbox_cap + (size_t)(pos % p.inbox_cap);
-                            s.jit[slot].p0 = (layer << 16) | (b * d.n_kv_heads + g);
-                            s.jit[slot].p1 = sp;
-                            s.jit_tag[slot].store(pos + 1, std::memory_order_release);
-                        }
-                }
+                expand(layer);
             }
         });
     }
@@ -802,7 +816,7 @@ bool dry_run(const HostPlan& p, int n_threads, uint64_t seed, int drop_task, int
         });
     }
     for (auto& t : th) t.join();
-    if (p.jit) sched.join();  // the scheduler exits once every message is popped (or on abort)
+    if (sched.joinable()) sched.join();  // the scheduler exits once every message is popped (or on abort)
     if (!s.abort.load())
         for (int l = 0; l < d.n_layers; ++l)
             if (s.ev[ev_attn(l)].load() != p.events[ev_attn(l)].required)

@@ -467,7 +467,7 @@ KParams make_params(const mk_plan* pl, const mk_weights* w, const mk_kv_cache* k
     p.scale = (float)(1.0 / std::sqrt((double)d.head_dim));
     p.epoch = pl->epoch;
     p.n_workers = hp.workers;
-    p.jit_on = hp.jit;
+    p.jit_on = hp.jit ? (hp.jit_inline ? 2 : 1) : 0;
     p.persistent = d.opts.mode == MK_PERSISTENT ? 1 : 0;
     p.inbox_mask = hp.inbox_cap - 1;
     p.n_elig = (int)hp.jit_elig.size();
@@ -659,7 +659,7 @@ int mk_plan_query(const mk_plan* pl, mk_plan_info* info) {
     info->weight_bytes_per_step = hp.weight_bytes;
     info->kv_bytes_per_token = hp.kv_bytes_per_token;
     info->device_bytes = (int64_t)pl->dbytes;
-    info->jit = hp.jit;
+    info->jit = hp.jit_inline ? 3 : hp.jit;
     info->mode = hp.desc.opts.mode;
     info->host_only = pl->host_only ? 1 : 0;
     info->schedule = hp.schedule;

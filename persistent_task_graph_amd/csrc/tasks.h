@@ -1265,6 +1265,81 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
 // partial-count plane `plane` (below the waiters' plane count).
 // The arrival that completes a JIT-triggering event posts a message to the
 // scheduler mailbox (§2.2: the data-dependent successor is launched JIT).
+// Expand layer `layer`'s JIT attention tasks (b, g, split) for every
+// sequence, in sequence order, from seq_lens and the step's split length,
+// and deal task i to eligible worker (start + i) mod n_elig's inbox (the
+// MPK article, §2.2). `lane` of `nlanes` cooperating threads takes tasks
+// lane, lane + nlanes, ...; `start` continues the previous expansion's
+// round-robin position (the caller reserved `total` positions).
+__device__ __forceinline__ int jit_total(const KParams& p, int chunk) {
+    int total = 0;
+    for (int b = 0; b < p.B; ++b) {
+        const int pos = p.seq_lens[b];
+        const bool ovf = pos < 0 || pos + 1 > p.cap;
+        total += (ovf ? 1 : (pos + 1 + chunk - 1) / chunk) * p.Hkv;
+    }
+    return total;
+}
+__device__ __forceinline__ void jit_expand(const KParams& p, int layer, int chunk, int total, int64_t start, int lane,
+                                           int nlanes) {
+    for (int i = lane; i < total; i += nlanes) {
+        int b = 0, off = 0, ns = 1;
+        for (;; ++b) {
+            const int pos = p.seq_lens[b];
+            const bool ovf = pos < 0 || pos + 1 > p.cap;
+            ns = ovf ? 1 : (pos + 1 + chunk - 1) / chunk;
+            if (i < off + ns * p.Hkv || b == p.B - 1) break;
+            off += ns * p.Hkv;
+        }
+        const int local = i - off, g = local / ns, sp = local % ns;
+        const int w = p.elig[(start + i) % p.n_elig];
+        const int64_t q = __hip_atomic_fetch_add(&p.inbox_tail[w], (int64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        RingSlot* sl = &p.inbox[(int64_t)w * (p.inbox_mask + 1) + (q & p.inbox_mask)];
+        st_co(&sl->p0, (layer << 16) | (b * p.Hkv + g));
+        st_co(&sl->p1, sp);
+        wait_stores();
+        __hip_atomic_store(&sl->tag, q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// signal_event of a GEMV task in a plan whose JIT attention is expanded by
+// the completing QKV arrival (batch >= 8 instances, all threads): the
+// arrival that completes a QKV event then expands that layer's attention
+// tasks into the inboxes with the whole workgroup.
+__device__ __forceinline__ void signal_gemv_jit_inline(const KParams& p, int e, const Lds& s, int plane) {
+    wait_stores();  // this thread's agent-coherent stores have completed
+    trace_mark(p, s.marks, 3);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int expand = 0;
+        if (e >= 0) {
+            const EventRec er = p.evrec[e];
+            if (er.jit_layer < 0) {
+                __hip_atomic_fetch_add(&p.ev[plane * p.ev_stride + e], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+                // the completing arrival must see the whole count: plane 0 only
+                const uint32_t old = __hip_atomic_fetch_add(&p.ev[e], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (old + 1u == er.required * (p.epoch + 1u)) expand = er.jit_layer + 1;
+            }
+        }
+        s.cmd[14] = expand;
+    }
+    __syncthreads();
+    const int jl = s.cmd[14] - 1;
+    if (jl < 0) return;  // uniform: read after the barrier
+    // every wave finds the split length; the whole workgroup deals the
+    // tasks, one per thread per round
+    const int chunk = attn_chunk(p), total = jit_total(p, chunk);
+    if (threadIdx.x == 0) {
+        const int64_t st = __hip_atomic_fetch_add(&p.ctrl->rr, (int64_t)total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s.cmd[10] = (int)(uint32_t)st;
+        s.cmd[11] = (int)(uint32_t)((uint64_t)st >> 32);
+    }
+    __syncthreads();
+    const int64_t start = (int64_t)(((uint64_t)(uint32_t)s.cmd[11] << 32) | (uint32_t)s.cmd[10]);
+    jit_expand(p, jl, chunk, total, start, threadIdx.x, kThreads);
+}
+
 __device__ __forceinline__ void signal_event(const KParams& p, int e, const Lds& s, int plane = 0) {
     wait_stores();  // this thread's agent-coherent stores have completed
     trace_mark(p, s.marks, 3);

@@ -204,8 +204,9 @@ def test_mid_modes_bitwise(mid_weights):
 @pytest.mark.parametrize("B,paged", [(8, False), (16, False), (8, True)])
 def test_mid_modes_bitwise_large_batch(mid_weights, B, paged):
     # the batch-8 and batch-16 kernel instances spread event arrivals over
-    # eight count planes; the persistent step (AOT slots and JIT through the
-    # scheduler waves) must still give the kernel-per-op bits exactly
+    # eight count planes; the persistent step (AOT slots, JIT through the
+    # scheduler waves, and JIT expanded by the completing QKV arrival) must
+    # still give the kernel-per-op bits exactly
     lens = [int(v) for v in np.linspace(0, 900, B)]
     log("mid bf16: persistent vs kernel-per-op vs JIT, B=%d paged=%s lens=%s" % (B, paged, lens))
     cap = max(lens) + 8
@@ -215,7 +216,8 @@ def test_mid_modes_bitwise_large_batch(mid_weights, B, paged):
     a, _ = _logits_seq(s, 3, tokens=t0)
     b, _ = _logits_seq(s, 3, tokens=t0, mode=1)
     c, _ = _logits_seq(s, 3, tokens=t0, jit=1)
-    for o in (b, c):
+    d, _ = _logits_seq(s, 3, tokens=t0, jit=3)
+    for o in (b, c, d):
         _bitwise(a, o)
         for (ta, la, na), (to, lo, no) in zip(a, o):
             assert np.array_equal(na, no)
@@ -297,16 +299,16 @@ def _greedy_seq(s, steps, tokens0, **opts):
     return out, d_len.cpu().numpy()
 
 
-@pytest.mark.parametrize("case", ["tiny", "mid3", "mid3_per_op", "mid16_jit"])
+@pytest.mark.parametrize("case", ["tiny", "mid3", "mid3_per_op", "mid16_jit", "mid16_jit3"])
 def test_greedy_step_equals_step_argmax_increment(tiny, mid_weights, case):
     # the fused step gives the logits, tokens and lengths of step + argmax + increment
     if case == "tiny":
         s, opts, steps = tiny, {}, 6
     else:
-        B = 16 if case == "mid16_jit" else 3
+        B = 16 if case.startswith("mid16") else 3
         lens = [0, 300, 77] if B == 3 else [int(x) for x in np.linspace(1, 500, B)]
         s = make_setup(MID, B, lens, 520, weights=mid_weights)
-        opts = {"mode": 1} if case == "mid3_per_op" else ({"jit": 1} if case == "mid16_jit" else {})
+        opts = {"mid3_per_op": {"mode": 1}, "mid16_jit": {"jit": 1}, "mid16_jit3": {"jit": 3}}.get(case, {})
         steps = 3
     log("greedy step vs step + argmax + increment: %s" % case)
     t0 = _tokens(s.shape, s.B, 5)

@@ -66,6 +66,16 @@ def test_workload_plans_verify(lib, name):
     ji = j.info()
     assert ji.workers == 252 and ji.sched_waves == 16
     assert ji.tasks_per_op[mk.OP_ATTN] == 0  # JIT: created on the device
+    # JIT expanded by the completing QKV arrival (batch >= 5): every CU is a worker
+    if wl.batch >= 5:
+        k = _plan(wl.shape, wl.batch, wl.capacity(), paged=wl.paged, jit=3)
+        k.verify()
+        ki = k.info()
+        assert ki.workers == 256 and ki.sched_waves == 0 and ki.jit == 3
+        assert ki.tasks_per_op[mk.OP_ATTN] == 0
+    else:
+        with pytest.raises(mk.MKError, match="batch >= 5"):
+            _plan(wl.shape, wl.batch, wl.capacity(), paged=wl.paged, jit=3)
 
 
 def test_eight_b_step_bytes_match_definition(lib):
@@ -76,12 +86,13 @@ def test_eight_b_step_bytes_match_definition(lib):
 
 
 @pytest.mark.parametrize("threads", [1, 3, 8, 64])
-@pytest.mark.parametrize("jit", [1, 2])
+@pytest.mark.parametrize("jit", [1, 2, 3])
 def test_dry_run_matches_sequential(lib, threads, jit):
     shape = replace(synth.Q8B, n_layers=3)
     rng = np.random.default_rng(threads * 10 + jit)
-    seq = rng.integers(0, 900, size=4).tolist()
-    p = _plan(shape, 4, 1024, jit=jit, workers=16, kv_chunk=128)
+    B = 8 if jit == 3 else 4
+    seq = rng.integers(0, 900, size=B).tolist()
+    p = _plan(shape, B, 1024, jit=jit, workers=16, kv_chunk=128)
     rc = p.dry_run(n_threads=threads, seed=threads, timeout_ms=20000, seq_lens=seq)
     assert rc == 0, mk.last_error()
 
@@ -222,9 +233,10 @@ def test_static_schedule_plans_verify_and_dry_run(lib, name):
     assert list(q.tasks_per_op) == list(inf.tasks_per_op) and q.kv_chunk == inf.kv_chunk
 
 
-def test_static_schedule_rejects_jit(lib):
+@pytest.mark.parametrize("jit", [1, 3])
+def test_static_schedule_rejects_jit(lib, jit):
     with pytest.raises(mk.MKError, match="static schedule"):
-        _plan(synth.TINY, 1, 64, schedule=1, jit=1)
+        _plan(replace(synth.Q8B, n_layers=2), 8, 64, schedule=1, jit=jit)
 
 
 # ---------------------------------------------------------------- prefill plans
@@ -241,9 +253,10 @@ def test_prefill_plan_has_append_level(lib, schedule):
     assert p.dry_run(n_threads=6, seed=2, seq_lens=list(range(100, 116))) == 0, mk.last_error()
 
 
-def test_prefill_plan_rejects_jit(lib):
+@pytest.mark.parametrize("jit", [1, 3])
+def test_prefill_plan_rejects_jit(lib, jit):
     with pytest.raises(mk.MKError, match="prefill"):
-        _plan(synth.TINY, 4, 64, prefill=1, jit=1)
+        _plan(replace(synth.Q8B, n_layers=2), 8, 64, prefill=1, jit=jit)
 
 
 def test_prefill_entry_point_checks(lib):
