@@ -200,11 +200,12 @@ class Plan:
             lib().mk_destroy_plan(self._h)
             self._h = None
 
-    def __del__(self):
+    def __del__(self, _finalizing=sys.is_finalizing):
         # no HIP call once the interpreter is finalizing: the plan was freed
         # by the atexit hook, or the process is ending and the driver takes
-        # the memory back
-        if sys.is_finalizing():
+        # the memory back (the check is bound at definition: module globals
+        # may already be gone)
+        if _finalizing():
             return
         try:
             self.close()
