@@ -186,7 +186,7 @@ typedef struct mk_model_desc {
     int32_t batch;
     int32_t max_seq_len;
     int32_t kv_layout;
-    int32_t kv_block;           /* paged: positions per block (16) */
+    int32_t kv_block;           /* paged: positions per block (16; a multiple of 16 for a bf16 cache) */
     int32_t max_blocks_per_seq; /* paged: row length of the block table */
     int32_t hidden_io;
     mk_exec_opts opts;

@@ -212,6 +212,9 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
     if (d.kv_layout != MK_KV_CONTIGUOUS && d.kv_layout != MK_KV_PAGED) return fail(err, "bad kv_layout");
     if (d.kv_layout == MK_KV_PAGED) {
         if (d.kv_block < 1 || d.kv_block > 1024) return fail(err, "kv_block must be in [1, 1024]");
+        // the matrix-core attention reads 16 consecutive positions of one block
+        if (d.kv_dtype == MK_BF16 && d.kv_block % 16)
+            return fail(err, "a paged bf16 cache needs kv_block a multiple of 16");
         if (d.max_blocks_per_seq < 1) return fail(err, "max_blocks_per_seq must be positive");
         if ((int64_t)d.max_blocks_per_seq * d.kv_block < d.max_seq_len)
             return fail(err, "max_blocks_per_seq * kv_block must cover max_seq_len");

@@ -1776,19 +1776,47 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
     auto vrow = [&](int base, int it) {
         return kMf ? base + wave * WR + it * PPW + rr : base + it * PER_IT + wave * PPW + rr;
     };
+    // Matrix-core layout (bf16 cache): a wave's K and V rows of a batch are
+    // the 16 rows tb .. tb + 15 (tb = base + 16 wave, a multiple of 16, as is
+    // j0). A paged bf16 cache has blocks of a multiple of 16 positions (the
+    // plan checks it), so the 16 rows share one block: its entry and the
+    // tile's offset are found once per batch and wave, not per row.
+    static_assert(!kMf || (NT == 1 && WR == 16 && NIT * PPW == 16), "one 16-row tile per wave and batch");
     // K and V rows of a batch into registers (rows at or past n fetch nothing)
     auto load_kv = [&](uint4 (&kd)[NK], uint4 (&vd)[NIT], int base, bool staged) {
+        if constexpr (kMf) {
+            {
+                const int tb = base + wave * WR;
+                uint32_t tile = kOOB;
+                if (tb < n) {
+                    const int jt = j0 + tb;
+                    if (!p.paged) {
+                        tile = (uint32_t)(jt * D * es);
+                    } else {
+                        const int bi = jt / p.kv_block;
+                        const int blk = staged ? s.btab[bi - blk0] : btab[bi];
+                        if ((unsigned)blk < (unsigned)p.n_pool_blocks)
+                            tile = (uint32_t)(((blk * Hkv + g) * p.kv_block + jt % p.kv_block) * D * es);
+                    }
+                }
+                // row tb + d of the tile, or out of range
+                auto off = [&](int d, uint32_t add) -> uint32_t {
+                    const int j = tb + d;
+                    if (tile == kOOB || j >= n || (own_lds && j0 + j == pos)) return kOOB;
+                    return tile + (uint32_t)(d * D * es) + add;
+                };
 #pragma unroll
-        for (int q = 0; q < NK; ++q) {
-            if constexpr (kMf) {
-                const int j = base + wave * WR + 16 * (q / KS) + li;
-                kd[q] = buf_load16(krs, row_off(j, (uint32_t)(16 * (4 * (q % KS) + lg)), staged), 0);
-            } else {
-                kd[q] = buf_load16(krs, row_off(vrow(base, q), (uint32_t)(cc * 16), staged), 0);
+                for (int q = 0; q < NK; ++q) kd[q] = buf_load16(krs, off(li, (uint32_t)(16 * (4 * (q % KS) + lg))), 0);
+#pragma unroll
+                for (int it = 0; it < NIT; ++it) vd[it] = buf_load16(vrs, off(it * PPW + rr, (uint32_t)(cc * 16)), 0);
             }
-        }
+        } else {
 #pragma unroll
-        for (int it = 0; it < NIT; ++it) vd[it] = buf_load16(vrs, row_off(vrow(base, it), (uint32_t)(cc * 16), staged), 0);
+            for (int q = 0; q < NK; ++q) kd[q] = buf_load16(krs, row_off(vrow(base, q), (uint32_t)(cc * 16), staged), 0);
+#pragma unroll
+            for (int it = 0; it < NIT; ++it)
+                vd[it] = buf_load16(vrs, row_off(vrow(base, it), (uint32_t)(cc * 16), staged), 0);
+        }
     };
     // the first batch of K and V rows is requested before the prologue's math
     const bool one_batch = n <= SUB;
