@@ -526,7 +526,45 @@ def main():
             "hbm_gbs": round(ach4, 1), "hbm_frac": round(ach4 / PEAK_HBM_GBS, 4), "bytes_per_launch": int(b4),
         }
         plan4.close()
-        del dm4, kv4
+        del kv4
+        # the same 4-bit model at batch 16 (matrix cores), log-uniform KV lengths
+        wl16 = synth.WORKLOADS["q8b_b16"]
+        lens16 = synth.seq_lengths(wl16)
+        cap16w = int(lens16.max()) + args.warmup + args.w4_steps + 8
+        kv16w = harness.DeviceKV(sh4, 16, cap16w)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(synth.SEED_KV)
+        for tt in (kv16w.k, kv16w.v):
+            for li in range(tt.shape[0]):
+                tt[li].copy_(torch.randn(tt[li].shape, generator=gen, device=dev).to(torch.bfloat16).view(torch.int16))
+        plan16w = harness.build_plan(sh4, 16, cap16w, **opts)
+        d_tok16w = torch.from_numpy(synth.tokens(wl16, stream=3)).to(dev)
+        d_len16w = torch.from_numpy(lens16.astype(np.int32)).to(dev)
+        logits16w = torch.empty((16, sh4.vocab), dtype=torch.float32, device=dev)
+        for _ in range(args.warmup):
+            plan16w.step_greedy(dm4.struct, kv16w.struct, d_tok16w, d_len16w, logits16w)
+        torch.cuda.synchronize()
+        l16 = d_len16w.cpu().numpy().astype(np.int64)
+        e0.record(st)
+        for i in range(args.w4_steps):
+            plan16w.step_greedy(dm4.struct, kv16w.struct, d_tok16w, d_len16w, logits16w)
+        e1.record(st)
+        torch.cuda.synchronize()
+        if plan16w.device_error():
+            raise SystemExit("device error during W4 batch-16 steps")
+        t16w = e0.elapsed_time(e1) / args.w4_steps
+        b16w = float(np.mean([harness.step_bytes(sh4, (l16 + i).tolist(), 16) for i in range(args.w4_steps)]))
+        ach16w = b16w / (t16w * 1e-3) / 1e9
+        log("W4 B=16: %.3f ms/step, %.1f tok/s, %.0f GB/s = %.1f%%"
+            % (t16w, 16 / (t16w * 1e-3), ach16w, 100 * ach16w / PEAK_HBM_GBS))
+        result["w4_b16"] = {
+            "workload": "q8b_w4_b16: the 4-bit model at batch 16 (matrix-core GEMV, codes dequantized in registers), "
+                        "KV lengths log-uniform in [32, 4096] (seeded device-side N(0,1) K/V), greedy decode",
+            "value": round(16 / (t16w * 1e-3), 2), "unit": "tokens/s", "ms_per_step": round(t16w, 4),
+            "hbm_gbs": round(ach16w, 1), "hbm_frac": round(ach16w / PEAK_HBM_GBS, 4), "bytes_per_launch": int(b16w),
+        }
+        plan16w.close()
+        del dm4, kv16w
 
     # ---------------------------------------------------------------- tiny fp32 model (latency-bound)
     if not args.no_tiny:

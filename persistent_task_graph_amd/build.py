@@ -20,7 +20,8 @@ ARCH = os.environ.get("MK_OFFLOAD_ARCH", "gfx950")
 UNITS = [("runtime.hip", []), ("plan.cpp", [])] + \
     [("kernels.hip", ["-DMK_WT_BF16", "-DMK_NB=%d" % nb]) for nb in (1, 2, 4, 8, 16)] + \
     [("kernels.hip", ["-DMK_WT_F32", "-DMK_NB=%d" % nb]) for nb in (1, 2, 4)] + \
-    [("kernels.hip", ["-DMK_WT_BF16", "-DMK_NB=1", "-DMK_LDS_STREAM"])]
+    [("kernels.hip", ["-DMK_WT_BF16", "-DMK_NB=1", "-DMK_LDS_STREAM"])] + \
+    [("kernels.hip", ["-DMK_WT_BF16", "-DMK_NB=%d" % nb, "-DMK_W4_KERNELS"]) for nb in (4, 8, 16)]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

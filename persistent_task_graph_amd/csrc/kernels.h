@@ -13,6 +13,9 @@ void* mk_kernels_bf16_2(int kind);
 void* mk_kernels_bf16_4(int kind);
 void* mk_kernels_bf16_8(int kind);
 void* mk_kernels_bf16_16(int kind);
+void* mk_kernels_bf16_4w(int kind);
+void* mk_kernels_bf16_8w(int kind);
+void* mk_kernels_bf16_16w(int kind);
 void* mk_kernels_f32_1(int kind);
 void* mk_kernels_f32_2(int kind);
 void* mk_kernels_f32_4(int kind);

@@ -1,6 +1,7 @@
 // One instantiation unit of the device kernels: compiled once per weight
 // type (MK_WT_BF16 or MK_WT_F32) and batch tile MK_NB; MK_LDS_STREAM selects
-// the batch-1 variant that streams weights through an LDS page ring.
+// the batch-1 variant that streams weights through an LDS page ring, and
+// MK_W4_KERNELS the batch >= 4 instances for 4-bit layer matrices.
 #include "megakernel.h"
 #include "kernels.h"
 
@@ -21,6 +22,8 @@
 #define MK_CAT4(a, b, c, d) a##b##_##c##d
 #ifdef MK_LDS_STREAM
 #define MK_NAME(tag, nb) MK_CAT4(mk_kernels_, tag, nb, s)
+#elif defined(MK_W4_KERNELS)
+#define MK_NAME(tag, nb) MK_CAT4(mk_kernels_, tag, nb, w)
 #else
 #define MK_NAME(tag, nb) MK_CAT3(mk_kernels_, tag, nb)
 #endif

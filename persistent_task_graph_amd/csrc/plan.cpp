@@ -188,7 +188,6 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
         return fail(err, "weight_dtype must be MK_BF16, MK_F32 or MK_W4");
     if (d.weight_dtype == MK_W4) {
         if (d.kv_dtype != MK_BF16) return fail(err, "W4 weights need a bf16 KV cache");
-        if (d.batch > 2) return fail(err, "W4 weights support batch <= 2");
         if (d.opts.lds_stream == 1) return fail(err, "W4 weights do not support lds_stream");
         const int64_t ks[3] = {d.hidden, d.ffn, (int64_t)d.n_heads * d.head_dim};
         for (int64_t k : ks)

@@ -190,6 +190,7 @@ struct mk_plan {
     uint32_t epoch = 0;
     int lds_bytes = 0;
     int lds_bytes_persistent = 0;
+    int lds_bytes_level = 0;  // kernel-per-op GEMV levels
 };
 
 namespace {
@@ -212,6 +213,13 @@ int nb_for(int B) { return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : B <= 8 ? 8 : 1
 
 void* kernel_for(const mk_plan* pl, int kind) {
     const int nb = nb_for(pl->hp.desc.batch);
+    if (pl->hp.desc.weight_dtype == MK_W4 && nb >= 4) {
+        switch (nb) {
+            case 4: return mk_kernels_bf16_4w(kind);
+            case 8: return mk_kernels_bf16_8w(kind);
+            default: return mk_kernels_bf16_16w(kind);
+        }
+    }
     if (pl->hp.desc.weight_dtype == MK_BF16 || pl->hp.desc.weight_dtype == MK_W4) {
         switch (nb) {
             case 1: return pl->hp.desc.opts.lds_stream == 1 ? mk_kernels_bf16_1s(kind) : mk_kernels_bf16_1(kind);
@@ -360,6 +368,12 @@ bool upload_plan(mk_plan* pl) {
     const bool ring = nb_for(d.batch) == 1 && d.weight_dtype != MK_F32 && d.opts.lds_stream == 1;
     pl->lds_bytes_persistent = ring ? pl->lds_bytes : std::max(pl->lds_bytes, 82 * 1024);
     if (lds_preload_on(pl)) pl->lds_bytes_persistent = std::max(pl->lds_bytes_persistent, lds_bytes_preload());
+    // a W4 matrix-core GEMV (batch >= 3) stages a pass's scales after the partial sums
+    pl->lds_bytes_level = lds_bytes_gemv();
+    if (d.weight_dtype == MK_W4 && nb_for(d.batch) >= 4) {
+        pl->lds_bytes_level = lds_bytes_gemv() + kW4ScaleLdsBytes;
+        pl->lds_bytes_persistent = std::max(pl->lds_bytes_persistent, pl->lds_bytes_level);
+    }
     // 160 KB per CU, less the statically declared prefetch sink (4 KB)
     if (pl->lds_bytes_persistent > 156 * 1024) {
         set_err("LDS need exceeds 156 KB of dynamic LDS (reduce kv_chunk_max)");
@@ -371,7 +385,7 @@ bool upload_plan(mk_plan* pl) {
     if (!hip_ok(hipFuncSetAttribute(kp, hipFuncAttributeMaxDynamicSharedMemorySize, pl->lds_bytes_persistent),
                 "hipFuncSetAttribute(persistent)"))
         return false;
-    if (!hip_ok(hipFuncSetAttribute(kl, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes_gemv()), "hipFuncSetAttribute"))
+    if (!hip_ok(hipFuncSetAttribute(kl, hipFuncAttributeMaxDynamicSharedMemorySize, pl->lds_bytes_level), "hipFuncSetAttribute"))
         return false;
     if (!hip_ok(hipFuncSetAttribute(ka, hipFuncAttributeMaxDynamicSharedMemorySize, pl->lds_bytes), "hipFuncSetAttribute"))
         return false;
@@ -580,7 +594,7 @@ int launch_step(mk_plan* pl, const mk_weights* w, const mk_kv_cache* kv, const i
             if (n == 0) continue;
             const int32_t* ids = pl->d_level_tasks + hp.level_off[lv];
             void* args[] = {&p, (void*)&ids};
-            if (!hip_ok(hipLaunchKernel(level_kernel(pl), dim3(n), dim3(kThreads), args, lds_bytes_gemv(), st),
+            if (!hip_ok(hipLaunchKernel(level_kernel(pl), dim3(n), dim3(kThreads), args, pl->lds_bytes_level, st),
                         "hipLaunchKernel(level)"))
                 return MK_ERR_HIP;
         }

@@ -41,6 +41,9 @@ constexpr int kAttnFloats = 8 * 128 + 2 * 128 + kWaves * 8 * 128 + kWaves * 16 +
                             kWaves * 32 * 8;
 // GEMV and embedding tasks touch only the header and the partial sums
 __host__ __device__ constexpr int lds_bytes_gemv() { return 4 * (kLdsHeader + kPartFloats); }
+// W4 matrix-core GEMV: a pass's scales, [TMAX][NM][16 rows][K / 128] floats:
+// at most 3 x 2 tiles (gate/up) of K / 128 <= 96 groups (K <= 12288)
+constexpr int kW4ScaleLdsBytes = 4 * 3 * 2 * 16 * 96;
 // Preload pages: after the partial sums, 1 KB slots per wave, each holding
 // one wave-wide 16-byte-per-lane load of the next GEMV task's weights (the
 // MPK article's paged shared memory, §3.1, filled during the wait, §3.2).
@@ -411,6 +414,11 @@ __device__ __forceinline__ void gemv_rowwave(int r0, int r1, int K, const float*
 // per byte (low nibble first), rows * K / 2 bytes; then, from that size
 // rounded up to 256 bytes, one bf16 scale per 128 inputs of a row. The
 // weight is (code - 8) * scale.
+#ifdef MK_W4_KERNELS
+constexpr bool kW4MfmaKernels = true;  // batch >= 4 instances for W4 plans
+#else
+constexpr bool kW4MfmaKernels = false;
+#endif
 constexpr int kW4Group = 128;
 __host__ __device__ constexpr int64_t w4_scale_offset(int64_t rows, int64_t K) { return (rows * K / 2 + 255) / 256 * 256; }
 
@@ -711,27 +719,39 @@ typedef float mk_f32x4 __attribute__((ext_vector_type(4)));
 
 // one run of output rows backed by one matrix (two for gate/up)
 struct MSeg {
-    __amdgpu_buffer_rsrc_t a, b;  // rows [0, n) of the matrix (matrices)
+    __amdgpu_buffer_rsrc_t a, b;  // rows [0, n) of the matrix (matrices); W4: their codes
     int n;                        // rows in the run
     int out0;                     // output row of the run's first row
+    __amdgpu_buffer_rsrc_t sa, sb;  // W4: the rows' group scales (bf16 [n][K / 128])
 };
 
 __device__ __forceinline__ mk_f32x4 mfma_bf16(const uint4& a, const mk_bf16x8& b, mk_f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mk_bf16x8, a), b, c, 0, 0, 0);
 }
 
-template <int NB, bool DUAL, int TMAX, int NSEG, typename OutFn, int NST = 2>
+// W4M: the matrices are W4 buffers (codes two per byte, offset 8, and bf16
+// scales per 128 inputs). A lane's 8 codes of a k-step become the exact bf16
+// values code - 8 for the A operand; a block's two k-steps (64 inputs, one
+// scale group) are multiplied into a fresh tile, which is then scaled row by
+// row (the scales staged in LDS per pass) and added to the accumulator. (Codes
+// as 128 + code, one byte permute per pair, with 136 times the sum of x taken
+// off afterwards, measured 10x the error: the matrix cores add the large
+// partial sums less exactly.)
+template <int NB, bool DUAL, int TMAX, int NSEG, typename OutFn, int NST = 2, bool W4M = false>
 __device__ __forceinline__ void gemv_mfma(const MSeg (&seg)[NSEG], int K, const float* x, int ldx, int B,
                                           const bf16_t* gain, float eps, OutFn out, const Lds& s, bool tr) {
     constexpr int NM = DUAL ? 2 : 1;
     static_assert(kWaves * TMAX * NM * 256 <= kPartFloats, "partial tiles exceed the LDS window");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lk = lane >> 4;
-    const uint32_t rowbytes = (uint32_t)K * 2u;
+    const uint32_t rowbytes = W4M ? (uint32_t)K / 2u : (uint32_t)K * 2u;  // bytes per weight row (codes for W4)
+    const uint32_t srow = (uint32_t)(K / kW4Group) * 2u;                  // W4: scale bytes per row
+    const int ngroups = K / kW4Group;
+    float* scs = s.part + kPartFloats;  // W4: [TMAX][NM][16 rows][ngroups] scales of the pass
     const int nblk = (K + 63) >> 6;
     const int nmine = (nblk - wave + kWaves - 1) / kWaves;  // blocks of this wave
     const __amdgpu_buffer_rsrc_t xr_rs = make_rsrc(x, (uint32_t)(B * ldx) * 4u);
-    const __amdgpu_buffer_rsrc_t g_rs = make_rsrc(gain, gain ? rowbytes : 0u);
+    const __amdgpu_buffer_rsrc_t g_rs = make_rsrc(gain, gain ? (uint32_t)K * 2u : 0u);
     const bool bok = li < B;
 
     int ntile = 0;
@@ -741,8 +761,8 @@ __device__ __forceinline__ void gemv_mfma(const MSeg (&seg)[NSEG], int K, const 
     float ss = 0.f;  // sum of x^2 over this lane's (sequence li, k) values
     for (int t0 = 0; t0 < ntile; t0 += TMAX) {
         // this pass's tile table (uniform): resources, row offset, valid rows, output row
-        __amdgpu_buffer_rsrc_t ta[TMAX], tb[TMAX];
-        uint32_t tsoff[TMAX];
+        __amdgpu_buffer_rsrc_t ta[TMAX], tb[TMAX], tsa[TMAX], tsb[TMAX];
+        uint32_t tsoff[TMAX], tsoffs[TMAX];
         int tval[TMAX], tout[TMAX];
 #pragma unroll
         for (int t = 0; t < TMAX; ++t) {
@@ -758,7 +778,9 @@ __device__ __forceinline__ void gemv_mfma(const MSeg (&seg)[NSEG], int K, const 
             }
             ta[t] = seg[0].a;
             tb[t] = seg[0].b;
-            tsoff[t] = 0;
+            tsa[t] = seg[0].sa;
+            tsb[t] = seg[0].sb;
+            tsoff[t] = tsoffs[t] = 0;
             tval[t] = 0;
             tout[t] = 0;
 #pragma unroll
@@ -766,15 +788,39 @@ __device__ __forceinline__ void gemv_mfma(const MSeg (&seg)[NSEG], int K, const 
                 if (q == qq) {
                     ta[t] = seg[qq].a;
                     tb[t] = seg[qq].b;
+                    tsa[t] = seg[qq].sa;
+                    tsb[t] = seg[qq].sb;
                     tsoff[t] = (uint32_t)(gt * 16) * rowbytes;
+                    tsoffs[t] = (uint32_t)(gt * 16) * srow;
                     tval[t] = min(16, seg[qq].n - gt * 16);
                     tout[t] = seg[qq].out0 + gt * 16;
                 }
         }
+        if constexpr (W4M) {
+            // the pass's scales as floats (rows past the run: 0); read after
+            // the barrier, rewritten only after the pass's closing barrier
+#pragma unroll
+            for (int t = 0; t < TMAX; ++t)
+#pragma unroll
+                for (int m = 0; m < NM; ++m)
+                    for (int i = tid; i < 16 * ngroups; i += kThreads) {
+                        const int row = i / ngroups, g = i % ngroups;
+                        float v = 0.f;
+                        if (t0 + t < ntile && row < tval[t]) {
+                            const uint32_t h = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
+                                m == 0 ? tsa[t] : tsb[t], (uint32_t)row * srow + (uint32_t)g * 2u, tsoffs[t], 0);
+                            v = __uint_as_float(h << 16);
+                        }
+                        scs[((t * NM + m) * 16 + row) * ngroups + g] = v;
+                    }
+            __syncthreads();
+        }
         struct Stage {
             uint4 w[TMAX][NM][2];
+            uint32_t q[TMAX][NM][2];  // W4: 8 codes of the lane's k-step
             uint4 x[2][2];
             uint4 g[2];
+            int blk;
         };
         // block i of this wave: k = 64 * (wave + 4 i) + 32 c + 8 lk
         auto load = [&](Stage& st, int i) {
@@ -785,14 +831,21 @@ __device__ __forceinline__ void gemv_mfma(const MSeg (&seg)[NSEG], int K, const 
                 const uint32_t xo = (kok && bok) ? (uint32_t)(li * ldx + k) * 4u : kOOB;
 #pragma unroll
                 for (int t = 0; t < TMAX; ++t) {
-                    const uint32_t vo = (kok && li < tval[t]) ? (uint32_t)li * rowbytes + (uint32_t)k * 2u : kOOB;
-                    st.w[t][0][c] = buf_load16(ta[t], vo, tsoff[t]);
-                    if constexpr (DUAL) st.w[t][1][c] = buf_load16(tb[t], vo, tsoff[t]);
+                    if constexpr (W4M) {
+                        const uint32_t vo = (kok && li < tval[t]) ? (uint32_t)li * rowbytes + (uint32_t)k / 2u : kOOB;
+                        st.q[t][0][c] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(ta[t], vo, tsoff[t], 0);
+                        if constexpr (DUAL) st.q[t][1][c] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(tb[t], vo, tsoff[t], 0);
+                    } else {
+                        const uint32_t vo = (kok && li < tval[t]) ? (uint32_t)li * rowbytes + (uint32_t)k * 2u : kOOB;
+                        st.w[t][0][c] = buf_load16(ta[t], vo, tsoff[t]);
+                        if constexpr (DUAL) st.w[t][1][c] = buf_load16(tb[t], vo, tsoff[t]);
+                    }
                 }
                 st.x[c][0] = buf_load16_act(xr_rs, xo, 0);
                 st.x[c][1] = buf_load16_act(xr_rs, xo, 16);
                 st.g[c] = buf_load16(g_rs, kok ? (uint32_t)k * 2u : kOOB, 0);
             }
+            st.blk = i;
         };
         mk_f32x4 acc[TMAX][NM];
 #pragma unroll
@@ -801,6 +854,13 @@ __device__ __forceinline__ void gemv_mfma(const MSeg (&seg)[NSEG], int K, const 
             for (int m = 0; m < NM; ++m) acc[t][m] = mk_f32x4{0.f, 0.f, 0.f, 0.f};
         const bool stat = gain != nullptr && t0 == 0;
         auto compute = [&](const Stage& st) {
+            mk_f32x4 tmp[TMAX][NM];  // W4: the block's unscaled products of (code - 8) and x
+            if constexpr (W4M) {
+#pragma unroll
+                for (int t = 0; t < TMAX; ++t)
+#pragma unroll
+                    for (int m = 0; m < NM; ++m) tmp[t][m] = mk_f32x4{0.f, 0.f, 0.f, 0.f};
+            }
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 float xv[8], gv[8];
@@ -822,14 +882,42 @@ __device__ __forceinline__ void gemv_mfma(const MSeg (&seg)[NSEG], int K, const 
                     hi[e] = h;
                     lo[e] = (__bf16)(a - (float)h);
                 }
+
 #pragma unroll
                 for (int t = 0; t < TMAX; ++t) {
                     if (t0 + t >= ntile) continue;
 #pragma unroll
                     for (int m = 0; m < NM; ++m) {
-                        acc[t][m] = mfma_bf16(st.w[t][m][c], hi, acc[t][m]);
-                        acc[t][m] = mfma_bf16(st.w[t][m][c], lo, acc[t][m]);
+                        if constexpr (W4M) {
+                            // code e of the lane sits in bits 4e .. 4e + 3 (low nibble first);
+                            // with its top bit flipped, the nibble read as a signed 4-bit
+                            // field is code - 8, which bf16 holds exactly
+                            const uint32_t q = st.q[t][m][c] ^ 0x88888888u;
+                            mk_bf16x8 aq;
+#pragma unroll
+                            for (int e = 0; e < 8; ++e)
+                                aq[e] = (__bf16)(float)((int)(q << (28 - 4 * e)) >> 28);
+                            tmp[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, hi, tmp[t][m], 0, 0, 0);
+                            tmp[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, lo, tmp[t][m], 0, 0, 0);
+                        } else {
+                            acc[t][m] = mfma_bf16(st.w[t][m][c], hi, acc[t][m]);
+                            acc[t][m] = mfma_bf16(st.w[t][m][c], lo, acc[t][m]);
+                        }
                     }
+                }
+            }
+            if constexpr (W4M) {
+                // the block's 64 inputs share scale group (64 (wave + 4 blk)) / 128;
+                // lane l's tile rows are 4 (l / 16) + r
+                const int g = (wave + kWaves * st.blk) >> 1;
+#pragma unroll
+                for (int t = 0; t < TMAX; ++t) {
+                    if (t0 + t >= ntile) continue;
+#pragma unroll
+                    for (int m = 0; m < NM; ++m)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            acc[t][m][r] = fmaf(scs[((t * NM + m) * 16 + 4 * lk + r) * ngroups + g], tmp[t][m][r], acc[t][m][r]);
                 }
             }
         };
@@ -1131,16 +1219,87 @@ __device__ __forceinline__ void run_w4_task(const KParams& p, const TaskRec& t, 
     trace_mark(p, s.marks, 2);
 }
 
+// A GEMV task of a plan whose layer matrices are W4, batch >= 3: the
+// matrix-core GEMV with the codes dequantized in registers (the same tiles,
+// passes and outputs as the bf16 path).
+template <int NB>
+__device__ __forceinline__ void run_w4_mfma_task(const KParams& p, const TaskRec& t, const Lds& s, const LayerPtrs& w) {
+    const int l = t.layer, B = p.B, H = p.H, r0 = t.a0, r1 = t.a1;
+    const bool tr = p.trace != nullptr;
+    switch (t.op) {
+        case OP_QKV: {
+            const float* x = layer_in(p, l);
+            const int QD = p.QD, KD = p.KD, ld = QD + 2 * KD;
+            const W4Tile tq = w4_tile(w.wq, H, QD, r0, r1), tk = w4_tile(w.wk, H, KD, r0 - QD, r1 - QD),
+                         tv = w4_tile(w.wv, H, KD, r0 - QD - KD, r1 - QD - KD);
+            float* o = layer_buf(p, l, p.off_qkv);
+            auto out = [&](int r, int b, float v, float) { st_co(&o[(int64_t)b * ld + r], v * s.rstd[b]); };
+            const MSeg sg[3] = {{tq.q, tq.q, tq.n, tq.lo, tq.sc, tq.sc},
+                                {tk.q, tk.q, tk.n, QD + tk.lo, tk.sc, tk.sc},
+                                {tv.q, tv.q, tv.n, QD + KD + tv.lo, tv.sc, tv.sc}};
+            gemv_mfma<NB, false, 2, 3, decltype(out), 2, true>(sg, H, x, H, B, (const bf16_t*)w.attn_norm, p.eps, out, s, tr);
+            break;
+        }
+        case OP_O: {
+            const float* a = layer_buf(p, l, p.off_attn);
+            const float* xin = layer_in(p, l);
+            float* o = layer_buf(p, l, p.off_xmid);
+            const int K = p.QD;
+            const W4Tile to = w4_tile(w.wo, K, H, r0, r1);
+            auto out = [&](int r, int b, float v, float) {
+                const int64_t i = (int64_t)b * H + r;
+                st_co(&o[i], ld_act(&xin[i]) + v);
+            };
+            const MSeg sg[1] = {{to.q, to.q, to.n, to.lo, to.sc, to.sc}};
+            gemv_mfma<NB, false, 1, 1, decltype(out), 3, true>(sg, K, a, K, B, (const bf16_t*)nullptr, p.eps, out, s, tr);
+            break;
+        }
+        case OP_GATEUP: {
+            const float* x = layer_buf(p, l, p.off_xmid);
+            float* o = layer_buf(p, l, p.off_h);
+            const int F = p.F;
+            const W4Tile tg = w4_tile(w.w_gate, H, F, r0, r1), tu = w4_tile(w.w_up, H, F, r0, r1);
+            auto out = [&](int r, int b, float g, float u) {
+                const float rs = s.rstd[b];
+                const float gg = g * rs, uu = u * rs;
+                st_co(&o[(int64_t)b * F + r], (gg / (1.0f + __expf(-gg))) * uu);
+            };
+            const MSeg sg[1] = {{tg.q, tu.q, tg.n, tg.lo, tg.sc, tu.sc}};
+            gemv_mfma<NB, true, 3, 1, decltype(out), 2, true>(sg, H, x, H, B, (const bf16_t*)w.mlp_norm, p.eps, out, s, tr);
+            break;
+        }
+        case OP_DOWN: {
+            const float* h = layer_buf(p, l, p.off_h);
+            const float* xm = layer_buf(p, l, p.off_xmid);
+            float* o = layer_out(p, l);
+            const int F = p.F;
+            const W4Tile td = w4_tile(w.w_down, F, H, r0, r1);
+            auto out = [&](int r, int b, float v, float) {
+                const int64_t i = (int64_t)b * H + r;
+                st_co(&o[i], ld_act(&xm[i]) + v);
+            };
+            const MSeg sg[1] = {{td.q, td.q, td.n, td.lo, td.sc, td.sc}};
+            gemv_mfma<NB, false, 1, 1, decltype(out), 3, true>(sg, F, h, F, B, (const bf16_t*)nullptr, p.eps, out, s, tr);
+            break;
+        }
+        default: break;
+    }
+    trace_mark(p, s.marks, 2);
+}
+
 // w: the task's layer pointers, p.lw[t.layer] (the worker reads them before
 // the task's event fires). pre_rows: leading rows of the task whose weights
 // were preloaded into this worker's LDS slots (batch <= 2 only; 0 otherwise).
 template <typename WT, int NB>
 __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t, const Lds& s, const LayerPtrs& w,
                                               int pre_rows = 0) {
-    // 4-bit layer matrices (batch <= 2)
-    if constexpr (std::is_same<WT, bf16_t>::value && NB <= 2) {
+    // 4-bit layer matrices: VALU GEMV at batch <= 2 (in the bf16 instances),
+    // matrix cores above (in instances of their own: in the bf16 batch >= 4
+    // kernels that code would cost registers, and spills, when unused)
+    if constexpr (std::is_same<WT, bf16_t>::value && (NB <= 2 || kW4MfmaKernels)) {
         if (p.w4 && t.op != OP_LM && t.op != OP_EMBED && t.op != OP_APPEND) {
-            run_w4_task<NB>(p, t, s, w);
+            if constexpr (NB <= 2) run_w4_task<NB>(p, t, s, w);
+            else run_w4_mfma_task<NB>(p, t, s, w);
             return;
         }
     }

@@ -271,20 +271,26 @@ def test_q8b_b16_32_row_steps_top1(q8b):
     plan.close()
 
 
-def test_q8b_w4_b1_greedy_steps_match_oracle():
+@pytest.fixture(scope="module")
+def q8b_w4():
+    t0 = time.time()
+    w = synth.model_weights(synth.Q8B_W4)
+    dm = harness.DeviceModel(synth.Q8B_W4, w)
+    orc = oracle.Oracle(synth.Q8B_W4, w)
+    log("8B W4 weights generated and uploaded in %.1fs" % (time.time() - t0))
+    return w, dm, orc
+
+
+def test_q8b_w4_b1_greedy_steps_match_oracle(q8b_w4):
     # the 36-layer model with 4-bit layer matrices (bf16 embedding and LM
     # head), 1024 cached random keys, 6 greedy steps with the oracle
     # teacher-forced on the GPU's tokens
-    import torch
-
+    w, dm, orc = q8b_w4
     shape = synth.Q8B_W4
     L0, steps = 1024, 6
     cap = L0 + steps + 8
     t0 = time.time()
-    w = synth.model_weights(shape)
-    dm = harness.DeviceModel(shape, w)
-    orc = oracle.Oracle(shape, w)
-    log("q8b W4 B=1: weights in %.1fs; %d cached keys, %d greedy steps" % (time.time() - t0, L0, steps))
+    log("q8b W4 B=1: %d cached keys, %d greedy steps" % (L0, steps))
     cache = synth.kv_sequence(shape, 0, L0, cap)
     kv = harness.DeviceKV(shape, 1, cap)
     kv.load_sequence(0, cache["k"], cache["v"], L0)
@@ -292,6 +298,34 @@ def test_q8b_w4_b1_greedy_steps_match_oracle():
     out = _decode(plan, dm, kv, synth.tokens(synth.WORKLOADS["q8b_w4_b1"]), [L0], steps, shape)
     worst, agree = _check_rows(out, orc, [cache], [L0], [0])
     log("  max|d|/std = %.3g, top-1 = %.3f (%.1fs)" % (worst, agree, time.time() - t0))
+    assert worst <= TOL
+    assert agree >= 0.99
+    plan.close()
+
+
+def test_q8b_w4_b16_sampled_rows_match_oracle(q8b_w4):
+    # batch 16 on the matrix cores with the codes dequantized in registers,
+    # log-uniform lengths: the shortest, a middle and the longest sequence
+    # over 3 greedy steps
+    w, dm, orc = q8b_w4
+    shape = synth.Q8B_W4
+    lens = synth.seq_lengths(synth.WORKLOADS["q8b_b16"])
+    B, steps = 16, 3
+    cap = int(lens.max()) + steps + 8
+    order = np.argsort(lens)
+    rows = sorted({int(order[0]), int(order[8]), int(order[-1])})
+    log("q8b W4 B=16: rows %s (lengths %s), %d steps" % (rows, [int(lens[b]) for b in rows], steps))
+    kv = harness.DeviceKV(shape, B, cap)
+    caches = {}
+    for b in range(B):
+        c = synth.kv_sequence(shape, b, int(lens[b]), cap)
+        kv.load_sequence(b, c["k"], c["v"], int(lens[b]))
+        if b in rows:
+            caches[b] = c
+    plan = harness.build_plan(shape, B, cap)
+    out = _decode(plan, dm, kv, synth.tokens(synth.WORKLOADS["q8b_b16"], stream=3), lens, steps, shape)
+    worst, agree = _check_rows(out, orc, caches, lens, rows)
+    log("  max|d|/std = %.3g, top-1 = %.3f over %d row-steps" % (worst, agree, steps * len(rows)))
     assert worst <= TOL
     assert agree >= 0.99
     plan.close()

@@ -480,6 +480,38 @@ def test_mid_w4_matches_oracle(mid_w4_weights, B, lens, gains):
     plan.close()
 
 
+@pytest.mark.parametrize("B,gains", [(4, "unit"), (16, "unit"), (8, "random")])
+def test_mid_w4_matrix_cores_match_oracle(mid_w4_weights, B, gains):
+    # batch >= 3: the matrix-core GEMV with the codes dequantized in registers
+    lens = [int(v) for v in np.linspace(3, 700, B)]
+    log("mid W4 (matrix cores): B=%d lens=%s gains=%s" % (B, lens, gains))
+    w = mid_w4_weights if gains == "unit" else synth.with_gains(MID_W4, mid_w4_weights, "random")
+    s = make_setup(MID_W4, B, lens, max(lens) + 8, weights=w)
+    plan = plan_for(s)
+    kv = device_kv(s)
+    out, err = run_gpu(s, plan, kv, _tokens(MID_W4, B, 14), 2)
+    assert err == 0
+    rows = list(range(B)) if B <= 8 else [0, 7, 15]
+    orc, caches = run_oracle(s, out, rows=rows)
+    worst, agree = compare(out, orc, rows=rows)
+    log("  max|d|/std = %.3g, top-1 = %.3f" % (worst, agree))
+    assert worst <= 2e-2 and agree >= 0.99
+    _check_appended(s, kv, caches, rows, 2)
+    plan.close()
+
+
+def test_mid_w4_matrix_cores_modes_bitwise(mid_w4_weights):
+    # persistent = kernel-per-op = static schedule = JIT at batch 16 with W4
+    log("mid W4 B=16: persistent vs kernel-per-op vs static schedule vs JIT")
+    lens = [int(v) for v in np.linspace(1, 500, 16)]
+    s = make_setup(MID_W4, 16, lens, 520, weights=mid_w4_weights)
+    t0 = _tokens(MID_W4, 16, 15)
+    a, _ = _logits_seq(s, 3, tokens=t0, kv_chunk=128, kv_chunk_max=128)
+    for o in (dict(mode=1), dict(schedule=1), dict(jit=3), dict(jit=1)):
+        b, _ = _logits_seq(s, 3, tokens=t0, kv_chunk=128, kv_chunk_max=128, **o)
+        _bitwise(a, b)
+
+
 def test_mid_w4_modes_bitwise(mid_w4_weights):
     # persistent = kernel-per-op = no prefetch = static schedule; several steps per launch
     log("mid W4 B=2: persistent vs kernel-per-op vs no prefetch vs static schedule")

@@ -274,3 +274,12 @@ def test_prefill_entry_point_checks(lib):
     d = _plan(synth.TINY, 4, 64)  # a decode plan refuses prefill
     kv4 = mk.make_kv(fake, fake, 4 * stride)
     assert lib.mk_prefill(d.handle, ctypes.byref(w), ctypes.byref(kv4), fake, 0, 8, fake, None) == mk.MK_ERR_STATE
+
+
+@pytest.mark.parametrize("B", [1, 4, 16])
+def test_w4_plans_any_batch(lib, B):
+    # 4-bit layer matrices: the VALU GEMV at batch <= 2, the matrix cores above
+    p = _plan(synth.Q8B_W4, B, 2048)
+    p.verify()
+    assert p.info().weight_bytes_per_step == synth.Q8B_W4.step_weight_bytes()
+    assert p.dry_run(n_threads=4, seed=B, seq_lens=[100 + 7 * b for b in range(B)]) == 0, mk.last_error()
