@@ -161,7 +161,8 @@ typedef struct mk_exec_opts {
  *  weight_dtype, kv_dtype: MK_BF16 or MK_F32 (bf16 weights need a bf16 cache
  *  and f32 weights an f32 cache), or weight_dtype MK_W4 with a bf16 cache:
  *  4-bit layer matrices (the Ada-MK summary's W4A16, gist.science
- *  "Hauptbeiträge" 4), batch <= 2, hidden, ffn and n_heads * head_dim
+ *  "Hauptbeiträge" 4), any batch (VALU GEMV at batch <= 2, matrix cores
+ *  with the codes dequantized in registers above), hidden, ffn and n_heads * head_dim
  *  multiples of 1024 and at most 12288. Each W4 matrix [rows, K] is one
  *  buffer: 4-bit codes in row order, two per byte (low nibble first),
  *  rows * K / 2 bytes; then, from that size rounded up to 256 bytes, one
