@@ -853,71 +853,73 @@ __device__ __forceinline__ void gemv_mfma(const MSeg (&seg)[NSEG], int K, const 
 #pragma unroll
             for (int m = 0; m < NM; ++m) acc[t][m] = mk_f32x4{0.f, 0.f, 0.f, 0.f};
         const bool stat = gain != nullptr && t0 == 0;
-        auto compute = [&](const Stage& st) {
-            mk_f32x4 tmp[TMAX][NM];  // W4: the block's unscaled products of (code - 8) and x
-            if constexpr (W4M) {
+        // k-step c of x (times the gain) as hi + lo bf16 terms, with hardware
+        // round-to-nearest-even conversions (v_cvt_pk_bf16_f32)
+        auto split = [&](const Stage& st, int c, mk_bf16x8& hi, mk_bf16x8& lo) {
+            float xv[8], gv[8];
+            xv[0] = __uint_as_float(st.x[c][0].x); xv[1] = __uint_as_float(st.x[c][0].y);
+            xv[2] = __uint_as_float(st.x[c][0].z); xv[3] = __uint_as_float(st.x[c][0].w);
+            xv[4] = __uint_as_float(st.x[c][1].x); xv[5] = __uint_as_float(st.x[c][1].y);
+            xv[6] = __uint_as_float(st.x[c][1].z); xv[7] = __uint_as_float(st.x[c][1].w);
+            if (gain) Vec16<bf16_t>::widen(st.g[c], gv);
+            else
 #pragma unroll
-                for (int t = 0; t < TMAX; ++t)
+                for (int e = 0; e < 8; ++e) gv[e] = 1.f;
 #pragma unroll
-                    for (int m = 0; m < NM; ++m) tmp[t][m] = mk_f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int e = 0; e < 8; ++e) {
+                if (stat) ss += xv[e] * xv[e];
+                const float a = xv[e] * gv[e];
+                const __bf16 h = (__bf16)a;
+                hi[e] = h;
+                lo[e] = (__bf16)(a - (float)h);
             }
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                float xv[8], gv[8];
-                xv[0] = __uint_as_float(st.x[c][0].x); xv[1] = __uint_as_float(st.x[c][0].y);
-                xv[2] = __uint_as_float(st.x[c][0].z); xv[3] = __uint_as_float(st.x[c][0].w);
-                xv[4] = __uint_as_float(st.x[c][1].x); xv[5] = __uint_as_float(st.x[c][1].y);
-                xv[6] = __uint_as_float(st.x[c][1].z); xv[7] = __uint_as_float(st.x[c][1].w);
-                if (gain) Vec16<bf16_t>::widen(st.g[c], gv);
-                else
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) gv[e] = 1.f;
-                // hardware round-to-nearest-even conversions (v_cvt_pk_bf16_f32)
-                mk_bf16x8 hi, lo;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    if (stat) ss += xv[e] * xv[e];
-                    const float a = xv[e] * gv[e];
-                    const __bf16 h = (__bf16)a;
-                    hi[e] = h;
-                    lo[e] = (__bf16)(a - (float)h);
-                }
-
+        };
+        auto compute = [&](const Stage& st) {
+            if constexpr (W4M) {
+                mk_bf16x8 hi[2], lo[2];
+                split(st, 0, hi[0], lo[0]);
+                split(st, 1, hi[1], lo[1]);
+                // the block's 64 inputs share scale group (64 (wave + 4 blk)) / 128;
+                // lane l's tile rows are 4 (l / 16) + r. One tile at a time: its
+                // two k-steps into a fresh product, then scaled into the accumulator
+                const int g = (wave + kWaves * st.blk) >> 1;
 #pragma unroll
                 for (int t = 0; t < TMAX; ++t) {
                     if (t0 + t >= ntile) continue;
 #pragma unroll
                     for (int m = 0; m < NM; ++m) {
-                        if constexpr (W4M) {
+                        mk_f32x4 tp = mk_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int c = 0; c < 2; ++c) {
                             // code e of the lane sits in bits 4e .. 4e + 3 (low nibble first);
                             // with its top bit flipped, the nibble read as a signed 4-bit
                             // field is code - 8, which bf16 holds exactly
                             const uint32_t q = st.q[t][m][c] ^ 0x88888888u;
                             mk_bf16x8 aq;
 #pragma unroll
-                            for (int e = 0; e < 8; ++e)
-                                aq[e] = (__bf16)(float)((int)(q << (28 - 4 * e)) >> 28);
-                            tmp[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, hi, tmp[t][m], 0, 0, 0);
-                            tmp[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, lo, tmp[t][m], 0, 0, 0);
-                        } else {
+                            for (int e = 0; e < 8; ++e) aq[e] = (__bf16)(float)((int)(q << (28 - 4 * e)) >> 28);
+                            tp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, hi[c], tp, 0, 0, 0);
+                            tp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, lo[c], tp, 0, 0, 0);
+                        }
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            acc[t][m][r] = fmaf(scs[((t * NM + m) * 16 + 4 * lk + r) * ngroups + g], tp[r], acc[t][m][r]);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    mk_bf16x8 hi, lo;
+                    split(st, c, hi, lo);
+#pragma unroll
+                    for (int t = 0; t < TMAX; ++t) {
+                        if (t0 + t >= ntile) continue;
+#pragma unroll
+                        for (int m = 0; m < NM; ++m) {
                             acc[t][m] = mfma_bf16(st.w[t][m][c], hi, acc[t][m]);
                             acc[t][m] = mfma_bf16(st.w[t][m][c], lo, acc[t][m]);
                         }
                     }
-                }
-            }
-            if constexpr (W4M) {
-                // the block's 64 inputs share scale group (64 (wave + 4 blk)) / 128;
-                // lane l's tile rows are 4 (l / 16) + r
-                const int g = (wave + kWaves * st.blk) >> 1;
-#pragma unroll
-                for (int t = 0; t < TMAX; ++t) {
-                    if (t0 + t >= ntile) continue;
-#pragma unroll
-                    for (int m = 0; m < NM; ++m)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            acc[t][m][r] = fmaf(scs[((t * NM + m) * 16 + 4 * lk + r) * ngroups + g], tmp[t][m][r], acc[t][m][r]);
                 }
             }
         };
