@@ -97,6 +97,8 @@ def parse():
     ap.add_argument("--kv-chunk", type=int, default=0)
     ap.add_argument("--workers", type=int, default=0)
     ap.add_argument("--lds-preload", type=int, default=0, help="1: preload GEMV rows into LDS pages (batch <= 2)")
+    ap.add_argument("--prefetch-kb", type=int, default=0,
+                    help="KB of the awaited task's weights each worker prefetches (0: the plan default, -1: none)")
     ap.add_argument("--quick", action="store_true", help="tiny prompt, few steps (profiling runs)")
     ap.add_argument("--no-tiny", action="store_true", help="skip the tiny-model step time")
     ap.add_argument("--no-w4", action="store_true", help="skip the 4-bit-weight (W4A16) batch-1 measurement")
@@ -162,7 +164,7 @@ def main():
     torch.cuda.synchronize()
     log("weights uploaded in %.1fs" % (time.time() - t0))
     opts = dict(mode=args.mode, jit=args.jit, kv_chunk=args.kv_chunk, workers=args.workers,
-                lds_preload=args.lds_preload)
+                lds_preload=args.lds_preload, prefetch_kb=args.prefetch_kb)
 
     # ---------------------------------------------------------------- batch 1
     B = 1
@@ -720,7 +722,7 @@ def phases(args):
     plan = harness.build_plan(shape, B, cap, paged=wl.paged, block=wl.kv_block,
                               max_blocks=table.shape[1] if table is not None else 0, trace=4096,
                               mode=args.mode, jit=args.jit, kv_chunk=args.kv_chunk, workers=args.workers,
-                              lds_preload=args.lds_preload)
+                              lds_preload=args.lds_preload, prefetch_kb=args.prefetch_kb)
     d_tok = torch.from_numpy(synth.tokens(wl)).to(dev)
     d_len = torch.from_numpy(lens.astype(np.int32)).to(dev)
     logits = torch.empty((B, shape.vocab), dtype=torch.float32, device=dev)

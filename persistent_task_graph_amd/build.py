@@ -38,12 +38,14 @@ def _hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False, jobs: int = 2) -> str:
-    """Always recompiles (the build check must compile every time)."""
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    """Always recompiles (the build check must compile every time). At most
+    `jobs` compiles run at once (0: one per CPU, at most 16)."""
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     hipcc = _hipcc()
-    procs = []
+    jobs = jobs if jobs > 0 else max(1, min(16, os.cpu_count() or 1))
+    cmds = []
     objs = []
     for src, defs in UNITS:
         tag = "".join(d.replace("-D", "_").replace("=", "") for d in defs)
@@ -53,11 +55,10 @@ def build(verbose: bool = False, jobs: int = 2) -> str:
             cmd = [hipcc, "-c", os.path.join(CSRC, src), "-o", obj, "--offload-arch=" + ARCH] + COMMON + DEVICE + defs
         else:
             cmd = [hipcc, "-x", "c++", "-c", os.path.join(CSRC, src), "-o", obj] + COMMON
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        procs.append((src + tag, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+        cmds.append((src + tag, cmd))
     failed = []
-    for src, p in procs:
+
+    def finish(src, p):
         out, _ = p.communicate()
         text = out.decode(errors="replace")
         # hipcc's host pass does not know the device-only feature flag
@@ -67,6 +68,16 @@ def build(verbose: bool = False, jobs: int = 2) -> str:
             sys.stderr.write("\n".join(lines) + "\n")
         elif verbose and lines:
             print("\n".join(lines))
+
+    running = []
+    for src, cmd in cmds:
+        if len(running) >= jobs:
+            finish(*running.pop(0))
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        running.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+    for src, p in running:
+        finish(src, p)
     if failed:
         raise RuntimeError("hipcc failed for: " + ", ".join(failed))
     tmp = LIB + ".tmp%d" % os.getpid()

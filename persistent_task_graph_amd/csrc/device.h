@@ -315,6 +315,58 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t v
     const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
+// Cache policy of the once-per-step streams, chosen per kernel instance
+// (each batch tile is its own compilation unit, MK_NB). At batch <= 2 a
+// wave's weight load covers whole 128-byte lines that nothing reads again,
+// so weights stream with the non-temporal policy: a plain read of a large
+// buffer measured 6.1 TB/s, a non-temporal one 6.6-6.7 TB/s, and the batch-1
+// step went 3.744 -> 3.514 ms. Cached K/V keeps the plain policy there (its
+// rows were pulled into L2 while the attention slot waited; non-temporal:
+// 3.525 ms). In the matrix-core instances (batch >= 4) each load reads half
+// of a line and the next k-step the other half: non-temporal weights made
+// the batch-16 step 9% slower (5.81 -> 6.36 ms), so everything stays plain.
+// The prefetch loads must stay plain: their lines are meant to be kept.
+#ifndef MK_STREAM_AUX_SMALL
+#define MK_STREAM_AUX_SMALL 2
+#endif
+#ifndef MK_KV_AUX_SMALL
+#define MK_KV_AUX_SMALL 0
+#endif
+#ifndef MK_STREAM_AUX_LARGE
+#define MK_STREAM_AUX_LARGE 0
+#endif
+#ifndef MK_KV_AUX_LARGE
+#define MK_KV_AUX_LARGE 0
+#endif
+#if defined(MK_NB) && MK_NB >= 4
+#ifndef MK_STREAM_AUX
+#define MK_STREAM_AUX MK_STREAM_AUX_LARGE
+#endif
+#ifndef MK_KV_AUX
+#define MK_KV_AUX MK_KV_AUX_LARGE
+#endif
+#else
+#ifndef MK_STREAM_AUX
+#define MK_STREAM_AUX MK_STREAM_AUX_SMALL
+#endif
+#ifndef MK_KV_AUX
+#define MK_KV_AUX MK_KV_AUX_SMALL
+#endif
+#endif
+#ifndef MK_PF_AUX
+#define MK_PF_AUX 0
+#endif
+constexpr int kStreamAux = MK_STREAM_AUX;  // cache policy of weight loads (0 plain, 2 non-temporal)
+constexpr int kKvAux = MK_KV_AUX;          // cache policy of cached K/V loads
+constexpr int kPfAux = MK_PF_AUX;          // cache policy of the prefetch loads (they must stay in L2)
+__device__ __forceinline__ uint4 buf_load16_w(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kStreamAux);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 buf_load16_kv(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kKvAux);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 // agent-coherent variant for data written earlier in the same step
 __device__ __forceinline__ uint4 buf_load16_co(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kSC1);

@@ -197,7 +197,7 @@ __device__ __forceinline__ void gemv_ksplit(int r0, int r1, int K, const float* 
 #pragma unroll
             for (int m = 0; m < NM; ++m)
 #pragma unroll
-                for (int j = 0; j < NSW; ++j) w[u][m][j] = buf_load16(rf[m].r, rv ? voff[j] : kOOB, rf[m].soff);
+                for (int j = 0; j < NSW; ++j) w[u][m][j] = buf_load16_w(rf[m].r, rv ? voff[j] : kOOB, rf[m].soff);
         }
     };
     // preloaded rows [r0, rp) lie in the first window; their DMA loads were
@@ -368,7 +368,7 @@ __device__ __forceinline__ void gemv_rowwave(int r0, int r1, int K, const float*
         for (int k = lane * E; k < K; k += SEG) {
             uint4 w[NM];
 #pragma unroll
-            for (int m = 0; m < NM; ++m) w[m] = buf_load16(rf[m].r, (uint32_t)k * (uint32_t)sizeof(WT), rf[m].soff);
+            for (int m = 0; m < NM; ++m) w[m] = buf_load16_w(rf[m].r, (uint32_t)k * (uint32_t)sizeof(WT), rf[m].soff);
             float g[E];
             if (gain) V::widen(*(const uint4*)(gain + k), g);
             else
@@ -490,7 +490,7 @@ __device__ __forceinline__ void gemv_w4(int r0, int r1, int K, const float* x, i
 #pragma unroll
                 for (int j = 0; j < NSW; ++j) {
                     const uint32_t qo = rv ? qoff[j] : kOOB, so = rv ? soff[j] : kOOB;
-                    const auto v = __builtin_amdgcn_raw_buffer_load_b64(t.q, qo, (uint32_t)rr * t.qrow, 0);
+                    const auto v = __builtin_amdgcn_raw_buffer_load_b64(t.q, qo, (uint32_t)rr * t.qrow, kStreamAux);
                     w[u].q[m][j] = make_uint2((uint32_t)v[0], (uint32_t)v[1]);
                     w[u].sc[m][j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(t.sc, so, (uint32_t)rr * t.srow, 0);
                 }
@@ -833,12 +833,12 @@ __device__ __forceinline__ void gemv_mfma(const MSeg (&seg)[NSEG], int K, const 
                 for (int t = 0; t < TMAX; ++t) {
                     if constexpr (W4M) {
                         const uint32_t vo = (kok && li < tval[t]) ? (uint32_t)li * rowbytes + (uint32_t)k / 2u : kOOB;
-                        st.q[t][0][c] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(ta[t], vo, tsoff[t], 0);
-                        if constexpr (DUAL) st.q[t][1][c] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(tb[t], vo, tsoff[t], 0);
+                        st.q[t][0][c] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(ta[t], vo, tsoff[t], kStreamAux);
+                        if constexpr (DUAL) st.q[t][1][c] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(tb[t], vo, tsoff[t], kStreamAux);
                     } else {
                         const uint32_t vo = (kok && li < tval[t]) ? (uint32_t)li * rowbytes + (uint32_t)k * 2u : kOOB;
-                        st.w[t][0][c] = buf_load16(ta[t], vo, tsoff[t]);
-                        if constexpr (DUAL) st.w[t][1][c] = buf_load16(tb[t], vo, tsoff[t]);
+                        st.w[t][0][c] = buf_load16_w(ta[t], vo, tsoff[t]);
+                        if constexpr (DUAL) st.w[t][1][c] = buf_load16_w(tb[t], vo, tsoff[t]);
                     }
                 }
                 st.x[c][0] = buf_load16_act(xr_rs, xo, 0);
@@ -1779,11 +1779,11 @@ __device__ __forceinline__ void prefetch_step(Prefetch& f) {
         const uint32_t i = f.next + (uint32_t)(k * kWaves + wave);
         if (i >= f.end) break;
         if (f.kb_b == 0) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(f.a, sink, 16, lane * 16, i * 1024u, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(f.a, sink, 16, lane * 16, i * 1024u, 0, kPfAux);
         } else {
             const uint32_t o = (i >> 1) * 1024u;
-            if (i & 1) __builtin_amdgcn_raw_ptr_buffer_load_lds(f.b, sink, 16, lane * 16, o, 0, 0);
-            else __builtin_amdgcn_raw_ptr_buffer_load_lds(f.a, sink, 16, lane * 16, o, 0, 0);
+            if (i & 1) __builtin_amdgcn_raw_ptr_buffer_load_lds(f.b, sink, 16, lane * 16, o, 0, kPfAux);
+            else __builtin_amdgcn_raw_ptr_buffer_load_lds(f.a, sink, 16, lane * 16, o, 0, kPfAux);
         }
     }
     f.next += (uint32_t)(kPrefetchSlice * kWaves);
@@ -1967,16 +1967,16 @@ __device__ __forceinline__ void attention_body(const KParams& p, int l, int bg, 
                     return tile + (uint32_t)(d * D * es) + add;
                 };
 #pragma unroll
-                for (int q = 0; q < NK; ++q) kd[q] = buf_load16(krs, off(li, (uint32_t)(16 * (4 * (q % KS) + lg))), 0);
+                for (int q = 0; q < NK; ++q) kd[q] = buf_load16_kv(krs, off(li, (uint32_t)(16 * (4 * (q % KS) + lg))), 0);
 #pragma unroll
-                for (int it = 0; it < NIT; ++it) vd[it] = buf_load16(vrs, off(it * PPW + rr, (uint32_t)(cc * 16)), 0);
+                for (int it = 0; it < NIT; ++it) vd[it] = buf_load16_kv(vrs, off(it * PPW + rr, (uint32_t)(cc * 16)), 0);
             }
         } else {
 #pragma unroll
-            for (int q = 0; q < NK; ++q) kd[q] = buf_load16(krs, row_off(vrow(base, q), (uint32_t)(cc * 16), staged), 0);
+            for (int q = 0; q < NK; ++q) kd[q] = buf_load16_kv(krs, row_off(vrow(base, q), (uint32_t)(cc * 16), staged), 0);
 #pragma unroll
             for (int it = 0; it < NIT; ++it)
-                vd[it] = buf_load16(vrs, row_off(vrow(base, it), (uint32_t)(cc * 16), staged), 0);
+                vd[it] = buf_load16_kv(vrs, row_off(vrow(base, it), (uint32_t)(cc * 16), staged), 0);
         }
     };
     // the first batch of K and V rows is requested before the prologue's math
