@@ -21,9 +21,15 @@ namespace {  // kernels get internal linkage: each instantiation unit registers 
 // Pop the next attention task dealt to this worker (single consumer: only
 // thread 0 of the owning workgroup reads its inbox; `head` lives in a
 // register and is written back when the workgroup exits).
-__device__ __forceinline__ bool inbox_try_pop(const KParams& p, int64_t& head, int& layer, int& bg, int& split) {
-    const RingSlot* sl = &p.inbox[(int64_t)blockIdx.x * (p.inbox_mask + 1) + (head & p.inbox_mask)];
-    if (ld_relaxed64(&sl->tag) != head + 1) return false;
+__device__ __forceinline__ const RingSlot* inbox_slot(const KParams& p, int64_t head) {
+    return &p.inbox[(int64_t)blockIdx.x * (p.inbox_mask + 1) + (head & p.inbox_mask)];
+}
+// `tag` is the slot's tag, loaded by the caller together with its other
+// polling loads
+__device__ __forceinline__ bool inbox_try_pop(const KParams& p, int64_t tag, int64_t& head, int& layer, int& bg,
+                                              int& split) {
+    const RingSlot* sl = inbox_slot(p, head);
+    if (tag != head + 1) return false;
     const int p0 = ld_co(&sl->p0), p1 = ld_co(&sl->p1);
     head++;
     layer = p0 >> 16;
@@ -45,8 +51,9 @@ __device__ __forceinline__ void scheduler_wave(const KParams& p) {
         int status = 0;  // 0 retry, 1 got message, 2 done, 3 abort
         if (lane == 0) {
             h = ld_relaxed64(&p.ctrl->mb_head);
+            const bool ab = aborted(p.ctrl);  // loaded together with the head
             if (h >= want) status = 2;
-            else if (aborted(p.ctrl)) status = 3;
+            else if (ab) status = 3;
             else {
                 RingSlot* sl = &p.mb[h & p.mb_mask];
                 if (ld_relaxed64(&sl->tag) == h + 1) {
@@ -211,14 +218,20 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s, uint
             if (waiting) {
                 if (threadIdx.x == 0) {
                     int c = 2;
+                    // the count planes, the abort flag and the inbox tag are
+                    // loaded together: one memory round trip per poll, not
+                    // one per check (the abort flag had been read only after
+                    // the count came back, doubling the time to see an event)
                     uint32_t v = 0;
 #pragma unroll
                     for (int j = 0; j < NP; ++j) v += ld_relaxed(&p.ev[j * p.ev_stride + t.wait_ev]);
+                    const bool ab = aborted(p.ctrl);
+                    const int64_t tag = p.jit_on ? ld_relaxed64(&inbox_slot(p, head)->tag) : 0;
                     if ((int32_t)(v - target) >= 0) c = 0;
-                    else if (aborted(p.ctrl)) c = 3;
+                    else if (ab) c = 3;
                     else {
                         int a, bb, cc;
-                        if (p.jit_on && inbox_try_pop(p, head, a, bb, cc)) {
+                        if (p.jit_on && inbox_try_pop(p, tag, head, a, bb, cc)) {
                             c = 1;
                             s.cmd[1] = a;
                             s.cmd[2] = bb;
@@ -319,8 +332,11 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s, uint
             if (threadIdx.x == 0) {
                 const uint64_t tb = now_ticks();
                 int c = 0;
-                while ((int32_t)(ld_relaxed(&p.ctrl->step_done) - ep1) < 0) {
-                    if (aborted(p.ctrl)) { c = 1; break; }
+                for (;;) {
+                    const uint32_t done = ld_relaxed(&p.ctrl->step_done);
+                    const bool ab = aborted(p.ctrl);  // loaded together with the step word
+                    if ((int32_t)(done - ep1) >= 0) break;
+                    if (ab) { c = 1; break; }
                     if (now_ticks() - tb > p.watchdog_ticks) { raise_abort(p.ctrl); c = 1; break; }
                     __builtin_amdgcn_s_sleep(1);
                 }
