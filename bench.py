@@ -3,8 +3,8 @@
 Workload (the headline): the 36-layer Qwen3-8B-shaped decoder (hidden 4096,
 32 query / 8 KV heads of 128, SwiGLU 12288, vocab 151936, bf16 weights
 ~N(0, 0.02) from a fixed seed), batch 1, a prompt of 1024 random token ids
-prefilled by teacher-forced decode steps (outside the timed region), then
-greedy decode. One timed step = one mk_decode_step_greedy launch: the
+prefilled by a prefill plan, 16 positions per launch (timed on its own, outside
+the decode's timed region), then greedy decode. One timed step = one mk_decode_step_greedy launch: the
 whole step, the greedy argmax and the seq_lens increment in one persistent
 launch.
 Further numbers, reported inside the same JSON object: the same model at
@@ -12,7 +12,10 @@ batch 16 with KV lengths log-uniform in [32, 4096] (`batch16`), at batch 8
 with a paged cache and KV lengths uniform in [4096, 16384] (`batch8_paged`),
 one 8B-shaped layer with hidden-state input/output, rotating over three
 weight copies so that the weights come from HBM (`layer8b`), and the tiny
-fp32 two-layer model (`tiny`, latency-bound: us/step only).
+fp32 two-layer model (`tiny`, latency-bound: us/step only). The matrix-core
+plans (batch 16, batch 8, the prefill chunks) read tiled copies of the layer
+matrices and the LM head (mk_pack_tiled; the same bits as row-major, which the
+batch-16 ablation times too); --no-tiled keeps them row-major.
 --phases B prints instead a per-operator summary of the in-kernel task
 trace (where a step's time goes) at batch B; --cpu-extended times the oracle
 on the first steps of the batch-16 and paged workloads (all rows).
@@ -100,6 +103,8 @@ def parse():
     ap.add_argument("--prefetch-kb", type=int, default=0,
                     help="KB of the awaited task's weights each worker prefetches (0: the plan default, -1: none)")
     ap.add_argument("--quick", action="store_true", help="tiny prompt, few steps (profiling runs)")
+    ap.add_argument("--no-tiled", action="store_true",
+                    help="row-major weights for the matrix-core plans too (default: their tiled copies)")
     ap.add_argument("--no-tiny", action="store_true", help="skip the tiny-model step time")
     ap.add_argument("--no-w4", action="store_true", help="skip the 4-bit-weight (W4A16) batch-1 measurement")
     ap.add_argument("--w4-steps", type=int, default=64)
@@ -161,14 +166,22 @@ def main():
     log("weights generated in %.1fs" % (time.time() - t0))
     t0 = time.time()
     dm = harness.DeviceModel(shape, weights, dev)
+    # the matrix-core plans (batch 16 and 8, the 16-position prefill chunks)
+    # read tiled copies of the layer matrices and the LM head
+    tiled = not args.no_tiled
+    if tiled:
+        dm.add_tiled()
     torch.cuda.synchronize()
-    log("weights uploaded in %.1fs" % (time.time() - t0))
+    log("weights uploaded%s in %.1fs" % (" and tiled" if tiled else "", time.time() - t0))
+
+    def wstruct(o):
+        return dm.struct_tiled if o.get("tiled") else dm.struct
     opts = dict(mode=args.mode, jit=args.jit, kv_chunk=args.kv_chunk, workers=args.workers,
                 lds_preload=args.lds_preload, prefetch_kb=args.prefetch_kb)
 
     # ---------------------------------------------------------------- batch 1
     B = 1
-    n_abl = 0 if args.no_ablation else 4 * (args.ablation_steps + 4)
+    n_abl = 0 if args.no_ablation else 5 * (args.ablation_steps + 4)  # at most five ablation runs
     n_multi = 0 if args.multi_step <= 0 else args.multi_step * (1 + max(1, args.steps // args.multi_step))
     cap = args.prompt + args.warmup + args.steps + n_abl + n_multi + 8
     kv = harness.DeviceKV(shape, B, cap)
@@ -184,13 +197,14 @@ def main():
     if args.prompt > 0:
         # the prompt in chunks of 16 positions per launch (a prefill plan);
         # the second, timed run rewrites the same bits into the cache
-        pplan = harness.build_plan(shape, PREFILL_CHUNK, cap, prefill=1, mode=args.mode, workers=args.workers)
+        pplan = harness.build_plan(shape, PREFILL_CHUNK, cap, prefill=1, mode=args.mode, workers=args.workers,
+                                   tiled=tiled)
         plog = torch.empty(shape.vocab, dtype=torch.float32, device=dev)
         pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        pplan.prefill(dm.struct, kv.struct, d_prompt, 0, args.prompt, plog)
+        pplan.prefill(wstruct(dict(tiled=tiled)), kv.struct, d_prompt, 0, args.prompt, plog)
         torch.cuda.synchronize()
         pe0.record(st)
-        pplan.prefill(dm.struct, kv.struct, d_prompt, 0, args.prompt, plog)
+        pplan.prefill(wstruct(dict(tiled=tiled)), kv.struct, d_prompt, 0, args.prompt, plog)
         pe1.record(st)
         torch.cuda.synchronize()
         if pplan.device_error():
@@ -208,35 +222,41 @@ def main():
         log("prefill of %d tokens: %.1f ms in %d launches (%.0f tokens/s)"
             % (args.prompt, p_ms, n_launch, prefill["value"]))
 
-    def run(n, plan, kv, d_tok, d_len, logits, events=None):
+    def run(n, plan, kv, d_tok, d_len, logits, events=None, ws=None):
         # greedy decode: each launch also writes the next tokens and advances the lengths
+        ws = dm.struct if ws is None else ws
         for i in range(n):
             if events is not None:
                 events[i][0].record(st)
-            plan.step_greedy(dm.struct, kv.struct, d_tok, d_len, logits)
+            plan.step_greedy(ws, kv.struct, d_tok, d_len, logits)
             if events is not None:
                 events[i][1].record(st)
 
-    def ablation(Bn, capn, kv, d_tok, d_len, logits):
+    def ablation(Bn, capn, kv, d_tok, d_len, logits, base=None):
         """ms/step of the same step with JIT attention through the scheduler
         waves, with JIT attention expanded by the completing QKV arrival on
-        all workers, in kernel-per-operator mode (same results, bitwise), and
-        with the static (searched) schedule (its own fixed split length)."""
+        all workers, in kernel-per-operator mode (same results, bitwise),
+        with the static (searched) schedule (its own fixed split length) and,
+        for a plan on tiled weights, with the row-major ones (same bits)."""
+        base = opts if base is None else base
         out = {"kv_len_start": int(d_len[0].item())}
-        runs = [("jit_scheduler", dict(opts, jit=1))]
+        runs = [("jit_scheduler", dict(base, jit=1))]
         if Bn >= 5:  # JIT expanded by the completing QKV arrival: the batch >= 8 instances
-            runs.append(("jit_inline", dict(opts, jit=3)))
-        runs += [("kernel_per_op", dict(opts, mode=1)), ("static_schedule", dict(opts, schedule=1))]
+            runs.append(("jit_inline", dict(base, jit=3)))
+        runs += [("kernel_per_op", dict(base, mode=1)), ("static_schedule", dict(base, schedule=1))]
+        if base.get("tiled"):
+            runs.append(("row_major_weights", dict(base, tiled=False)))
         for name, o in runs:
             pl = harness.build_plan(shape, Bn, capn, **o)
-            run(4, pl, kv, d_tok, d_len, logits)
+            run(4, pl, kv, d_tok, d_len, logits, ws=wstruct(o))
             torch.cuda.synchronize()
             e0.record(st)
-            run(args.ablation_steps, pl, kv, d_tok, d_len, logits)
+            run(args.ablation_steps, pl, kv, d_tok, d_len, logits, ws=wstruct(o))
             e1.record(st)
             torch.cuda.synchronize()
-            if pl.device_error():
-                raise SystemExit("device error in the %s ablation" % name)
+            err = pl.device_error()
+            if err:
+                raise SystemExit("device error %d in the %s ablation" % (err, name))
             out[name + "_ms_per_step"] = round(e0.elapsed_time(e1) / args.ablation_steps, 4)
             pl.close()
         return out
@@ -348,16 +368,17 @@ def main():
         del caches
         torch.cuda.synchronize()
         log("B=16 KV ready in %.1fs" % (time.time() - t0))
-        plan16 = harness.build_plan(shape, B16, cap16, **opts)
+        opts16 = dict(opts, tiled=tiled)
+        plan16 = harness.build_plan(shape, B16, cap16, **opts16)
         d_tok16 = torch.from_numpy(synth.tokens(wl16)).to(dev)
         d_len16 = torch.from_numpy(lens.astype(np.int32)).to(dev)
         logits16 = torch.empty((B16, shape.vocab), dtype=torch.float32, device=dev)
-        run(args.warmup, plan16, kv16, d_tok16, d_len16, logits16)
+        run(args.warmup, plan16, kv16, d_tok16, d_len16, logits16, ws=wstruct(opts16))
         torch.cuda.synchronize()
         l16 = d_len16.cpu().numpy().copy()
         ev16 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.b16_steps)]
         e0.record(st)
-        run(args.b16_steps, plan16, kv16, d_tok16, d_len16, logits16, ev16)
+        run(args.b16_steps, plan16, kv16, d_tok16, d_len16, logits16, ev16, ws=wstruct(opts16))
         e1.record(st)
         torch.cuda.synchronize()
         err = plan16.device_error()
@@ -375,10 +396,11 @@ def main():
             "value": round(tok16, 2), "unit": "tokens/s", "ms_per_step": round(t16 / args.b16_steps, 4),
             "kernel_ms_mean": round(float(k16.mean()), 4), "hbm_gbs": round(ach16, 1),
             "hbm_frac": round(ach16 / PEAK_HBM_GBS, 4), "bytes_per_launch": int(b16_bytes),
+            "weights": "tiled" if tiled else "row-major",
         }
         plan16.close()
         if not args.no_ablation:
-            result["batch16"]["ablation"] = ablation(B16, cap16, kv16, d_tok16, d_len16, logits16)
+            result["batch16"]["ablation"] = ablation(B16, cap16, kv16, d_tok16, d_len16, logits16, base=opts16)
             log("B=16 ablation: %s" % result["batch16"]["ablation"])
         del kv16
 
@@ -400,16 +422,17 @@ def main():
                 t[l].copy_(torch.randn(t[l].shape, generator=gen, device=dev).to(torch.bfloat16).view(torch.int16))
         torch.cuda.synchronize()
         log("B=8 paged KV ready in %.1fs (%d blocks)" % (time.time() - t0, kv8.n_blocks))
-        plan8 = harness.build_plan(shape, B8, cap8, paged=True, block=wl8.kv_block, max_blocks=table8.shape[1], **opts)
+        opts8 = dict(opts, tiled=tiled)
+        plan8 = harness.build_plan(shape, B8, cap8, paged=True, block=wl8.kv_block, max_blocks=table8.shape[1], **opts8)
         d_tok8 = torch.from_numpy(synth.tokens(wl8)).to(dev)
         d_len8 = torch.from_numpy(lens8.astype(np.int32)).to(dev)
         logits8 = torch.empty((B8, shape.vocab), dtype=torch.float32, device=dev)
-        run(args.warmup, plan8, kv8, d_tok8, d_len8, logits8)
+        run(args.warmup, plan8, kv8, d_tok8, d_len8, logits8, ws=wstruct(opts8))
         torch.cuda.synchronize()
         l8 = d_len8.cpu().numpy().copy()
         ev8 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(st8)]
         e0.record(st)
-        run(st8, plan8, kv8, d_tok8, d_len8, logits8, ev8)
+        run(st8, plan8, kv8, d_tok8, d_len8, logits8, ev8, ws=wstruct(opts8))
         e1.record(st)
         torch.cuda.synchronize()
         err = plan8.device_error()
@@ -428,6 +451,7 @@ def main():
             "value": round(tok8, 2), "unit": "tokens/s", "ms_per_step": round(t8 / st8, 4),
             "kernel_ms_mean": round(float(k8.mean()), 4), "hbm_gbs": round(ach8, 1),
             "hbm_frac": round(ach8 / PEAK_HBM_GBS, 4), "bytes_per_launch": int(b8_bytes),
+            "weights": "tiled" if tiled else "row-major",
         }
         plan8.close()
         del kv8
@@ -711,7 +735,8 @@ def phases(args):
     if name == "q8b_b1":
         lens = np.array([1100])
     cap = int(lens.max()) + 16
-    dm = harness.DeviceModel(shape, synth.model_weights(shape), dev)
+    tiled = B >= 3 and not args.no_tiled  # the matrix-core plans read tiled weights, as in the bench
+    dm = harness.DeviceModel(shape, synth.model_weights(shape), dev, tiled=tiled)
     table = synth.block_table([cap] * B, wl.kv_block) if wl.paged else None
     kv = harness.DeviceKV(shape, B, cap, paged=wl.paged, block=wl.kv_block, block_table=table)
     gen = torch.Generator(device=dev)
@@ -722,12 +747,12 @@ def phases(args):
     plan = harness.build_plan(shape, B, cap, paged=wl.paged, block=wl.kv_block,
                               max_blocks=table.shape[1] if table is not None else 0, trace=4096,
                               mode=args.mode, jit=args.jit, kv_chunk=args.kv_chunk, workers=args.workers,
-                              lds_preload=args.lds_preload, prefetch_kb=args.prefetch_kb)
+                              lds_preload=args.lds_preload, prefetch_kb=args.prefetch_kb, tiled=tiled)
     d_tok = torch.from_numpy(synth.tokens(wl)).to(dev)
     d_len = torch.from_numpy(lens.astype(np.int32)).to(dev)
     logits = torch.empty((B, shape.vocab), dtype=torch.float32, device=dev)
     for _ in range(4):
-        plan.step_greedy(dm.struct, kv.struct, d_tok, d_len, logits)
+        plan.step_greedy(dm.struct_tiled if tiled else dm.struct, kv.struct, d_tok, d_len, logits)
     torch.cuda.synchronize()
     tr = plan.trace()
     if plan.device_error():

@@ -176,7 +176,21 @@ typedef struct mk_exec_opts {
  *  max_seq_len bounds seq_lens[b] + 1.
  *  hidden_io: 1 = no embedding and no LM head; steps read and write hidden
  *  states (mk_decode_step_hidden).
+ *  weight_layout: MK_WEIGHTS_ROWS (0): every matrix [rows, K] row-major.
+ *  MK_WEIGHTS_TILED (1): the seven layer matrices and the LM head are in
+ *  the tiled layout that mk_pack_tiled writes (the embedding and the norm
+ *  gains stay as they are); the matrix-core GEMV then reads each 16-byte
+ *  lane load from 512-byte runs of consecutive bytes instead of 16 rows x
+ *  64 bytes (the MPK article's GEMV tasks stream weight tiles, §2.1; the
+ *  layout is this library's, chosen for the CDNA4 matrix-core operand).
+ *  Needs bf16 weights, batch >= 3 (the matrix-core instances), every row
+ *  count (n_heads*head_dim, n_kv_heads*head_dim, hidden, ffn, vocab) a
+ *  multiple of 8 and every K (hidden, ffn, n_heads*head_dim) a multiple of
+ *  64; other plans reject it (MK_ERR_ARG at mk_build_graph). Results are
+ *  bit-identical to the row-major layout.
  */
+enum mk_weight_layout { MK_WEIGHTS_ROWS = 0, MK_WEIGHTS_TILED = 1 };
+
 typedef struct mk_model_desc {
     int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, ffn, vocab;
     float rms_eps;
@@ -191,6 +205,7 @@ typedef struct mk_model_desc {
     int32_t max_blocks_per_seq; /* paged: row length of the block table */
     int32_t hidden_io;
     mk_exec_opts opts;
+    int32_t weight_layout;      /* MK_WEIGHTS_ROWS (default) or MK_WEIGHTS_TILED, below */
 } mk_model_desc;
 
 /* Device pointers to one layer's weights, PyTorch [out, in] row-major. */
@@ -380,6 +395,26 @@ int mk_decode_step_hidden(mk_plan* plan, const mk_weights* weights, const mk_kv_
  * production list, §5.3, done on the device).
  */
 int mk_get_device_error(mk_plan* plan, void* stream);
+
+/*
+ * Writes the tiled copy (MK_WEIGHTS_TILED) of one row-major bf16 matrix.
+ * Defining passage: the MPK article's GEMV tasks, each streaming the weight
+ * tile of its output rows (devpress.csdn.net, §2.1); the tile order is this
+ * library's own, fitted to the operand of the CDNA4 16x16x32 matrix cores.
+ *  src   device bf16 [rows, cols], row-major.
+ *  dst   device bf16, rows * cols elements, caller-owned, not overlapping src.
+ *        Rows are grouped in units of 8 (unit u: rows 8u .. 8u + 7), each
+ *        unit is 8 * cols consecutive elements, and inside a unit the
+ *        element of row 8u + i, column 32 s + 8 j + e (i, e < 8, j < 4) sits
+ *        at s * 256 + (8 j + i) * 8 + e: for each 32-column step, the 16
+ *        bytes of row i and column group j in the order the matrix cores'
+ *        lanes load them.
+ *  rows  a positive multiple of 8; cols a positive multiple of 64.
+ *  Runs on the current device, stream-ordered on `stream`.
+ * Returns MK_OK, MK_ERR_ARG (bad sizes or a null pointer; nothing launched)
+ * or MK_ERR_HIP.
+ */
+int mk_pack_tiled(const void* src, void* dst, int64_t rows, int64_t cols, void* stream);
 
 /*
  * Greedy next token: out_tokens[b] = argmax_v logits[b, v] (lowest index on

@@ -89,6 +89,7 @@ struct KParams {
     int prefetch_kb;          // next-task weight bytes pulled into L2 per worker (KB)
     int pre_slots;            // LDS preload slots per wave for the awaited GEMV task (0: off)
     int w4;                   // 1: the layer matrices are W4 buffers (batch <= 2); gains, embedding, LM head bf16
+    int wtiled;               // 1: layer matrices and LM head in the tiled layout (matrix-core instances)
     int prefill;              // 1: the batch rows are consecutive positions of sequence 0 (prompt chunk)
     int32_t* greedy_tokens;   // greedy step: next token of each sequence written here (else null)
     int32_t* greedy_lens;     // greedy step: each sequence's length advanced here
@@ -356,11 +357,25 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t v
 #ifndef MK_PF_AUX
 #define MK_PF_AUX 0
 #endif
+// Tiled weights (MK_WEIGHTS_TILED): a matrix-core load reads 512-byte runs
+// of consecutive bytes, whole lines that nothing reads again, so they stream
+// non-temporally. A stream probe on one MI355X (all CUs, four blocks in
+// flight per wave) measured 4.4-5.1 TB/s for the row-major operand pattern,
+// 5.6-5.9 TB/s for the same bytes in tile order with plain loads and
+// 6.2-6.5 TB/s with non-temporal ones.
+#ifndef MK_TILED_AUX
+#define MK_TILED_AUX 2
+#endif
 constexpr int kStreamAux = MK_STREAM_AUX;  // cache policy of weight loads (0 plain, 2 non-temporal)
+constexpr int kTiledAux = MK_TILED_AUX;    // cache policy of tiled weight loads
 constexpr int kKvAux = MK_KV_AUX;          // cache policy of cached K/V loads
 constexpr int kPfAux = MK_PF_AUX;          // cache policy of the prefetch loads (they must stay in L2)
 __device__ __forceinline__ uint4 buf_load16_w(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kStreamAux);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 buf_load16_wt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kTiledAux);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 __device__ __forceinline__ uint4 buf_load16_kv(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {

@@ -196,6 +196,21 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
         return fail(err, "kv_dtype must equal weight_dtype (bf16/bf16 or f32/f32)");
     }
     if (d.weight_dtype == MK_F32 && d.batch > 4) return fail(err, "f32 weights support batch <= 4");
+    if (d.weight_layout != MK_WEIGHTS_ROWS && d.weight_layout != MK_WEIGHTS_TILED)
+        return fail(err, "weight_layout must be MK_WEIGHTS_ROWS or MK_WEIGHTS_TILED");
+    const bool tiled = d.weight_layout == MK_WEIGHTS_TILED;
+    if (tiled) {
+        // the tiled layout is read by the matrix-core GEMV only
+        if (d.weight_dtype != MK_BF16) return fail(err, "tiled weights must be bf16");
+        if (d.batch < 3) return fail(err, "tiled weights need batch >= 3 (the matrix-core GEMV)");
+        const int64_t QD = (int64_t)d.n_heads * d.head_dim, KD = (int64_t)d.n_kv_heads * d.head_dim;
+        const int64_t rows[5] = {QD, KD, d.hidden, d.ffn, d.hidden_io ? 8 : d.vocab};
+        for (int64_t r : rows)
+            if (r % 8) return fail(err, "tiled weights: every matrix's row count must be a multiple of 8");
+        const int64_t ks[3] = {d.hidden, d.ffn, QD};
+        for (int64_t k : ks)
+            if (k % 64) return fail(err, "tiled weights: hidden, ffn and n_heads*head_dim must be multiples of 64");
+    }
     {
         const int64_t seg = d.weight_dtype == MK_F32 ? 256 : 512;
         const int64_t kmax = 4 * 8 * seg;  // four waves x eight 16-byte segments per lane
@@ -329,14 +344,17 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
             level++;
             return;
         }
-        int64_t nt = std::min<int64_t>(W, (rows + min_rows - 1) / min_rows);
+        // tiled weights: tasks own whole 8-row units of the tiled layout
+        const int64_t unit = (tiled && op != OP_EMBED && op != OP_APPEND) ? 8 : 1;
+        const int64_t units = rows / unit;
+        int64_t nt = std::min<int64_t>(W, (units + min_rows - 1) / min_rows);
         add_level(op, layer);
         for (int64_t i = 0; i < nt; ++i) {
             TaskRec t{};
             t.op = (uint8_t)op;
             t.layer = (uint16_t)layer;
-            t.a0 = (int32_t)(i * rows / nt);
-            t.a1 = (int32_t)((i + 1) * rows / nt);
+            t.a0 = (int32_t)(i * units / nt * unit);
+            t.a1 = (int32_t)((i + 1) * units / nt * unit);
             if (t.a1 <= t.a0) continue;
             t.wait_ev = wait;
             t.sig_ev = sig;
@@ -522,7 +540,10 @@ bool verify_plan(const HostPlan& p, std::string& err) {
         }
         std::sort(r.begin(), r.end());
         int64_t at = 0;
+        // tiled weights: every matrix task starts and ends on an 8-row unit
+        const bool unit8 = d.weight_layout == MK_WEIGHTS_TILED && op != OP_EMBED && op != OP_APPEND;
         for (auto& x : r) {
+            if (unit8 && (x.first % 8 || x.second % 8)) return fail(err, "tiled weights: task rows not on 8-row units");
             if (x.first != at || x.second <= x.first) return fail(err, "rows not covered exactly once at level " + std::to_string(lv));
             at = x.second;
         }

@@ -17,6 +17,7 @@
 // one kernel per task-graph level running the same task bodies.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -125,6 +126,20 @@ __global__ __launch_bounds__(64) void k_argmax_final(const ArgmaxScratch* sc, in
     if (lane == 0) out[b] = bi < V ? bi : 0;
 }
 static_assert(kArgBlocks == 64, "k_argmax_final reduces one slice winner per lane");
+
+// Tiled copy of a row-major bf16 matrix (mk_pack_tiled): one thread per
+// 16-byte piece of the destination. Piece j of unit u (8 rows) is 32-column
+// step j / 32 and, inside it, (column group, row) = ((j % 32) / 8, j % 8):
+// the piece a matrix-core lane (row i, group jj) loads for that step.
+__global__ __launch_bounds__(256) void k_pack_tiled(const uint4* src, uint4* dst, int64_t rows, int64_t cols) {
+    const int64_t n = rows * cols / 8;  // 16-byte pieces
+    const int64_t cp = cols / 8;        // pieces per row
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < n; q += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t u = q / cols, j = q % cols;  // a unit holds 8 * cols elements = cols pieces
+        const int64_t step = j / 32, grp = (j % 32) / 8, row = j % 8;
+        dst[q] = src[(u * 8 + row) * cp + step * 4 + grp];
+    }
+}
 
 // prefill chunk: row i takes prompt position min(i, n - 1) of the chunk
 __global__ void k_prefill_rows(const int32_t* tokens, int n, int pos, int B, int32_t* ptok, int32_t* plen) {
@@ -491,6 +506,7 @@ KParams make_params(const mk_plan* pl, const mk_weights* w, const mk_kv_cache* k
     p.prefetch_kb = d.opts.prefetch_kb == 0 ? 256 : (d.opts.prefetch_kb < 0 ? 0 : d.opts.prefetch_kb);
     p.pre_slots = lds_preload_on(pl) ? kPreSlots : 0;
     p.w4 = d.weight_dtype == MK_W4 ? 1 : 0;
+    p.wtiled = d.weight_layout == MK_WEIGHTS_TILED ? 1 : 0;
     p.prefill = hp.prefill;
     p.trace = pl->d_trace;
     p.trace_n = pl->d_trace_n;
@@ -810,6 +826,20 @@ int mk_argmax_noalloc(const float* logits, int32_t batch, int32_t vocab, int32_t
     if (!hip_ok(hipGetLastError(), "k_argmax_part launch")) return MK_ERR_HIP;
     hipLaunchKernelGGL(k_argmax_final, dim3(batch), dim3(64), 0, st, (const ArgmaxScratch*)sc, vocab, out_tokens);
     if (!hip_ok(hipGetLastError(), "k_argmax_final launch")) return MK_ERR_HIP;
+    return MK_OK;
+}
+
+int mk_pack_tiled(const void* src, void* dst, int64_t rows, int64_t cols, void* stream) {
+    if (!src || !dst) return set_err("mk_pack_tiled: null pointer"), MK_ERR_ARG;
+    if (rows < 8 || rows % 8 || cols < 64 || cols % 64)
+        return set_err("mk_pack_tiled: rows must be a positive multiple of 8 and cols of 64"), MK_ERR_ARG;
+    const int64_t pieces = rows * cols / 8;
+    const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst, nb = (uintptr_t)pieces * 16u;
+    if (a < b + nb && b < a + nb) return set_err("mk_pack_tiled: src and dst must not overlap"), MK_ERR_ARG;
+    const int blocks = (int)std::min<int64_t>((pieces + 255) / 256, 65536);
+    hipLaunchKernelGGL(k_pack_tiled, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const uint4*)src, (uint4*)dst,
+                       rows, cols);
+    if (!hip_ok(hipGetLastError(), "k_pack_tiled launch")) return MK_ERR_HIP;
     return MK_OK;
 }
 

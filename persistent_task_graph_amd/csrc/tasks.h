@@ -737,7 +737,12 @@ __device__ __forceinline__ mk_f32x4 mfma_bf16(const uint4& a, const mk_bf16x8& b
 // as 128 + code, one byte permute per pair, with 136 times the sum of x taken
 // off afterwards, measured 10x the error: the matrix cores add the large
 // partial sums less exactly.)
-template <int NB, bool DUAL, int TMAX, int NSEG, typename OutFn, int NST = 2, bool W4M = false>
+// TL: the matrices are in the tiled layout (MK_WEIGHTS_TILED): row 8u + i,
+// column 32 s + 8 j + e of a run at u * 8 * K + s * 256 + (8 j + i) * 8 + e,
+// so the 16 lanes (row, group j) of a load read 256 consecutive bytes and
+// the whole load two 512-byte runs; the operands, and so the bits, are the
+// row-major path's.
+template <int NB, bool DUAL, int TMAX, int NSEG, typename OutFn, int NST = 2, bool W4M = false, bool TL = false>
 __device__ __forceinline__ void gemv_mfma(const MSeg (&seg)[NSEG], int K, const float* x, int ldx, int B,
                                           const bf16_t* gain, float eps, OutFn out, const Lds& s, bool tr) {
     constexpr int NM = DUAL ? 2 : 1;
@@ -835,6 +840,13 @@ __device__ __forceinline__ void gemv_mfma(const MSeg (&seg)[NSEG], int K, const 
                         const uint32_t vo = (kok && li < tval[t]) ? (uint32_t)li * rowbytes + (uint32_t)k / 2u : kOOB;
                         st.q[t][0][c] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(ta[t], vo, tsoff[t], kStreamAux);
                         if constexpr (DUAL) st.q[t][1][c] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(tb[t], vo, tsoff[t], kStreamAux);
+                    } else if constexpr (TL) {
+                        const uint32_t vo = (kok && li < tval[t])
+                                                ? (uint32_t)(li >> 3) * 8u * rowbytes + (uint32_t)(k >> 5) * 512u +
+                                                      (uint32_t)((lk << 3) | (li & 7)) * 16u
+                                                : kOOB;
+                        st.w[t][0][c] = buf_load16_wt(ta[t], vo, tsoff[t]);
+                        if constexpr (DUAL) st.w[t][1][c] = buf_load16_wt(tb[t], vo, tsoff[t]);
                     } else {
                         const uint32_t vo = (kok && li < tval[t]) ? (uint32_t)li * rowbytes + (uint32_t)k * 2u : kOOB;
                         st.w[t][0][c] = buf_load16_w(ta[t], vo, tsoff[t]);
@@ -1292,6 +1304,20 @@ __device__ __forceinline__ void run_w4_mfma_task(const KParams& p, const TaskRec
 // w: the task's layer pointers, p.lw[t.layer] (the worker reads them before
 // the task's event fires). pre_rows: leading rows of the task whose weights
 // were preloaded into this worker's LDS slots (batch <= 2 only; 0 otherwise).
+// Runs f(std::true_type) for a plan with tiled weights, else
+// f(std::false_type). The W4 instances never see tiled weights (plans reject
+// the combination), so they compile the row-major path only.
+template <typename F>
+__device__ __forceinline__ void mfma_dispatch(const KParams& p, F f) {
+    if constexpr (!kW4MfmaKernels) {
+        if (p.wtiled) {
+            f(std::true_type{});
+            return;
+        }
+    }
+    f(std::false_type{});
+}
+
 template <typename WT, int NB>
 __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t, const Lds& s, const LayerPtrs& w,
                                               int pre_rows = 0) {
@@ -1331,7 +1357,10 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
             auto out = [&](int r, int b, float v, float) { st_co(&o[(int64_t)b * ld + r], v * s.rstd[b]); };
             if constexpr (kMfma) {
                 const MSeg sg[3] = {{tq.r, tq.r, tq.n, tq.lo}, {tk.r, tk.r, tk.n, QD + tk.lo}, {tv.r, tv.r, tv.n, QD + KD + tv.lo}};
-                gemv_mfma<NB, false, 2>(sg, H, x, H, B, (const bf16_t*)w.attn_norm, p.eps, out, s, p.trace != nullptr);
+                mfma_dispatch(p, [&](auto tl) {
+                    gemv_mfma<NB, false, 2, 3, decltype(out), 2, false, decltype(tl)::value>(
+                        sg, H, x, H, B, (const bf16_t*)w.attn_norm, p.eps, out, s, p.trace != nullptr);
+                });
             } else {
                 gemv_dispatch<WT, NB, false>(r0, r1, H, x, H, B, (const WT*)w.attn_norm, p.eps, rowp, out, s, p.trace != nullptr, pre_rows);
             }
@@ -1350,7 +1379,10 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
             };
             if constexpr (kMfma) {
                 const MSeg sg[1] = {{to.r, to.r, to.n, to.lo}};
-                gemv_mfma<NB, false, 1, 1, decltype(out), 3>(sg, K, a, K, B, (const bf16_t*)nullptr, p.eps, out, s, p.trace != nullptr);
+                mfma_dispatch(p, [&](auto tl) {
+                    gemv_mfma<NB, false, 1, 1, decltype(out), 3, false, decltype(tl)::value>(
+                        sg, K, a, K, B, (const bf16_t*)nullptr, p.eps, out, s, p.trace != nullptr);
+                });
             } else {
                 gemv_dispatch<WT, NB, false>(r0, r1, K, a, K, B, (const WT*)nullptr, p.eps, rowp, out, s, p.trace != nullptr, pre_rows);
             }
@@ -1373,7 +1405,10 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
             };
             if constexpr (kMfma) {
                 const MSeg sg[1] = {{tg.r, tu.r, tg.n, tg.lo}};
-                gemv_mfma<NB, true, 3>(sg, H, x, H, B, (const bf16_t*)w.mlp_norm, p.eps, out, s, p.trace != nullptr);
+                mfma_dispatch(p, [&](auto tl) {
+                    gemv_mfma<NB, true, 3, 1, decltype(out), 2, false, decltype(tl)::value>(
+                        sg, H, x, H, B, (const bf16_t*)w.mlp_norm, p.eps, out, s, p.trace != nullptr);
+                });
             } else {
                 gemv_dispatch<WT, NB, true>(r0, r1, H, x, H, B, (const WT*)w.mlp_norm, p.eps, rowp, out, s, p.trace != nullptr, pre_rows);
             }
@@ -1392,7 +1427,10 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
             };
             if constexpr (kMfma) {
                 const MSeg sg[1] = {{td.r, td.r, td.n, td.lo}};
-                gemv_mfma<NB, false, 1, 1, decltype(out), 3>(sg, F, h, F, B, (const bf16_t*)nullptr, p.eps, out, s, p.trace != nullptr);
+                mfma_dispatch(p, [&](auto tl) {
+                    gemv_mfma<NB, false, 1, 1, decltype(out), 3, false, decltype(tl)::value>(
+                        sg, F, h, F, B, (const bf16_t*)nullptr, p.eps, out, s, p.trace != nullptr);
+                });
             } else {
                 gemv_dispatch<WT, NB, false>(r0, r1, F, h, F, B, (const WT*)nullptr, p.eps, rowp, out, s, p.trace != nullptr, pre_rows);
             }
@@ -1407,7 +1445,10 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
             auto out = [&](int r, int b, float v, float) { o[(int64_t)b * V + r] = v * s.rstd[b]; };  // read after the launch
             if constexpr (kMfma) {
                 const MSeg sg[1] = {{tl.r, tl.r, tl.n, tl.lo}};
-                gemv_mfma<NB, false, 8>(sg, H, x, H, B, (const bf16_t*)p.final_norm, p.eps, out, s, p.trace != nullptr);
+                mfma_dispatch(p, [&](auto tl) {
+                    gemv_mfma<NB, false, 8, 1, decltype(out), 2, false, decltype(tl)::value>(
+                        sg, H, x, H, B, (const bf16_t*)p.final_norm, p.eps, out, s, p.trace != nullptr);
+                });
             } else {
                 gemv_dispatch<WT, NB, false>(r0, r1, H, x, H, B, (const WT*)p.final_norm, p.eps, rowp, out, s, p.trace != nullptr, pre_rows);
             }

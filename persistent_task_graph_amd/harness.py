@@ -37,10 +37,17 @@ def from_device(t) -> np.ndarray:
     return a
 
 
-class DeviceModel:
-    """Weights of one model on the device plus the mk_weights struct."""
+TILED_MATRICES = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
 
-    def __init__(self, shape, weights: Dict, device="cuda"):
+
+class DeviceModel:
+    """Weights of one model on the device plus the mk_weights struct.
+
+    tiled=True also makes tiled copies (mk_pack_tiled) of the layer matrices
+    and the LM head, with their own struct `struct_tiled` for plans built
+    with tiled=True (the embedding and the gains are shared)."""
+
+    def __init__(self, shape, weights: Dict, device="cuda", tiled: bool = False):
         self.shape = shape
         self.layers: List[Dict[str, object]] = []
         for lw in weights["layers"]:
@@ -49,6 +56,27 @@ class DeviceModel:
         self.lm_head = to_device(weights["lm_head"], device) if "lm_head" in weights else None
         self.final_norm = to_device(weights["final_norm"], device) if "final_norm" in weights else None
         self.struct = mk.make_weights(self.layers, self.embed, self.final_norm, self.lm_head)
+        self.struct_tiled = None
+        if tiled:
+            self.add_tiled()
+
+    def add_tiled(self) -> None:
+        """Tiled copies of the seven layer matrices and the LM head."""
+        torch = _torch()
+
+        def pack(t):
+            out = torch.empty_like(t)
+            mk.pack_tiled(t, out, t.shape[0], t.shape[1])
+            return out
+
+        self.layers_tiled = []
+        for lw in self.layers:
+            d = dict(lw)
+            for k in TILED_MATRICES:
+                d[k] = pack(lw[k])
+            self.layers_tiled.append(d)
+        self.lm_head_tiled = pack(self.lm_head) if self.lm_head is not None else None
+        self.struct_tiled = mk.make_weights(self.layers_tiled, self.embed, self.final_norm, self.lm_head_tiled)
 
 
 class DeviceKV:

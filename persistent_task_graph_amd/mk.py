@@ -27,7 +27,8 @@ OP_QKV, OP_O, OP_GATEUP, OP_DOWN, OP_LM, OP_ATTN, OP_EMBED, OP_APPEND = 1, 2, 3,
 
 EXPORTS = ["mk_build_graph", "mk_destroy_plan", "mk_last_error", "mk_plan_query", "mk_decode_step",
            "mk_decode_step_greedy", "mk_decode_step_hidden", "mk_get_device_error", "mk_argmax", "mk_plan_verify", "mk_plan_dry_run",
-           "mk_plan_trace", "mk_argmax_noalloc", "mk_decode_steps_greedy", "mk_prefill"]
+           "mk_plan_trace", "mk_argmax_noalloc", "mk_decode_steps_greedy", "mk_prefill", "mk_pack_tiled"]
+MK_WEIGHTS_ROWS, MK_WEIGHTS_TILED = 0, 1
 
 
 class ExecOpts(ctypes.Structure):
@@ -42,7 +43,7 @@ class ModelDesc(ctypes.Structure):
                [("rms_eps", ctypes.c_float), ("rope_base", ctypes.c_float)] + \
                [(n, ctypes.c_int32) for n in ("qk_norm", "weight_dtype", "kv_dtype", "batch", "max_seq_len", "kv_layout",
                                                "kv_block", "max_blocks_per_seq", "hidden_io")] + \
-               [("opts", ExecOpts)]
+               [("opts", ExecOpts), ("weight_layout", ctypes.c_int32)]
 
 
 LAYER_FIELDS = ("attn_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo", "mlp_norm", "w_gate", "w_up", "w_down")
@@ -109,7 +110,8 @@ def lib() -> ctypes.CDLL:
         L.mk_argmax_noalloc.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp, vp]
         L.mk_decode_steps_greedy.argtypes = [vp, P(Weights), P(KVCache), vp, vp, vp, ctypes.c_int32, vp, vp]
         L.mk_prefill.argtypes = [vp, P(Weights), P(KVCache), vp, ctypes.c_int32, ctypes.c_int32, vp, vp]
-        for f in ("mk_argmax_noalloc", "mk_decode_steps_greedy", "mk_prefill", "mk_plan_query", "mk_decode_step", "mk_decode_step_greedy", "mk_decode_step_hidden",
+        L.mk_pack_tiled.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int64, vp]
+        for f in ("mk_pack_tiled", "mk_argmax_noalloc", "mk_decode_steps_greedy", "mk_prefill", "mk_plan_query", "mk_decode_step", "mk_decode_step_greedy", "mk_decode_step_hidden",
                   "mk_get_device_error", "mk_argmax", "mk_plan_verify", "mk_plan_dry_run", "mk_plan_trace"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -127,9 +129,11 @@ def _check(rc: int, what: str) -> int:
 
 
 def make_desc(shape, batch: int, max_seq_len: int, *, paged: bool = False, kv_block: int = 16,
-              max_blocks_per_seq: int = 0, **opts) -> ModelDesc:
-    """Fill mk_model_desc from a model shape (attributes as in synth.ModelShape)."""
+              max_blocks_per_seq: int = 0, tiled: bool = False, **opts) -> ModelDesc:
+    """Fill mk_model_desc from a model shape (attributes as in synth.ModelShape).
+    tiled: the layer matrices and LM head are in the tiled layout (mk_pack_tiled)."""
     d = ModelDesc()
+    d.weight_layout = MK_WEIGHTS_TILED if tiled else MK_WEIGHTS_ROWS
     d.n_layers, d.hidden, d.n_heads, d.n_kv_heads = shape.n_layers, shape.hidden, shape.n_heads, shape.n_kv_heads
     d.head_dim, d.ffn, d.vocab = shape.head_dim, shape.ffn, shape.vocab
     d.rms_eps, d.rope_base = shape.eps, shape.rope_base
@@ -277,6 +281,11 @@ def argmax_noalloc(logits, out_tokens, batch: int, vocab: int, stream=None) -> N
     """mk_argmax_noalloc: greedy tokens of `batch` rows of `vocab` logits, no plan, no allocation."""
     _check(lib().mk_argmax_noalloc(_ptr(logits), int(batch), int(vocab), _ptr(out_tokens), _stream(stream)),
            "mk_argmax_noalloc")
+
+
+def pack_tiled(src, dst, rows: int, cols: int, stream=None) -> None:
+    """mk_pack_tiled: tiled copy of a row-major bf16 [rows, cols] matrix into dst (device)."""
+    _check(lib().mk_pack_tiled(_ptr(src), _ptr(dst), int(rows), int(cols), _stream(stream)), "mk_pack_tiled")
 
 
 def make_weights(layer_ptrs, embed=None, final_norm=None, lm_head=None) -> Weights:

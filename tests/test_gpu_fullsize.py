@@ -191,6 +191,35 @@ def test_q8b_b16_loguniform_sampled_rows_match_oracle(q8b):
     plan.close()
 
 
+def test_q8b_b16_tiled_weights_bitwise(q8b):
+    # the 8B model's layer matrices and LM head in the tiled layout: the
+    # batch-16 steps give the row-major layout's logits and tokens bit for bit
+    import types
+
+    w, dm, orc = q8b
+    wl = synth.WORKLOADS["q8b_b16"]
+    shape, B = wl.shape, wl.batch
+    lens = synth.seq_lengths(wl)
+    steps = 2
+    cap = int(lens.max()) + steps + 8
+    log("q8b B=16: tiled vs row-major weights, %d steps" % steps)
+    kv = harness.DeviceKV(shape, B, cap)
+    for b in range(B):
+        c = synth.kv_sequence(shape, b, int(lens[b]), cap)
+        kv.load_sequence(b, c["k"], c["v"], int(lens[b]))
+    plan = harness.build_plan(shape, B, cap)
+    a = _decode(plan, dm, kv, synth.tokens(wl), lens, steps, shape)
+    plan.close()
+    if dm.struct_tiled is None:
+        dm.add_tiled()
+    plan = harness.build_plan(shape, B, cap, tiled=True)
+    b = _decode(plan, types.SimpleNamespace(struct=dm.struct_tiled, owner=dm), kv, synth.tokens(wl), lens, steps, shape)
+    plan.close()
+    for (ta, la, na), (tb, lb, nb) in zip(a, b):
+        assert np.array_equal(la.view(np.uint32), lb.view(np.uint32))
+        assert np.array_equal(na, nb)
+
+
 def test_q8b_b8_paged_long_context_sampled_row_matches_oracle(q8b):
     import torch
 

@@ -529,10 +529,10 @@ def test_mid_w4_modes_bitwise(mid_w4_weights):
 # e with |e| <= 2^-17 |x|: a dot product over K = 4096 then errs by at most
 # 2^-17 sum|w x|, about 2^-17 (2/pi) sqrt(K) times its rms for random signs.
 HILO_TOL = 2.0 ** -17 * (2 / np.pi) * np.sqrt(4096)  # 3.1e-4
-def _prefill_case(mid_weights, B, pos0, T, paged=False, **opts):
+def _prefill_case(mid_weights, B, pos0, T, paged=False, tiled=False, **opts):
     """Prefill T prompt tokens after pos0 cached positions with a batch-B
     prefill plan; returns (the setup, the device KV, the last logits, the
-    prompt)."""
+    prompt). tiled: the weights in the tiled layout."""
     import torch
     from persistent_task_graph_amd import harness
 
@@ -541,11 +541,13 @@ def _prefill_case(mid_weights, B, pos0, T, paged=False, **opts):
     s = make_setup(MID, 1, [pos0], cap, weights=mid_weights, paged=paged, table=table)
     kv = device_kv(s)
     mb = table.shape[1] if paged else 0
-    plan = harness.build_plan(MID, B, cap, paged=paged, max_blocks=mb, prefill=1, **opts)
+    plan = harness.build_plan(MID, B, cap, paged=paged, max_blocks=mb, prefill=1, tiled=tiled, **opts)
     prompt = synth.uniform_int(synth.SEED_TOKENS, 40 + pos0, 0, MID.vocab - 1, T).astype(np.int32)
     d_tok = torch.from_numpy(prompt).cuda()
     logits = torch.empty(MID.vocab, dtype=torch.float32, device="cuda")
-    plan.prefill(s.dm.struct, kv.struct, d_tok, pos0, T, logits)
+    if tiled:
+        s.dm.add_tiled()
+    plan.prefill(s.dm.struct_tiled if tiled else s.dm.struct, kv.struct, d_tok, pos0, T, logits)
     torch.cuda.synchronize()
     assert plan.device_error() == 0
     plan.close()
@@ -620,3 +622,93 @@ def test_prefill_then_decode_continues(mid_weights):
         assert int(tok.item()) == int(np.argmax(ref))
     assert plan.device_error() == 0
     plan.close()
+
+
+# ---------------------------------------------------------------- tiled weights
+
+def _tiled(s):
+    """The same setup with the layer matrices and the LM head in the tiled
+    layout (mk_pack_tiled); the embedding and gains are shared."""
+    import copy
+    import types
+
+    if s.dm.struct_tiled is None:
+        s.dm.add_tiled()
+    t = copy.copy(s)
+    # the struct holds bare pointers: keep the DeviceModel (and so the
+    # tensors they point into) alive with the view
+    t.dm = types.SimpleNamespace(struct=s.dm.struct_tiled, owner=s.dm)
+    return t
+
+
+def test_pack_tiled_matches_layout():
+    # the layout as mk.h defines it: row 8u + i, column 32 s + 8 j + e of the
+    # row-major matrix at u * 8 * cols + s * 256 + (8 j + i) * 8 + e
+    import torch
+    from persistent_task_graph_amd import harness, mk
+
+    rng = np.random.default_rng(5)
+    for R, C in ((8, 64), (40, 192), (24, 4096)):
+        w = rng.integers(0, 65536, size=(R, C), dtype=np.uint16)
+        src = harness.to_device(w)
+        dst = torch.empty_like(src)
+        mk.pack_tiled(src, dst, R, C)
+        torch.cuda.synchronize()
+        got = harness.from_device(dst).reshape(-1)
+        want = np.empty(R * C, np.uint16)
+        for u in range(R // 8):
+            for i in range(8):
+                for c in range(C):
+                    sidx, j, e = c // 32, (c % 32) // 8, c % 8
+                    want[u * 8 * C + sidx * 256 + (8 * j + i) * 8 + e] = w[8 * u + i, c]
+        assert np.array_equal(got, want), (R, C)
+
+
+@pytest.mark.parametrize("B,paged,opts", [
+    (3, False, {}),                 # the batch-4 instance with one empty column
+    (16, False, {}),
+    (8, True, {}),                  # paged cache
+    (16, False, {"mode": 1}),       # kernel-per-op
+    (16, False, {"jit": 3}),        # JIT expanded by the completing QKV arrival
+    (4, False, {"schedule": 1}),    # static schedule (16-row task cuts)
+])
+def test_mid_tiled_weights_bitwise(mid_weights, B, paged, opts):
+    # the matrix-core GEMV reads the same operands from the tiled copies: the
+    # logits and the greedy tokens are the row-major layout's, bit for bit
+    lens = [int(v) for v in np.linspace(5, 700, B)]
+    log("mid bf16: tiled vs row-major weights, B=%d paged=%s %s" % (B, paged, opts))
+    cap = max(lens) + 8
+    table = synth.block_table([cap] * B, 16) if paged else None
+    s = make_setup(MID, B, lens, cap, weights=mid_weights, paged=paged, table=table)
+    t0 = _tokens(MID, B, 21)
+    a, _ = _logits_seq(s, 3, tokens=t0, **opts)
+    b, _ = _logits_seq(_tiled(s), 3, tokens=t0, tiled=True, **opts)
+    _bitwise(a, b)
+    for (ta, la, na), (tb, lb, nb) in zip(a, b):
+        assert np.array_equal(na, nb)
+
+
+def test_mid_tiled_weights_match_oracle(mid_weights):
+    # and against the oracle directly (batch 16, ragged lengths)
+    B = 16
+    lens = [int(v) for v in np.linspace(0, 530, B)]
+    s = _tiled(make_setup(MID, B, lens, 540, weights=mid_weights))
+    plan = plan_for(s, tiled=True)
+    kv = device_kv(s)
+    out, err = run_gpu(s, plan, kv, _tokens(MID, B, 23), 2)
+    assert err == 0
+    orc, _ = run_oracle(s, out)
+    worst, agree = compare(out, orc)
+    log("mid tiled B=16: max|d|/std = %.3g, top-1 = %.3f" % (worst, agree))
+    assert worst <= 2e-2
+    assert agree >= 0.99
+    plan.close()
+
+
+def test_prefill_tiled_weights_bitwise(mid_weights):
+    log("prefill: tiled vs row-major weights, bitwise")
+    _, kv_a, a, _ = _prefill_case(mid_weights, 16, 30, 35)
+    _, kv_b, b, _ = _prefill_case(mid_weights, 16, 30, 35, tiled=True)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    for x, y in zip(kv_a.read_sequence(0, 65), kv_b.read_sequence(0, 65)):
+        assert np.array_equal(x, y)

@@ -283,3 +283,45 @@ def test_w4_plans_any_batch(lib, B):
     p.verify()
     assert p.info().weight_bytes_per_step == synth.Q8B_W4.step_weight_bytes()
     assert p.dry_run(n_threads=4, seed=B, seq_lens=[100 + 7 * b for b in range(B)]) == 0, mk.last_error()
+
+
+@pytest.mark.parametrize("opts", [dict(), dict(schedule=1), dict(prefill=1), dict(jit=3), dict(mode=1)])
+def test_tiled_plans_verify_on_8_row_units(lib, opts):
+    # tiled weights: the verifier also checks that every matrix task starts
+    # and ends on an 8-row unit of the tiled layout
+    for B in (3, 16):
+        if opts.get("jit") == 3 and B < 5:
+            continue
+        p = _plan(synth.Q8B, B, 4096, tiled=True, **opts)
+        p.verify()
+        assert p.dry_run(n_threads=4, seed=B, seq_lens=[100 + 37 * b for b in range(B)]) == 0, mk.last_error()
+
+
+@pytest.mark.parametrize("case, msg", [
+    (dict(batch=2), "batch >= 3"),
+    (dict(batch=1), "batch >= 3"),
+    (dict(shape=synth.TINY, batch=4), "bf16"),
+    (dict(shape=synth.Q8B_W4, batch=16), "bf16"),
+    (dict(shape=replace(synth.Q8B, vocab=151937), batch=16), "multiple of 8"),
+    (dict(shape=replace(synth.Q8B, ffn=12320), batch=16), "multiples of 64"),
+])
+def test_tiled_plans_rejected(lib, case, msg):
+    shape = case.get("shape", synth.Q8B)
+    d = mk.make_desc(shape, case["batch"], 1024, host_only=1, tiled=True)
+    h = lib.mk_build_graph(ctypes.byref(d))
+    assert not h
+    assert msg in mk.last_error()
+
+
+@pytest.mark.parametrize("rows, cols", [(12, 64), (0, 64), (16, 32), (16, 96)])
+def test_pack_tiled_rejects_bad_sizes(lib, rows, cols):
+    # checked before anything is launched
+    assert lib.mk_pack_tiled(ctypes.c_void_p(4096), ctypes.c_void_p(1 << 30), rows, cols, None) == mk.MK_ERR_ARG
+    assert "mk_pack_tiled" in mk.last_error()
+
+
+def test_pack_tiled_rejects_null_and_overlap(lib):
+    assert lib.mk_pack_tiled(None, ctypes.c_void_p(4096), 8, 64, None) == mk.MK_ERR_ARG
+    # [4096, 4096 + 1024) and [4608, ...) overlap
+    assert lib.mk_pack_tiled(ctypes.c_void_p(4096), ctypes.c_void_p(4608), 8, 64, None) == mk.MK_ERR_ARG
+    assert "overlap" in mk.last_error()
