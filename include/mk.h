@@ -132,6 +132,20 @@ enum mk_device_error {
  *                RoPE, K/V store) runs between QKV and attention, so each
  *                row's attention sees the rows before it. Ahead-of-time
  *                attention only (not jit = 1); token input only.
+ *  down_ksplit   parts the down projection's K (the SwiGLU width) is cut
+ *                into on the matrix-core path (bf16, batch >= 3, event
+ *                runtime): each part is its own task over 16 * ksplit rows,
+ *                writing a partial tile, and the last part of a row group
+ *                to arrive adds the partials in part order (the attention
+ *                combine's last-arrival rule, the MPK article §2.1) and
+ *                signals; every worker then reads 1 / ksplit of the input
+ *                vector instead of all of it. 0 (default): 4 where the
+ *                matrix-core path runs and ffn is a multiple of 256, else
+ *                1; 1: off; 2 or 4: that many parts (ffn a multiple of
+ *                64 * parts). Not with schedule = 1 (its search cuts whole
+ *                rows). Results differ from the unsplit sum only by
+ *                rounding order; every execution mode of one plan gives the
+ *                same bits.
  */
 typedef struct mk_exec_opts {
     int32_t mode;
@@ -151,6 +165,7 @@ typedef struct mk_exec_opts {
     int32_t lds_preload;
     int32_t schedule;
     int32_t prefill;
+    int32_t down_ksplit;
 } mk_exec_opts;
 
 /*

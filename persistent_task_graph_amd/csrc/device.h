@@ -90,6 +90,8 @@ struct KParams {
     int pre_slots;            // LDS preload slots per wave for the awaited GEMV task (0: off)
     int w4;                   // 1: the layer matrices are W4 buffers (batch <= 2); gains, embedding, LM head bf16
     int wtiled;               // 1: layer matrices and LM head in the tiled layout (matrix-core instances)
+    float* kpart;             // K-split down projection: partial tiles [rows][parts][16]
+    uint32_t* karrive;        // K-split down projection: arrivals per row group (self-resetting)
     int prefill;              // 1: the batch rows are consecutive positions of sequence 0 (prompt chunk)
     int32_t* greedy_tokens;   // greedy step: next token of each sequence written here (else null)
     int32_t* greedy_lens;     // greedy step: each sequence's length advanced here

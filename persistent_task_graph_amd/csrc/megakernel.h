@@ -171,10 +171,12 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s, uint
     int chunk = 0;  // the step's attention chunk, found before the first attention task
     Prefetch pf;
     pf.next = pf.end = 0;
+    pf.chunk_kb = 0;
     if constexpr (!kStream)
         if (qb < qe) pf = prefetch_setup<WT>(p, p.tasks[p.queue[qb]]);
     Prefetch pf_next;
     pf_next.next = pf_next.end = 0;
+    pf_next.chunk_kb = 0;
     for (int qi = qb; qi < qe; ++qi) {
         const int tid_task = p.queue[qi];
         const TaskRec t = p.tasks[tid_task];
@@ -285,18 +287,19 @@ __device__ __forceinline__ void worker_loop(const KParams& p, const Lds& s, uint
             t0 = now_ticks();
         }
         if (t.op != OP_ATTN) {
+            bool gemv_sig = true;  // false: a K-split part that did not merge its group
             if constexpr (kStream) {
                 if (is_streamed(t.op)) run_stream_task<WT>(p, st, ring, qe, t, s);
                 else if (t.op == OP_EMBED) embed_task<WT>(p, t);
             } else {
-                run_gemv_task<WT, NB>(p, t, s, lwt, (NB <= 2 && p.pre_slots > 0) ? preload_done_rows(s) : 0);
+                gemv_sig = run_gemv_task<WT, NB>(p, t, s, lwt, (NB <= 2 && p.pre_slots > 0) ? preload_done_rows(s) : 0);
             }
             // JIT expanded by the completing QKV arrival: batch >= 8
             // instances only (the expansion code in the batch <= 4 loops
             // costs those steps 1-3% even when it never runs)
-            bool signalled = false;
+            bool signalled = !gemv_sig;
             if constexpr (NB >= 8)
-                if (p.jit_on == 2) {
+                if (p.jit_on == 2 && !signalled) {
                     signal_gemv_jit_inline(p, t.sig_ev, s, (int)blockIdx.x & (NP - 1));
                     signalled = true;
                 }

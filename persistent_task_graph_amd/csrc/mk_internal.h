@@ -39,7 +39,8 @@ struct TaskRec {
     int32_t wait_ev;  // event to wait on, -1 = none
     int32_t sig_ev;   // event to signal on completion, -1 = none
     int32_t level;    // task-graph level (kernel-per-op grouping, queue order)
-    int32_t pad[2];
+    int32_t kpart;    // K-split GEMV: part index | (parts << 8); 0 = whole K
+    int32_t kgroup;   // K-split GEMV: the row group (its arrival counter)
 };
 static_assert(sizeof(TaskRec) == 32, "TaskRec size");
 // TaskRec.flags: an attention task of the static schedule, fixed to
@@ -88,6 +89,8 @@ struct HostPlan {
     int jit_inline = 0;  // JIT expanded by the completing QKV arrival (no scheduler workgroups)
     int schedule = 0;  // 0 event runtime, 1 static (searched) schedule
     int prefill = 0;   // 1: the batch rows are consecutive positions of one sequence (prompt chunks)
+    int down_ks = 1;   // K parts of the down projection (1: whole K)
+    int down_groups = 0;  // row groups of a K-split down projection
     double predicted_layer_us = 0;  // static schedule: cost-model time of one layer
     int kv_chunk = 256;     // base keys per split (sizes the partial records)
     int kv_chunk_max = 4096; // largest per-step chunk

@@ -272,6 +272,20 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
         p.attn_target = kAttnSplitTarget;
     }
     if (p.max_splits > 65535) return fail(err, "too many splits per sequence");
+    {
+        // K split of the down projection on the matrix-core path
+        const bool mf_path = d.weight_dtype == MK_BF16 && d.batch >= 3;
+        int ks = o.down_ksplit;
+        if (ks != 0 && ks != 1 && ks != 2 && ks != 4) return fail(err, "opts.down_ksplit must be 0, 1, 2 or 4");
+        if (ks == 0) {
+            ks = (mf_path && o.schedule == 0 && d.ffn % 256 == 0) ? 4 : 1;
+        } else if (ks > 1) {
+            if (!mf_path) return fail(err, "opts.down_ksplit > 1 needs the matrix-core path (bf16 weights, batch >= 3)");
+            if (o.schedule == 1) return fail(err, "opts.down_ksplit > 1 is not available with the static schedule");
+            if (d.ffn % (64 * ks)) return fail(err, "opts.down_ksplit: ffn must be a multiple of 64 * parts");
+        }
+        p.down_ks = ks;
+    }
     StaticChoice sc;
     if (p.schedule == 1) {
         // the split length is fixed for every step: chunk = chunk_max = the searched C
@@ -347,6 +361,40 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
         // tiled weights: tasks own whole 8-row units of the tiled layout
         const int64_t unit = (tiled && op != OP_EMBED && op != OP_APPEND) ? 8 : 1;
         const int64_t units = rows / unit;
+        if (op == OP_DOWN && p.down_ks > 1) {
+            // K split: row groups of about ks 16-row tiles, each group's K
+            // cut into ks parts, one task per part on consecutive workers;
+            // the last part to arrive merges and signals, so the event counts
+            // groups
+            const int ks = p.down_ks;
+            const int64_t groups = std::min<int64_t>(std::max(1, W / ks), units);
+            add_level(op, layer);
+            for (int64_t g = 0; g < groups; ++g) {
+                const int32_t a0 = (int32_t)(g * units / groups * unit), a1 = (int32_t)((g + 1) * units / groups * unit);
+                for (int kp = 0; kp < ks; ++kp) {
+                    TaskRec t{};
+                    t.op = (uint8_t)op;
+                    t.layer = (uint16_t)layer;
+                    t.a0 = a0;
+                    t.a1 = a1;
+                    t.kpart = kp | (ks << 8);
+                    t.kgroup = (int32_t)g;
+                    t.wait_ev = wait;
+                    t.sig_ev = sig;
+                    t.level = level;
+                    const int id = (int)p.tasks.size();
+                    p.tasks.push_back(t);
+                    p.level_tasks.push_back(id);
+                    q[(g * ks + kp + rot) % W].push_back(id);
+                    p.tasks_per_op[op]++;
+                }
+                if (sig >= 0) p.events[sig].required++;
+            }
+            p.down_groups = (int)groups;
+            rot = (int)((rot + groups * ks) % W);
+            level++;
+            return;
+        }
         int64_t nt = std::min<int64_t>(W, (units + min_rows - 1) / min_rows);
         add_level(op, layer);
         for (int64_t i = 0; i < nt; ++i) {
@@ -508,7 +556,8 @@ bool verify_plan(const HostPlan& p, std::string& err) {
     std::vector<int> prod_level(p.events.size(), -1);
     for (const TaskRec& t : p.tasks) {
         if (t.sig_ev >= (int)p.events.size() || t.wait_ev >= (int)p.events.size()) return fail(err, "event id range");
-        if (t.sig_ev >= 0 && t.op != OP_ATTN) {
+        // a K-split task group signals once (its merging part)
+        if (t.sig_ev >= 0 && t.op != OP_ATTN && (t.kpart & 0xFF) == 0) {
             prod[t.sig_ev]++;
             prod_level[t.sig_ev] = std::max(prod_level[t.sig_ev], t.level);
         }
@@ -532,11 +581,23 @@ bool verify_plan(const HostPlan& p, std::string& err) {
     for (int lv = 0; lv < p.n_levels; ++lv) {
         int op = p.level_op[lv];
         if (op == OP_ATTN) continue;
+        // every K part (0 .. ks - 1) covers the rows exactly once, in the
+        // same row groups
+        int ks = 1;
+        for (int i = p.level_off[lv]; i < p.level_off[lv + 1]; ++i) ks = std::max(ks, p.tasks[p.level_tasks[i]].kpart >> 8);
+        std::vector<std::vector<std::pair<int, int>>> parts(ks);
         std::vector<std::pair<int, int>> r;
         for (int i = p.level_off[lv]; i < p.level_off[lv + 1]; ++i) {
             const TaskRec& t = p.tasks[p.level_tasks[i]];
             if (t.op != op || t.level != lv) return fail(err, "level list mixes operators");
-            r.push_back({t.a0, t.a1});
+            const int kp = t.kpart & 0xFF, tks = t.kpart >> 8;
+            if (ks > 1 && (tks != ks || kp >= ks || t.kgroup < 0)) return fail(err, "K-split task with a bad part");
+            parts[kp].push_back({t.a0, t.a1});
+            if (kp == 0) r.push_back({t.a0, t.a1});
+        }
+        for (auto& v : parts) {
+            std::sort(v.begin(), v.end());
+            if (v != parts[0]) return fail(err, "K parts of a level cover different rows");
         }
         std::sort(r.begin(), r.end());
         int64_t at = 0;
@@ -580,6 +641,9 @@ struct DryState {
     std::vector<std::atomic<uint32_t>> ev;
     std::vector<std::atomic<uint32_t>> arrive;
     std::vector<std::atomic<uint64_t>> partial;  // [B*Hkv][max_splits]
+    // K-split levels: part values [rows][ks] and row-group arrivals, per level
+    std::vector<std::vector<std::atomic<uint64_t>>> kval;
+    std::vector<std::vector<std::atomic<uint32_t>>> karr;
     std::vector<RingSlot> jit;                     // [workers][inbox_cap]
     std::vector<std::atomic<int64_t>> jit_tag;     // [workers][inbox_cap]
     std::vector<std::atomic<int64_t>> jit_tail;    // per worker
@@ -621,11 +685,41 @@ int64_t level_rows(const HostPlan& p, int lv) {
     return op_rows(d, p.level_op[lv]);
 }
 
-void run_gemv(DryState& s, const TaskRec& t) {
+// value of K part kp of row r at level lv (a K-split row is the XOR of its parts)
+uint64_t kpart_value(uint64_t sum, int lv, int64_t r, int kp) {
+    return mix64(sum ^ ((uint64_t)lv << 40) ^ (uint64_t)r ^ ((uint64_t)(kp + 1) << 52));
+}
+
+// Returns whether the task signals its event: always, except the parts of a
+// K-split group other than the last to arrive, which merges the group.
+bool run_gemv(DryState& s, const TaskRec& t) {
     int in = input_level(s.p, t.level);
     uint64_t sum = in >= 0 ? level_input_sum(s, in) : 0x1234;
-    for (int r = t.a0; r < t.a1; ++r)
-        s.out[t.level][r].store(mix64(sum ^ ((uint64_t)t.level << 40) ^ (uint64_t)r), std::memory_order_release);
+    const int ks = t.kpart >> 8;
+    if (ks <= 1) {
+        for (int r = t.a0; r < t.a1; ++r)
+            s.out[t.level][r].store(mix64(sum ^ ((uint64_t)t.level << 40) ^ (uint64_t)r), std::memory_order_release);
+        return true;
+    }
+    const int kp = t.kpart & 0xFF;
+    auto& kv = s.kval[t.level];
+    for (int r = t.a0; r < t.a1; ++r) kv[(size_t)r * ks + kp].store(kpart_value(sum, t.level, r, kp), std::memory_order_release);
+    const uint32_t old = s.karr[t.level][t.kgroup].fetch_add(1, std::memory_order_acq_rel);
+    if ((int)old + 1 != ks) return false;
+    for (int r = t.a0; r < t.a1; ++r) {
+        uint64_t v = 0;
+        for (int q = 0; q < ks; ++q) v ^= kv[(size_t)r * ks + q].load(std::memory_order_acquire);
+        s.out[t.level][r].store(v, std::memory_order_release);
+    }
+    s.karr[t.level][t.kgroup].store(0, std::memory_order_relaxed);
+    return true;
+}
+
+// K parts of a level's tasks (1: whole K)
+int level_ks(const HostPlan& p, int lv) {
+    int ks = 1;
+    for (int i = p.level_off[lv]; i < p.level_off[lv + 1]; ++i) ks = std::max(ks, p.tasks[p.level_tasks[i]].kpart >> 8);
+    return ks;
 }
 
 // split task k of the step in (b, g, split) order, if the step has one
@@ -686,6 +780,16 @@ bool dry_run(const HostPlan& p, int n_threads, uint64_t seed, int drop_task, int
     s.arrive = std::vector<std::atomic<uint32_t>>(d.batch * d.n_kv_heads);
     for (auto& a : s.arrive) a.store(0);
     s.partial = std::vector<std::atomic<uint64_t>>((size_t)d.batch * d.n_kv_heads * p.max_splits);
+    s.kval = std::vector<std::vector<std::atomic<uint64_t>>>(p.n_levels);
+    s.karr = std::vector<std::vector<std::atomic<uint32_t>>>(p.n_levels);
+    for (int lv = 0; lv < p.n_levels; ++lv) {
+        const int ks = p.level_op[lv] == OP_ATTN ? 1 : level_ks(p, lv);
+        if (ks <= 1) continue;
+        s.kval[lv] = std::vector<std::atomic<uint64_t>>((size_t)level_rows(p, lv) * ks);
+        for (auto& v : s.kval[lv]) v.store(0);
+        s.karr[lv] = std::vector<std::atomic<uint32_t>>((size_t)p.workers);
+        for (auto& v : s.karr[lv]) v.store(0);
+    }
     s.jit.resize((size_t)p.workers * p.inbox_cap);
     s.jit_tag = std::vector<std::atomic<int64_t>>((size_t)p.workers * p.inbox_cap);
     for (auto& t : s.jit_tag) t.store(0);
@@ -820,9 +924,9 @@ bool dry_run(const HostPlan& p, int n_threads, uint64_t seed, int drop_task, int
                         if (located && run_attn(s, t.layer, bg, sp, t.level)) signal(t.sig_ev);
                         continue;
                     }
-                    run_gemv(s, t);
+                    const bool sg = run_gemv(s, t);
                     if ((int)(&t - p.tasks.data()) == s.drop) continue;  // injected fault: never signals
-                    signal(t.sig_ev);
+                    if (sg) signal(t.sig_ev);
                 }
                 if (!progressed) {
                     bool ran = false;
@@ -861,6 +965,13 @@ bool dry_run(const HostPlan& p, int n_threads, uint64_t seed, int drop_task, int
                 uint64_t c = 0;
                 for (int i = 0; i < ns; ++i) c = mix64(c ^ mix64(sum ^ ((uint64_t)bg << 20) ^ (uint64_t)i));
                 ref[lv][bg] = c;
+            }
+        } else if (level_ks(p, lv) > 1) {
+            const int ks = level_ks(p, lv);
+            for (int64_t r = 0; r < (int64_t)ref[lv].size(); ++r) {
+                uint64_t v = 0;
+                for (int q = 0; q < ks; ++q) v ^= kpart_value(sum, lv, r, q);
+                ref[lv][r] = v;
             }
         } else {
             for (int64_t r = 0; r < (int64_t)ref[lv].size(); ++r) ref[lv][r] = mix64(sum ^ ((uint64_t)lv << 40) ^ (uint64_t)r);

@@ -172,6 +172,8 @@ struct mk_plan {
     EventRec* d_evrec = nullptr;
     uint32_t* d_ev = nullptr;
     uint32_t* d_arrive = nullptr;
+    float* d_kpart = nullptr;       // K-split down projection: partial tiles
+    uint32_t* d_karrive = nullptr;  // K-split down projection: row-group arrivals
     unsigned long long* d_amax = nullptr;  // greedy step: per-sequence argmax keys
     uint32_t* d_lm_done = nullptr;         // greedy step: LM tasks finished (kernel-per-op)
     uint32_t* d_exit_cnt = nullptr;        // greedy step: workers done (persistent)
@@ -293,6 +295,8 @@ bool upload_plan(mk_plan* pl) {
     // zero-initialised control area: events, arrivals, rings, ctrl
     Region r_ev = take(sizeof(uint32_t) * (size_t)ev_plane_stride((int)hp.events.size()) * kEvPlanesMax);
     Region r_arr = take(sizeof(uint32_t) * (size_t)B * Hkv);
+    Region r_karr = take(sizeof(uint32_t) * (size_t)std::max(1, hp.down_groups));
+    Region r_kpart = take(hp.down_ks > 1 ? sizeof(float) * (size_t)H * hp.down_ks * 16 : 0);
     Region r_amax = take(sizeof(unsigned long long) * (size_t)B);
     Region r_lmd = take(sizeof(uint32_t));
     Region r_exit = take(sizeof(uint32_t));
@@ -330,6 +334,8 @@ bool upload_plan(mk_plan* pl) {
     pl->d_evrec = (EventRec*)(m + r_evrec.off);
     pl->d_ev = (uint32_t*)(m + r_ev.off);
     pl->d_arrive = (uint32_t*)(m + r_arr.off);
+    pl->d_karrive = (uint32_t*)(m + r_karr.off);
+    pl->d_kpart = hp.down_ks > 1 ? (float*)(m + r_kpart.off) : nullptr;
     pl->d_amax = (unsigned long long*)(m + r_amax.off);
     pl->d_lm_done = (uint32_t*)(m + r_lmd.off);
     pl->d_exit_cnt = (uint32_t*)(m + r_exit.off);
@@ -429,6 +435,8 @@ KParams make_params(const mk_plan* pl, const mk_weights* w, const mk_kv_cache* k
     p.ev = pl->d_ev;
     p.ev_stride = ev_plane_stride((int)hp.events.size());
     p.arrive = pl->d_arrive;
+    p.kpart = pl->d_kpart;
+    p.karrive = pl->d_karrive;
     p.amax = pl->d_amax;
     p.lm_done = pl->d_lm_done;
     p.exit_cnt = pl->d_exit_cnt;

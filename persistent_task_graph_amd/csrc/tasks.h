@@ -743,13 +743,17 @@ __device__ __forceinline__ mk_f32x4 mfma_bf16(const uint4& a, const mk_bf16x8& b
 // the whole load two 512-byte runs; the operands, and so the bits, are the
 // row-major path's.
 template <int NB, bool DUAL, int TMAX, int NSEG, typename OutFn, int NST = 2, bool W4M = false, bool TL = false>
+// kofs, kfull (K split): the K columns run from kofs, in rows of kfull
+// columns (0: K); x points at column kofs of its rows.
 __device__ __forceinline__ void gemv_mfma(const MSeg (&seg)[NSEG], int K, const float* x, int ldx, int B,
-                                          const bf16_t* gain, float eps, OutFn out, const Lds& s, bool tr) {
+                                          const bf16_t* gain, float eps, OutFn out, const Lds& s, bool tr,
+                                          int kofs = 0, int kfull = 0) {
     constexpr int NM = DUAL ? 2 : 1;
     static_assert(kWaves * TMAX * NM * 256 <= kPartFloats, "partial tiles exceed the LDS window");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lk = lane >> 4;
-    const uint32_t rowbytes = W4M ? (uint32_t)K / 2u : (uint32_t)K * 2u;  // bytes per weight row (codes for W4)
+    const int krow = kfull > 0 ? kfull : K;  // columns per weight row
+    const uint32_t rowbytes = W4M ? (uint32_t)krow / 2u : (uint32_t)krow * 2u;  // bytes per weight row (codes for W4)
     const uint32_t srow = (uint32_t)(K / kW4Group) * 2u;                  // W4: scale bytes per row
     const int ngroups = K / kW4Group;
     float* scs = s.part + kPartFloats;  // W4: [TMAX][NM][16 rows][ngroups] scales of the pass
@@ -842,13 +846,13 @@ __device__ __forceinline__ void gemv_mfma(const MSeg (&seg)[NSEG], int K, const 
                         if constexpr (DUAL) st.q[t][1][c] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(tb[t], vo, tsoff[t], kStreamAux);
                     } else if constexpr (TL) {
                         const uint32_t vo = (kok && li < tval[t])
-                                                ? (uint32_t)(li >> 3) * 8u * rowbytes + (uint32_t)(k >> 5) * 512u +
+                                                ? (uint32_t)(li >> 3) * 8u * rowbytes + (uint32_t)((kofs + k) >> 5) * 512u +
                                                       (uint32_t)((lk << 3) | (li & 7)) * 16u
                                                 : kOOB;
                         st.w[t][0][c] = buf_load16_wt(ta[t], vo, tsoff[t]);
                         if constexpr (DUAL) st.w[t][1][c] = buf_load16_wt(tb[t], vo, tsoff[t]);
                     } else {
-                        const uint32_t vo = (kok && li < tval[t]) ? (uint32_t)li * rowbytes + (uint32_t)k * 2u : kOOB;
+                        const uint32_t vo = (kok && li < tval[t]) ? (uint32_t)li * rowbytes + (uint32_t)(kofs + k) * 2u : kOOB;
                         st.w[t][0][c] = buf_load16_w(ta[t], vo, tsoff[t]);
                         if constexpr (DUAL) st.w[t][1][c] = buf_load16_w(tb[t], vo, tsoff[t]);
                     }
@@ -1304,6 +1308,14 @@ __device__ __forceinline__ void run_w4_mfma_task(const KParams& p, const TaskRec
 // w: the task's layer pointers, p.lw[t.layer] (the worker reads them before
 // the task's event fires). pre_rows: leading rows of the task whose weights
 // were preloaded into this worker's LDS slots (batch <= 2 only; 0 otherwise).
+// Pipeline stages of the matrix-core GEMV with tiled weights: QKV and
+// gate/up (several tiles per pass), O and down (one tile per pass).
+#ifndef MK_TILED_NST_QG
+#define MK_TILED_NST_QG 2
+#endif
+#ifndef MK_TILED_NST_OD
+#define MK_TILED_NST_OD 3
+#endif
 // Runs f(std::true_type) for a plan with tiled weights, else
 // f(std::false_type). The W4 instances never see tiled weights (plans reject
 // the combination), so they compile the row-major path only.
@@ -1318,8 +1330,75 @@ __device__ __forceinline__ void mfma_dispatch(const KParams& p, F f) {
     f(std::false_type{});
 }
 
+// One K part of a K-split down projection (matrix-core path): rows
+// [a0, a1) over columns [kp F / ks, (kp + 1) F / ks) of h, into the row
+// group's partial tile; the last part of the group to arrive adds the ks
+// partials in part order, adds the residual and stores the rows (the
+// combine rule of the split attention: a fixed order, whatever the arrival
+// order). Returns whether this task signals the event (the merging part
+// only). Partial layout: group at p.kpart + a0 * ks * 16, part kp at
+// kp * (a1 - a0) * 16, row i at i * 16, one float per sequence.
+template <int NB>
+__device__ __forceinline__ bool run_down_ksplit(const KParams& p, const TaskRec& t, const Lds& s, const LayerPtrs& w) {
+    const int kp = t.kpart & 0xFF, ks = t.kpart >> 8;
+    const int l = t.layer, B = p.B, H = p.H, F = p.F, r0 = t.a0, r1 = t.a1, nr = r1 - r0;
+    const int kw = F / ks, k0 = kp * kw;
+    float* part = p.kpart + (int64_t)r0 * ks * 16;
+    const MatTile<bf16_t> td((const bf16_t*)w.w_down, F, H, r0, r1);
+    auto out = [&](int r, int b, float v, float) { st_co(&part[((int64_t)kp * nr + (r - r0)) * 16 + b], v); };
+    const MSeg sg[1] = {{td.r, td.r, td.n, td.lo}};
+    const float* h = layer_buf(p, l, p.off_h) + k0;
+    mfma_dispatch(p, [&](auto tl) {
+        gemv_mfma<NB, false, 4, 1, decltype(out), 2, false, decltype(tl)::value>(
+            sg, kw, h, F, B, (const bf16_t*)nullptr, p.eps, out, s, p.trace != nullptr, k0, F);
+    });
+    // arrival on the group's counter once this part's stores are complete
+    wait_stores();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(&p.karrive[t.kgroup], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s.cmd[9] = (old + 1u == (uint32_t)ks) ? 1 : 0;
+    }
+    __syncthreads();
+    const bool last = s.cmd[9] != 0;
+    __syncthreads();
+    if (!last) return false;
+    // merge: each thread takes 4 sequences of one row, all parts' loads in
+    // flight together
+    const float* xm = layer_buf(p, l, p.off_xmid);
+    float* o = layer_out(p, l);
+    const __amdgpu_buffer_rsrc_t prs = make_rsrc(part, (uint32_t)(ks * nr * 16) * 4u);
+    for (int e = threadIdx.x; e < nr * 4; e += kThreads) {
+        const int i = e >> 2, b0 = (e & 3) * 4;
+        if (b0 >= B) continue;
+        uint4 v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            v[q] = buf_load16_co(prs, q < ks ? (uint32_t)(((q * nr + i) * 16 + b0) * 4) : kOOB, 0);
+        float acc[4] = {__uint_as_float(v[0].x), __uint_as_float(v[0].y), __uint_as_float(v[0].z), __uint_as_float(v[0].w)};
+#pragma unroll
+        for (int q = 1; q < 4; ++q) {
+            if (q >= ks) continue;
+            acc[0] += __uint_as_float(v[q].x);
+            acc[1] += __uint_as_float(v[q].y);
+            acc[2] += __uint_as_float(v[q].z);
+            acc[3] += __uint_as_float(v[q].w);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (b0 + j >= B) continue;
+            const int64_t idx = (int64_t)(b0 + j) * H + r0 + i;
+            st_co(&o[idx], ld_act(&xm[idx]) + acc[j]);
+        }
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(&p.karrive[t.kgroup], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+}
+
+// Returns whether the task signals its event (false only for the parts of a
+// K-split group that do not merge it).
 template <typename WT, int NB>
-__device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t, const Lds& s, const LayerPtrs& w,
+__device__ __forceinline__ bool run_gemv_task(const KParams& p, const TaskRec& t, const Lds& s, const LayerPtrs& w,
                                               int pre_rows = 0) {
     // 4-bit layer matrices: VALU GEMV at batch <= 2 (in the bf16 instances),
     // matrix cores above (in instances of their own: in the bf16 batch >= 4
@@ -1328,7 +1407,7 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
         if (p.w4 && t.op != OP_LM && t.op != OP_EMBED && t.op != OP_APPEND) {
             if constexpr (NB <= 2) run_w4_task<NB>(p, t, s, w);
             else run_w4_mfma_task<NB>(p, t, s, w);
-            return;
+            return true;
         }
     }
     // bf16 weights with more than two sequences run on the matrix cores
@@ -1358,7 +1437,8 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
             if constexpr (kMfma) {
                 const MSeg sg[3] = {{tq.r, tq.r, tq.n, tq.lo}, {tk.r, tk.r, tk.n, QD + tk.lo}, {tv.r, tv.r, tv.n, QD + KD + tv.lo}};
                 mfma_dispatch(p, [&](auto tl) {
-                    gemv_mfma<NB, false, 2, 3, decltype(out), 2, false, decltype(tl)::value>(
+                    gemv_mfma<NB, false, 2, 3, decltype(out), decltype(tl)::value ? MK_TILED_NST_QG : 2, false,
+                              decltype(tl)::value>(
                         sg, H, x, H, B, (const bf16_t*)w.attn_norm, p.eps, out, s, p.trace != nullptr);
                 });
             } else {
@@ -1380,7 +1460,8 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
             if constexpr (kMfma) {
                 const MSeg sg[1] = {{to.r, to.r, to.n, to.lo}};
                 mfma_dispatch(p, [&](auto tl) {
-                    gemv_mfma<NB, false, 1, 1, decltype(out), 3, false, decltype(tl)::value>(
+                    gemv_mfma<NB, false, 1, 1, decltype(out), decltype(tl)::value ? MK_TILED_NST_OD : 3, false,
+                              decltype(tl)::value>(
                         sg, K, a, K, B, (const bf16_t*)nullptr, p.eps, out, s, p.trace != nullptr);
                 });
             } else {
@@ -1406,7 +1487,8 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
             if constexpr (kMfma) {
                 const MSeg sg[1] = {{tg.r, tu.r, tg.n, tg.lo}};
                 mfma_dispatch(p, [&](auto tl) {
-                    gemv_mfma<NB, true, 3, 1, decltype(out), 2, false, decltype(tl)::value>(
+                    gemv_mfma<NB, true, 3, 1, decltype(out), decltype(tl)::value ? MK_TILED_NST_QG : 2, false,
+                              decltype(tl)::value>(
                         sg, H, x, H, B, (const bf16_t*)w.mlp_norm, p.eps, out, s, p.trace != nullptr);
                 });
             } else {
@@ -1415,6 +1497,12 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
             break;
         }
         case OP_DOWN: {
+            if constexpr (kMfma && !kW4MfmaKernels)
+                if (t.kpart >> 8 > 1) {
+                    const bool sig = run_down_ksplit<NB>(p, t, s, w);
+                    trace_mark(p, s.marks, 2);
+                    return sig;
+                }
             const float* h = layer_buf(p, l, p.off_h);
             const float* xm = layer_buf(p, l, p.off_xmid);
             float* o = layer_out(p, l);
@@ -1428,7 +1516,8 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
             if constexpr (kMfma) {
                 const MSeg sg[1] = {{td.r, td.r, td.n, td.lo}};
                 mfma_dispatch(p, [&](auto tl) {
-                    gemv_mfma<NB, false, 1, 1, decltype(out), 3, false, decltype(tl)::value>(
+                    gemv_mfma<NB, false, 1, 1, decltype(out), decltype(tl)::value ? MK_TILED_NST_OD : 3, false,
+                              decltype(tl)::value>(
                         sg, F, h, F, B, (const bf16_t*)nullptr, p.eps, out, s, p.trace != nullptr);
                 });
             } else {
@@ -1458,6 +1547,7 @@ __device__ __forceinline__ void run_gemv_task(const KParams& p, const TaskRec& t
         default: break;
     }
     trace_mark(p, s.marks, 2);
+    return true;
 }
 
 // ---------------------------------------------------------------- signalling
@@ -1728,6 +1818,7 @@ struct Prefetch {
     __amdgpu_buffer_rsrc_t a, b;  // one or two weight segments (gate and up interleave)
     uint32_t kb_a, kb_b;          // segment sizes in KB (rounded up)
     uint32_t next, end;           // next KB index to issue, total KB to issue
+    uint32_t chunk_kb, stride;    // strided segment a (K-split tasks): chunks of chunk_kb KB, stride bytes apart; 0: contiguous
 };
 
 __device__ __forceinline__ void prefetch_segment(const void* m, int K, int es, int rows, int r0, int r1,
@@ -1746,8 +1837,35 @@ __device__ __forceinline__ Prefetch prefetch_setup(const KParams& p, const TaskR
     Prefetch f;
     f.kb_a = f.kb_b = 0;
     f.next = f.end = 0;
+    f.chunk_kb = f.stride = 0;
     f.a = f.b = make_rsrc(p.zero, 0);
     if (p.prefetch_kb <= 0) return f;
+    if (t.op == OP_DOWN && (t.kpart >> 8) > 1) {
+        // a K part of the down projection reads columns [k0, k0 + kw) of its
+        // rows: per row kw * 2 bytes, F * 2 apart (row-major), or per 8-row
+        // unit kw * 16 bytes, 16 F apart (tiled); whole KB chunks only
+        const int ks = t.kpart >> 8, kp = t.kpart & 0xFF, F = p.F;
+        const int kw = F / ks, k0 = kp * kw, nr = t.a1 - t.a0;
+        const char* m = (const char*)p.lw[t.layer].w_down;
+        uint32_t chunk, n;
+        if (p.wtiled) {
+            m += (int64_t)t.a0 * F * 2 + (int64_t)(k0 / 32) * 512;
+            chunk = (uint32_t)kw * 16u;
+            f.stride = (uint32_t)F * 16u;
+            n = (uint32_t)(nr / 8);
+        } else {
+            m += ((int64_t)t.a0 * F + k0) * 2;
+            chunk = (uint32_t)kw * 2u;
+            f.stride = (uint32_t)F * 2u;
+            n = (uint32_t)nr;
+        }
+        if (chunk % 1024u || n == 0) return f;
+        f.chunk_kb = chunk / 1024u;
+        f.a = make_rsrc(m, (n - 1) * f.stride + chunk);
+        f.kb_a = n * f.chunk_kb;
+        f.end = min(f.kb_a, (uint32_t)p.prefetch_kb);
+        return f;
+    }
     // a W4 layer matrix streams K / 2 bytes of codes per row (its scales,
     // 1/64 of that, are not prefetched): the same cursor with halved K
     const bool w4m = p.w4 && t.op != OP_LM && t.op != OP_EMBED;
@@ -1790,6 +1908,7 @@ __device__ __forceinline__ Prefetch attn_prefetch_setup(const KParams& p, int l,
     Prefetch f;
     f.kb_a = f.kb_b = 0;
     f.next = f.end = 0;
+    f.chunk_kb = f.stride = 0;
     f.a = f.b = make_rsrc(p.zero, 0);
     // prefill: rows of this launch's chunk are stored by the append level,
     // so nothing before the event may pull their lines into a cache
@@ -1819,7 +1938,10 @@ __device__ __forceinline__ void prefetch_step(Prefetch& f) {
     for (int k = 0; k < kPrefetchSlice; ++k) {
         const uint32_t i = f.next + (uint32_t)(k * kWaves + wave);
         if (i >= f.end) break;
-        if (f.kb_b == 0) {
+        if (f.chunk_kb) {
+            const uint32_t o = (i / f.chunk_kb) * f.stride + (i % f.chunk_kb) * 1024u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(f.a, sink, 16, lane * 16, o, 0, kPfAux);
+        } else if (f.kb_b == 0) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(f.a, sink, 16, lane * 16, i * 1024u, 0, kPfAux);
         } else {
             const uint32_t o = (i >> 1) * 1024u;

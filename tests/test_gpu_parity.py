@@ -712,3 +712,46 @@ def test_prefill_tiled_weights_bitwise(mid_weights):
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
     for x, y in zip(kv_a.read_sequence(0, 65), kv_b.read_sequence(0, 65)):
         assert np.array_equal(x, y)
+
+
+# ---------------------------------------------------------------- K-split down projection
+
+@pytest.mark.parametrize("ks", [1, 2, 4])
+def test_mid_down_ksplit_matches_oracle(mid_weights_g, ks):
+    # the down projection with its K cut into 1, 2 or 4 parts merged by the
+    # last arrival, against the oracle (seeded gains), batch 16, ragged
+    # lengths; a part that merged the wrong partials, or too few, fails here
+    B = 16
+    lens = [int(v) for v in np.linspace(2, 610, B)]
+    log("mid bf16: down K split %d, B=16" % ks)
+    s = make_setup(MID, B, lens, 620, weights=mid_weights_g)
+    plan = plan_for(s, down_ksplit=ks)
+    kv = device_kv(s)
+    out, err = run_gpu(s, plan, kv, _tokens(MID, B, 31), 2)
+    assert err == 0
+    rows = [0, 6, 15]
+    orc, _ = run_oracle(s, out, rows=rows)
+    worst, agree = compare(out, orc, rows=rows)
+    log("  max|d|/std = %.3g, top-1 = %.3f" % (worst, agree))
+    assert worst <= 2e-2
+    assert agree >= 0.99
+    plan.close()
+
+
+@pytest.mark.parametrize("ks,B,paged", [(2, 16, False), (4, 3, False), (4, 8, True)])
+def test_mid_down_ksplit_modes_bitwise(mid_weights, ks, B, paged):
+    # one plan's K split gives the same bits in every execution mode
+    lens = [int(v) for v in np.linspace(7, 640, B)]
+    log("mid bf16: down K split %d, B=%d paged=%s: persistent vs kernel-per-op vs JIT" % (ks, B, paged))
+    cap = max(lens) + 8
+    table = synth.block_table([cap] * B, 16) if paged else None
+    s = make_setup(MID, B, lens, cap, weights=mid_weights, paged=paged, table=table)
+    t0 = _tokens(MID, B, 33)
+    a, _ = _logits_seq(s, 3, tokens=t0, down_ksplit=ks)
+    b, _ = _logits_seq(s, 3, tokens=t0, down_ksplit=ks, mode=1)
+    c, _ = _logits_seq(s, 3, tokens=t0, down_ksplit=ks, jit=1)
+    others = [b, c]
+    if B >= 5:
+        others.append(_logits_seq(s, 3, tokens=t0, down_ksplit=ks, jit=3)[0])
+    for o in others:
+        _bitwise(a, o)
