@@ -90,7 +90,8 @@ struct HostPlan {
     int schedule = 0;  // 0 event runtime, 1 static (searched) schedule
     int prefill = 0;   // 1: the batch rows are consecutive positions of one sequence (prompt chunks)
     int down_ks = 1;   // K parts of the down projection (1: whole K)
-    int down_groups = 0;  // row groups of a K-split down projection
+    int o_ks = 1;      // K parts of the O projection
+    int ksplit_groups = 0;  // most row groups of a K-split level (arrival counters)
     double predicted_layer_us = 0;  // static schedule: cost-model time of one layer
     int kv_chunk = 256;     // base keys per split (sizes the partial records)
     int kv_chunk_max = 4096; // largest per-step chunk

@@ -273,18 +273,24 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
     }
     if (p.max_splits > 65535) return fail(err, "too many splits per sequence");
     {
-        // K split of the down projection on the matrix-core path
+        // K split of the O and down projections on the matrix-core path
         const bool mf_path = d.weight_dtype == MK_BF16 && d.batch >= 3;
-        int ks = o.down_ksplit;
-        if (ks != 0 && ks != 1 && ks != 2 && ks != 4) return fail(err, "opts.down_ksplit must be 0, 1, 2 or 4");
-        if (ks == 0) {
-            ks = (mf_path && o.schedule == 0 && d.ffn % 256 == 0) ? 4 : 1;
-        } else if (ks > 1) {
-            if (!mf_path) return fail(err, "opts.down_ksplit > 1 needs the matrix-core path (bf16 weights, batch >= 3)");
-            if (o.schedule == 1) return fail(err, "opts.down_ksplit > 1 is not available with the static schedule");
-            if (d.ffn % (64 * ks)) return fail(err, "opts.down_ksplit: ffn must be a multiple of 64 * parts");
-        }
-        p.down_ks = ks;
+        // default: 4 parts for down, none for O (measured no faster split)
+        auto pick = [&](int ks, int64_t K, const char* name, int auto_parts, int& outk) {
+            const std::string n(name);
+            if (ks != 0 && ks != 1 && ks != 2 && ks != 4) return fail(err, "opts." + n + " must be 0, 1, 2 or 4");
+            if (ks == 0) {
+                ks = (mf_path && o.schedule == 0 && K % (64 * auto_parts) == 0) ? auto_parts : 1;
+            } else if (ks > 1) {
+                if (!mf_path) return fail(err, "opts." + n + " > 1 needs the matrix-core path (bf16 weights, batch >= 3)");
+                if (o.schedule == 1) return fail(err, "opts." + n + " > 1 is not available with the static schedule");
+                if (K % (64 * ks)) return fail(err, "opts." + n + ": K must be a multiple of 64 * parts");
+            }
+            outk = ks;
+            return true;
+        };
+        if (!pick(o.down_ksplit, d.ffn, "down_ksplit", 4, p.down_ks)) return false;
+        if (!pick(o.o_ksplit, (int64_t)d.n_heads * d.head_dim, "o_ksplit", 1, p.o_ks)) return false;
     }
     StaticChoice sc;
     if (p.schedule == 1) {
@@ -361,12 +367,12 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
         // tiled weights: tasks own whole 8-row units of the tiled layout
         const int64_t unit = (tiled && op != OP_EMBED && op != OP_APPEND) ? 8 : 1;
         const int64_t units = rows / unit;
-        if (op == OP_DOWN && p.down_ks > 1) {
+        if ((op == OP_DOWN && p.down_ks > 1) || (op == OP_O && p.o_ks > 1)) {
             // K split: row groups of about ks 16-row tiles, each group's K
             // cut into ks parts, one task per part on consecutive workers;
             // the last part to arrive merges and signals, so the event counts
             // groups
-            const int ks = p.down_ks;
+            const int ks = op == OP_DOWN ? p.down_ks : p.o_ks;
             const int64_t groups = std::min<int64_t>(std::max(1, W / ks), units);
             add_level(op, layer);
             for (int64_t g = 0; g < groups; ++g) {
@@ -390,7 +396,7 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
                 }
                 if (sig >= 0) p.events[sig].required++;
             }
-            p.down_groups = (int)groups;
+            p.ksplit_groups = std::max(p.ksplit_groups, (int)groups);
             rot = (int)((rot + groups * ks) % W);
             level++;
             return;

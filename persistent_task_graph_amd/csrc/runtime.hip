@@ -295,8 +295,12 @@ bool upload_plan(mk_plan* pl) {
     // zero-initialised control area: events, arrivals, rings, ctrl
     Region r_ev = take(sizeof(uint32_t) * (size_t)ev_plane_stride((int)hp.events.size()) * kEvPlanesMax);
     Region r_arr = take(sizeof(uint32_t) * (size_t)B * Hkv);
-    Region r_karr = take(sizeof(uint32_t) * (size_t)std::max(1, hp.down_groups));
-    Region r_kpart = take(hp.down_ks > 1 ? sizeof(float) * (size_t)H * hp.down_ks * 16 : 0);
+    // K-split levels (O, down: hidden rows each) share the partial tiles and
+    // counters: a level's merges all complete before its event fires, and the
+    // next split level waits (through the events) on that one
+    const int kmax = std::max(hp.down_ks, hp.o_ks);
+    Region r_karr = take(sizeof(uint32_t) * (size_t)std::max(1, hp.ksplit_groups));
+    Region r_kpart = take(kmax > 1 ? sizeof(float) * (size_t)H * kmax * 16 : 0);
     Region r_amax = take(sizeof(unsigned long long) * (size_t)B);
     Region r_lmd = take(sizeof(uint32_t));
     Region r_exit = take(sizeof(uint32_t));
@@ -335,7 +339,7 @@ bool upload_plan(mk_plan* pl) {
     pl->d_ev = (uint32_t*)(m + r_ev.off);
     pl->d_arrive = (uint32_t*)(m + r_arr.off);
     pl->d_karrive = (uint32_t*)(m + r_karr.off);
-    pl->d_kpart = hp.down_ks > 1 ? (float*)(m + r_kpart.off) : nullptr;
+    pl->d_kpart = kmax > 1 ? (float*)(m + r_kpart.off) : nullptr;
     pl->d_amax = (unsigned long long*)(m + r_amax.off);
     pl->d_lm_done = (uint32_t*)(m + r_lmd.off);
     pl->d_exit_cnt = (uint32_t*)(m + r_exit.off);

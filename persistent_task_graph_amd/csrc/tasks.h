@@ -1330,27 +1330,29 @@ __device__ __forceinline__ void mfma_dispatch(const KParams& p, F f) {
     f(std::false_type{});
 }
 
-// One K part of a K-split down projection (matrix-core path): rows
-// [a0, a1) over columns [kp F / ks, (kp + 1) F / ks) of h, into the row
-// group's partial tile; the last part of the group to arrive adds the ks
+// One K part of a K-split O or down projection (matrix-core path): rows
+// [a0, a1) over columns [kp K / ks, (kp + 1) K / ks) of the input, into the
+// row group's partial tile; the last part of the group to arrive adds the ks
 // partials in part order, adds the residual and stores the rows (the
 // combine rule of the split attention: a fixed order, whatever the arrival
 // order). Returns whether this task signals the event (the merging part
 // only). Partial layout: group at p.kpart + a0 * ks * 16, part kp at
 // kp * (a1 - a0) * 16, row i at i * 16, one float per sequence.
 template <int NB>
-__device__ __forceinline__ bool run_down_ksplit(const KParams& p, const TaskRec& t, const Lds& s, const LayerPtrs& w) {
+__device__ __forceinline__ bool run_ksplit(const KParams& p, const TaskRec& t, const Lds& s, const LayerPtrs& w) {
     const int kp = t.kpart & 0xFF, ks = t.kpart >> 8;
-    const int l = t.layer, B = p.B, H = p.H, F = p.F, r0 = t.a0, r1 = t.a1, nr = r1 - r0;
-    const int kw = F / ks, k0 = kp * kw;
+    const int l = t.layer, B = p.B, H = p.H, r0 = t.a0, r1 = t.a1, nr = r1 - r0;
+    const bool down = t.op == OP_DOWN;
+    const int K = down ? p.F : p.QD;
+    const int kw = K / ks, k0 = kp * kw;
     float* part = p.kpart + (int64_t)r0 * ks * 16;
-    const MatTile<bf16_t> td((const bf16_t*)w.w_down, F, H, r0, r1);
+    const MatTile<bf16_t> td((const bf16_t*)(down ? w.w_down : w.wo), K, H, r0, r1);
     auto out = [&](int r, int b, float v, float) { st_co(&part[((int64_t)kp * nr + (r - r0)) * 16 + b], v); };
     const MSeg sg[1] = {{td.r, td.r, td.n, td.lo}};
-    const float* h = layer_buf(p, l, p.off_h) + k0;
+    const float* xin = layer_buf(p, l, down ? p.off_h : p.off_attn) + k0;
     mfma_dispatch(p, [&](auto tl) {
         gemv_mfma<NB, false, 4, 1, decltype(out), 2, false, decltype(tl)::value>(
-            sg, kw, h, F, B, (const bf16_t*)nullptr, p.eps, out, s, p.trace != nullptr, k0, F);
+            sg, kw, xin, K, B, (const bf16_t*)nullptr, p.eps, out, s, p.trace != nullptr, k0, K);
     });
     // arrival on the group's counter once this part's stores are complete
     wait_stores();
@@ -1365,8 +1367,9 @@ __device__ __forceinline__ bool run_down_ksplit(const KParams& p, const TaskRec&
     if (!last) return false;
     // merge: each thread takes 4 sequences of one row, all parts' loads in
     // flight together
-    const float* xm = layer_buf(p, l, p.off_xmid);
-    float* o = layer_out(p, l);
+    // residual: O adds to the layer input into x_mid, down to x_mid into the layer output
+    const float* xm = down ? layer_buf(p, l, p.off_xmid) : layer_in(p, l);
+    float* o = down ? layer_out(p, l) : layer_buf(p, l, p.off_xmid);
     const __amdgpu_buffer_rsrc_t prs = make_rsrc(part, (uint32_t)(ks * nr * 16) * 4u);
     for (int e = threadIdx.x; e < nr * 4; e += kThreads) {
         const int i = e >> 2, b0 = (e & 3) * 4;
@@ -1447,6 +1450,12 @@ __device__ __forceinline__ bool run_gemv_task(const KParams& p, const TaskRec& t
             break;
         }
         case OP_O: {
+            if constexpr (kMfma && !kW4MfmaKernels)
+                if (t.kpart >> 8 > 1) {
+                    const bool sig = run_ksplit<NB>(p, t, s, w);
+                    trace_mark(p, s.marks, 2);
+                    return sig;
+                }
             const float* a = layer_buf(p, l, p.off_attn);
             const float* xin = layer_in(p, l);
             float* o = layer_buf(p, l, p.off_xmid);
@@ -1499,7 +1508,7 @@ __device__ __forceinline__ bool run_gemv_task(const KParams& p, const TaskRec& t
         case OP_DOWN: {
             if constexpr (kMfma && !kW4MfmaKernels)
                 if (t.kpart >> 8 > 1) {
-                    const bool sig = run_down_ksplit<NB>(p, t, s, w);
+                    const bool sig = run_ksplit<NB>(p, t, s, w);
                     trace_mark(p, s.marks, 2);
                     return sig;
                 }
@@ -1840,13 +1849,14 @@ __device__ __forceinline__ Prefetch prefetch_setup(const KParams& p, const TaskR
     f.chunk_kb = f.stride = 0;
     f.a = f.b = make_rsrc(p.zero, 0);
     if (p.prefetch_kb <= 0) return f;
-    if (t.op == OP_DOWN && (t.kpart >> 8) > 1) {
-        // a K part of the down projection reads columns [k0, k0 + kw) of its
-        // rows: per row kw * 2 bytes, F * 2 apart (row-major), or per 8-row
-        // unit kw * 16 bytes, 16 F apart (tiled); whole KB chunks only
-        const int ks = t.kpart >> 8, kp = t.kpart & 0xFF, F = p.F;
+    if ((t.op == OP_DOWN || t.op == OP_O) && (t.kpart >> 8) > 1) {
+        // a K part of the O or down projection reads columns [k0, k0 + kw)
+        // of its rows: per row kw * 2 bytes, F * 2 apart (row-major), or per
+        // 8-row unit kw * 16 bytes, 16 F apart (tiled; F: the row length);
+        // whole KB chunks only
+        const int ks = t.kpart >> 8, kp = t.kpart & 0xFF, F = t.op == OP_DOWN ? p.F : p.QD;
         const int kw = F / ks, k0 = kp * kw, nr = t.a1 - t.a0;
-        const char* m = (const char*)p.lw[t.layer].w_down;
+        const char* m = (const char*)(t.op == OP_DOWN ? p.lw[t.layer].w_down : p.lw[t.layer].wo);
         uint32_t chunk, n;
         if (p.wtiled) {
             m += (int64_t)t.a0 * F * 2 + (int64_t)(k0 / 32) * 512;

@@ -35,7 +35,7 @@ class ExecOpts(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("mode", "workers", "sched_wgs", "jit", "kv_chunk", "watchdog_ms",
                                                "host_only", "device_cus", "debug_event", "debug_extra_required",
                                                "trace", "prefetch_kb", "lds_stream", "kv_chunk_max", "lds_preload",
-                                               "schedule", "prefill", "down_ksplit")]
+                                               "schedule", "prefill", "down_ksplit", "o_ksplit")]
 
 
 class ModelDesc(ctypes.Structure):

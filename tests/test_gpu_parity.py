@@ -716,16 +716,16 @@ def test_prefill_tiled_weights_bitwise(mid_weights):
 
 # ---------------------------------------------------------------- K-split down projection
 
-@pytest.mark.parametrize("ks", [1, 2, 4])
-def test_mid_down_ksplit_matches_oracle(mid_weights_g, ks):
-    # the down projection with its K cut into 1, 2 or 4 parts merged by the
-    # last arrival, against the oracle (seeded gains), batch 16, ragged
+@pytest.mark.parametrize("ks,oks", [(1, 1), (2, 2), (4, 4), (4, 1), (1, 4)])
+def test_mid_down_ksplit_matches_oracle(mid_weights_g, ks, oks):
+    # the down and O projections with their K cut into 1, 2 or 4 parts merged
+    # by the last arrival, against the oracle (seeded gains), batch 16, ragged
     # lengths; a part that merged the wrong partials, or too few, fails here
     B = 16
     lens = [int(v) for v in np.linspace(2, 610, B)]
-    log("mid bf16: down K split %d, B=16" % ks)
+    log("mid bf16: down K split %d, O K split %d, B=16" % (ks, oks))
     s = make_setup(MID, B, lens, 620, weights=mid_weights_g)
-    plan = plan_for(s, down_ksplit=ks)
+    plan = plan_for(s, down_ksplit=ks, o_ksplit=oks)
     kv = device_kv(s)
     out, err = run_gpu(s, plan, kv, _tokens(MID, B, 31), 2)
     assert err == 0
@@ -747,11 +747,11 @@ def test_mid_down_ksplit_modes_bitwise(mid_weights, ks, B, paged):
     table = synth.block_table([cap] * B, 16) if paged else None
     s = make_setup(MID, B, lens, cap, weights=mid_weights, paged=paged, table=table)
     t0 = _tokens(MID, B, 33)
-    a, _ = _logits_seq(s, 3, tokens=t0, down_ksplit=ks)
-    b, _ = _logits_seq(s, 3, tokens=t0, down_ksplit=ks, mode=1)
-    c, _ = _logits_seq(s, 3, tokens=t0, down_ksplit=ks, jit=1)
+    a, _ = _logits_seq(s, 3, tokens=t0, down_ksplit=ks, o_ksplit=ks)
+    b, _ = _logits_seq(s, 3, tokens=t0, down_ksplit=ks, o_ksplit=ks, mode=1)
+    c, _ = _logits_seq(s, 3, tokens=t0, down_ksplit=ks, o_ksplit=ks, jit=1)
     others = [b, c]
     if B >= 5:
-        others.append(_logits_seq(s, 3, tokens=t0, down_ksplit=ks, jit=3)[0])
+        others.append(_logits_seq(s, 3, tokens=t0, down_ksplit=ks, o_ksplit=ks, jit=3)[0])
     for o in others:
         _bitwise(a, o)

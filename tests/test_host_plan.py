@@ -334,10 +334,11 @@ def test_down_ksplit_plans_verify_and_dry_run(lib, ks, opts):
     # event counts one arrival per group (its merging part), and the host dry
     # run's merge equals the sequential evaluation
     B = 16
-    p = _plan(synth.Q8B, B, 4096, down_ksplit=ks, **opts)
+    p = _plan(synth.Q8B, B, 4096, down_ksplit=ks, o_ksplit=ks, **opts)
     p.verify()
     assert p.dry_run(n_threads=8, seed=3 + ks, seq_lens=[50 + 211 * b for b in range(B)]) == 0, mk.last_error()
-    assert p.info().tasks_per_op[mk.OP_DOWN] == 256 * synth.Q8B.n_layers  # per layer: groups x parts = workers
+    for op in (mk.OP_DOWN, mk.OP_O):
+        assert p.info().tasks_per_op[op] == 256 * synth.Q8B.n_layers  # per layer: groups x parts = workers
 
 
 @pytest.mark.parametrize("case, msg", [
@@ -345,6 +346,8 @@ def test_down_ksplit_plans_verify_and_dry_run(lib, ks, opts):
     (dict(batch=16, down_ksplit=3), "down_ksplit must be"),
     (dict(batch=16, down_ksplit=4, schedule=1), "static schedule"),
     (dict(batch=16, down_ksplit=4, shape=replace(synth.Q8B, ffn=12352)), "multiple of 64 * parts"),
+    (dict(batch=2, o_ksplit=2), "matrix-core path"),
+    (dict(batch=16, o_ksplit=4, schedule=1), "static schedule"),
 ])
 def test_down_ksplit_rejected(lib, case, msg):
     shape = case.pop("shape", synth.Q8B)
