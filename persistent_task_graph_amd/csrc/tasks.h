@@ -1849,6 +1849,10 @@ __device__ __forceinline__ Prefetch prefetch_setup(const KParams& p, const TaskR
     f.chunk_kb = f.stride = 0;
     f.a = f.b = make_rsrc(p.zero, 0);
     if (p.prefetch_kb <= 0) return f;
+#if defined(MK_NB) && MK_NB >= 4
+    // K-split tasks exist on the matrix-core path only: the branch is left out
+    // of the batch <= 2 instances (there it measured 1% slower at batch 1 even
+    // though it never ran: it changes their register allocation)
     if ((t.op == OP_DOWN || t.op == OP_O) && (t.kpart >> 8) > 1) {
         // a K part of the O or down projection reads columns [k0, k0 + kw)
         // of its rows: per row kw * 2 bytes, F * 2 apart (row-major), or per
@@ -1876,6 +1880,7 @@ __device__ __forceinline__ Prefetch prefetch_setup(const KParams& p, const TaskR
         f.end = min(f.kb_a, (uint32_t)p.prefetch_kb);
         return f;
     }
+#endif
     // a W4 layer matrix streams K / 2 bytes of codes per row (its scales,
     // 1/64 of that, are not prefetched): the same cursor with halved K
     const bool w4m = p.w4 && t.op != OP_LM && t.op != OP_EMBED;

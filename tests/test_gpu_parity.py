@@ -430,7 +430,8 @@ def test_multi_step_launch_equals_repeated_greedy_steps(tiny, mid_weights, case)
 @pytest.mark.parametrize("B,paged", [(1, False), (4, False), (16, False), (4, True)])
 def test_static_schedule_equals_event_runtime(mid_weights, B, paged):
     # the static (searched) schedule runs the event runtime's task bodies: at
-    # the same attention split length the logits are the same bits
+    # the same attention split length, and with whole-K down-projection tasks
+    # as the static schedule has them, the logits are the same bits
     from persistent_task_graph_amd import harness
 
     lens = [int(v) for v in np.linspace(5, 900, B)]
@@ -443,7 +444,7 @@ def test_static_schedule_equals_event_runtime(mid_weights, B, paged):
         % (B, paged, C, list(info.tasks_per_op)))
     t0 = _tokens(MID, B, 8)
     a, _ = _logits_seq(s, 3, tokens=t0, schedule=1)
-    b, _ = _logits_seq(s, 3, tokens=t0, kv_chunk=C, kv_chunk_max=C)
+    b, _ = _logits_seq(s, 3, tokens=t0, kv_chunk=C, kv_chunk_max=C, down_ksplit=1)
     _bitwise(a, b)
     if B == 16:
         rows = [0, 15]
