@@ -100,7 +100,9 @@ enum mk_device_error {
  *  prefetch_kb   KB of the next GEMV task's weights each worker pulls toward
  *                the chip (L2 / memory-side cache) while it waits for that
  *                task's event, issued in small slices between polls
- *                (default 256; -1 = off).
+ *                (0: the default, 256 at batch <= 2 and off at batch >= 3,
+ *                where the matrix-core GEMV's streams measured faster
+ *                without it; -1 = off).
  *  lds_stream    1: at batch 1 with bf16 weights, the persistent kernel streams
  *                weight pages through a per-wave LDS ring filled by
  *                direct-to-LDS buffer loads (experimental; same results).

@@ -515,7 +515,12 @@ KParams make_params(const mk_plan* pl, const mk_weights* w, const mk_kv_cache* k
     p.mb_mask = hp.mb_cap - 1;
     const int wd = d.opts.watchdog_ms > 0 ? d.opts.watchdog_ms : 2000;
     p.watchdog_ticks = (uint64_t)wd * 100000ull;
-    p.prefetch_kb = d.opts.prefetch_kb == 0 ? 256 : (d.opts.prefetch_kb < 0 ? 0 : d.opts.prefetch_kb);
+    // default: on for the batch <= 2 instances (batch 1: 3.76 -> 3.55 ms/step),
+    // off for the matrix-core ones, whose non-temporal streams lost to the
+    // L2 prefetch (batch 16 4.60 -> 4.44, paged batch 8 6.20 -> 6.11, W4 batch
+    // 16 6.58 -> 6.16 ms/step with it off)
+    p.prefetch_kb = d.opts.prefetch_kb == 0 ? (nb_for(d.batch) <= 2 ? 256 : 0)
+                                            : (d.opts.prefetch_kb < 0 ? 0 : d.opts.prefetch_kb);
     p.pre_slots = lds_preload_on(pl) ? kPreSlots : 0;
     p.w4 = d.weight_dtype == MK_W4 ? 1 : 0;
     p.wtiled = d.weight_layout == MK_WEIGHTS_TILED ? 1 : 0;
