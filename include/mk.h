@@ -45,7 +45,7 @@ enum mk_status {
     MK_OK = 0,
     MK_ERR_ARG = -1,         /* invalid argument (null pointer, bad shape, mismatch with the plan) */
     MK_ERR_HIP = -2,         /* a HIP runtime call failed (message says which) */
-    MK_ERR_UNSUPPORTED = -3, /* valid request this build does not support */
+    MK_ERR_UNSUPPORTED = -3, /* valid request this library does not support */
     MK_ERR_STATE = -4        /* plan in a state that forbids the call (e.g. host-only plan) */
 };
 
