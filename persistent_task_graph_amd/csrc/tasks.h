@@ -1306,9 +1306,6 @@ __device__ __forceinline__ void run_w4_mfma_task(const KParams& p, const TaskRec
     trace_mark(p, s.marks, 2);
 }
 
-// w: the task's layer pointers, p.lw[t.layer] (the worker reads them before
-// the task's event fires). pre_rows: leading rows of the task whose weights
-// were preloaded into this worker's LDS slots (batch <= 2 only; 0 otherwise).
 // Pipeline stages of the matrix-core GEMV with tiled weights: QKV and
 // gate/up (several tiles per pass), O and down (one tile per pass).
 #ifndef MK_TILED_NST_QG
@@ -1407,6 +1404,9 @@ __device__ __forceinline__ bool run_ksplit(const KParams& p, const TaskRec& t, c
     return true;
 }
 
+// w: the task's layer pointers, p.lw[t.layer] (the worker reads them before
+// the task's event fires). pre_rows: leading rows of the task whose weights
+// were preloaded into this worker's LDS slots (batch <= 2 only; 0 otherwise).
 // Returns whether the task signals its event (false only for the parts of a
 // K-split group that do not merge it).
 template <typename WT, int NB>
