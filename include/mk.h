@@ -135,8 +135,8 @@ enum mk_device_error {
  *                row's attention sees the rows before it. Ahead-of-time
  *                attention only (not jit = 1); token input only.
  *  down_ksplit   parts the down projection's K (the SwiGLU width) is cut
- *                into on the matrix-core path (bf16 or W4 weights, batch >= 3,
- *                event runtime; W4 parts span whole 128-input scale groups): each part is its own task over 16 * ksplit rows,
+ *                into on the matrix-core path (bf16, batch >= 3, event
+ *                runtime): each part is its own task over 16 * ksplit rows,
  *                writing a partial tile, and the last part of a row group
  *                to arrive adds the partials in part order (the attention
  *                combine's last-arrival rule, the MPK article §2.1) and

@@ -273,20 +273,18 @@ bool build_host_plan(const mk_model_desc& d, int device_cus, HostPlan& p, std::s
     }
     if (p.max_splits > 65535) return fail(err, "too many splits per sequence");
     {
-        // K split of the O and down projections on the matrix-core path (bf16
-        // or W4 weights; W4 parts span whole 128-input scale groups)
-        const bool mf_path = (d.weight_dtype == MK_BF16 || d.weight_dtype == MK_W4) && d.batch >= 3;
+        // K split of the O and down projections on the matrix-core path
+        const bool mf_path = d.weight_dtype == MK_BF16 && d.batch >= 3;
         // default: 4 parts for down, none for O (measured no faster split)
         auto pick = [&](int ks, int64_t K, const char* name, int auto_parts, int& outk) {
             const std::string n(name);
             if (ks != 0 && ks != 1 && ks != 2 && ks != 4) return fail(err, "opts." + n + " must be 0, 1, 2 or 4");
-            const int64_t unit = d.weight_dtype == MK_W4 ? 128 : 64;  // a part's K granule (W4: one scale group)
             if (ks == 0) {
-                ks = (mf_path && o.schedule == 0 && K % (unit * auto_parts) == 0) ? auto_parts : 1;
+                ks = (mf_path && o.schedule == 0 && K % (64 * auto_parts) == 0) ? auto_parts : 1;
             } else if (ks > 1) {
-                if (!mf_path) return fail(err, "opts." + n + " > 1 needs the matrix-core path (bf16 or W4 weights, batch >= 3)");
+                if (!mf_path) return fail(err, "opts." + n + " > 1 needs the matrix-core path (bf16 weights, batch >= 3)");
                 if (o.schedule == 1) return fail(err, "opts." + n + " > 1 is not available with the static schedule");
-                if (K % (unit * ks)) return fail(err, "opts." + n + ": K must be a multiple of " + std::to_string(unit) + " * parts");
+                if (K % (64 * ks)) return fail(err, "opts." + n + ": K must be a multiple of 64 * parts");
             }
             outk = ks;
             return true;

@@ -754,8 +754,7 @@ __device__ __forceinline__ void gemv_mfma(const MSeg (&seg)[NSEG], int K, const 
     const int li = lane & 15, lk = lane >> 4;
     const int krow = kfull > 0 ? kfull : K;  // columns per weight row
     const uint32_t rowbytes = W4M ? (uint32_t)krow / 2u : (uint32_t)krow * 2u;  // bytes per weight row (codes for W4)
-    const uint32_t srow = (uint32_t)(krow / kW4Group) * 2u;               // W4: scale bytes per row
-    const uint32_t sofs = (uint32_t)(kofs / kW4Group) * 2u;               // W4: the K range's first scale
+    const uint32_t srow = (uint32_t)(K / kW4Group) * 2u;                  // W4: scale bytes per row
     const int ngroups = K / kW4Group;
     float* scs = s.part + kPartFloats;  // W4: [TMAX][NM][16 rows][ngroups] scales of the pass
     const int nblk = (K + 63) >> 6;
@@ -818,7 +817,7 @@ __device__ __forceinline__ void gemv_mfma(const MSeg (&seg)[NSEG], int K, const 
                         float v = 0.f;
                         if (t0 + t < ntile && row < tval[t]) {
                             const uint32_t h = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
-                                m == 0 ? tsa[t] : tsb[t], (uint32_t)row * srow + sofs + (uint32_t)g * 2u, tsoffs[t], 0);
+                                m == 0 ? tsa[t] : tsb[t], (uint32_t)row * srow + (uint32_t)g * 2u, tsoffs[t], 0);
                             v = __uint_as_float(h << 16);
                         }
                         scs[((t * NM + m) * 16 + row) * ngroups + g] = v;
@@ -842,7 +841,7 @@ __device__ __forceinline__ void gemv_mfma(const MSeg (&seg)[NSEG], int K, const 
 #pragma unroll
                 for (int t = 0; t < TMAX; ++t) {
                     if constexpr (W4M) {
-                        const uint32_t vo = (kok && li < tval[t]) ? (uint32_t)li * rowbytes + (uint32_t)(kofs + k) / 2u : kOOB;
+                        const uint32_t vo = (kok && li < tval[t]) ? (uint32_t)li * rowbytes + (uint32_t)k / 2u : kOOB;
                         st.q[t][0][c] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(ta[t], vo, tsoff[t], kStreamAux);
                         if constexpr (DUAL) st.q[t][1][c] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(tb[t], vo, tsoff[t], kStreamAux);
                     } else if constexpr (TL) {
@@ -1336,8 +1335,7 @@ __device__ __forceinline__ void mfma_dispatch(const KParams& p, F f) {
 // order). Returns whether this task signals the event (the merging part
 // only). Partial layout: group at p.kpart + a0 * ks * 16, part kp at
 // kp * (a1 - a0) * 16, row i at i * 16, one float per sequence.
-// W4: the same with 4-bit codes (K parts on whole 128-input scale groups).
-template <int NB, bool W4 = false>
+template <int NB>
 __device__ __forceinline__ bool run_ksplit(const KParams& p, const TaskRec& t, const Lds& s, const LayerPtrs& w) {
     const int kp = t.kpart & 0xFF, ks = t.kpart >> 8;
     const int l = t.layer, B = p.B, H = p.H, r0 = t.a0, r1 = t.a1, nr = r1 - r0;
@@ -1345,21 +1343,14 @@ __device__ __forceinline__ bool run_ksplit(const KParams& p, const TaskRec& t, c
     const int K = down ? p.F : p.QD;
     const int kw = K / ks, k0 = kp * kw;
     float* part = p.kpart + (int64_t)r0 * ks * 16;
+    const MatTile<bf16_t> td((const bf16_t*)(down ? w.w_down : w.wo), K, H, r0, r1);
     auto out = [&](int r, int b, float v, float) { st_co(&part[((int64_t)kp * nr + (r - r0)) * 16 + b], v); };
+    const MSeg sg[1] = {{td.r, td.r, td.n, td.lo}};
     const float* xin = layer_buf(p, l, down ? p.off_h : p.off_attn) + k0;
-    if constexpr (W4) {
-        const W4Tile td = w4_tile(down ? w.w_down : w.wo, K, H, r0, r1);
-        const MSeg sg[1] = {{td.q, td.q, td.n, td.lo, td.sc, td.sc}};
-        gemv_mfma<NB, false, 4, 1, decltype(out), 2, true>(sg, kw, xin, K, B, (const bf16_t*)nullptr, p.eps, out, s,
-                                                          p.trace != nullptr, k0, K);
-    } else {
-        const MatTile<bf16_t> td((const bf16_t*)(down ? w.w_down : w.wo), K, H, r0, r1);
-        const MSeg sg[1] = {{td.r, td.r, td.n, td.lo}};
-        mfma_dispatch(p, [&](auto tl) {
-            gemv_mfma<NB, false, 4, 1, decltype(out), 2, false, decltype(tl)::value>(
-                sg, kw, xin, K, B, (const bf16_t*)nullptr, p.eps, out, s, p.trace != nullptr, k0, K);
-        });
-    }
+    mfma_dispatch(p, [&](auto tl) {
+        gemv_mfma<NB, false, 4, 1, decltype(out), 2, false, decltype(tl)::value>(
+            sg, kw, xin, K, B, (const bf16_t*)nullptr, p.eps, out, s, p.trace != nullptr, k0, K);
+    });
     // arrival on the group's counter once this part's stores are complete
     wait_stores();
     __syncthreads();
@@ -1417,16 +1408,8 @@ __device__ __forceinline__ bool run_gemv_task(const KParams& p, const TaskRec& t
     // kernels that code would cost registers, and spills, when unused)
     if constexpr (std::is_same<WT, bf16_t>::value && (NB <= 2 || kW4MfmaKernels)) {
         if (p.w4 && t.op != OP_LM && t.op != OP_EMBED && t.op != OP_APPEND) {
-            if constexpr (NB <= 2) {
-                run_w4_task<NB>(p, t, s, w);
-            } else {
-                if (t.kpart >> 8 > 1) {
-                    const bool sig = run_ksplit<NB, true>(p, t, s, w);
-                    trace_mark(p, s.marks, 2);
-                    return sig;
-                }
-                run_w4_mfma_task<NB>(p, t, s, w);
-            }
+            if constexpr (NB <= 2) run_w4_task<NB>(p, t, s, w);
+            else run_w4_mfma_task<NB>(p, t, s, w);
             return true;
         }
     }
@@ -1871,7 +1854,6 @@ __device__ __forceinline__ Prefetch prefetch_setup(const KParams& p, const TaskR
     // of the batch <= 2 instances (there it measured 1% slower at batch 1 even
     // though it never ran: it changes their register allocation)
     if ((t.op == OP_DOWN || t.op == OP_O) && (t.kpart >> 8) > 1) {
-        if (p.w4) return f;  // W4 parts: no prefetch (their code rows are not whole KB chunks)
         // a K part of the O or down projection reads columns [k0, k0 + kw)
         // of its rows: per row kw * 2 bytes, F * 2 apart (row-major), or per
         // 8-row unit kw * 16 bytes, 16 F apart (tiled; F: the row length);

@@ -508,14 +508,9 @@ def test_mid_w4_matrix_cores_modes_bitwise(mid_w4_weights):
     s = make_setup(MID_W4, 16, lens, 520, weights=mid_w4_weights)
     t0 = _tokens(MID_W4, 16, 15)
     a, _ = _logits_seq(s, 3, tokens=t0, kv_chunk=128, kv_chunk_max=128)
-    for o in (dict(mode=1), dict(jit=3), dict(jit=1)):
+    for o in (dict(mode=1), dict(schedule=1), dict(jit=3), dict(jit=1)):
         b, _ = _logits_seq(s, 3, tokens=t0, kv_chunk=128, kv_chunk_max=128, **o)
         _bitwise(a, b)
-    # the static schedule keeps whole-K down tasks: the same bits as the
-    # event runtime without the K split
-    a1, _ = _logits_seq(s, 3, tokens=t0, kv_chunk=128, kv_chunk_max=128, down_ksplit=1)
-    b, _ = _logits_seq(s, 3, tokens=t0, kv_chunk=128, kv_chunk_max=128, schedule=1)
-    _bitwise(a1, b)
 
 
 def test_mid_w4_modes_bitwise(mid_w4_weights):
