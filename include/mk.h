@@ -69,7 +69,7 @@ enum mk_device_error {
  *                task of a layer posts it to a mailbox, the scheduler waves
  *                expand its split tasks from seq_lens and deal them into the
  *                workers' inboxes, 2 = AOT: each layer queues one attention
- *                slot per split task a step can have (min(240, batch *
+ *                slot per split task a step can have (min(256, batch *
  *                n_kv_heads * max splits), or batch * n_kv_heads *
  *                ceil(max_seq_len / kv_chunk_max) if larger) on the
  *                workers; once the layer's QKV event fires, slot i runs
@@ -83,7 +83,7 @@ enum mk_device_error {
  *  kv_chunk      KV positions per attention split task (default 128; a
  *                multiple of 16). Each step uses the smallest multiple of 16
  *                from kv_chunk up to kv_chunk_max for which the step has at
- *                most 240 split tasks (kv_chunk_max if none does); the rule
+ *                most 256 split tasks (kv_chunk_max if none does); the rule
  *                depends only on seq_lens, so every mode computes the same
  *                splits.
  *  kv_chunk_max  upper bound of that chunk (default 4096, at most 16384, a

@@ -141,11 +141,13 @@ MK_HD inline int ev_append(int l, int n_layers) { return 5 * n_layers + 1 + l; }
 
 MK_HD inline int n_splits_for(int keys, int chunk) { return (keys + chunk - 1) / chunk; }
 
-// Split tasks per step that the attention chunk is sized for: a little
-// under one per worker of a 256-CU device (252 workers), so that a step's
-// split tasks run in one round. A constant (not the worker count), so that
-// results do not depend on how many workers a plan uses.
-constexpr int kAttnSplitTarget = 240;
+// Split tasks per step that the attention chunk is sized for: one per
+// worker of a 256-CU device, so that a step's split tasks run in one round
+// (batch 16, log-uniform lengths: 240 -> 256 took the step from 4.44 to
+// 4.40 ms; 272 or 320, a second round for some workers, 5.0 ms). A constant
+// (not the worker count), so that results do not depend on how many workers
+// a plan uses.
+constexpr int kAttnSplitTarget = 256;
 
 // Keys per attention split in one step: the smallest multiple of 16 in
 // [c0, cmax] for which the step's split tasks, total(c) = sum over b of

@@ -146,7 +146,7 @@ def test_step_on_host_only_plan_is_state_error(lib):
 
 
 def test_aot_attention_slots(lib):
-    # one slot per split task a step can have: at most 240 while the chunk can
+    # one slot per split task a step can have: at most 256 while the chunk can
     # still grow, else every split at kv_chunk_max
     p = _plan(synth.TINY, 1, 48, jit=2, kv_chunk=16)
     inf = p.info()
@@ -159,12 +159,12 @@ def test_aot_attention_slots(lib):
     assert inf.tasks_per_op[mk.OP_ATTN] == 2 * 16 * 8 * 2  # 4200 keys need 2 splits of 4096
     p.verify()
     p = _plan(replace(synth.Q8B, n_layers=2), 4, 1024, jit=2, kv_chunk=128)
-    assert p.info().tasks_per_op[mk.OP_ATTN] == 2 * 240
+    assert p.info().tasks_per_op[mk.OP_ATTN] == 2 * 256
     p.verify()
 
 
 def test_aot_slots_dry_run_capped_chunk(lib):
-    # the chunk capped at kv_chunk_max: more than 240 split tasks, one slot each
+    # the chunk capped at kv_chunk_max: more than 256 split tasks, one slot each
     shape = replace(synth.Q8B, n_layers=2)
     p = _plan(shape, 16, 4200, jit=2, workers=24, kv_chunk=64, kv_chunk_max=64)
     seq = [4000] * 16  # 16 * 8 * 63 split tasks per layer
